@@ -1,0 +1,134 @@
+"""CPU oracle for dense GEMM, C = alpha*A*B + beta*C.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the GPU library and
+its Python binding never do, and nothing here imports them.
+
+The arithmetic lives in ``gemm_oracle.c`` (plain C, double accumulation, see
+its header for the passages it follows).  This module only marshals numpy
+buffers into it.
+
+Element types: ``"f32"`` buffers are float32 (or their uint32 bit patterns),
+``"bf16"`` and ``"f16"`` buffers are uint16 bit patterns.  Matrices are flat
+buffers addressed with a leading dimension, an order (``ROW`` or ``COL``) and
+a per-batch stride in elements, exactly as the GEMM library takes them.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+ROW, COL = 0, 1
+_TYPES = {"f32": 0, "bf16": 1, "f16": 2}
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # ORACLE_LIB lets the mutation test load a deliberately broken build.
+        path = os.environ.get("ORACLE_LIB", _build.LIB)
+        if path == _build.LIB and not os.path.exists(path):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        prob = [i32, i32, i64, i64, i64, dbl, vp, i64, i32, vp, i64, i32, dbl, vp, i64,
+                i32, i64, i64, i64]
+        lib.orc_gemm.argtypes = prob + [i64, vp, vp]
+        lib.orc_gemm.restype = None
+        lib.orc_gemm_at.argtypes = prob + [i64, vp, vp, vp]
+        lib.orc_gemm_at.restype = None
+        lib.orc_decode.argtypes = [i32, vp, vp, i64]
+        lib.orc_decode.restype = None
+        lib.orc_round.argtypes = [i32, vp, vp, i64]
+        lib.orc_round.restype = None
+        lib.orc_max_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _storage(dtype):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+def _buf(x, dtype):
+    """Contiguous host buffer of the stored element type (keeps a reference)."""
+    if x is None:
+        return None, None
+    a = np.ascontiguousarray(x)
+    if dtype == "f32" and a.dtype == np.uint32:
+        a = a.view(np.float32)
+    want = _storage(dtype)
+    if a.dtype != want:
+        raise TypeError(f"oracle: {dtype} buffer must be {np.dtype(want).name}, got {a.dtype}")
+    return a, a.ctypes.data
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def decode(dtype, bits) -> np.ndarray:
+    """Exact values of stored elements, as float64."""
+    a, p = _buf(bits, dtype)
+    out = np.empty(a.size, np.float64)
+    _load().orc_decode(_TYPES[dtype], p, out.ctypes.data, a.size)
+    return out.reshape(a.shape)
+
+
+def round_bits(dtype, x) -> np.ndarray:
+    """Round float64 values to ``dtype`` (nearest-even, directly from double).
+
+    Returns the stored patterns: uint32 for f32, uint16 for bf16/f16.
+    """
+    src = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(src.size, np.uint32 if dtype == "f32" else np.uint16)
+    _load().orc_round(_TYPES[dtype], src.ctypes.data, out.ctypes.data, src.size)
+    return out.reshape(src.shape)
+
+
+def _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
+          ldc, order_c, stride_a, stride_b, stride_c):
+    keep = []
+    ptrs = []
+    for x, dt in ((A, in_dtype), (B, in_dtype), (C0, c_dtype)):
+        a, p = _buf(x, dt)
+        keep.append(a)
+        ptrs.append(p)
+    args = [_TYPES[in_dtype], _TYPES[c_dtype], M, N, K, float(alpha), ptrs[0], lda, order_a,
+            ptrs[1], ldb, order_b, float(beta), ptrs[2], ldc, order_c, stride_a, stride_b,
+            stride_c]
+    return args, keep
+
+
+def gemm(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
+         ldc, order_c, batch=1, stride_a=0, stride_b=0, stride_c=0):
+    """Every element: returns (ref, den) as float64 arrays [batch][M][N].
+
+    ref = alpha*sum_k A_ik B_kj + beta*C0_ij and
+    den = |alpha|*sum_k |A_ik B_kj| + |beta|*|C0_ij|, accumulated in double.
+    """
+    args, keep = _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b,
+                       beta, C0, ldc, order_c, stride_a, stride_b, stride_c)
+    ref = np.empty((batch, M, N), np.float64)
+    den = np.empty((batch, M, N), np.float64)
+    _load().orc_gemm(*args, batch, ref.ctypes.data, den.ctypes.data)
+    del keep
+    return ref, den
+
+
+def gemm_at(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
+            ldc, order_c, idx, stride_a=0, stride_b=0, stride_c=0):
+    """Only the elements listed in ``idx`` (an (n, 3) array of (b, i, j))."""
+    idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 3)
+    args, keep = _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b,
+                       beta, C0, ldc, order_c, stride_a, stride_b, stride_c)
+    n = idx.shape[0]
+    ref = np.empty(n, np.float64)
+    den = np.empty(n, np.float64)
+    _load().orc_gemm_at(*args, n, idx.ctypes.data, ref.ctypes.data, den.ctypes.data)
+    del keep
+    return ref, den

@@ -1,0 +1,238 @@
+/*
+ * CPU oracle for the dense general matrix multiply C = alpha*A*B + beta*C.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the GPU library: it is a separate, plain C
+ * program that anyone can check against the definition by eye.
+ *
+ * What it follows:
+ *   - "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site), section 2.1: the GEMM
+ *     definition C = alpha x A x B + beta x C with A of size M x K, B of size
+ *     K x N and C of size M x N, each output element taking K multiply-adds.
+ *   - "三个周末，从 312 GFLOPS 到 10124 GFLOPS" (m.lqnn.cn), section 1.2: the
+ *     kernel result is checked against a CPU computation in double precision.
+ *
+ * Every output element is the textbook dot product, accumulated in double, in
+ * increasing k order, one rounded double multiply and one rounded double add
+ * per step (the file is compiled with -ffp-contract=off so nothing is fused).
+ * Inputs are decoded from their stored bit patterns exactly into double.
+ * Alongside the result the oracle returns the magnitude scale of the terms,
+ *   den = |alpha| * sum_k |A_ik * B_kj| + |beta| * |C0_ij|,
+ * which the tests use to normalise the error of a GPU result.
+ *
+ * Readings taken where the pages are silent:
+ *   - beta == 0: C0 is not read (BLAS convention), so NaN in C0 does not leak.
+ *   - alpha == 0 or K == 0: the product term is skipped and A, B are not read.
+ *   - 16-bit results are rounded from double to the target format directly,
+ *     round-to-nearest-even, never through float (no double rounding).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_F16 2
+
+#define ORC_ROW 0
+#define ORC_COL 1
+
+/* ---------------------------------------------------------------- decoding */
+
+static double decode_f32(uint32_t bits) {
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* bf16 is the top half of an IEEE binary32 pattern. */
+static double decode_bf16(uint16_t bits) { return decode_f32((uint32_t)bits << 16); }
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double decode_f16(uint16_t bits) {
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 0x1f;
+    int m = bits & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);             /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static double load(int type, const void *base, int64_t idx) {
+    switch (type) {
+    case ORC_F32: {
+        uint32_t b;
+        memcpy(&b, (const char *)base + 4 * idx, 4);
+        return decode_f32(b);
+    }
+    case ORC_BF16:
+        return decode_bf16(((const uint16_t *)base)[idx]);
+    default:
+        return decode_f16(((const uint16_t *)base)[idx]);
+    }
+}
+
+/* Offset of element (r, c) of a matrix stored with leading dimension ld. */
+static int64_t offset(int order, int64_t r, int64_t c, int64_t ld) {
+    return order == ORC_ROW ? r * ld + c : c * ld + r;
+}
+
+/* ---------------------------------------------------------------- rounding */
+
+/*
+ * Round x to the nearest value of a binary format with p significand bits
+ * (counting the implicit one), minimum normal exponent emin and maximum
+ * exponent emax; ties go to even; results beyond the largest finite value
+ * become infinity.  Within one binade the representable values are the
+ * multiples of q = 2^(e - p + 1); below the normal range the spacing stays at
+ * 2^(emin - p + 1).  x / q and r * q are exact (q is a power of two), and
+ * nearbyint rounds to nearest-even in the default floating-point mode.
+ */
+static double round_to_format(double x, int p, int emin, int emax) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e2;
+    frexp(x, &e2);          /* x = f * 2^e2 with 0.5 <= |f| < 1 */
+    int e = e2 - 1;         /* x = 1.xxx * 2^e */
+    if (e < emin) e = emin; /* subnormal range keeps the smallest spacing */
+    double q = ldexp(1.0, e - (p - 1));
+    double r = nearbyint(x / q) * q;
+    double maxfinite = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+    if (fabs(r) > maxfinite) r = copysign(INFINITY, x);
+    return r;
+}
+
+static uint16_t encode_bf16(double r) {
+    /* r is already a bf16 value, hence exactly a binary32 value. */
+    if (isnan(r)) return 0x7fc0;
+    float f = (float)r;
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    return (uint16_t)(b >> 16);
+}
+
+static uint16_t encode_f16(double r) {
+    if (isnan(r)) return 0x7e00;
+    uint16_t sign = signbit(r) ? 0x8000 : 0;
+    double a = fabs(r);
+    if (isinf(a)) return sign | 0x7c00;
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int e = e2 - 1;
+    if (e < -14) /* subnormal: a = m * 2^-24 */
+        return sign | (uint16_t)ldexp(a, 24);
+    uint16_t m = (uint16_t)(ldexp(a, 10 - e) - 1024.0);
+    return sign | (uint16_t)((e + 15) << 10) | m;
+}
+
+/* ---------------------------------------------------------------- exports */
+
+int orc_version(void) { return 1; }
+
+void orc_decode(int type, const void *src, double *dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = load(type, src, i);
+}
+
+/* Round doubles to the stored bit patterns of `type` (uint32 for f32). */
+void orc_round(int type, const double *src, void *dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) {
+        switch (type) {
+        case ORC_F32: {
+            double r = round_to_format(src[i], 24, -126, 127);
+            float f = (float)r; /* exact: r is a binary32 value or inf */
+            if (isnan(src[i])) f = NAN;
+            memcpy((char *)dst + 4 * i, &f, 4);
+            break;
+        }
+        case ORC_BF16:
+            ((uint16_t *)dst)[i] = encode_bf16(round_to_format(src[i], 8, -126, 127));
+            break;
+        default:
+            ((uint16_t *)dst)[i] = encode_f16(round_to_format(src[i], 11, -14, 15));
+            break;
+        }
+    }
+}
+
+struct problem {
+    int in_type, c_type;
+    int64_t M, N, K;
+    double alpha, beta;
+    const void *A, *B, *C0;
+    int64_t lda, ldb, ldc;
+    int oA, oB, oC;
+    int64_t sA, sB, sC;
+};
+
+/*
+ * One output element (b, i, j): the definition of section 2.1 of the
+ * zhenwei.site guide, written out.  A(b,i,k) is element (i, k) of the b-th
+ * M x K matrix, which starts sA elements after the previous one; likewise
+ * B(b,k,j) and C0(b,i,j).
+ */
+static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
+                    double *ref, double *den) {
+    double s = 0.0, t = 0.0;
+    if (P->alpha != 0.0) {
+        const int64_t a0 = b * P->sA, b0 = b * P->sB;
+        for (int64_t k = 0; k < P->K; ++k) {
+            double a = load(P->in_type, P->A, a0 + offset(P->oA, i, k, P->lda));
+            double x = load(P->in_type, P->B, b0 + offset(P->oB, k, j, P->ldb));
+            double p = a * x;
+            s = s + p;
+            t = t + fabs(p);
+        }
+    }
+    double r = P->alpha * s;
+    double d = fabs(P->alpha) * t;
+    if (P->beta != 0.0) {
+        double c0 = load(P->c_type, P->C0, b * P->sC + offset(P->oC, i, j, P->ldc));
+        r = r + P->beta * c0;
+        d = d + fabs(P->beta) * fabs(c0);
+    }
+    *ref = r;
+    *den = d;
+}
+
+#define PROBLEM_ARGS                                                                   \
+    int in_type, int c_type, int64_t M, int64_t N, int64_t K, double alpha,            \
+        const void *A, int64_t lda, int oA, const void *B, int64_t ldb, int oB,        \
+        double beta, const void *C0, int64_t ldc, int oC, int64_t sA, int64_t sB,      \
+        int64_t sC
+
+#define PROBLEM_INIT                                                                   \
+    struct problem P = {in_type, c_type, M,   N,   K,   alpha, beta, A,  B,            \
+                        C0,      lda,    ldb, ldc, oA,  oB,    oC,   sA, sB, sC}
+
+/* All batch*M*N elements; ref and den are dense [batch][M][N]. */
+void orc_gemm(PROBLEM_ARGS, int64_t batch, double *ref, double *den) {
+    PROBLEM_INIT;
+    const int64_t total = batch * M * N;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t e = 0; e < total; ++e) {
+        int64_t b = e / (M * N), i = (e / N) % M, j = e % N;
+        element(&P, b, i, j, &ref[e], &den[e]);
+    }
+}
+
+/* Only the listed elements; idx holds count triples (b, i, j). */
+void orc_gemm_at(PROBLEM_ARGS, int64_t count, const int64_t *idx, double *ref,
+                 double *den) {
+    PROBLEM_INIT;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t e = 0; e < count; ++e)
+        element(&P, idx[3 * e], idx[3 * e + 1], idx[3 * e + 2], &ref[e], &den[e]);
+}
+
+#ifdef _OPENMP
+#include <omp.h>
+int orc_max_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_max_threads(void) { return 1; }
+#endif

@@ -1,0 +1,51 @@
+"""Plant mistakes in copies of the oracle and check that its pins catch each one.
+
+Every mutant is a one-line edit of ``oracle/gemm_oracle.c`` of the kind a
+careless implementation would make (a wrong sign, a dropped term, a swapped
+index, an operand read transposed, an off-by-one bound, truncation instead of
+rounding).  Each is compiled on the CPU into a temporary library, and the pin
+suite is run against it in a child process; the pins must fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "sum_sign": ("s = s + p;", "s = s - p;"),
+    "a_transposed": ("offset(P->oA, i, k, P->lda)", "offset(P->oA, k, i, P->lda)"),
+    "b_transposed": ("offset(P->oB, k, j, P->ldb)", "offset(P->oB, j, k, P->ldb)"),
+    "beta_dropped": ("r = r + P->beta * c0;", "r = r + c0;"),
+    "alpha_dropped": ("double r = P->alpha * s;", "double r = s;"),
+    "den_beta_dropped": ("d = d + fabs(P->beta) * fabs(c0);", "d = d;"),
+    "last_k_dropped": ("k < P->K; ++k", "k + 1 < P->K; ++k"),
+    "col_major_ignored": ("order == ORC_ROW ? r * ld + c : c * ld + r",
+                          "order == ORC_ROW ? r * ld + c : r * ld + c"),
+    "batch_stride_b_wrong": ("b0 = b * P->sB", "b0 = b * P->sA"),
+    "f16_exponent_off": ("e - 25); /* (1 + m/1024)", "e - 24); /* (1 + m/1024)"),
+    "round_truncates": ("nearbyint(x / q)", "trunc(x / q)"),
+    "no_overflow_to_inf": ("if (fabs(r) > maxfinite) r = copysign(INFINITY, x);", ""),
+    "subnormal_spacing": ("if (e < emin) e = emin;", ""),
+    "flat_index_wrong": ("i = (e / N) % M, j = e % N", "i = (e / N) % M, j = (e + 1) % N"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut_src = tmp_path / "mutant.c"
+    mut_src.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    obuild.build(src=str(mut_src), out=lib)
+    env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

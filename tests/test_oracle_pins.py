@@ -1,0 +1,429 @@
+"""Pins for the CPU oracle, against things other than the oracle itself.
+
+Each test checks the oracle against a fact fixed by mathematics or by an
+independent library routine: exact rational arithmetic on tiny problems,
+closed forms (identity, permutation, all-ones, rank-1), numpy's own float16
+and float32 conversions, exhaustive decoding of every 16-bit pattern, layout
+and batch invariants, and a hand-worked example of the definition.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import COL, ROW
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+U = 2.0 ** -53  # unit roundoff of double
+
+
+# --------------------------------------------------------------- independent helpers
+
+def np_decode(dtype, bits):
+    """Decode stored patterns with numpy only (independent of the oracle)."""
+    bits = np.asarray(bits)
+    if dtype == "f32":
+        return np.asarray(bits, np.float32).astype(np.float64) if bits.dtype != np.uint32 \
+            else bits.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rne_fraction(x: Fraction, p: int, emin: int, emax: int) -> float:
+    """Exact round-to-nearest-even of a rational to a p-bit binary format."""
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    q = Fraction(2) ** (e - p + 1)
+    n = a / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * q
+    if r > (2 - Fraction(2) ** (1 - p)) * Fraction(2) ** emax:
+        return sign * math.inf
+    return sign * float(r)
+
+
+FORMATS = {"bf16": (8, -126, 127), "f16": (11, -14, 15), "f32": (24, -126, 127)}
+
+
+def rand_bits(rng, dtype, n, scale=1.0):
+    x = rng.standard_normal(n) * scale
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    f = x.astype(np.float32).view(np.uint32)
+    return (f >> 16).astype(np.uint16)  # truncation is fine: any pattern is a valid input
+
+
+def stored(dtype, values):
+    """Exactly representable small values -> stored patterns."""
+    v = np.asarray(values, np.float64)
+    if dtype == "f32":
+        return v.astype(np.float32)
+    if dtype == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def put(mat, order, ld=None):
+    """Store a 2-D float array in row- or column-major order with leading dim ld."""
+    r, c = mat.shape
+    if order == ROW:
+        ld = ld or c
+        out = np.zeros(max(0, (r - 1) * ld + c) if r and c else 0, mat.dtype)
+        for i in range(r):
+            out[i * ld:i * ld + c] = mat[i]
+    else:
+        ld = ld or r
+        out = np.zeros(max(0, (c - 1) * ld + r) if r and c else 0, mat.dtype)
+        for j in range(c):
+            out[j * ld:j * ld + r] = mat[:, j]
+    return out, ld
+
+
+# --------------------------------------------------------------- decoding / rounding
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_decode_every_16bit_pattern(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(dtype, bits)
+    want = np_decode(dtype, bits)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def _round_cases(rng):
+    x = np.concatenate([
+        rng.standard_normal(20000),
+        rng.standard_normal(5000) * 1e-6,
+        rng.standard_normal(5000) * 1e4,
+        np.ldexp(rng.uniform(1, 2, 2000), rng.integers(-160, 140, 2000)),
+    ])
+    return x
+
+
+def test_round_f16_matches_numpy():
+    rng = np.random.default_rng(1)
+    x = _round_cases(rng)
+    # exact ties between neighbouring f16 values, and ties nudged by 2^-40
+    base = rng.standard_normal(4000).astype(np.float16).astype(np.float64)
+    ulp = np.spacing(base.astype(np.float16)).astype(np.float64)
+    ties = base + ulp / 2
+    x = np.concatenate([x, ties, ties + np.abs(ties) * 2.0 ** -40, ties - np.abs(ties) * 2.0 ** -40,
+                        [65504.0, 65519.99, 65520.0, 1e6, -7e4, 2.0 ** -24, 2.0 ** -25,
+                         3 * 2.0 ** -26, 0.0, -0.0]])
+    got = oracle.round_bits("f16", x)
+    want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_round_f32_matches_numpy():
+    rng = np.random.default_rng(2)
+    x = _round_cases(rng)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float32).view(np.uint32)
+    assert np.array_equal(oracle.round_bits("f32", x), want)
+
+
+def test_round_bf16_matches_exact_rational():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([_round_cases(rng)[:6000],
+                        # ties of bf16 (1 + 2^-8) and ties nudged below float's resolution,
+                        # which a double -> float -> bf16 path would round the wrong way
+                        [1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 3 * 2.0 ** -8,
+                         -(1 + 2.0 ** -8 + 2.0 ** -40), 3.3895313892515355e38, 3.4e38,
+                         2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135]])
+    got = oracle.decode("bf16", oracle.round_bits("bf16", x))
+    p, emin, emax = FORMATS["bf16"]
+    want = np.array([rne_fraction(Fraction(v), p, emin, emax) for v in x])
+    assert np.array_equal(got, want)
+    # the nudged tie rounds up, the exact tie rounds to even (down)
+    assert got[6000] == 1.0 and got[6001] == 1 + 2.0 ** -7
+
+
+def test_round_bf16_agrees_with_torch_on_float32_values():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(4)
+    x32 = rng.standard_normal(50000).astype(np.float32) * 3
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_bits("bf16", x32.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------- brute force, exact rationals
+
+def exact_problem(rng, dtype, c_dtype, M, N, K, oA, oB, oC, alpha, beta, batch, bcast):
+    A_mats = [rand_bits(rng, dtype, M * K).reshape(M, K) for _ in range(batch)]
+    B_mats = [rand_bits(rng, dtype, K * N).reshape(K, N) for _ in range(batch)]
+    C_mats = [rand_bits(rng, c_dtype, M * N).reshape(M, N) for _ in range(batch)]
+    if bcast == "a":
+        A_mats = [A_mats[0]] * batch
+    if bcast == "b":
+        B_mats = [B_mats[0]] * batch
+
+    def pack(mats, order, ld_pad, bc):
+        bufs, ld = [], None
+        for m in mats[:1] if bc else mats:
+            buf, ld = put(m, order, (m.shape[1] if order == ROW else m.shape[0]) + ld_pad)
+            bufs.append(buf)
+        stride = 0 if bc else bufs[0].size + 3
+        total = np.zeros(stride * (len(bufs) - 1) + bufs[0].size, bufs[0].dtype)
+        for b, buf in enumerate(bufs):
+            total[b * stride:b * stride + buf.size] = buf
+        return total, ld, stride
+
+    A, lda, sA = pack(A_mats, oA, 2, bcast == "a")
+    B, ldb, sB = pack(B_mats, oB, 1, bcast == "b")
+    C, ldc, sC = pack(C_mats, oC, 0, False)
+    ref, den = oracle.gemm(dtype, c_dtype, M, N, K, alpha, A, lda, oA, B, ldb, oB, beta, C, ldc,
+                           oC, batch=batch, stride_a=sA, stride_b=sB, stride_c=sC)
+    fa, fb, fc = (lambda m: np_decode(dtype, m)), (lambda m: np_decode(dtype, m)), \
+        (lambda m: np_decode(c_dtype, m))
+    exact = np.empty((batch, M, N), object)
+    scale = np.empty((batch, M, N), object)
+    for b in range(batch):
+        a, bb, c = fa(A_mats[b]), fb(B_mats[b]), fc(C_mats[b])
+        for i in range(M):
+            for j in range(N):
+                terms = [Fraction(a[i, k]) * Fraction(bb[k, j]) for k in range(K)]
+                s = Fraction(alpha) * sum(terms, Fraction(0))
+                t = abs(Fraction(alpha)) * sum((abs(x) for x in terms), Fraction(0))
+                if beta != 0:
+                    s += Fraction(beta) * Fraction(c[i, j])
+                    t += abs(Fraction(beta)) * abs(Fraction(c[i, j]))
+                exact[b, i, j], scale[b, i, j] = s, t
+    return ref, den, exact, scale
+
+
+CASES = []
+_r = np.random.default_rng(7)
+for n in range(60):
+    dt = ["f32", "bf16", "f16"][n % 3]
+    CASES.append(dict(
+        seed=100 + n, dtype=dt, c_dtype=dt if n % 4 else "f32",
+        M=int(_r.integers(1, 7)), N=int(_r.integers(1, 7)), K=int(_r.integers(1, 9)),
+        oA=int(_r.integers(0, 2)), oB=int(_r.integers(0, 2)), oC=int(_r.integers(0, 2)),
+        alpha=float([1.0, 0.5, -1.75, 3.0][n % 4]), beta=float([0.0, 1.0, -0.25, 2.0][(n // 4) % 4]),
+        batch=int(_r.integers(1, 4)), bcast=["", "a", "b", ""][n % 4]))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c['dtype']}-{c['M']}x{c['N']}x{c['K']}-"
+                         f"o{c['oA']}{c['oB']}{c['oC']}-b{c['batch']}{c['bcast']}-s{c['seed']}")
+def test_oracle_vs_exact_rationals(case):
+    rng = np.random.default_rng(case["seed"])
+    K = case["K"]
+    ref, den, exact, scale = exact_problem(
+        rng, case["dtype"], case["c_dtype"], case["M"], case["N"], K, case["oA"], case["oB"],
+        case["oC"], case["alpha"], case["beta"], case["batch"], case["bcast"])
+    bound = (K + 3) * U
+    for idx in np.ndindex(ref.shape):
+        ex, sc = exact[idx], scale[idx]
+        assert abs(Fraction(ref[idx]) - ex) <= Fraction(bound) * sc, idx
+        assert abs(Fraction(den[idx]) - sc) <= Fraction(bound) * sc, idx
+    # 16-bit results: rounding the double result gives the exact result's rounding
+    for dt in ("bf16", "f16"):
+        p, emin, emax = FORMATS[dt]
+        q = oracle.decode(dt, oracle.round_bits(dt, ref))
+        for idx in np.ndindex(ref.shape):
+            want = rne_fraction(exact[idx], p, emin, emax)
+            if q[idx] != want:
+                # only allowed when the exact value sits within the error bound of a tie
+                lo, hi = sorted([q[idx], want])
+                mid = (Fraction(lo) + Fraction(hi)) / 2
+                assert abs(mid - exact[idx]) <= Fraction(bound) * scale[idx], idx
+
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_2x2.json")))
+    A = np.array(g["A"], np.float32).ravel()
+    B = np.array(g["B"], np.float32).ravel()
+    C0 = np.array(g["C0"], np.float32).ravel()
+    ref, den = oracle.gemm("f32", "f32", 2, 2, 2, g["alpha"], A, 2, ROW, B, 2, ROW, g["beta"], C0,
+                           2, ROW)
+    assert np.array_equal(ref[0], np.array(g["C"], np.float64))
+    assert np.array_equal(den[0], np.array(g["abs_scale"], np.float64))
+
+
+# --------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_identity(dtype):
+    rng = np.random.default_rng(11)
+    M = N = 13
+    A = stored(dtype, np.eye(M))
+    B = rand_bits(rng, dtype, M * N)
+    C0 = rand_bits(rng, dtype, M * N)
+    ref, _ = oracle.gemm(dtype, dtype, M, N, M, 1.0, A, M, ROW, B, N, ROW, 0.0, C0, N, ROW)
+    assert np.array_equal(ref[0].ravel(), np_decode(dtype, B))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_permutation(dtype):
+    rng = np.random.default_rng(12)
+    M, N = 17, 9
+    perm = rng.permutation(M)
+    P = np.zeros((M, M))
+    P[np.arange(M), perm] = 1.0
+    B = rand_bits(rng, dtype, M * N)
+    ref, _ = oracle.gemm(dtype, dtype, M, N, M, 1.0, stored(dtype, P.ravel()), M, ROW, B, N, ROW,
+                         0.0, None, N, ROW)
+    assert np.array_equal(ref[0], np_decode(dtype, B).reshape(M, N)[perm])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_all_ones_closed_form(dtype):
+    # every C_ij = K*alpha + beta*C0_ij, exactly (all values small integers / halves)
+    rng = np.random.default_rng(13)
+    M, N, K = 7, 11, 300
+    alpha, beta = 1.5, -2.0
+    c0 = rng.integers(-8, 9, M * N).astype(np.float64)
+    ref, den = oracle.gemm(dtype, dtype, M, N, K, alpha, stored(dtype, np.ones(M * K)), K, ROW,
+                           stored(dtype, np.ones(K * N)), N, ROW, beta, stored(dtype, c0), N, ROW)
+    assert np.array_equal(ref[0].ravel(), K * alpha + beta * c0)
+    assert np.array_equal(den[0].ravel(), K * abs(alpha) + abs(beta) * np.abs(c0))
+
+
+def test_rank_one_closed_form():
+    rng = np.random.default_rng(14)
+    M, N, K = 9, 10, 57
+    a = rng.integers(-5, 6, M).astype(np.float64)
+    b = rng.integers(-5, 6, N).astype(np.float64)
+    A = np.repeat(a[:, None], K, axis=1)
+    B = np.repeat(b[None, :], K, axis=0)
+    ref, _ = oracle.gemm("f32", "f32", M, N, K, 1.0, stored("f32", A.ravel()), K, ROW,
+                         stored("f32", B.ravel()), N, ROW, 0.0, None, N, ROW)
+    assert np.array_equal(ref[0], K * np.outer(a, b))
+
+
+def test_integer_product_matches_int64_matmul():
+    # integer entries keep every double operation exact, so the oracle must equal the
+    # exact integer product (numpy int64 matmul) for any shape and layout
+    rng = np.random.default_rng(15)
+    M, N, K = 23, 31, 45
+    A = rng.integers(-8, 9, (M, K))
+    B = rng.integers(-8, 9, (K, N))
+    want = (A @ B).astype(np.float64)
+    for oA in (ROW, COL):
+        for oB in (ROW, COL):
+            Ab, lda = put(A.astype(np.float32), oA, (K if oA == ROW else M) + 5)
+            Bb, ldb = put(B.astype(np.float32), oB)
+            ref, _ = oracle.gemm("f32", "f32", M, N, K, 1.0, Ab, lda, oA, Bb, ldb, oB, 0.0, None,
+                                 N, ROW)
+            assert np.array_equal(ref[0], want), (oA, oB)
+
+
+def test_close_to_numpy_float64_matmul():
+    rng = np.random.default_rng(16)
+    M, N, K = 33, 47, 61
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    ref, den = oracle.gemm("f32", "f32", M, N, K, 1.0, A.ravel(), K, ROW, B.ravel(), N, ROW, 0.0,
+                           None, N, ROW)
+    want = A.astype(np.float64) @ B.astype(np.float64)
+    assert np.all(np.abs(ref[0] - want) <= 2 * K * U * den[0])
+    assert np.allclose(den[0], np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64)),
+                       rtol=4 * K * U, atol=0)
+
+
+# --------------------------------------------------------------- layout, batch, quick returns
+
+def test_layouts_give_identical_doubles():
+    rng = np.random.default_rng(17)
+    M, N, K = 12, 19, 33
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    C = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    base = None
+    for oA in (ROW, COL):
+        for oB in (ROW, COL):
+            for oC in (ROW, COL):
+                Ab, lda = put(A, oA, None)
+                Bb, ldb = put(B, oB, None)
+                Cb, ldc = put(C, oC, None)
+                ref, den = oracle.gemm("f32", "f32", M, N, K, 0.75, Ab, lda, oA, Bb, ldb, oB,
+                                       -1.25, Cb, ldc, oC)
+                if base is None:
+                    base = (ref, den)
+                assert np.array_equal(ref, base[0]) and np.array_equal(den, base[1])
+
+
+def test_batch_slices_equal_single_calls():
+    rng = np.random.default_rng(18)
+    M, N, K, batch = 6, 5, 7, 4
+    A = rng.uniform(-1, 1, batch * M * K).astype(np.float32)
+    B = rng.uniform(-1, 1, K * N).astype(np.float32)  # broadcast: stride 0
+    C = rng.uniform(-1, 1, batch * M * N).astype(np.float32)
+    ref, den = oracle.gemm("f32", "f32", M, N, K, 1.0, A, K, ROW, B, N, ROW, 0.5, C, N, ROW,
+                           batch=batch, stride_a=M * K, stride_b=0, stride_c=M * N)
+    for b in range(batch):
+        r1, d1 = oracle.gemm("f32", "f32", M, N, K, 1.0, A[b * M * K:(b + 1) * M * K], K, ROW, B,
+                             N, ROW, 0.5, C[b * M * N:(b + 1) * M * N], N, ROW)
+        assert np.array_equal(ref[b], r1[0]) and np.array_equal(den[b], d1[0])
+
+
+def test_gemm_at_matches_full():
+    rng = np.random.default_rng(19)
+    M, N, K, batch = 9, 8, 10, 3
+    A = rand_bits(rng, "bf16", batch * M * K)
+    B = rand_bits(rng, "bf16", batch * K * N)
+    C = rand_bits(rng, "bf16", batch * M * N)
+    kw = dict(stride_a=M * K, stride_b=K * N, stride_c=M * N)
+    ref, den = oracle.gemm("bf16", "bf16", M, N, K, 2.0, A, M, COL, B, N, ROW, 1.0, C, N, ROW,
+                           batch=batch, **kw)
+    idx = np.stack([rng.integers(0, batch, 50), rng.integers(0, M, 50), rng.integers(0, N, 50)], 1)
+    r, d = oracle.gemm_at("bf16", "bf16", M, N, K, 2.0, A, M, COL, B, N, ROW, 1.0, C, N, ROW,
+                          idx, **kw)
+    assert np.array_equal(r, ref[idx[:, 0], idx[:, 1], idx[:, 2]])
+    assert np.array_equal(d, den[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
+def test_beta_zero_does_not_read_c():
+    rng = np.random.default_rng(20)
+    M, N, K = 4, 5, 6
+    A = rng.uniform(-1, 1, M * K).astype(np.float32)
+    B = rng.uniform(-1, 1, K * N).astype(np.float32)
+    C = np.full(M * N, np.nan, np.float32)
+    ref, den = oracle.gemm("f32", "f32", M, N, K, 1.0, A, K, ROW, B, N, ROW, 0.0, C, N, ROW)
+    assert np.all(np.isfinite(ref)) and np.all(np.isfinite(den))
+
+
+def test_alpha_zero_and_k_zero_scale_c_only():
+    M, N, K = 4, 5, 6
+    A = np.full(M * K, np.nan, np.float32)
+    B = np.full(K * N, np.nan, np.float32)
+    C = np.arange(M * N, dtype=np.float32) - 7
+    ref, _ = oracle.gemm("f32", "f32", M, N, K, 0.0, A, K, ROW, B, N, ROW, -0.5, C, N, ROW)
+    assert np.array_equal(ref[0].ravel(), -0.5 * C.astype(np.float64))
+    ref, _ = oracle.gemm("f32", "f32", M, N, 0, 3.0, None, 1, ROW, None, N, ROW, 2.0, C, N, ROW)
+    assert np.array_equal(ref[0].ravel(), 2.0 * C.astype(np.float64))
+
+
+def test_page_throughput_figures_follow_2mnk():
+    # the TFLOPS figures the pages print are 2*M*N*K / t; the benchmark uses the same count
+    g = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+    for e in g["entries"]:
+        flop = 2 * e["M"] * e["N"] * e["K"]
+        if "gflop" in e:
+            assert abs(flop / 1e9 - e["gflop"]) <= e["gflop_rel_tol"] * e["gflop"], e["cite"]
+        if "tflops" in e:
+            assert abs(flop / e["time_s"] / 1e12 - e["tflops"]) <= e["tflops_rel_tol"] * e["tflops"], \
+                e["cite"]

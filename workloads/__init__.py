@@ -1,0 +1,209 @@
+"""Seeded synthetic inputs for the GEMM workloads.
+
+This module is the one piece that both the GPU tests and the CPU oracle
+consume.  It holds no GEMM arithmetic: it draws random numbers, rounds them to
+the stored element type and describes each problem (shapes, scalars, layouts).
+
+Recipe (the pages fix shapes but not distributions or seeds beyond what is
+listed here, so the reading taken is stated once, here):
+
+* random numbers come from numpy's PCG64 (``np.random.default_rng(seed)``),
+  seed 0 unless a workload states another, drawn in the order A, B, then C0
+  (P for the attention product), each in row-major element order of the
+  matrix as a mathematical object (independent of how it is then stored);
+* fp32 entries: ``uniform(-1, 1)`` in float64, rounded to float32;
+* bf16/fp16 entries: ``sigma * standard_normal()`` in float64, rounded to
+  float32, then to the 16-bit type with round-to-nearest-even (torch's CPU
+  conversion);
+* softmax rows (the attention probabilities): logits uniform(-1, 1), a
+  row-wise softmax in float64, then rounded like any bf16 entry.
+
+Shapes follow the pages: the square 4096 problem of "CUDA GEMM 矩阵乘法优化指南"
+section 2.1 and of the hgemm sm120 article's benchmark; the transformer-layer
+shapes listed in section 1 of "第4章：经典算子实现 —— GEMM" (QKV projection,
+FFN up/down, batched QK^T and PV).
+"""
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+import torch
+
+ROW, COL = 0, 1
+
+
+@dataclass
+class Problem:
+    """One (possibly batched) GEMM: C = alpha * op(A) @ op(B) + beta * C.
+
+    Element (i, k) of A lives at ``A[b*stride_a + i*lda + k]`` when
+    ``order_a == ROW`` and at ``A[b*stride_a + k*lda + i]`` when COL; likewise
+    B (K x N) and C (M x N).  ``in_dtype`` is the type of A and B, ``c_dtype``
+    the type of C (both its initial value and the result).
+    """
+    name: str
+    in_dtype: str
+    c_dtype: str
+    M: int
+    N: int
+    K: int
+    alpha: float = 1.0
+    beta: float = 0.0
+    order_a: int = ROW
+    order_b: int = ROW
+    order_c: int = ROW
+    lda: Optional[int] = None
+    ldb: Optional[int] = None
+    ldc: Optional[int] = None
+    batch: int = 1
+    stride_a: Optional[int] = None
+    stride_b: Optional[int] = None
+    stride_c: Optional[int] = None
+    sigma_a: float = 1.0
+    sigma_b: float = 1.0
+    sigma_c: float = 1.0
+    a_kind: str = "default"          # "default" or "softmax" (rows of P)
+    seed: int = 0
+    note: str = ""
+
+    def __post_init__(self):
+        M, N, K = self.M, self.N, self.K
+        if self.lda is None:
+            self.lda = max(1, K if self.order_a == ROW else M)
+        if self.ldb is None:
+            self.ldb = max(1, N if self.order_b == ROW else K)
+        if self.ldc is None:
+            self.ldc = max(1, N if self.order_c == ROW else M)
+        if self.stride_a is None:
+            self.stride_a = self.footprint("a")
+        if self.stride_b is None:
+            self.stride_b = self.footprint("b")
+        if self.stride_c is None:
+            self.stride_c = self.footprint("c")
+
+    def dims(self, which):
+        return {"a": (self.M, self.K, self.order_a, self.lda),
+                "b": (self.K, self.N, self.order_b, self.ldb),
+                "c": (self.M, self.N, self.order_c, self.ldc)}[which]
+
+    def footprint(self, which) -> int:
+        """Elements one matrix of the batch spans (0 if it is empty)."""
+        r, c, order, ld = self.dims(which)
+        if r == 0 or c == 0:
+            return 0
+        outer, inner = (r, c) if order == ROW else (c, r)
+        return (outer - 1) * ld + inner
+
+    def buffer_elems(self, which) -> int:
+        stride = {"a": self.stride_a, "b": self.stride_b, "c": self.stride_c}[which]
+        fp = self.footprint(which)
+        if self.batch == 0 or fp == 0:
+            return 0
+        return (self.batch - 1) * stride + fp
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K * self.batch
+
+    def with_(self, **kw) -> "Problem":
+        return replace(self, **kw)
+
+
+def _f32(x64: np.ndarray) -> np.ndarray:
+    return x64.astype(np.float32)
+
+
+def to_16bit(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float values to bf16/fp16 bit patterns (uint16), nearest-even."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return t.to(tdt).view(torch.int16).numpy().view(np.uint16)
+
+
+def _draw(rng, dtype, rows, cols, sigma, kind="default"):
+    """Draw a rows x cols matrix (row-major element order) in its stored type."""
+    if kind == "softmax":
+        logits = rng.uniform(-1.0, 1.0, size=(rows, cols))
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        return to_16bit(_f32(p), dtype) if dtype != "f32" else _f32(p)
+    if dtype == "f32":
+        return _f32(rng.uniform(-1.0, 1.0, size=(rows, cols)) * sigma)
+    return to_16bit(_f32(rng.standard_normal(size=(rows, cols)) * sigma), dtype)
+
+
+def _store(mat: np.ndarray, order: int, ld: int, batch_stride: int, b: int,
+           out: np.ndarray):
+    rows, cols = mat.shape
+    if rows == 0 or cols == 0:
+        return
+    base = b * batch_stride
+    if order == ROW:
+        view = np.lib.stride_tricks.as_strided(
+            out[base:], shape=(rows, cols), strides=(ld * out.itemsize, out.itemsize))
+    else:
+        view = np.lib.stride_tricks.as_strided(
+            out[base:], shape=(rows, cols), strides=(out.itemsize, ld * out.itemsize))
+    view[...] = mat
+
+
+def generate(p: Problem, seed: Optional[int] = None):
+    """Host buffers (flat numpy arrays) for A, B and the initial C.
+
+    Padding elements (beyond the matrix inside ld, or between batch slices)
+    are zero.  C0 is drawn even when beta == 0, so the draws of a workload do
+    not depend on its scalars.  A stride of 0 for A or B (one matrix shared
+    by the whole batch) draws that matrix once.
+    """
+    rng = np.random.default_rng(p.seed if seed is None else seed)
+    bufs = {}
+    for which, dt, sig, kind in (("a", p.in_dtype, p.sigma_a, p.a_kind),
+                                 ("b", p.in_dtype, p.sigma_b, "default"),
+                                 ("c", p.c_dtype, p.sigma_c, "default")):
+        r, c, order, ld = p.dims(which)
+        stride = {"a": p.stride_a, "b": p.stride_b, "c": p.stride_c}[which]
+        out = np.zeros(p.buffer_elems(which), np.float32 if dt == "f32" else np.uint16)
+        nb = 1 if stride == 0 else p.batch
+        for b in range(nb):
+            _store(_draw(rng, dt, r, c, sig, kind), order, ld, stride, b, out)
+        bufs[which] = out
+    return bufs["a"], bufs["b"], bufs["c"]
+
+
+def _configs():
+    cfgs = [
+        Problem("f32_256", "f32", "f32", 256, 256, 256,
+                note="fp32 SGEMM 256^3, row-major, alpha=1 beta=0, U[-1,1], seed 0"),
+        Problem("f32_4096", "f32", "f32", 4096, 4096, 4096,
+                note="fp32 SGEMM 4096^3, row-major, alpha=1 beta=0, U[-1,1]"),
+        Problem("bf16_4096", "bf16", "bf16", 4096, 4096, 4096,
+                note="bf16 HGEMM 4096^3, fp32 accumulate, bf16 out, N(0,1)"),
+        Problem("f16_4096", "f16", "f16", 4096, 4096, 4096,
+                note="fp16 HGEMM 4096^3, fp32 accumulate, fp16 out, N(0,1)"),
+        Problem("bf16_qkv", "bf16", "bf16", 4096, 12288, 4096, beta=1.0, sigma_b=0.02,
+                note="QKV projection X(4096x4096) W(4096x12288), beta=1, C0 N(0,1)"),
+        Problem("bf16_ffn_up", "bf16", "bf16", 4096, 16384, 4096, beta=1.0, sigma_b=0.02,
+                note="FFN up X(4096x4096) W1(4096x16384), beta=1, C0 N(0,1)"),
+        Problem("bf16_ffn_down", "bf16", "bf16", 4096, 4096, 16384, beta=1.0, sigma_b=0.02,
+                note="FFN down H(4096x16384) W2(16384x4096), beta=1, C0 N(0,1)"),
+        Problem("f32_edge", "f32", "f32", 4095, 4097, 1001, alpha=0.5, beta=2.0,
+                note="unaligned fp32 4095x4097x1001, alpha=0.5 beta=2, C0 U[-1,1]"),
+        Problem("bf16_edge", "bf16", "bf16", 4095, 4097, 1001, alpha=0.5, beta=2.0,
+                note="unaligned bf16 4095x4097x1001, alpha=0.5 beta=2, C0 N(0,1)"),
+        Problem("bf16_skinny", "bf16", "bf16", 16, 4096, 4096,
+                note="skinny bf16 16x4096x4096 (bandwidth-bound)"),
+        # Q (2048x128) times K^T: K is stored 2048x128 row-major, which is the
+        # 128x2048 operand B in column-major order with ldb = 128.
+        Problem("bf16_attn_qk", "bf16", "bf16", 2048, 2048, 128, order_b=COL, ldb=128,
+                batch=32, note="batched QK^T, 32 x (2048x128)(128x2048)"),
+        Problem("bf16_attn_pv", "bf16", "bf16", 2048, 128, 2048, a_kind="softmax",
+                batch=32, note="batched PV, 32 x (2048x2048)(2048x128), P softmax rows"),
+    ]
+    return {c.name: c for c in cfgs}
+
+
+CONFIGS = _configs()
+
+
+def config(name: str) -> Problem:
+    return CONFIGS[name]
