@@ -1,0 +1,174 @@
+"""ctypes binding of libgemm's C ABI (argument marshalling only).
+
+The functions here have the names and argument order of ``include/libgemm.h``
+and take device pointers as integers.  Every computation happens in the HIP
+kernels of ``libgemm.so``; if that library is missing or cannot be loaded this
+module raises instead of computing anything another way.
+
+``torch`` is imported first so that the process has one HIP runtime: torch's
+own ``libamdhip64`` carries the same soname as the system one, so the loader
+resolves libgemm's dependency to the already-loaded copy and device pointers
+and streams from torch are valid in libgemm calls.
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime libgemm links against)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm.so")
+
+ROW_MAJOR, COL_MAJOR = 0, 1
+DTYPE_SAME, DTYPE_F32 = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libgemm.so not found at {LIB_PATH}; build it with "
+                "`python -m dense_gemm_optimisation_amd.build` (or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, f32, vp, i32 = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+        common = [i64, i64, i64, f32, vp, i64, i32, vp, i64, i32, f32, vp, i64, i32]
+        lib.gemm_f32.argtypes = common + [i64, i64, i64, i64, vp]
+        lib.gemm_f32.restype = i32
+        for name in ("gemm_bf16", "gemm_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = common + [i32, i64, i64, i64, i64, vp]
+            fn.restype = i32
+        lib.gemm_status_string.argtypes = [i32]
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_abi_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().gemm_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return library().gemm_abi_version()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status, name, raise_on_error):
+    if raise_on_error and status != OK:
+        raise GemmError(status, name)
+    return status
+
+
+def gemm_f32(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+             batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None, raise_on_error=True):
+    """C <- alpha*op(A)*op(B) + beta*C in fp32; A, B, C are device addresses (int)."""
+    st = library().gemm_f32(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                            order_c, batch, stride_a, stride_b, stride_c, _stream(stream))
+    return _check(st, "gemm_f32", raise_on_error)
+
+
+def gemm_bf16(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+              c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
+              raise_on_error=True):
+    """bf16 inputs, fp32 accumulation, bf16 (DTYPE_SAME) or fp32 (DTYPE_F32) C."""
+    st = library().gemm_bf16(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                             order_c, c_dtype, batch, stride_a, stride_b, stride_c,
+                             _stream(stream))
+    return _check(st, "gemm_bf16", raise_on_error)
+
+
+def gemm_f16(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+             c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
+             raise_on_error=True):
+    """fp16 inputs, fp32 accumulation, fp16 (DTYPE_SAME) or fp32 (DTYPE_F32) C."""
+    st = library().gemm_f16(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                            order_c, c_dtype, batch, stride_a, stride_b, stride_c,
+                            _stream(stream))
+    return _check(st, "gemm_f16", raise_on_error)
+
+
+_ENTRY = {"f32": gemm_f32, "bf16": gemm_bf16, "f16": gemm_f16}
+
+
+def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+         c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
+         raise_on_error=True):
+    """Dispatch on the input type name ("f32", "bf16" or "f16")."""
+    fn = _ENTRY[in_dtype]
+    if in_dtype == "f32":
+        return fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                  batch, stride_a, stride_b, stride_c, stream, raise_on_error)
+    return fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c, c_dtype,
+              batch, stride_a, stride_b, stride_c, stream, raise_on_error)
+
+
+def _matrix_layout(t):
+    """(order, ld) of a 2-D strided view, or None if it is neither row- nor column-major."""
+    r, c = t.shape[-2], t.shape[-1]
+    sr, sc = t.stride(-2), t.stride(-1)
+    if sc == 1 or c == 1:
+        return ROW_MAJOR, max(sr if r > 1 else c, c, 1)
+    if sr == 1 or r == 1:
+        return COL_MAJOR, max(sc if c > 1 else r, r, 1)
+    return None
+
+
+_TORCH_IN = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
+def matmul(a, b, c=None, alpha=1.0, beta=0.0, out_dtype=None, stream=None):
+    """C = alpha*a@b + beta*c on torch CUDA tensors (2-D, or 3-D batched).
+
+    ``a`` (..., M, K) and ``b`` (..., K, N) may be row- or column-major views;
+    a 3-D operand with batch stride 0 (an expanded view) is shared across the
+    batch.  Returns ``c`` (allocated when None).  Only marshalling happens here.
+    """
+    if a.dtype != b.dtype or a.dtype not in _TORCH_IN:
+        raise TypeError("a and b must share one of float32, bfloat16, float16")
+    in_dtype = _TORCH_IN[a.dtype]
+    batched = a.dim() == 3 or b.dim() == 3
+    M, K = a.shape[-2], a.shape[-1]
+    N = b.shape[-1]
+    if b.shape[-2] != K:
+        raise ValueError("inner dimensions differ")
+    batch = max(a.shape[0] if a.dim() == 3 else 1, b.shape[0] if b.dim() == 3 else 1)
+    if out_dtype is None:
+        out_dtype = a.dtype if c is None else c.dtype
+    if in_dtype == "f32" and out_dtype != torch.float32:
+        raise TypeError("fp32 inputs give fp32 output")
+    if out_dtype not in (a.dtype, torch.float32):
+        raise TypeError("output must be the input type or float32")
+    if c is None:
+        shape = (batch, M, N) if batched else (M, N)
+        c = torch.empty(shape, dtype=out_dtype, device=a.device)
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs c")
+    lay = [_matrix_layout(t) for t in (a, b, c)]
+    if None in lay:
+        raise ValueError("operands must be row- or column-major (unit stride in one dimension)")
+
+    def bstride(t):
+        return t.stride(0) if t.dim() == 3 and t.shape[0] > 1 else 0
+
+    c_dtype = DTYPE_SAME if (out_dtype == a.dtype) else DTYPE_F32
+    gemm(in_dtype, M, N, K, alpha, a.data_ptr(), lay[0][1], lay[0][0], b.data_ptr(), lay[1][1],
+         lay[1][0], beta, c.data_ptr(), lay[2][1], lay[2][0], c_dtype, batch, bstride(a),
+         bstride(b), bstride(c) if batch > 1 else 0, stream)
+    return c

@@ -1,0 +1,174 @@
+// C ABI of libgemm: argument validation, canonicalisation and dispatch.
+//
+// Every check runs before any HIP call, so an invalid call has no effect.
+// A column-major C is handled by computing its transpose, which is row-major:
+// C^T = B^T A^T (the transpose identity used with the column-major BLAS call
+// in section 7.1 of "第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech).
+// The kernels therefore only ever write a row-major C.
+#include <cstdint>
+#include <cstring>
+
+#include "gemm_problem.hpp"
+#include "libgemm.h"
+
+using namespace libgemm;
+
+namespace {
+
+bool valid_order(int o) { return o == GEMM_ROW_MAJOR || o == GEMM_COL_MAJOR; }
+
+// Elements spanned by one rows x cols matrix stored with leading dimension ld.
+int64_t span(int64_t rows, int64_t cols, int order, int64_t ld) {
+    if (rows == 0 || cols == 0) return 0;
+    const int64_t outer = order == GEMM_ROW_MAJOR ? rows : cols;
+    const int64_t inner = order == GEMM_ROW_MAJOR ? cols : rows;
+    return (outer - 1) * ld + inner;
+}
+
+// Byte range [lo, hi) that a batched operand touches.
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range range_of(const void *p, int64_t span_elems, int64_t batch, int64_t stride, int esize) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    const int64_t elems = span_elems == 0 ? 0 : (batch - 1) * stride + span_elems;
+    return {lo, lo + static_cast<uintptr_t>(elems) * static_cast<uintptr_t>(esize)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+// Product of non-negative dimensions overflowing int64 (or the 2^31 grid).
+bool too_big(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
+
+gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
+                  const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
+                  float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
+                  int64_t strideB, int64_t strideC, hipStream_t stream) {
+    // ---- argument checks (no HIP call before this block is done)
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
+    if (strideA < 0 || strideB < 0 || strideC < 0) return GEMM_ERR_INVALID_ARG;
+    if (!valid_order(orderA) || !valid_order(orderB) || !valid_order(orderC))
+        return GEMM_ERR_INVALID_ARG;
+    auto min_ld = [](int order, int64_t rows, int64_t cols) {
+        const int64_t inner = order == GEMM_ROW_MAJOR ? cols : rows;
+        return inner > 1 ? inner : int64_t(1);
+    };
+    if (lda < min_ld(orderA, M, K) || ldb < min_ld(orderB, K, N) || ldc < min_ld(orderC, M, N))
+        return GEMM_ERR_INVALID_ARG;
+    if (too_big(M, N) || too_big(M * N, batch) || too_big(M, K) || too_big(K, N))
+        return GEMM_ERR_INVALID_ARG;
+
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+
+    const bool reads_ab = K > 0 && alpha != 0.0f;
+    const int ein = elem_bytes(in), eout = elem_bytes(out);
+    const int64_t span_a = span(M, K, orderA, lda);
+    const int64_t span_b = span(K, N, orderB, ldb);
+    const int64_t span_c = span(M, N, orderC, ldc);
+    if (C == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (reads_ab && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_ARG;
+    if (batch > 1 && strideC < span_c) return GEMM_ERR_INVALID_ARG;  // C slices overlap
+    if (too_big(batch - 1, strideC) || too_big(batch - 1, strideA) || too_big(batch - 1, strideB))
+        return GEMM_ERR_INVALID_ARG;
+    const Range rc = range_of(C, span_c, batch, strideC, eout);
+    if (reads_ab) {
+        if (overlap(rc, range_of(A, span_a, batch, strideA, ein)) ||
+            overlap(rc, range_of(B, span_b, batch, strideB, ein)))
+            return GEMM_ERR_INVALID_ARG;
+    }
+
+    // ---- canonical problem: row-major C
+    Problem p{};
+    p.K = K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.C = C;
+    p.ldc = ldc;
+    p.batch = batch;
+    p.sC = strideC;
+    p.in = in;
+    p.out = out;
+    if (orderC == GEMM_ROW_MAJOR) {
+        p.M = M;
+        p.N = N;
+        p.A = A;
+        p.lda = lda;
+        p.a_kmajor = orderA == GEMM_ROW_MAJOR;
+        p.sA = strideA;
+        p.B = B;
+        p.ldb = ldb;
+        p.b_kmajor = orderB == GEMM_COL_MAJOR;
+        p.sB = strideB;
+    } else {
+        // C^T (N x M, row-major) = B^T (N x K) * A^T (K x M).
+        p.M = N;
+        p.N = M;
+        p.A = B;
+        p.lda = ldb;
+        p.a_kmajor = orderB == GEMM_COL_MAJOR;
+        p.sA = strideB;
+        p.B = A;
+        p.ldb = lda;
+        p.b_kmajor = orderA == GEMM_ROW_MAJOR;
+        p.sB = strideA;
+    }
+
+    hipError_t err;
+    if (!reads_ab)
+        err = launch_scale(p, stream);
+    else if (in == Elem::F32)
+        err = launch_sgemm(p, stream);
+    else
+        err = launch_hgemm(p, stream);
+    if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+Elem out_type(Elem in, gemm_dtype_t c_dtype) { return c_dtype == GEMM_DTYPE_F32 ? Elem::F32 : in; }
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                       gemm_order_t orderA, const float *B, int64_t ldb, gemm_order_t orderB,
+                       float beta, float *C, int64_t ldc, gemm_order_t orderC, int64_t batch,
+                       int64_t strideA, int64_t strideB, int64_t strideC, hipStream_t stream) {
+    return run(Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
+               orderC, batch, strideA, strideB, strideC, stream);
+}
+
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                        int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                        gemm_order_t orderB, float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                        gemm_dtype_t c_dtype, int64_t batch, int64_t strideA, int64_t strideB,
+                        int64_t strideC, hipStream_t stream) {
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
+    return run(Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, stream);
+}
+
+gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                       int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                       gemm_order_t orderB, float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                       gemm_dtype_t c_dtype, int64_t batch, int64_t strideA, int64_t strideB,
+                       int64_t strideC, hipStream_t stream) {
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
+    return run(Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, stream);
+}
+
+const char *gemm_status_string(gemm_status_t status) {
+    switch (status) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: invalid argument";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: combination not supported";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP: kernel launch failed";
+    }
+    return "unknown gemm_status_t";
+}
+
+int gemm_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// The canonical problem the host layer hands to the kernels, and the kernel
+// launch entry points.  The host layer has already validated every argument
+// and rewritten a column-major C as the row-major C^T = B^T A^T, so every
+// kernel writes a row-major C.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace libgemm {
+
+enum class Elem : int { F32 = 0, BF16 = 1, F16 = 2 };
+
+struct Problem {
+    int64_t M, N, K;
+    float alpha, beta;
+    // a_kmajor: A(i, k) at A[i*lda + k] (K contiguous); else at A[k*lda + i].
+    const void *A;
+    int64_t lda;
+    bool a_kmajor;
+    // b_kmajor: B(k, j) at B[j*ldb + k] (K contiguous); else at B[k*ldb + j].
+    const void *B;
+    int64_t ldb;
+    bool b_kmajor;
+    // C(i, j) at C[i*ldc + j].
+    void *C;
+    int64_t ldc;
+    int64_t batch, sA, sB, sC;  // batch count and per-batch strides (elements)
+    Elem in, out;
+};
+
+// Element size in bytes.
+inline int elem_bytes(Elem e) { return e == Elem::F32 ? 4 : 2; }
+
+// True when a pointer, leading dimension and batch stride allow 16-byte
+// vector access to every row of the operand.
+inline bool vec16_ok(const void *p, int64_t ld, int64_t stride, int esize) {
+    const int64_t per = 16 / esize;
+    return (reinterpret_cast<uintptr_t>(p) % 16) == 0 && ld % per == 0 && stride % per == 0;
+}
+
+// Kernel launchers; each returns the launch status.
+hipError_t launch_sgemm(const Problem &p, hipStream_t stream);  // fp32 on the vector ALUs
+hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA
+hipError_t launch_scale(const Problem &p, hipStream_t stream);  // C <- beta*C only
+
+}  // namespace libgemm

@@ -1,0 +1,129 @@
+/*
+ * libgemm — dense general matrix multiply on AMD Instinct MI355X (gfx950).
+ *
+ *   C <- alpha * op(A) * op(B) + beta * C
+ *
+ * with op(A) an M x K matrix, op(B) a K x N matrix and C an M x N matrix.
+ * This is the GEMM of "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site),
+ * section 2.1 (C = alpha x A x B + beta x C, A M x K, B K x N, C M x N).
+ * The scalars and the argument order (dimensions, alpha, A and its leading
+ * dimension, B and its leading dimension, beta, C and its leading dimension)
+ * follow the BLAS call shown in section 7.1 of "第4章：经典算子实现 —— GEMM"
+ * (aiinfra.vidrealm.tech), with per-operand storage orders in place of the
+ * column-major-only convention of that library.
+ *
+ * Entry points
+ *   gemm_f32   fp32 inputs, fp32 output, fp32 arithmetic on the vector ALUs.
+ *   gemm_bf16  bf16 inputs, fp32 accumulation on the matrix cores, output in
+ *              bf16 (c_dtype = GEMM_DTYPE_SAME) or fp32 (GEMM_DTYPE_F32).
+ *   gemm_f16   the same for IEEE fp16 inputs.
+ *
+ * Layout
+ *   Each matrix has its own order.  Element (i, k) of A is at
+ *   A[i*lda + k] when orderA == GEMM_ROW_MAJOR and at A[k*lda + i] when
+ *   GEMM_COL_MAJOR; element (k, j) of B and (i, j) of C likewise.  A leading
+ *   dimension must be at least max(1, extent of the contiguous dimension).
+ *   Any element-aligned pointer and leading dimension are accepted; 16-byte
+ *   aligned bases with leading dimensions and strides that are multiples of
+ *   16 bytes take the fast vector path, anything else a slower exact path.
+ *
+ * Batch
+ *   `batch` independent problems; problem b uses A + b*strideA, B + b*strideB
+ *   and C + b*strideC (strides in elements, >= 0).  A stride of 0 for A or B
+ *   shares one matrix across the batch.  C slices must not overlap each
+ *   other (strideC at least the span of one C matrix when batch > 1).
+ *
+ * Scalars and semantics
+ *   alpha and beta are fp32 for every element type; the epilogue computes
+ *   alpha*acc + beta*C_old in fp32 and rounds to the output type
+ *   round-to-nearest-even.  beta == 0: C is written without being read (NaN
+ *   in C does not propagate).  alpha == 0 or K == 0: C <- beta*C and A, B are
+ *   not read.  M == 0, N == 0 or batch == 0: nothing is done.
+ *
+ * Ownership and synchronisation
+ *   The caller owns every buffer; A, B and C are device pointers valid on
+ *   `stream`.  The library allocates nothing, retains no pointer and keeps no
+ *   state between calls.  A call only enqueues work on `stream` (a hipStream_t;
+ *   0 means the null stream) and returns; results are visible after the
+ *   stream is synchronised.  C must not overlap A or B.
+ *
+ * Errors
+ *   Every argument is validated before any HIP call; an invalid call launches
+ *   nothing, changes no memory and returns a negative status.  Nothing is
+ *   printed and no exception crosses this interface.
+ *     GEMM_ERR_INVALID_ARG  negative dimension, batch or stride; leading
+ *                           dimension too small; null pointer for a matrix
+ *                           that must be read or written; order or dtype out
+ *                           of range; C slices overlapping each other; C
+ *                           overlapping A or B (checked on the address ranges
+ *                           the operands span).
+ *     GEMM_ERR_UNSUPPORTED  a combination this build does not provide.
+ *     GEMM_ERR_HIP          the kernel launch reported a HIP error.
+ */
+#ifndef LIBGEMM_H
+#define LIBGEMM_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_order_t {
+    GEMM_ROW_MAJOR = 0,
+    GEMM_COL_MAJOR = 1
+} gemm_order_t;
+
+typedef enum gemm_dtype_t {
+    GEMM_DTYPE_SAME = 0, /* output in the input type (bf16 or fp16) */
+    GEMM_DTYPE_F32 = 1   /* output in fp32 */
+} gemm_dtype_t;
+
+typedef enum gemm_status_t {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = -1,
+    GEMM_ERR_UNSUPPORTED = -2,
+    GEMM_ERR_HIP = -3
+} gemm_status_t;
+
+/* fp32 SGEMM.  A, B, C point to float; see the header comment for layout,
+ * batch, semantics and errors. */
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha,
+                       const float *A, int64_t lda, gemm_order_t orderA,
+                       const float *B, int64_t ldb, gemm_order_t orderB,
+                       float beta, float *C, int64_t ldc, gemm_order_t orderC,
+                       int64_t batch, int64_t strideA, int64_t strideB,
+                       int64_t strideC, hipStream_t stream);
+
+/* bf16 HGEMM with fp32 accumulation.  A and B hold bf16 bit patterns
+ * (uint16_t); C holds bf16 patterns (c_dtype = GEMM_DTYPE_SAME) or float
+ * (GEMM_DTYPE_F32).  The hgemm sm120 article (wingedge777.com) computes this
+ * product with fp16/bf16 operands and fp32 accumulation on matrix units. */
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
+                        const uint16_t *A, int64_t lda, gemm_order_t orderA,
+                        const uint16_t *B, int64_t ldb, gemm_order_t orderB,
+                        float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                        gemm_dtype_t c_dtype, int64_t batch, int64_t strideA,
+                        int64_t strideB, int64_t strideC, hipStream_t stream);
+
+/* IEEE fp16 HGEMM with fp32 accumulation; as gemm_bf16. */
+gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha,
+                       const uint16_t *A, int64_t lda, gemm_order_t orderA,
+                       const uint16_t *B, int64_t ldb, gemm_order_t orderB,
+                       float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                       gemm_dtype_t c_dtype, int64_t batch, int64_t strideA,
+                       int64_t strideB, int64_t strideC, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *gemm_status_string(gemm_status_t status);
+
+/* Version of this interface; bumped on any incompatible change. */
+int gemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_H */

@@ -1,0 +1,131 @@
+"""The C ABI on the CPU: every declared symbol is exported, and argument
+validation returns its status codes before any HIP call (so none of these
+tests needs a GPU: no call here reaches a kernel launch)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from dense_gemm_optimisation_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from dense_gemm_optimisation_amd import build
+        build.build()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_f16", "gemm_f32",
+                                    "gemm_status_string"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib.library(), name) is not None
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "libgemm.h"\nint f(void){return gemm_abi_version();}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-c",
+                    str(src), "-o", str(tmp_path / "use.o")], check=True)
+
+
+def test_status_strings(lib):
+    assert lib.status_string(0) == "GEMM_OK"
+    for code in (-1, -2, -3):
+        assert lib.status_string(code).startswith("GEMM_ERR_")
+    assert lib.status_string(7) == "unknown gemm_status_t"
+    assert lib.abi_version() == 1
+
+
+P = 0x10000  # a fake, never-dereferenced device address
+
+
+def call(lib, fn="f32", M=8, N=8, K=8, alpha=1.0, A=P, lda=8, oa=0, B=P * 3, ldb=8, ob=0,
+         beta=0.0, C=P * 5, ldc=8, oc=0, c_dtype=0, batch=1, sa=0, sb=0, sc=0):
+    if fn == "f32":
+        return lib.gemm_f32(M, N, K, alpha, A, lda, oa, B, ldb, ob, beta, C, ldc, oc, batch, sa,
+                            sb, sc, 0, raise_on_error=False)
+    f = lib.gemm_bf16 if fn == "bf16" else lib.gemm_f16
+    return f(M, N, K, alpha, A, lda, oa, B, ldb, ob, beta, C, ldc, oc, c_dtype, batch, sa, sb,
+             sc, 0, raise_on_error=False)
+
+
+INVALID = {
+    "negative M": dict(M=-1),
+    "negative N": dict(N=-1),
+    "negative K": dict(K=-2),
+    "negative batch": dict(batch=-1),
+    "negative stride": dict(sa=-1),
+    "order A out of range": dict(oa=2),
+    "order B out of range": dict(ob=-1),
+    "order C out of range": dict(oc=5),
+    "lda < K (row-major A)": dict(lda=7),
+    "lda < M (col-major A)": dict(oa=1, M=9, lda=8),
+    "ldb < N (row-major B)": dict(ldb=7),
+    "ldb < K (col-major B)": dict(ob=1, ldb=7),
+    "ldc < N": dict(ldc=7),
+    "ldc < M (col-major C)": dict(oc=1, M=12, lda=8, ldc=8),
+    "ld zero": dict(M=1, K=0, lda=0),
+    "null A": dict(A=0),
+    "null B": dict(B=0),
+    "null C": dict(C=0),
+    "C overlaps A": dict(C=P + 4 * 10),
+    "C overlaps B": dict(C=P * 3 + 4 * 63),
+    "C slices overlap": dict(batch=2, sc=63),
+    "C slices coincide": dict(batch=3, sc=0),
+}
+
+
+@pytest.mark.parametrize("fn", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("case", sorted(INVALID))
+def test_invalid_arguments(lib, fn, case):
+    kw = dict(INVALID[case])
+    if fn != "f32" and case == "C overlaps A":
+        kw["C"] = P + 2 * 10
+    if fn != "f32" and case == "C overlaps B":
+        kw["C"] = P * 3 + 2 * 63
+    assert call(lib, fn, **kw) == lib.ERR_INVALID_ARG, case
+
+
+@pytest.mark.parametrize("fn", ["bf16", "f16"])
+def test_bad_c_dtype(lib, fn):
+    assert call(lib, fn, c_dtype=2) == lib.ERR_INVALID_ARG
+    assert call(lib, fn, c_dtype=-1) == lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("kw", [dict(M=0), dict(N=0), dict(batch=0),
+                                dict(M=0, A=0, B=0, C=0), dict(batch=0, A=0, B=0, C=0)])
+def test_empty_problems_return_ok_without_work(lib, fn, kw):
+    assert call(lib, fn, **kw) == lib.OK
+
+
+def test_adjacent_buffers_are_not_overlap(lib):
+    # C starting exactly where A ends is fine; validation must not flag it.
+    # (M == 0 keeps the call from launching anything.)
+    assert call(lib, "f32", M=0, C=P + 4 * 64) == lib.OK
+
+
+def test_raises_on_error(lib):
+    with pytest.raises(lib.GemmError) as e:
+        lib.gemm_f32(-1, 1, 1, 1.0, P, 1, 0, P, 1, 0, 0.0, P, 1, 0)
+    assert e.value.status == lib.ERR_INVALID_ARG

@@ -1,0 +1,212 @@
+"""GPU parity: libgemm's HIP kernels against the CPU oracle, element by element.
+
+Small and medium problems compare every element; full-size workloads compare
+whole rows and columns, tile-boundary elements and random samples.  Every run
+also checks the canary guard bands and ld/batch padding around C and that A
+and B are unchanged (see parity.py for the tolerances).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import COL, ROW, Problem
+
+from parity import log, run
+
+pytestmark = pytest.mark.gpu
+
+DT = ["f32", "bf16", "f16"]
+
+
+def P(name, dt, M, N, K, c_dtype=None, **kw):
+    return Problem(name, dt, c_dtype or dt, M, N, K, **kw)
+
+
+def check(p, **kw):
+    res, out = run(p, **kw)
+    assert res.ok, res.why
+    return res, out
+
+
+# ------------------------------------------------------------------ shapes and edges
+
+SHAPES = [(1, 1, 1), (1, 7, 3), (2, 3, 5), (7, 9, 13), (31, 33, 17), (64, 64, 64),
+          (127, 129, 65), (128, 128, 128), (129, 127, 200), (255, 257, 63), (256, 256, 256),
+          (300, 290, 130), (513, 130, 77), (70, 600, 33), (33, 70, 1000)]
+
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(dt, shape):
+    M, N, K = shape
+    check(P(f"shape-{dt}", dt, M, N, K, alpha=1.0, beta=0.0), seed=M * 7 + N * 3 + K)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (37, 45, 29), (256, 256, 64), (300, 290, 130)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp32_output(dt, shape):
+    M, N, K = shape
+    check(P(f"f32out-{dt}", dt, M, N, K, c_dtype="f32", alpha=0.75, beta=-1.5), seed=5)
+
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("orders", [(a, b, c) for a in (ROW, COL) for b in (ROW, COL)
+                                    for c in (ROW, COL)], ids=lambda o: "%d%d%d" % o)
+def test_layouts_with_padded_ld(dt, orders):
+    oa, ob, oc = orders
+    M, N, K = 261, 199, 150
+    lda = (K if oa == ROW else M) + 13
+    ldb = (N if ob == ROW else K) + 8
+    ldc = (N if oc == ROW else M) + 5
+    check(P(f"layout-{dt}", dt, M, N, K, alpha=1.25, beta=0.5, order_a=oa, order_b=ob,
+            order_c=oc, lda=lda, ldb=ldb, ldc=ldc), seed=11)
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_misaligned_bases_and_odd_ld(dt):
+    p = P(f"misaligned-{dt}", dt, 190, 211, 97, alpha=1.0, beta=1.0, lda=99, ldb=213, ldc=215)
+    check(p, seed=12, base_offset=(1, 3, 1))
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_aligned_ld_but_ragged_k(dt):
+    # 16-byte aligned rows, but K not a multiple of the vector width or tile
+    check(P(f"raggedk-{dt}", dt, 300, 260, 1001, lda=1008, ldb=264, ldc=264), seed=13)
+
+
+# ------------------------------------------------------------------ alpha / beta semantics
+
+@pytest.mark.parametrize("dt", DT)
+def test_beta_zero_ignores_nan_in_c(dt):
+    nan = np.float32(np.nan) if dt == "f32" else (0x7FC0 if dt == "bf16" else 0x7E00)
+    res, _ = check(P(f"beta0nan-{dt}", dt, 140, 150, 70, alpha=1.0, beta=0.0), seed=14,
+                   c_init=nan)
+
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("case", ["alpha0", "k0", "alpha0_beta0"])
+def test_scale_only_paths(dt, case):
+    kw = dict(alpha=0.0, beta=-2.0) if case == "alpha0" else \
+        dict(alpha=1.5, beta=0.5) if case == "k0" else dict(alpha=0.0, beta=0.0)
+    K = 0 if case == "k0" else 33
+    p = P(f"{case}-{dt}", dt, 77, 65, K, **kw)
+    if case == "alpha0_beta0":
+        nan = np.float32(np.nan) if dt == "f32" else (0x7FC0 if dt == "bf16" else 0x7E00)
+        check(p, seed=15, c_init=nan)
+    else:
+        check(p, seed=15)
+
+
+# ------------------------------------------------------------------ exact results
+
+def _int_host(p, rng, lo=-8, hi=8):
+    def mk(n, dt):
+        v = rng.integers(lo, hi + 1, n).astype(np.float32)
+        return v if dt == "f32" else workloads.to_16bit(v, dt)
+    return (mk(p.buffer_elems("a"), p.in_dtype), mk(p.buffer_elems("b"), p.in_dtype),
+            mk(p.buffer_elems("c"), p.c_dtype))
+
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("shape", [(256, 256, 1001), (300, 517, 260), (64, 4096, 512)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_integer_inputs_bit_exact(dt, shape):
+    # every product and partial sum of small integers is exact in fp32, so
+    # the result must equal the oracle's correctly rounded value bit for bit
+    M, N, K = shape
+    p = P(f"int-{dt}", dt, M, N, K, alpha=2.0, beta=1.0)
+    host = _int_host(p, np.random.default_rng(16))
+    res, out = check(p, host=host)
+    assert res.max_err == 0.0 and res.max_ulp == 0
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_identity_and_permutation_bit_exact(dt):
+    M, N = 300, 257
+    rng = np.random.default_rng(17)
+    perm = rng.permutation(M)
+    Pm = np.zeros((M, M), np.float32)
+    Pm[np.arange(M), perm] = 1.0
+    for name, a in (("identity", np.eye(M, dtype=np.float32)), ("permutation", Pm)):
+        p = P(f"{name}-{dt}", dt, M, N, M)
+        a_st = a.ravel() if dt == "f32" else workloads.to_16bit(a.ravel(), dt)
+        _, b, c = workloads.generate(p, seed=18)
+        res, out = check(p, host=(a_st, b, c))
+        if dt != "f32":
+            assert res.max_ulp == 0
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_all_ones_closed_form(dt):
+    M, N, K = 200, 300, 700
+    p = P(f"ones-{dt}", dt, M, N, K, alpha=0.5, beta=-1.0)
+    one = np.ones(1, np.float32)
+    mk = (lambda n: np.ones(n, np.float32)) if dt == "f32" else \
+        (lambda n: workloads.to_16bit(np.ones(n, np.float32), dt))
+    c0 = np.random.default_rng(19).integers(-4, 5, M * N).astype(np.float32)
+    c0s = c0 if dt == "f32" else workloads.to_16bit(c0, dt)
+    res, out = check(p, host=(mk(M * K), mk(K * N), c0s))
+    assert res.max_err == 0.0 and res.max_ulp == 0
+    del one
+
+
+# ------------------------------------------------------------------ batches
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("bcast", ["none", "a", "b"])
+def test_batched_strided(dt, bcast):
+    M, N, K, batch = 130, 260, 90, 3
+    kw = {}
+    if bcast == "a":
+        kw["stride_a"] = 0
+    if bcast == "b":
+        kw["stride_b"] = 0
+    p = P(f"batch-{bcast}-{dt}", dt, M, N, K, batch=batch, beta=1.0, stride_c=M * N + 17, **kw)
+    res, out = check(p, seed=20)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_batch_slice_equals_single_call(dt):
+    M, N, K, batch = 257, 129, 140, 3
+    pb = P(f"batch-vs-single-{dt}", dt, M, N, K, batch=batch)
+    a, b, c = workloads.generate(pb, seed=21)
+    _, out_b = check(pb, host=(a, b, c))
+    from parity import GUARD
+    for i in range(batch):
+        ps = P(f"single{i}-{dt}", dt, M, N, K)
+        sl = lambda x, s, n: x[i * s:i * s + n]
+        host = (sl(a, pb.stride_a, M * K), sl(b, pb.stride_b, K * N), sl(c, pb.stride_c, M * N))
+        _, out_s = check(ps, host=host)
+        assert np.array_equal(out_s[GUARD:GUARD + M * N],
+                              out_b[GUARD + i * pb.stride_c:GUARD + i * pb.stride_c + M * N])
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_repeat_runs_bit_identical(dt):
+    check(P(f"determinism-{dt}", dt, 520, 700, 300, beta=0.5), seed=22, repeat=3)
+
+
+# ------------------------------------------------------------------ the workloads
+
+SMALL_CONFIGS = ["f32_256"]
+FULL_CONFIGS = ["f32_4096", "bf16_4096", "f16_4096", "f32_edge", "bf16_edge", "bf16_skinny",
+                "bf16_attn_qk", "bf16_attn_pv", "bf16_qkv", "bf16_ffn_up", "bf16_ffn_down"]
+
+
+@pytest.mark.parametrize("name", SMALL_CONFIGS)
+def test_small_config_every_element(name):
+    check(workloads.config(name))
+
+
+@pytest.mark.parametrize("name", FULL_CONFIGS)
+def test_full_config_sampled(name):
+    check(workloads.config(name), sample="auto")
+
+
+@pytest.mark.parametrize("name", ["bf16_4096", "bf16_edge", "bf16_attn_pv"])
+def test_full_config_fp32_output(name):
+    p = workloads.config(name)
+    check(p.with_(name=p.name + "-f32out", c_dtype="f32"), sample="auto")
