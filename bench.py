@@ -1,0 +1,211 @@
+"""Throughput of libgemm on one MI355X: TFLOPS = 2*M*N*K / t.
+
+A step is one pass of the whole path over the headline workload: one fp32
+SGEMM, one bf16 HGEMM and one fp16 HGEMM, each 4096 x 4096 x 4096, row-major,
+alpha = 1, beta = 0 (the square 4096 problem the pages benchmark; inputs
+U[-1, 1] for fp32 and N(0, 1) rounded to bf16/fp16, generated on the host and
+resident in HBM before timing starts).  `value` is the step's whole-job
+throughput (three GEMMs' FLOPs over the step's wall time); `per_kernel` gives
+each GEMM's own TFLOPS and fraction of MI355X's dense peak for its dtype,
+from HIP events recorded on the stream the kernels run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--no-context]
+--workload runs a single named workload (see workloads.CONFIGS) instead of
+the headline step, for profiling.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense, published
+HBM_GBS = 8000.0
+
+HEADLINE = ["f32_4096", "bf16_4096", "f16_4096"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_buffers(p, torch):
+    import workloads
+    a, b, c = workloads.generate(p)
+    view = np.float32 if p.in_dtype == "f32" else np.int16
+    cview = np.float32 if p.c_dtype == "f32" else np.int16
+    return (torch.from_numpy(a.view(view)).to("cuda"), torch.from_numpy(b.view(view)).to("cuda"),
+            torch.from_numpy(c.view(cview)).to("cuda"))
+
+
+def make_launch(p, bufs, stream):
+    from dense_gemm_optimisation_amd import binding
+    da, db, dc = bufs
+    c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
+    args = (p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a, db.data_ptr(),
+            p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch, p.stride_a,
+            p.stride_b, p.stride_c, stream.cuda_stream)
+
+    def launch():
+        binding.gemm(*args)
+    return launch
+
+
+def cpu_baseline(problems, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    import workloads
+    total_flop, total_t, parts = 0.0, 0.0, []
+    per = budget_s / len(problems)
+    for p in problems:
+        a, b, c = workloads.generate(p)
+        rows = 1
+        while True:  # calibrate on one row, then size the sample to the budget
+            idx = np.stack([np.zeros(rows * p.N, np.int64), np.repeat(np.arange(rows), p.N),
+                            np.tile(np.arange(p.N), rows)], 1)
+            t0 = time.perf_counter()
+            oracle.gemm_at(p.in_dtype, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda, p.order_a, b,
+                           p.ldb, p.order_b, p.beta, c, p.ldc, p.order_c, idx)
+            dt = time.perf_counter() - t0
+            if dt >= 0.5 * per or rows >= p.M:
+                break
+            rows = min(p.M, max(rows * 2, int(rows * per / max(dt, 1e-3))))
+        flop = 2.0 * rows * p.N * p.K
+        total_flop += flop
+        total_t += dt
+        parts.append(f"{p.name}: first {rows} rows x {p.N} cols ({dt:.1f} s)")
+    return {"value": total_flop / total_t / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "; ".join(parts) +
+            " -- double-accumulating triple loop, timed with perf_counter"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-context", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the GEMM path has no multi-GPU "
+              "sharding (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from dense_gemm_optimisation_amd import binding
+    binding.library()  # fails loudly if libgemm.so is missing
+    torch.cuda.set_device(0)
+    names = HEADLINE if args.workload == "headline" else [args.workload]
+    problems = [workloads.config(n) for n in names]
+    stream = torch.cuda.Stream()  # default priority
+    launches = []
+    with torch.cuda.stream(stream):
+        for p in problems:
+            log(f"[bench] preparing {p.name}: {p.note}")
+            bufs = device_buffers(p, torch)
+            launches.append((p, bufs, make_launch(p, bufs, stream)))
+    torch.cuda.synchronize()
+
+    # warmup
+    for _ in range(args.warmup):
+        for _, _, fn in launches:
+            fn()
+    torch.cuda.synchronize()
+
+    # timed region: every launch bracketed by events on the kernels' stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for k, (_, _, fn) in enumerate(launches):
+            ev[s][k][0].record(stream)
+            fn()
+            ev[s][k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel = {}
+    flops_step = 0
+    for k, (p, _, _) in enumerate(launches):
+        ms = np.array([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)])
+        tfl = p.flops / (ms.mean() * 1e-3) / 1e12
+        flops_step += p.flops
+        alg_bytes = (p.M * p.K + p.K * p.N) * (4 if p.in_dtype == "f32" else 2) * p.batch + \
+            p.M * p.N * (4 if p.c_dtype == "f32" else 2) * p.batch * (2 if p.beta else 1)
+        per_kernel[p.name] = {
+            "dtype": p.in_dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+            "mean_us": round(float(ms.mean()) * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
+            "min_us": round(float(ms.min()) * 1e3, 2), "tflops": round(tfl, 2),
+            "tflops_best": round(p.flops / (ms.min() * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(tfl / PEAK_TFLOPS[p.in_dtype], 4),
+            "alg_gbs": round(alg_bytes / (ms.mean() * 1e-3) / 1e9, 1)}
+    ms_step = wall / args.steps * 1e3
+    value = flops_step / (wall / args.steps) / 1e12
+
+    def roof(name):
+        k = per_kernel[name]
+        p = workloads.config(name)
+        if p.in_dtype == "f32":
+            return {"kernel": f"sgemm_valu {name}", "bound": "alu", "achieved": k["tflops"],
+                    "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                    "frac": round(k["tflops"] / PEAK_TFLOPS["f32"], 4),
+                    "traffic": None}
+        return {"kernel": f"hgemm_mfma {name}", "bound": "mfma", "achieved": k["tflops"],
+                "peak": PEAK_TFLOPS[p.in_dtype], "unit": "TFLOP/s",
+                "frac": round(k["tflops"] / PEAK_TFLOPS[p.in_dtype], 4), "traffic": None}
+
+    dominant = max(per_kernel, key=lambda n: per_kernel[n]["mean_us"])
+    out = {
+        "metric": "TFLOPS (2MNK/t) at 4096^3 fp32 and bf16; % of MI355X dense peak per dtype",
+        "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "+".join(p.in_dtype for p in problems),
+        "data": "synthetic",
+        "config": {"workload": " + ".join(f"{p.name} ({p.note})" for p in problems),
+                   "global_batch": 1, "parallelism": "none (1 GPU)"},
+        "per_kernel": per_kernel,
+        "roofline": roof(dominant),
+        "roofline_all": [roof(n) for n in per_kernel],
+    }
+    if not args.no_context and args.workload == "headline":
+        out["context_torch_matmul"] = torch_context(problems, stream, torch)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(problems[:2], args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def torch_context(problems, stream, torch):
+    """torch.matmul (the vendor BLAS) on the same shapes: context only, not the path."""
+    res = {}
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    with torch.cuda.stream(stream):
+        for p in problems:
+            a = torch.randn(p.M, p.K, device="cuda").to(dt[p.in_dtype])
+            b = torch.randn(p.K, p.N, device="cuda").to(dt[p.in_dtype])
+            for _ in range(3):
+                torch.matmul(a, b)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                torch.matmul(a, b)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            res[p.name] = round(p.flops / (ms * 1e-3) / 1e12, 2)
+    return {"unit": "TFLOPS", "note": "torch.matmul on identical shapes; context only", **res}
+
+
+if __name__ == "__main__":
+    main()
