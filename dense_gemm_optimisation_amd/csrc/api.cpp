@@ -6,6 +6,7 @@
 // in section 7.1 of "第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech).
 // The kernels therefore only ever write a row-major C.
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "gemm_problem.hpp"
@@ -40,6 +41,13 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.h
 
 // Product of non-negative dimensions overflowing int64 (or the 2^31 grid).
 bool too_big(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
+
+// LIBGEMM_FORCE_GENERAL=1 routes every bf16/fp16 call to the general
+// kernel (used to test the two matrix-core kernels against each other).
+bool force_general() {
+    const char *v = std::getenv("LIBGEMM_FORCE_GENERAL");
+    return v != nullptr && v[0] == '1';
+}
 
 gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
@@ -119,6 +127,8 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
         err = launch_scale(p, stream);
     else if (in == Elem::F32)
         err = launch_sgemm(p, stream);
+    else if (hgemm_dma_eligible(p) && !force_general())
+        err = launch_hgemm_dma(p, stream);
     else
         err = launch_hgemm(p, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;

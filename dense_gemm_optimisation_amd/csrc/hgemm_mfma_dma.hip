@@ -1,0 +1,518 @@
+// bf16 / fp16 GEMM on the CDNA4 matrix cores, fast path for aligned operands.
+//
+// Same block tile -> wave tile -> matrix instruction hierarchy as the general
+// kernel ("GPU GEMM 优化完全拆解（三）", pinghaoyang.com.cn, section
+// "从 kernel 到库"), with the data movement rebuilt around three gfx950
+// features:
+//
+//   * direct global -> LDS loads (buffer_load_dwordx4 ... lds): every lane
+//     moves 16 bytes into LDS at M0 + 16*lane without passing through
+//     registers, so a wave fills 1 KiB of LDS per instruction.  This is the
+//     role cp.async / TMA play on the pages' hardware (section 9.2 of
+//     "CUDA GEMM 矩阵乘法优化指南", blog.zhenwei.site; section 3 of the hgemm
+//     sm120 article, wingedge777.com).  The buffer's range check turns loads
+//     outside the matrix into zeros, which handles ragged M, N and K tiles;
+//   * LDS transpose reads (ds_read_b64_tr_b16): within each group of 16
+//     lanes, lane j receives element j%4 of the 8-byte piece that lane
+//     4e + j/4 addressed, as its element e.  If lane i of the group addresses
+//     row i/4, columns 4(i%4)..4(i%4)+3 of a row-major 4 x 16 block, lane j
+//     receives column j.  An operand stored contiguous along M or N (row-major
+//     B, column-major A) is therefore copied into LDS unchanged and read in
+//     the K-contiguous form the matrix instruction wants (the role ldmatrix
+//     .trans plays in section "ldmatrix" of the pinghaoyang.com.cn page);
+//   * v_mfma_f32_32x32x16_{bf16,f16} with the operands swapped (C^T blocks =
+//     B^T A^T): each lane's accumulators then hold four consecutive columns
+//     of one row of C, which the epilogue stores as one 8- or 16-byte vector.
+//
+// Pipeline: two LDS stages of BK = 64 (2 x 64 KiB).  While the matrix
+// instructions of stage s run, stage s + 1 is landing in the other buffer;
+// operand fragments are double-buffered in registers, so the reads for k-step
+// kk + 1 are in flight during the matrix instructions of k-step kk, and the
+// reads of the next stage's first k-step are issued before the current
+// stage's last matrix instructions (the two buffering scopes, shared memory
+// and registers, of section 3.3 of the hgemm sm120 article).  One barrier per
+// stage separates the last reads of a buffer from the loads that refill it.
+//
+// LDS layouts (both XOR-swizzled in 16-byte chunks; the swizzle is applied by
+// choosing which global chunk each lane fetches, because the direct loads
+// place lanes linearly):
+//   K-contiguous operand: [256 rows][64 k], 128 B per row, chunk c of row r
+//     at c ^ ((r ^ (r >> 3)) & 7): 16 consecutive rows read at one logical
+//     chunk hit distinct banks.
+//   M/N-contiguous operand: [64 k][256 cols], 512 B per row, chunk c of row r
+//     at c ^ 4*t(r), t(r) = (r & 7) ^ 4*((r >> 3) & 1): the eight rows one
+//     transpose read touches fall in eight different 64-byte bank groups.
+#include "gemm_problem.hpp"
+#include "tile_schedule.hpp"
+
+namespace libgemm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+#define LDS __attribute__((address_space(3)))
+
+constexpr int BM = 256, BN = 256;       // block tile (rows of A and columns of B)
+constexpr uint32_t OOB = 0x80000000u;    // voffset beyond any accepted buffer size
+constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2;
+
+struct DmaArgs {
+    int64_t M, N, K;
+    float alpha, beta;
+    const uint16_t *A;
+    const uint16_t *B;
+    void *C;
+    int64_t lda, ldb, ldc;
+    int64_t sA, sB, sC;
+    TileGrid grid;
+    int vec_c;
+};
+
+struct BF16 {};
+struct F16 {};
+
+template <class T>
+__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ inline f32x16 mfma32<BF16>(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ inline f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Values the compiler cannot prove wave-uniform (they come out of 64-bit
+// divisions done on the vector ALU) are moved to scalar registers, so that
+// buffer descriptors and M0 are built once per wave instead of in a loop
+// over distinct lane values.
+__device__ inline int64_t uniform(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(uint64_t(x) >> 32));
+    return static_cast<int64_t>((uint64_t(hi) << 32) | lo);
+}
+template <class T>
+__device__ inline T *uniform_ptr(T *p) {
+    return reinterpret_cast<T *>(uniform(reinterpret_cast<int64_t>(p)));
+}
+
+// Swizzle of a K-contiguous panel row (CH 16-byte chunks per row): a
+// permutation of [0, CH) chosen so that 16 consecutive rows read at one
+// logical chunk fall on 16 distinct 16-byte bank groups of a 256-byte wide
+// LDS (and 8 consecutive rows on 8 distinct groups of a 128-byte one).
+template <int CH>
+__device__ inline int swz_k(int row) {
+    if (CH == 8) return (row ^ (row >> 3)) & 7;
+    return ((row >> 1) ^ (row >> 2)) & 3;  // CH == 4
+}
+// Swizzle of an M/N-contiguous panel row (32 chunks of 16 bytes): XOR of
+// chunk bits 2..4 with t(r) = (r & 7) ^ 4*((r >> 3) & 1), so the eight rows
+// one transpose read touches use eight different 64-byte bank groups.
+__device__ inline int swz_mn(int krow) { return ((krow & 7) ^ (((krow >> 3) & 1) << 2)) << 2; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from the buffer `rs` at
+// byte offset `voffset` into LDS at `lds` + 16 * lane.  Issued as inline
+// assembly on purpose: the compiler does not then treat the load as a
+// pending LDS write, so it does not wait for every outstanding prefetch
+// before each LDS read (the prefetches target other buffers).  Visibility is
+// ensured explicitly: s_waitcnt vmcnt for the stage being consumed, then a
+// workgroup barrier.  A descriptor and LDS address that are not
+// wave-uniform would be wrong here, so both come from scalar values.
+__device__ inline void direct_load16(u32x4 rs, uint32_t lds, uint32_t voffset) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"(voffset), "s"(rs)
+        : "memory", "m0");
+}
+
+// One operand panel of the tile (256 rows of A or 256 columns of B, BK deep):
+// where each lane fetches from, and how the wave reads fragments back.
+template <bool KMAJOR, int WAVES, int BK>
+struct Operand {
+    static constexpr int PANEL = 256 * BK * 2;        // bytes
+    static constexpr int BLOCKS = PANEL / 1024;       // 1 KiB direct loads per panel
+    static constexpr int PER_WAVE = BLOCKS / WAVES;   // direct loads per wave per stage
+    static constexpr int CH = BK / 8;                 // chunks per K-contiguous row
+    static constexpr int ROWS_PER_BLOCK = 1024 / (2 * BK);
+    static_assert(PER_WAVE >= 1 && BLOCKS % WAVES == 0, "panel split over waves");
+    uint32_t voff[PER_WAVE];  // byte offset of this lane's chunk, stage 0
+    int kl[PER_WAVE];         // k index (within a stage) of this lane's chunk
+    const uint16_t *base;
+    int64_t bytes;            // extent of the operand slice in bytes
+    int64_t step;             // bytes the base advances per stage
+
+    // X(r, k): KMAJOR -> X[r*ld + k], else X[k*ld + r]; rows [r0, r0+256) of R.
+    __device__ void init(const uint16_t *x, int64_t ld, int64_t R, int64_t r0, int64_t span,
+                         int wave, int lane) {
+        base = x;
+        bytes = span * 2;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int blk = wave * PER_WAVE + i;
+            if (KMAJOR) {
+                const int row = blk * ROWS_PER_BLOCK + lane / CH;
+                const int c = (lane % CH) ^ swz_k<CH>(row);
+                kl[i] = c * 8;
+                const int64_t gr = r0 + row;
+                voff[i] = gr < R ? uint32_t((gr * ld + c * 8) * 2) : OOB;
+            } else {
+                const int krow = blk * 2 + (lane >> 5);
+                const int c = (lane & 31) ^ swz_mn(krow);
+                kl[i] = krow;
+                const int64_t gc = r0 + c * 8;
+                voff[i] = gc < R ? uint32_t((krow * ld + gc) * 2) : OOB;
+            }
+        }
+        step = KMAJOR ? int64_t(BK) * 2 : int64_t(BK) * ld * 2;
+    }
+
+    // Direct loads of stage `stage` (k from stage*BK) into the LDS panel at dst.
+    __device__ void issue(LDS char *dst, int64_t stage, int64_t K, int wave) const {
+        const int64_t off = uniform(stage * step);
+        const uint64_t addr = static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(base) + off));
+        u32x4 rs;  // raw buffer descriptor: base, stride 0, size in bytes, 32-bit format
+        rs[0] = static_cast<uint32_t>(addr);
+        rs[1] = static_cast<uint32_t>(addr >> 32) & 0xffffu;
+        rs[2] = static_cast<uint32_t>(uniform(bytes - off));
+        rs[3] = 0x00020000u;
+        const int64_t kleft = K - stage * BK;
+        const bool tail = kleft < BK;
+        const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const uint32_t v = (tail && kl[i] >= kleft) ? OOB : voff[i];
+            direct_load16(rs, lds0 + (wave * PER_WAVE + i) * 1024, v);
+        }
+    }
+
+    // Fragment of 32 rows (from row `row0` of the panel) for k16 step kk.
+    __device__ u32x4 frag(const LDS char *panel, int row0, int kk, int lane) const {
+        if (KMAJOR) {
+            const int row = row0 + (lane & 31);
+            const int c = kk * 2 + (lane >> 5);
+            return *reinterpret_cast<const LDS u32x4 *>(panel + row * (2 * BK) +
+                                                        ((c ^ swz_k<CH>(row)) << 4));
+        } else {
+            const int g = lane >> 5, h = (lane >> 4) & 1, ii = lane & 15;
+            const int col = row0 + h * 16 + 4 * (ii & 3);
+            u32x4 out;
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const int krow = kk * 16 + g * 8 + e2 * 4 + (ii >> 2);
+                const int c = (col >> 3) ^ swz_mn(krow);
+                const LDS s16x4 *p = reinterpret_cast<const LDS s16x4 *>(
+                    panel + krow * 512 + (c << 4) + ((col & 7) << 1));
+                const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                              const_cast<LDS s16x4 *>(p)));
+                out[2 * e2] = v[0];
+                out[2 * e2 + 1] = v[1];
+            }
+            return out;
+        }
+    }
+};
+
+template <int OUT>
+__device__ inline void store4(void *C, int64_t off, f32x4 v, float beta, bool vec, int nvalid) {
+    if (OUT == OUT_F32) {
+        float *p = static_cast<float *>(C) + off;
+        if (vec && nvalid == 4) {
+            if (beta != 0.0f) {
+                const f32x4 o = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, o[e], v[e]);
+            }
+            *reinterpret_cast<f32x4 *>(p) = v;
+        } else {
+            for (int e = 0; e < nvalid; ++e) p[e] = beta != 0.0f ? __builtin_fmaf(beta, p[e], v[e]) : v[e];
+        }
+    } else {
+        uint16_t *p = static_cast<uint16_t *>(C) + off;
+        auto dec = [](uint16_t b) {
+            return OUT == OUT_BF16 ? __builtin_bit_cast(float, uint32_t(b) << 16)
+                                   : static_cast<float>(__builtin_bit_cast(_Float16, b));
+        };
+        auto enc = [](float x) {
+            return OUT == OUT_BF16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(x))
+                                   : __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+        };
+        if (vec && nvalid == 4) {
+            if (beta != 0.0f) {
+                const u16x4 o = *reinterpret_cast<const u16x4 *>(p);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, dec(o[e]), v[e]);
+            }
+            u16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = enc(v[e]);
+            *reinterpret_cast<u16x4 *>(p) = w;
+        } else {
+            for (int e = 0; e < nvalid; ++e)
+                p[e] = enc(beta != 0.0f ? __builtin_fmaf(beta, dec(p[e]), v[e]) : v[e]);
+        }
+    }
+}
+
+// Waits until at most `n` stages of direct loads (each `per` instructions)
+// remain in flight; s_waitcnt takes an immediate, so the few possible
+// counts are enumerated.
+template <int PER, int STAGES>
+__device__ inline void wait_stages(int n) {
+    if (STAGES > 3 && n >= 3) { wait_vmcnt<(STAGES > 3 ? 3 : 0) * PER>(); return; }
+    if (STAGES > 2 && n >= 2) { wait_vmcnt<(STAGES > 2 ? 2 : 0) * PER>(); return; }
+    if (n >= 1) { wait_vmcnt<PER>(); return; }
+    wait_vmcnt<0>();
+}
+
+// Scheduling hint for one k step: alternate one matrix instruction with one
+// LDS read (the next step's fragments), then the remaining matrix
+// instructions, so the reads' latency hides under the matrix work instead
+// of being issued in a burst right before it is needed.
+template <int NREAD, int NMFMA>
+__device__ inline void interleave_reads() {
+    // two reads after each of the first matrix instructions, so every read
+    // is issued in the first half of the step
+    constexpr int PAIRS = (NREAD + 1) / 2 < NMFMA ? (NREAD + 1) / 2 : NMFMA;
+#pragma unroll
+    for (int i = 0; i < PAIRS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    }
+    if (NMFMA > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - PAIRS, 0);
+}
+
+template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, int WAVES_M, int WAVES_N, int BK,
+          int STAGES>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(DmaArgs p) {
+    constexpr int WAVES = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int KK = BK / 16;  // matrix-instruction k steps per stage
+    // LDS read instructions per k step: one per K-contiguous fragment, two
+    // transpose reads per M/N-contiguous one
+    constexpr int NREAD = FM * (A_KMAJOR ? 1 : 2) + FN * (B_KMAJOR ? 1 : 2);
+    using OpA = Operand<A_KMAJOR, WAVES, BK>;
+    using OpB = Operand<B_KMAJOR, WAVES, BK>;
+    constexpr int PANEL = OpA::PANEL;
+    constexpr int STAGE = 2 * PANEL;
+    constexpr int PER_STAGE = OpA::PER_WAVE + OpB::PER_WAVE;  // direct loads per wave per stage
+    static_assert(STAGES >= 2 && STAGES <= 5 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+    TileCoord t = tile_of(p.grid, blockIdx.x);
+    t.batch = uniform(t.batch);
+    t.tm = uniform(t.tm);
+    t.tn = uniform(t.tn);
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The wave index is uniform across the wave; saying so keeps the LDS
+    // destination of the direct loads (M0) in a scalar register.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+
+    OpA opa;
+    OpB opb;
+    const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
+    const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
+    opa.init(p.A + t.batch * p.sA, p.lda, p.M, m0, span_a, wave, lane);
+    opb.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, span_b, wave, lane);
+
+    LDS char *lds = (LDS char *)smem;  // generic -> LDS address space
+    const int64_t steps = (p.K + BK - 1) / BK;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Prologue: fill every stage buffer, then wait for the first.
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) {
+        if (st < steps) {
+            opa.issue(lds + st * STAGE, st, p.K, wave);
+            opb.issue(lds + st * STAGE + PANEL, st, p.K, wave);
+        }
+    }
+    wait_stages<PER_STAGE, STAGES>(int(steps - 1 < STAGES - 1 ? steps - 1 : STAGES - 1));
+    __syncthreads();
+
+    u32x4 fa[2][FM], fb[2][FN];
+    auto read = [&](int buf, int kk, int slot) {
+        const LDS char *sa = lds + buf * STAGE;
+        const LDS char *sb = sa + PANEL;
+        // in the order the matrix instructions consume them: all of B's
+        // fragments are used by the first row of instructions
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[slot][j] = opb.frag(sb, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[slot][i] = opa.frag(sa, wm * WTM + i * 32, kk, lane);
+    };
+    read(0, 0, 0);
+
+    int buf = 0;
+    for (int64_t s = 0; s < steps; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int slot = kk & 1;
+            if (kk < KK - 1) {
+                read(buf, kk + 1, slot ^ 1);
+            } else if (s + 1 < steps) {
+                // stage s + 1 must have landed (this wave's loads, then every
+                // wave's), and every wave must be done reading this buffer
+                // before it is refilled
+                const int64_t later = steps - 2 - s;
+                wait_stages<PER_STAGE, STAGES>(int(later < STAGES - 2 ? later : STAGES - 2));
+                wait_lgkmcnt0();
+                __syncthreads();
+                const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
+                read(nbuf, 0, slot ^ 1);
+                if (s + STAGES < steps) {
+                    opa.issue(lds + buf * STAGE, s + STAGES, p.K, wave);
+                    opb.issue(lds + buf * STAGE + PANEL, s + STAGES, p.K, wave);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = mfma32<T>(fb[slot][j], fa[slot][i], acc[i][j]);
+            interleave_reads<NREAD, FM * FN>();
+        }
+        buf = buf + 1 == STAGES ? 0 : buf + 1;
+    }
+
+    // Epilogue.  Block (i, j) is C^T: lane l holds row m = l % 32 of the
+    // block and, in registers 4q .. 4q+3, columns 8q + 4*(l / 32) + 0..3.
+    char *Cb = static_cast<char *>(p.C) + t.batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + wn * WTN + j * 32 + q * 8 + 4 * (lane >> 5);
+                if (n >= p.N) continue;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[i][j][4 * q + e];
+                const int nvalid = p.N - n >= 4 ? 4 : int(p.N - n);
+                store4<OUT>(Cb, m * p.ldc + n, v, p.beta, p.vec_c, nvalid);
+            }
+        }
+    }
+}
+
+// Tile configuration of the fast path: 256 x 256 block tile, BK-deep
+// stages, a ring of STAGES buffers, WAVES_M x WAVES_N waves.
+#ifndef LIBGEMM_DMA_WM
+#define LIBGEMM_DMA_WM 2
+#endif
+#ifndef LIBGEMM_DMA_WN
+#define LIBGEMM_DMA_WN 4
+#endif
+#ifndef LIBGEMM_DMA_BK
+#define LIBGEMM_DMA_BK 64
+#endif
+#ifndef LIBGEMM_DMA_STAGES
+#define LIBGEMM_DMA_STAGES 2
+#endif
+#ifndef LIBGEMM_DMA_GROUP_M
+#define LIBGEMM_DMA_GROUP_M 4
+#endif
+
+template <class T, int OUT, bool AK, bool BKM>
+hipError_t launch(DmaArgs &a, hipStream_t stream) {
+    constexpr int WM = LIBGEMM_DMA_WM, WN = LIBGEMM_DMA_WN;
+    void *args[] = {&a};
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(
+            &hgemm_dma_kernel<T, OUT, AK, BKM, WM, WN, LIBGEMM_DMA_BK, LIBGEMM_DMA_STAGES>),
+        dim3(static_cast<unsigned>(a.grid.count())), dim3(WM * WN * 64), args, 0, stream);
+}
+
+template <class T, int OUT>
+hipError_t launch_layout(const Problem &p, DmaArgs &a, hipStream_t stream) {
+    if (p.a_kmajor)
+        return p.b_kmajor ? launch<T, OUT, true, true>(a, stream)
+                          : launch<T, OUT, true, false>(a, stream);
+    return p.b_kmajor ? launch<T, OUT, false, true>(a, stream)
+                      : launch<T, OUT, false, false>(a, stream);
+}
+
+int64_t span_of(int64_t rows, int64_t cols, bool row_contig, int64_t ld) {
+    // rows x cols with `cols` contiguous when row_contig
+    return row_contig ? (rows - 1) * ld + cols : (cols - 1) * ld + rows;
+}
+
+}  // namespace
+
+// The fast path needs every operand chunk either fully inside or fully
+// outside its matrix (extents along the contiguous dimension, leading
+// dimensions and batch strides multiples of 8 elements, 16-byte aligned
+// bases) and slices whose byte extent fits the buffer range check.
+bool hgemm_dma_eligible(const Problem &p) {
+    if (p.in != Elem::BF16 && p.in != Elem::F16) return false;
+    const int64_t sa = p.batch > 1 ? p.sA : 0, sb = p.batch > 1 ? p.sB : 0;
+    if (!vec16_ok(p.A, p.lda, sa, 2) || !vec16_ok(p.B, p.ldb, sb, 2)) return false;
+    if ((p.a_kmajor ? p.K : p.M) % 8 || (p.b_kmajor ? p.K : p.N) % 8) return false;
+    const int64_t limit = int64_t(1) << 30;
+    if (2 * span_of(p.M, p.K, p.a_kmajor, p.lda) >= limit) return false;
+    if (2 * span_of(p.K, p.N, !p.b_kmajor, p.ldb) >= limit) return false;
+    return true;
+}
+
+hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
+    DmaArgs a{};
+    a.M = p.M;
+    a.N = p.N;
+    a.K = p.K;
+    a.alpha = p.alpha;
+    a.beta = p.beta;
+    a.A = static_cast<const uint16_t *>(p.A);
+    a.B = static_cast<const uint16_t *>(p.B);
+    a.C = p.C;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.sA = p.batch > 1 ? p.sA : 0;
+    a.sB = p.batch > 1 ? p.sB : 0;
+    a.sC = p.batch > 1 ? p.sC : 0;
+    a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, LIBGEMM_DMA_GROUP_M, 8};
+    if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int esz = p.out == Elem::F32 ? 4 : 2;
+    a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % (4 * esz)) == 0 && p.ldc % 4 == 0 &&
+              a.sC % 4 == 0;
+    const bool bf = p.in == Elem::BF16;
+    if (p.out == Elem::F32)
+        return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)
+                  : launch_layout<F16, OUT_F32>(p, a, stream);
+    return bf ? launch_layout<BF16, OUT_BF16>(p, a, stream)
+              : launch_layout<F16, OUT_F16>(p, a, stream);
+}
+
+}  // namespace libgemm

@@ -210,3 +210,34 @@ def test_full_config_sampled(name):
 def test_full_config_fp32_output(name):
     p = workloads.config(name)
     check(p.with_(name=p.name + "-f32out", c_dtype="f32"), sample="auto")
+
+
+# ------------------------------------------------------------------ fast (direct-load) path
+
+DMA_SHAPES = [(8, 8, 8), (256, 256, 64), (264, 520, 72), (512, 256, 128), (1000, 1032, 1000),
+              (24, 4096, 512), (2048, 264, 136)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_direct_load_path_ragged_aligned(dt, shape, orders):
+    # extents multiples of 8 but not of the 256 x 256 x 64 tile: the direct
+    # loads' range check and the last-stage k mask produce the edge zeros
+    M, N, K = shape
+    oa, ob = orders
+    check(P(f"dma-{dt}", dt, M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob),
+          seed=M + N + K)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_direct_load_path_fp32_out_and_col_major_c(dt):
+    check(P(f"dma-f32out-{dt}", dt, 520, 264, 200, c_dtype="f32", beta=-1.0), seed=31)
+    check(P(f"dma-colC-{dt}", dt, 520, 264, 200, order_c=COL, beta=0.25), seed=32)
+
+
+def test_general_kernel_forced_on_aligned_problem(monkeypatch):
+    # the same aligned problem through the general kernel (register-staged)
+    monkeypatch.setenv("LIBGEMM_FORCE_GENERAL", "1")
+    check(P("forced-general-bf16", "bf16", 512, 768, 320, beta=1.0), seed=33)
