@@ -10,9 +10,16 @@ each GEMM's own TFLOPS and fraction of MI355X's dense peak for its dtype,
 from HIP events recorded on the stream the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-context]
+                       [--no-cpu-baseline] [--no-context] [--copy-calibration MiB]
 --workload runs a single named workload (see workloads.CONFIGS) instead of
-the headline step, for profiling.
+the headline step, for profiling.  --copy-calibration runs only a plain
+device-to-device copy of the given size (the reference kernel against which
+the HBM byte counters FETCH_SIZE / WRITE_SIZE are scaled).
+
+The roofline's `traffic` is the dominant kernel's HBM bytes per launch, read
+from profiles/hbm_traffic.txt (counters taken with rocprofv3 --pmc, scaled by
+the copy calibration).  Each entry records a hash of the kernel source it was
+measured on; when the source has changed since, `traffic` is null.
 """
 import argparse
 import json
@@ -29,6 +36,10 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense, pu
 HBM_GBS = 8000.0
 
 HEADLINE = ["f32_4096", "bf16_4096", "f16_4096"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+# kernel family -> the source file that defines it (hashed to detect changes)
+KERNEL_SOURCE = {"sgemm_valu": "sgemm_valu.hip", "hgemm_mfma_dma": "hgemm_mfma_dma.hip",
+                 "hgemm_mfma": "hgemm_mfma.hip"}
 
 
 def log(*a):
@@ -55,6 +66,52 @@ def make_launch(p, bufs, stream):
     def launch():
         binding.gemm(*args)
     return launch
+
+
+def kernel_family(p):
+    """Which libgemm kernel serves a workload (the library's own selection
+    rule: bf16/fp16 problems whose contiguous extents, leading dimensions and
+    strides are multiples of 8 elements take the direct-load kernel)."""
+    if p.in_dtype == "f32":
+        return "sgemm_valu"
+    ext_a = p.K if p.order_a == 0 else p.M
+    ext_b = p.N if p.order_b == 0 else p.K
+    ok = all(v % 8 == 0 for v in (ext_a, ext_b, p.lda, p.ldb)) and \
+        (p.batch <= 1 or (p.stride_a % 8 == 0 and p.stride_b % 8 == 0))
+    return "hgemm_mfma_dma" if ok else "hgemm_mfma"
+
+
+def source_hash(family):
+    import hashlib
+    path = os.path.join(ROOT, "dense_gemm_optimisation_amd", "csrc", KERNEL_SOURCE[family])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(family, workload):
+    """HBM bytes per launch from profiles/hbm_traffic.txt, or None when the
+    entry is missing or was measured on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = source_hash(family)
+    for ln in open(TRAFFIC_FILE):
+        f = ln.split()
+        # family  source-sha  workload  fetch_bytes  write_bytes  (scaled, per launch)
+        if len(f) >= 5 and not ln.startswith("#") and f[0] == family and f[2] == workload:
+            return int(float(f[3]) + float(f[4])) if f[1] == want else None
+    return None
+
+
+def copy_calibration(mib, torch):
+    """A plain copy of `mib` MiB, five times: the counters' reference kernel."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
 
 
 def cpu_baseline(problems, budget_s):
@@ -94,6 +151,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the GEMM path has no multi-GPU "
@@ -105,6 +163,9 @@ def main():
     from dense_gemm_optimisation_amd import binding
     binding.library()  # fails loudly if libgemm.so is missing
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, torch)
+        return
     names = HEADLINE if args.workload == "headline" else [args.workload]
     problems = [workloads.config(n) for n in names]
     stream = torch.cuda.Stream()  # default priority
@@ -156,14 +217,12 @@ def main():
     def roof(name):
         k = per_kernel[name]
         p = workloads.config(name)
-        if p.in_dtype == "f32":
-            return {"kernel": f"sgemm_valu {name}", "bound": "alu", "achieved": k["tflops"],
-                    "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                    "frac": round(k["tflops"] / PEAK_TFLOPS["f32"], 4),
-                    "traffic": None}
-        return {"kernel": f"hgemm_mfma {name}", "bound": "mfma", "achieved": k["tflops"],
-                "peak": PEAK_TFLOPS[p.in_dtype], "unit": "TFLOP/s",
-                "frac": round(k["tflops"] / PEAK_TFLOPS[p.in_dtype], 4), "traffic": None}
+        fam = kernel_family(p)
+        bound, peak = ("alu", PEAK_TFLOPS["f32"]) if p.in_dtype == "f32" else \
+            ("mfma", PEAK_TFLOPS[p.in_dtype])
+        return {"kernel": f"{fam} {name}", "bound": bound, "achieved": k["tflops"],
+                "peak": peak, "unit": "TFLOP/s", "frac": round(k["tflops"] / peak, 4),
+                "traffic": measured_traffic(fam, name)}
 
     dominant = max(per_kernel, key=lambda n: per_kernel[n]["mean_us"])
     out = {
