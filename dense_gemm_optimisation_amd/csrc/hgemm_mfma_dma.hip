@@ -273,6 +273,34 @@ __device__ inline void store4(void *C, int64_t off, f32x4 v, float beta, bool ve
     }
 }
 
+// Epilogue: C = alpha*acc + beta*C_old for one wave's FM x FN blocks of
+// 32 x 32, whose top-left element is (mw, nw).  Block (i, j) holds C^T (the
+// operands were swapped): lane l holds row mw + 32i + l % 32 and, in
+// registers 4q .. 4q+3, columns nw + 32j + 8q + 4*(l / 32) + 0..3.
+template <int OUT, int FM, int FN>
+__device__ inline void store_tile(const DmaArgs &p, const f32x16 (&acc)[FM][FN], int64_t batch,
+                                  int64_t mw, int64_t nw, int lane) {
+    char *Cb = static_cast<char *>(p.C) + batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = mw + i * 32 + (lane & 31);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = nw + j * 32 + q * 8 + 4 * (lane >> 5);
+                if (n >= p.N) continue;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[i][j][4 * q + e];
+                const int nvalid = p.N - n >= 4 ? 4 : int(p.N - n);
+                store4<OUT>(Cb, m * p.ldc + n, v, p.beta, p.vec_c, nvalid);
+            }
+        }
+    }
+}
+
 // Waits until at most `n` stages of direct loads (each `per` instructions)
 // remain in flight; s_waitcnt takes an immediate, so the few possible
 // counts are enumerated.
@@ -404,28 +432,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
         buf = buf + 1 == STAGES ? 0 : buf + 1;
     }
 
-    // Epilogue.  Block (i, j) is C^T: lane l holds row m = l % 32 of the
-    // block and, in registers 4q .. 4q+3, columns 8q + 4*(l / 32) + 0..3.
-    char *Cb = static_cast<char *>(p.C) + t.batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * WTN + j * 32 + q * 8 + 4 * (lane >> 5);
-                if (n >= p.N) continue;
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[i][j][4 * q + e];
-                const int nvalid = p.N - n >= 4 ? 4 : int(p.N - n);
-                store4<OUT>(Cb, m * p.ldc + n, v, p.beta, p.vec_c, nvalid);
-            }
-        }
-    }
+    store_tile<OUT, FM, FN>(p, acc, t.batch, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
+
 
 // Tile configuration of the fast path: 256 x 256 block tile, BK-deep
 // stages, a ring of STAGES buffers, WAVES_M x WAVES_N waves.
