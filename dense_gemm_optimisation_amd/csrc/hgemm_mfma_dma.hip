@@ -186,23 +186,33 @@ struct Operand {
         step = KMAJOR ? int64_t(BK) * 2 : int64_t(BK) * ld * 2;
     }
 
-    // Direct loads of stage `stage` (k from stage*BK) into the LDS panel at dst.
-    __device__ void issue(LDS char *dst, int64_t stage, int64_t K, int wave) const {
+    // Buffer descriptor of the slice that stage `stage` starts (raw buffer:
+    // base, stride 0, size in bytes, 32-bit format); reads past its end
+    // return zero.
+    __device__ u32x4 rsrc(int64_t stage) const {
         const int64_t off = uniform(stage * step);
         const uint64_t addr = static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(base) + off));
-        u32x4 rs;  // raw buffer descriptor: base, stride 0, size in bytes, 32-bit format
+        u32x4 rs;
         rs[0] = static_cast<uint32_t>(addr);
         rs[1] = static_cast<uint32_t>(addr >> 32) & 0xffffu;
         rs[2] = static_cast<uint32_t>(uniform(bytes - off));
         rs[3] = 0x00020000u;
-        const int64_t kleft = K - stage * BK;
-        const bool tail = kleft < BK;
+        return rs;
+    }
+
+    // Direct load i (of PER_WAVE) of this wave for the stage with descriptor
+    // rs and kleft = K - stage*BK valid k values, into the panel at lds0.
+    __device__ void load(u32x4 rs, uint32_t lds0, int i, int64_t kleft, int wave) const {
+        const uint32_t v = (kleft < BK && kl[i] >= kleft) ? OOB : voff[i];
+        direct_load16(rs, lds0 + (wave * PER_WAVE + i) * 1024, v);
+    }
+
+    // All direct loads of stage `stage` (k from stage*BK) into the panel at dst.
+    __device__ void issue(LDS char *dst, int64_t stage, int64_t K, int wave) const {
+        const u32x4 rs = rsrc(stage);
         const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const uint32_t v = (tail && kl[i] >= kleft) ? OOB : voff[i];
-            direct_load16(rs, lds0 + (wave * PER_WAVE + i) * 1024, v);
-        }
+        for (int i = 0; i < PER_WAVE; ++i) load(rs, lds0, i, K - stage * BK, wave);
     }
 
     // Fragment of 32 rows (from row `row0` of the panel) for k16 step kk.
@@ -400,36 +410,65 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
     };
     read(0, 0, 0);
 
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<T>(fb[slot][j], fa[slot][i], acc[i][j]);
+    };
+
+    // Every stage but the last.  Its first KK - 1 k16 steps read the next
+    // step's fragments while computing.  Its last step waits for stage s + 1
+    // (this wave's loads, then every wave's through the barrier, which also
+    // says every wave is done reading this stage's buffer), reads stage
+    // s + 1's first fragments, and runs its matrix instructions with the
+    // refill of this buffer (stage s + STAGES) spread between them, so a load
+    // that waits for the memory pipeline does not hold back the matrix core.
+    // The last stage is peeled off so that no branch joins the code after the
+    // barrier: the LDS counter waits stay exact there.
     int buf = 0;
-    for (int64_t s = 0; s < steps; ++s) {
+    const int64_t main_steps = steps - 1;
+    for (int64_t s = 0; s < main_steps; ++s) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int slot = kk & 1;
-            if (kk < KK - 1) {
-                read(buf, kk + 1, slot ^ 1);
-            } else if (s + 1 < steps) {
-                // stage s + 1 must have landed (this wave's loads, then every
-                // wave's), and every wave must be done reading this buffer
-                // before it is refilled
-                const int64_t later = steps - 2 - s;
-                wait_stages<PER_STAGE, STAGES>(int(later < STAGES - 2 ? later : STAGES - 2));
-                wait_lgkmcnt0();
-                __syncthreads();
-                const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
-                read(nbuf, 0, slot ^ 1);
-                if (s + STAGES < steps) {
-                    opa.issue(lds + buf * STAGE, s + STAGES, p.K, wave);
-                    opb.issue(lds + buf * STAGE + PANEL, s + STAGES, p.K, wave);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma32<T>(fb[slot][j], fa[slot][i], acc[i][j]);
+        for (int kk = 0; kk < KK - 1; ++kk) {
+            read(buf, kk + 1, (kk & 1) ^ 1);
+            mfmas(kk & 1);
             interleave_reads<NREAD, FM * FN>();
         }
-        buf = buf + 1 == STAGES ? 0 : buf + 1;
+        constexpr int LAST = (KK - 1) & 1;
+        const int64_t later = steps - 2 - s;
+        wait_stages<PER_STAGE, STAGES>(int(later < STAGES - 2 ? later : STAGES - 2));
+        wait_lgkmcnt0();
+        __syncthreads();
+        const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
+        read(nbuf, 0, LAST ^ 1);
+        const int64_t refill = s + STAGES;
+        const bool do_refill = refill < steps;
+        const u32x4 ra = opa.rsrc(refill), rb = opb.rsrc(refill);
+        const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + buf * STAGE));
+        const uint32_t lb = la + PANEL;
+        const int64_t kleft = p.K - refill * BK;
+        // one direct load after each matrix instruction
+        static_assert(PER_STAGE <= FM * FN, "loads per instruction");
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j] = mfma32<T>(fb[LAST][j], fa[LAST][i], acc[i][j]);
+                const int q = i * FN + j;
+                if (do_refill) {
+                    if (q < OpA::PER_WAVE) opa.load(ra, la, q, kleft, wave);
+                    else if (q < PER_STAGE) opb.load(rb, lb, q - OpA::PER_WAVE, kleft, wave);
+                }
+            }
+        buf = nbuf;
+    }
+    // The last stage.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        if (kk < KK - 1) read(buf, kk + 1, (kk & 1) ^ 1);
+        mfmas(kk & 1);
+        interleave_reads<NREAD, FM * FN>();
     }
 
     store_tile<OUT, FM, FN>(p, acc, t.batch, m0 + wm * WTM, n0 + wn * WTN, lane);
