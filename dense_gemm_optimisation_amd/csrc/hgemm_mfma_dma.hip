@@ -242,70 +242,100 @@ struct Operand {
     }
 };
 
-template <int OUT>
-__device__ inline void store4(void *C, int64_t off, f32x4 v, float beta, bool vec, int nvalid) {
-    if (OUT == OUT_F32) {
-        float *p = static_cast<float *>(C) + off;
-        if (vec && nvalid == 4) {
-            if (beta != 0.0f) {
-                const f32x4 o = *reinterpret_cast<const f32x4 *>(p);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, o[e], v[e]);
-            }
-            *reinterpret_cast<f32x4 *>(p) = v;
-        } else {
-            for (int e = 0; e < nvalid; ++e) p[e] = beta != 0.0f ? __builtin_fmaf(beta, p[e], v[e]) : v[e];
-        }
-    } else {
-        uint16_t *p = static_cast<uint16_t *>(C) + off;
-        auto dec = [](uint16_t b) {
-            return OUT == OUT_BF16 ? __builtin_bit_cast(float, uint32_t(b) << 16)
-                                   : static_cast<float>(__builtin_bit_cast(_Float16, b));
-        };
-        auto enc = [](float x) {
-            return OUT == OUT_BF16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(x))
-                                   : __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-        };
-        if (vec && nvalid == 4) {
-            if (beta != 0.0f) {
-                const u16x4 o = *reinterpret_cast<const u16x4 *>(p);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, dec(o[e]), v[e]);
-            }
-            u16x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = enc(v[e]);
-            *reinterpret_cast<u16x4 *>(p) = w;
-        } else {
-            for (int e = 0; e < nvalid; ++e)
-                p[e] = enc(beta != 0.0f ? __builtin_fmaf(beta, dec(p[e]), v[e]) : v[e]);
-        }
-    }
-}
-
-// Epilogue: C = alpha*acc + beta*C_old for one wave's FM x FN blocks of
-// 32 x 32, whose top-left element is (mw, nw).  Block (i, j) holds C^T (the
-// operands were swapped): lane l holds row mw + 32i + l % 32 and, in
-// registers 4q .. 4q+3, columns nw + 32j + 8q + 4*(l / 32) + 0..3.
+// Epilogue through LDS.  One wave's tile is FM x FN blocks of 32 x 32 (top
+// left at (mw, nw)); block (i, j) holds C^T (the operands were swapped), so
+// lane l has row mw + 32i + l % 32 and, in registers 4q .. 4q+3, columns
+// nw + 32j + 8q + 4*(l / 32) + 0..3.  Each 32-row strip i is written to the
+// wave's own LDS area as alpha*acc in fp32, row-major with its 16-byte
+// chunks XOR-swizzled by row (chunk c of row r at c ^ (r mod 16), so the 32
+// rows one write instruction touches spread over the banks), then read back so
+// that every lane owns 16 contiguous bytes of one output row: a store
+// instruction then writes whole rows of the strip (8 rows of 128 bytes for
+// a 64-column bf16 strip) instead of 32 rows of 16 bytes, and C_old is read
+// the same way when beta != 0.  Rows or columns outside C are skipped, and a
+// chunk that crosses the right edge of C, or any chunk when C's rows are not
+// 16-byte aligned, is stored element by element.
 template <int OUT, int FM, int FN>
-__device__ inline void store_tile(const DmaArgs &p, const f32x16 (&acc)[FM][FN], int64_t batch,
-                                  int64_t mw, int64_t nw, int lane) {
+__device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][FN], int64_t batch,
+                                      int64_t mw, int64_t nw, int lane, LDS float *scratch) {
+    constexpr int W = FN * 32;          // strip width (columns)
+    constexpr int PITCH = W;            // floats per staged row
+    constexpr int SWZ = W / 4 - 1 < 15 ? W / 4 - 1 : 15;
+    auto at = [&](int r, int col) {     // staged float (r, col), col a multiple of 4
+        return scratch + r * PITCH + ((((col >> 2) ^ (r & SWZ))) << 2);
+    };
+    constexpr int CW = OUT == OUT_F32 ? 4 : 8;  // output elements per 16-byte chunk
+    constexpr int CPR = W / CW;         // chunks per row
+    constexpr int RPI = 64 / CPR;       // rows per store instruction
     char *Cb = static_cast<char *>(p.C) + batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
+    auto dec = [](uint16_t b) {
+        return OUT == OUT_BF16 ? __builtin_bit_cast(float, uint32_t(b) << 16)
+                               : static_cast<float>(__builtin_bit_cast(_Float16, b));
+    };
+    auto enc = [](float x) {
+        return OUT == OUT_BF16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(x))
+                               : __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+    };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int64_t m = mw + i * 32 + (lane & 31);
-        if (m >= p.M) continue;
+        // stage alpha*acc of strip i
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t n = nw + j * 32 + q * 8 + 4 * (lane >> 5);
-                if (n >= p.N) continue;
                 f32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[i][j][4 * q + e];
-                const int nvalid = p.N - n >= 4 ? 4 : int(p.N - n);
-                store4<OUT>(Cb, m * p.ldc + n, v, p.beta, p.vec_c, nvalid);
+                *reinterpret_cast<LDS f32x4 *>(at(lane & 31, j * 32 + q * 8 + 4 * (lane >> 5))) = v;
+            }
+        // write it out row by row (the wave's own LDS reads follow its writes)
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int r = it * RPI + lane / CPR, cc = (lane % CPR) * CW;
+            const int64_t m = mw + i * 32 + r, n = nw + cc;
+            float x[CW];
+#pragma unroll
+            for (int e4 = 0; e4 < CW / 4; ++e4) {
+                const f32x4 v = *reinterpret_cast<const LDS f32x4 *>(at(r, cc + 4 * e4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[4 * e4 + e] = v[e];
+            }
+            if (m >= p.M || n >= p.N) continue;
+            const int64_t off = m * p.ldc + n;
+            if (p.vec_c && n + CW <= p.N) {
+                if (OUT == OUT_F32) {
+                    float *c = reinterpret_cast<float *>(Cb) + off;
+                    f32x4 v = {x[0], x[1], x[2], x[3]};
+                    if (p.beta != 0.0f) {
+                        const f32x4 o = *reinterpret_cast<const f32x4 *>(c);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, o[e], v[e]);
+                    }
+                    *reinterpret_cast<f32x4 *>(c) = v;
+                } else {
+                    uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off;
+                    if (p.beta != 0.0f) {
+                        const u32x4 o = *reinterpret_cast<const u32x4 *>(c);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            x[e] = __builtin_fmaf(p.beta, dec(uint16_t(o[e / 2] >> (16 * (e % 2)))), x[e]);
+                    }
+                    u32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = uint32_t(enc(x[2 * e])) | (uint32_t(enc(x[2 * e + 1])) << 16);
+                    *reinterpret_cast<u32x4 *>(c) = w;
+                }
+            } else {
+                const int nvalid = p.N - n < CW ? int(p.N - n) : CW;
+                for (int e = 0; e < nvalid; ++e) {
+                    if (OUT == OUT_F32) {
+                        float *c = reinterpret_cast<float *>(Cb) + off + e;
+                        *c = p.beta != 0.0f ? __builtin_fmaf(p.beta, *c, x[e]) : x[e];
+                    } else {
+                        uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off + e;
+                        *c = enc(p.beta != 0.0f ? __builtin_fmaf(p.beta, dec(*c), x[e]) : x[e]);
+                    }
+                }
             }
         }
     }
@@ -471,7 +501,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
         interleave_reads<NREAD, FM * FN>();
     }
 
-    store_tile<OUT, FM, FN>(p, acc, t.batch, m0 + wm * WTM, n0 + wn * WTN, lane);
+    // C is staged in a buffer the last stage does not use: every wave
+    // finished reading it before the last barrier, and no load targets it
+    // any more, so no further barrier is needed.
+    static_assert(WAVES * 32 * WTN * 4 <= STAGE, "epilogue staging fits in one stage buffer");
+    LDS char *stage_free = lds + (buf + 1 == STAGES ? 0 : buf + 1) * STAGE;
+    store_tile_lds<OUT, FM, FN>(p, acc, t.batch, m0 + wm * WTM, n0 + wn * WTN, lane,
+                                reinterpret_cast<LDS float *>(stage_free) + wave * 32 * WTN);
 }
 
 
@@ -553,8 +589,9 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
     a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, LIBGEMM_DMA_GROUP_M, 8};
     if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int esz = p.out == Elem::F32 ? 4 : 2;
-    a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % (4 * esz)) == 0 && p.ldc % 4 == 0 &&
-              a.sC % 4 == 0;
+    // 16-byte chunks of C rows (8 bf16/fp16 or 4 fp32 elements)
+    const int cw = 16 / esz;
+    a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % 16) == 0 && p.ldc % cw == 0 && a.sC % cw == 0;
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)
         return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)
