@@ -61,6 +61,7 @@ struct HgemmArgs {
     int64_t sA, sB, sC;
     TileGrid grid;
     int vec_a, vec_b;
+    int ubuf_a, ubuf_b;  // the operand's span fits a raw buffer (unaligned vector path)
 };
 
 struct BF16 {};
@@ -98,26 +99,96 @@ __device__ inline u32x4 load8(const uint16_t *x, bool vec, bool inside, int64_t 
     return v;
 }
 
+// Unaligned operands (a leading dimension or base that is not a multiple of
+// 16 bytes) are read through a raw buffer whose base is the operand's first
+// byte rounded down to 4 bytes and whose size is the operand's span: eight
+// consecutive elements are one 16-byte load plus one 4-byte load at the
+// enclosing dword boundary, shifted into place by two bytes when the chunk
+// starts at an odd 16-bit position, instead of eight 2-byte loads.
+struct UBuf {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t mis;    // bytes between the buffer base and element 0
+    uint32_t limit;  // buffer size in bytes
+};
+
+__device__ inline UBuf make_ubuf(const uint16_t *x, int64_t span) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x);
+    const uintptr_t base = a & ~uintptr_t(3);
+    UBuf u;
+    u.mis = static_cast<uint32_t>(a - base);
+    u.limit = static_cast<uint32_t>(u.mis + 2 * span);
+    u.rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0,
+                                             static_cast<int>(u.limit), 0x00020000);
+    return u;
+}
+
+// Elements x[e .. e+7] with those at index >= valid (0..8) zero.  A chunk
+// whose 20-byte window would pass the end of the buffer is read element by
+// element: a load that is only partly inside the buffer's range may come
+// back as all zeros.
+__device__ inline u32x4 load8u(const UBuf &u, const uint16_t *x, int64_t e, int valid) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (valid <= 0) return zero;
+    const uint32_t bo = u.mis + static_cast<uint32_t>(e) * 2;
+    const uint32_t dw = bo & ~3u;
+    u32x4 v;
+    if (dw + 20 > u.limit) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = 2 * q < valid ? x[e + 2 * q] : 0u;
+            const uint32_t hi = 2 * q + 1 < valid ? x[e + 2 * q + 1] : 0u;
+            v[q] = lo | (hi << 16);
+        }
+        return v;
+    }
+    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(u.rs, dw, 0, 0));
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(u.rs, dw + 16, 0, 0);
+    const bool odd = (bo & 2) != 0;
+    v[0] = odd ? __builtin_amdgcn_alignbyte(lo[1], lo[0], 2) : lo[0];
+    v[1] = odd ? __builtin_amdgcn_alignbyte(lo[2], lo[1], 2) : lo[1];
+    v[2] = odd ? __builtin_amdgcn_alignbyte(lo[3], lo[2], 2) : lo[2];
+    v[3] = odd ? __builtin_amdgcn_alignbyte(hi, lo[3], 2) : lo[3];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t keep = (2 * q + 1 < valid ? 0xffff0000u : 0u) | (2 * q < valid ? 0xffffu : 0u);
+        v[q] &= keep;
+    }
+    return v;
+}
+
 // Global -> registers: one operand panel for the K step starting at k0.
 //   KMAJOR: element (r, k) at X[r*ld + k]; thread loads 8 chunks of 8 k.
 //   else:   element (r, k) at X[k*ld + r]; thread loads an 8 (k) x 8 (r) block.
-template <bool KMAJOR>
+//   UB: the operand is read through its raw buffer (any alignment);
+//   otherwise with 16-byte vector loads when `vec`, else element by element.
+template <bool KMAJOR, bool UB>
 __device__ inline void load_panel(const uint16_t *X, int64_t ld, int64_t rows, int64_t r0,
-                                  int64_t k0, int64_t K, bool vec, int tid, u32x4 v[8]) {
+                                  int64_t k0, int64_t K, bool vec, const UBuf &u, int tid,
+                                  u32x4 v[8]) {
     if (KMAJOR) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int c = tid + THREADS * i;
             const int row = c >> 3, kc = c & 7;
             const int64_t gr = r0 + row, gk = k0 + kc * 8;
-            v[i] = load8(X + gr * ld + gk, vec, gr < rows, gk, K);
+            if (UB) {
+                const int64_t left = K - gk;
+                v[i] = load8u(u, X, gr * ld + gk, gr < rows ? int(left < 8 ? left : 8) : 0);
+            } else {
+                v[i] = load8(X + gr * ld + gk, vec, gr < rows, gk, K);
+            }
         }
     } else {
         const int rb = tid & 31, kb = tid >> 5;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t gk = k0 + kb * 8 + i, gr = r0 + rb * 8;
-            v[i] = load8(X + gk * ld + gr, vec, gk < K, gr, rows);
+            if (UB) {
+                const int64_t left = rows - gr;
+                v[i] = load8u(u, X, gk * ld + gr, gk < K ? int(left < 8 ? left : 8) : 0);
+            } else {
+                v[i] = load8(X + gk * ld + gr, vec, gk < K, gr, rows);
+            }
         }
     }
 }
@@ -174,7 +245,7 @@ __device__ inline void store_c(void *C, int64_t off, float v) {
         static_cast<uint16_t *>(C)[off] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
 }
 
-template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR>
+template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, bool UB>
 __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
     __shared__ u32x4 smem[2][2][PANEL];  // [buffer][A, B][chunk]: 128 KiB
 
@@ -196,9 +267,12 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int64_t steps = (p.K + BK - 1) / BK;
+    const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
+    const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
+    const UBuf ua = make_ubuf(A, UB ? span_a : 0), ub = make_ubuf(B, UB ? span_b : 0);
     u32x4 va[8], vb[8];
-    load_panel<A_KMAJOR>(A, p.lda, p.M, m0, 0, p.K, p.vec_a, tid, va);
-    load_panel<B_KMAJOR>(B, p.ldb, p.N, n0, 0, p.K, p.vec_b, tid, vb);
+    load_panel<A_KMAJOR, UB>(A, p.lda, p.M, m0, 0, p.K, p.vec_a, ua, tid, va);
+    load_panel<B_KMAJOR, UB>(B, p.ldb, p.N, n0, 0, p.K, p.vec_b, ub, tid, vb);
     store_panel<A_KMAJOR>(smem[0][0], tid, va);
     store_panel<B_KMAJOR>(smem[0][1], tid, vb);
     __syncthreads();
@@ -208,8 +282,8 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
         const bool more = s + 1 < steps;
         if (more) {
             const int64_t k0 = (s + 1) * BK;
-            load_panel<A_KMAJOR>(A, p.lda, p.M, m0, k0, p.K, p.vec_a, tid, va);
-            load_panel<B_KMAJOR>(B, p.ldb, p.N, n0, k0, p.K, p.vec_b, tid, vb);
+            load_panel<A_KMAJOR, UB>(A, p.lda, p.M, m0, k0, p.K, p.vec_a, ua, tid, va);
+            load_panel<B_KMAJOR, UB>(B, p.ldb, p.N, n0, k0, p.K, p.vec_b, ub, tid, vb);
         }
         const u32x4 *sa = smem[cur][0];
         const u32x4 *sb = smem[cur][1];
@@ -262,8 +336,10 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
 template <class T, int OUT, bool AK, bool BKM>
 hipError_t launch(HgemmArgs &a, hipStream_t stream) {
     void *args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&hgemm_kernel<T, OUT, AK, BKM>),
-                           dim3(static_cast<unsigned>(a.grid.count())), dim3(THREADS), args, 0,
+    const void *k = a.ubuf_a && a.ubuf_b
+                        ? reinterpret_cast<const void *>(&hgemm_kernel<T, OUT, AK, BKM, true>)
+                        : reinterpret_cast<const void *>(&hgemm_kernel<T, OUT, AK, BKM, false>);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(a.grid.count())), dim3(THREADS), args, 0,
                            stream);
 }
 
@@ -298,6 +374,11 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
     if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.vec_a = vec16_ok(p.A, p.lda, a.sA, 2);
     a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 2);
+    // raw buffer sizes are 31-bit byte counts
+    const int64_t span_a = p.a_kmajor ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
+    const int64_t span_b = p.b_kmajor ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
+    a.ubuf_a = 2 * span_a + 4 < (int64_t(1) << 31);
+    a.ubuf_b = 2 * span_b + 4 < (int64_t(1) << 31);
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)
         return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)
