@@ -526,7 +526,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
 #define LIBGEMM_DMA_STAGES 2
 #endif
 #ifndef LIBGEMM_DMA_GROUP_M
-#define LIBGEMM_DMA_GROUP_M 4
+#define LIBGEMM_DMA_GROUP_M 8
 #endif
 
 template <class T, int OUT, bool AK, bool BKM>

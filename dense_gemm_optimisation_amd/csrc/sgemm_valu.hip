@@ -1,12 +1,14 @@
 // fp32 SGEMM on the vector ALUs of gfx950.
 //
-// One workgroup of 256 threads (four wave64 waves) computes a 128 x 128 tile
+// One workgroup of 256 threads (four wave64 waves) computes a 128 x 256 tile
 // of C.  The K dimension is walked in steps of 16: each step stages a 128 x 16
-// panel of A and a 16 x 128 panel of B in LDS, and every thread accumulates an
-// 8 x 8 block of C in registers as a sum of outer products (register tiling,
-// "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site) section 7; the 8 x 8 thread
-// tile and the 128/128/8 block shape of section 4 of "第4章：经典算子实现 ——
-// GEMM").  A is stored transposed in LDS (k-major) so that a thread's eight A
+// panel of A and a 16 x 256 panel of B in LDS, and every thread accumulates an
+// 8 x 16 block of C in registers as a sum of outer products (register tiling,
+// "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site) section 7; the 128/128/8
+// block shape and 8 x 8 thread tile of section 4 of "第4章：经典算子实现 ——
+// GEMM", widened along N).  An 8 x 16 thread tile issues six 16-byte LDS
+// reads per 128 fused multiply-adds, against four per 64 for 8 x 8; the LDS
+// read rate is what an 8 x 8 tile runs out of first on gfx950.  A is stored transposed in LDS (k-major) so that a thread's eight A
 // values for one k are contiguous, with four floats of padding per row against
 // bank conflicts (section 4.2 of the m.lqnn.cn SGEMM article).  Global loads
 // are 16-byte vectors when the operand's base, leading dimension and batch
@@ -16,7 +18,7 @@
 // (section 9 of the zhenwei.site guide), one barrier per step.
 //
 // Thread layout: thread t owns rows {4*ty + i, 64 + 4*ty + i} and columns
-// {4*tx + j, 64 + 4*tx + j} (ty = t / 16, tx = t % 16, i, j < 4).  Within a
+// {64*g + 4*tx + j} (ty = t / 16, tx = t % 16, i, j < 4, g < 4).  Within a
 // wave the four ty values read four distinct 16-byte A words (broadcast to 16
 // lanes each) and the sixteen tx values read 256 contiguous bytes of B.
 //
@@ -29,7 +31,8 @@
 namespace libgemm {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int NB = 4;  // 64-column groups per thread row
+constexpr int BM = 128, BN = 64 * NB, BK = 16;
 constexpr int THREADS = 256;
 constexpr int PAD = 4;
 constexpr int SA = BM + PAD;  // floats per k-row of the A panel
@@ -59,10 +62,10 @@ __device__ inline f4 load4(const float *x, bool vec, bool inside, int64_t first,
     return v;
 }
 
-// Global -> registers for one K step: two 4-float chunks of A and of B.
+// Global -> registers for one K step: two 4-float chunks of A and NB of B.
 template <bool A_KMAJOR, bool B_KMAJOR>
 __device__ inline void load_step(const SgemmArgs &p, const float *A, const float *B, int64_t m0,
-                                 int64_t n0, int64_t k0, int tid, f4 ra[2], f4 rb[2]) {
+                                 int64_t n0, int64_t k0, int tid, f4 ra[2], f4 rb[NB]) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int c = tid + THREADS * r;  // chunk id, 0..511
@@ -75,12 +78,16 @@ __device__ inline void load_step(const SgemmArgs &p, const float *A, const float
             const int64_t gk = k0 + k, gm = m0 + mq * 4;
             ra[r] = load4(A + gk * p.lda + gm, p.vec_a, gk < p.K, gm, p.M);
         }
-        if (B_KMAJOR) {  // 128 columns x 4 chunks along k
+    }
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        const int c = tid + THREADS * r;  // chunk id, 0 .. 256*NB-1
+        if (B_KMAJOR) {                   // BN columns x 4 chunks along k
             const int col = c >> 2, kq = c & 3;
             const int64_t gn = n0 + col, gk = k0 + kq * 4;
             rb[r] = load4(B + gn * p.ldb + gk, p.vec_b, gn < p.N, gk, p.K);
-        } else {  // 16 k-rows x 32 chunks along n
-            const int k = c >> 5, nq = c & 31;
+        } else {  // 16 k-rows x BN/4 chunks along n
+            const int k = c / (BN / 4), nq = c % (BN / 4);
             const int64_t gk = k0 + k, gn = n0 + nq * 4;
             rb[r] = load4(B + gk * p.ldb + gn, p.vec_b, gk < p.K, gn, p.N);
         }
@@ -90,7 +97,7 @@ __device__ inline void load_step(const SgemmArgs &p, const float *A, const float
 // Registers -> LDS panels (A transposed to k-major, B k-major).
 template <bool A_KMAJOR, bool B_KMAJOR>
 __device__ inline void store_step(float (*sA)[SA], float (*sB)[SB], int tid, const f4 ra[2],
-                                  const f4 rb[2]) {
+                                  const f4 rb[NB]) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int c = tid + THREADS * r;
@@ -102,19 +109,23 @@ __device__ inline void store_step(float (*sA)[SA], float (*sB)[SB], int tid, con
             const int k = c >> 5, mq = c & 31;
             *reinterpret_cast<f4 *>(&sA[k][mq * 4]) = ra[r];
         }
+    }
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        const int c = tid + THREADS * r;
         if (B_KMAJOR) {
             const int col = c >> 2, kq = c & 3;
 #pragma unroll
             for (int e = 0; e < 4; ++e) sB[kq * 4 + e][col] = rb[r][e];
         } else {
-            const int k = c >> 5, nq = c & 31;
+            const int k = c / (BN / 4), nq = c % (BN / 4);
             *reinterpret_cast<f4 *>(&sB[k][nq * 4]) = rb[r];
         }
     }
 }
 
 template <bool A_KMAJOR, bool B_KMAJOR>
-__global__ __launch_bounds__(THREADS, 2) void sgemm_kernel(SgemmArgs p) {
+__global__ __launch_bounds__(THREADS, 1) void sgemm_kernel(SgemmArgs p) {
     __shared__ float sA[2][BK][SA];
     __shared__ float sB[2][BK][SB];
 
@@ -126,14 +137,14 @@ __global__ __launch_bounds__(THREADS, 2) void sgemm_kernel(SgemmArgs p) {
     const int tid = threadIdx.x;
     const int ty = tid >> 4, tx = tid & 15;
 
-    float acc[8][8];
+    float acc[8][4 * NB];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+        for (int j = 0; j < 4 * NB; ++j) acc[i][j] = 0.0f;
 
     const int64_t steps = (p.K + BK - 1) / BK;
-    f4 ra[2], rb[2];
+    f4 ra[2], rb[NB];
     load_step<A_KMAJOR, B_KMAJOR>(p, A, B, m0, n0, 0, tid, ra, rb);
     store_step<A_KMAJOR, B_KMAJOR>(sA[0], sB[0], tid, ra, rb);
     __syncthreads();
@@ -142,19 +153,23 @@ __global__ __launch_bounds__(THREADS, 2) void sgemm_kernel(SgemmArgs p) {
         const int cur = s & 1;
         const bool more = s + 1 < steps;
         if (more) load_step<A_KMAJOR, B_KMAJOR>(p, A, B, m0, n0, (s + 1) * BK, tid, ra, rb);
-        // Unrolling all 16 k hoists every LDS read ahead and spills; 8 does not.
-#pragma unroll 8
+        // Unrolled by two: unrolled further, the compiler issues more
+        // k-steps' LDS reads up front and runs out of registers.
+#pragma unroll 2
         for (int k = 0; k < BK; ++k) {
             const f4 a0 = *reinterpret_cast<const f4 *>(&sA[cur][k][ty * 4]);
             const f4 a1 = *reinterpret_cast<const f4 *>(&sA[cur][k][64 + ty * 4]);
-            const f4 b0 = *reinterpret_cast<const f4 *>(&sB[cur][k][tx * 4]);
-            const f4 b1 = *reinterpret_cast<const f4 *>(&sB[cur][k][64 + tx * 4]);
-            float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            f4 b[NB];
+#pragma unroll
+            for (int g = 0; g < NB; ++g) b[g] = *reinterpret_cast<const f4 *>(&sB[cur][k][64 * g + tx * 4]);
+            const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+                for (int g = 0; g < NB; ++g)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][4 * g + j] = __builtin_fmaf(a[i], b[g][j], acc[i][4 * g + j]);
         }
         if (more) store_step<A_KMAJOR, B_KMAJOR>(sA[cur ^ 1], sB[cur ^ 1], tid, ra, rb);
         __syncthreads();
@@ -166,7 +181,7 @@ __global__ __launch_bounds__(THREADS, 2) void sgemm_kernel(SgemmArgs p) {
         const int64_t row = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
         if (row >= p.M) continue;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NB; ++h) {
             const int64_t col = n0 + h * 64 + tx * 4;
             float *dst = C + row * p.ldc + col;
             f4 v;
