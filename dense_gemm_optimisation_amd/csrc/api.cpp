@@ -127,6 +127,8 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
         err = launch_scale(p, stream);
     else if (in == Elem::F32)
         err = launch_sgemm(p, stream);
+    else if (hgemm_splitk_eligible(p) && !force_general())
+        err = launch_hgemm_splitk(p, stream);
     else if (hgemm_dma_eligible(p) && !force_general())
         err = launch_hgemm_dma(p, stream);
     else

@@ -47,6 +47,10 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on 
 // hgemm_dma_eligible() holds (aligned operands, extents multiple of 8).
 bool hgemm_dma_eligible(const Problem &p);
 hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream);
+// bf16/fp16 split-K inside a workgroup, for problems with few output tiles
+// and a long K (hgemm_splitk_eligible()).
+bool hgemm_splitk_eligible(const Problem &p);
+hipError_t launch_hgemm_splitk(const Problem &p, hipStream_t stream);
 hipError_t launch_scale(const Problem &p, hipStream_t stream);  // C <- beta*C only
 
 }  // namespace libgemm

@@ -241,3 +241,33 @@ def test_general_kernel_forced_on_aligned_problem(monkeypatch):
     # the same aligned problem through the general kernel (register-staged)
     monkeypatch.setenv("LIBGEMM_FORCE_GENERAL", "1")
     check(P("forced-general-bf16", "bf16", 512, 768, 320, beta=1.0), seed=33)
+
+
+# ------------------------------------------------------------------ split-K path (few tiles, long K)
+
+SPLITK_SHAPES = [(16, 4096, 4096), (8, 8, 4096), (40, 1000, 1736), (256, 256, 8192), (24, 520, 512)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_splitk_path(dt, shape, orders):
+    # under 64 tiles of 256 x 256 and K >= 512: the workgroup splits K eight
+    # ways (slices ragged against K where 8*64 does not divide it)
+    M, N, K = shape
+    oa, ob = orders
+    big = M * N * K > 100_000_000
+    check(P(f"splitk-{dt}", dt, M, N, K, alpha=0.75, beta=-0.5, order_a=oa, order_b=ob),
+          seed=M + 3 * N + K, sample="auto" if big else None)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_splitk_fp32_output_batch_and_col_major_c(dt):
+    check(P(f"splitk-f32out-{dt}", dt, 24, 520, 2048, c_dtype="f32", beta=1.0, batch=3), seed=41)
+    check(P(f"splitk-colC-{dt}", dt, 520, 24, 2048, order_c=COL, beta=0.5), seed=42)
+    # integer inputs: every partial sum exact in fp32, so the fixed-order
+    # reduction of the eight slices must reproduce the oracle bit for bit
+    p = P(f"splitk-int-{dt}", dt, 16, 264, 4096, alpha=2.0, beta=1.0)
+    res, _ = check(p, host=_int_host(p, np.random.default_rng(43)))
+    assert res.max_err == 0.0 and res.max_ulp == 0
