@@ -39,7 +39,7 @@ HEADLINE = ["f32_4096", "bf16_4096", "f16_4096"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 # kernel family -> the source file that defines it (hashed to detect changes)
 KERNEL_SOURCE = {"sgemm_valu": "sgemm_valu.hip", "hgemm_mfma_dma": "hgemm_mfma_dma.hip",
-                 "hgemm_mfma": "hgemm_mfma.hip"}
+                 "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip"}
 
 
 def log(*a):
@@ -71,14 +71,19 @@ def make_launch(p, bufs, stream):
 def kernel_family(p):
     """Which libgemm kernel serves a workload (the library's own selection
     rule: bf16/fp16 problems whose contiguous extents, leading dimensions and
-    strides are multiples of 8 elements take the direct-load kernel)."""
+    strides are multiples of 8 elements take a direct-load kernel; of those,
+    problems with fewer than 64 output tiles of 256 x 256 and K >= 512 split
+    K inside a workgroup)."""
     if p.in_dtype == "f32":
         return "sgemm_valu"
     ext_a = p.K if p.order_a == 0 else p.M
     ext_b = p.N if p.order_b == 0 else p.K
     ok = all(v % 8 == 0 for v in (ext_a, ext_b, p.lda, p.ldb)) and \
         (p.batch <= 1 or (p.stride_a % 8 == 0 and p.stride_b % 8 == 0))
-    return "hgemm_mfma_dma" if ok else "hgemm_mfma"
+    if not ok:
+        return "hgemm_mfma"
+    big_tiles = -(-p.M // 256) * -(-p.N // 256) * max(p.batch, 1)
+    return "hgemm_splitk" if big_tiles < 64 and p.K >= 512 else "hgemm_mfma_dma"
 
 
 def source_hash(family):

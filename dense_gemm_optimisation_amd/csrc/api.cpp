@@ -42,10 +42,19 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.h
 // Product of non-negative dimensions overflowing int64 (or the 2^31 grid).
 bool too_big(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
 
-// LIBGEMM_FORCE_GENERAL=1 routes every bf16/fp16 call to the general
-// kernel (used to test the two matrix-core kernels against each other).
+// LIBGEMM_FORCE_GENERAL=1 routes every call to the general matrix-core
+// kernel of its type instead of a fast path (used to test the kernels
+// against each other).
 bool force_general() {
     const char *v = std::getenv("LIBGEMM_FORCE_GENERAL");
+    return v != nullptr && v[0] == '1';
+}
+
+// LIBGEMM_F32_VALU=1 routes fp32 calls to the register-tiled vector-ALU
+// kernel instead of the matrix-core one (used to test the two against each
+// other and to time the vector-ALU design).
+bool f32_valu() {
+    const char *v = std::getenv("LIBGEMM_F32_VALU");
     return v != nullptr && v[0] == '1';
 }
 
@@ -126,7 +135,9 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
     if (!reads_ab)
         err = launch_scale(p, stream);
     else if (in == Elem::F32)
-        err = launch_sgemm(p, stream);
+        err = f32_valu()                                    ? launch_sgemm(p, stream)
+              : sgemm_dma_eligible(p) && !force_general() ? launch_sgemm_dma(p, stream)
+                                                          : launch_sgemm_mfma(p, stream);
     else if (hgemm_splitk_eligible(p) && !force_general())
         err = launch_hgemm_splitk(p, stream);
     else if (hgemm_dma_eligible(p) && !force_general())

@@ -41,7 +41,12 @@ inline bool vec16_ok(const void *p, int64_t ld, int64_t stride, int esize) {
 }
 
 // Kernel launchers; each returns the launch status.
-hipError_t launch_sgemm(const Problem &p, hipStream_t stream);  // fp32 on the vector ALUs
+hipError_t launch_sgemm(const Problem &p, hipStream_t stream);       // fp32 on the vector ALUs
+hipError_t launch_sgemm_mfma(const Problem &p, hipStream_t stream);  // fp32 on the matrix cores
+// fp32 on the matrix cores with direct global->LDS loads; only for problems
+// where sgemm_dma_eligible() holds (aligned operands, extents multiple of 4).
+bool sgemm_dma_eligible(const Problem &p);
+hipError_t launch_sgemm_dma(const Problem &p, hipStream_t stream);
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA, any shape
 // bf16/fp16 on MFMA with direct global->LDS loads; only for problems where
 // hgemm_dma_eligible() holds (aligned operands, extents multiple of 8).

@@ -43,10 +43,17 @@
 //     at c ^ 4*t(r), t(r) = (r & 7) ^ 4*((r >> 3) & 1): the eight rows one
 //     transpose read touches fall in eight different 64-byte bank groups.
 #include "gemm_problem.hpp"
+#include "lds_dma.hpp"
 #include "tile_schedule.hpp"
 
 namespace libgemm {
 namespace {
+
+using dma::OOB;
+using dma::direct_load16;
+using dma::uniform;
+using dma::wait_lgkmcnt0;
+using dma::wait_vmcnt;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -57,10 +64,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-#define LDS __attribute__((address_space(3)))
-
 constexpr int BM = 256, BN = 256;       // block tile (rows of A and columns of B)
-constexpr uint32_t OOB = 0x80000000u;    // voffset beyond any accepted buffer size
 constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2;
 
 struct DmaArgs {
@@ -91,20 +95,6 @@ __device__ inline f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Values the compiler cannot prove wave-uniform (they come out of 64-bit
-// divisions done on the vector ALU) are moved to scalar registers, so that
-// buffer descriptors and M0 are built once per wave instead of in a loop
-// over distinct lane values.
-__device__ inline int64_t uniform(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(uint64_t(x) >> 32));
-    return static_cast<int64_t>((uint64_t(hi) << 32) | lo);
-}
-template <class T>
-__device__ inline T *uniform_ptr(T *p) {
-    return reinterpret_cast<T *>(uniform(reinterpret_cast<int64_t>(p)));
-}
-
 // Swizzle of a K-contiguous panel row (CH 16-byte chunks per row): a
 // permutation of [0, CH) chosen so that 16 consecutive rows read at one
 // logical chunk fall on 16 distinct 16-byte bank groups of a 256-byte wide
@@ -118,32 +108,6 @@ __device__ inline int swz_k(int row) {
 // chunk bits 2..4 with t(r) = (r & 7) ^ 4*((r >> 3) & 1), so the eight rows
 // one transpose read touches use eight different 64-byte bank groups.
 __device__ inline int swz_mn(int krow) { return ((krow & 7) ^ (((krow >> 3) & 1) << 2)) << 2; }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ inline void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
-// buffer_load_dwordx4 ... lds: 16 bytes per lane from the buffer `rs` at
-// byte offset `voffset` into LDS at `lds` + 16 * lane.  Issued as inline
-// assembly on purpose: the compiler does not then treat the load as a
-// pending LDS write, so it does not wait for every outstanding prefetch
-// before each LDS read (the prefetches target other buffers).  Visibility is
-// ensured explicitly: s_waitcnt vmcnt for the stage being consumed, then a
-// workgroup barrier.  A descriptor and LDS address that are not
-// wave-uniform would be wrong here, so both come from scalar values.
-__device__ inline void direct_load16(u32x4 rs, uint32_t lds, uint32_t voffset) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
-        :
-        : "s"(lds), "v"(voffset), "s"(rs)
-        : "memory", "m0");
-}
 
 // One operand panel of the tile (256 rows of A or 256 columns of B, BK deep):
 // where each lane fetches from, and how the wave reads fragments back.
@@ -191,13 +155,8 @@ struct Operand {
     // return zero.
     __device__ u32x4 rsrc(int64_t stage) const {
         const int64_t off = uniform(stage * step);
-        const uint64_t addr = static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(base) + off));
-        u32x4 rs;
-        rs[0] = static_cast<uint32_t>(addr);
-        rs[1] = static_cast<uint32_t>(addr >> 32) & 0xffffu;
-        rs[2] = static_cast<uint32_t>(uniform(bytes - off));
-        rs[3] = 0x00020000u;
-        return rs;
+        return dma::raw_buffer(static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(base) + off)),
+                               static_cast<uint32_t>(uniform(bytes - off)));
     }
 
     // Direct load i (of PER_WAVE) of this wave for the stage with descriptor

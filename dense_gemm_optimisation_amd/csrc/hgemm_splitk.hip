@@ -25,9 +25,15 @@
 //     fp32 epilogue computes alpha*sum + beta*C_old (C_old not read when
 //     beta == 0) and rounds to the output type to nearest-even.
 #include "gemm_problem.hpp"
+#include "lds_dma.hpp"
 
 namespace libgemm {
 namespace {
+
+using dma::OOB;
+using dma::direct_load16;
+using dma::wait_lgkmcnt0;
+using dma::wait_vmcnt;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -36,14 +42,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-#define LDS __attribute__((address_space(3)))
 
 constexpr int WAVES = 8;
 constexpr int TILE = 32;                     // output tile is TILE x TILE
 constexpr int CK = 64;                       // k values per chunk
 constexpr int PANEL = TILE * CK * 2;         // bytes of one operand chunk (4 KiB)
 constexpr int WAVE_LDS = 2 * 2 * PANEL;      // two chunks of A and B per wave
-constexpr uint32_t OOB = 0x80000000u;        // voffset beyond any accepted buffer size
 constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2;
 
 struct SplitArgs {
@@ -74,30 +78,6 @@ __device__ inline f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-__device__ inline uint32_t uniform32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ inline uint64_t uniform64(uint64_t x) {
-    return (uint64_t(uniform32(uint32_t(x >> 32))) << 32) | uniform32(uint32_t(x));
-}
-
-// 16 bytes per lane from the raw buffer `rs` at byte offset `voffset` into
-// LDS at `lds` + 16 * lane (see the main kernel for why this is inline
-// assembly: completion is tracked explicitly with s_waitcnt vmcnt).
-__device__ inline void direct_load16(u32x4 rs, uint32_t lds, uint32_t voffset) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
-        :
-        : "s"(lds), "v"(voffset), "s"(rs)
-        : "memory", "m0");
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
 // One operand of the tile: TILE rows (of A: m; of B: n) by a wave's K slice.
 //   KMAJOR: element (r, k) at X[r*ld + k]; a chunk is stored [32 r][64 k],
 //           128 bytes per row, loaded 8 rows per instruction.
@@ -110,11 +90,7 @@ struct Slice {
     int64_t r0;        // first row of the tile
 
     __device__ void init(const uint16_t *x, int64_t ld_, int64_t rows_, int64_t r0_, int64_t span) {
-        const uint64_t a = uniform64(reinterpret_cast<uint64_t>(x));
-        rs[0] = uint32_t(a);
-        rs[1] = uint32_t(a >> 32) & 0xffffu;
-        rs[2] = uint32_t(span * 2);
-        rs[3] = 0x00020000u;
+        rs = dma::raw_buffer(dma::uniform(reinterpret_cast<int64_t>(x)), uint32_t(span * 2));
         ld = ld_;
         rows = rows_;
         r0 = r0_;

@@ -1,0 +1,502 @@
+// fp32 SGEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
+//
+// gfx950's matrix cores take fp32 operands at the same peak rate as its
+// vector ALUs, but an fp32 matrix instruction does 32 x 32 x 2 multiply-adds
+// from two registers per lane, so the operands a wave must fetch from LDS per
+// multiply-add are a small fraction of what a register-tiled vector kernel
+// needs, and no vector-register bank conflicts arise.  The tiling is the
+// block tile -> wave tile -> matrix instruction hierarchy of "GPU GEMM
+// 优化完全拆解（三）" (pinghaoyang.com.cn), section "从 kernel 到库":
+//
+//   * one workgroup of 256 threads (four wave64 waves, 2 x 2) computes a
+//     128 x 128 tile of C; each wave owns 64 x 64 of it as 2 x 2
+//     accumulators of 32 x 32 (16 fp32 per lane each);
+//   * K advances 16 at a time through two LDS panels (128 x 16 of A,
+//     16 x 128 of B).  A panel whose operand is K-contiguous in memory is
+//     stored [row][k] with its four 16-byte chunks per row XOR-swizzled, and
+//     a lane's operands for four consecutive matrix instructions are one
+//     16-byte read (the instruction's K index, lane / 32, selects the first
+//     or second group of four k, the instruction number the element inside
+//     it, the same assignment for A and B: eight k per four instructions).
+//     A panel whose operand is contiguous along M or N is stored [k][row]:
+//     global loads of four consecutive rows go to LDS as one 16-byte store,
+//     and a lane reads two adjacent rows at one k with one 8-byte read, so
+//     the wave's two 32-row tiles interleave (tile t, lane index i is row
+//     2i + t).  Neither layout has LDS bank conflicts on reads or writes;
+//   * the instruction computes C^T = B^T A^T (B's operand in the first
+//     slot), which leaves every lane with consecutive columns of one row of
+//     C (four, or eight when B is N-contiguous): 16-byte stores in the
+//     epilogue;
+//   * the next K step's global loads are issued before the current step's
+//     matrix instructions and written to the other LDS buffer after them
+//     (double buffering, section 9 of "CUDA GEMM 矩阵乘法优化指南",
+//     blog.zhenwei.site); one barrier per step;
+//   * edges: elements outside the matrices read as zero and stores outside C
+//     are skipped (section 5.2 of the same guide), so any shape, leading
+//     dimension and alignment is exact; 16-byte vector loads are used when
+//     the operand allows them.
+//
+// The epilogue computes alpha*acc + beta*C_old in fp32 (C_old not read when
+// beta == 0).
+#include "gemm_problem.hpp"
+#include "lds_dma.hpp"
+#include "tile_schedule.hpp"
+
+namespace libgemm {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int THREADS = 256;
+constexpr int PANEL = BM * BK;  // floats per operand panel (8 KiB)
+static_assert(BM == BN, "both panels share one layout");
+
+struct SgemmArgs {
+    int64_t M, N, K;
+    float alpha, beta;
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int64_t sA, sB, sC;
+    TileGrid grid;
+    int vec_a, vec_b, vec_c;  // 16-byte vector access allowed for the operand
+};
+
+// Four consecutive elements x[0..3] of one operand row, zero outside
+// [0, limit); `inside` says the whole row exists.
+__device__ inline f4 load4(const float *x, bool vec, bool inside, int64_t first, int64_t limit) {
+    if (vec && inside && first + 4 <= limit) return *reinterpret_cast<const f4 *>(x);
+    f4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (inside && first + e < limit) ? x[e] : 0.0f;
+    return v;
+}
+
+// One operand panel in LDS: 128 rows (of A: output rows; of B: output
+// columns) by 16 k.
+//
+// KMAJOR (the operand is K-contiguous in memory): stored [row][k], chunk c
+// of row r at chunk c ^ ((r >> 2) & 3).  A lane's operands for four
+// instructions are one 16-byte read of four consecutive k, and the two
+// 32-row tiles of a wave's 64 rows are rows 0..31 and 32..63.
+//
+// Otherwise (contiguous along rows in memory): stored [k][row], 128 floats
+// per k.  A lane reads two adjacent rows at one k with one 8-byte read, and
+// the two 32-row tiles of a wave's 64 rows interleave: tile t, lane index i
+// is row 2*i + t.  Global loads of four consecutive rows are written as
+// one 16-byte store.
+template <bool KMAJOR>
+struct Panel {
+    __device__ static int at(int row, int k) {
+        if (KMAJOR) return row * BK + ((((k >> 2) ^ (row >> 2)) & 3) << 2) + (k & 3);
+        return k * BM + row;
+    }
+
+    // Row (within the wave's 64) that tile t, lane index i stands for.
+    __device__ static int row_of(int t, int i) { return KMAJOR ? t * 32 + i : 2 * i + t; }
+
+    // Global -> registers for the K step at k0: two 4-float chunks per
+    // thread.  `rows` is the operand's M (or N) extent, `x` its batch slice;
+    // element (row, k) at x[row*ld + k] if KMAJOR, else at x[k*ld + row].
+    __device__ static void load(const float *x, int64_t ld, bool vec, int64_t r0, int64_t rows,
+                                int64_t k0, int64_t K, int tid, f4 v[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + THREADS * i;  // chunk id, 0..511
+            if (KMAJOR) {                     // 128 rows x 4 chunks along k
+                const int row = c >> 2, kq = c & 3;
+                const int64_t gr = r0 + row, gk = k0 + kq * 4;
+                v[i] = load4(x + gr * ld + gk, vec, gr < rows, gk, K);
+            } else {  // 16 k-rows x 32 chunks along the row index
+                const int k = c >> 5, rq = c & 31;
+                const int64_t gk = k0 + k, gr = r0 + rq * 4;
+                v[i] = load4(x + gk * ld + gr, vec, gk < K, gr, rows);
+            }
+        }
+    }
+
+    __device__ static void store(float *s, int tid, const f4 v[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + THREADS * i;
+            if (KMAJOR)
+                *reinterpret_cast<f4 *>(s + at(c >> 2, (c & 3) * 4)) = v[i];
+            else
+                *reinterpret_cast<f4 *>(s + at((c & 31) * 4, c >> 5)) = v[i];
+        }
+    }
+
+    // Operands of the four instructions of k group g (k = 8g .. 8g+7) for
+    // the wave's two tiles: f[t][e] is the value at k = 8g + 4*half + e of
+    // the row tile t, lane index idx stands for.
+    __device__ static void frag(const float *s, int w0, int g, int idx, int half, float f[2][4]) {
+        const int k = 8 * g + 4 * half;
+        if (KMAJOR) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f4 v = *reinterpret_cast<const f4 *>(s + at(w0 + row_of(t, idx), k));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[t][e] = v[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f2 v = *reinterpret_cast<const f2 *>(s + at(w0 + 2 * idx, k + e));
+                f[0][e] = v[0];
+                f[1][e] = v[1];
+            }
+        }
+    }
+};
+
+// Epilogue of one wave: C = alpha*acc + beta*C_old for its 64 x 64 tile,
+// whose top left corner is (mw, nw); C_old is not read when beta == 0.
+template <bool A_KMAJOR, bool B_KMAJOR>
+__device__ inline void store_c(const SgemmArgs &p, const f32x16 (&acc)[2][2], float *C, int64_t mw,
+                               int64_t nw, int idx, int half) {
+    // Accumulator (i, j) register 4q + e of this lane holds
+    // C[mw + Panel<A_KMAJOR>::row_of(i, idx)][nw + Panel<B_KMAJOR>::row_of(j, 8q + 4*half + e)]
+    // (the instruction computes C^T, so B's tile index picks the column).
+    // It is written as eight 4-column chunks per accumulator row: with a
+    // K-contiguous B, chunk (j, q) is columns j*32 + 8q + 4*half + 0..3; with
+    // an N-contiguous B, chunk (q, c) is columns 16q + 8*half + 4c + 0..3,
+    // column 2e' + j of the eight holding register 4q + e' of tile j.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t row = mw + Panel<A_KMAJOR>::row_of(i, idx);
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+            int64_t col;
+            f4 v;
+            if (B_KMAJOR) {
+                const int j = ch >> 2, q = ch & 3;
+                col = nw + j * 32 + 8 * q + 4 * half;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[i][j][4 * q + e];
+            } else {
+                const int q = ch >> 1, c = ch & 1;
+                col = nw + 16 * q + 8 * half + 4 * c;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = p.alpha * acc[i][u & 1][4 * q + 2 * c + (u >> 1)];
+            }
+            float *dst = C + row * p.ldc + col;
+            if (p.vec_c && col + 4 <= p.N) {
+                if (p.beta != 0.0f) {
+                    const f4 old = *reinterpret_cast<const f4 *>(dst);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, old[e], v[e]);
+                }
+                *reinterpret_cast<f4 *>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (col + e < p.N) {
+                        float x = v[e];
+                        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, dst[e], x);
+                        dst[e] = x;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR>
+__global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_kernel(SgemmArgs p) {
+    __shared__ __attribute__((aligned(16))) float smem[2][2][PANEL];  // [buffer][A, B]
+    using PA = Panel<A_KMAJOR>;
+    using PB = Panel<B_KMAJOR>;
+
+    const TileCoord t = tile_of(p.grid, blockIdx.x);
+    const float *A = p.A + t.batch * p.sA;
+    const float *B = p.B + t.batch * p.sB;
+    float *C = p.C + t.batch * p.sC;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int idx = lane & 31, half = lane >> 5;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t steps = (p.K + BK - 1) / BK;
+    f4 va[2], vb[2];
+    PA::load(A, p.lda, p.vec_a, m0, p.M, 0, p.K, tid, va);
+    PB::load(B, p.ldb, p.vec_b, n0, p.N, 0, p.K, tid, vb);
+    PA::store(smem[0][0], tid, va);
+    PB::store(smem[0][1], tid, vb);
+    __syncthreads();
+
+    for (int64_t s = 0; s < steps; ++s) {
+        const int cur = s & 1;
+        const bool more = s + 1 < steps;
+        if (more) {
+            PA::load(A, p.lda, p.vec_a, m0, p.M, (s + 1) * BK, p.K, tid, va);
+            PB::load(B, p.ldb, p.vec_b, n0, p.N, (s + 1) * BK, p.K, tid, vb);
+        }
+#pragma unroll
+        for (int g = 0; g < BK / 8; ++g) {
+            float fa[2][4], fb[2][4];
+            PA::frag(smem[cur][0], wm * 64, g, idx, half, fa);
+            PB::frag(smem[cur][1], wn * 64, g, idx, half, fb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[j][e], fa[i][e],
+                                                                         acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            PA::store(smem[cur ^ 1][0], tid, va);
+            PB::store(smem[cur ^ 1][1], tid, vb);
+        }
+        __syncthreads();
+    }
+
+    store_c<A_KMAJOR, B_KMAJOR>(p, acc, C, m0 + wm * 64, n0 + wn * 64, idx, half);
+}
+
+// Direct global -> LDS loads of one operand panel, same layouts as Panel:
+// the 8 KiB panel is eight 1 KiB blocks, two per wave, and lane L of block b
+// fills the panel's 16-byte chunk 64b + L.  A K-contiguous panel's chunk P
+// is row P / 4, physical chunk P % 4, which holds logical chunk
+// (P % 4) ^ ((row >> 2) & 3), so each lane fetches that global chunk (the
+// swizzle is applied on the global side because the loads place lanes
+// linearly).  An M/N-contiguous panel's chunk P is k = P / 32, rows
+// 4(P % 32) .. +3.  Chunks outside the operand get an out-of-range offset
+// and read as zero; that needs every chunk to be wholly inside or outside,
+// which the eligibility test guarantees (contiguous extent a multiple of 4).
+template <bool KMAJOR>
+struct DmaPanel {
+    static constexpr int PER_WAVE = PANEL * 4 / 1024 / (THREADS / 64);
+    static_assert(PER_WAVE == 2, "two 1 KiB loads per wave per panel");
+    uint32_t voff[PER_WAVE];  // byte offset of this lane's chunk in the first stage
+    int kl[PER_WAVE];         // first k (within a stage) of this lane's chunk
+    const float *base;
+    int64_t bytes;            // extent of the operand slice in bytes
+    int64_t step;             // bytes the slice start advances per stage
+
+    // X(r, k): KMAJOR -> X[r*ld + k], else X[k*ld + r]; rows [r0, r0+128) of R.
+    __device__ void init(const float *x, int64_t ld, int64_t R, int64_t r0, int64_t span, int wave,
+                         int lane) {
+        base = x;
+        bytes = span * 4;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int P = (wave * PER_WAVE + i) * 64 + lane;
+            if (KMAJOR) {
+                const int row = P >> 2;
+                const int c = (P & 3) ^ ((row >> 2) & 3);
+                kl[i] = 4 * c;
+                const int64_t gr = r0 + row;
+                voff[i] = gr < R ? uint32_t((gr * ld + 4 * c) * 4) : dma::OOB;
+            } else {
+                const int k = P >> 5;
+                const int64_t gr = r0 + 4 * (P & 31);
+                kl[i] = k;
+                voff[i] = gr < R ? uint32_t((k * ld + gr) * 4) : dma::OOB;
+            }
+        }
+        step = KMAJOR ? int64_t(BK) * 4 : int64_t(BK) * ld * 4;
+    }
+
+    // The loads of stage `stage` (k from stage*BK) into the panel at LDS
+    // address `lds`.
+    __device__ void issue(uint32_t lds, int64_t stage, int64_t K, int wave) const {
+        const int64_t off = dma::uniform(stage * step);
+        const dma::u32x4 rs =
+            dma::raw_buffer(static_cast<uint64_t>(dma::uniform(reinterpret_cast<int64_t>(base) + off)),
+                            static_cast<uint32_t>(dma::uniform(bytes - off)));
+        const int64_t kleft = K - stage * BK;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const uint32_t v = (kleft < BK && kl[i] >= kleft) ? dma::OOB : voff[i];
+            dma::direct_load16(rs, lds + (wave * PER_WAVE + i) * 1024, v);
+        }
+    }
+};
+
+// Fast path for aligned operands: the loads of stage s + 1 land in one LDS
+// buffer while the matrix instructions of stage s read the other, without
+// passing through registers, which leaves the registers for double-buffered
+// operand fragments: the reads of a stage's second k group are in flight
+// during its first group's matrix instructions, and the reads of the next
+// stage's first group (issued right after the barrier) during its second.
+// One barrier per stage: it follows this wave's wait for the next stage's
+// loads and for its own last reads of the current buffer, so after it every
+// wave's data has landed and the current buffer is free to be refilled with
+// stage s + 2.
+template <bool A_KMAJOR, bool B_KMAJOR>
+__global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p) {
+    __shared__ __attribute__((aligned(1024))) float smem[2][2][PANEL];  // [buffer][A, B]
+    using PA = Panel<A_KMAJOR>;
+    using PB = Panel<B_KMAJOR>;
+
+    TileCoord t = tile_of(p.grid, blockIdx.x);
+    t.batch = dma::uniform(t.batch);
+    t.tm = dma::uniform(t.tm);
+    t.tn = dma::uniform(t.tn);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int idx = lane & 31, half = lane >> 5;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+
+    DmaPanel<A_KMAJOR> da;
+    DmaPanel<B_KMAJOR> db;
+    const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
+    const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
+    da.init(p.A + t.batch * p.sA, p.lda, p.M, m0, span_a, wave, lane);
+    db.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, span_b, wave, lane);
+    auto addr = [&](int buf, int op) {
+        return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS float *)&smem[buf][op][0]));
+    };
+    auto issue = [&](int buf, int64_t stage) {
+        da.issue(addr(buf, 0), stage, p.K, wave);
+        db.issue(addr(buf, 1), stage, p.K, wave);
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    float fa[2][2][4], fb[2][2][4];  // [k group slot][tile][instruction]
+    auto read = [&](int buf, int g, int slot) {
+        PA::frag(smem[buf][0], wm * 64, g, idx, half, fa[slot]);
+        PB::frag(smem[buf][1], wn * 64, g, idx, half, fb[slot]);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[slot][j][e], fa[slot][i][e],
+                                                                     acc[i][j], 0, 0, 0);
+    };
+
+    const int64_t steps = (p.K + BK - 1) / BK;
+    issue(0, 0);
+    if (steps > 1) {
+        issue(1, 1);
+        dma::wait_vmcnt<2 * DmaPanel<A_KMAJOR>::PER_WAVE>();
+    } else {
+        dma::wait_vmcnt<0>();
+    }
+    __syncthreads();
+    read(0, 0, 0);
+    for (int64_t s = 0; s + 1 < steps; ++s) {
+        const int buf = s & 1;
+        read(buf, 1, 1);
+        mfmas(0);
+        dma::wait_vmcnt<0>();
+        dma::wait_lgkmcnt0();
+        __syncthreads();
+        if (s + 2 < steps) issue(buf, s + 2);
+        read(buf ^ 1, 0, 0);
+        mfmas(1);
+    }
+    read((steps - 1) & 1, 1, 1);
+    mfmas(0);
+    mfmas(1);
+
+    float *C = p.C + t.batch * p.sC;
+    store_c<A_KMAJOR, B_KMAJOR>(p, acc, C, m0 + wm * 64, n0 + wn * 64, idx, half);
+}
+
+template <bool AK, bool BK_>
+hipError_t launch(const SgemmArgs &a0, bool direct, hipStream_t stream) {
+    SgemmArgs a = a0;
+    void *args[] = {&a};
+    const void *fn = direct ? reinterpret_cast<const void *>(&sgemm_mfma_dma_kernel<AK, BK_>)
+                            : reinterpret_cast<const void *>(&sgemm_mfma_kernel<AK, BK_>);
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.grid.count())), dim3(THREADS), args, 0,
+                           stream);
+}
+
+int64_t span_of(int64_t rows, int64_t cols, bool row_contig, int64_t ld) {
+    // rows x cols with `cols` contiguous when row_contig
+    return row_contig ? (rows - 1) * ld + cols : (cols - 1) * ld + rows;
+}
+
+}  // namespace
+
+// The direct-load kernel needs 16-byte aligned operand rows (base, leading
+// dimension and batch stride), a contiguous extent that is a multiple of 4
+// (so every 16-byte chunk is wholly inside or outside the operand) and
+// operand slices below 2^31 bytes (32-bit buffer offsets, with the
+// out-of-range offset beyond every slice).
+bool sgemm_dma_eligible(const Problem &p) {
+    if (p.in != Elem::F32) return false;
+    const int64_t sa = p.batch > 1 ? p.sA : 0, sb = p.batch > 1 ? p.sB : 0;
+    if (!vec16_ok(p.A, p.lda, sa, 4) || !vec16_ok(p.B, p.ldb, sb, 4)) return false;
+    if ((p.a_kmajor ? p.K : p.M) % 4 || (p.b_kmajor ? p.K : p.N) % 4) return false;
+    const int64_t limit = int64_t(1) << 31;
+    return 4 * span_of(p.M, p.K, p.a_kmajor, p.lda) < limit &&
+           4 * span_of(p.K, p.N, !p.b_kmajor, p.ldb) < limit;
+}
+
+namespace {
+
+SgemmArgs make_args(const Problem &p) {
+    SgemmArgs a{};
+    a.M = p.M;
+    a.N = p.N;
+    a.K = p.K;
+    a.alpha = p.alpha;
+    a.beta = p.beta;
+    a.A = static_cast<const float *>(p.A);
+    a.B = static_cast<const float *>(p.B);
+    a.C = static_cast<float *>(p.C);
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.sA = p.batch > 1 ? p.sA : 0;
+    a.sB = p.batch > 1 ? p.sB : 0;
+    a.sC = p.batch > 1 ? p.sC : 0;
+    a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, 8, 8};
+    a.vec_a = vec16_ok(p.A, p.lda, a.sA, 4);
+    a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 4);
+    a.vec_c = vec16_ok(p.C, p.ldc, a.sC, 4);
+    return a;
+}
+
+hipError_t launch_any(const Problem &p, bool direct, hipStream_t stream) {
+    const SgemmArgs a = make_args(p);
+    if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (p.a_kmajor)
+        return p.b_kmajor ? launch<true, true>(a, direct, stream)
+                          : launch<true, false>(a, direct, stream);
+    return p.b_kmajor ? launch<false, true>(a, direct, stream)
+                      : launch<false, false>(a, direct, stream);
+}
+
+}  // namespace
+
+hipError_t launch_sgemm_mfma(const Problem &p, hipStream_t stream) {
+    return launch_any(p, false, stream);
+}
+
+hipError_t launch_sgemm_dma(const Problem &p, hipStream_t stream) {
+    return launch_any(p, true, stream);
+}
+
+}  // namespace libgemm

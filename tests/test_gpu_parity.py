@@ -243,6 +243,42 @@ def test_general_kernel_forced_on_aligned_problem(monkeypatch):
     check(P("forced-general-bf16", "bf16", 512, 768, 320, beta=1.0), seed=33)
 
 
+# ------------------------------------------------------------------ fp32 kernels
+
+F32_DMA_SHAPES = [(4, 4, 4), (128, 128, 16), (132, 260, 20), (260, 132, 1000), (1000, 1028, 1004),
+                  (24, 4096, 512), (2048, 132, 68)]
+
+
+@pytest.mark.parametrize("shape", F32_DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_f32_direct_load_path_ragged_aligned(shape, orders):
+    # extents multiples of 4 but not of the 128 x 128 x 16 tile: the direct
+    # loads' range check and the last-stage k mask produce the edge zeros
+    M, N, K = shape
+    oa, ob = orders
+    check(P("dma-f32", "f32", M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob), seed=M + N + K)
+
+
+def test_f32_direct_load_path_batch_and_col_major_c():
+    check(P("dma-f32-batch", "f32", 260, 132, 200, beta=-1.0, batch=3), seed=51)
+    check(P("dma-f32-colC", "f32", 260, 132, 200, order_c=COL, beta=0.25), seed=52)
+    p = P("dma-f32-int", "f32", 264, 136, 4096, alpha=2.0, beta=1.0)
+    res, _ = check(p, host=_int_host(p, np.random.default_rng(53)))
+    assert res.max_err == 0.0
+
+
+@pytest.mark.parametrize("env", ["LIBGEMM_FORCE_GENERAL", "LIBGEMM_F32_VALU"])
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_f32_other_kernels_forced_on_aligned_problem(monkeypatch, env, orders):
+    # the aligned problem the direct-load kernel would take, through the
+    # register-staged matrix-core kernel and through the vector-ALU kernel
+    monkeypatch.setenv(env, "1")
+    oa, ob = orders
+    check(P(f"forced-{env}", "f32", 520, 392, 300, beta=1.0, order_a=oa, order_b=ob), seed=54)
+
+
 # ------------------------------------------------------------------ split-K path (few tiles, long K)
 
 SPLITK_SHAPES = [(16, 4096, 4096), (8, 8, 4096), (40, 1000, 1736), (256, 256, 8192), (24, 520, 512)]
