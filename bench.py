@@ -38,7 +38,8 @@ HBM_GBS = 8000.0
 HEADLINE = ["f32_4096", "bf16_4096", "f16_4096"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 # kernel family -> the source file that defines it (hashed to detect changes)
-KERNEL_SOURCE = {"sgemm_valu": "sgemm_valu.hip", "hgemm_mfma_dma": "hgemm_mfma_dma.hip",
+KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.hip",
+                 "sgemm_valu": "sgemm_valu.hip", "hgemm_mfma_dma": "hgemm_mfma_dma.hip",
                  "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip"}
 
 
@@ -70,17 +71,23 @@ def make_launch(p, bufs, stream):
 
 def kernel_family(p):
     """Which libgemm kernel serves a workload (the library's own selection
-    rule: bf16/fp16 problems whose contiguous extents, leading dimensions and
-    strides are multiples of 8 elements take a direct-load kernel; of those,
-    problems with fewer than 64 output tiles of 256 x 256 and K >= 512 split
-    K inside a workgroup)."""
-    if p.in_dtype == "f32":
-        return "sgemm_valu"
+    rule).  fp32: operands whose contiguous extents, leading dimensions and
+    strides are multiples of 4 elements take the direct-load matrix-core
+    kernel, others the register-staged one.  bf16/fp16: multiples of 8 take a
+    direct-load kernel; of those, problems with fewer than 64 output tiles of
+    256 x 256 and K >= 512 split K inside a workgroup.  LIBGEMM_F32_VALU and
+    LIBGEMM_FORCE_GENERAL override the choice as they do in the library."""
+    env = lambda k: os.environ.get(k, "")[:1] == "1"
     ext_a = p.K if p.order_a == 0 else p.M
     ext_b = p.N if p.order_b == 0 else p.K
-    ok = all(v % 8 == 0 for v in (ext_a, ext_b, p.lda, p.ldb)) and \
-        (p.batch <= 1 or (p.stride_a % 8 == 0 and p.stride_b % 8 == 0))
-    if not ok:
+    per = 4 if p.in_dtype == "f32" else 8
+    ok = all(v % per == 0 for v in (ext_a, ext_b, p.lda, p.ldb)) and \
+        (p.batch <= 1 or (p.stride_a % per == 0 and p.stride_b % per == 0))
+    if p.in_dtype == "f32":
+        if env("LIBGEMM_F32_VALU"):
+            return "sgemm_valu"
+        return "sgemm_mfma_dma" if ok and not env("LIBGEMM_FORCE_GENERAL") else "sgemm_mfma"
+    if not ok or env("LIBGEMM_FORCE_GENERAL"):
         return "hgemm_mfma"
     big_tiles = -(-p.M // 256) * -(-p.N // 256) * max(p.batch, 1)
     return "hgemm_splitk" if big_tiles < 64 and p.K >= 512 else "hgemm_mfma_dma"
@@ -150,8 +157,8 @@ def cpu_baseline(problems, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -223,8 +230,11 @@ def main():
         k = per_kernel[name]
         p = workloads.config(name)
         fam = kernel_family(p)
-        bound, peak = ("alu", PEAK_TFLOPS["f32"]) if p.in_dtype == "f32" else \
-            ("mfma", PEAK_TFLOPS[p.in_dtype])
+        # the vector-ALU fp32 kernel is bound by the FMA rate of the vector
+        # units; every other kernel by the matrix cores' rate for its dtype
+        # (MI355X publishes the same 157.3 TF/s for both fp32 units)
+        bound = "alu" if fam == "sgemm_valu" else "mfma"
+        peak = PEAK_TFLOPS[p.in_dtype]
         return {"kernel": f"{fam} {name}", "bound": bound, "achieved": k["tflops"],
                 "peak": peak, "unit": "TFLOP/s", "frac": round(k["tflops"] / peak, 4),
                 "traffic": measured_traffic(fam, name)}
