@@ -10,7 +10,11 @@ each GEMM's own TFLOPS and fraction of MI355X's dense peak for its dtype,
 from HIP events recorded on the stream the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-context] [--copy-calibration MiB]
+                       [--no-cpu-baseline] [--no-context] [--no-rotate]
+                       [--copy-calibration MiB]
+Each kernel cycles through at least three copies of its buffers, enough that
+their footprint exceeds twice the 256 MB MALL, so inputs come from HBM;
+--no-rotate reuses one set (the warm-cache figure).
 --workload runs a single named workload (see workloads.CONFIGS) instead of
 the headline step, for profiling.  --copy-calibration runs only a plain
 device-to-device copy of the given size (the reference kernel against which
@@ -40,7 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 # kernel family -> the source file that defines it (hashed to detect changes)
 KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.hip",
                  "sgemm_valu": "sgemm_valu.hip", "hgemm_mfma_dma": "hgemm_mfma_dma.hip",
-                 "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip"}
+                 "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip",
+                 "sgemm_splitk": "sgemm_splitk.hip"}
 
 
 def log(*a):
@@ -56,16 +61,37 @@ def device_buffers(p, torch):
             torch.from_numpy(c.view(cview)).to("cuda"))
 
 
-def make_launch(p, bufs, stream):
+# Each kernel cycles through enough copies of its buffers that their combined
+# footprint exceeds twice the 256 MB Infinity Cache (MALL), so a launch finds
+# its inputs in HBM rather than left in the MALL by the previous launch.
+ROTATE_BYTES = 600_000_000
+MIN_SETS, MAX_SETS = 3, 16
+
+
+def buffer_sets(bufs, n):
+    """`bufs` plus n - 1 device copies of it (same values, other addresses)."""
+    return [bufs] + [tuple(t.clone() for t in bufs) for _ in range(n - 1)]
+
+
+def sets_needed(bufs, rotate):
+    if not rotate:
+        return 1
+    nbytes = sum(t.numel() * t.element_size() for t in bufs)
+    return min(MAX_SETS, max(MIN_SETS, -(-ROTATE_BYTES // nbytes)))
+
+
+def make_launch(p, sets, stream):
+    """A callable that runs the GEMM on the next buffer set in turn."""
     from dense_gemm_optimisation_amd import binding
-    da, db, dc = bufs
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
-    args = (p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a, db.data_ptr(),
-            p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch, p.stride_a,
-            p.stride_b, p.stride_c, stream.cuda_stream)
+    argsets = [(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a, db.data_ptr(),
+                p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch,
+                p.stride_a, p.stride_b, p.stride_c, stream.cuda_stream) for da, db, dc in sets]
+    turn = [0]
 
     def launch():
-        binding.gemm(*args)
+        binding.gemm(*argsets[turn[0]])
+        turn[0] = (turn[0] + 1) % len(argsets)
     return launch
 
 
@@ -73,10 +99,12 @@ def kernel_family(p):
     """Which libgemm kernel serves a workload (the library's own selection
     rule).  fp32: operands whose contiguous extents, leading dimensions and
     strides are multiples of 4 elements take the direct-load matrix-core
-    kernel, others the register-staged one.  bf16/fp16: multiples of 8 take a
-    direct-load kernel; of those, problems with fewer than 64 output tiles of
-    256 x 256 and K >= 512 split K inside a workgroup.  LIBGEMM_F32_VALU and
-    LIBGEMM_FORCE_GENERAL override the choice as they do in the library."""
+    kernel, others the register-staged one; of the former, problems with fewer
+    than 160 output tiles of 128 x 128 and K >= 256 split K inside a
+    workgroup.  bf16/fp16: multiples of 8 take a direct-load kernel; of those,
+    problems with fewer than 64 output tiles of 256 x 256 and K >= 512 split K
+    inside a workgroup.  LIBGEMM_F32_VALU, LIBGEMM_FORCE_GENERAL and
+    LIBGEMM_NO_SPLITK override the choice as they do in the library."""
     env = lambda k: os.environ.get(k, "")[:1] == "1"
     ext_a = p.K if p.order_a == 0 else p.M
     ext_b = p.N if p.order_b == 0 else p.K
@@ -86,11 +114,16 @@ def kernel_family(p):
     if p.in_dtype == "f32":
         if env("LIBGEMM_F32_VALU"):
             return "sgemm_valu"
-        return "sgemm_mfma_dma" if ok and not env("LIBGEMM_FORCE_GENERAL") else "sgemm_mfma"
+        if not ok or env("LIBGEMM_FORCE_GENERAL"):
+            return "sgemm_mfma"
+        tiles = -(-p.M // 128) * -(-p.N // 128) * max(p.batch, 1)
+        split = tiles < 160 and p.K >= 256 and not env("LIBGEMM_NO_SPLITK")
+        return "sgemm_splitk" if split else "sgemm_mfma_dma"
     if not ok or env("LIBGEMM_FORCE_GENERAL"):
         return "hgemm_mfma"
     big_tiles = -(-p.M // 256) * -(-p.N // 256) * max(p.batch, 1)
-    return "hgemm_splitk" if big_tiles < 64 and p.K >= 512 else "hgemm_mfma_dma"
+    split = big_tiles < 64 and p.K >= 512 and not env("LIBGEMM_NO_SPLITK")
+    return "hgemm_splitk" if split else "hgemm_mfma_dma"
 
 
 def source_hash(family):
@@ -159,6 +192,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="reuse one buffer set per kernel (inputs may stay in the MALL)")
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -181,12 +216,14 @@ def main():
     names = HEADLINE if args.workload == "headline" else [args.workload]
     problems = [workloads.config(n) for n in names]
     stream = torch.cuda.Stream()  # default priority
-    launches = []
+    launches, nsets = [], {}
     with torch.cuda.stream(stream):
         for p in problems:
             log(f"[bench] preparing {p.name}: {p.note}")
             bufs = device_buffers(p, torch)
-            launches.append((p, bufs, make_launch(p, bufs, stream)))
+            sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
+            nsets[p.name] = len(sets)
+            launches.append((p, sets, make_launch(p, sets, stream)))
     torch.cuda.synchronize()
 
     # warmup
@@ -247,7 +284,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "+".join(p.in_dtype for p in problems),
         "data": "synthetic",
         "config": {"workload": " + ".join(f"{p.name} ({p.note})" for p in problems),
-                   "global_batch": 1, "parallelism": "none (1 GPU)"},
+                   "global_batch": 1, "parallelism": "none (1 GPU)",
+                   "buffer_sets": nsets},
         "per_kernel": per_kernel,
         "roofline": roof(dominant),
         "roofline_all": [roof(n) for n in per_kernel],

@@ -50,12 +50,29 @@ bool force_general() {
     return v != nullptr && v[0] == '1';
 }
 
+// LIBGEMM_NO_SPLITK=1 keeps few-tile problems on the main kernels instead
+// of the split-K ones (used to test the two against each other).
+bool no_splitk() {
+    const char *v = std::getenv("LIBGEMM_NO_SPLITK");
+    return v != nullptr && v[0] == '1';
+}
+
 // LIBGEMM_F32_VALU=1 routes fp32 calls to the register-tiled vector-ALU
 // kernel instead of the matrix-core one (used to test the two against each
 // other and to time the vector-ALU design).
 bool f32_valu() {
     const char *v = std::getenv("LIBGEMM_F32_VALU");
     return v != nullptr && v[0] == '1';
+}
+
+// fp32 kernel choice: split-K for few-tile problems, the direct-load kernel
+// for aligned operands, the register-staged kernel for everything else.
+hipError_t launch_f32(const Problem &p, hipStream_t stream) {
+    if (f32_valu()) return launch_sgemm(p, stream);
+    if (force_general()) return launch_sgemm_mfma(p, stream);
+    if (sgemm_splitk_eligible(p) && !no_splitk()) return launch_sgemm_splitk(p, stream);
+    if (sgemm_dma_eligible(p)) return launch_sgemm_dma(p, stream);
+    return launch_sgemm_mfma(p, stream);
 }
 
 gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
@@ -135,10 +152,8 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
     if (!reads_ab)
         err = launch_scale(p, stream);
     else if (in == Elem::F32)
-        err = f32_valu()                                    ? launch_sgemm(p, stream)
-              : sgemm_dma_eligible(p) && !force_general() ? launch_sgemm_dma(p, stream)
-                                                          : launch_sgemm_mfma(p, stream);
-    else if (hgemm_splitk_eligible(p) && !force_general())
+        err = launch_f32(p, stream);
+    else if (hgemm_splitk_eligible(p) && !force_general() && !no_splitk())
         err = launch_hgemm_splitk(p, stream);
     else if (hgemm_dma_eligible(p) && !force_general())
         err = launch_hgemm_dma(p, stream);

@@ -47,6 +47,10 @@ hipError_t launch_sgemm_mfma(const Problem &p, hipStream_t stream);  // fp32 on 
 // where sgemm_dma_eligible() holds (aligned operands, extents multiple of 4).
 bool sgemm_dma_eligible(const Problem &p);
 hipError_t launch_sgemm_dma(const Problem &p, hipStream_t stream);
+// fp32 split-K inside a workgroup, for problems with few output tiles
+// (sgemm_splitk_eligible()).
+bool sgemm_splitk_eligible(const Problem &p);
+hipError_t launch_sgemm_splitk(const Problem &p, hipStream_t stream);
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA, any shape
 // bf16/fp16 on MFMA with direct global->LDS loads; only for problems where
 // hgemm_dma_eligible() holds (aligned operands, extents multiple of 8).

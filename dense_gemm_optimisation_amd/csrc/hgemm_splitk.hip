@@ -26,6 +26,7 @@
 //     beta == 0) and rounds to the output type to nearest-even.
 #include "gemm_problem.hpp"
 #include "lds_dma.hpp"
+#include "tile_schedule.hpp"
 
 namespace libgemm {
 namespace {
@@ -161,9 +162,12 @@ template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR>
 __global__ __launch_bounds__(WAVES * 64, 1) void hgemm_splitk_kernel(SplitArgs p) {
     __shared__ __attribute__((aligned(1024))) char smem[WAVES * WAVE_LDS];
 
+    // consecutive tiles (which share cache lines of B when it is N-contiguous)
+    // go to one XCD
     const int64_t per_batch = p.tiles_m * p.tiles_n;
-    const int64_t batch = blockIdx.x / per_batch;
-    const int64_t local = blockIdx.x - batch * per_batch;
+    const int64_t id = xcd_remap(blockIdx.x, gridDim.x, 8);
+    const int64_t batch = id / per_batch;
+    const int64_t local = id - batch * per_batch;
     const int64_t m0 = (local / p.tiles_n) * TILE, n0 = (local % p.tiles_n) * TILE;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -222,9 +222,11 @@ DMA_SHAPES = [(8, 8, 8), (256, 256, 64), (264, 520, 72), (512, 256, 128), (1000,
 @pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
                          ids=lambda o: "%d%d" % o)
-def test_direct_load_path_ragged_aligned(dt, shape, orders):
+def test_direct_load_path_ragged_aligned(monkeypatch, dt, shape, orders):
     # extents multiples of 8 but not of the 256 x 256 x 64 tile: the direct
     # loads' range check and the last-stage k mask produce the edge zeros
+    # (few-tile shapes kept off the split-K kernel)
+    monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
     M, N, K = shape
     oa, ob = orders
     check(P(f"dma-{dt}", dt, M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob),
@@ -252,15 +254,18 @@ F32_DMA_SHAPES = [(4, 4, 4), (128, 128, 16), (132, 260, 20), (260, 132, 1000), (
 @pytest.mark.parametrize("shape", F32_DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
                          ids=lambda o: "%d%d" % o)
-def test_f32_direct_load_path_ragged_aligned(shape, orders):
+def test_f32_direct_load_path_ragged_aligned(monkeypatch, shape, orders):
     # extents multiples of 4 but not of the 128 x 128 x 16 tile: the direct
     # loads' range check and the last-stage k mask produce the edge zeros
+    # (few-tile shapes kept off the split-K kernel)
+    monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
     M, N, K = shape
     oa, ob = orders
     check(P("dma-f32", "f32", M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob), seed=M + N + K)
 
 
-def test_f32_direct_load_path_batch_and_col_major_c():
+def test_f32_direct_load_path_batch_and_col_major_c(monkeypatch):
+    monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
     check(P("dma-f32-batch", "f32", 260, 132, 200, beta=-1.0, batch=3), seed=51)
     check(P("dma-f32-colC", "f32", 260, 132, 200, order_c=COL, beta=0.25), seed=52)
     p = P("dma-f32-int", "f32", 264, 136, 4096, alpha=2.0, beta=1.0)
@@ -280,6 +285,32 @@ def test_f32_other_kernels_forced_on_aligned_problem(monkeypatch, env, orders):
 
 
 # ------------------------------------------------------------------ split-K path (few tiles, long K)
+
+F32_SPLITK_SHAPES = [(256, 256, 256), (16, 4096, 4096), (8, 8, 4096), (40, 1000, 1736),
+                     (260, 132, 512), (24, 520, 300), (1000, 1028, 1004)]
+
+
+@pytest.mark.parametrize("shape", F32_SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_f32_splitk_path(shape, orders):
+    # under 128 tiles of 128 x 128 and K >= 256: the workgroup splits K eight
+    # ways (slices ragged against K where 8*32 does not divide it)
+    M, N, K = shape
+    oa, ob = orders
+    big = M * N * K > 100_000_000
+    check(P("splitk-f32", "f32", M, N, K, alpha=0.75, beta=-0.5, order_a=oa, order_b=ob),
+          seed=M + 5 * N + K, sample="auto" if big else None)
+
+
+def test_f32_splitk_batch_col_major_c_and_integers():
+    check(P("splitk-f32-batch", "f32", 24, 520, 2048, beta=1.0, batch=3), seed=61)
+    check(P("splitk-f32-colC", "f32", 520, 24, 2048, order_c=COL, beta=0.5), seed=62)
+    # integer inputs: the fixed-order reduction of the slices is exact
+    p = P("splitk-f32-int", "f32", 16, 264, 4096, alpha=2.0, beta=1.0)
+    res, _ = check(p, host=_int_host(p, np.random.default_rng(63)))
+    assert res.max_err == 0.0
+
 
 SPLITK_SHAPES = [(16, 4096, 4096), (8, 8, 4096), (40, 1000, 1736), (256, 256, 8192), (24, 520, 512)]
 
