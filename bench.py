@@ -45,7 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.hip",
                  "sgemm_valu": "sgemm_valu.hip", "hgemm_mfma_dma": "hgemm_mfma_dma.hip",
                  "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip",
-                 "sgemm_splitk": "sgemm_splitk.hip"}
+                 "sgemm_splitk": "sgemm_splitk.hip", "gemm_skinny": "gemm_skinny.hip",
+                 "scale": "scale.hip"}
 
 
 def log(*a):
@@ -95,35 +96,16 @@ def make_launch(p, sets, stream):
     return launch
 
 
-def kernel_family(p):
-    """Which libgemm kernel serves a workload (the library's own selection
-    rule).  fp32: operands whose contiguous extents, leading dimensions and
-    strides are multiples of 4 elements take the direct-load matrix-core
-    kernel, others the register-staged one; of the former, problems with fewer
-    than 160 output tiles of 128 x 128 and K >= 256 split K inside a
-    workgroup.  bf16/fp16: multiples of 8 take a direct-load kernel; of those,
-    problems with fewer than 64 output tiles of 256 x 256 and K >= 512 split K
-    inside a workgroup.  LIBGEMM_F32_VALU, LIBGEMM_FORCE_GENERAL and
-    LIBGEMM_NO_SPLITK override the choice as they do in the library."""
-    env = lambda k: os.environ.get(k, "")[:1] == "1"
-    ext_a = p.K if p.order_a == 0 else p.M
-    ext_b = p.N if p.order_b == 0 else p.K
-    per = 4 if p.in_dtype == "f32" else 8
-    ok = all(v % per == 0 for v in (ext_a, ext_b, p.lda, p.ldb)) and \
-        (p.batch <= 1 or (p.stride_a % per == 0 and p.stride_b % per == 0))
-    if p.in_dtype == "f32":
-        if env("LIBGEMM_F32_VALU"):
-            return "sgemm_valu"
-        if not ok or env("LIBGEMM_FORCE_GENERAL"):
-            return "sgemm_mfma"
-        tiles = -(-p.M // 128) * -(-p.N // 128) * max(p.batch, 1)
-        split = tiles < 160 and p.K >= 256 and not env("LIBGEMM_NO_SPLITK")
-        return "sgemm_splitk" if split else "sgemm_mfma_dma"
-    if not ok or env("LIBGEMM_FORCE_GENERAL"):
-        return "hgemm_mfma"
-    big_tiles = -(-p.M // 256) * -(-p.N // 256) * max(p.batch, 1)
-    split = big_tiles < 64 and p.K >= 512 and not env("LIBGEMM_NO_SPLITK")
-    return "hgemm_splitk" if split else "hgemm_mfma_dma"
+def kernel_family(p, bufs):
+    """The kernel libgemm launches for workload p on these device buffers
+    (asked of the library itself, so the answer follows its dispatch rules
+    and the buffers' actual alignment)."""
+    from dense_gemm_optimisation_amd import binding
+    da, db, dc = bufs
+    c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
+    return binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a,
+                               db.data_ptr(), p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc,
+                               p.order_c, c_dt, p.batch, p.stride_a, p.stride_b, p.stride_c)
 
 
 def source_hash(family):
@@ -216,13 +198,14 @@ def main():
     names = HEADLINE if args.workload == "headline" else [args.workload]
     problems = [workloads.config(n) for n in names]
     stream = torch.cuda.Stream()  # default priority
-    launches, nsets = [], {}
+    launches, nsets, families = [], {}, {}
     with torch.cuda.stream(stream):
         for p in problems:
             log(f"[bench] preparing {p.name}: {p.note}")
             bufs = device_buffers(p, torch)
             sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
             nsets[p.name] = len(sets)
+            families[p.name] = kernel_family(p, bufs)
             launches.append((p, sets, make_launch(p, sets, stream)))
     torch.cuda.synchronize()
 
@@ -266,7 +249,7 @@ def main():
     def roof(name):
         k = per_kernel[name]
         p = workloads.config(name)
-        fam = kernel_family(p)
+        fam = families[name]
         # the vector-ALU fp32 kernel is bound by the FMA rate of the vector
         # units; every other kernel by the matrix cores' rate for its dtype
         # (MI355X publishes the same 157.3 TF/s for both fp32 units)

@@ -50,6 +50,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_status_string.argtypes = [i32]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_abi_version.restype = i32
+        lib.gemm_kernel_name.argtypes = [i32] + common + [i32, i64, i64, i64, i64]
+        lib.gemm_kernel_name.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -105,6 +107,17 @@ def gemm_f16(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, ord
 
 
 _ENTRY = {"f32": gemm_f32, "bf16": gemm_bf16, "f16": gemm_f16}
+_INPUT = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0):
+    """The kernel the GEMM call with these arguments would launch ("" for an
+    empty problem, None for invalid arguments); host only, no GPU needed."""
+    name = library().gemm_kernel_name(_INPUT[in_dtype], M, N, K, alpha, A, lda, order_a, B, ldb,
+                                      order_b, beta, C, ldc, order_c, c_dtype, batch, stride_a,
+                                      stride_b, stride_c)
+    return None if name is None else name.decode()
 
 
 def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,

@@ -50,8 +50,8 @@ bool force_general() {
     return v != nullptr && v[0] == '1';
 }
 
-// LIBGEMM_NO_SPLITK=1 keeps few-tile problems on the main kernels instead
-// of the split-K ones (used to test the two against each other).
+// LIBGEMM_NO_SPLITK=1 keeps few-tile and skinny problems on the main
+// kernels instead of the split-K ones (used to test them against each other).
 bool no_splitk() {
     const char *v = std::getenv("LIBGEMM_NO_SPLITK");
     return v != nullptr && v[0] == '1';
@@ -65,20 +65,78 @@ bool f32_valu() {
     return v != nullptr && v[0] == '1';
 }
 
-// fp32 kernel choice: split-K for few-tile problems, the direct-load kernel
-// for aligned operands, the register-staged kernel for everything else.
-hipError_t launch_f32(const Problem &p, hipStream_t stream) {
-    if (f32_valu()) return launch_sgemm(p, stream);
-    if (force_general()) return launch_sgemm_mfma(p, stream);
-    if (sgemm_splitk_eligible(p) && !no_splitk()) return launch_sgemm_splitk(p, stream);
-    if (sgemm_dma_eligible(p)) return launch_sgemm_dma(p, stream);
-    return launch_sgemm_mfma(p, stream);
+// The kernels a call can end in.
+enum class Kernel {
+    None,        // empty problem: nothing to do
+    Scale,       // C <- beta*C only
+    SgemmValu,   // fp32, vector ALUs (opt-in)
+    SgemmMfma,   // fp32, matrix cores, any shape
+    SgemmDma,    // fp32, matrix cores, direct loads
+    SgemmSplitk, // fp32, few tiles: split-K inside a workgroup
+    Skinny,      // any type, at most 16 rows of C
+    HgemmMfma,   // bf16/fp16, any shape
+    HgemmDma,    // bf16/fp16, direct loads
+    HgemmSplitk, // bf16/fp16, few tiles: split-K inside a workgroup
+};
+
+const char *kernel_name(Kernel k) {
+    switch (k) {
+    case Kernel::None: return "";
+    case Kernel::Scale: return "scale";
+    case Kernel::SgemmValu: return "sgemm_valu";
+    case Kernel::SgemmMfma: return "sgemm_mfma";
+    case Kernel::SgemmDma: return "sgemm_mfma_dma";
+    case Kernel::SgemmSplitk: return "sgemm_splitk";
+    case Kernel::Skinny: return "gemm_skinny";
+    case Kernel::HgemmMfma: return "hgemm_mfma";
+    case Kernel::HgemmDma: return "hgemm_mfma_dma";
+    case Kernel::HgemmSplitk: return "hgemm_splitk";
+    }
+    return "";
 }
 
-gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
-                  const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
-                  float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
-                  int64_t strideB, int64_t strideC, hipStream_t stream) {
+// Kernel choice for a canonical problem that reads A and B: the skinny
+// kernel for at most 16 rows of C, split-K for other few-tile problems, the
+// direct-load kernel for aligned operands, the register-staged kernel for
+// everything else.
+Kernel choose(const Problem &p) {
+    const bool splits = !force_general() && !no_splitk();
+    if (p.in == Elem::F32) {
+        if (f32_valu()) return Kernel::SgemmValu;
+        if (force_general()) return Kernel::SgemmMfma;
+        if (splits && skinny_eligible(p)) return Kernel::Skinny;
+        if (splits && sgemm_splitk_eligible(p)) return Kernel::SgemmSplitk;
+        return sgemm_dma_eligible(p) ? Kernel::SgemmDma : Kernel::SgemmMfma;
+    }
+    if (splits && skinny_eligible(p)) return Kernel::Skinny;
+    if (splits && hgemm_splitk_eligible(p)) return Kernel::HgemmSplitk;
+    if (!force_general() && hgemm_dma_eligible(p)) return Kernel::HgemmDma;
+    return Kernel::HgemmMfma;
+}
+
+hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
+    switch (k) {
+    case Kernel::None: return hipSuccess;
+    case Kernel::Scale: return launch_scale(p, stream);
+    case Kernel::SgemmValu: return launch_sgemm(p, stream);
+    case Kernel::SgemmMfma: return launch_sgemm_mfma(p, stream);
+    case Kernel::SgemmDma: return launch_sgemm_dma(p, stream);
+    case Kernel::SgemmSplitk: return launch_sgemm_splitk(p, stream);
+    case Kernel::Skinny: return launch_skinny(p, stream);
+    case Kernel::HgemmMfma: return launch_hgemm(p, stream);
+    case Kernel::HgemmDma: return launch_hgemm_dma(p, stream);
+    case Kernel::HgemmSplitk: return launch_hgemm_splitk(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Validates a call and builds its canonical problem and kernel choice.  No
+// HIP call is made.
+gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
+                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
+                   float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
+                   int64_t strideB, int64_t strideC, Problem &p, Kernel &kernel) {
+    kernel = Kernel::None;
     // ---- argument checks (no HIP call before this block is done)
     if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
     if (strideA < 0 || strideB < 0 || strideC < 0) return GEMM_ERR_INVALID_ARG;
@@ -93,7 +151,7 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
     if (too_big(M, N) || too_big(M * N, batch) || too_big(M, K) || too_big(K, N))
         return GEMM_ERR_INVALID_ARG;
 
-    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;  // kernel stays None
 
     const bool reads_ab = K > 0 && alpha != 0.0f;
     const int ein = elem_bytes(in), eout = elem_bytes(out);
@@ -113,7 +171,7 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
     }
 
     // ---- canonical problem: row-major C
-    Problem p{};
+    p = Problem{};
     p.K = K;
     p.alpha = alpha;
     p.beta = beta;
@@ -148,17 +206,20 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
         p.sB = strideA;
     }
 
-    hipError_t err;
-    if (!reads_ab)
-        err = launch_scale(p, stream);
-    else if (in == Elem::F32)
-        err = launch_f32(p, stream);
-    else if (hgemm_splitk_eligible(p) && !force_general() && !no_splitk())
-        err = launch_hgemm_splitk(p, stream);
-    else if (hgemm_dma_eligible(p) && !force_general())
-        err = launch_hgemm_dma(p, stream);
-    else
-        err = launch_hgemm(p, stream);
+    kernel = reads_ab ? choose(p) : Kernel::Scale;
+    return GEMM_OK;
+}
+
+gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
+                  const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
+                  float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
+                  int64_t strideB, int64_t strideC, hipStream_t stream) {
+    Problem p;
+    Kernel k;
+    const gemm_status_t st = plan(in, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C,
+                                  ldc, orderC, batch, strideA, strideB, strideC, p, k);
+    if (st != GEMM_OK || k == Kernel::None) return st;
+    const hipError_t err = launch(k, p, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -208,5 +269,29 @@ const char *gemm_status_string(gemm_status_t status) {
 }
 
 int gemm_abi_version(void) { return 1; }
+
+const char *gemm_kernel_name(gemm_input_t in, int64_t M, int64_t N, int64_t K, float alpha,
+                             const void *A, int64_t lda, gemm_order_t orderA, const void *B,
+                             int64_t ldb, gemm_order_t orderB, float beta, const void *C,
+                             int64_t ldc, gemm_order_t orderC, gemm_dtype_t c_dtype, int64_t batch,
+                             int64_t strideA, int64_t strideB, int64_t strideC) {
+    Elem ein;
+    if (in == GEMM_INPUT_F32)
+        ein = Elem::F32;
+    else if (in == GEMM_INPUT_BF16)
+        ein = Elem::BF16;
+    else if (in == GEMM_INPUT_F16)
+        ein = Elem::F16;
+    else
+        return nullptr;
+    if (ein != Elem::F32 && c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return nullptr;
+    Problem p;
+    Kernel k;
+    const gemm_status_t st =
+        plan(ein, ein == Elem::F32 ? Elem::F32 : out_type(ein, c_dtype), M, N, K, alpha, A, lda,
+             orderA, B, ldb, orderB, beta, const_cast<void *>(C), ldc, orderC, batch, strideA,
+             strideB, strideC, p, k);
+    return st == GEMM_OK ? kernel_name(k) : nullptr;
+}
 
 }  // extern "C"

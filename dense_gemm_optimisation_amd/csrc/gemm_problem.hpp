@@ -60,6 +60,10 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream);
 // and a long K (hgemm_splitk_eligible()).
 bool hgemm_splitk_eligible(const Problem &p);
 hipError_t launch_hgemm_splitk(const Problem &p, hipStream_t stream);
+// Any input type, at most 16 rows of C: B streamed at HBM rate, split-K
+// inside a workgroup (skinny_eligible()).
+bool skinny_eligible(const Problem &p);
+hipError_t launch_skinny(const Problem &p, hipStream_t stream);
 hipError_t launch_scale(const Problem &p, hipStream_t stream);  // C <- beta*C only
 
 }  // namespace libgemm

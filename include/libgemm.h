@@ -13,10 +13,13 @@
  * column-major-only convention of that library.
  *
  * Entry points
- *   gemm_f32   fp32 inputs, fp32 output, fp32 arithmetic on the vector ALUs.
+ *   gemm_f32   fp32 inputs, fp32 output, fp32 arithmetic (on the matrix cores;
+ *              the vector-ALU kernel when LIBGEMM_F32_VALU=1 is set).
  *   gemm_bf16  bf16 inputs, fp32 accumulation on the matrix cores, output in
  *              bf16 (c_dtype = GEMM_DTYPE_SAME) or fp32 (GEMM_DTYPE_F32).
  *   gemm_f16   the same for IEEE fp16 inputs.
+ *   gemm_kernel_name  which kernel a GEMM call with the given arguments would
+ *              launch (host only; for tests and profiling).
  *
  * Layout
  *   Each matrix has its own order.  Element (i, k) of A is at
@@ -81,6 +84,12 @@ typedef enum gemm_dtype_t {
     GEMM_DTYPE_F32 = 1   /* output in fp32 */
 } gemm_dtype_t;
 
+typedef enum gemm_input_t {
+    GEMM_INPUT_F32 = 0,
+    GEMM_INPUT_BF16 = 1,
+    GEMM_INPUT_F16 = 2
+} gemm_input_t;
+
 typedef enum gemm_status_t {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_ARG = -1,
@@ -121,6 +130,26 @@ const char *gemm_status_string(gemm_status_t status);
 
 /* Version of this interface; bumped on any incompatible change. */
 int gemm_abi_version(void);
+
+/* The kernel that gemm_f32 (in = GEMM_INPUT_F32; c_dtype is then ignored),
+ * gemm_bf16 or gemm_f16 would launch for the same arguments, as a static
+ * string: "sgemm_mfma_dma", "sgemm_mfma", "sgemm_splitk", "sgemm_valu",
+ * "hgemm_mfma_dma", "hgemm_mfma", "hgemm_splitk", "gemm_skinny" or "scale";
+ * "" when the call would return without launching anything (M, N or batch
+ * is 0); NULL when the arguments are invalid (the GEMM call would return an
+ * error status).  The choice depends on the shape, the orders, the
+ * alignment of the pointers, leading dimensions and strides, and the
+ * environment switches LIBGEMM_F32_VALU, LIBGEMM_FORCE_GENERAL and
+ * LIBGEMM_NO_SPLITK, exactly as in the GEMM calls.  Pointers are compared
+ * and tested for alignment but never dereferenced; no HIP call is made, so
+ * this works without a GPU. */
+const char *gemm_kernel_name(gemm_input_t in, int64_t M, int64_t N, int64_t K,
+                             float alpha, const void *A, int64_t lda,
+                             gemm_order_t orderA, const void *B, int64_t ldb,
+                             gemm_order_t orderB, float beta, const void *C,
+                             int64_t ldc, gemm_order_t orderC,
+                             gemm_dtype_t c_dtype, int64_t batch,
+                             int64_t strideA, int64_t strideB, int64_t strideC);
 
 #ifdef __cplusplus
 }

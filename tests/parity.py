@@ -27,7 +27,7 @@ import workloads
 from dense_gemm_optimisation_amd import binding
 
 TOL = {("f32", "f32"): 1e-4, ("bf16", "f32"): 1e-3, ("f16", "f32"): 1e-3}
-GUARD = 97  # guard elements before and after each buffer
+GUARD = 96  # guard elements before and after each buffer (keeps data 16-byte aligned)
 CANARY = {"f32": np.uint32(0x7FC0DEAD), "bf16": np.uint16(0x7FC1), "f16": np.uint16(0x7E1D)}
 TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -89,6 +89,7 @@ class Result:
     strict_fail: int = 0          # 16-bit elements beyond 2 ulp
     exempt: int = 0               # ... of which accepted as cancellations
     checked: int = 0
+    kernel: str = ""              # the kernel the library launched
     ok: bool = True
     why: str = ""
 
@@ -189,6 +190,9 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
                   dc.data_ptr() + sc * esz_out)
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     cview = np.int32 if p.c_dtype == "f32" else np.int16
+    kernel = binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb,
+                                 p.ldb, p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch,
+                                 p.stride_a, p.stride_b, p.stride_c)
     outs = []
     for r in range(repeat):
         if r:
@@ -199,7 +203,7 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         torch.cuda.synchronize()
         outs.append(dc.cpu().numpy().view(fc.dtype).copy())
     out = outs[0]
-    res = Result(name=p.name)
+    res = Result(name=p.name, kernel=kernel)
     if any(not np.array_equal(o, out) for o in outs[1:]):
         res.ok, res.why = False, "repeated runs differ"
         return res, out
@@ -230,6 +234,7 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         bb, ii, jj = idx[:, 0], idx[:, 1], idx[:, 2]
     got = out[sc + offsets(p, "c", bb, ii, jj)]
     res = compare(p, got, ref, den, p.name)
-    log(f"[parity]   -> ok={res.ok} max_err={res.max_err:.3e} max_ulp={res.max_ulp} "
+    res.kernel = kernel
+    log(f"[parity]   -> {kernel} ok={res.ok} max_err={res.max_err:.3e} max_ulp={res.max_ulp} "
         f"strict_fail={res.strict_fail} exempt={res.exempt} checked={res.checked} {res.why}")
     return res, out

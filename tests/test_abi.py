@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_f16", "gemm_f32",
-                                    "gemm_status_string"]
+                                    "gemm_kernel_name", "gemm_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -129,3 +129,97 @@ def test_raises_on_error(lib):
     with pytest.raises(lib.GemmError) as e:
         lib.gemm_f32(-1, 1, 1, 1.0, P, 1, 0, P, 1, 0, 0.0, P, 1, 0)
     assert e.value.status == lib.ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ kernel choice (host only)
+
+GB = 1 << 32  # operands 4 GiB apart: fake, never-dereferenced, 16-byte aligned addresses
+
+
+def kname(lib, dt, M, N, K, alpha=1.0, oa=0, ob=0, oc=0, lda=None, ldb=None, ldc=None,
+          A=GB, B=2 * GB, C=3 * GB, beta=0.0, c_dtype=0, batch=1, sa=0, sb=0, sc=0):
+    lda = lda or (K if oa == 0 else M)
+    ldb = ldb or (N if ob == 0 else K)
+    ldc = ldc or (N if oc == 0 else M)
+    return lib.kernel_name(dt, M, N, K, alpha, A, lda, oa, B, ldb, ob, beta, C, ldc, oc, c_dtype,
+                           batch, sa, sb, sc)
+
+
+@pytest.fixture
+def clean_env(monkeypatch):
+    for v in ("LIBGEMM_F32_VALU", "LIBGEMM_FORCE_GENERAL", "LIBGEMM_NO_SPLITK"):
+        monkeypatch.delenv(v, raising=False)
+    return monkeypatch
+
+
+KERNEL_CASES = [
+    # (dtype, M, N, K, extra arguments, kernel)
+    ("f32", 4096, 4096, 4096, {}, "sgemm_mfma_dma"),
+    ("f32", 4096, 4096, 4096, dict(A=GB + 4), "sgemm_mfma"),        # base not 16-byte aligned
+    ("f32", 4096, 4096, 4096, dict(lda=4097), "sgemm_mfma"),        # rows not 16-byte aligned
+    ("f32", 4096, 4096, 4098, {}, "sgemm_mfma"),                    # K not a multiple of 4
+    ("f32", 256, 256, 256, {}, "sgemm_splitk"),                     # 4 tiles of 128 x 128
+    ("f32", 1536, 1536, 1536, {}, "sgemm_splitk"),                  # 144 tiles
+    ("f32", 2048, 2048, 2048, {}, "sgemm_mfma_dma"),                # 256 tiles
+    ("f32", 256, 256, 128, {}, "sgemm_mfma_dma"),                   # K too short to split
+    ("f32", 16, 4096, 4096, {}, "gemm_skinny"),
+    ("f32", 16, 4096, 4096, dict(oa=1), "sgemm_splitk"),            # skinny needs K-contiguous A
+    ("f32", 17, 4096, 4096, {}, "sgemm_splitk"),
+    ("bf16", 4096, 4096, 4096, {}, "hgemm_mfma_dma"),
+    ("f16", 4096, 4096, 4096, dict(ob=1), "hgemm_mfma_dma"),
+    ("bf16", 4095, 4097, 1001, {}, "hgemm_mfma"),
+    ("bf16", 4096, 4096, 4096, dict(B=2 * GB + 2), "hgemm_mfma"),
+    ("bf16", 16, 4096, 4096, {}, "gemm_skinny"),
+    ("bf16", 1, 4096, 4096, dict(ob=1), "gemm_skinny"),
+    ("bf16", 32, 4096, 4096, {}, "hgemm_splitk"),
+    ("bf16", 256, 256, 8192, {}, "hgemm_splitk"),
+    ("bf16", 256, 256, 256, {}, "hgemm_mfma_dma"),                  # K too short to split
+    ("bf16", 4096, 12288, 4096, {}, "hgemm_mfma_dma"),
+    ("bf16", 4096, 4096, 4096, dict(alpha=0.0, beta=2.0), "scale"),
+    ("f32", 4096, 4096, 0, dict(beta=2.0, lda=1), "scale"),
+    ("bf16", 0, 4096, 4096, {}, ""),
+    ("f32", 4096, 4096, 4096, dict(lda=100), None),                 # invalid: lda < K
+    # column-major C: computed as C^T = B^T A^T, so the roles of M and N swap
+    ("bf16", 4096, 16, 4096, dict(oc=1, ob=1), "gemm_skinny"),
+    ("bf16", 4096, 16, 4096, dict(oc=1), "hgemm_splitk"),
+]
+
+
+@pytest.mark.parametrize("case", KERNEL_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[5]}")
+def test_kernel_choice(lib, clean_env, case):
+    dt, M, N, K, kw, want = case
+    assert kname(lib, dt, M, N, K, **kw) == want
+
+
+def test_kernel_choice_environment_switches(lib, clean_env):
+    clean_env.setenv("LIBGEMM_NO_SPLITK", "1")
+    assert kname(lib, "f32", 256, 256, 256) == "sgemm_mfma_dma"
+    assert kname(lib, "bf16", 16, 4096, 4096) == "hgemm_mfma_dma"
+    clean_env.delenv("LIBGEMM_NO_SPLITK")
+    clean_env.setenv("LIBGEMM_FORCE_GENERAL", "1")
+    assert kname(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma"
+    assert kname(lib, "bf16", 16, 4096, 4096) == "hgemm_mfma"
+    clean_env.delenv("LIBGEMM_FORCE_GENERAL")
+    clean_env.setenv("LIBGEMM_F32_VALU", "1")
+    assert kname(lib, "f32", 16, 4096, 4096) == "sgemm_valu"
+    assert kname(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"
+
+
+def test_kernel_choice_for_every_workload(lib, clean_env):
+    # the kernel each benchmark workload runs on, with its own layouts and
+    # (16-byte aligned) buffers
+    import workloads
+    want = {"f32_256": "sgemm_splitk", "f32_4096": "sgemm_mfma_dma",
+            "bf16_4096": "hgemm_mfma_dma", "f16_4096": "hgemm_mfma_dma",
+            "bf16_qkv": "hgemm_mfma_dma", "bf16_ffn_up": "hgemm_mfma_dma",
+            "bf16_ffn_down": "hgemm_mfma_dma", "f32_edge": "sgemm_mfma",
+            "bf16_edge": "hgemm_mfma", "bf16_skinny": "gemm_skinny",
+            "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma"}
+    assert sorted(want) == sorted(workloads.CONFIGS)
+    for name, k in want.items():
+        p = workloads.config(name)
+        c_dt = 1 if (p.c_dtype == "f32" and p.in_dtype != "f32") else 0
+        got = lib.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, GB, p.lda, p.order_a, 2 * GB,
+                              p.ldb, p.order_b, p.beta, 3 * GB, p.ldc, p.order_c, c_dt, p.batch,
+                              p.stride_a, p.stride_b, p.stride_c)
+        assert got == k, name

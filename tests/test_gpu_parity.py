@@ -24,9 +24,14 @@ def P(name, dt, M, N, K, c_dtype=None, **kw):
     return Problem(name, dt, c_dtype or dt, M, N, K, **kw)
 
 
-def check(p, **kw):
+def check(p, kernel=None, **kw):
+    """Run p against the oracle; with `kernel`, also require that the library
+    launched that kernel (so a test of a fast path cannot silently fall back
+    to another one)."""
     res, out = run(p, **kw)
     assert res.ok, res.why
+    if kernel is not None:
+        assert res.kernel == kernel, f"{p.name} ran on {res.kernel!r}, expected {kernel!r}"
     return res, out
 
 
@@ -230,19 +235,21 @@ def test_direct_load_path_ragged_aligned(monkeypatch, dt, shape, orders):
     M, N, K = shape
     oa, ob = orders
     check(P(f"dma-{dt}", dt, M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob),
-          seed=M + N + K)
+          kernel="hgemm_mfma_dma", seed=M + N + K)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_direct_load_path_fp32_out_and_col_major_c(dt):
-    check(P(f"dma-f32out-{dt}", dt, 520, 264, 200, c_dtype="f32", beta=-1.0), seed=31)
-    check(P(f"dma-colC-{dt}", dt, 520, 264, 200, order_c=COL, beta=0.25), seed=32)
+    check(P(f"dma-f32out-{dt}", dt, 520, 264, 200, c_dtype="f32", beta=-1.0),
+          kernel="hgemm_mfma_dma", seed=31)
+    check(P(f"dma-colC-{dt}", dt, 520, 264, 200, order_c=COL, beta=0.25),
+          kernel="hgemm_mfma_dma", seed=32)
 
 
 def test_general_kernel_forced_on_aligned_problem(monkeypatch):
     # the same aligned problem through the general kernel (register-staged)
     monkeypatch.setenv("LIBGEMM_FORCE_GENERAL", "1")
-    check(P("forced-general-bf16", "bf16", 512, 768, 320, beta=1.0), seed=33)
+    check(P("forced-general-bf16", "bf16", 512, 768, 320, beta=1.0), kernel="hgemm_mfma", seed=33)
 
 
 # ------------------------------------------------------------------ fp32 kernels
@@ -261,15 +268,18 @@ def test_f32_direct_load_path_ragged_aligned(monkeypatch, shape, orders):
     monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
     M, N, K = shape
     oa, ob = orders
-    check(P("dma-f32", "f32", M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob), seed=M + N + K)
+    check(P("dma-f32", "f32", M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob),
+          kernel="sgemm_mfma_dma", seed=M + N + K)
 
 
 def test_f32_direct_load_path_batch_and_col_major_c(monkeypatch):
     monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
-    check(P("dma-f32-batch", "f32", 260, 132, 200, beta=-1.0, batch=3), seed=51)
-    check(P("dma-f32-colC", "f32", 260, 132, 200, order_c=COL, beta=0.25), seed=52)
+    check(P("dma-f32-batch", "f32", 260, 132, 200, beta=-1.0, batch=3), kernel="sgemm_mfma_dma",
+          seed=51)
+    check(P("dma-f32-colC", "f32", 260, 132, 200, order_c=COL, beta=0.25), kernel="sgemm_mfma_dma",
+          seed=52)
     p = P("dma-f32-int", "f32", 264, 136, 4096, alpha=2.0, beta=1.0)
-    res, _ = check(p, host=_int_host(p, np.random.default_rng(53)))
+    res, _ = check(p, kernel="sgemm_mfma_dma", host=_int_host(p, np.random.default_rng(53)))
     assert res.max_err == 0.0
 
 
@@ -281,12 +291,48 @@ def test_f32_other_kernels_forced_on_aligned_problem(monkeypatch, env, orders):
     # register-staged matrix-core kernel and through the vector-ALU kernel
     monkeypatch.setenv(env, "1")
     oa, ob = orders
-    check(P(f"forced-{env}", "f32", 520, 392, 300, beta=1.0, order_a=oa, order_b=ob), seed=54)
+    want = {"LIBGEMM_FORCE_GENERAL": "sgemm_mfma", "LIBGEMM_F32_VALU": "sgemm_valu"}[env]
+    check(P(f"forced-{env}", "f32", 520, 392, 300, beta=1.0, order_a=oa, order_b=ob), kernel=want,
+          seed=54)
+
+
+# ------------------------------------------------------------------ skinny path (at most 16 rows of C)
+
+SKINNY_SHAPES = [(1, 520, 256), (5, 4096, 1000), (16, 4096, 4096), (16, 16, 8200), (11, 264, 2056)]
+
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("shape", SKINNY_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("ob", [ROW, COL], ids=["Brow", "Bcol"])
+def test_skinny_path(dt, shape, ob):
+    # M <= 16 with a row-major A: B streamed through LDS in 16-column blocks,
+    # K split eight ways (slices ragged against K, rows past M zero)
+    M, N, K = shape
+    check(P(f"skinny-{dt}", dt, M, N, K, alpha=0.75, beta=-0.5, order_b=ob), kernel="gemm_skinny",
+          seed=M + 7 * N + K, sample="auto" if M * N * K > 100_000_000 else None)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_skinny_fp32_output_and_batch(dt):
+    check(P(f"skinny-f32out-{dt}", dt, 16, 520, 2048, c_dtype="f32", beta=1.0, batch=3),
+          kernel="gemm_skinny", seed=71)
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_skinny_column_major_c_and_integers(dt):
+    # column-major C with 12 columns is computed as the 12-row C^T = B^T A^T,
+    # which is skinny when B is column-major (A^T of the swapped problem is
+    # then K-contiguous)
+    check(P(f"skinny-colC-{dt}", dt, 520, 12, 2048, order_b=COL, order_c=COL, beta=0.5),
+          kernel="gemm_skinny", seed=72)
+    p = P(f"skinny-int-{dt}", dt, 16, 264, 4096, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="gemm_skinny", host=_int_host(p, np.random.default_rng(73)))
+    assert res.max_err == 0.0
 
 
 # ------------------------------------------------------------------ split-K path (few tiles, long K)
 
-F32_SPLITK_SHAPES = [(256, 256, 256), (16, 4096, 4096), (8, 8, 4096), (40, 1000, 1736),
+F32_SPLITK_SHAPES = [(256, 256, 256), (32, 4096, 4096), (24, 8, 4096), (40, 1000, 1736),
                      (260, 132, 512), (24, 520, 300), (1000, 1028, 1004)]
 
 
@@ -300,19 +346,21 @@ def test_f32_splitk_path(shape, orders):
     oa, ob = orders
     big = M * N * K > 100_000_000
     check(P("splitk-f32", "f32", M, N, K, alpha=0.75, beta=-0.5, order_a=oa, order_b=ob),
-          seed=M + 5 * N + K, sample="auto" if big else None)
+          kernel="sgemm_splitk", seed=M + 5 * N + K, sample="auto" if big else None)
 
 
 def test_f32_splitk_batch_col_major_c_and_integers():
-    check(P("splitk-f32-batch", "f32", 24, 520, 2048, beta=1.0, batch=3), seed=61)
-    check(P("splitk-f32-colC", "f32", 520, 24, 2048, order_c=COL, beta=0.5), seed=62)
+    check(P("splitk-f32-batch", "f32", 24, 520, 2048, beta=1.0, batch=3), kernel="sgemm_splitk",
+          seed=61)
+    check(P("splitk-f32-colC", "f32", 520, 24, 2048, order_c=COL, beta=0.5), kernel="sgemm_splitk",
+          seed=62)
     # integer inputs: the fixed-order reduction of the slices is exact
-    p = P("splitk-f32-int", "f32", 16, 264, 4096, alpha=2.0, beta=1.0)
-    res, _ = check(p, host=_int_host(p, np.random.default_rng(63)))
+    p = P("splitk-f32-int", "f32", 24, 264, 4096, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="sgemm_splitk", host=_int_host(p, np.random.default_rng(63)))
     assert res.max_err == 0.0
 
 
-SPLITK_SHAPES = [(16, 4096, 4096), (8, 8, 4096), (40, 1000, 1736), (256, 256, 8192), (24, 520, 512)]
+SPLITK_SHAPES = [(32, 4096, 4096), (24, 8, 4096), (40, 1000, 1736), (256, 256, 8192), (24, 520, 512)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
@@ -326,15 +374,17 @@ def test_splitk_path(dt, shape, orders):
     oa, ob = orders
     big = M * N * K > 100_000_000
     check(P(f"splitk-{dt}", dt, M, N, K, alpha=0.75, beta=-0.5, order_a=oa, order_b=ob),
-          seed=M + 3 * N + K, sample="auto" if big else None)
+          kernel="hgemm_splitk", seed=M + 3 * N + K, sample="auto" if big else None)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_splitk_fp32_output_batch_and_col_major_c(dt):
-    check(P(f"splitk-f32out-{dt}", dt, 24, 520, 2048, c_dtype="f32", beta=1.0, batch=3), seed=41)
-    check(P(f"splitk-colC-{dt}", dt, 520, 24, 2048, order_c=COL, beta=0.5), seed=42)
+    check(P(f"splitk-f32out-{dt}", dt, 24, 520, 2048, c_dtype="f32", beta=1.0, batch=3),
+          kernel="hgemm_splitk", seed=41)
+    check(P(f"splitk-colC-{dt}", dt, 520, 24, 2048, order_c=COL, beta=0.5), kernel="hgemm_splitk",
+          seed=42)
     # integer inputs: every partial sum exact in fp32, so the fixed-order
     # reduction of the eight slices must reproduce the oracle bit for bit
-    p = P(f"splitk-int-{dt}", dt, 16, 264, 4096, alpha=2.0, beta=1.0)
-    res, _ = check(p, host=_int_host(p, np.random.default_rng(43)))
+    p = P(f"splitk-int-{dt}", dt, 24, 264, 4096, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="hgemm_splitk", host=_int_host(p, np.random.default_rng(43)))
     assert res.max_err == 0.0 and res.max_ulp == 0
