@@ -279,10 +279,20 @@ hipError_t launch(const Problem &p, SkinnyArgs &a, int64_t blocks, hipStream_t s
 
 // At most 16 rows of C, A contiguous along K, a K worth splitting eight
 // ways, and operands the direct loads can read whole 16-byte chunks of (the
-// same conditions as the main kernels' direct-load paths).
+// same conditions as the main kernels' direct-load paths).  For fp32 the
+// kernel's 16-column blocks read half cache lines of an N-contiguous B,
+// where the fp32 split-K kernel's 32-column blocks read whole ones; measured
+// on MI355X that kernel is faster there, and also once N is large enough to
+// give it 256 or more workgroups, so fp32 takes this path only for a
+// K-contiguous B and N below 8192.
+#ifndef LIBGEMM_SKINNY_MAX_M
+#define LIBGEMM_SKINNY_MAX_M 16
+#endif
+
 bool skinny_eligible(const Problem &p) {
-    if (p.M > TN || !p.a_kmajor || p.K < 256) return false;
-    return p.in == Elem::F32 ? sgemm_dma_eligible(p) : hgemm_dma_eligible(p);
+    if (p.M > LIBGEMM_SKINNY_MAX_M || !p.a_kmajor || p.K < 256) return false;
+    if (p.in == Elem::F32) return p.b_kmajor && p.N < 8192 && sgemm_dma_eligible(p);
+    return hgemm_dma_eligible(p);
 }
 
 hipError_t launch_skinny(const Problem &p, hipStream_t stream) {

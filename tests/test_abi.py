@@ -162,8 +162,10 @@ KERNEL_CASES = [
     ("f32", 1536, 1536, 1536, {}, "sgemm_splitk"),                  # 144 tiles
     ("f32", 2048, 2048, 2048, {}, "sgemm_mfma_dma"),                # 256 tiles
     ("f32", 256, 256, 128, {}, "sgemm_mfma_dma"),                   # K too short to split
-    ("f32", 16, 4096, 4096, {}, "gemm_skinny"),
-    ("f32", 16, 4096, 4096, dict(oa=1), "sgemm_splitk"),            # skinny needs K-contiguous A
+    ("f32", 16, 4096, 4096, {}, "sgemm_splitk"),                    # N-contiguous B: split-K
+    ("f32", 16, 4096, 4096, dict(ob=1), "gemm_skinny"),
+    ("f32", 16, 16384, 4096, dict(ob=1), "sgemm_splitk"),
+    ("f32", 16, 4096, 4096, dict(oa=1, ob=1), "sgemm_splitk"),      # skinny needs K-contiguous A
     ("f32", 17, 4096, 4096, {}, "sgemm_splitk"),
     ("bf16", 4096, 4096, 4096, {}, "hgemm_mfma_dma"),
     ("f16", 4096, 4096, 4096, dict(ob=1), "hgemm_mfma_dma"),
@@ -201,7 +203,7 @@ def test_kernel_choice_environment_switches(lib, clean_env):
     assert kname(lib, "bf16", 16, 4096, 4096) == "hgemm_mfma"
     clean_env.delenv("LIBGEMM_FORCE_GENERAL")
     clean_env.setenv("LIBGEMM_F32_VALU", "1")
-    assert kname(lib, "f32", 16, 4096, 4096) == "sgemm_valu"
+    assert kname(lib, "f32", 16, 4096, 4096, ob=1) == "sgemm_valu"
     assert kname(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"
 
 

@@ -306,9 +306,11 @@ SKINNY_SHAPES = [(1, 520, 256), (5, 4096, 1000), (16, 4096, 4096), (16, 16, 8200
 @pytest.mark.parametrize("ob", [ROW, COL], ids=["Brow", "Bcol"])
 def test_skinny_path(dt, shape, ob):
     # M <= 16 with a row-major A: B streamed through LDS in 16-column blocks,
-    # K split eight ways (slices ragged against K, rows past M zero)
+    # K split eight ways (slices ragged against K, rows past M zero); fp32
+    # takes this path only with a K-contiguous B (else split-K)
     M, N, K = shape
-    check(P(f"skinny-{dt}", dt, M, N, K, alpha=0.75, beta=-0.5, order_b=ob), kernel="gemm_skinny",
+    want = "sgemm_splitk" if (dt == "f32" and ob == ROW) else "gemm_skinny"
+    check(P(f"skinny-{dt}", dt, M, N, K, alpha=0.75, beta=-0.5, order_b=ob), kernel=want,
           seed=M + 7 * N + K, sample="auto" if M * N * K > 100_000_000 else None)
 
 
@@ -323,9 +325,12 @@ def test_skinny_column_major_c_and_integers(dt):
     # column-major C with 12 columns is computed as the 12-row C^T = B^T A^T,
     # which is skinny when B is column-major (A^T of the swapped problem is
     # then K-contiguous)
+    # (the swapped problem's B is A^T, K-contiguous since A is row-major, so
+    # fp32 takes the skinny kernel here too)
     check(P(f"skinny-colC-{dt}", dt, 520, 12, 2048, order_b=COL, order_c=COL, beta=0.5),
           kernel="gemm_skinny", seed=72)
-    p = P(f"skinny-int-{dt}", dt, 16, 264, 4096, alpha=2.0, beta=1.0)
+    p = P(f"skinny-int-{dt}", dt, 16, 264, 4096, alpha=2.0, beta=1.0,
+          order_b=COL if dt == "f32" else ROW)
     res, _ = check(p, kernel="gemm_skinny", host=_int_host(p, np.random.default_rng(73)))
     assert res.max_err == 0.0
 
