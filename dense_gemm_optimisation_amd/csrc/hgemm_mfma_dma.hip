@@ -460,11 +460,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
         interleave_reads<NREAD, FM * FN>();
     }
 
-    // C is staged in a buffer the last stage does not use: every wave
-    // finished reading it before the last barrier, and no load targets it
-    // any more, so no further barrier is needed.
-    static_assert(WAVES * 32 * WTN * 4 <= STAGE, "epilogue staging fits in one stage buffer");
-    LDS char *stage_free = lds + (buf + 1 == STAGES ? 0 : buf + 1) * STAGE;
+    // C is staged in stage buffers the last stage does not use: every wave
+    // finished reading them before the last barrier, and no load targets
+    // them any more, so no further barrier is needed.  Staging takes NEED
+    // consecutive buffers: the next one when one suffices, else the first
+    // NEED or the NEED after them, whichever excludes the last stage's.
+    constexpr int NEED = (WAVES * 32 * WTN * 4 + STAGE - 1) / STAGE;
+    static_assert(NEED == 1 || 2 * NEED <= STAGES, "epilogue staging fits beside the last stage");
+    const int free0 = NEED == 1 ? (buf + 1 == STAGES ? 0 : buf + 1) : (buf >= NEED ? 0 : NEED);
+    LDS char *stage_free = lds + free0 * STAGE;
     store_tile_lds<OUT, FM, FN>(p, acc, t.batch, m0 + wm * WTM, n0 + wn * WTN, lane,
                                 reinterpret_cast<LDS float *>(stage_free) + wave * 32 * WTN);
 }
