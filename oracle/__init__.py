@@ -1,4 +1,4 @@
-"""CPU oracle for dense GEMM, C = alpha*A*B + beta*C.
+"""CPU oracle for dense GEMM, C = act(alpha*A*B + beta*C + bias).
 
 TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package; the GPU library and
@@ -21,6 +21,7 @@ import numpy as np
 from . import build as _build
 
 ROW, COL = 0, 1
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 _TYPES = {"f32": 0, "bf16": 1, "f16": 2}
 
 _lib = None
@@ -36,7 +37,7 @@ def _load():
         lib = ctypes.CDLL(path)
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         prob = [i32, i32, i64, i64, i64, dbl, vp, i64, i32, vp, i64, i32, dbl, vp, i64,
-                i32, i64, i64, i64]
+                i32, i64, i64, i64, vp, i64, i32]
         lib.orc_gemm.argtypes = prob + [i64, vp, vp]
         lib.orc_gemm.restype = None
         lib.orc_gemm_at.argtypes = prob + [i64, vp, vp, vp]
@@ -91,28 +92,32 @@ def round_bits(dtype, x) -> np.ndarray:
 
 
 def _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
-          ldc, order_c, stride_a, stride_b, stride_c):
+          ldc, order_c, stride_a, stride_b, stride_c, bias, stride_bias, act):
     keep = []
     ptrs = []
-    for x, dt in ((A, in_dtype), (B, in_dtype), (C0, c_dtype)):
+    for x, dt in ((A, in_dtype), (B, in_dtype), (C0, c_dtype), (bias, in_dtype)):
         a, p = _buf(x, dt)
         keep.append(a)
         ptrs.append(p)
     args = [_TYPES[in_dtype], _TYPES[c_dtype], M, N, K, float(alpha), ptrs[0], lda, order_a,
             ptrs[1], ldb, order_b, float(beta), ptrs[2], ldc, order_c, stride_a, stride_b,
-            stride_c]
+            stride_c, ptrs[3], stride_bias, int(act)]
     return args, keep
 
 
 def gemm(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
-         ldc, order_c, batch=1, stride_a=0, stride_b=0, stride_c=0):
+         ldc, order_c, batch=1, stride_a=0, stride_b=0, stride_c=0, bias=None, stride_bias=0,
+         act=ACT_NONE):
     """Every element: returns (ref, den) as float64 arrays [batch][M][N].
 
-    ref = alpha*sum_k A_ik B_kj + beta*C0_ij and
-    den = |alpha|*sum_k |A_ik B_kj| + |beta|*|C0_ij|, accumulated in double.
+    ref = act(alpha*sum_k A_ik B_kj + beta*C0_ij + bias_j) and
+    den = |alpha|*sum_k |A_ik B_kj| + |beta|*|C0_ij| + |bias_j|, accumulated in
+    double.  ``bias`` (optional) holds N input-type elements per batch entry,
+    ``stride_bias`` apart; ``act`` is ACT_NONE, ACT_RELU or ACT_GELU.
     """
     args, keep = _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b,
-                       beta, C0, ldc, order_c, stride_a, stride_b, stride_c)
+                       beta, C0, ldc, order_c, stride_a, stride_b, stride_c, bias, stride_bias,
+                       act)
     ref = np.empty((batch, M, N), np.float64)
     den = np.empty((batch, M, N), np.float64)
     _load().orc_gemm(*args, batch, ref.ctypes.data, den.ctypes.data)
@@ -121,11 +126,13 @@ def gemm(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, be
 
 
 def gemm_at(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
-            ldc, order_c, idx, stride_a=0, stride_b=0, stride_c=0):
+            ldc, order_c, idx, stride_a=0, stride_b=0, stride_c=0, bias=None, stride_bias=0,
+            act=ACT_NONE):
     """Only the elements listed in ``idx`` (an (n, 3) array of (b, i, j))."""
     idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 3)
     args, keep = _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b,
-                       beta, C0, ldc, order_c, stride_a, stride_b, stride_c)
+                       beta, C0, ldc, order_c, stride_a, stride_b, stride_c, bias, stride_bias,
+                       act)
     n = idx.shape[0]
     ref = np.empty(n, np.float64)
     den = np.empty(n, np.float64)

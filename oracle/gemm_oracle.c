@@ -21,6 +21,18 @@
  *   den = |alpha| * sum_k |A_ik * B_kj| + |beta| * |C0_ij|,
  * which the tests use to normalise the error of a GPU result.
  *
+ * The fused epilogue (optional): the pages fold "GEMM + bias + activation"
+ * into one kernel ("第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech,
+ * section 7.2, on CUTLASS) and apply element-wise operations such as ReLU on
+ * the accumulators before the store ("GPU GEMM 优化完全拆解（三）",
+ * pinghaoyang.com.cn, section on mainloop and epilogue).  Here
+ *   D_ij = act(alpha * sum_k A_ik B_kj + beta * C0_ij + bias_j),
+ * bias_j the j-th element of a vector of N input-type values (one per
+ * column of C, the b-th batch entry sBias elements after the previous one),
+ * act one of identity, ReLU max(x, 0), or GELU x * Phi(x) with Phi the
+ * standard normal distribution function, 0.5 * (1 + erf(x / sqrt 2)).  den
+ * gains |bias_j|; it stays the scale of the terms before the activation.
+ *
  * Readings taken where the pages are silent:
  *   - beta == 0: C0 is not read (BLAS convention), so NaN in C0 does not leak.
  *   - alpha == 0 or K == 0: the product term is skipped and A, B are not read.
@@ -37,6 +49,10 @@
 
 #define ORC_ROW 0
 #define ORC_COL 1
+
+#define ORC_ACT_NONE 0
+#define ORC_ACT_RELU 1
+#define ORC_ACT_GELU 2
 
 /* ---------------------------------------------------------------- decoding */
 
@@ -133,7 +149,7 @@ static uint16_t encode_f16(double r) {
 
 /* ---------------------------------------------------------------- exports */
 
-int orc_version(void) { return 1; }
+int orc_version(void) { return 2; }
 
 void orc_decode(int type, const void *src, double *dst, int64_t n) {
     for (int64_t i = 0; i < n; ++i) dst[i] = load(type, src, i);
@@ -168,6 +184,9 @@ struct problem {
     int64_t lda, ldb, ldc;
     int oA, oB, oC;
     int64_t sA, sB, sC;
+    const void *bias; /* NULL: no bias */
+    int64_t sBias;
+    int act;
 };
 
 /*
@@ -196,6 +215,15 @@ static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
         r = r + P->beta * c0;
         d = d + fabs(P->beta) * fabs(c0);
     }
+    if (P->bias != NULL) {
+        double bj = load(P->in_type, P->bias, b * P->sBias + j);
+        r = r + bj;
+        d = d + fabs(bj);
+    }
+    if (P->act == ORC_ACT_RELU)
+        r = r > 0.0 ? r : 0.0;
+    else if (P->act == ORC_ACT_GELU)
+        r = r * 0.5 * (1.0 + erf(r / sqrt(2.0)));
     *ref = r;
     *den = d;
 }
@@ -204,11 +232,12 @@ static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
     int in_type, int c_type, int64_t M, int64_t N, int64_t K, double alpha,            \
         const void *A, int64_t lda, int oA, const void *B, int64_t ldb, int oB,        \
         double beta, const void *C0, int64_t ldc, int oC, int64_t sA, int64_t sB,      \
-        int64_t sC
+        int64_t sC, const void *bias, int64_t sBias, int act
 
 #define PROBLEM_INIT                                                                   \
-    struct problem P = {in_type, c_type, M,   N,   K,   alpha, beta, A,  B,            \
-                        C0,      lda,    ldb, ldc, oA,  oB,    oC,   sA, sB, sC}
+    struct problem P = {in_type, c_type, M,  N,  K,  alpha, beta, A,     B,    C0,    \
+                        lda,     ldb,    ldc, oA, oB, oC,    sA,   sB,    sC,   bias, \
+                        sBias,   act}
 
 /* All batch*M*N elements; ref and den are dense [batch][M][N]. */
 void orc_gemm(PROBLEM_ARGS, int64_t batch, double *ref, double *den) {

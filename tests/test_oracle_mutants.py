@@ -32,6 +32,14 @@ MUTANTS = {
     "no_overflow_to_inf": ("if (fabs(r) > maxfinite) r = copysign(INFINITY, x);", ""),
     "subnormal_spacing": ("if (e < emin) e = emin;", ""),
     "flat_index_wrong": ("i = (e / N) % M, j = e % N", "i = (e / N) % M, j = (e + 1) % N"),
+    "bias_per_row": ("b * P->sBias + j", "b * P->sBias + i"),
+    "bias_batch_stride_dropped": ("b * P->sBias + j", "j"),
+    "bias_dropped": ("r = r + bj;", "r = r;"),
+    "den_bias_dropped": ("d = d + fabs(bj);", "d = d;"),
+    "relu_keeps_negatives": ("r = r > 0.0 ? r : 0.0;", "r = r > 0.0 ? r : -r;"),
+    "gelu_tanh_form": ("r = r * 0.5 * (1.0 + erf(r / sqrt(2.0)));",
+                       "r = r * 0.5 * (1.0 + tanh(0.7978845608 * (r + 0.044715 * r * r * r)));"),
+    "gelu_wrong_scale": ("erf(r / sqrt(2.0))", "erf(r / 2.0)"),
 }
 
 

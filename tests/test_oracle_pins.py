@@ -427,3 +427,68 @@ def test_page_throughput_figures_follow_2mnk():
         if "tflops" in e:
             assert abs(flop / e["time_s"] / 1e12 - e["tflops"]) <= e["tflops_rel_tol"] * e["tflops"], \
                 e["cite"]
+
+
+# --------------------------------------------------------------- fused epilogue
+
+def one_by_one(x, act, bias=None, dtype="f32"):
+    """A 1 x 1 x 1 product x * 1, so the value entering the epilogue is x exactly."""
+    b = None if bias is None else stored(dtype, [bias])
+    ref, den = oracle.gemm(dtype, dtype, 1, 1, 1, 1.0, stored(dtype, [x]), 1, ROW,
+                           stored(dtype, [1.0]), 1, ROW, 0.0, None, 1, ROW, bias=b, act=act)
+    return ref[0, 0, 0], den[0, 0, 0]
+
+
+def test_gelu_matches_the_normal_table():
+    table = json.load(open(os.path.join(GOLDEN, "normal_cdf.json")))
+    for x, phi in table["phi"]:
+        for xs, ph in ((x, phi), (-x, 1.0 - phi)):
+            got, _ = one_by_one(xs, oracle.ACT_GELU)
+            assert abs(got - xs * ph) <= 1e-14 * max(1.0, abs(xs)), (xs, got, xs * ph)
+    assert one_by_one(0.0, oracle.ACT_GELU)[0] == 0.0
+    # Phi(8) = 1 - 6.2e-16: GELU is the identity above and zero below, to double precision
+    assert abs(one_by_one(8.0, oracle.ACT_GELU)[0] - 8.0) < 1e-13
+    assert abs(one_by_one(-8.0, oracle.ACT_GELU)[0]) < 1e-13
+
+
+def test_relu_of_x_then_bias_order():
+    # the activation comes after the bias: relu(-1 + 2) = 1, not relu(-1) + 2 = 2
+    assert one_by_one(-1.0, oracle.ACT_RELU, bias=2.0)[0] == 1.0
+    assert one_by_one(-3.0, oracle.ACT_RELU, bias=2.0)[0] == 0.0
+    assert one_by_one(3.0, oracle.ACT_RELU)[0] == 3.0
+    assert one_by_one(-3.0, oracle.ACT_NONE, bias=2.0) == (-1.0, 5.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_bias_and_activations_on_integers_match_int64(dtype):
+    # integer data keep every double operation exact: the oracle must equal
+    # max(2*(A@B) + bias_j, 0) computed in int64, for bias broadcast along rows
+    rng = np.random.default_rng(21)
+    M, N, K = 13, 17, 29
+    A = rng.integers(-6, 7, (M, K))
+    B = rng.integers(-6, 7, (K, N))
+    bias = rng.integers(-50, 51, N)
+    pre = 2 * (A @ B) + bias[None, :]
+    for act, want in ((oracle.ACT_NONE, pre), (oracle.ACT_RELU, np.maximum(pre, 0))):
+        ref, den = oracle.gemm(dtype, dtype, M, N, K, 2.0, stored(dtype, A.ravel()), K, ROW,
+                               stored(dtype, B.ravel()), N, ROW, 0.0, None, N, ROW,
+                               bias=stored(dtype, bias), act=act)
+        assert np.array_equal(ref[0], want.astype(np.float64)), act
+        assert np.array_equal(den[0], (2 * (np.abs(A) @ np.abs(B)) + np.abs(bias)[None, :])
+                              .astype(np.float64))
+
+
+def test_bias_is_per_column_and_per_batch_entry():
+    # A = 0: C = beta*C0 + bias_j; M != N so a bias indexed by the row would differ
+    M, N, K, batch = 3, 5, 4, 2
+    c0 = np.arange(batch * M * N, dtype=np.float64)
+    bias = np.arange(batch * N, dtype=np.float64) * 10
+    for stride in (N, 0):
+        ref, den = oracle.gemm("f32", "f32", M, N, K, 1.0, stored("f32", np.zeros(M * K)), K, ROW,
+                               stored("f32", np.zeros(K * N)), N, ROW, 0.5,
+                               stored("f32", c0), N, ROW, batch=batch, stride_c=M * N,
+                               bias=stored("f32", bias), stride_bias=stride)
+        for b in range(batch):
+            want = 0.5 * c0[b * M * N:(b + 1) * M * N].reshape(M, N) + \
+                bias[b * stride:b * stride + N][None, :]
+            assert np.array_equal(ref[b], want), (stride, b)
