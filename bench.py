@@ -62,6 +62,15 @@ def device_buffers(p, torch):
             torch.from_numpy(c.view(cview)).to("cuda"))
 
 
+def device_bias(p, torch):
+    """The bias vector of a fused-epilogue workload on the device, or None."""
+    import workloads
+    bias = workloads.bias_vector(p)
+    if bias is None:
+        return None
+    return torch.from_numpy(bias.view(np.float32 if p.in_dtype == "f32" else np.int16)).to("cuda")
+
+
 # Each kernel cycles through enough copies of its buffers that their combined
 # footprint exceeds twice the 256 MB Infinity Cache (MALL), so a launch finds
 # its inputs in HBM rather than left in the MALL by the previous launch.
@@ -81,17 +90,20 @@ def sets_needed(bufs, rotate):
     return min(MAX_SETS, max(MIN_SETS, -(-ROTATE_BYTES // nbytes)))
 
 
-def make_launch(p, sets, stream):
-    """A callable that runs the GEMM on the next buffer set in turn."""
+def make_launch(p, sets, stream, bias=None):
+    """A callable that runs the GEMM on the next buffer set in turn (with the
+    workload's fused bias and activation, if it has them)."""
     from dense_gemm_optimisation_amd import binding
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     argsets = [(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a, db.data_ptr(),
                 p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch,
                 p.stride_a, p.stride_b, p.stride_c, stream.cuda_stream) for da, db, dc in sets]
+    epi = dict(bias=None if bias is None else bias.data_ptr(), stride_bias=p.stride_bias,
+               act=p.act)
     turn = [0]
 
     def launch():
-        binding.gemm(*argsets[turn[0]])
+        binding.gemm(*argsets[turn[0]], **epi)
         turn[0] = (turn[0] + 1) % len(argsets)
     return launch
 
@@ -206,7 +218,8 @@ def main():
             sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
             nsets[p.name] = len(sets)
             families[p.name] = kernel_family(p, bufs)
-            launches.append((p, sets, make_launch(p, sets, stream)))
+            bias = device_bias(p, torch)
+            launches.append((p, sets, make_launch(p, sets, stream, bias)))
     torch.cuda.synchronize()
 
     # warmup

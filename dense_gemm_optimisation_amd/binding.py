@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm.so"
 
 ROW_MAJOR, COL_MAJOR = 0, 1
 DTYPE_SAME, DTYPE_F32 = 0, 1
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 
 _lib = None
@@ -50,6 +51,12 @@ def library() -> ctypes.CDLL:
         lib.gemm_status_string.argtypes = [i32]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_abi_version.restype = i32
+        lib.gemm_f32_bias_act.argtypes = common + [i64, i64, i64, i64, vp, i64, i32, vp]
+        lib.gemm_f32_bias_act.restype = i32
+        for name in ("gemm_bf16_bias_act", "gemm_f16_bias_act"):
+            fn = getattr(lib, name)
+            fn.argtypes = common + [i32, i64, i64, i64, i64, vp, i64, i32, vp]
+            fn.restype = i32
         lib.gemm_kernel_name.argtypes = [i32] + common + [i32, i64, i64, i64, i64]
         lib.gemm_kernel_name.restype = ctypes.c_char_p
         _lib = lib
@@ -106,7 +113,39 @@ def gemm_f16(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, ord
     return _check(st, "gemm_f16", raise_on_error)
 
 
+def gemm_f32_bias_act(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                      batch=1, stride_a=0, stride_b=0, stride_c=0, bias=0, stride_bias=0,
+                      act=ACT_NONE, stream=None, raise_on_error=True):
+    """C <- act(alpha*op(A)*op(B) + beta*C + bias) in fp32; bias is a device
+    address of N floats per batch entry (0 for none)."""
+    st = library().gemm_f32_bias_act(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C,
+                                     ldc, order_c, batch, stride_a, stride_b, stride_c, bias,
+                                     stride_bias, act, _stream(stream))
+    return _check(st, "gemm_f32_bias_act", raise_on_error)
+
+
+def gemm_bf16_bias_act(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                       c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, bias=0,
+                       stride_bias=0, act=ACT_NONE, stream=None, raise_on_error=True):
+    """bf16 inputs with the fused bias/activation epilogue (bias in bf16)."""
+    st = library().gemm_bf16_bias_act(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C,
+                                      ldc, order_c, c_dtype, batch, stride_a, stride_b, stride_c,
+                                      bias, stride_bias, act, _stream(stream))
+    return _check(st, "gemm_bf16_bias_act", raise_on_error)
+
+
+def gemm_f16_bias_act(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                      c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, bias=0,
+                      stride_bias=0, act=ACT_NONE, stream=None, raise_on_error=True):
+    """fp16 inputs with the fused bias/activation epilogue (bias in fp16)."""
+    st = library().gemm_f16_bias_act(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C,
+                                     ldc, order_c, c_dtype, batch, stride_a, stride_b, stride_c,
+                                     bias, stride_bias, act, _stream(stream))
+    return _check(st, "gemm_f16_bias_act", raise_on_error)
+
+
 _ENTRY = {"f32": gemm_f32, "bf16": gemm_bf16, "f16": gemm_f16}
+_ENTRY_EPI = {"f32": gemm_f32_bias_act, "bf16": gemm_bf16_bias_act, "f16": gemm_f16_bias_act}
 _INPUT = {"f32": 0, "bf16": 1, "f16": 2}
 
 
@@ -122,8 +161,18 @@ def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta
 
 def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
          c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
-         raise_on_error=True):
-    """Dispatch on the input type name ("f32", "bf16" or "f16")."""
+         raise_on_error=True, bias=None, stride_bias=0, act=ACT_NONE):
+    """Dispatch on the input type name ("f32", "bf16" or "f16"); a bias
+    address or an activation selects the fused-epilogue entry point."""
+    if bias is not None or act != ACT_NONE:
+        fn = _ENTRY_EPI[in_dtype]
+        if in_dtype == "f32":
+            return fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                      batch, stride_a, stride_b, stride_c, bias or 0, stride_bias, act, stream,
+                      raise_on_error)
+        return fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                  c_dtype, batch, stride_a, stride_b, stride_c, bias or 0, stride_bias, act,
+                  stream, raise_on_error)
     fn = _ENTRY[in_dtype]
     if in_dtype == "f32":
         return fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
@@ -146,12 +195,15 @@ def _matrix_layout(t):
 _TORCH_IN = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
 
 
-def matmul(a, b, c=None, alpha=1.0, beta=0.0, out_dtype=None, stream=None):
-    """C = alpha*a@b + beta*c on torch CUDA tensors (2-D, or 3-D batched).
+def matmul(a, b, c=None, alpha=1.0, beta=0.0, out_dtype=None, stream=None, bias=None,
+           act=ACT_NONE):
+    """C = act(alpha*a@b + beta*c + bias) on torch CUDA tensors (2-D, or 3-D batched).
 
     ``a`` (..., M, K) and ``b`` (..., K, N) may be row- or column-major views;
     a 3-D operand with batch stride 0 (an expanded view) is shared across the
-    batch.  Returns ``c`` (allocated when None).  Only marshalling happens here.
+    batch.  ``bias`` (optional) is a contiguous (N,) or (batch, N) tensor of
+    the input type; ``act`` is ACT_NONE, ACT_RELU or ACT_GELU.  Returns ``c``
+    (allocated when None).  Only marshalling happens here.
     """
     if a.dtype != b.dtype or a.dtype not in _TORCH_IN:
         raise TypeError("a and b must share one of float32, bfloat16, float16")
@@ -181,7 +233,14 @@ def matmul(a, b, c=None, alpha=1.0, beta=0.0, out_dtype=None, stream=None):
         return t.stride(0) if t.dim() == 3 and t.shape[0] > 1 else 0
 
     c_dtype = DTYPE_SAME if (out_dtype == a.dtype) else DTYPE_F32
+    bias_ptr, bias_stride = None, 0
+    if bias is not None:
+        if bias.dtype != a.dtype or bias.shape[-1] != N or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous (N,) or (batch, N) tensor of the input type")
+        bias_ptr = bias.data_ptr()
+        bias_stride = N if (bias.dim() == 2 and bias.shape[0] > 1) else 0
     gemm(in_dtype, M, N, K, alpha, a.data_ptr(), lay[0][1], lay[0][0], b.data_ptr(), lay[1][1],
          lay[1][0], beta, c.data_ptr(), lay[2][1], lay[2][0], c_dtype, batch, bstride(a),
-         bstride(b), bstride(c) if batch > 1 else 0, stream)
+         bstride(b), bstride(c) if batch > 1 else 0, stream, bias=bias_ptr,
+         stride_bias=bias_stride, act=act)
     return c

@@ -135,11 +135,14 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
 gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                    const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                    float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
-                   int64_t strideB, int64_t strideC, Problem &p, Kernel &kernel) {
+                   int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
+                   Problem &p, Kernel &kernel) {
     kernel = Kernel::None;
     // ---- argument checks (no HIP call before this block is done)
     if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
-    if (strideA < 0 || strideB < 0 || strideC < 0) return GEMM_ERR_INVALID_ARG;
+    if (strideA < 0 || strideB < 0 || strideC < 0 || strideBias < 0) return GEMM_ERR_INVALID_ARG;
+    if (act != GEMM_ACT_NONE && act != GEMM_ACT_RELU && act != GEMM_ACT_GELU)
+        return GEMM_ERR_INVALID_ARG;
     if (!valid_order(orderA) || !valid_order(orderB) || !valid_order(orderC))
         return GEMM_ERR_INVALID_ARG;
     auto min_ld = [](int order, int64_t rows, int64_t cols) {
@@ -161,9 +164,12 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
     if (C == nullptr) return GEMM_ERR_INVALID_ARG;
     if (reads_ab && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_ARG;
     if (batch > 1 && strideC < span_c) return GEMM_ERR_INVALID_ARG;  // C slices overlap
-    if (too_big(batch - 1, strideC) || too_big(batch - 1, strideA) || too_big(batch - 1, strideB))
+    if (too_big(batch - 1, strideC) || too_big(batch - 1, strideA) || too_big(batch - 1, strideB) ||
+        too_big(batch - 1, strideBias))
         return GEMM_ERR_INVALID_ARG;
     const Range rc = range_of(C, span_c, batch, strideC, eout);
+    if (bias != nullptr && overlap(rc, range_of(bias, N, batch, strideBias, ein)))
+        return GEMM_ERR_INVALID_ARG;
     if (reads_ab) {
         if (overlap(rc, range_of(A, span_a, batch, strideA, ein)) ||
             overlap(rc, range_of(B, span_b, batch, strideB, ein)))
@@ -181,6 +187,13 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
     p.sC = strideC;
     p.in = in;
     p.out = out;
+    // the bias runs along the caller's columns: along the kernel's rows when
+    // C is computed transposed
+    p.epi.bias = bias;
+    p.epi.bias_stride = batch > 1 ? strideBias : 0;
+    p.epi.per_row = orderC == GEMM_COL_MAJOR;
+    p.epi.bias_type = static_cast<int>(in);
+    p.epi.act = act;
     if (orderC == GEMM_ROW_MAJOR) {
         p.M = M;
         p.N = N;
@@ -213,11 +226,13 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
 gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                   float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
-                  int64_t strideB, int64_t strideC, hipStream_t stream) {
+                  int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
+                  hipStream_t stream) {
     Problem p;
     Kernel k;
-    const gemm_status_t st = plan(in, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C,
-                                  ldc, orderC, batch, strideA, strideB, strideC, p, k);
+    const gemm_status_t st =
+        plan(in, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC, batch,
+             strideA, strideB, strideC, bias, strideBias, act, p, k);
     if (st != GEMM_OK || k == Kernel::None) return st;
     const hipError_t err = launch(k, p, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
@@ -235,7 +250,7 @@ gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float
                        float beta, float *C, int64_t ldc, gemm_order_t orderC, int64_t batch,
                        int64_t strideA, int64_t strideB, int64_t strideC, hipStream_t stream) {
     return run(Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
-               orderC, batch, strideA, strideB, strideC, stream);
+               orderC, batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream);
 }
 
 gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
@@ -245,7 +260,8 @@ gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const uint
                         int64_t strideC, hipStream_t stream) {
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
     return run(Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
-               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, stream);
+               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
+               GEMM_ACT_NONE, stream);
 }
 
 gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
@@ -255,7 +271,44 @@ gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha, const uint1
                        int64_t strideC, hipStream_t stream) {
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
     return run(Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
-               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, stream);
+               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
+               GEMM_ACT_NONE, stream);
+}
+
+gemm_status_t gemm_f32_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                                int64_t lda, gemm_order_t orderA, const float *B, int64_t ldb,
+                                gemm_order_t orderB, float beta, float *C, int64_t ldc,
+                                gemm_order_t orderC, int64_t batch, int64_t strideA,
+                                int64_t strideB, int64_t strideC, const float *bias,
+                                int64_t strideBias, gemm_activation_t act, hipStream_t stream) {
+    return run(Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
+               orderC, batch, strideA, strideB, strideC, bias, strideBias, act, stream);
+}
+
+gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                                 int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                                 gemm_order_t orderB, float beta, void *C, int64_t ldc,
+                                 gemm_order_t orderC, gemm_dtype_t c_dtype, int64_t batch,
+                                 int64_t strideA, int64_t strideB, int64_t strideC,
+                                 const uint16_t *bias, int64_t strideBias, gemm_activation_t act,
+                                 hipStream_t stream) {
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
+    return run(Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, bias, strideBias,
+               act, stream);
+}
+
+gemm_status_t gemm_f16_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                                int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                                gemm_order_t orderB, float beta, void *C, int64_t ldc,
+                                gemm_order_t orderC, gemm_dtype_t c_dtype, int64_t batch,
+                                int64_t strideA, int64_t strideB, int64_t strideC,
+                                const uint16_t *bias, int64_t strideBias, gemm_activation_t act,
+                                hipStream_t stream) {
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
+    return run(Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+               orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, bias, strideBias,
+               act, stream);
 }
 
 const char *gemm_status_string(gemm_status_t status) {
@@ -290,7 +343,7 @@ const char *gemm_kernel_name(gemm_input_t in, int64_t M, int64_t N, int64_t K, f
     const gemm_status_t st =
         plan(ein, ein == Elem::F32 ? Elem::F32 : out_type(ein, c_dtype), M, N, K, alpha, A, lda,
              orderA, B, ldb, orderB, beta, const_cast<void *>(C), ldc, orderC, batch, strideA,
-             strideB, strideC, p, k);
+             strideB, strideC, nullptr, 0, GEMM_ACT_NONE, p, k);
     return st == GEMM_OK ? kernel_name(k) : nullptr;
 }
 

@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "epilogue.hpp"
+
 namespace libgemm {
 
 enum class Elem : int { F32 = 0, BF16 = 1, F16 = 2 };
@@ -28,6 +30,7 @@ struct Problem {
     int64_t ldc;
     int64_t batch, sA, sB, sC;  // batch count and per-batch strides (elements)
     Elem in, out;
+    Epilogue epi;               // bias and activation applied before the store
 };
 
 // Element size in bytes.

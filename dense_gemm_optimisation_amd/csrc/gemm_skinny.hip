@@ -74,6 +74,7 @@ struct SkinnyArgs {
     int64_t sA, sB, sC;
     int64_t tiles_n;
     int64_t kper;  // k per wave slice, a multiple of the k per chunk
+    Epilogue epi;
 };
 
 template <class T>
@@ -261,6 +262,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void skinny_kernel(SkinnyArgs p) {
             const int64_t off = m * p.ldc + n;
             float v = p.alpha * s;
             if (p.beta != 0.0f) v = __builtin_fmaf(p.beta, load_c<OUT>(Cb, off), v);
+            if (p.epi.active()) v = epilogue_apply(p.epi, v, batch, m, n);
             store_c<OUT>(Cb, off, v);
         }
     }
@@ -314,6 +316,7 @@ hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
     a.tiles_n = (p.N + TN - 1) / TN;
     const int64_t ck = CHUNK / (TN * elem_bytes(p.in));
     a.kper = ((p.K + WAVES * ck - 1) / (WAVES * ck)) * ck;
+    a.epi = p.epi;
     const int64_t blocks = a.tiles_n * p.batch;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (p.in == Elem::F32) return launch<F32, OUT_F32>(p, a, blocks, stream);

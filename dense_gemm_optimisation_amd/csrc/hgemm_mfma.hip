@@ -62,6 +62,7 @@ struct HgemmArgs {
     TileGrid grid;
     int vec_a, vec_b;
     int ubuf_a, ubuf_b;  // the operand's span fits a raw buffer (unaligned vector path)
+    Epilogue epi;
 };
 
 struct BF16 {};
@@ -326,6 +327,7 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
                     const int64_t off = row * p.ldc + col;
                     float v = p.alpha * acc[i][j][r];
                     if (p.beta != 0.0f) v = __builtin_fmaf(p.beta, load_c<OUT>(C, off), v);
+                    if (p.epi.active()) v = epilogue_apply(p.epi, v, t.batch, row, col);
                     store_c<OUT>(C, off, v);
                 }
             }
@@ -379,6 +381,7 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
     const int64_t span_b = p.b_kmajor ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
     a.ubuf_a = 2 * span_a + 4 < (int64_t(1) << 31);
     a.ubuf_b = 2 * span_b + 4 < (int64_t(1) << 31);
+    a.epi = p.epi;
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)
         return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)

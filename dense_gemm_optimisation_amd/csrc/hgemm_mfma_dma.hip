@@ -77,6 +77,7 @@ struct DmaArgs {
     int64_t sA, sB, sC;
     TileGrid grid;
     int vec_c;
+    Epilogue epi;
 };
 
 struct BF16 {};
@@ -235,6 +236,34 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
         return OUT == OUT_BF16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(x))
                                : __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
     };
+    // Fused epilogue: the bias values this lane adds, loaded up front (its
+    // columns are the same in every row it writes; its rows are known).
+    const bool epi = p.epi.active();
+    const int lcc = (lane % CPR) * CW;
+    float bcol[CW], brow[FM][32 / RPI];
+#pragma unroll
+    for (int e = 0; e < CW; ++e) bcol[e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) brow[i][it] = 0.0f;
+    if (p.epi.bias != nullptr) {
+        if (p.epi.per_row) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int it = 0; it < 32 / RPI; ++it)
+                    brow[i][it] = epilogue_bias_or_zero(p.epi, batch,
+                                                        mw + i * 32 + it * RPI + lane / CPR, p.M);
+        } else {
+#pragma unroll
+            for (int e = 0; e < CW; ++e)
+                bcol[e] = epilogue_bias_or_zero(p.epi, batch, nw + lcc + e, p.N);
+        }
+    }
+    auto finish = [&](float v, int i, int it, int e) {
+        return epilogue_act(p.epi.act, v + bcol[e] + brow[i][it]);
+    };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         // stage alpha*acc of strip i
@@ -270,6 +299,9 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, o[e], v[e]);
                     }
+                    if (epi)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = finish(v[e], i, it, e);
                     *reinterpret_cast<f32x4 *>(c) = v;
                 } else {
                     uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off;
@@ -279,6 +311,9 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
                         for (int e = 0; e < 8; ++e)
                             x[e] = __builtin_fmaf(p.beta, dec(uint16_t(o[e / 2] >> (16 * (e % 2)))), x[e]);
                     }
+                    if (epi)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] = finish(x[e], i, it, e);
                     u32x4 w;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = uint32_t(enc(x[2 * e])) | (uint32_t(enc(x[2 * e + 1])) << 16);
@@ -289,10 +324,14 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
                 for (int e = 0; e < nvalid; ++e) {
                     if (OUT == OUT_F32) {
                         float *c = reinterpret_cast<float *>(Cb) + off + e;
-                        *c = p.beta != 0.0f ? __builtin_fmaf(p.beta, *c, x[e]) : x[e];
+                        float v = p.beta != 0.0f ? __builtin_fmaf(p.beta, *c, x[e]) : x[e];
+                        if (epi) v = finish(v, i, it, e);
+                        *c = v;
                     } else {
                         uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off + e;
-                        *c = enc(p.beta != 0.0f ? __builtin_fmaf(p.beta, dec(*c), x[e]) : x[e]);
+                        float v = p.beta != 0.0f ? __builtin_fmaf(p.beta, dec(*c), x[e]) : x[e];
+                        if (epi) v = finish(v, i, it, e);
+                        *c = enc(v);
                     }
                 }
             }
@@ -555,6 +594,7 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
     // 16-byte chunks of C rows (8 bf16/fp16 or 4 fp32 elements)
     const int cw = 16 / esz;
     a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % 16) == 0 && p.ldc % cw == 0 && a.sC % cw == 0;
+    a.epi = p.epi;
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)
         return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)

@@ -61,6 +61,7 @@ struct SplitArgs {
     int64_t sA, sB, sC;
     int64_t tiles_m, tiles_n;
     int64_t kper;  // k values per wave slice (a multiple of CK)
+    Epilogue epi;
 };
 
 struct BF16 {};
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void hgemm_splitk_kernel(SplitArgs p
             const int64_t off = m * p.ldc + n;
             float v = p.alpha * s;
             if (p.beta != 0.0f) v = __builtin_fmaf(p.beta, load_c<OUT>(Cb, off), v);
+            if (p.epi.active()) v = epilogue_apply(p.epi, v, batch, m, n);
             store_c<OUT>(Cb, off, v);
         }
     }
@@ -293,6 +295,7 @@ hipError_t launch_hgemm_splitk(const Problem &p, hipStream_t stream) {
     a.tiles_m = (p.M + TILE - 1) / TILE;
     a.tiles_n = (p.N + TILE - 1) / TILE;
     a.kper = ((p.K + WAVES * CK - 1) / (WAVES * CK)) * CK;
+    a.epi = p.epi;
     const int64_t blocks = a.tiles_m * a.tiles_n * p.batch;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool bf = p.in == Elem::BF16;

@@ -1,6 +1,7 @@
 // C <- beta * C for the calls whose product term vanishes (alpha == 0 or
-// K == 0), where A and B are not read.  With beta == 0, C is written with
-// zeros without being read, so NaN or Inf already in C does not propagate.
+// K == 0), where A and B are not read, followed by the fused epilogue (bias,
+// activation) when one is requested.  With beta == 0, C is written without
+// being read, so NaN or Inf already in C does not propagate.
 #include "gemm_problem.hpp"
 
 namespace libgemm {
@@ -12,6 +13,7 @@ struct ScaleArgs {
     void *C;
     int64_t ldc, sC;
     int out;  // Elem of C
+    Epilogue epi;
 };
 
 __device__ inline float load_elem(const void *c, int64_t i, int out) {
@@ -39,7 +41,8 @@ __global__ __launch_bounds__(256) void scale_kernel(ScaleArgs a) {
         const int64_t r = e - b * a.M * a.N;
         const int64_t i = r / a.N, j = r - (r / a.N) * a.N;
         const int64_t off = b * a.sC + i * a.ldc + j;
-        const float v = a.beta == 0.0f ? 0.0f : a.beta * load_elem(a.C, off, a.out);
+        float v = a.beta == 0.0f ? 0.0f : a.beta * load_elem(a.C, off, a.out);
+        if (a.epi.active()) v = epilogue_apply(a.epi, v, b, i, j);
         store_elem(a.C, off, a.out, v);
     }
 }
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(256) void scale_kernel(ScaleArgs a) {
 
 hipError_t launch_scale(const Problem &p, hipStream_t stream) {
     ScaleArgs a{p.M, p.N, p.batch, p.beta, p.C, p.ldc, p.batch > 1 ? p.sC : 0,
-                static_cast<int>(p.out)};
+                static_cast<int>(p.out), p.epi};
     const int64_t total = p.M * p.N * p.batch;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;

@@ -64,11 +64,13 @@ struct SgemmArgs {
     int64_t sA, sB, sC;
     TileGrid grid;
     int vec_a, vec_b, vec_c;  // 16-byte vector access allowed for the operand
+    Epilogue epi;
 };
 
 // Four consecutive elements x[0..3] of one operand row, zero outside
 // [0, limit); `inside` says the whole row exists.
-__device__ inline f4 load4(const float *x, bool vec, bool inside, int64_t first, int64_t limit) {
+__device__ __attribute__((always_inline)) inline f4 load4(const float *x, bool vec, bool inside,
+                                                          int64_t first, int64_t limit) {
     if (vec && inside && first + 4 <= limit) return *reinterpret_cast<const f4 *>(x);
     f4 v;
 #pragma unroll
@@ -102,8 +104,9 @@ struct Panel {
     // Global -> registers for the K step at k0: two 4-float chunks per
     // thread.  `rows` is the operand's M (or N) extent, `x` its batch slice;
     // element (row, k) at x[row*ld + k] if KMAJOR, else at x[k*ld + row].
-    __device__ static void load(const float *x, int64_t ld, bool vec, int64_t r0, int64_t rows,
-                                int64_t k0, int64_t K, int tid, f4 v[2]) {
+    __device__ __attribute__((always_inline)) static void load(const float *x, int64_t ld, bool vec,
+                                                               int64_t r0, int64_t rows, int64_t k0,
+                                                               int64_t K, int tid, f4 v[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + THREADS * i;  // chunk id, 0..511
@@ -119,7 +122,7 @@ struct Panel {
         }
     }
 
-    __device__ static void store(float *s, int tid, const f4 v[2]) {
+    __device__ __attribute__((always_inline)) static void store(float *s, int tid, const f4 v[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + THREADS * i;
@@ -157,7 +160,7 @@ struct Panel {
 // whose top left corner is (mw, nw); C_old is not read when beta == 0.
 template <bool A_KMAJOR, bool B_KMAJOR>
 __device__ inline void store_c(const SgemmArgs &p, const f32x16 (&acc)[2][2], float *C, int64_t mw,
-                               int64_t nw, int idx, int half) {
+                               int64_t nw, int idx, int half, int64_t batch) {
     // Accumulator (i, j) register 4q + e of this lane holds
     // C[mw + Panel<A_KMAJOR>::row_of(i, idx)][nw + Panel<B_KMAJOR>::row_of(j, 8q + 4*half + e)]
     // (the instruction computes C^T, so B's tile index picks the column).
@@ -191,6 +194,9 @@ __device__ inline void store_c(const SgemmArgs &p, const f32x16 (&acc)[2][2], fl
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, old[e], v[e]);
                 }
+                if (p.epi.active())
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = epilogue_apply(p.epi, v[e], batch, row, col + e);
                 *reinterpret_cast<f4 *>(dst) = v;
             } else {
 #pragma unroll
@@ -198,6 +204,7 @@ __device__ inline void store_c(const SgemmArgs &p, const f32x16 (&acc)[2][2], fl
                     if (col + e < p.N) {
                         float x = v[e];
                         if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, dst[e], x);
+                        if (p.epi.active()) x = epilogue_apply(p.epi, x, batch, row, col + e);
                         dst[e] = x;
                     }
                 }
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_kernel(SgemmArgs p) {
         __syncthreads();
     }
 
-    store_c<A_KMAJOR, B_KMAJOR>(p, acc, C, m0 + wm * 64, n0 + wn * 64, idx, half);
+    store_c<A_KMAJOR, B_KMAJOR>(p, acc, C, m0 + wm * 64, n0 + wn * 64, idx, half, t.batch);
 }
 
 // Direct global -> LDS loads of one operand panel, same layouts as Panel:
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p)
     mfmas(1);
 
     float *C = p.C + t.batch * p.sC;
-    store_c<A_KMAJOR, B_KMAJOR>(p, acc, C, m0 + wm * 64, n0 + wn * 64, idx, half);
+    store_c<A_KMAJOR, B_KMAJOR>(p, acc, C, m0 + wm * 64, n0 + wn * 64, idx, half, t.batch);
 }
 
 template <bool AK, bool BK_>
@@ -476,6 +483,7 @@ SgemmArgs make_args(const Problem &p) {
     a.vec_a = vec16_ok(p.A, p.lda, a.sA, 4);
     a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 4);
     a.vec_c = vec16_ok(p.C, p.ldc, a.sC, 4);
+    a.epi = p.epi;
     return a;
 }
 

@@ -52,6 +52,7 @@ struct SplitArgs {
     int64_t sA, sB, sC;
     int64_t tiles_m, tiles_n;
     int64_t kper;  // k values per wave slice (a multiple of CK)
+    Epilogue epi;
 };
 
 // One operand of the tile: TILE rows (of A: m; of B: n) by a wave's K slice.
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void sgemm_splitk_kernel(SplitArgs p
             float *dst = C + m * p.ldc + n;
             float v = p.alpha * s;
             if (p.beta != 0.0f) v = __builtin_fmaf(p.beta, *dst, v);
+            if (p.epi.active()) v = epilogue_apply(p.epi, v, batch, m, n);
             *dst = v;
         }
     }
@@ -244,6 +246,7 @@ hipError_t launch_sgemm_splitk(const Problem &p, hipStream_t stream) {
     a.tiles_m = (p.M + TILE - 1) / TILE;
     a.tiles_n = (p.N + TILE - 1) / TILE;
     a.kper = ((p.K + WAVES * CK - 1) / (WAVES * CK)) * CK;
+    a.epi = p.epi;
     const int64_t blocks = a.tiles_m * a.tiles_n * p.batch;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (p.a_kmajor)

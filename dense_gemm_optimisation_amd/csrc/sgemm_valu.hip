@@ -48,6 +48,7 @@ struct SgemmArgs {
     int64_t sA, sB, sC;
     TileGrid grid;
     int vec_a, vec_b, vec_c;  // 16-byte vector access allowed for the operand
+    Epilogue epi;
 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -193,6 +194,9 @@ __global__ __launch_bounds__(THREADS, 1) void sgemm_kernel(SgemmArgs p) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(p.beta, old[j], v[j]);
                 }
+                if (p.epi.active())
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = epilogue_apply(p.epi, v[j], t.batch, row, col + j);
                 *reinterpret_cast<f4 *>(dst) = v;
             } else {
 #pragma unroll
@@ -200,6 +204,7 @@ __global__ __launch_bounds__(THREADS, 1) void sgemm_kernel(SgemmArgs p) {
                     if (col + j < p.N) {
                         float x = v[j];
                         if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, dst[j], x);
+                        if (p.epi.active()) x = epilogue_apply(p.epi, x, t.batch, row, col + j);
                         dst[j] = x;
                     }
                 }
@@ -239,6 +244,7 @@ hipError_t launch_sgemm(const Problem &p, hipStream_t stream) {
     a.vec_a = vec16_ok(p.A, p.lda, a.sA, 4);
     a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 4);
     a.vec_c = vec16_ok(p.C, p.ldc, a.sC, 4);
+    a.epi = p.epi;
     if (p.a_kmajor)
         return p.b_kmajor ? launch<true, true>(a, stream) : launch<true, false>(a, stream);
     return p.b_kmajor ? launch<false, true>(a, stream) : launch<false, false>(a, stream);

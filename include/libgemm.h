@@ -18,6 +18,9 @@
  *   gemm_bf16  bf16 inputs, fp32 accumulation on the matrix cores, output in
  *              bf16 (c_dtype = GEMM_DTYPE_SAME) or fp32 (GEMM_DTYPE_F32).
  *   gemm_f16   the same for IEEE fp16 inputs.
+ *   gemm_f32_bias_act, gemm_bf16_bias_act, gemm_f16_bias_act
+ *              the same products with a fused epilogue: a per-column bias
+ *              and an activation applied before the store (see below).
  *   gemm_kernel_name  which kernel a GEMM call with the given arguments would
  *              launch (host only; for tests and profiling).
  *
@@ -90,6 +93,12 @@ typedef enum gemm_input_t {
     GEMM_INPUT_F16 = 2
 } gemm_input_t;
 
+typedef enum gemm_activation_t {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1, /* max(x, 0) */
+    GEMM_ACT_GELU = 2  /* x * Phi(x), Phi the standard normal distribution function */
+} gemm_activation_t;
+
 typedef enum gemm_status_t {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_ARG = -1,
@@ -124,6 +133,59 @@ gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha,
                        float beta, void *C, int64_t ldc, gemm_order_t orderC,
                        gemm_dtype_t c_dtype, int64_t batch, int64_t strideA,
                        int64_t strideB, int64_t strideC, hipStream_t stream);
+
+/* Fused epilogue: C <- act(alpha * op(A) * op(B) + beta * C + bias), with
+ * the bias one value per column j of C (bias[j], added to every row) and
+ * act applied to each element after the bias, in fp32, before the rounding
+ * to the output type.  The pages fold "GEMM + bias + activation" into one
+ * kernel ("第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech, section 7.2)
+ * and apply element-wise operations such as ReLU to the accumulators before
+ * the store ("GPU GEMM 优化完全拆解（三）", pinghaoyang.com.cn, section on
+ * mainloop and epilogue).
+ *   bias        device vector of N elements of the input type (float for
+ *               gemm_f32_bias_act, bf16/fp16 bit patterns otherwise), or
+ *               NULL for no bias.  It must not overlap C.
+ *   strideBias  elements between the bias vectors of consecutive batch
+ *               entries (>= 0; 0 shares one vector).
+ *   act         GEMM_ACT_NONE, GEMM_ACT_RELU or GEMM_ACT_GELU.  GELU is
+ *               x * Phi(x); Phi is evaluated in fp32 through the rational
+ *               approximation 7.1.26 of Abramowitz and Stegun for erfc
+ *               (absolute error at most 1.5e-7 in Phi).
+ * All other arguments, the layouts, batch rules, ownership and errors are
+ * those of gemm_f32 / gemm_bf16 / gemm_f16; an act out of range, a negative
+ * strideBias or a bias overlapping C is GEMM_ERR_INVALID_ARG.  With
+ * alpha == 0 or K == 0 the result is act(beta * C + bias). */
+gemm_status_t gemm_f32_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                                const float *A, int64_t lda, gemm_order_t orderA,
+                                const float *B, int64_t ldb, gemm_order_t orderB,
+                                float beta, float *C, int64_t ldc,
+                                gemm_order_t orderC, int64_t batch,
+                                int64_t strideA, int64_t strideB,
+                                int64_t strideC, const float *bias,
+                                int64_t strideBias, gemm_activation_t act,
+                                hipStream_t stream);
+
+gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                                 const uint16_t *A, int64_t lda,
+                                 gemm_order_t orderA, const uint16_t *B,
+                                 int64_t ldb, gemm_order_t orderB, float beta,
+                                 void *C, int64_t ldc, gemm_order_t orderC,
+                                 gemm_dtype_t c_dtype, int64_t batch,
+                                 int64_t strideA, int64_t strideB,
+                                 int64_t strideC, const uint16_t *bias,
+                                 int64_t strideBias, gemm_activation_t act,
+                                 hipStream_t stream);
+
+gemm_status_t gemm_f16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                                const uint16_t *A, int64_t lda,
+                                gemm_order_t orderA, const uint16_t *B,
+                                int64_t ldb, gemm_order_t orderB, float beta,
+                                void *C, int64_t ldc, gemm_order_t orderC,
+                                gemm_dtype_t c_dtype, int64_t batch,
+                                int64_t strideA, int64_t strideB,
+                                int64_t strideC, const uint16_t *bias,
+                                int64_t strideBias, gemm_activation_t act,
+                                hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *gemm_status_string(gemm_status_t status);

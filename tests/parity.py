@@ -165,10 +165,11 @@ def default_sample(p: workloads.Problem, rng, n_random=4096):
 
 
 def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
-        base_offset=(0, 0, 0), repeat=1):
+        base_offset=(0, 0, 0), repeat=1, bias_host=None):
     """Run p on the GPU (optionally `repeat` times) and compare with the oracle.
 
     host: (A, B, C0) host buffers, else generated from the workload recipe.
+    bias_host: the bias buffer of a fused-epilogue problem, else generated.
     sample: None for every element, "auto" for default_sample, or an index array.
     c_init: a value written over the whole initial C (e.g. NaN when beta == 0).
     base_offset: elements by which each device base pointer is shifted (to
@@ -177,17 +178,21 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
     """
     log(f"[parity] {p.name} {p.in_dtype}->{p.c_dtype} M={p.M} N={p.N} K={p.K} "
         f"batch={p.batch} orders={p.order_a}{p.order_b}{p.order_c} "
-        f"ld={p.lda},{p.ldb},{p.ldc} alpha={p.alpha} beta={p.beta}")
+        f"ld={p.lda},{p.ldb},{p.ldc} alpha={p.alpha} beta={p.beta} bias={p.bias} act={p.act}")
     a, b, c0 = host if host is not None else workloads.generate(p, seed)
     if c_init is not None:
         c0 = np.full_like(c0, c_init)
+    bias = bias_host if bias_host is not None else workloads.bias_vector(p, seed)
     da, fa, sa = _device(a, p.in_dtype, base_offset[0])
     db, fb, sb = _device(b, p.in_dtype, base_offset[1])
     dc, fc, sc = _device(c0, p.c_dtype, base_offset[2])
+    if bias is not None:
+        dbias, fbias, sbias = _device(bias, p.in_dtype)
     esz_in = 4 if p.in_dtype == "f32" else 2
     esz_out = 4 if p.c_dtype == "f32" else 2
     pa, pb, pc = (da.data_ptr() + sa * esz_in, db.data_ptr() + sb * esz_in,
                   dc.data_ptr() + sc * esz_out)
+    pbias = dbias.data_ptr() + sbias * esz_in if bias is not None else None
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     cview = np.int32 if p.c_dtype == "f32" else np.int16
     kernel = binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb,
@@ -199,7 +204,7 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
             dc.copy_(torch.from_numpy(fc.view(cview)))
         binding.gemm(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
                      p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch, p.stride_a,
-                     p.stride_b, p.stride_c)
+                     p.stride_b, p.stride_c, bias=pbias, stride_bias=p.stride_bias, act=p.act)
         torch.cuda.synchronize()
         outs.append(dc.cpu().numpy().view(fc.dtype).copy())
     out = outs[0]
@@ -208,8 +213,9 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         res.ok, res.why = False, "repeated runs differ"
         return res, out
     if not (np.array_equal(da.cpu().numpy().view(fa.dtype), fa)
-            and np.array_equal(db.cpu().numpy().view(fb.dtype), fb)):
-        res.ok, res.why = False, "A or B was modified"
+            and np.array_equal(db.cpu().numpy().view(fb.dtype), fb)
+            and (bias is None or np.array_equal(dbias.cpu().numpy().view(fbias.dtype), fbias))):
+        res.ok, res.why = False, "A, B or the bias was modified"
         return res, out
     # everything outside the matrix C is bit-unchanged
     outside = np.ones(out.size, bool)
@@ -219,7 +225,8 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         res.ok, res.why = False, f"write outside C at buffer element {k} (data starts at {sc})"
         log(f"[parity]   -> FAIL {res.why}")
         return res, out
-    kw = dict(stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c)
+    kw = dict(stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c, bias=bias,
+              stride_bias=p.stride_bias, act=p.act)
     if sample is None:
         ref, den = oracle.gemm(p.in_dtype, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda, p.order_a,
                                b, p.ldb, p.order_b, p.beta, c0, p.ldc, p.order_c, batch=p.batch,

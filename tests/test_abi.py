@@ -27,8 +27,10 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_f16", "gemm_f32",
-                                    "gemm_kernel_name", "gemm_status_string"]
+    assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
+                                    "gemm_f16", "gemm_f16_bias_act", "gemm_f32",
+                                    "gemm_f32_bias_act", "gemm_kernel_name",
+                                    "gemm_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -125,6 +127,49 @@ def test_adjacent_buffers_are_not_overlap(lib):
     assert call(lib, "f32", M=0, C=P + 4 * 64) == lib.OK
 
 
+def epi_call(lib, fn="f32", bias=P * 7, stride_bias=0, act=0, **kw):
+    args = dict(M=8, N=8, K=8, alpha=1.0, A=P, lda=8, oa=0, B=P * 3, ldb=8, ob=0, beta=0.0,
+                C=P * 5, ldc=8, oc=0, c_dtype=0, batch=1, sa=0, sb=0, sc=0)
+    args.update(kw)
+    a = args
+    if fn == "f32":
+        return lib.gemm_f32_bias_act(a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["oa"],
+                                     a["B"], a["ldb"], a["ob"], a["beta"], a["C"], a["ldc"],
+                                     a["oc"], a["batch"], a["sa"], a["sb"], a["sc"], bias,
+                                     stride_bias, act, 0, raise_on_error=False)
+    f = lib.gemm_bf16_bias_act if fn == "bf16" else lib.gemm_f16_bias_act
+    return f(a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["oa"], a["B"], a["ldb"],
+             a["ob"], a["beta"], a["C"], a["ldc"], a["oc"], a["c_dtype"], a["batch"], a["sa"],
+             a["sb"], a["sc"], bias, stride_bias, act, 0, raise_on_error=False)
+
+
+@pytest.mark.parametrize("fn", ["f32", "bf16", "f16"])
+def test_fused_epilogue_invalid_arguments(lib, fn):
+    esz = 4 if fn == "f32" else 2
+    assert epi_call(lib, fn, act=3) == lib.ERR_INVALID_ARG
+    assert epi_call(lib, fn, act=-1) == lib.ERR_INVALID_ARG
+    assert epi_call(lib, fn, stride_bias=-1) == lib.ERR_INVALID_ARG
+    # the bias may not overlap C (C spans 64 elements from P*5)
+    assert epi_call(lib, fn, bias=P * 5 + esz * 60) == lib.ERR_INVALID_ARG
+    # ... nor, through its batch stride, reach into C
+    assert epi_call(lib, fn, bias=P * 5 - esz * 100, stride_bias=70, batch=3, sc=64) == \
+        lib.ERR_INVALID_ARG
+    # the usual checks still apply
+    assert epi_call(lib, fn, M=-1) == lib.ERR_INVALID_ARG
+    assert epi_call(lib, fn, lda=7) == lib.ERR_INVALID_ARG
+    if fn != "f32":
+        assert epi_call(lib, fn, c_dtype=2) == lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", ["f32", "bf16", "f16"])
+def test_fused_epilogue_empty_problems_and_null_bias(lib, fn):
+    assert epi_call(lib, fn, M=0, act=2) == lib.OK
+    assert epi_call(lib, fn, batch=0, bias=0, act=1) == lib.OK
+    # a bias right after C is fine (C is 64 elements); M == 0 launches nothing
+    esz = 4 if fn == "f32" else 2
+    assert epi_call(lib, fn, M=0, bias=P * 5 + esz * 64) == lib.OK
+
+
 def test_raises_on_error(lib):
     with pytest.raises(lib.GemmError) as e:
         lib.gemm_f32(-1, 1, 1, 1.0, P, 1, 0, P, 1, 0, 0.0, P, 1, 0)
@@ -216,7 +261,8 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_qkv": "hgemm_mfma_dma", "bf16_ffn_up": "hgemm_mfma_dma",
             "bf16_ffn_down": "hgemm_mfma_dma", "f32_edge": "sgemm_mfma",
             "bf16_edge": "hgemm_mfma", "bf16_skinny": "gemm_skinny",
-            "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma"}
+            "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma",
+            "bf16_ffn_up_gelu": "hgemm_mfma_dma"}
     assert sorted(want) == sorted(workloads.CONFIGS)
     for name, k in want.items():
         p = workloads.config(name)

@@ -198,7 +198,8 @@ def test_repeat_runs_bit_identical(dt):
 
 SMALL_CONFIGS = ["f32_256"]
 FULL_CONFIGS = ["f32_4096", "bf16_4096", "f16_4096", "f32_edge", "bf16_edge", "bf16_skinny",
-                "bf16_attn_qk", "bf16_attn_pv", "bf16_qkv", "bf16_ffn_up", "bf16_ffn_down"]
+                "bf16_attn_qk", "bf16_attn_pv", "bf16_qkv", "bf16_ffn_up", "bf16_ffn_down",
+                "bf16_ffn_up_gelu"]
 
 
 @pytest.mark.parametrize("name", SMALL_CONFIGS)
@@ -333,6 +334,76 @@ def test_skinny_column_major_c_and_integers(dt):
           order_b=COL if dt == "f32" else ROW)
     res, _ = check(p, kernel="gemm_skinny", host=_int_host(p, np.random.default_rng(73)))
     assert res.max_err == 0.0
+
+
+# ------------------------------------------------------------------ fused epilogue (bias, activation)
+
+RELU, GELU = 1, 2
+EPI_CASES = [
+    # (input type, output type, M, N, K, extra problem fields, kernel)
+    ("f32", "f32", 520, 264, 200, {}, "sgemm_mfma_dma"),
+    ("f32", "f32", 190, 211, 97, {}, "sgemm_mfma"),
+    ("f32", "f32", 64, 136, 512, {}, "sgemm_splitk"),
+    ("f32", "f32", 8, 136, 512, dict(order_b=COL), "gemm_skinny"),
+    ("bf16", "bf16", 520, 264, 200, {}, "hgemm_mfma_dma"),
+    ("bf16", "f32", 520, 264, 200, {}, "hgemm_mfma_dma"),
+    ("f16", "f16", 520, 264, 200, dict(order_a=COL, order_b=COL), "hgemm_mfma_dma"),
+    ("bf16", "bf16", 190, 211, 97, {}, "hgemm_mfma"),
+    ("bf16", "bf16", 64, 136, 1024, {}, "hgemm_splitk"),
+    ("f16", "f32", 8, 136, 512, {}, "gemm_skinny"),
+]
+
+
+@pytest.mark.parametrize("case", EPI_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[6]}")
+@pytest.mark.parametrize("act", [0, RELU, GELU], ids=["bias", "bias-relu", "bias-gelu"])
+def test_fused_bias_and_activation(case, act):
+    dt, ct, M, N, K, extra, kernel = case
+    check(P(f"epi-{dt}-{kernel}-{act}", dt, M, N, K, c_dtype=ct, alpha=0.75, beta=0.5,
+            bias=True, act=act, **extra), kernel=kernel, seed=M + N + act)
+
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("act", [RELU, GELU], ids=["relu", "gelu"])
+def test_fused_activation_without_bias(dt, act):
+    check(P(f"epi-nobias-{dt}", dt, 264, 520, 136, act=act), seed=81 + act)
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_fused_epilogue_col_major_c_and_batches(dt):
+    # column-major C: the library computes C^T, where the bias runs along rows
+    check(P(f"epi-colC-{dt}", dt, 520, 264, 200, order_c=COL, beta=0.5, bias=True, act=RELU),
+          seed=82)
+    # one bias vector per batch entry, and one shared by all
+    check(P(f"epi-batch-{dt}", dt, 264, 136, 200, batch=3, bias=True, act=GELU), seed=83)
+    check(P(f"epi-batch-shared-{dt}", dt, 264, 136, 200, batch=3, bias=True, stride_bias=0,
+            act=GELU), seed=84)
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_fused_epilogue_without_product_term(dt):
+    # alpha == 0 and K == 0: C <- act(beta*C + bias), A and B not read
+    check(P(f"epi-alpha0-{dt}", dt, 130, 70, 40, alpha=0.0, beta=0.5, bias=True, act=RELU),
+          kernel="scale", seed=85)
+    check(P(f"epi-k0-{dt}", dt, 130, 70, 0, beta=-1.5, bias=True, act=GELU), kernel="scale",
+          seed=86)
+
+
+def test_fused_epilogue_on_vector_alu_kernel(monkeypatch):
+    monkeypatch.setenv("LIBGEMM_F32_VALU", "1")
+    check(P("epi-valu", "f32", 520, 264, 200, beta=0.5, bias=True, act=GELU),
+          kernel="sgemm_valu", seed=87)
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_fused_relu_bias_integers_bit_exact(dt):
+    # integer data and an integer bias: every step is exact, and so is ReLU
+    p = P(f"epi-int-{dt}", dt, 264, 136, 200, alpha=2.0, beta=1.0, bias=True, act=RELU)
+    rng = np.random.default_rng(88)
+    bias = rng.integers(-200, 201, p.N).astype(np.float32)
+    bias = bias if dt == "f32" else workloads.to_16bit(bias, dt)
+    res, _ = check(p, kernel="sgemm_mfma_dma" if dt == "f32" else "hgemm_mfma_dma",
+                   host=_int_host(p, rng), bias_host=bias)
+    assert res.max_err == 0.0 and res.max_ulp == 0
 
 
 # ------------------------------------------------------------------ split-K path (few tiles, long K)

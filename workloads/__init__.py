@@ -16,7 +16,10 @@ listed here, so the reading taken is stated once, here):
   float32, then to the 16-bit type with round-to-nearest-even (torch's CPU
   conversion);
 * softmax rows (the attention probabilities): logits uniform(-1, 1), a
-  row-wise softmax in float64, then rounded like any bf16 entry.
+  row-wise softmax in float64, then rounded like any bf16 entry;
+* the bias of a problem with a fused epilogue comes from a second stream,
+  ``np.random.default_rng([seed, 1])``, N entries per batch entry (one vector
+  when ``stride_bias`` is 0), drawn like an entry of A with ``sigma_bias``.
 
 Shapes follow the pages: the square 4096 problem of "CUDA GEMM 矩阵乘法优化指南"
 section 2.1 and of the hgemm sm120 article's benchmark; the transformer-layer
@@ -65,6 +68,11 @@ class Problem:
     a_kind: str = "default"          # "default" or "softmax" (rows of P)
     seed: int = 0
     note: str = ""
+    # fused epilogue: C = act(alpha*A@B + beta*C + bias_j)
+    bias: bool = False               # add a per-column bias vector
+    stride_bias: Optional[int] = None  # elements between batch entries' vectors
+    sigma_bias: float = 1.0
+    act: int = 0                     # 0 none, 1 ReLU, 2 GELU
 
     def __post_init__(self):
         M, N, K = self.M, self.N, self.K
@@ -80,6 +88,8 @@ class Problem:
             self.stride_b = self.footprint("b")
         if self.stride_c is None:
             self.stride_c = self.footprint("c")
+        if self.stride_bias is None:
+            self.stride_bias = N if self.batch > 1 else 0
 
     def dims(self, which):
         return {"a": (self.M, self.K, self.order_a, self.lda),
@@ -170,6 +180,20 @@ def generate(p: Problem, seed: Optional[int] = None):
     return bufs["a"], bufs["b"], bufs["c"]
 
 
+def bias_vector(p: Problem, seed: Optional[int] = None):
+    """The bias of a fused-epilogue problem as a flat stored-type buffer of
+    (batch - 1) * stride_bias + N elements, or None when p has no bias."""
+    if not p.bias:
+        return None
+    rng = np.random.default_rng([p.seed if seed is None else seed, 1])
+    n = (p.batch - 1) * p.stride_bias + p.N if p.batch > 0 else 0
+    out = np.zeros(n, np.float32 if p.in_dtype == "f32" else np.uint16)
+    for b in range(1 if p.stride_bias == 0 else p.batch):
+        out[b * p.stride_bias:b * p.stride_bias + p.N] = _draw(rng, p.in_dtype, 1, p.N,
+                                                               p.sigma_bias)[0]
+    return out
+
+
 def _configs():
     cfgs = [
         Problem("f32_256", "f32", "f32", 256, 256, 256,
@@ -198,6 +222,11 @@ def _configs():
                 batch=32, note="batched QK^T, 32 x (2048x128)(128x2048)"),
         Problem("bf16_attn_pv", "bf16", "bf16", 2048, 128, 2048, a_kind="softmax",
                 batch=32, note="batched PV, 32 x (2048x2048)(2048x128), P softmax rows"),
+        # the FFN up projection with its bias and activation fused into the
+        # GEMM's epilogue (the "GEMM + bias + activation" case of the pages)
+        Problem("bf16_ffn_up_gelu", "bf16", "bf16", 4096, 16384, 4096, sigma_b=0.02,
+                bias=True, act=2,
+                note="FFN up X(4096x4096) W1(4096x16384) + b1 then GELU, fused epilogue"),
     ]
     return {c.name: c for c in cfgs}
 
