@@ -9,7 +9,8 @@ its header for the passages it follows).  This module only marshals numpy
 buffers into it.
 
 Element types: ``"f32"`` buffers are float32 (or their uint32 bit patterns),
-``"bf16"`` and ``"f16"`` buffers are uint16 bit patterns.  Matrices are flat
+``"bf16"`` and ``"f16"`` buffers are uint16 bit patterns, ``"e4m3"`` and
+``"e5m2"`` (8-bit floats) uint8 bit patterns.  Matrices are flat
 buffers addressed with a leading dimension, an order (``ROW`` or ``COL``) and
 a per-batch stride in elements, exactly as the GEMM library takes them.
 """
@@ -22,7 +23,7 @@ from . import build as _build
 
 ROW, COL = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
-_TYPES = {"f32": 0, "bf16": 1, "f16": 2}
+_TYPES = {"f32": 0, "bf16": 1, "f16": 2, "e4m3": 3, "e5m2": 4}
 
 _lib = None
 
@@ -37,7 +38,7 @@ def _load():
         lib = ctypes.CDLL(path)
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         prob = [i32, i32, i64, i64, i64, dbl, vp, i64, i32, vp, i64, i32, dbl, vp, i64,
-                i32, i64, i64, i64, vp, i64, i32]
+                i32, i64, i64, i64, vp, i64, i32, i32]
         lib.orc_gemm.argtypes = prob + [i64, vp, vp]
         lib.orc_gemm.restype = None
         lib.orc_gemm_at.argtypes = prob + [i64, vp, vp, vp]
@@ -52,7 +53,9 @@ def _load():
 
 
 def _storage(dtype):
-    return np.float32 if dtype == "f32" else np.uint16
+    if dtype == "f32":
+        return np.float32
+    return np.uint8 if dtype in ("e4m3", "e5m2") else np.uint16
 
 
 def _buf(x, dtype):
@@ -92,32 +95,34 @@ def round_bits(dtype, x) -> np.ndarray:
 
 
 def _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
-          ldc, order_c, stride_a, stride_b, stride_c, bias, stride_bias, act):
+          ldc, order_c, stride_a, stride_b, stride_c, bias, stride_bias, act, b_dtype):
+    b_dtype = b_dtype or in_dtype
     keep = []
     ptrs = []
-    for x, dt in ((A, in_dtype), (B, in_dtype), (C0, c_dtype), (bias, in_dtype)):
+    for x, dt in ((A, in_dtype), (B, b_dtype), (C0, c_dtype), (bias, in_dtype)):
         a, p = _buf(x, dt)
         keep.append(a)
         ptrs.append(p)
     args = [_TYPES[in_dtype], _TYPES[c_dtype], M, N, K, float(alpha), ptrs[0], lda, order_a,
             ptrs[1], ldb, order_b, float(beta), ptrs[2], ldc, order_c, stride_a, stride_b,
-            stride_c, ptrs[3], stride_bias, int(act)]
+            stride_c, ptrs[3], stride_bias, int(act), _TYPES[b_dtype]]
     return args, keep
 
 
 def gemm(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
          ldc, order_c, batch=1, stride_a=0, stride_b=0, stride_c=0, bias=None, stride_bias=0,
-         act=ACT_NONE):
+         act=ACT_NONE, b_dtype=None):
     """Every element: returns (ref, den) as float64 arrays [batch][M][N].
 
     ref = act(alpha*sum_k A_ik B_kj + beta*C0_ij + bias_j) and
     den = |alpha|*sum_k |A_ik B_kj| + |beta|*|C0_ij| + |bias_j|, accumulated in
     double.  ``bias`` (optional) holds N input-type elements per batch entry,
     ``stride_bias`` apart; ``act`` is ACT_NONE, ACT_RELU or ACT_GELU.
+    ``b_dtype`` is B's element type when it differs from A's (8-bit inputs).
     """
     args, keep = _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b,
                        beta, C0, ldc, order_c, stride_a, stride_b, stride_c, bias, stride_bias,
-                       act)
+                       act, b_dtype)
     ref = np.empty((batch, M, N), np.float64)
     den = np.empty((batch, M, N), np.float64)
     _load().orc_gemm(*args, batch, ref.ctypes.data, den.ctypes.data)
@@ -127,12 +132,12 @@ def gemm(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, be
 
 def gemm_at(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C0,
             ldc, order_c, idx, stride_a=0, stride_b=0, stride_c=0, bias=None, stride_bias=0,
-            act=ACT_NONE):
+            act=ACT_NONE, b_dtype=None):
     """Only the elements listed in ``idx`` (an (n, 3) array of (b, i, j))."""
     idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 3)
     args, keep = _args(in_dtype, c_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b,
                        beta, C0, ldc, order_c, stride_a, stride_b, stride_c, bias, stride_bias,
-                       act)
+                       act, b_dtype)
     n = idx.shape[0]
     ref = np.empty(n, np.float64)
     den = np.empty(n, np.float64)

@@ -33,6 +33,13 @@
  * standard normal distribution function, 0.5 * (1 + erf(x / sqrt 2)).  den
  * gains |bias_j|; it stays the scale of the terms before the activation.
  *
+ * 8-bit inputs: the pages list the 8-bit floating formats E4M3 and E5M2 for
+ * matrix units ("第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech, section
+ * 13.2).  They are the OCP formats: E4M3 has no infinities and one NaN
+ * pattern per sign (S.1111.111), largest finite 448; E5M2 follows the IEEE
+ * rules (infinities at exponent 31 with a zero fraction, NaNs otherwise).
+ * Both have subnormals.  A and B may be in different 8-bit formats.
+ *
  * Readings taken where the pages are silent:
  *   - beta == 0: C0 is not read (BLAS convention), so NaN in C0 does not leak.
  *   - alpha == 0 or K == 0: the product term is skipped and A, B are not read.
@@ -46,6 +53,8 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_F16 2
+#define ORC_E4M3 3 /* OCP 8-bit float: 1 sign, 4 exponent (bias 7), 3 fraction bits */
+#define ORC_E5M2 4 /* OCP 8-bit float: 1 sign, 5 exponent (bias 15), 2 fraction bits */
 
 #define ORC_ROW 0
 #define ORC_COL 1
@@ -80,6 +89,36 @@ static double decode_f16(uint16_t bits) {
     return sign ? -v : v;
 }
 
+/* E4M3: value (1 + m/8) * 2^(e-7), subnormal m/8 * 2^-6; S.1111.111 is NaN. */
+static double decode_e4m3(uint8_t bits) {
+    int sign = bits >> 7;
+    int e = (bits >> 3) & 0xf;
+    int m = bits & 0x7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);           /* m/8 * 2^-6 */
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* E5M2: value (1 + m/4) * 2^(e-15), subnormal m/4 * 2^-14; e == 31 is Inf/NaN. */
+static double decode_e5m2(uint8_t bits) {
+    int sign = bits >> 7;
+    int e = (bits >> 2) & 0x1f;
+    int m = bits & 0x3;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -16);          /* m/4 * 2^-14 */
+    else
+        v = ldexp((double)(4 + m), e - 17); /* (1 + m/4) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
 static double load(int type, const void *base, int64_t idx) {
     switch (type) {
     case ORC_F32: {
@@ -89,6 +128,10 @@ static double load(int type, const void *base, int64_t idx) {
     }
     case ORC_BF16:
         return decode_bf16(((const uint16_t *)base)[idx]);
+    case ORC_E4M3:
+        return decode_e4m3(((const uint8_t *)base)[idx]);
+    case ORC_E5M2:
+        return decode_e5m2(((const uint8_t *)base)[idx]);
     default:
         return decode_f16(((const uint16_t *)base)[idx]);
     }
@@ -149,7 +192,7 @@ static uint16_t encode_f16(double r) {
 
 /* ---------------------------------------------------------------- exports */
 
-int orc_version(void) { return 2; }
+int orc_version(void) { return 3; }
 
 void orc_decode(int type, const void *src, double *dst, int64_t n) {
     for (int64_t i = 0; i < n; ++i) dst[i] = load(type, src, i);
@@ -178,6 +221,7 @@ void orc_round(int type, const double *src, void *dst, int64_t n) {
 
 struct problem {
     int in_type, c_type;
+    int b_type; /* type of B (and of the bias: in_type) */
     int64_t M, N, K;
     double alpha, beta;
     const void *A, *B, *C0;
@@ -202,7 +246,7 @@ static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
         const int64_t a0 = b * P->sA, b0 = b * P->sB;
         for (int64_t k = 0; k < P->K; ++k) {
             double a = load(P->in_type, P->A, a0 + offset(P->oA, i, k, P->lda));
-            double x = load(P->in_type, P->B, b0 + offset(P->oB, k, j, P->ldb));
+            double x = load(P->b_type, P->B, b0 + offset(P->oB, k, j, P->ldb));
             double p = a * x;
             s = s + p;
             t = t + fabs(p);
@@ -232,12 +276,12 @@ static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
     int in_type, int c_type, int64_t M, int64_t N, int64_t K, double alpha,            \
         const void *A, int64_t lda, int oA, const void *B, int64_t ldb, int oB,        \
         double beta, const void *C0, int64_t ldc, int oC, int64_t sA, int64_t sB,      \
-        int64_t sC, const void *bias, int64_t sBias, int act
+        int64_t sC, const void *bias, int64_t sBias, int act, int b_type
 
 #define PROBLEM_INIT                                                                   \
-    struct problem P = {in_type, c_type, M,  N,  K,  alpha, beta, A,     B,    C0,    \
-                        lda,     ldb,    ldc, oA, oB, oC,    sA,   sB,    sC,   bias, \
-                        sBias,   act}
+    struct problem P = {in_type, c_type, b_type, M,     N,  K,  alpha, beta, A,     \
+                        B,       C0,     lda,    ldb,   ldc, oA, oB,    oC,   sA,    \
+                        sB,      sC,     bias,   sBias, act}
 
 /* All batch*M*N elements; ref and den are dense [batch][M][N]. */
 void orc_gemm(PROBLEM_ARGS, int64_t batch, double *ref, double *den) {

@@ -40,6 +40,12 @@ MUTANTS = {
     "gelu_tanh_form": ("r = r * 0.5 * (1.0 + erf(r / sqrt(2.0)));",
                        "r = r * 0.5 * (1.0 + tanh(0.7978845608 * (r + 0.044715 * r * r * r)));"),
     "gelu_wrong_scale": ("erf(r / sqrt(2.0))", "erf(r / 2.0)"),
+    "e4m3_bias_off": ("e - 10); /* (1 + m/8)", "e - 9); /* (1 + m/8)"),
+    "e4m3_nan_rule": ("if (e == 15 && m == 7)", "if (e == 15)"),
+    "e5m2_subnormal_scale": ("ldexp((double)m, -16)", "ldexp((double)m, -15)"),
+    "e5m2_inf_as_nan": ("v = m ? NAN : INFINITY;\n    else if (e == 0)\n        v = ldexp((double)m, -16);",
+                        "v = NAN;\n    else if (e == 0)\n        v = ldexp((double)m, -16);"),
+    "b_type_ignored": ("load(P->b_type, P->B", "load(P->in_type, P->B"),
 }
 
 

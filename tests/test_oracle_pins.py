@@ -492,3 +492,62 @@ def test_bias_is_per_column_and_per_batch_entry():
             want = 0.5 * c0[b * M * N:(b + 1) * M * N].reshape(M, N) + \
                 bias[b * stride:b * stride + N][None, :]
             assert np.array_equal(ref[b], want), (stride, b)
+
+
+# --------------------------------------------------------------- 8-bit inputs
+
+def torch_decode_8bit(dtype, bits):
+    """Decode 8-bit patterns with torch's float8 types (independent of the oracle)."""
+    import torch
+    tdt = torch.float8_e4m3fn if dtype == "e4m3" else torch.float8_e5m2
+    return torch.from_numpy(np.asarray(bits, np.uint8)).view(tdt).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "e5m2"])
+def test_decode_every_8bit_pattern(dtype):
+    bits = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(dtype, bits)
+    want = torch_decode_8bit(dtype, bits)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    # the format limits the pages' formats imply
+    if dtype == "e4m3":
+        assert np.nanmax(got) == 448.0 and np.isnan(got).sum() == 2 and not np.isinf(got).any()
+    else:
+        assert np.nanmax(got[~np.isinf(got)]) == 57344.0 and np.isinf(got).sum() == 2
+
+
+def stored8(dtype, values):
+    import torch
+    tdt = torch.float8_e4m3fn if dtype == "e4m3" else torch.float8_e5m2
+    t = torch.from_numpy(np.asarray(values, np.float32)).to(tdt)
+    return t.view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"),
+                                   ("e5m2", "e4m3")])
+def test_8bit_integer_product_matches_int64(fa, fb):
+    # integers of magnitude <= 7 are exact in both formats and every double
+    # operation on them is exact: the oracle must equal the int64 product
+    rng = np.random.default_rng(31)
+    M, N, K = 19, 23, 41
+    A = rng.integers(-7, 8, (M, K))
+    B = rng.integers(-7, 8, (K, N))
+    for oA, oB in ((ROW, COL), (ROW, ROW), (COL, ROW)):
+        Ab, lda = put(stored8(fa, A), oA)
+        Bb, ldb = put(stored8(fb, B), oB)
+        ref, den = oracle.gemm(fa, "f32", M, N, K, 1.0, Ab, lda, oA, Bb, ldb, oB, 0.0, None, N,
+                               ROW, b_dtype=fb)
+        assert np.array_equal(ref[0], (A @ B).astype(np.float64)), (oA, oB)
+        assert np.array_equal(den[0], (np.abs(A) @ np.abs(B)).astype(np.float64))
+
+
+def test_8bit_formats_are_read_per_operand():
+    # 0x3c is 1.5 in E4M3 and 1.0 in E5M2; a 1 x 1 x 1 product tells them apart
+    a = np.array([0x3c], np.uint8)
+    for fa, fb, want in (("e4m3", "e4m3", 2.25), ("e4m3", "e5m2", 1.5), ("e5m2", "e4m3", 1.5),
+                         ("e5m2", "e5m2", 1.0)):
+        ref, _ = oracle.gemm(fa, "f32", 1, 1, 1, 1.0, a, 1, ROW, a, 1, ROW, 0.0, None, 1, ROW,
+                             b_dtype=fb)
+        assert ref[0, 0, 0] == want, (fa, fb)
