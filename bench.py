@@ -36,7 +36,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense, published
+# MI355X dense peaks, published (8-bit floats: twice the 16-bit rate)
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2}
+ESIZE = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1, "e5m2": 1}
+VIEW = {"f32": np.float32, "bf16": np.int16, "f16": np.int16, "e4m3": np.int8, "e5m2": np.int8}
 HBM_GBS = 8000.0
 
 HEADLINE = ["f32_4096", "bf16_4096", "f16_4096"]
@@ -46,6 +49,7 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "sgemm_valu": "sgemm_valu.hip", "hgemm_mfma_dma": "hgemm_mfma_dma.hip",
                  "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip",
                  "sgemm_splitk": "sgemm_splitk.hip", "gemm_skinny": "gemm_skinny.hip",
+                 "f8gemm_mfma_dma": "f8gemm_mfma.hip", "f8gemm_mfma": "f8gemm_mfma.hip",
                  "scale": "scale.hip"}
 
 
@@ -56,10 +60,9 @@ def log(*a):
 def device_buffers(p, torch):
     import workloads
     a, b, c = workloads.generate(p)
-    view = np.float32 if p.in_dtype == "f32" else np.int16
-    cview = np.float32 if p.c_dtype == "f32" else np.int16
-    return (torch.from_numpy(a.view(view)).to("cuda"), torch.from_numpy(b.view(view)).to("cuda"),
-            torch.from_numpy(c.view(cview)).to("cuda"))
+    return (torch.from_numpy(a.view(VIEW[p.in_dtype])).to("cuda"),
+            torch.from_numpy(b.view(VIEW[p.b_dtype])).to("cuda"),
+            torch.from_numpy(c.view(VIEW[p.c_dtype])).to("cuda"))
 
 
 def device_bias(p, torch):
@@ -99,7 +102,7 @@ def make_launch(p, sets, stream, bias=None):
                 p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch,
                 p.stride_a, p.stride_b, p.stride_c, stream.cuda_stream) for da, db, dc in sets]
     epi = dict(bias=None if bias is None else bias.data_ptr(), stride_bias=p.stride_bias,
-               act=p.act)
+               act=p.act, b_dtype=p.b_dtype, out_dtype=p.c_dtype)
     turn = [0]
 
     def launch():
@@ -117,7 +120,8 @@ def kernel_family(p, bufs):
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     return binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a,
                                db.data_ptr(), p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc,
-                               p.order_c, c_dt, p.batch, p.stride_a, p.stride_b, p.stride_c)
+                               p.order_c, c_dt, p.batch, p.stride_a, p.stride_b, p.stride_c,
+                               b_dtype=p.b_dtype, out_dtype=p.c_dtype)
 
 
 def source_hash(family):
@@ -167,7 +171,7 @@ def cpu_baseline(problems, budget_s):
                             np.tile(np.arange(p.N), rows)], 1)
             t0 = time.perf_counter()
             oracle.gemm_at(p.in_dtype, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda, p.order_a, b,
-                           p.ldb, p.order_b, p.beta, c, p.ldc, p.order_c, idx)
+                           p.ldb, p.order_b, p.beta, c, p.ldc, p.order_c, idx, b_dtype=p.b_dtype)
             dt = time.perf_counter() - t0
             if dt >= 0.5 * per or rows >= p.M:
                 break
@@ -247,8 +251,8 @@ def main():
         ms = np.array([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)])
         tfl = p.flops / (ms.mean() * 1e-3) / 1e12
         flops_step += p.flops
-        alg_bytes = (p.M * p.K + p.K * p.N) * (4 if p.in_dtype == "f32" else 2) * p.batch + \
-            p.M * p.N * (4 if p.c_dtype == "f32" else 2) * p.batch * (2 if p.beta else 1)
+        alg_bytes = (p.M * p.K * ESIZE[p.in_dtype] + p.K * p.N * ESIZE[p.b_dtype]) * p.batch + \
+            p.M * p.N * ESIZE[p.c_dtype] * p.batch * (2 if p.beta else 1)
         per_kernel[p.name] = {
             "dtype": p.in_dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
             "mean_us": round(float(ms.mean()) * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
@@ -286,7 +290,7 @@ def main():
         "roofline": roof(dominant),
         "roofline_all": [roof(n) for n in per_kernel],
     }
-    if not args.no_context and args.workload == "headline":
+    if not args.no_context:
         out["context_torch_matmul"] = torch_context(problems, stream, torch)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -297,17 +301,35 @@ def main():
 def torch_context(problems, stream, torch):
     """torch.matmul (the vendor BLAS) on the same shapes: context only, not the path."""
     res = {}
-    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+          "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
     with torch.cuda.stream(stream):
         for p in problems:
+            if p.batch != 1:
+                continue
             a = torch.randn(p.M, p.K, device="cuda").to(dt[p.in_dtype])
-            b = torch.randn(p.K, p.N, device="cuda").to(dt[p.in_dtype])
-            for _ in range(3):
-                torch.matmul(a, b)
+            b = torch.randn(p.K, p.N, device="cuda").to(dt[p.b_dtype])
+            if p.in_dtype in ("e4m3", "e5m2"):
+                # torch's scaled 8-bit product (row-major A, column-major B)
+                one = torch.ones((), device="cuda")
+                bt = b.t().contiguous().t()
+                out_dt = dt[p.c_dtype]
+
+                def fn():
+                    torch._scaled_mm(a, bt, scale_a=one, scale_b=one, out_dtype=out_dt)
+            else:
+                def fn():
+                    torch.matmul(a, b)
+            try:
+                for _ in range(3):
+                    fn()
+            except RuntimeError as e:  # not every torch build has the 8-bit product
+                res[p.name] = f"unavailable: {str(e).splitlines()[0][:80]}"
+                continue
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(10):
-                torch.matmul(a, b)
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / 10

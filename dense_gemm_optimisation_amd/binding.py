@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm.so"
 ROW_MAJOR, COL_MAJOR = 0, 1
 DTYPE_SAME, DTYPE_F32 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+F8_E4M3, F8_E5M2 = 0, 1
+OUTPUT_F32, OUTPUT_BF16, OUTPUT_F16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 
 _lib = None
@@ -59,6 +61,12 @@ def library() -> ctypes.CDLL:
             fn.restype = i32
         lib.gemm_kernel_name.argtypes = [i32] + common + [i32, i64, i64, i64, i64]
         lib.gemm_kernel_name.restype = ctypes.c_char_p
+        f8 = [i64, i64, i64, f32, vp, i64, i32, i32, vp, i64, i32, i32, f32, vp, i64, i32, i32,
+              i64, i64, i64, i64]
+        lib.gemm_f8.argtypes = f8 + [vp]
+        lib.gemm_f8.restype = i32
+        lib.gemm_f8_kernel_name.argtypes = f8
+        lib.gemm_f8_kernel_name.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -144,15 +152,45 @@ def gemm_f16_bias_act(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C,
     return _check(st, "gemm_f16_bias_act", raise_on_error)
 
 
+def gemm_f8(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, format_b, beta, C, ldc,
+            order_c, type_c, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
+            raise_on_error=True):
+    """8-bit float inputs (F8_E4M3 / F8_E5M2 per operand), fp32 accumulation,
+    C of type OUTPUT_F32, OUTPUT_BF16 or OUTPUT_F16."""
+    st = library().gemm_f8(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, format_b,
+                           beta, C, ldc, order_c, type_c, batch, stride_a, stride_b, stride_c,
+                           _stream(stream))
+    return _check(st, "gemm_f8", raise_on_error)
+
+
+def f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, format_b, beta, C,
+                   ldc, order_c, type_c, batch=1, stride_a=0, stride_b=0, stride_c=0):
+    """The kernel gemm_f8 would launch for these arguments (see kernel_name)."""
+    name = library().gemm_f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb,
+                                         order_b, format_b, beta, C, ldc, order_c, type_c, batch,
+                                         stride_a, stride_b, stride_c)
+    return None if name is None else name.decode()
+
+
+_F8_FORMAT = {"e4m3": F8_E4M3, "e5m2": F8_E5M2}
+_OUTPUT = {"f32": OUTPUT_F32, "bf16": OUTPUT_BF16, "f16": OUTPUT_F16}
+
 _ENTRY = {"f32": gemm_f32, "bf16": gemm_bf16, "f16": gemm_f16}
 _ENTRY_EPI = {"f32": gemm_f32_bias_act, "bf16": gemm_bf16_bias_act, "f16": gemm_f16_bias_act}
 _INPUT = {"f32": 0, "bf16": 1, "f16": 2}
 
 
 def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
-                c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0):
+                c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, b_dtype=None,
+                out_dtype=None):
     """The kernel the GEMM call with these arguments would launch ("" for an
-    empty problem, None for invalid arguments); host only, no GPU needed."""
+    empty problem, None for invalid arguments); host only, no GPU needed.
+    For 8-bit inputs ("e4m3"/"e5m2") b_dtype and out_dtype name B's format
+    and C's type, as in gemm()."""
+    if in_dtype in _F8_FORMAT:
+        return f8_kernel_name(M, N, K, alpha, A, lda, order_a, _F8_FORMAT[in_dtype], B, ldb,
+                              order_b, _F8_FORMAT[b_dtype or in_dtype], beta, C, ldc, order_c,
+                              _OUTPUT[out_dtype], batch, stride_a, stride_b, stride_c)
     name = library().gemm_kernel_name(_INPUT[in_dtype], M, N, K, alpha, A, lda, order_a, B, ldb,
                                       order_b, beta, C, ldc, order_c, c_dtype, batch, stride_a,
                                       stride_b, stride_c)
@@ -161,9 +199,18 @@ def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta
 
 def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
          c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
-         raise_on_error=True, bias=None, stride_bias=0, act=ACT_NONE):
-    """Dispatch on the input type name ("f32", "bf16" or "f16"); a bias
-    address or an activation selects the fused-epilogue entry point."""
+         raise_on_error=True, bias=None, stride_bias=0, act=ACT_NONE, b_dtype=None,
+         out_dtype=None):
+    """Dispatch on the input type name ("f32", "bf16", "f16", or the 8-bit
+    "e4m3"/"e5m2" with B's format in b_dtype (default: A's) and C's type
+    name in out_dtype); a bias address or an activation selects the
+    fused-epilogue entry point (not offered for 8-bit inputs)."""
+    if in_dtype in _F8_FORMAT:
+        if bias is not None or act != ACT_NONE:
+            raise ValueError("8-bit inputs have no fused-epilogue entry point")
+        return gemm_f8(M, N, K, alpha, A, lda, order_a, _F8_FORMAT[in_dtype], B, ldb, order_b,
+                       _F8_FORMAT[b_dtype or in_dtype], beta, C, ldc, order_c, _OUTPUT[out_dtype],
+                       batch, stride_a, stride_b, stride_c, stream, raise_on_error)
     if bias is not None or act != ACT_NONE:
         fn = _ENTRY_EPI[in_dtype]
         if in_dtype == "f32":

@@ -26,7 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "scale.hip", "sgemm_valu.hip", "sgemm_mfma.hip", "sgemm_splitk.hip", "hgemm_mfma.hip", "hgemm_mfma_dma.hip",
-           "hgemm_splitk.hip", "gemm_skinny.hip"]
+           "hgemm_splitk.hip", "gemm_skinny.hip", "f8gemm_mfma.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -77,6 +77,8 @@ enum class Kernel {
     HgemmMfma,   // bf16/fp16, any shape
     HgemmDma,    // bf16/fp16, direct loads
     HgemmSplitk, // bf16/fp16, few tiles: split-K inside a workgroup
+    F8Mfma,      // 8-bit floats, any shape and order
+    F8Dma,       // 8-bit floats, K-contiguous aligned operands, direct loads
 };
 
 const char *kernel_name(Kernel k) {
@@ -91,6 +93,8 @@ const char *kernel_name(Kernel k) {
     case Kernel::HgemmMfma: return "hgemm_mfma";
     case Kernel::HgemmDma: return "hgemm_mfma_dma";
     case Kernel::HgemmSplitk: return "hgemm_splitk";
+    case Kernel::F8Mfma: return "f8gemm_mfma";
+    case Kernel::F8Dma: return "f8gemm_mfma_dma";
     }
     return "";
 }
@@ -101,6 +105,8 @@ const char *kernel_name(Kernel k) {
 // everything else.
 Kernel choose(const Problem &p) {
     const bool splits = !force_general() && !no_splitk();
+    if (elem_is_8bit(p.in))
+        return !force_general() && f8gemm_dma_eligible(p) ? Kernel::F8Dma : Kernel::F8Mfma;
     if (p.in == Elem::F32) {
         if (f32_valu()) return Kernel::SgemmValu;
         if (force_general()) return Kernel::SgemmMfma;
@@ -126,13 +132,16 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::HgemmMfma: return launch_hgemm(p, stream);
     case Kernel::HgemmDma: return launch_hgemm_dma(p, stream);
     case Kernel::HgemmSplitk: return launch_hgemm_splitk(p, stream);
+    case Kernel::F8Mfma: return launch_f8gemm(p, stream);
+    case Kernel::F8Dma: return launch_f8gemm_dma(p, stream);
     }
     return hipErrorInvalidValue;
 }
 
 // Validates a call and builds its canonical problem and kernel choice.  No
-// HIP call is made.
-gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
+// HIP call is made.  `in` is A's type and `in_b` B's (they differ only for
+// 8-bit inputs); a bias has A's type.
+gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                    const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                    float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
                    int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
@@ -157,7 +166,7 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;  // kernel stays None
 
     const bool reads_ab = K > 0 && alpha != 0.0f;
-    const int ein = elem_bytes(in), eout = elem_bytes(out);
+    const int ein = elem_bytes(in), ein_b = elem_bytes(in_b), eout = elem_bytes(out);
     const int64_t span_a = span(M, K, orderA, lda);
     const int64_t span_b = span(K, N, orderB, ldb);
     const int64_t span_c = span(M, N, orderC, ldc);
@@ -172,7 +181,7 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
         return GEMM_ERR_INVALID_ARG;
     if (reads_ab) {
         if (overlap(rc, range_of(A, span_a, batch, strideA, ein)) ||
-            overlap(rc, range_of(B, span_b, batch, strideB, ein)))
+            overlap(rc, range_of(B, span_b, batch, strideB, ein_b)))
             return GEMM_ERR_INVALID_ARG;
     }
 
@@ -185,7 +194,6 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
     p.ldc = ldc;
     p.batch = batch;
     p.sC = strideC;
-    p.in = in;
     p.out = out;
     // the bias runs along the caller's columns: along the kernel's rows when
     // C is computed transposed
@@ -197,6 +205,8 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
     if (orderC == GEMM_ROW_MAJOR) {
         p.M = M;
         p.N = N;
+        p.in = in;
+        p.in_b = in_b;
         p.A = A;
         p.lda = lda;
         p.a_kmajor = orderA == GEMM_ROW_MAJOR;
@@ -209,6 +219,8 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
         // C^T (N x M, row-major) = B^T (N x K) * A^T (K x M).
         p.M = N;
         p.N = M;
+        p.in = in_b;
+        p.in_b = in;
         p.A = B;
         p.lda = ldb;
         p.a_kmajor = orderB == GEMM_COL_MAJOR;
@@ -223,7 +235,7 @@ gemm_status_t plan(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alp
     return GEMM_OK;
 }
 
-gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
+gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                   float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
                   int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
@@ -231,8 +243,8 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
     Problem p;
     Kernel k;
     const gemm_status_t st =
-        plan(in, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC, batch,
-             strideA, strideB, strideC, bias, strideBias, act, p, k);
+        plan(in, in_b, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC,
+             batch, strideA, strideB, strideC, bias, strideBias, act, p, k);
     if (st != GEMM_OK || k == Kernel::None) return st;
     const hipError_t err = launch(k, p, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
@@ -240,6 +252,21 @@ gemm_status_t run(Elem in, Elem out, int64_t M, int64_t N, int64_t K, float alph
 }
 
 Elem out_type(Elem in, gemm_dtype_t c_dtype) { return c_dtype == GEMM_DTYPE_F32 ? Elem::F32 : in; }
+
+// 8-bit format and output-type enumerators; false when out of range.
+bool f8_type(gemm_f8_format_t f, Elem &e) {
+    if (f == GEMM_F8_E4M3) e = Elem::E4M3;
+    else if (f == GEMM_F8_E5M2) e = Elem::E5M2;
+    else return false;
+    return true;
+}
+bool output_type(gemm_output_t t, Elem &e) {
+    if (t == GEMM_OUTPUT_F32) e = Elem::F32;
+    else if (t == GEMM_OUTPUT_BF16) e = Elem::BF16;
+    else if (t == GEMM_OUTPUT_F16) e = Elem::F16;
+    else return false;
+    return true;
+}
 
 }  // namespace
 
@@ -249,7 +276,7 @@ gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float
                        gemm_order_t orderA, const float *B, int64_t ldb, gemm_order_t orderB,
                        float beta, float *C, int64_t ldc, gemm_order_t orderC, int64_t batch,
                        int64_t strideA, int64_t strideB, int64_t strideC, hipStream_t stream) {
-    return run(Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
+    return run(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
                orderC, batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream);
 }
 
@@ -259,7 +286,7 @@ gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const uint
                         gemm_dtype_t c_dtype, int64_t batch, int64_t strideA, int64_t strideB,
                         int64_t strideC, hipStream_t stream) {
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
-    return run(Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+    return run(Elem::BF16, Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
                orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
                GEMM_ACT_NONE, stream);
 }
@@ -270,7 +297,7 @@ gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha, const uint1
                        gemm_dtype_t c_dtype, int64_t batch, int64_t strideA, int64_t strideB,
                        int64_t strideC, hipStream_t stream) {
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
-    return run(Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+    return run(Elem::F16, Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
                orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
                GEMM_ACT_NONE, stream);
 }
@@ -281,7 +308,7 @@ gemm_status_t gemm_f32_bias_act(int64_t M, int64_t N, int64_t K, float alpha, co
                                 gemm_order_t orderC, int64_t batch, int64_t strideA,
                                 int64_t strideB, int64_t strideC, const float *bias,
                                 int64_t strideBias, gemm_activation_t act, hipStream_t stream) {
-    return run(Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
+    return run(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
                orderC, batch, strideA, strideB, strideC, bias, strideBias, act, stream);
 }
 
@@ -293,7 +320,7 @@ gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha, c
                                  const uint16_t *bias, int64_t strideBias, gemm_activation_t act,
                                  hipStream_t stream) {
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
-    return run(Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+    return run(Elem::BF16, Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
                orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, bias, strideBias,
                act, stream);
 }
@@ -306,9 +333,22 @@ gemm_status_t gemm_f16_bias_act(int64_t M, int64_t N, int64_t K, float alpha, co
                                 const uint16_t *bias, int64_t strideBias, gemm_activation_t act,
                                 hipStream_t stream) {
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
-    return run(Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
+    return run(Elem::F16, Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb,
                orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC, bias, strideBias,
                act, stream);
+}
+
+gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha, const uint8_t *A, int64_t lda,
+                      gemm_order_t orderA, gemm_f8_format_t formatA, const uint8_t *B,
+                      int64_t ldb, gemm_order_t orderB, gemm_f8_format_t formatB, float beta,
+                      void *C, int64_t ldc, gemm_order_t orderC, gemm_output_t typeC,
+                      int64_t batch, int64_t strideA, int64_t strideB, int64_t strideC,
+                      hipStream_t stream) {
+    Elem ea, eb, ec;
+    if (!f8_type(formatA, ea) || !f8_type(formatB, eb) || !output_type(typeC, ec))
+        return GEMM_ERR_INVALID_ARG;
+    return run(ea, eb, ec, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC,
+               batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream);
 }
 
 const char *gemm_status_string(gemm_status_t status) {
@@ -341,9 +381,26 @@ const char *gemm_kernel_name(gemm_input_t in, int64_t M, int64_t N, int64_t K, f
     Problem p;
     Kernel k;
     const gemm_status_t st =
-        plan(ein, ein == Elem::F32 ? Elem::F32 : out_type(ein, c_dtype), M, N, K, alpha, A, lda,
+        plan(ein, ein, ein == Elem::F32 ? Elem::F32 : out_type(ein, c_dtype), M, N, K, alpha, A, lda,
              orderA, B, ldb, orderB, beta, const_cast<void *>(C), ldc, orderC, batch, strideA,
              strideB, strideC, nullptr, 0, GEMM_ACT_NONE, p, k);
+    return st == GEMM_OK ? kernel_name(k) : nullptr;
+}
+
+const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha, const uint8_t *A,
+                                int64_t lda, gemm_order_t orderA, gemm_f8_format_t formatA,
+                                const uint8_t *B, int64_t ldb, gemm_order_t orderB,
+                                gemm_f8_format_t formatB, float beta, const void *C, int64_t ldc,
+                                gemm_order_t orderC, gemm_output_t typeC, int64_t batch,
+                                int64_t strideA, int64_t strideB, int64_t strideC) {
+    Elem ea, eb, ec;
+    if (!f8_type(formatA, ea) || !f8_type(formatB, eb) || !output_type(typeC, ec)) return nullptr;
+    Problem p;
+    Kernel k;
+    const gemm_status_t st =
+        plan(ea, eb, ec, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta,
+             const_cast<void *>(C), ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
+             GEMM_ACT_NONE, p, k);
     return st == GEMM_OK ? kernel_name(k) : nullptr;
 }
 

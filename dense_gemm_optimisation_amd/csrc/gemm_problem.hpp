@@ -12,7 +12,10 @@
 
 namespace libgemm {
 
-enum class Elem : int { F32 = 0, BF16 = 1, F16 = 2 };
+// E4M3 and E5M2 are the OCP 8-bit floating-point formats (1 sign bit; 4
+// exponent bits with bias 7 and 3 fraction bits, no infinities; 5 exponent
+// bits with bias 15 and 2 fraction bits, IEEE-style infinities and NaNs).
+enum class Elem : int { F32 = 0, BF16 = 1, F16 = 2, E4M3 = 3, E5M2 = 4 };
 
 struct Problem {
     int64_t M, N, K;
@@ -29,12 +32,15 @@ struct Problem {
     void *C;
     int64_t ldc;
     int64_t batch, sA, sB, sC;  // batch count and per-batch strides (elements)
-    Elem in, out;
+    Elem in, in_b, out;         // types of A, of B (differs from A's only for 8-bit), of C
     Epilogue epi;               // bias and activation applied before the store
 };
 
 // Element size in bytes.
-inline int elem_bytes(Elem e) { return e == Elem::F32 ? 4 : 2; }
+inline int elem_bytes(Elem e) {
+    return e == Elem::F32 ? 4 : (e == Elem::BF16 || e == Elem::F16) ? 2 : 1;
+}
+inline bool elem_is_8bit(Elem e) { return e == Elem::E4M3 || e == Elem::E5M2; }
 
 // True when a pointer, leading dimension and batch stride allow 16-byte
 // vector access to every row of the operand.
@@ -67,6 +73,12 @@ hipError_t launch_hgemm_splitk(const Problem &p, hipStream_t stream);
 // inside a workgroup (skinny_eligible()).
 bool skinny_eligible(const Problem &p);
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
+// 8-bit floats (E4M3/E5M2) on the scaled 8-bit matrix instructions: the
+// direct-load kernel for K-contiguous aligned operands (f8gemm_dma_eligible())
+// and a general kernel for any order, alignment and shape.
+bool f8gemm_dma_eligible(const Problem &p);
+hipError_t launch_f8gemm_dma(const Problem &p, hipStream_t stream);
+hipError_t launch_f8gemm(const Problem &p, hipStream_t stream);
 hipError_t launch_scale(const Problem &p, hipStream_t stream);  // C <- beta*C only
 
 }  // namespace libgemm

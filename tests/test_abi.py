@@ -29,8 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
                                     "gemm_f16", "gemm_f16_bias_act", "gemm_f32",
-                                    "gemm_f32_bias_act", "gemm_kernel_name",
-                                    "gemm_status_string"]
+                                    "gemm_f32_bias_act", "gemm_f8", "gemm_f8_kernel_name",
+                                    "gemm_kernel_name", "gemm_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -62,7 +62,11 @@ P = 0x10000  # a fake, never-dereferenced device address
 
 
 def call(lib, fn="f32", M=8, N=8, K=8, alpha=1.0, A=P, lda=8, oa=0, B=P * 3, ldb=8, ob=0,
-         beta=0.0, C=P * 5, ldc=8, oc=0, c_dtype=0, batch=1, sa=0, sb=0, sc=0):
+         beta=0.0, C=P * 5, ldc=8, oc=0, c_dtype=0, batch=1, sa=0, sb=0, sc=0, fa=0, fb=0,
+         type_c=1):
+    if fn == "e4m3":  # gemm_f8, formats fa / fb, C of type type_c (bf16 by default)
+        return lib.gemm_f8(M, N, K, alpha, A, lda, oa, fa, B, ldb, ob, fb, beta, C, ldc, oc,
+                           type_c, batch, sa, sb, sc, 0, raise_on_error=False)
     if fn == "f32":
         return lib.gemm_f32(M, N, K, alpha, A, lda, oa, B, ldb, ob, beta, C, ldc, oc, batch, sa,
                             sb, sc, 0, raise_on_error=False)
@@ -97,15 +101,25 @@ INVALID = {
 }
 
 
-@pytest.mark.parametrize("fn", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fn", ["f32", "bf16", "f16", "e4m3"])
 @pytest.mark.parametrize("case", sorted(INVALID))
 def test_invalid_arguments(lib, fn, case):
     kw = dict(INVALID[case])
-    if fn != "f32" and case == "C overlaps A":
-        kw["C"] = P + 2 * 10
-    if fn != "f32" and case == "C overlaps B":
-        kw["C"] = P * 3 + 2 * 63
+    esz = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}[fn]  # A and B span 64 elements
+    if case == "C overlaps A":
+        kw["C"] = P + esz * 10
+    if case == "C overlaps B":
+        kw["C"] = P * 3 + esz * 63
     assert call(lib, fn, **kw) == lib.ERR_INVALID_ARG, case
+
+
+def test_f8_bad_formats_and_output_type(lib):
+    for kw in (dict(fa=2), dict(fa=-1), dict(fb=2), dict(type_c=3), dict(type_c=-1)):
+        assert call(lib, "e4m3", **kw) == lib.ERR_INVALID_ARG, kw
+    for fa in (0, 1):
+        for fb in (0, 1):
+            for tc in (0, 1, 2):
+                assert call(lib, "e4m3", M=0, fa=fa, fb=fb, type_c=tc) == lib.OK
 
 
 @pytest.mark.parametrize("fn", ["bf16", "f16"])
@@ -114,7 +128,7 @@ def test_bad_c_dtype(lib, fn):
     assert call(lib, fn, c_dtype=-1) == lib.ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("fn", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fn", ["f32", "bf16", "f16", "e4m3"])
 @pytest.mark.parametrize("kw", [dict(M=0), dict(N=0), dict(batch=0),
                                 dict(M=0, A=0, B=0, C=0), dict(batch=0, A=0, B=0, C=0)])
 def test_empty_problems_return_ok_without_work(lib, fn, kw):
@@ -182,12 +196,13 @@ GB = 1 << 32  # operands 4 GiB apart: fake, never-dereferenced, 16-byte aligned 
 
 
 def kname(lib, dt, M, N, K, alpha=1.0, oa=0, ob=0, oc=0, lda=None, ldb=None, ldc=None,
-          A=GB, B=2 * GB, C=3 * GB, beta=0.0, c_dtype=0, batch=1, sa=0, sb=0, sc=0):
+          A=GB, B=2 * GB, C=3 * GB, beta=0.0, c_dtype=0, batch=1, sa=0, sb=0, sc=0, bdt=None,
+          out="bf16"):
     lda = lda or (K if oa == 0 else M)
     ldb = ldb or (N if ob == 0 else K)
     ldc = ldc or (N if oc == 0 else M)
     return lib.kernel_name(dt, M, N, K, alpha, A, lda, oa, B, ldb, ob, beta, C, ldc, oc, c_dtype,
-                           batch, sa, sb, sc)
+                           batch, sa, sb, sc, b_dtype=bdt, out_dtype=out)
 
 
 @pytest.fixture
@@ -229,6 +244,21 @@ KERNEL_CASES = [
     # column-major C: computed as C^T = B^T A^T, so the roles of M and N swap
     ("bf16", 4096, 16, 4096, dict(oc=1, ob=1), "gemm_skinny"),
     ("bf16", 4096, 16, 4096, dict(oc=1), "hgemm_splitk"),
+    # 8-bit floats: the direct-load kernel for K-contiguous, aligned A and B
+    ("e4m3", 4096, 4096, 4096, dict(ob=1), "f8gemm_mfma_dma"),
+    ("e5m2", 4096, 4096, 4096, dict(ob=1, bdt="e4m3", out="f32"), "f8gemm_mfma_dma"),
+    ("e4m3", 4096, 4096, 4096, dict(ob=1, oc=1, out="f16"), "f8gemm_mfma_dma"),
+    ("e4m3", 16, 4096, 4096, dict(ob=1), "f8gemm_mfma_dma"),       # no skinny kernel for 8-bit
+    ("e4m3", 4095, 4097, 4096, dict(ob=1), "f8gemm_mfma_dma"),     # ragged M, N are fine
+    ("e4m3", 4096, 4096, 4096, {}, "f8gemm_mfma"),                 # N-contiguous B
+    ("e4m3", 4096, 4096, 4096, dict(oa=1, ob=1), "f8gemm_mfma"),   # M-contiguous A
+    ("e4m3", 4096, 4096, 4104, dict(ob=1), "f8gemm_mfma"),         # K not a multiple of 16
+    ("e4m3", 4096, 4096, 4096, dict(ob=1, A=GB + 8), "f8gemm_mfma"),
+    ("e4m3", 4096, 4096, 4096, dict(ob=1, ldb=4100), "f8gemm_mfma"),
+    ("e4m3", 4096, 4096, 4096, dict(ob=1, batch=2, sa=4096 * 4096 + 8, sb=0,
+                                    sc=4096 * 4096), "f8gemm_mfma"),
+    ("e4m3", 4096, 4096, 4096, dict(ob=1, alpha=0.0, beta=1.0), "scale"),
+    ("e4m3", 4096, 4096, 4096, dict(ob=1, lda=100), None),
 ]
 
 
@@ -246,7 +276,11 @@ def test_kernel_choice_environment_switches(lib, clean_env):
     clean_env.setenv("LIBGEMM_FORCE_GENERAL", "1")
     assert kname(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma"
     assert kname(lib, "bf16", 16, 4096, 4096) == "hgemm_mfma"
+    assert kname(lib, "e4m3", 4096, 4096, 4096, ob=1) == "f8gemm_mfma"
     clean_env.delenv("LIBGEMM_FORCE_GENERAL")
+    clean_env.setenv("LIBGEMM_NO_SPLITK", "1")
+    assert kname(lib, "e4m3", 4096, 4096, 4096, ob=1) == "f8gemm_mfma_dma"
+    clean_env.delenv("LIBGEMM_NO_SPLITK")
     clean_env.setenv("LIBGEMM_F32_VALU", "1")
     assert kname(lib, "f32", 16, 4096, 4096, ob=1) == "sgemm_valu"
     assert kname(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"
@@ -262,12 +296,13 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_ffn_down": "hgemm_mfma_dma", "f32_edge": "sgemm_mfma",
             "bf16_edge": "hgemm_mfma", "bf16_skinny": "gemm_skinny",
             "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma",
-            "bf16_ffn_up_gelu": "hgemm_mfma_dma"}
+            "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma"}
     assert sorted(want) == sorted(workloads.CONFIGS)
     for name, k in want.items():
         p = workloads.config(name)
         c_dt = 1 if (p.c_dtype == "f32" and p.in_dtype != "f32") else 0
         got = lib.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, GB, p.lda, p.order_a, 2 * GB,
                               p.ldb, p.order_b, p.beta, 3 * GB, p.ldc, p.order_c, c_dt, p.batch,
-                              p.stride_a, p.stride_b, p.stride_c)
+                              p.stride_a, p.stride_b, p.stride_c, b_dtype=p.b_dtype,
+                              out_dtype=p.c_dtype)
         assert got == k, name

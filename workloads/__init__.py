@@ -15,6 +15,9 @@ listed here, so the reading taken is stated once, here):
 * bf16/fp16 entries: ``sigma * standard_normal()`` in float64, rounded to
   float32, then to the 16-bit type with round-to-nearest-even (torch's CPU
   conversion);
+* 8-bit float entries (OCP E4M3 "e4m3", E5M2 "e5m2"): drawn like bf16 ones,
+  then converted by torch's float8_e4m3fn / float8_e5m2 (nearest-even); A and
+  B may have different 8-bit types (``b_dtype``);
 * softmax rows (the attention probabilities): logits uniform(-1, 1), a
   row-wise softmax in float64, then rounded like any bf16 entry;
 * the bias of a problem with a fused epilogue comes from a second stream,
@@ -45,7 +48,7 @@ class Problem:
     the type of C (both its initial value and the result).
     """
     name: str
-    in_dtype: str
+    in_dtype: str                    # type of A (and B unless b_dtype is set)
     c_dtype: str
     M: int
     N: int
@@ -73,6 +76,7 @@ class Problem:
     stride_bias: Optional[int] = None  # elements between batch entries' vectors
     sigma_bias: float = 1.0
     act: int = 0                     # 0 none, 1 ReLU, 2 GELU
+    b_dtype: Optional[str] = None    # type of B when it differs from A's (8-bit floats)
 
     def __post_init__(self):
         M, N, K = self.M, self.N, self.K
@@ -90,6 +94,8 @@ class Problem:
             self.stride_c = self.footprint("c")
         if self.stride_bias is None:
             self.stride_bias = N if self.batch > 1 else 0
+        if self.b_dtype is None:
+            self.b_dtype = self.in_dtype
 
     def dims(self, which):
         return {"a": (self.M, self.K, self.order_a, self.lda),
@@ -123,6 +129,23 @@ def _f32(x64: np.ndarray) -> np.ndarray:
     return x64.astype(np.float32)
 
 
+EIGHT_BIT = ("e4m3", "e5m2")
+
+
+def storage(dtype: str):
+    """numpy type of a stored element."""
+    if dtype == "f32":
+        return np.float32
+    return np.uint8 if dtype in EIGHT_BIT else np.uint16
+
+
+def to_8bit(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float values to OCP 8-bit float bit patterns (uint8), nearest-even."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    tdt = torch.float8_e4m3fn if dtype == "e4m3" else torch.float8_e5m2
+    return t.to(tdt).view(torch.uint8).numpy()
+
+
 def to_16bit(x: np.ndarray, dtype: str) -> np.ndarray:
     """Round float values to bf16/fp16 bit patterns (uint16), nearest-even."""
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
@@ -139,7 +162,8 @@ def _draw(rng, dtype, rows, cols, sigma, kind="default"):
         return to_16bit(_f32(p), dtype) if dtype != "f32" else _f32(p)
     if dtype == "f32":
         return _f32(rng.uniform(-1.0, 1.0, size=(rows, cols)) * sigma)
-    return to_16bit(_f32(rng.standard_normal(size=(rows, cols)) * sigma), dtype)
+    x = _f32(rng.standard_normal(size=(rows, cols)) * sigma)
+    return to_8bit(x, dtype) if dtype in EIGHT_BIT else to_16bit(x, dtype)
 
 
 def _store(mat: np.ndarray, order: int, ld: int, batch_stride: int, b: int,
@@ -168,11 +192,11 @@ def generate(p: Problem, seed: Optional[int] = None):
     rng = np.random.default_rng(p.seed if seed is None else seed)
     bufs = {}
     for which, dt, sig, kind in (("a", p.in_dtype, p.sigma_a, p.a_kind),
-                                 ("b", p.in_dtype, p.sigma_b, "default"),
+                                 ("b", p.b_dtype, p.sigma_b, "default"),
                                  ("c", p.c_dtype, p.sigma_c, "default")):
         r, c, order, ld = p.dims(which)
         stride = {"a": p.stride_a, "b": p.stride_b, "c": p.stride_c}[which]
-        out = np.zeros(p.buffer_elems(which), np.float32 if dt == "f32" else np.uint16)
+        out = np.zeros(p.buffer_elems(which), storage(dt))
         nb = 1 if stride == 0 else p.batch
         for b in range(nb):
             _store(_draw(rng, dt, r, c, sig, kind), order, ld, stride, b, out)
@@ -227,6 +251,10 @@ def _configs():
         Problem("bf16_ffn_up_gelu", "bf16", "bf16", 4096, 16384, 4096, sigma_b=0.02,
                 bias=True, act=2,
                 note="FFN up X(4096x4096) W1(4096x16384) + b1 then GELU, fused epilogue"),
+        # 8-bit float inputs in the layout 8-bit GEMMs take: A row-major and B
+        # column-major (both contiguous along K), output bf16
+        Problem("fp8_4096", "e4m3", "bf16", 4096, 4096, 4096, order_b=COL,
+                note="E4M3 GEMM 4096^3, A row-major, B column-major, fp32 accumulate, bf16 out"),
     ]
     return {c.name: c for c in cfgs}
 
