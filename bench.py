@@ -15,8 +15,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Each kernel cycles through at least three copies of its buffers, enough that
 their footprint exceeds twice the 256 MB MALL, so inputs come from HBM;
 --no-rotate reuses one set (the warm-cache figure).
---workload runs a single named workload (see workloads.CONFIGS) instead of
-the headline step, for profiling.  --copy-calibration runs only a plain
+--workload runs the named workload, or a comma-separated list of them (see
+workloads.CONFIGS), instead of the headline step, for profiling.  --copy-calibration runs only a plain
 device-to-device copy of the given size (the reference kernel against which
 the HBM byte counters FETCH_SIZE / WRITE_SIZE are scaled).
 
@@ -211,7 +211,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, torch)
         return
-    names = HEADLINE if args.workload == "headline" else [args.workload]
+    names = HEADLINE if args.workload == "headline" else args.workload.split(",")
     problems = [workloads.config(n) for n in names]
     stream = torch.cuda.Stream()  # default priority
     launches, nsets, families = [], {}, {}
@@ -232,34 +232,36 @@ def main():
             fn()
     torch.cuda.synchronize()
 
-    # timed region: every launch bracketed by events on the kernels' stream
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in launches] for _ in range(args.steps)]
+    # Timed region: the step's kernels, each launched `steps` times back to
+    # back between one pair of HIP events on the stream they run on (an event
+    # pair around every launch would add its own gap to each launch's time).
+    # A kernel's mean launch duration is its event interval / steps; the
+    # step's wall time is the whole region / steps.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in launches]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        for k, (_, _, fn) in enumerate(launches):
-            ev[s][k][0].record(stream)
+    for k, (_, _, fn) in enumerate(launches):
+        ev[k][0].record(stream)
+        for _ in range(args.steps):
             fn()
-            ev[s][k][1].record(stream)
+        ev[k][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     per_kernel = {}
     flops_step = 0
     for k, (p, _, _) in enumerate(launches):
-        ms = np.array([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)])
-        tfl = p.flops / (ms.mean() * 1e-3) / 1e12
+        ms = ev[k][0].elapsed_time(ev[k][1]) / args.steps
+        tfl = p.flops / (ms * 1e-3) / 1e12
         flops_step += p.flops
         alg_bytes = (p.M * p.K * ESIZE[p.in_dtype] + p.K * p.N * ESIZE[p.b_dtype]) * p.batch + \
             p.M * p.N * ESIZE[p.c_dtype] * p.batch * (2 if p.beta else 1)
         per_kernel[p.name] = {
             "dtype": p.in_dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
-            "mean_us": round(float(ms.mean()) * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
-            "min_us": round(float(ms.min()) * 1e3, 2), "tflops": round(tfl, 2),
-            "tflops_best": round(p.flops / (ms.min() * 1e-3) / 1e12, 2),
+            "mean_us": round(ms * 1e3, 2), "tflops": round(tfl, 2),
             "frac_of_peak": round(tfl / PEAK_TFLOPS[p.in_dtype], 4),
-            "alg_gbs": round(alg_bytes / (ms.mean() * 1e-3) / 1e9, 1)}
+            "alg_gbs": round(alg_bytes / (ms * 1e-3) / 1e9, 1)}
     ms_step = wall / args.steps * 1e3
     value = flops_step / (wall / args.steps) / 1e12
 

@@ -82,11 +82,24 @@ __device__ inline void hint_row() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// An empty volatile statement that takes x as an operand in the given
+// register file: the instruction that produced x cannot move past it.
+template <bool AGPR>
+__device__ inline void pin(const f32x16 &x) {
+    if (!AGPR) asm volatile("" ::"v"(x));
+}
+
+#ifndef LIBGEMM_F8_WM
+#define LIBGEMM_F8_WM 2
+#endif
+#ifndef LIBGEMM_F8_WN
+#define LIBGEMM_F8_WN 4
+#endif
 #ifndef LIBGEMM_F8_STAGES
 #define LIBGEMM_F8_STAGES 2
 #endif
 #ifndef LIBGEMM_F8_GROUP_M
-#define LIBGEMM_F8_GROUP_M 8
+#define LIBGEMM_F8_GROUP_M 16
 #endif
 
 // Fast-path kernel.  2 x 4 waves, each with a 128 x 64 wave tile (4 x 2
@@ -102,11 +115,15 @@ __device__ inline void hint_row() {
 // workgroup barrier; the refill of the stage just consumed is issued between
 // the last two instructions, after the barrier has shown that every wave
 // has read it.
-template <int FA, int FB, int OUT, int STAGES>
-__global__ __launch_bounds__(512, 1) void f8gemm_dma_kernel(DmaArgs p) {
-    constexpr int WAVES_N = 4, WAVES = 8;
-    constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
+template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(DmaArgs p) {
+    constexpr int WAVES = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 32, FN = WTN / 32;
     constexpr int BK = 64;  // 16-bit units per stage
+    // Accumulators beyond 128 registers per lane live in the AGPRs (one
+    // wave per SIMD); the statement that pins the instructions in place
+    // must name the register file they are in.
+    constexpr bool ACC_AGPR = FM * FN * 16 > 128;
     static_assert(FM % 2 == 0, "A fragments alternate between two slots");
     using Op = Operand<true, WAVES, BK>;
     constexpr int CH = Op::CH;
@@ -114,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void f8gemm_dma_kernel(DmaArgs p) {
     constexpr int STAGE = 2 * PANEL;
     constexpr int PER_STAGE = 2 * Op::PER_WAVE;  // direct loads per wave per stage
     static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(PER_STAGE % 2 == 0, "refill split over the last two instructions");
+    static_assert(PER_STAGE % FN == 0, "refill split over the last row's instructions");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
     TileCoord t = tile_of(p.grid, blockIdx.x);
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(512, 1) void f8gemm_dma_kernel(DmaArgs p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             acc[i][j] = mma8<FA, FB>(fb[slot][j], fa[i & 1], acc[i][j]);
-            asm volatile("" ::"v"(acc[i][j]));
+            pin<ACC_AGPR>(acc[i][j]);
         }
     };
     // k step 0 of a stage in buffer `buf` (B fragments in slot 0); its last
@@ -218,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void f8gemm_dma_kernel(DmaArgs p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             acc[FM - 1][j] = mma8<FA, FB>(fb[1][j], fa[(FM - 1) & 1], acc[FM - 1][j]);
-            asm volatile("" ::"v"(acc[FM - 1][j]));
+            pin<ACC_AGPR>(acc[FM - 1][j]);
             if (do_refill) {
 #pragma unroll
                 for (int q = j * PER_STAGE / FN; q < (j + 1) * PER_STAGE / FN; ++q) {
@@ -401,8 +418,10 @@ struct LaunchDma {
     static hipError_t go(const Problem &, DmaArgs &a, hipStream_t stream) {
         void *args[] = {&a};
         return hipLaunchKernel(
-            reinterpret_cast<const void *>(&f8gemm_dma_kernel<FA, FB, OUT, LIBGEMM_F8_STAGES>),
-            dim3(static_cast<unsigned>(a.grid.count())), dim3(512), args, 0, stream);
+            reinterpret_cast<const void *>(&f8gemm_dma_kernel<FA, FB, OUT, LIBGEMM_F8_WM,
+                                                              LIBGEMM_F8_WN, LIBGEMM_F8_STAGES>),
+            dim3(static_cast<unsigned>(a.grid.count())), dim3(LIBGEMM_F8_WM * LIBGEMM_F8_WN * 64),
+            args, 0, stream);
     }
 };
 
