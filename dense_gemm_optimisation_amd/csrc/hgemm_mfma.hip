@@ -123,11 +123,32 @@ __device__ inline UBuf make_ubuf(const uint16_t *x, int64_t span) {
     return u;
 }
 
-// Elements x[e .. e+7] with those at index >= valid (0..8) zero.  A chunk
-// whose 20-byte window would pass the end of the buffer is read element by
-// element: a load that is only partly inside the buffer's range may come
-// back as all zeros.
-__device__ inline u32x4 load8u(const UBuf &u, const uint16_t *x, int64_t e, int valid) {
+// Elements x[e .. e+7] with those at index >= valid (0..8) zero, in two
+// halves so that a panel's loads are all in flight before any is used.
+// load8u_issue issues the 16-byte and the 4-byte load at the enclosing dword
+// boundary; a chunk with nothing to load, or whose 20-byte window would pass
+// the end of the buffer, is sent to an offset beyond any buffer (the loads
+// return zeros and cost no memory traffic).  load8u_finish shifts the loaded
+// words into place, masks the elements past `valid`, and reads the chunks at
+// the end of the buffer element by element (a load only partly inside the
+// buffer's range may come back as all zeros).
+struct Raw8 {
+    u32x4 lo;
+    uint32_t hi;
+};
+
+__device__ inline Raw8 load8u_issue(const UBuf &u, int64_t e, int valid) {
+    const uint32_t bo = u.mis + static_cast<uint32_t>(e) * 2;
+    const uint32_t dw = bo & ~3u;
+    const uint32_t off = (valid > 0 && dw + 20 <= u.limit) ? dw : 0x80000000u;
+    Raw8 r;
+    r.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(u.rs, off, 0, 0));
+    r.hi = __builtin_amdgcn_raw_buffer_load_b32(u.rs, off + 16, 0, 0);
+    return r;
+}
+
+__device__ inline u32x4 load8u_finish(const UBuf &u, const uint16_t *x, int64_t e, int valid,
+                                      const Raw8 &r) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     if (valid <= 0) return zero;
     const uint32_t bo = u.mis + static_cast<uint32_t>(e) * 2;
@@ -142,13 +163,11 @@ __device__ inline u32x4 load8u(const UBuf &u, const uint16_t *x, int64_t e, int 
         }
         return v;
     }
-    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(u.rs, dw, 0, 0));
-    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(u.rs, dw + 16, 0, 0);
     const bool odd = (bo & 2) != 0;
-    v[0] = odd ? __builtin_amdgcn_alignbyte(lo[1], lo[0], 2) : lo[0];
-    v[1] = odd ? __builtin_amdgcn_alignbyte(lo[2], lo[1], 2) : lo[1];
-    v[2] = odd ? __builtin_amdgcn_alignbyte(lo[3], lo[2], 2) : lo[2];
-    v[3] = odd ? __builtin_amdgcn_alignbyte(hi, lo[3], 2) : lo[3];
+    v[0] = odd ? __builtin_amdgcn_alignbyte(r.lo[1], r.lo[0], 2) : r.lo[0];
+    v[1] = odd ? __builtin_amdgcn_alignbyte(r.lo[2], r.lo[1], 2) : r.lo[1];
+    v[2] = odd ? __builtin_amdgcn_alignbyte(r.lo[3], r.lo[2], 2) : r.lo[2];
+    v[3] = odd ? __builtin_amdgcn_alignbyte(r.hi, r.lo[3], 2) : r.lo[3];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t keep = (2 * q + 1 < valid ? 0xffff0000u : 0u) | (2 * q < valid ? 0xffffu : 0u);
@@ -160,37 +179,67 @@ __device__ inline u32x4 load8u(const UBuf &u, const uint16_t *x, int64_t e, int 
 // Global -> registers: one operand panel for the K step starting at k0.
 //   KMAJOR: element (r, k) at X[r*ld + k]; thread loads 8 chunks of 8 k.
 //   else:   element (r, k) at X[k*ld + r]; thread loads an 8 (k) x 8 (r) block.
-//   UB: the operand is read through its raw buffer (any alignment);
-//   otherwise with 16-byte vector loads when `vec`, else element by element.
-template <bool KMAJOR, bool UB>
-__device__ inline void load_panel(const uint16_t *X, int64_t ld, int64_t rows, int64_t r0,
-                                  int64_t k0, int64_t K, bool vec, const UBuf &u, int tid,
-                                  u32x4 v[8]) {
+// Chunk i of this thread starts at element e of X with `valid` elements
+// inside the matrix (chunk_of).  The raw-buffer path (any alignment) issues
+// every chunk's loads first (issue_panel) and assembles the chunks later
+// (finish_panel), after the matrix instructions of the current step; the
+// other path (operands too large for a raw buffer) loads 16-byte vectors
+// when `vec`, else element by element.
+template <bool KMAJOR>
+__device__ inline void chunk_of(int64_t ld, int64_t rows, int64_t r0, int64_t k0, int64_t K,
+                                int tid, int i, int64_t &e, int &valid) {
     if (KMAJOR) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + THREADS * i;
-            const int row = c >> 3, kc = c & 7;
-            const int64_t gr = r0 + row, gk = k0 + kc * 8;
-            if (UB) {
-                const int64_t left = K - gk;
-                v[i] = load8u(u, X, gr * ld + gk, gr < rows ? int(left < 8 ? left : 8) : 0);
-            } else {
-                v[i] = load8(X + gr * ld + gk, vec, gr < rows, gk, K);
-            }
-        }
+        const int c = tid + THREADS * i;
+        const int row = c >> 3, kc = c & 7;
+        const int64_t gr = r0 + row, gk = k0 + kc * 8;
+        const int64_t left = K - gk;
+        e = gr * ld + gk;
+        valid = gr < rows ? int(left < 8 ? left : 8) : 0;
     } else {
         const int rb = tid & 31, kb = tid >> 5;
+        const int64_t gk = k0 + kb * 8 + i, gr = r0 + rb * 8;
+        const int64_t left = rows - gr;
+        e = gk * ld + gr;
+        valid = gk < K ? int(left < 8 ? left : 8) : 0;
+    }
+}
+
+template <bool KMAJOR>
+__device__ inline void issue_panel(const UBuf &u, int64_t ld, int64_t rows, int64_t r0,
+                                   int64_t k0, int64_t K, int tid, Raw8 raw[8]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t gk = k0 + kb * 8 + i, gr = r0 + rb * 8;
-            if (UB) {
-                const int64_t left = rows - gr;
-                v[i] = load8u(u, X, gk * ld + gr, gk < K ? int(left < 8 ? left : 8) : 0);
-            } else {
-                v[i] = load8(X + gk * ld + gr, vec, gk < K, gr, rows);
-            }
-        }
+    for (int i = 0; i < 8; ++i) {
+        int64_t e;
+        int valid;
+        chunk_of<KMAJOR>(ld, rows, r0, k0, K, tid, i, e, valid);
+        raw[i] = load8u_issue(u, e, valid);
+    }
+}
+
+template <bool KMAJOR>
+__device__ inline void finish_panel(const UBuf &u, const uint16_t *X, int64_t ld, int64_t rows,
+                                    int64_t r0, int64_t k0, int64_t K, int tid, const Raw8 raw[8],
+                                    u32x4 v[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int64_t e;
+        int valid;
+        chunk_of<KMAJOR>(ld, rows, r0, k0, K, tid, i, e, valid);
+        v[i] = load8u_finish(u, X, e, valid, raw[i]);
+    }
+}
+
+template <bool KMAJOR>
+__device__ inline void load_panel(const uint16_t *X, int64_t ld, int64_t rows, int64_t r0,
+                                  int64_t k0, int64_t K, bool vec, int tid, u32x4 v[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int64_t e;
+        int valid;
+        chunk_of<KMAJOR>(ld, rows, r0, k0, K, tid, i, e, valid);
+        // chunk_of's `valid` covers both the row bound and the extent along
+        // the contiguous dimension: pass it as the limit
+        v[i] = load8(X + e, vec, valid > 0, 0, valid);
     }
 }
 
@@ -272,8 +321,16 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
     const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
     const UBuf ua = make_ubuf(A, UB ? span_a : 0), ub = make_ubuf(B, UB ? span_b : 0);
     u32x4 va[8], vb[8];
-    load_panel<A_KMAJOR, UB>(A, p.lda, p.M, m0, 0, p.K, p.vec_a, ua, tid, va);
-    load_panel<B_KMAJOR, UB>(B, p.ldb, p.N, n0, 0, p.K, p.vec_b, ub, tid, vb);
+    Raw8 ra[8], rb[8];
+    if (UB) {
+        issue_panel<A_KMAJOR>(ua, p.lda, p.M, m0, 0, p.K, tid, ra);
+        issue_panel<B_KMAJOR>(ub, p.ldb, p.N, n0, 0, p.K, tid, rb);
+        finish_panel<A_KMAJOR>(ua, A, p.lda, p.M, m0, 0, p.K, tid, ra, va);
+        finish_panel<B_KMAJOR>(ub, B, p.ldb, p.N, n0, 0, p.K, tid, rb, vb);
+    } else {
+        load_panel<A_KMAJOR>(A, p.lda, p.M, m0, 0, p.K, p.vec_a, tid, va);
+        load_panel<B_KMAJOR>(B, p.ldb, p.N, n0, 0, p.K, p.vec_b, tid, vb);
+    }
     store_panel<A_KMAJOR>(smem[0][0], tid, va);
     store_panel<B_KMAJOR>(smem[0][1], tid, vb);
     __syncthreads();
@@ -281,10 +338,15 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
     for (int64_t s = 0; s < steps; ++s) {
         const int cur = s & 1;
         const bool more = s + 1 < steps;
+        const int64_t k0 = (s + 1) * BK;
         if (more) {
-            const int64_t k0 = (s + 1) * BK;
-            load_panel<A_KMAJOR, UB>(A, p.lda, p.M, m0, k0, p.K, p.vec_a, ua, tid, va);
-            load_panel<B_KMAJOR, UB>(B, p.ldb, p.N, n0, k0, p.K, p.vec_b, ub, tid, vb);
+            if (UB) {
+                issue_panel<A_KMAJOR>(ua, p.lda, p.M, m0, k0, p.K, tid, ra);
+                issue_panel<B_KMAJOR>(ub, p.ldb, p.N, n0, k0, p.K, tid, rb);
+            } else {
+                load_panel<A_KMAJOR>(A, p.lda, p.M, m0, k0, p.K, p.vec_a, tid, va);
+                load_panel<B_KMAJOR>(B, p.ldb, p.N, n0, k0, p.K, p.vec_b, tid, vb);
+            }
         }
         const u32x4 *sa = smem[cur][0];
         const u32x4 *sb = smem[cur][1];
@@ -306,6 +368,10 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(a[i], b[j], acc[i][j]);
         }
         if (more) {
+            if (UB) {
+                finish_panel<A_KMAJOR>(ua, A, p.lda, p.M, m0, k0, p.K, tid, ra, va);
+                finish_panel<B_KMAJOR>(ub, B, p.ldb, p.N, n0, k0, p.K, tid, rb, vb);
+            }
             store_panel<A_KMAJOR>(smem[cur ^ 1][0], tid, va);
             store_panel<B_KMAJOR>(smem[cur ^ 1][1], tid, vb);
         }
@@ -313,22 +379,41 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
     }
 
     // Epilogue.  Accumulator register r of the 32 x 32 block (i, j) holds
-    // row 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that block.
+    // row 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that block.  The
+    // 16 old values of C a lane needs for a block are loaded before any is
+    // used, from element 0 of C where the element lies outside the matrix (a
+    // valid address, the value discarded): a load behind each element's
+    // bounds test would be waited for before the next one is issued.
     void *C = static_cast<char *>(p.C) + t.batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t col = n0 + wn * 128 + j * 32 + lrow;
+            int64_t off[16];
+            bool in[16];
+            float old[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
-                if (row < p.M && col < p.N) {
-                    const int64_t off = row * p.ldc + col;
+                in[r] = row < p.M && col < p.N;
+                off[r] = in[r] ? row * p.ldc + col : 0;
+                old[r] = 0.0f;
+            }
+            if (p.beta != 0.0f) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) old[r] = load_c<OUT>(C, off[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (in[r]) {
                     float v = p.alpha * acc[i][j][r];
-                    if (p.beta != 0.0f) v = __builtin_fmaf(p.beta, load_c<OUT>(C, off), v);
-                    if (p.epi.active()) v = epilogue_apply(p.epi, v, t.batch, row, col);
-                    store_c<OUT>(C, off, v);
+                    if (p.beta != 0.0f) v = __builtin_fmaf(p.beta, old[r], v);
+                    if (p.epi.active()) {
+                        const int64_t row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+                        v = epilogue_apply(p.epi, v, t.batch, row, col);
+                    }
+                    store_c<OUT>(C, off[r], v);
                 }
             }
         }

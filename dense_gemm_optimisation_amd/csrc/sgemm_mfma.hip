@@ -199,11 +199,19 @@ __device__ inline void store_c(const SgemmArgs &p, const f32x16 (&acc)[2][2], fl
                     for (int e = 0; e < 4; ++e) v[e] = epilogue_apply(p.epi, v[e], batch, row, col + e);
                 *reinterpret_cast<f4 *>(dst) = v;
             } else {
+                // the chunk's old values are loaded before any is used (from
+                // element 0 of C where an element lies outside the matrix), so
+                // the four loads are in flight together
+                float old[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (p.beta != 0.0f) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) old[e] = *(col + e < p.N ? dst + e : C);
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if (col + e < p.N) {
                         float x = v[e];
-                        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, dst[e], x);
+                        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, old[e], x);
                         if (p.epi.active()) x = epilogue_apply(p.epi, x, batch, row, col + e);
                         dst[e] = x;
                     }
