@@ -11,12 +11,14 @@ from HIP events recorded on the stream the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--no-context] [--no-rotate]
-                       [--copy-calibration MiB]
+                       [--copy-calibration MiB] [--workspace]
 Each kernel cycles through at least three copies of its buffers, enough that
 their footprint exceeds twice the 256 MB MALL, so inputs come from HBM;
 --no-rotate reuses one set (the warm-cache figure).
 --workload runs the named workload, or a comma-separated list of them (see
-workloads.CONFIGS), instead of the headline step, for profiling.  --copy-calibration runs only a plain
+workloads.CONFIGS), instead of the headline step, for profiling.  --workspace runs bf16/fp16 workloads
+through the workspace entry points, which use the stream-K schedule where
+it applies.  --copy-calibration runs only a plain
 device-to-device copy of the given size (the reference kernel against which
 the HBM byte counters FETCH_SIZE / WRITE_SIZE are scaled).
 
@@ -50,6 +52,7 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip",
                  "sgemm_splitk": "sgemm_splitk.hip", "gemm_skinny": "gemm_skinny.hip",
                  "f8gemm_mfma_dma": "f8gemm_mfma.hip", "f8gemm_mfma": "f8gemm_mfma.hip",
+                 "hgemm_mfma_streamk": "hgemm_mfma.hip",
                  "scale": "scale.hip"}
 
 
@@ -93,9 +96,10 @@ def sets_needed(bufs, rotate):
     return min(MAX_SETS, max(MIN_SETS, -(-ROTATE_BYTES // nbytes)))
 
 
-def make_launch(p, sets, stream, bias=None):
+def make_launch(p, sets, stream, bias=None, workspace=None):
     """A callable that runs the GEMM on the next buffer set in turn (with the
-    workload's fused bias and activation, if it has them)."""
+    workload's fused bias and activation, if it has them; through the
+    workspace entry point when a workspace tensor is given)."""
     from dense_gemm_optimisation_amd import binding
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     argsets = [(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a, db.data_ptr(),
@@ -103,6 +107,8 @@ def make_launch(p, sets, stream, bias=None):
                 p.stride_a, p.stride_b, p.stride_c, stream.cuda_stream) for da, db, dc in sets]
     epi = dict(bias=None if bias is None else bias.data_ptr(), stride_bias=p.stride_bias,
                act=p.act, b_dtype=p.b_dtype, out_dtype=p.c_dtype)
+    if workspace is not None:
+        epi.update(workspace=workspace.data_ptr(), workspace_bytes=workspace.numel() * 4)
     turn = [0]
 
     def launch():
@@ -111,7 +117,7 @@ def make_launch(p, sets, stream, bias=None):
     return launch
 
 
-def kernel_family(p, bufs):
+def kernel_family(p, bufs, workspace=None):
     """The kernel libgemm launches for workload p on these device buffers
     (asked of the library itself, so the answer follows its dispatch rules
     and the buffers' actual alignment)."""
@@ -121,7 +127,9 @@ def kernel_family(p, bufs):
     return binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a,
                                db.data_ptr(), p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc,
                                p.order_c, c_dt, p.batch, p.stride_a, p.stride_b, p.stride_c,
-                               b_dtype=p.b_dtype, out_dtype=p.c_dtype)
+                               b_dtype=p.b_dtype, out_dtype=p.c_dtype,
+                               workspace=None if workspace is None else workspace.data_ptr(),
+                               workspace_bytes=0 if workspace is None else workspace.numel() * 4)
 
 
 def source_hash(family):
@@ -197,6 +205,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    ap.add_argument("--workspace", action="store_true",
+                    help="bf16/fp16 workloads through the workspace entry points (stream-K)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the GEMM path has no multi-GPU "
@@ -214,6 +224,9 @@ def main():
     names = HEADLINE if args.workload == "headline" else args.workload.split(",")
     problems = [workloads.config(n) for n in names]
     stream = torch.cuda.Stream()  # default priority
+    ws = None
+    if args.workspace:
+        ws = torch.empty(binding.workspace_size() // 4, dtype=torch.int32, device="cuda")
     launches, nsets, families = [], {}, {}
     with torch.cuda.stream(stream):
         for p in problems:
@@ -221,9 +234,11 @@ def main():
             bufs = device_buffers(p, torch)
             sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
             nsets[p.name] = len(sets)
-            families[p.name] = kernel_family(p, bufs)
+            pws = ws if (ws is not None and p.in_dtype in ("bf16", "f16") and not p.bias
+                         and not p.act) else None
+            families[p.name] = kernel_family(p, bufs, pws)
             bias = device_bias(p, torch)
-            launches.append((p, sets, make_launch(p, sets, stream, bias)))
+            launches.append((p, sets, make_launch(p, sets, stream, bias, pws)))
     torch.cuda.synchronize()
 
     # warmup

@@ -67,6 +67,15 @@ def library() -> ctypes.CDLL:
         lib.gemm_f8.restype = i32
         lib.gemm_f8_kernel_name.argtypes = f8
         lib.gemm_f8_kernel_name.restype = ctypes.c_char_p
+        sz = ctypes.c_size_t
+        lib.gemm_workspace_size.argtypes = []
+        lib.gemm_workspace_size.restype = sz
+        for name in ("gemm_bf16_ws", "gemm_f16_ws"):
+            fn = getattr(lib, name)
+            fn.argtypes = common + [i32, i64, i64, i64, i64, vp, sz, vp]
+            fn.restype = i32
+        lib.gemm_kernel_name_ws.argtypes = [i32] + common + [i32, i64, i64, i64, i64, vp, sz]
+        lib.gemm_kernel_name_ws.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -172,6 +181,31 @@ def f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, f
     return None if name is None else name.decode()
 
 
+def workspace_size() -> int:
+    """Bytes of workspace that let gemm_bf16_ws / gemm_f16_ws use every schedule."""
+    return library().gemm_workspace_size()
+
+
+def gemm_bf16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                 c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, workspace=0,
+                 workspace_bytes=0, stream=None, raise_on_error=True):
+    """gemm_bf16 with a device workspace (address, bytes) for the stream-K schedule."""
+    st = library().gemm_bf16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                                order_c, c_dtype, batch, stride_a, stride_b, stride_c, workspace,
+                                workspace_bytes, _stream(stream))
+    return _check(st, "gemm_bf16_ws", raise_on_error)
+
+
+def gemm_f16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, workspace=0,
+                workspace_bytes=0, stream=None, raise_on_error=True):
+    """gemm_f16 with a device workspace (address, bytes) for the stream-K schedule."""
+    st = library().gemm_f16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                               order_c, c_dtype, batch, stride_a, stride_b, stride_c, workspace,
+                               workspace_bytes, _stream(stream))
+    return _check(st, "gemm_f16_ws", raise_on_error)
+
+
 _F8_FORMAT = {"e4m3": F8_E4M3, "e5m2": F8_E5M2}
 _OUTPUT = {"f32": OUTPUT_F32, "bf16": OUTPUT_BF16, "f16": OUTPUT_F16}
 
@@ -182,11 +216,18 @@ _INPUT = {"f32": 0, "bf16": 1, "f16": 2}
 
 def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
                 c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, b_dtype=None,
-                out_dtype=None):
+                out_dtype=None, workspace=None, workspace_bytes=0):
     """The kernel the GEMM call with these arguments would launch ("" for an
     empty problem, None for invalid arguments); host only, no GPU needed.
     For 8-bit inputs ("e4m3"/"e5m2") b_dtype and out_dtype name B's format
-    and C's type, as in gemm()."""
+    and C's type, as in gemm(); a workspace (16-bit inputs) asks about the
+    workspace entry points."""
+    if workspace is not None:
+        name = library().gemm_kernel_name_ws(_INPUT[in_dtype], M, N, K, alpha, A, lda, order_a, B,
+                                             ldb, order_b, beta, C, ldc, order_c, c_dtype, batch,
+                                             stride_a, stride_b, stride_c, workspace,
+                                             workspace_bytes)
+        return None if name is None else name.decode()
     if in_dtype in _F8_FORMAT:
         return f8_kernel_name(M, N, K, alpha, A, lda, order_a, _F8_FORMAT[in_dtype], B, ldb,
                               order_b, _F8_FORMAT[b_dtype or in_dtype], beta, C, ldc, order_c,
@@ -200,11 +241,19 @@ def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta
 def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
          c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
          raise_on_error=True, bias=None, stride_bias=0, act=ACT_NONE, b_dtype=None,
-         out_dtype=None):
+         out_dtype=None, workspace=None, workspace_bytes=0):
     """Dispatch on the input type name ("f32", "bf16", "f16", or the 8-bit
     "e4m3"/"e5m2" with B's format in b_dtype (default: A's) and C's type
     name in out_dtype); a bias address or an activation selects the
-    fused-epilogue entry point (not offered for 8-bit inputs)."""
+    fused-epilogue entry point (not offered for 8-bit inputs); a workspace
+    address (bf16/fp16, no epilogue) selects the workspace entry point."""
+    if workspace is not None:
+        if in_dtype not in ("bf16", "f16") or bias is not None or act != ACT_NONE:
+            raise ValueError("the workspace entry points take bf16/fp16 inputs without epilogue")
+        fn = gemm_bf16_ws if in_dtype == "bf16" else gemm_f16_ws
+        return fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c, c_dtype,
+                  batch, stride_a, stride_b, stride_c, workspace, workspace_bytes, stream,
+                  raise_on_error)
     if in_dtype in _F8_FORMAT:
         if bias is not None or act != ACT_NONE:
             raise ValueError("8-bit inputs have no fused-epilogue entry point")

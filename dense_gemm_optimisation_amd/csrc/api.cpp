@@ -79,6 +79,7 @@ enum class Kernel {
     HgemmSplitk, // bf16/fp16, few tiles: split-K inside a workgroup
     F8Mfma,      // 8-bit floats, any shape and order
     F8Dma,       // 8-bit floats, K-contiguous aligned operands, direct loads
+    HgemmStreamK,  // bf16/fp16 general kernel on the stream-K schedule (workspace)
 };
 
 const char *kernel_name(Kernel k) {
@@ -95,6 +96,7 @@ const char *kernel_name(Kernel k) {
     case Kernel::HgemmSplitk: return "hgemm_splitk";
     case Kernel::F8Mfma: return "f8gemm_mfma";
     case Kernel::F8Dma: return "f8gemm_mfma_dma";
+    case Kernel::HgemmStreamK: return "hgemm_mfma_streamk";
     }
     return "";
 }
@@ -134,6 +136,7 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::HgemmSplitk: return launch_hgemm_splitk(p, stream);
     case Kernel::F8Mfma: return launch_f8gemm(p, stream);
     case Kernel::F8Dma: return launch_f8gemm_dma(p, stream);
+    case Kernel::HgemmStreamK: return hipErrorInvalidValue;  // needs the workspace: run()
     }
     return hipErrorInvalidValue;
 }
@@ -235,18 +238,46 @@ gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K
     return GEMM_OK;
 }
 
+// With a workspace: its checks, and the switch of the general 16-bit kernel
+// to the stream-K schedule where that schedule applies.
+gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, int orderA,
+                            int64_t lda, int orderB, int64_t ldb, int orderC, int64_t ldc,
+                            int64_t strideA, int64_t strideB, int64_t strideC,
+                            const void *bias, int64_t strideBias, const void *A, const void *B,
+                            const void *C, const void *workspace, size_t bytes, Kernel &k) {
+    if (bytes == 0) return GEMM_OK;
+    if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return GEMM_ERR_INVALID_ARG;
+    const int esz = elem_bytes(p.in), eout = elem_bytes(p.out);
+    const Range rw{reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + bytes};
+    if (overlap(rw, range_of(C, span(M, N, orderC, ldc), p.batch, strideC, eout)) ||
+        overlap(rw, range_of(A, span(M, K, orderA, lda), p.batch, strideA, esz)) ||
+        overlap(rw, range_of(B, span(K, N, orderB, ldb), p.batch, strideB, esz)) ||
+        (bias != nullptr && overlap(rw, range_of(bias, N, p.batch, strideBias, esz))))
+        return GEMM_ERR_INVALID_ARG;
+    if (k == Kernel::HgemmMfma && !force_general() &&
+        bytes >= static_cast<size_t>(hgemm_streamk_workspace_bytes()) && hgemm_streamk_eligible(p))
+        k = Kernel::HgemmStreamK;
+    return GEMM_OK;
+}
+
 gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                   float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
                   int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
-                  hipStream_t stream) {
+                  hipStream_t stream, void *workspace = nullptr, size_t workspace_bytes = 0) {
     Problem p;
     Kernel k;
-    const gemm_status_t st =
+    gemm_status_t st =
         plan(in, in_b, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC,
              batch, strideA, strideB, strideC, bias, strideBias, act, p, k);
+    if (st == GEMM_OK && k != Kernel::None)
+        st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
+                           strideC, bias, strideBias, A, B, C, workspace, workspace_bytes, k);
     if (st != GEMM_OK || k == Kernel::None) return st;
-    const hipError_t err = launch(k, p, stream);
+    const hipError_t err = k == Kernel::HgemmStreamK ? launch_hgemm_streamk(p, workspace, stream)
+                                                     : launch(k, p, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -351,6 +382,32 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha, const uint8_
                batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream);
 }
 
+size_t gemm_workspace_size(void) { return static_cast<size_t>(hgemm_streamk_workspace_bytes()); }
+
+gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                           int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                           gemm_order_t orderB, float beta, void *C, int64_t ldc,
+                           gemm_order_t orderC, gemm_dtype_t c_dtype, int64_t batch,
+                           int64_t strideA, int64_t strideB, int64_t strideC, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
+    return run(Elem::BF16, Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha, A, lda,
+               orderA, B, ldb, orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC,
+               nullptr, 0, GEMM_ACT_NONE, stream, workspace, workspace_bytes);
+}
+
+gemm_status_t gemm_f16_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                          int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                          gemm_order_t orderB, float beta, void *C, int64_t ldc,
+                          gemm_order_t orderC, gemm_dtype_t c_dtype, int64_t batch,
+                          int64_t strideA, int64_t strideB, int64_t strideC, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
+    return run(Elem::F16, Elem::F16, out_type(Elem::F16, c_dtype), M, N, K, alpha, A, lda,
+               orderA, B, ldb, orderB, beta, C, ldc, orderC, batch, strideA, strideB, strideC,
+               nullptr, 0, GEMM_ACT_NONE, stream, workspace, workspace_bytes);
+}
+
 const char *gemm_status_string(gemm_status_t status) {
     switch (status) {
     case GEMM_OK: return "GEMM_OK";
@@ -401,6 +458,32 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha, co
         plan(ea, eb, ec, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta,
              const_cast<void *>(C), ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
              GEMM_ACT_NONE, p, k);
+    return st == GEMM_OK ? kernel_name(k) : nullptr;
+}
+
+const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K, float alpha,
+                                const void *A, int64_t lda, gemm_order_t orderA, const void *B,
+                                int64_t ldb, gemm_order_t orderB, float beta, const void *C,
+                                int64_t ldc, gemm_order_t orderC, gemm_dtype_t c_dtype,
+                                int64_t batch, int64_t strideA, int64_t strideB, int64_t strideC,
+                                const void *workspace, size_t workspace_bytes) {
+    Elem ein;
+    if (in == GEMM_INPUT_BF16)
+        ein = Elem::BF16;
+    else if (in == GEMM_INPUT_F16)
+        ein = Elem::F16;
+    else
+        return nullptr;
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return nullptr;
+    Problem p;
+    Kernel k;
+    gemm_status_t st =
+        plan(ein, ein, out_type(ein, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb, orderB,
+             beta, const_cast<void *>(C), ldc, orderC, batch, strideA, strideB, strideC, nullptr,
+             0, GEMM_ACT_NONE, p, k);
+    if (st == GEMM_OK && k != Kernel::None)
+        st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
+                           strideC, nullptr, 0, A, B, C, workspace, workspace_bytes, k);
     return st == GEMM_OK ? kernel_name(k) : nullptr;
 }
 

@@ -40,6 +40,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -295,49 +296,53 @@ __device__ inline void store_c(void *C, int64_t off, float v) {
         static_cast<uint16_t *>(C)[off] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
 }
 
-template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, bool UB>
-__global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
-    __shared__ u32x4 smem[2][2][PANEL];  // [buffer][A, B][chunk]: 128 KiB
+// threadIdx.x behind an empty volatile statement: values derived from it
+// are then recomputed where they are used instead of being hoisted out of
+// the stream-K kernel's loop over pieces, where they would stay live across
+// the k-step loop and push it into spilling.  (In the one-tile kernel it
+// changes nothing.)
+__device__ inline int opaque_tid() {
+    int t = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(t));
+    return t;
+}
 
-    const TileCoord t = tile_of(p.grid, blockIdx.x);
-    const uint16_t *A = p.A + t.batch * p.sA;
-    const uint16_t *B = p.B + t.batch * p.sB;
-    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
-    const int tid = threadIdx.x;
+// Accumulates k steps [kb, ke) (BK = 64 k each) of tile t into acc:
+// register-staged double buffering through the two LDS buffers, one barrier
+// per step; on return every wave is past the last barrier, so the buffers
+// are free.
+template <class T, bool A_KMAJOR, bool B_KMAJOR, bool UB>
+__device__ __forceinline__ void tile_steps(const HgemmArgs &p, u32x4 (*smem)[2][PANEL],
+                                           const TileCoord &t, int64_t kb, int64_t ke,
+                                           f32x16 (&acc)[4][4]) {
+    const int tid = opaque_tid();
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int lrow = lane & 31, lk = lane >> 5;
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int64_t steps = (p.K + BK - 1) / BK;
+    const uint16_t *A = p.A + t.batch * p.sA;
+    const uint16_t *B = p.B + t.batch * p.sB;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
     const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
     const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
     const UBuf ua = make_ubuf(A, UB ? span_a : 0), ub = make_ubuf(B, UB ? span_b : 0);
     u32x4 va[8], vb[8];
     Raw8 ra[8], rb[8];
     if (UB) {
-        issue_panel<A_KMAJOR>(ua, p.lda, p.M, m0, 0, p.K, tid, ra);
-        issue_panel<B_KMAJOR>(ub, p.ldb, p.N, n0, 0, p.K, tid, rb);
-        finish_panel<A_KMAJOR>(ua, A, p.lda, p.M, m0, 0, p.K, tid, ra, va);
-        finish_panel<B_KMAJOR>(ub, B, p.ldb, p.N, n0, 0, p.K, tid, rb, vb);
+        issue_panel<A_KMAJOR>(ua, p.lda, p.M, m0, kb * BK, p.K, tid, ra);
+        issue_panel<B_KMAJOR>(ub, p.ldb, p.N, n0, kb * BK, p.K, tid, rb);
+        finish_panel<A_KMAJOR>(ua, A, p.lda, p.M, m0, kb * BK, p.K, tid, ra, va);
+        finish_panel<B_KMAJOR>(ub, B, p.ldb, p.N, n0, kb * BK, p.K, tid, rb, vb);
     } else {
-        load_panel<A_KMAJOR>(A, p.lda, p.M, m0, 0, p.K, p.vec_a, tid, va);
-        load_panel<B_KMAJOR>(B, p.ldb, p.N, n0, 0, p.K, p.vec_b, tid, vb);
+        load_panel<A_KMAJOR>(A, p.lda, p.M, m0, kb * BK, p.K, p.vec_a, tid, va);
+        load_panel<B_KMAJOR>(B, p.ldb, p.N, n0, kb * BK, p.K, p.vec_b, tid, vb);
     }
     store_panel<A_KMAJOR>(smem[0][0], tid, va);
     store_panel<B_KMAJOR>(smem[0][1], tid, vb);
     __syncthreads();
 
-    for (int64_t s = 0; s < steps; ++s) {
-        const int cur = s & 1;
-        const bool more = s + 1 < steps;
+    for (int64_t s = kb; s < ke; ++s) {
+        const int cur = (s - kb) & 1;
+        const bool more = s + 1 < ke;
         const int64_t k0 = (s + 1) * BK;
         if (more) {
             if (UB) {
@@ -377,7 +382,17 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
         }
         __syncthreads();
     }
+}
 
+// Epilogue of tile t: alpha * acc (+ beta * C_old, bias, activation) into C.
+template <int OUT>
+__device__ __forceinline__ void tile_store(const HgemmArgs &p, const TileCoord &t,
+                                           const f32x16 (&acc)[4][4]) {
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int tid = opaque_tid();
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = lane & 31, lk = lane >> 5;
     // Epilogue.  Accumulator register r of the 32 x 32 block (i, j) holds
     // row 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that block.  The
     // 16 old values of C a lane needs for a block are loaded before any is
@@ -420,6 +435,159 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
     }
 }
 
+template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, bool UB>
+__global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
+    __shared__ u32x4 smem[2][2][PANEL];  // [buffer][A, B][chunk]: 128 KiB
+    const TileCoord t = tile_of(p.grid, blockIdx.x);
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    tile_steps<T, A_KMAJOR, B_KMAJOR, UB>(p, smem, t, 0, (p.K + BK - 1) / BK, acc);
+    tile_store<OUT>(p, t, acc);
+}
+
+// Stream-K schedule (the persistent / stream-K tile scheduler of section 12.5
+// of "CUDA GEMM 矩阵乘法优化指南", blog.zhenwei.site).  The work is the
+// sequence of (tile, k step) iterations, tiles in the grouped order of
+// tile_of, each tile's steps in k order; workgroup w of G takes the
+// contiguous iterations [w*W/G, (w+1)*W/G).  A tile cut between workgroups
+// is finished by the last of them, the one that runs its final step: it
+// adds the partial sums of the others, lowest workgroup first, to its own and
+// stores the tile.  Every other piece is the piece at the end of its
+// workgroup's range (a range that starts inside a tile and reaches that
+// tile's end is its finisher; one that ends inside a tile ends there), so
+// each workgroup leaves at most one partial tile: workspace slot w, then
+// flag w.  A finisher waits only for lower workgroups, for pieces that are
+// the first work they do, and every wait is bounded, so the grid always
+// drains.
+struct StreamK {
+    float *partials;    // G slots of 256 x 256 floats, [register][thread] per slot
+    uint32_t *flags;    // G flags, zeroed before the launch
+    int64_t steps;      // k steps per tile
+    int64_t iters;      // tiles * steps
+};
+
+constexpr int SK_SLOT = BM * BN;          // floats per partial tile
+constexpr int SK_SPIN_LIMIT = 1 << 22;    // bounded wait (~0.3 s at 128 clocks per try)
+
+// Slot g of the partial tiles as a raw buffer: a lane addresses its values
+// by its thread index (voffset) and the register index (soffset), so no
+// per-register address is kept in vector registers.
+__device__ inline __amdgpu_buffer_rsrc_t slot_rsrc(const StreamK &sk, int64_t g) {
+    return __builtin_amdgcn_make_buffer_rsrc(sk.partials + g * SK_SLOT, 0, SK_SLOT * 4, 0x00020000);
+}
+
+// The schedule's indices are the same in every lane, but 64-bit divisions
+// leave them in vector registers, where they would stay live across the
+// k-step loop and push it into spilling: they are moved to scalar registers.
+__device__ inline int64_t sk_uniform(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(uint64_t(x) >> 32));
+    return static_cast<int64_t>((uint64_t(hi) << 32) | lo);
+}
+
+__global__ __launch_bounds__(256) void sk_clear_flags(uint32_t *flags, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) flags[i] = 0u;
+}
+
+template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, bool UB>
+__global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, StreamK sk) {
+    __shared__ u32x4 smem[2][2][PANEL];
+    // Logical workgroup w: the hardware id regrouped per XCD (xcd_remap),
+    // so that the 32 workgroups of one die take consecutive ranges and share
+    // their tiles' panels in its L2.  Within a die logical order is dispatch
+    // order, and every wait below is for a lower logical id, so the chain of
+    // waits still ends at logical 0, which waits for nothing.
+    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters;
+    const int64_t w = sk_uniform(xcd_remap(blockIdx.x, G, 8));
+    const int tid = threadIdx.x;
+    // The range is walked from its end: its last piece (a partial tile
+    // whenever the range ends inside a tile) is computed and published first,
+    // and its first piece (which finishes a tile begun by lower workgroups,
+    // whenever the range starts inside one) last, so a finisher waits for
+    // pieces that were the first work of their workgroups rather than their
+    // last (which would chain every workgroup behind the one before it).
+    const int64_t begin = sk_uniform(w * W / G);
+    int64_t it_end = sk_uniform((w + 1) * W / G);
+    while (it_end > begin) {
+        const int64_t tile = sk_uniform((it_end - 1) / S);
+        const int64_t kb = (begin > tile * S ? begin : tile * S) - tile * S;
+        const int64_t ke = it_end - tile * S;
+        TileCoord t = tile_of(p.grid, tile);
+        t.batch = sk_uniform(t.batch);
+        t.tm = sk_uniform(t.tm);
+        t.tn = sk_uniform(t.tn);
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        tile_steps<T, A_KMAJOR, B_KMAJOR, UB>(p, smem, t, kb, ke, acc);
+        if (ke < S) {
+            // a partial tile: into slot w, then flag w (release: the writes
+            // reach memory before the flag, for finishers on other dies)
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, w);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // the whole vector is reinterpreted, then indexed: a bit
+                    // cast of one element of it reads element 0 with this
+                    // compiler
+                    const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs, tid * 4,
+                                                              ((i * 4 + j) * 16 + r) * THREADS * 4, 0);
+                }
+            __syncthreads();
+            if (tid == 0) {
+                __threadfence();
+                __hip_atomic_store(sk.flags + w, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            if (kb > 0) {
+                // the workgroups that ran steps [0, kb) of this tile: from the
+                // owner of its first iteration up to w - 1
+                const int64_t g0 = sk_uniform(((tile * S + 1) * G - 1) / W);
+                for (int64_t g = g0; g < w; ++g) {
+                    if (tid == 0) {
+                        int spins = 0;
+                        while (__hip_atomic_load(sk.flags + g, __ATOMIC_ACQUIRE,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+                               ++spins < SK_SPIN_LIMIT)
+                            __builtin_amdgcn_s_sleep(2);
+                    }
+                    __syncthreads();
+                    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, g);
+                    // one 32 x 32 block at a time (the scheduling barrier
+                    // keeps the compiler from loading all 256 values first)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                acc[i][j][r] += __builtin_bit_cast(
+                                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rs, tid * 4, ((i * 4 + j) * 16 + r) * THREADS * 4, 0));
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                }
+            }
+            tile_store<OUT>(p, t, acc);
+        }
+        it_end -= ke - kb;
+    }
+}
+
 template <class T, int OUT, bool AK, bool BKM>
 hipError_t launch(HgemmArgs &a, hipStream_t stream) {
     void *args[] = {&a};
@@ -441,7 +609,9 @@ hipError_t launch_layout(const Problem &p, HgemmArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
+namespace {
+
+HgemmArgs make_args(const Problem &p, int32_t xcds) {
     HgemmArgs a{};
     a.M = p.M;
     a.N = p.N;
@@ -457,8 +627,7 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
     a.sA = p.batch > 1 ? p.sA : 0;
     a.sB = p.batch > 1 ? p.sB : 0;
     a.sC = p.batch > 1 ? p.sC : 0;
-    a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, 4, 8};
-    if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
+    a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, 4, xcds};
     a.vec_a = vec16_ok(p.A, p.lda, a.sA, 2);
     a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 2);
     // raw buffer sizes are 31-bit byte counts
@@ -467,12 +636,89 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
     a.ubuf_a = 2 * span_a + 4 < (int64_t(1) << 31);
     a.ubuf_b = 2 * span_b + 4 < (int64_t(1) << 31);
     a.epi = p.epi;
+    return a;
+}
+
+// Only the raw-buffer variant exists on this schedule (hgemm_streamk_eligible
+// requires operand spans that fit a raw buffer).
+template <class T, int OUT, bool AK, bool BKM>
+hipError_t launch_sk(HgemmArgs &a, StreamK &sk, int64_t G, hipStream_t stream) {
+    void *args[] = {&a, &sk};
+    const void *k = reinterpret_cast<const void *>(&hgemm_streamk_kernel<T, OUT, AK, BKM, true>);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(G)), dim3(THREADS), args, 0, stream);
+}
+
+template <class T, int OUT>
+hipError_t launch_sk_layout(const Problem &p, HgemmArgs &a, StreamK &sk, int64_t G,
+                            hipStream_t stream) {
+    if (p.a_kmajor)
+        return p.b_kmajor ? launch_sk<T, OUT, true, true>(a, sk, G, stream)
+                          : launch_sk<T, OUT, true, false>(a, sk, G, stream);
+    return p.b_kmajor ? launch_sk<T, OUT, false, true>(a, sk, G, stream)
+                      : launch_sk<T, OUT, false, false>(a, sk, G, stream);
+}
+
+// Workgroups of the stream-K grid: one per compute unit of the current
+// device, at most HGEMM_STREAMK_MAX_GRID (the workspace is sized for that).
+int64_t streamk_grid(int64_t iters) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = HGEMM_STREAMK_MAX_GRID;
+    int64_t g = cus < HGEMM_STREAMK_MAX_GRID ? cus : HGEMM_STREAMK_MAX_GRID;
+    return iters < g ? iters : g;
+}
+
+}  // namespace
+
+hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
+    HgemmArgs a = make_args(p, 8);
+    if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)
         return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)
                   : launch_layout<F16, OUT_F32>(p, a, stream);
     return bf ? launch_layout<BF16, OUT_BF16>(p, a, stream)
               : launch_layout<F16, OUT_F16>(p, a, stream);
+}
+
+// Stream-K pays off when the tiles leave the last wave of workgroups (one
+// per compute unit) partly idle; beyond four waves the idle share is small.
+bool hgemm_streamk_eligible(const Problem &p) {
+    if (p.in != Elem::BF16 && p.in != Elem::F16) return false;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+    const int64_t steps = (p.K + BK - 1) / BK;
+    const int64_t g = HGEMM_STREAMK_MAX_GRID;
+    const HgemmArgs a = make_args(p, 1);
+    return a.ubuf_a && a.ubuf_b && tiles % g != 0 && tiles < 4 * g && tiles * steps >= 2 * g &&
+           tiles * steps < (int64_t(1) << 40);
+}
+
+hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+    HgemmArgs a = make_args(p, 1);  // the work order itself spreads tiles over the dies
+    StreamK sk{};
+    sk.steps = (p.K + BK - 1) / BK;
+    sk.iters = a.grid.count() * sk.steps;
+    const int64_t G = streamk_grid(sk.iters);
+    sk.partials = static_cast<float *>(workspace);
+    sk.flags = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
+                                            HGEMM_STREAMK_MAX_GRID * int64_t(SK_SLOT) * 4);
+    {
+        uint32_t *flags = sk.flags;
+        int n = static_cast<int>(G);
+        void *args[] = {&flags, &n};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sk_clear_flags),
+                                             dim3(static_cast<unsigned>((G + 255) / 256)),
+                                             dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    const bool bf = p.in == Elem::BF16;
+    if (p.out == Elem::F32)
+        return bf ? launch_sk_layout<BF16, OUT_F32>(p, a, sk, G, stream)
+                  : launch_sk_layout<F16, OUT_F32>(p, a, sk, G, stream);
+    return bf ? launch_sk_layout<BF16, OUT_BF16>(p, a, sk, G, stream)
+              : launch_sk_layout<F16, OUT_F16>(p, a, sk, G, stream);
 }
 
 }  // namespace libgemm

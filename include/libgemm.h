@@ -23,7 +23,11 @@
  *              and an activation applied before the store (see below).
  *   gemm_f8    8-bit float inputs (OCP E4M3 or E5M2, each operand in its own
  *              format), fp32 accumulation, output in fp32, bf16 or fp16.
- *   gemm_kernel_name, gemm_f8_kernel_name  which kernel a GEMM call with the
+ *   gemm_bf16_ws, gemm_f16_ws  gemm_bf16 / gemm_f16 with a caller-provided
+ *              workspace, which lets the library run the stream-K schedule
+ *              (see below); gemm_workspace_size gives the bytes it uses.
+ *   gemm_kernel_name, gemm_f8_kernel_name, gemm_kernel_name_ws  which kernel
+ *              a GEMM call with the
  *              given arguments would launch (host only; for tests and
  *              profiling).
  *
@@ -72,6 +76,7 @@
 #ifndef LIBGEMM_H
 #define LIBGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -235,6 +240,47 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
                       gemm_output_t typeC, int64_t batch, int64_t strideA,
                       int64_t strideB, int64_t strideC, hipStream_t stream);
 
+/* Workspace entry points.  gemm_bf16_ws / gemm_f16_ws take the arguments of
+ * gemm_bf16 / gemm_f16 plus a device workspace, and compute the same product.
+ * With at least gemm_workspace_size() bytes, a problem on the general kernel
+ * (operands that are not 16-byte aligned) whose 256 x 256 tiles leave the
+ * last wave of workgroups partly idle (tiles not a multiple of 256, fewer
+ * than 1024 of them) runs on the stream-K schedule ("CUDA GEMM 矩阵乘法优化
+ * 指南", blog.zhenwei.site, section 12.5, persistent kernels and Stream-K):
+ * the (tile, k-step) iterations are split evenly over one workgroup per
+ * compute unit, a tile cut between workgroups being finished by the last of
+ * them, which adds the others' partial sums in a fixed order.  Results are
+ * deterministic run to run; they may differ in rounding from gemm_bf16 (the
+ * partial sums are grouped differently), within the same accuracy.  Every
+ * other call ignores the workspace and behaves exactly like gemm_bf16.
+ *   workspace        device memory, 256-byte aligned, not overlapping A, B or
+ *                    C; owned by the caller and clobbered by the call (it
+ *                    holds partial tiles and flags while the kernels run on
+ *                    `stream`; calls that share a workspace must be ordered
+ *                    on one stream).  NULL only with workspace_bytes = 0.
+ *   workspace_bytes  its size; smaller than gemm_workspace_size() (0
+ *                    included) means the workspace is not used.
+ * A misaligned, overlapping or NULL (with bytes > 0) workspace is
+ * GEMM_ERR_INVALID_ARG; everything else is as for gemm_bf16. */
+size_t gemm_workspace_size(void);
+
+gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                           const uint16_t *A, int64_t lda, gemm_order_t orderA,
+                           const uint16_t *B, int64_t ldb, gemm_order_t orderB,
+                           float beta, void *C, int64_t ldc,
+                           gemm_order_t orderC, gemm_dtype_t c_dtype,
+                           int64_t batch, int64_t strideA, int64_t strideB,
+                           int64_t strideC, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+gemm_status_t gemm_f16_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                          const uint16_t *A, int64_t lda, gemm_order_t orderA,
+                          const uint16_t *B, int64_t ldb, gemm_order_t orderB,
+                          float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                          gemm_dtype_t c_dtype, int64_t batch, int64_t strideA,
+                          int64_t strideB, int64_t strideC, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *gemm_status_string(gemm_status_t status);
 
@@ -274,6 +320,20 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
                                 gemm_order_t orderC, gemm_output_t typeC,
                                 int64_t batch, int64_t strideA,
                                 int64_t strideB, int64_t strideC);
+
+/* The kernel gemm_bf16_ws (in = GEMM_INPUT_BF16) or gemm_f16_ws
+ * (GEMM_INPUT_F16) would launch: the names of gemm_kernel_name, or
+ * "hgemm_mfma_streamk" for the stream-K schedule; "" and NULL as for
+ * gemm_kernel_name (NULL also for in = GEMM_INPUT_F32).  The workspace is
+ * only checked, never dereferenced. */
+const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K,
+                                float alpha, const void *A, int64_t lda,
+                                gemm_order_t orderA, const void *B, int64_t ldb,
+                                gemm_order_t orderB, float beta, const void *C,
+                                int64_t ldc, gemm_order_t orderC,
+                                gemm_dtype_t c_dtype, int64_t batch,
+                                int64_t strideA, int64_t strideB, int64_t strideC,
+                                const void *workspace, size_t workspace_bytes);
 
 #ifdef __cplusplus
 }

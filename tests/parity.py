@@ -189,8 +189,21 @@ def default_sample(p: workloads.Problem, rng, n_random=4096):
     return idx
 
 
+_WORKSPACE = []
+
+
+def workspace():
+    """One device workspace of gemm_workspace_size() bytes, shared by the
+    tests (each call reuses it, as a caller would), filled with NaN patterns
+    so that a partial tile read before it was written shows up."""
+    if not _WORKSPACE:
+        n = binding.workspace_size()
+        _WORKSPACE.append(torch.full((n // 4,), -1, dtype=torch.int32, device="cuda"))
+    return _WORKSPACE[0]
+
+
 def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
-        base_offset=(0, 0, 0), repeat=1, bias_host=None):
+        base_offset=(0, 0, 0), repeat=1, bias_host=None, use_workspace=False, workspace_bytes=None):
     """Run p on the GPU (optionally `repeat` times) and compare with the oracle.
 
     host: (A, B, C0) host buffers, else generated from the workload recipe.
@@ -199,6 +212,8 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
     c_init: a value written over the whole initial C (e.g. NaN when beta == 0).
     base_offset: elements by which each device base pointer is shifted (to
     test misaligned bases).
+    use_workspace: call the workspace entry point (bf16/fp16) with the
+    shared workspace, of workspace_bytes bytes (default: all of it).
     Returns (Result, output bits of the whole C buffer including guards).
     """
     log(f"[parity] {p.name} {p.in_dtype}->{p.c_dtype} M={p.M} N={p.N} K={p.K} "
@@ -220,11 +235,16 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
                   dc.data_ptr() + sc * esz_out)
     pbias = dbias.data_ptr() + sbias * esz_in if bias is not None else None
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
+    ws = {}
+    if use_workspace:
+        w = workspace()
+        ws = dict(workspace=w.data_ptr(),
+                  workspace_bytes=w.numel() * 4 if workspace_bytes is None else workspace_bytes)
     cview = np.int32 if p.c_dtype == "f32" else np.int16
     kernel = binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb,
                                  p.ldb, p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch,
                                  p.stride_a, p.stride_b, p.stride_c, b_dtype=p.b_dtype,
-                                 out_dtype=p.c_dtype)
+                                 out_dtype=p.c_dtype, **ws)
     outs = []
     for r in range(repeat):
         if r:
@@ -232,7 +252,7 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         binding.gemm(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
                      p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch, p.stride_a,
                      p.stride_b, p.stride_c, bias=pbias, stride_bias=p.stride_bias, act=p.act,
-                     b_dtype=p.b_dtype, out_dtype=p.c_dtype)
+                     b_dtype=p.b_dtype, out_dtype=p.c_dtype, **ws)
         torch.cuda.synchronize()
         outs.append(dc.cpu().numpy().view(fc.dtype).copy())
     out = outs[0]

@@ -28,9 +28,11 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
-                                    "gemm_f16", "gemm_f16_bias_act", "gemm_f32",
-                                    "gemm_f32_bias_act", "gemm_f8", "gemm_f8_kernel_name",
-                                    "gemm_kernel_name", "gemm_status_string"]
+                                    "gemm_bf16_ws", "gemm_f16", "gemm_f16_bias_act",
+                                    "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act", "gemm_f8",
+                                    "gemm_f8_kernel_name", "gemm_kernel_name",
+                                    "gemm_kernel_name_ws", "gemm_status_string",
+                                    "gemm_workspace_size"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -306,3 +308,57 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
                               p.stride_a, p.stride_b, p.stride_c, b_dtype=p.b_dtype,
                               out_dtype=p.c_dtype)
         assert got == k, name
+
+
+# ------------------------------------------------------------------ workspace entry points (host only)
+
+WS = 5 * GB  # fake, 256-byte aligned workspace address
+
+
+def test_workspace_size(lib):
+    # one 256 x 256 fp32 partial tile and one flag per workgroup, 256 workgroups
+    assert lib.workspace_size() == 256 * 256 * 256 * 4 + 256 * 4
+
+
+def kname_ws(lib, dt, M, N, K, ws=WS, nbytes=None, **kw):
+    oa, ob, oc = kw.pop("oa", 0), kw.pop("ob", 0), kw.pop("oc", 0)
+    lda = kw.pop("lda", K if oa == 0 else M)
+    ldb = kw.pop("ldb", N if ob == 0 else K)
+    ldc = kw.pop("ldc", N if oc == 0 else M)
+    nbytes = lib.workspace_size() if nbytes is None else nbytes
+    return lib.kernel_name(dt, M, N, K, kw.pop("alpha", 1.0), GB, lda, oa, 2 * GB, ldb, ob, 0.0,
+                           3 * GB, ldc, oc, 0, kw.pop("batch", 1), 0, 0, 0, workspace=ws,
+                           workspace_bytes=nbytes)
+
+
+def test_streamk_kernel_choice(lib, clean_env):
+    # unaligned (general kernel), 272 tiles: stream-K
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_streamk"
+    assert kname_ws(lib, "f16", 300, 290, 8193) == "hgemm_mfma_streamk"
+    # workspace too small, or absent: the plain general kernel
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001, nbytes=1 << 20) == "hgemm_mfma"
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001, ws=0, nbytes=0) == "hgemm_mfma"
+    # whole waves (256 tiles), too little work, or the aligned fast path
+    assert kname_ws(lib, "bf16", 4095, 4095, 1001) == "hgemm_mfma"
+    assert kname_ws(lib, "bf16", 300, 290, 131) == "hgemm_mfma"
+    assert kname_ws(lib, "bf16", 4096, 4352, 1024) == "hgemm_mfma_dma"
+    # fp32 has no workspace entry point; K = 0 scales C
+    assert kname_ws(lib, "f32", 4095, 4097, 1001) is None
+    assert kname_ws(lib, "bf16", 4095, 4097, 0, lda=1) == "scale"
+    clean_env.setenv("LIBGEMM_FORCE_GENERAL", "1")
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma"
+
+
+def test_workspace_invalid_arguments(lib):
+    n = lib.workspace_size()
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001, ws=0, nbytes=n) is None       # NULL
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001, ws=WS + 16) is None           # misaligned
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001, ws=3 * GB - 256) is None      # overlaps C
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001, ws=GB + 1024) is None         # overlaps A
+    args = (8, 8, 8, 1.0, P, 8, 0, P * 3, 8, 0, 0.0, P * 5, 8, 0, 0, 1, 0, 0, 0)
+    for fn in (lib.gemm_bf16_ws, lib.gemm_f16_ws):
+        assert fn(*args, 0, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG
+        assert fn(*args, P * 5 - 256, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG  # over C
+        assert fn(-1, *args[1:], WS, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG
+        assert fn(0, *args[1:], WS, n, 0, raise_on_error=False) == lib.OK
+        assert fn(*args[:14], 2, *args[15:], WS, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG

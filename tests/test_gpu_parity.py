@@ -646,3 +646,56 @@ def test_f8_truncation_worst_case_within_bound():
             workloads.to_8bit(b.astype(np.float32).ravel(), "e5m2"), np.zeros(M * N, np.float32))
     res, _ = check(p, kernel="f8gemm_mfma_dma", host=host)
     log(f"f8 truncation worst case: max normalised error {res.max_err:.3e}")
+
+
+# ------------------------------------------------------------------ stream-K schedule (workspace entry points)
+
+# Shapes on the general kernel (leading dimensions not multiples of 8
+# elements) whose tiles do not fill whole waves of 256 workgroups: few tiles
+# with a long K (every tile cut across many workgroups), and the 272-tile
+# problem with one tile per workgroup and a little more.
+SK_SHAPES = [(300, 290, 8193), (513, 770, 3001), (1000, 1030, 1701)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_streamk_general_kernel(dt, shape, orders):
+    M, N, K = shape
+    oa, ob = orders
+    check(P(f"streamk-{dt}", dt, M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
+          kernel="hgemm_mfma_streamk", seed=M + K, use_workspace=True, repeat=2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_streamk_fp32_output_batch_and_col_major_c(dt):
+    check(P(f"streamk-f32out-{dt}", dt, 300, 290, 4099, c_dtype="f32", beta=1.0, batch=3),
+          kernel="hgemm_mfma_streamk", seed=80, use_workspace=True)
+    check(P(f"streamk-colC-{dt}", dt, 290, 300, 8197, order_c=COL, ldc=293, beta=0.5),
+          kernel="hgemm_mfma_streamk", seed=81, use_workspace=True)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_streamk_integers_bit_exact(dt):
+    # every partial sum of small integers is exact in fp32, so the fixed-order
+    # fix-up must reproduce the oracle bit for bit
+    p = P(f"streamk-int-{dt}", dt, 513, 770, 3001, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="hgemm_mfma_streamk", host=_int_host(p, np.random.default_rng(82)),
+                   use_workspace=True)
+    assert res.max_err == 0.0 and res.max_ulp == 0
+
+
+def test_streamk_workspace_too_small_is_the_plain_call():
+    p = P("streamk-small-ws", "bf16", 513, 770, 3001, beta=0.5)
+    host = workloads.generate(p, seed=83)
+    _, plain = check(p, kernel="hgemm_mfma", host=host)
+    _, small = check(p, kernel="hgemm_mfma", host=host, use_workspace=True,
+                     workspace_bytes=1 << 20)
+    assert np.array_equal(plain, small)
+
+
+def test_streamk_edge_config_sampled():
+    # the unaligned 4095 x 4097 x 1001 problem: 272 tiles on 256 compute units
+    check(workloads.config("bf16_edge"), kernel="hgemm_mfma_streamk", sample="auto",
+          use_workspace=True, repeat=2)
