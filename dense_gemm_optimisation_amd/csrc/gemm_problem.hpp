@@ -63,10 +63,11 @@ hipError_t launch_sgemm_splitk(const Problem &p, hipStream_t stream);
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA, any shape
 // The same kernel's stream-K schedule, which cuts tiles across workgroups
 // through a caller-provided workspace of hgemm_streamk_workspace_bytes()
-// (partial tiles and flags); only where hgemm_streamk_eligible() holds.
+// (two fp32 partial 256 x 256 tiles per workgroup); only where
+// hgemm_streamk_eligible() holds.
 constexpr int64_t HGEMM_STREAMK_MAX_GRID = 256;
 constexpr int64_t hgemm_streamk_workspace_bytes() {
-    return HGEMM_STREAMK_MAX_GRID * 256 * 256 * 4 + HGEMM_STREAMK_MAX_GRID * 4;
+    return 2 * HGEMM_STREAMK_MAX_GRID * 256 * 256 * 4;
 }
 bool hgemm_streamk_eligible(const Problem &p);
 hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);

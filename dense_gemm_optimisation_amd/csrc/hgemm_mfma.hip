@@ -40,6 +40,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -384,6 +385,55 @@ __device__ __forceinline__ void tile_steps(const HgemmArgs &p, u32x4 (*smem)[2][
     }
 }
 
+// Epilogue of registers [r0, r0 + NR) of accumulator block (i, j) of the
+// thread's wave in tile t, v[q] holding register r0 + q (a vector of at least
+// NR floats), for the stream-K fix-up: the same arithmetic as tile_store
+// (below), alpha * v (+ beta * C_old, bias, activation) into C.  Accumulator register r of a 32 x 32 block holds row
+// 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that block.  The old
+// values of C are loaded before any is used, from element 0 of C where the
+// element lies outside the matrix (a valid address, the value discarded): a
+// load behind each element's bounds test would be waited for before the next
+// one is issued.
+template <int OUT, int NR, class V>
+__device__ __forceinline__ void store_regs(const HgemmArgs &p, const TileCoord &t, int i, int j,
+                                           int r0, const V &v) {
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int tid = opaque_tid();
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = lane & 31, lk = lane >> 5;
+    void *C = static_cast<char *>(p.C) + t.batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
+    const int64_t col = n0 + wn * 128 + j * 32 + lrow;
+    int64_t off[NR];
+    bool in[NR];
+    float old[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+        const int r = r0 + q;
+        const int64_t row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+        in[q] = row < p.M && col < p.N;
+        off[q] = in[q] ? row * p.ldc + col : 0;
+        old[q] = 0.0f;
+    }
+    if (p.beta != 0.0f) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) old[q] = load_c<OUT>(C, off[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+        if (in[q]) {
+            float x = p.alpha * v[q];
+            if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, old[q], x);
+            if (p.epi.active()) {
+                const int r = r0 + q;
+                const int64_t row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+                x = epilogue_apply(p.epi, x, t.batch, row, col);
+            }
+            store_c<OUT>(C, off[q], x);
+        }
+    }
+}
+
 // Epilogue of tile t: alpha * acc (+ beta * C_old, bias, activation) into C.
 template <int OUT>
 __device__ __forceinline__ void tile_store(const HgemmArgs &p, const TileCoord &t,
@@ -451,34 +501,42 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
 }
 
 // Stream-K schedule (the persistent / stream-K tile scheduler of section 12.5
-// of "CUDA GEMM 矩阵乘法优化指南", blog.zhenwei.site).  The work is the
-// sequence of (tile, k step) iterations, tiles in the grouped order of
-// tile_of, each tile's steps in k order; workgroup w of G takes the
-// contiguous iterations [w*W/G, (w+1)*W/G).  A tile cut between workgroups
-// is finished by the last of them, the one that runs its final step: it
-// adds the partial sums of the others, lowest workgroup first, to its own and
-// stores the tile.  Every other piece is the piece at the end of its
-// workgroup's range (a range that starts inside a tile and reaches that
-// tile's end is its finisher; one that ends inside a tile ends there), so
-// each workgroup leaves at most one partial tile: workspace slot w, then
-// flag w.  A finisher waits only for lower workgroups, for pieces that are
-// the first work they do, and every wait is bounded, so the grid always
-// drains.
+// of "CUDA GEMM 矩阵乘法优化指南", blog.zhenwei.site), in two kernels.
+//
+// hgemm_streamk_kernel runs one workgroup per compute unit (G of them).  The
+// tiles that fill whole waves of G workgroups, in the grouped order of
+// tile_of, are computed as in hgemm_kernel, tile w + n*G by workgroup w.  The
+// rest, the last partial wave of T_r tiles, is cut into its W = T_r * S
+// (tile, k step) iterations, each tile's steps in k order, and workgroup
+// w < Gs = min(G, W) takes the contiguous iterations [w*W/Gs, (w+1)*W/Gs).
+// A piece that covers a whole tile is stored through the epilogue; any other
+// is a partial tile, written to the workspace.  Only the first and the last
+// piece of a range can be partial, so workgroup w owns two slots: 2w for the
+// piece holding its last iteration, 2w + 1 for the one holding its first.
+//
+// hgemm_streamk_fixup then finishes each tile that was cut: 64 workgroups per
+// tile, each summing one quarter of one 32 x 32 block per wave over the
+// tile's pieces in increasing workgroup order (a fixed order, so results do
+// not change from run to run) and applying the epilogue.  The kernels
+// exchange data only across the launch boundary on one stream: no workgroup
+// waits for another.
 struct StreamK {
-    float *partials;    // G slots of 256 x 256 floats, [register][thread] per slot
-    uint32_t *flags;    // G flags, zeroed before the launch
-    int64_t steps;      // k steps per tile
-    int64_t iters;      // tiles * steps
+    float *partials;    // 2 * Gs slots of 256 x 256 floats
+    int64_t steps;      // k steps per tile (S)
+    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
+    int64_t iters;      // W = (tiles - dp_tiles) * steps
+    int64_t groups;     // Gs = min(grid, W)
 };
 
-constexpr int SK_SLOT = BM * BN;          // floats per partial tile
-constexpr int SK_SPIN_LIMIT = 1 << 22;    // bounded wait (~0.3 s at 128 clocks per try)
+constexpr int SK_SLOT = BM * BN;  // floats per partial tile
 
-// Slot g of the partial tiles as a raw buffer: a lane addresses its values
-// by its thread index (voffset) and the register index (soffset), so no
-// per-register address is kept in vector registers.
-__device__ inline __amdgpu_buffer_rsrc_t slot_rsrc(const StreamK &sk, int64_t g) {
-    return __builtin_amdgcn_make_buffer_rsrc(sk.partials + g * SK_SLOT, 0, SK_SLOT * 4, 0x00020000);
+// Slot `slot` of the partial tiles as a raw buffer.  Within a slot, register
+// quad q (registers 4q .. 4q+3) of block (i, j) of thread tid is the 16 bytes
+// at ((i*4 + j)*4 + q) * THREADS * 16 + tid * 16: every store and load of a
+// wave covers 1 KiB of consecutive bytes.
+__device__ inline __amdgpu_buffer_rsrc_t slot_rsrc(const StreamK &sk, int64_t slot) {
+    return __builtin_amdgcn_make_buffer_rsrc(sk.partials + slot * SK_SLOT, 0, SK_SLOT * 4,
+                                             0x00020000);
 }
 
 // The schedule's indices are the same in every lane, but 64-bit divisions
@@ -490,34 +548,32 @@ __device__ inline int64_t sk_uniform(int64_t x) {
     return static_cast<int64_t>((uint64_t(hi) << 32) | lo);
 }
 
-__global__ __launch_bounds__(256) void sk_clear_flags(uint32_t *flags, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) flags[i] = 0u;
-}
-
 template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, bool UB>
 __global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, StreamK sk) {
     __shared__ u32x4 smem[2][2][PANEL];
-    // Logical workgroup w: the hardware id regrouped per XCD (xcd_remap),
-    // so that the 32 workgroups of one die take consecutive ranges and share
-    // their tiles' panels in its L2.  Within a die logical order is dispatch
-    // order, and every wait below is for a lower logical id, so the chain of
-    // waits still ends at logical 0, which waits for nothing.
-    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters;
+    // Logical workgroup w: the hardware id regrouped per XCD (xcd_remap), so
+    // that the workgroups of one die take consecutive tiles and ranges and
+    // share their panels in its L2.
+    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters, Gs = sk.groups;
     const int64_t w = sk_uniform(xcd_remap(blockIdx.x, G, 8));
-    const int tid = threadIdx.x;
-    // The range is walked from its end: its last piece (a partial tile
-    // whenever the range ends inside a tile) is computed and published first,
-    // and its first piece (which finishes a tile begun by lower workgroups,
-    // whenever the range starts inside one) last, so a finisher waits for
-    // pieces that were the first work of their workgroups rather than their
-    // last (which would chain every workgroup behind the one before it).
-    const int64_t begin = sk_uniform(w * W / G);
-    int64_t it_end = sk_uniform((w + 1) * W / G);
-    while (it_end > begin) {
-        const int64_t tile = sk_uniform((it_end - 1) / S);
-        const int64_t kb = (begin > tile * S ? begin : tile * S) - tile * S;
-        const int64_t ke = it_end - tile * S;
+    const int64_t n_dp = w < sk.dp_tiles ? sk_uniform((sk.dp_tiles - w + G - 1) / G) : 0;
+    const int64_t begin = w < Gs ? sk_uniform(w * W / Gs) : 0;
+    const int64_t end = w < Gs ? sk_uniform((w + 1) * W / Gs) : 0;
+    int64_t it = begin;
+    for (int64_t item = 0;; ++item) {
+        int64_t tile, kb, ke, local = 0;
+        if (item < n_dp) {
+            tile = w + item * G;
+            kb = 0;
+            ke = S;
+        } else {
+            if (it >= end) break;
+            local = sk_uniform(it / S);
+            kb = it - local * S;
+            ke = end - local * S < S ? end - local * S : S;
+            tile = sk.dp_tiles + local;
+            it = local * S + ke;
+        }
         TileCoord t = tile_of(p.grid, tile);
         t.batch = sk_uniform(t.batch);
         t.tm = sk_uniform(t.tm);
@@ -530,10 +586,12 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         tile_steps<T, A_KMAJOR, B_KMAJOR, UB>(p, smem, t, kb, ke, acc);
-        if (ke < S) {
-            // a partial tile: into slot w, then flag w (release: the writes
-            // reach memory before the flag, for finishers on other dies)
-            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, w);
+        if (kb == 0 && ke == S) {
+            tile_store<OUT>(p, t, acc);
+        } else {
+            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, 2 * w + side);
+            const int tid = opaque_tid();
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -543,49 +601,57 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, 
                     // compiler
                     const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs, tid * 4,
-                                                              ((i * 4 + j) * 16 + r) * THREADS * 4, 0);
-                }
-            __syncthreads();
-            if (tid == 0) {
-                __threadfence();
-                __hip_atomic_store(sk.flags + w, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        } else {
-            if (kb > 0) {
-                // the workgroups that ran steps [0, kb) of this tile: from the
-                // owner of its first iteration up to w - 1
-                const int64_t g0 = sk_uniform(((tile * S + 1) * G - 1) / W);
-                for (int64_t g = g0; g < w; ++g) {
-                    if (tid == 0) {
-                        int spins = 0;
-                        while (__hip_atomic_load(sk.flags + g, __ATOMIC_ACQUIRE,
-                                                 __HIP_MEMORY_SCOPE_AGENT) == 0u &&
-                               ++spins < SK_SPIN_LIMIT)
-                            __builtin_amdgcn_s_sleep(2);
+                    for (int q = 0; q < 4; ++q) {
+                        const u32x4 v = {bits[4 * q], bits[4 * q + 1], bits[4 * q + 2],
+                                         bits[4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v, rs, tid * 16, ((i * 4 + j) * 4 + q) * THREADS * 16, 0);
                     }
-                    __syncthreads();
-                    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, g);
-                    // one 32 x 32 block at a time (the scheduling barrier
-                    // keeps the compiler from loading all 256 values first)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                            for (int r = 0; r < 16; ++r)
-                                acc[i][j][r] += __builtin_bit_cast(
-                                    float, __builtin_amdgcn_raw_buffer_load_b32(
-                                               rs, tid * 4, ((i * 4 + j) * 16 + r) * THREADS * 4, 0));
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
                 }
-            }
-            tile_store<OUT>(p, t, acc);
         }
-        it_end -= ke - kb;
     }
+}
+
+// The workgroup that owns iteration x of the cut tiles: the largest g with
+// g*W/Gs <= x.
+__device__ inline int64_t sk_owner(const StreamK &sk, int64_t x) {
+    return ((x + 1) * sk.groups - 1) / sk.iters;
+}
+
+// Workgroup (local tile, piece): piece = (i*4 + j)*4 + q sums register quad q
+// of block (i, j) over the pieces of local tile `local` of the cut tiles,
+// lowest workgroup first, and stores it.  A tile inside one range was stored
+// whole by hgemm_streamk_kernel and its workgroups return at once.
+constexpr int SK_BATCH = 8;  // pieces whose loads are in flight together
+
+template <int OUT>
+__global__ __launch_bounds__(THREADS) void hgemm_streamk_fixup(HgemmArgs p, StreamK sk) {
+    const int64_t S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t local = blockIdx.x / 64;
+    const int piece = blockIdx.x % 64;
+    const int64_t g0 = sk_owner(sk, local * S), g1 = sk_owner(sk, local * S + S - 1);
+    if (g0 == g1) return;
+    const int tid = threadIdx.x;
+    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t g = g0; g <= g1; g += SK_BATCH) {
+        u32x4 v[SK_BATCH];
+#pragma unroll
+        for (int u = 0; u < SK_BATCH; ++u) {
+            // past the last piece: an offset beyond the buffer reads zeros
+            const int64_t gu = g + u <= g1 ? g + u : g1;
+            const int64_t end = (gu + 1) * W / Gs;
+            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
+            const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
+            v[u] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, 2 * gu + side), off,
+                                                             piece * THREADS * 16, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < SK_BATCH; ++u) sum += __builtin_bit_cast(f32x4, v[u]);
+    }
+    const TileCoord t = tile_of(p.grid, sk.dp_tiles + local);
+    const int blk = piece >> 2, q = piece & 3;
+    store_regs<OUT, 4>(p, t, blk >> 2, blk & 3, 4 * q, sum);
 }
 
 template <class T, int OUT, bool AK, bool BKM>
@@ -642,33 +708,43 @@ HgemmArgs make_args(const Problem &p, int32_t xcds) {
 // Only the raw-buffer variant exists on this schedule (hgemm_streamk_eligible
 // requires operand spans that fit a raw buffer).
 template <class T, int OUT, bool AK, bool BKM>
-hipError_t launch_sk(HgemmArgs &a, StreamK &sk, int64_t G, hipStream_t stream) {
+hipError_t launch_sk(HgemmArgs &a, StreamK &sk, int64_t grid, hipStream_t stream) {
     void *args[] = {&a, &sk};
     const void *k = reinterpret_cast<const void *>(&hgemm_streamk_kernel<T, OUT, AK, BKM, true>);
-    return hipLaunchKernel(k, dim3(static_cast<unsigned>(G)), dim3(THREADS), args, 0, stream);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(grid)), dim3(THREADS), args, 0, stream);
 }
 
 template <class T, int OUT>
-hipError_t launch_sk_layout(const Problem &p, HgemmArgs &a, StreamK &sk, int64_t G,
+hipError_t launch_sk_layout(const Problem &p, HgemmArgs &a, StreamK &sk, int64_t grid,
                             hipStream_t stream) {
+    hipError_t e;
     if (p.a_kmajor)
-        return p.b_kmajor ? launch_sk<T, OUT, true, true>(a, sk, G, stream)
-                          : launch_sk<T, OUT, true, false>(a, sk, G, stream);
-    return p.b_kmajor ? launch_sk<T, OUT, false, true>(a, sk, G, stream)
-                      : launch_sk<T, OUT, false, false>(a, sk, G, stream);
+        e = p.b_kmajor ? launch_sk<T, OUT, true, true>(a, sk, grid, stream)
+                       : launch_sk<T, OUT, true, false>(a, sk, grid, stream);
+    else
+        e = p.b_kmajor ? launch_sk<T, OUT, false, true>(a, sk, grid, stream)
+                       : launch_sk<T, OUT, false, false>(a, sk, grid, stream);
+    if (e != hipSuccess || sk.iters == 0) return e;
+    void *args[] = {&a, &sk};
+    const int64_t cut = a.grid.count() - sk.dp_tiles;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&hgemm_streamk_fixup<OUT>),
+                           dim3(static_cast<unsigned>(cut * 64)), dim3(THREADS), args, 0, stream);
 }
 
 // Workgroups of the stream-K grid: one per compute unit of the current
 // device, at most HGEMM_STREAMK_MAX_GRID (the workspace is sized for that).
-int64_t streamk_grid(int64_t iters) {
+int64_t streamk_grid() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = HGEMM_STREAMK_MAX_GRID;
-    int64_t g = cus < HGEMM_STREAMK_MAX_GRID ? cus : HGEMM_STREAMK_MAX_GRID;
-    return iters < g ? iters : g;
+    return cus < HGEMM_STREAMK_MAX_GRID ? cus : HGEMM_STREAMK_MAX_GRID;
 }
+
+// Cost of the partial-tile exchange (writing the pieces, the fix-up kernel),
+// in k steps of one 256 x 256 tile, measured on MI355X.
+constexpr int64_t SK_EXCHANGE_STEPS = 4;
 
 }  // namespace
 
@@ -684,41 +760,40 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
 }
 
 // Stream-K pays off when the tiles leave the last wave of workgroups (one
-// per compute unit) partly idle; beyond four waves the idle share is small.
+// per compute unit) partly idle, and when the steps it saves there exceed the
+// cost of exchanging partial tiles: the last wave then takes
+// ceil(T_r * S / G) steps per workgroup instead of S.  The model uses
+// HGEMM_STREAMK_MAX_GRID compute units (MI355X has 256).
 bool hgemm_streamk_eligible(const Problem &p) {
     if (p.in != Elem::BF16 && p.in != Elem::F16) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
     const int64_t steps = (p.K + BK - 1) / BK;
     const int64_t g = HGEMM_STREAMK_MAX_GRID;
+    const int64_t cut = tiles % g;
+    if (cut == 0 || tiles >= (int64_t(1) << 24) || steps >= (int64_t(1) << 24)) return false;
+    const int64_t tail = (cut * steps + g - 1) / g;
     const HgemmArgs a = make_args(p, 1);
-    return a.ubuf_a && a.ubuf_b && tiles % g != 0 && tiles < 4 * g && tiles * steps >= 2 * g &&
-           tiles * steps < (int64_t(1) << 40);
+    return a.ubuf_a && a.ubuf_b && steps - tail > SK_EXCHANGE_STEPS;
 }
 
 hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {
     HgemmArgs a = make_args(p, 1);  // the work order itself spreads tiles over the dies
+    const int64_t tiles = a.grid.count();
+    const int64_t G = streamk_grid();
     StreamK sk{};
-    sk.steps = (p.K + BK - 1) / BK;
-    sk.iters = a.grid.count() * sk.steps;
-    const int64_t G = streamk_grid(sk.iters);
     sk.partials = static_cast<float *>(workspace);
-    sk.flags = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
-                                            HGEMM_STREAMK_MAX_GRID * int64_t(SK_SLOT) * 4);
-    {
-        uint32_t *flags = sk.flags;
-        int n = static_cast<int>(G);
-        void *args[] = {&flags, &n};
-        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sk_clear_flags),
-                                             dim3(static_cast<unsigned>((G + 255) / 256)),
-                                             dim3(256), args, 0, stream);
-        if (e != hipSuccess) return e;
-    }
+    sk.steps = (p.K + BK - 1) / BK;
+    sk.dp_tiles = tiles / G * G;
+    sk.iters = (tiles - sk.dp_tiles) * sk.steps;
+    sk.groups = sk.iters < G ? sk.iters : G;
+    const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
+    if (grid == 0) return hipSuccess;
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)
-        return bf ? launch_sk_layout<BF16, OUT_F32>(p, a, sk, G, stream)
-                  : launch_sk_layout<F16, OUT_F32>(p, a, sk, G, stream);
-    return bf ? launch_sk_layout<BF16, OUT_BF16>(p, a, sk, G, stream)
-              : launch_sk_layout<F16, OUT_F16>(p, a, sk, G, stream);
+        return bf ? launch_sk_layout<BF16, OUT_F32>(p, a, sk, grid, stream)
+                  : launch_sk_layout<F16, OUT_F32>(p, a, sk, grid, stream);
+    return bf ? launch_sk_layout<BF16, OUT_BF16>(p, a, sk, grid, stream)
+              : launch_sk_layout<F16, OUT_F16>(p, a, sk, grid, stream);
 }
 
 }  // namespace libgemm

@@ -244,18 +244,21 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
  * gemm_bf16 / gemm_f16 plus a device workspace, and compute the same product.
  * With at least gemm_workspace_size() bytes, a problem on the general kernel
  * (operands that are not 16-byte aligned) whose 256 x 256 tiles leave the
- * last wave of workgroups partly idle (tiles not a multiple of 256, fewer
- * than 1024 of them) runs on the stream-K schedule ("CUDA GEMM 矩阵乘法优化
- * 指南", blog.zhenwei.site, section 12.5, persistent kernels and Stream-K):
- * the (tile, k-step) iterations are split evenly over one workgroup per
- * compute unit, a tile cut between workgroups being finished by the last of
- * them, which adds the others' partial sums in a fixed order.  Results are
- * deterministic run to run; they may differ in rounding from gemm_bf16 (the
- * partial sums are grouped differently), within the same accuracy.  Every
- * other call ignores the workspace and behaves exactly like gemm_bf16.
+ * last wave of workgroups partly idle runs on the stream-K schedule ("CUDA
+ * GEMM 矩阵乘法优化指南", blog.zhenwei.site, section 12.5, persistent kernels
+ * and Stream-K): the tiles that fill whole waves of one workgroup per compute
+ * unit are computed whole, and the k steps of the remaining tiles are split
+ * evenly over the workgroups; the pieces of a tile that was cut are written to
+ * the workspace and added, in a fixed order, by a second kernel on the same
+ * stream, which also applies the epilogue.  It is chosen when the steps saved
+ * in the last wave outweigh that exchange (about four k steps of one tile).
+ * Results are deterministic run to run; they may differ in rounding from
+ * gemm_bf16 (the partial sums are grouped differently), within the same
+ * accuracy.  Every other call ignores the workspace and behaves exactly like
+ * gemm_bf16.
  *   workspace        device memory, 256-byte aligned, not overlapping A, B or
  *                    C; owned by the caller and clobbered by the call (it
- *                    holds partial tiles and flags while the kernels run on
+ *                    holds partial tiles while the kernels run on
  *                    `stream`; calls that share a workspace must be ordered
  *                    on one stream).  NULL only with workspace_bytes = 0.
  *   workspace_bytes  its size; smaller than gemm_workspace_size() (0

@@ -316,8 +316,8 @@ WS = 5 * GB  # fake, 256-byte aligned workspace address
 
 
 def test_workspace_size(lib):
-    # one 256 x 256 fp32 partial tile and one flag per workgroup, 256 workgroups
-    assert lib.workspace_size() == 256 * 256 * 256 * 4 + 256 * 4
+    # two 256 x 256 fp32 partial tiles per workgroup, 256 workgroups
+    assert lib.workspace_size() == 2 * 256 * 256 * 256 * 4
 
 
 def kname_ws(lib, dt, M, N, K, ws=WS, nbytes=None, **kw):
@@ -326,8 +326,10 @@ def kname_ws(lib, dt, M, N, K, ws=WS, nbytes=None, **kw):
     ldb = kw.pop("ldb", N if ob == 0 else K)
     ldc = kw.pop("ldc", N if oc == 0 else M)
     nbytes = lib.workspace_size() if nbytes is None else nbytes
+    batch = kw.pop("batch", 1)
+    strides = (M * K, K * N, M * N) if batch > 1 else (0, 0, 0)
     return lib.kernel_name(dt, M, N, K, kw.pop("alpha", 1.0), GB, lda, oa, 2 * GB, ldb, ob, 0.0,
-                           3 * GB, ldc, oc, 0, kw.pop("batch", 1), 0, 0, 0, workspace=ws,
+                           3 * GB, ldc, oc, 0, batch, *strides, workspace=ws,
                            workspace_bytes=nbytes)
 
 
@@ -341,6 +343,10 @@ def test_streamk_kernel_choice(lib, clean_env):
     # whole waves (256 tiles), too little work, or the aligned fast path
     assert kname_ws(lib, "bf16", 4095, 4095, 1001) == "hgemm_mfma"
     assert kname_ws(lib, "bf16", 300, 290, 131) == "hgemm_mfma"
+    # 500 tiles: the last wave (244 tiles) is nearly full, the exchange would cost more
+    assert kname_ws(lib, "bf16", 5119, 6399, 1001) == "hgemm_mfma"
+    # 65 batches of 4 tiles: 256 tiles whole, 4 cut over the grid
+    assert kname_ws(lib, "bf16", 300, 290, 1001, batch=65) == "hgemm_mfma_streamk"
     assert kname_ws(lib, "bf16", 4096, 4352, 1024) == "hgemm_mfma_dma"
     # fp32 has no workspace entry point; K = 0 scales C
     assert kname_ws(lib, "f32", 4095, 4097, 1001) is None

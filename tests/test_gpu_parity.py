@@ -652,8 +652,7 @@ def test_f8_truncation_worst_case_within_bound():
 
 # Shapes on the general kernel (leading dimensions not multiples of 8
 # elements) whose tiles do not fill whole waves of 256 workgroups: few tiles
-# with a long K (every tile cut across many workgroups), and the 272-tile
-# problem with one tile per workgroup and a little more.
+# with a long K, every tile cut across many workgroups.
 SK_SHAPES = [(300, 290, 8193), (513, 770, 3001), (1000, 1030, 1701)]
 
 
@@ -684,6 +683,14 @@ def test_streamk_integers_bit_exact(dt):
     res, _ = check(p, kernel="hgemm_mfma_streamk", host=_int_host(p, np.random.default_rng(82)),
                    use_workspace=True)
     assert res.max_err == 0.0 and res.max_ulp == 0
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_streamk_whole_waves_and_cut_tail(dt):
+    # 65 batches of 2 x 2 tiles: 256 tiles computed whole, 4 cut over the
+    # grid (16 pieces each); beta = 0.5, so the fix-up also reads C
+    check(P(f"streamk-dp-{dt}", dt, 300, 290, 1001, beta=0.5, batch=65),
+          kernel="hgemm_mfma_streamk", seed=84, use_workspace=True, repeat=2)
 
 
 def test_streamk_workspace_too_small_is_the_plain_call():
