@@ -27,15 +27,34 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "scale.hip", "sgemm_valu.hip", "sgemm_mfma.hip", "sgemm_splitk.hip", "hgemm_mfma.hip", "hgemm_mfma_dma.hip",
            "hgemm_splitk.hip", "gemm_skinny.hip", "f8gemm_mfma.hip"]
+# Sources compiled once per part (-DLIBGEMM_HGEMM_PART=k, one object each), so
+# that their many kernel instantiations build in parallel.
+PARTS = {"hgemm_mfma.hip": 4}
+
+
+def units():
+    """(source, part or None) for every object of the library."""
+    out = []
+    for s in SOURCES:
+        n = PARTS.get(s)
+        out += [(s, None)] if n is None else [(s, k) for k in range(n)]
+    return out
+
+
+def object_path(src: str, part=None) -> str:
+    suffix = "" if part is None else f".p{part}"
+    return os.path.join(BUILD_DIR, os.path.basename(src) + suffix + ".o")
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str, verbose: bool):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, verbose: bool, part=None):
+    obj = object_path(src, part)
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if part is not None:
+        cmd.insert(1, f"-DLIBGEMM_HGEMM_PART={part}")
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
         cmd.append("-Rpass-analysis=kernel-resource-usage")
@@ -68,7 +87,9 @@ def _resource_report(logs):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        results = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        # longest compilations first, so they do not start last
+        todo = sorted(units(), key=lambda u: u[0] not in PARTS)
+        results = list(ex.map(lambda u: _compile(u[0], verbose, u[1]), todo))
     objs = [o for o, _ in results]
     lines, spills = _resource_report([log for _, log in results])
     with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:

@@ -32,10 +32,45 @@
 //
 // The epilogue computes alpha*acc + beta*C_old in fp32 (C_old is not read
 // when beta == 0) and rounds to the output type to nearest-even.
+//
+// The file is compiled once per (input type, order of A) with
+// LIBGEMM_HGEMM_PART = 0..3 set, each object holding that part's kernels and
+// their launchers, so the parts build in parallel; part 0 also holds the
+// host entry points.  Without the macro one object holds everything.
 #include "gemm_problem.hpp"
 #include "tile_schedule.hpp"
 
+#ifndef LIBGEMM_HGEMM_PART
+#define LIBGEMM_HGEMM_PART -1
+#endif
+#define LIBGEMM_HGEMM_HAS(part) (LIBGEMM_HGEMM_PART < 0 || LIBGEMM_HGEMM_PART == (part))
+
 namespace libgemm {
+
+// Arguments of the kernels, shared by the objects of the parts (named, so
+// that the launchers of one part can be called from another).
+struct HgemmArgs {
+    int64_t M, N, K;
+    float alpha, beta;
+    const uint16_t *A;
+    const uint16_t *B;
+    void *C;
+    int64_t lda, ldb, ldc;
+    int64_t sA, sB, sC;
+    TileGrid grid;
+    int vec_a, vec_b;
+    int ubuf_a, ubuf_b;  // the operand's span fits a raw buffer (unaligned vector path)
+    Epilogue epi;
+};
+
+struct StreamK {
+    float *partials;    // 2 * Gs slots of 256 x 256 floats
+    int64_t steps;      // k steps per tile (S)
+    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
+    int64_t iters;      // W = (tiles - dp_tiles) * steps
+    int64_t groups;     // Gs = min(grid, W)
+};
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -53,19 +88,6 @@ static_assert(BM == BN, "both panels share one layout");
 
 constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2;
 
-struct HgemmArgs {
-    int64_t M, N, K;
-    float alpha, beta;
-    const uint16_t *A;
-    const uint16_t *B;
-    void *C;
-    int64_t lda, ldb, ldc;
-    int64_t sA, sB, sC;
-    TileGrid grid;
-    int vec_a, vec_b;
-    int ubuf_a, ubuf_b;  // the operand's span fits a raw buffer (unaligned vector path)
-    Epilogue epi;
-};
 
 struct BF16 {};
 struct F16 {};
@@ -520,13 +542,6 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_kernel(HgemmArgs p) {
 // not change from run to run) and applying the epilogue.  The kernels
 // exchange data only across the launch boundary on one stream: no workgroup
 // waits for another.
-struct StreamK {
-    float *partials;    // 2 * Gs slots of 256 x 256 floats
-    int64_t steps;      // k steps per tile (S)
-    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
-    int64_t iters;      // W = (tiles - dp_tiles) * steps
-    int64_t groups;     // Gs = min(grid, W)
-};
 
 constexpr int SK_SLOT = BM * BN;  // floats per partial tile
 
@@ -654,6 +669,8 @@ __global__ __launch_bounds__(THREADS) void hgemm_streamk_fixup(HgemmArgs p, Stre
     store_regs<OUT, 4>(p, t, blk >> 2, blk & 3, 4 * q, sum);
 }
 
+// Launchers of one part: input type T, order of A (AK).  The kernels of a
+// part are instantiated in its object only.
 template <class T, int OUT, bool AK, bool BKM>
 hipError_t launch(HgemmArgs &a, hipStream_t stream) {
     void *args[] = {&a};
@@ -664,17 +681,80 @@ hipError_t launch(HgemmArgs &a, hipStream_t stream) {
                            stream);
 }
 
-template <class T, int OUT>
-hipError_t launch_layout(const Problem &p, HgemmArgs &a, hipStream_t stream) {
-    if (p.a_kmajor)
-        return p.b_kmajor ? launch<T, OUT, true, true>(a, stream)
-                          : launch<T, OUT, true, false>(a, stream);
-    return p.b_kmajor ? launch<T, OUT, false, true>(a, stream)
-                      : launch<T, OUT, false, false>(a, stream);
+template <class T, int OUT, bool AK>
+hipError_t launch_b(const Problem &p, HgemmArgs &a, hipStream_t stream) {
+    return p.b_kmajor ? launch<T, OUT, AK, true>(a, stream) : launch<T, OUT, AK, false>(a, stream);
+}
+
+template <class T, int OWN, bool AK>
+hipError_t launch_part(const Problem &p, HgemmArgs &a, hipStream_t stream) {
+    return p.out == Elem::F32 ? launch_b<T, OUT_F32, AK>(p, a, stream)
+                              : launch_b<T, OWN, AK>(p, a, stream);
+}
+
+// Only the raw-buffer variant exists on this schedule (hgemm_streamk_eligible
+// requires operand spans that fit a raw buffer).
+template <class T, int OUT, bool AK, bool BKM>
+hipError_t launch_sk(HgemmArgs &a, StreamK &sk, int64_t grid, hipStream_t stream) {
+    void *args[] = {&a, &sk};
+    const void *k = reinterpret_cast<const void *>(&hgemm_streamk_kernel<T, OUT, AK, BKM, true>);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(grid)), dim3(THREADS), args, 0, stream);
+}
+
+template <class T, int OUT, bool AK>
+hipError_t launch_sk_b(const Problem &p, HgemmArgs &a, StreamK &sk, int64_t grid,
+                       hipStream_t stream) {
+    const hipError_t e = p.b_kmajor ? launch_sk<T, OUT, AK, true>(a, sk, grid, stream)
+                                    : launch_sk<T, OUT, AK, false>(a, sk, grid, stream);
+    if (e != hipSuccess || sk.iters == 0) return e;
+    void *args[] = {&a, &sk};
+    const int64_t cut = a.grid.count() - sk.dp_tiles;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&hgemm_streamk_fixup<OUT>),
+                           dim3(static_cast<unsigned>(cut * 64)), dim3(THREADS), args, 0, stream);
+}
+
+template <class T, int OWN, bool AK>
+hipError_t launch_sk_part(const Problem &p, HgemmArgs &a, StreamK &sk, int64_t grid,
+                          hipStream_t stream) {
+    return p.out == Elem::F32 ? launch_sk_b<T, OUT_F32, AK>(p, a, sk, grid, stream)
+                              : launch_sk_b<T, OWN, AK>(p, a, sk, grid, stream);
 }
 
 }  // namespace
 
+// Part k = (input type, order of A): 0 bf16 with A along M, 1 bf16 with A
+// along K, 2 and 3 the same for fp16.
+template <int PART>
+hipError_t hgemm_part(const Problem &p, HgemmArgs &a, hipStream_t stream);
+template <int PART>
+hipError_t hgemm_streamk_part(const Problem &p, HgemmArgs &a, StreamK &sk, int64_t grid,
+                              hipStream_t stream);
+
+#define LIBGEMM_HGEMM_PART_DEF(part, T, OWN, AK)                                              \
+    template <>                                                                                \
+    hipError_t hgemm_part<part>(const Problem &p, HgemmArgs &a, hipStream_t stream) {          \
+        return launch_part<T, OWN, AK>(p, a, stream);                                          \
+    }                                                                                          \
+    template <>                                                                                \
+    hipError_t hgemm_streamk_part<part>(const Problem &p, HgemmArgs &a, StreamK &sk,           \
+                                        int64_t grid, hipStream_t stream) {                    \
+        return launch_sk_part<T, OWN, AK>(p, a, sk, grid, stream);                             \
+    }
+
+#if LIBGEMM_HGEMM_HAS(0)
+LIBGEMM_HGEMM_PART_DEF(0, BF16, OUT_BF16, false)
+#endif
+#if LIBGEMM_HGEMM_HAS(1)
+LIBGEMM_HGEMM_PART_DEF(1, BF16, OUT_BF16, true)
+#endif
+#if LIBGEMM_HGEMM_HAS(2)
+LIBGEMM_HGEMM_PART_DEF(2, F16, OUT_F16, false)
+#endif
+#if LIBGEMM_HGEMM_HAS(3)
+LIBGEMM_HGEMM_PART_DEF(3, F16, OUT_F16, true)
+#endif
+
+#if LIBGEMM_HGEMM_PART <= 0
 namespace {
 
 HgemmArgs make_args(const Problem &p, int32_t xcds) {
@@ -705,32 +785,6 @@ HgemmArgs make_args(const Problem &p, int32_t xcds) {
     return a;
 }
 
-// Only the raw-buffer variant exists on this schedule (hgemm_streamk_eligible
-// requires operand spans that fit a raw buffer).
-template <class T, int OUT, bool AK, bool BKM>
-hipError_t launch_sk(HgemmArgs &a, StreamK &sk, int64_t grid, hipStream_t stream) {
-    void *args[] = {&a, &sk};
-    const void *k = reinterpret_cast<const void *>(&hgemm_streamk_kernel<T, OUT, AK, BKM, true>);
-    return hipLaunchKernel(k, dim3(static_cast<unsigned>(grid)), dim3(THREADS), args, 0, stream);
-}
-
-template <class T, int OUT>
-hipError_t launch_sk_layout(const Problem &p, HgemmArgs &a, StreamK &sk, int64_t grid,
-                            hipStream_t stream) {
-    hipError_t e;
-    if (p.a_kmajor)
-        e = p.b_kmajor ? launch_sk<T, OUT, true, true>(a, sk, grid, stream)
-                       : launch_sk<T, OUT, true, false>(a, sk, grid, stream);
-    else
-        e = p.b_kmajor ? launch_sk<T, OUT, false, true>(a, sk, grid, stream)
-                       : launch_sk<T, OUT, false, false>(a, sk, grid, stream);
-    if (e != hipSuccess || sk.iters == 0) return e;
-    void *args[] = {&a, &sk};
-    const int64_t cut = a.grid.count() - sk.dp_tiles;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&hgemm_streamk_fixup<OUT>),
-                           dim3(static_cast<unsigned>(cut * 64)), dim3(THREADS), args, 0, stream);
-}
-
 // Workgroups of the stream-K grid: one per compute unit of the current
 // device, at most HGEMM_STREAMK_MAX_GRID (the workspace is sized for that).
 int64_t streamk_grid() {
@@ -751,12 +805,13 @@ constexpr int64_t SK_EXCHANGE_STEPS = 4;
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
     HgemmArgs a = make_args(p, 8);
     if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool bf = p.in == Elem::BF16;
-    if (p.out == Elem::F32)
-        return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)
-                  : launch_layout<F16, OUT_F32>(p, a, stream);
-    return bf ? launch_layout<BF16, OUT_BF16>(p, a, stream)
-              : launch_layout<F16, OUT_F16>(p, a, stream);
+    const int part = (p.in == Elem::BF16 ? 0 : 2) + (p.a_kmajor ? 1 : 0);
+    switch (part) {
+    case 0: return hgemm_part<0>(p, a, stream);
+    case 1: return hgemm_part<1>(p, a, stream);
+    case 2: return hgemm_part<2>(p, a, stream);
+    default: return hgemm_part<3>(p, a, stream);
+    }
 }
 
 // Stream-K pays off when the tiles leave the last wave of workgroups (one
@@ -788,12 +843,15 @@ hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t s
     sk.groups = sk.iters < G ? sk.iters : G;
     const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
     if (grid == 0) return hipSuccess;
-    const bool bf = p.in == Elem::BF16;
-    if (p.out == Elem::F32)
-        return bf ? launch_sk_layout<BF16, OUT_F32>(p, a, sk, grid, stream)
-                  : launch_sk_layout<F16, OUT_F32>(p, a, sk, grid, stream);
-    return bf ? launch_sk_layout<BF16, OUT_BF16>(p, a, sk, grid, stream)
-              : launch_sk_layout<F16, OUT_F16>(p, a, sk, grid, stream);
+    const int part = (p.in == Elem::BF16 ? 0 : 2) + (p.a_kmajor ? 1 : 0);
+    switch (part) {
+    case 0: return hgemm_streamk_part<0>(p, a, sk, grid, stream);
+    case 1: return hgemm_streamk_part<1>(p, a, sk, grid, stream);
+    case 2: return hgemm_streamk_part<2>(p, a, sk, grid, stream);
+    default: return hgemm_streamk_part<3>(p, a, sk, grid, stream);
+    }
 }
+
+#endif  // LIBGEMM_HGEMM_PART <= 0
 
 }  // namespace libgemm
