@@ -253,6 +253,65 @@ __device__ inline void finish_panel(const UBuf &u, const uint16_t *X, int64_t ld
     }
 }
 
+// Interior steps.  A panel step is interior when every chunk lies inside the
+// matrix and the 20-byte window of its two loads inside the buffer: all 256
+// rows exist, the 64 k exist, and where the last row (KMAJOR) or the last k
+// (otherwise) is touched, two more elements follow it (a chunk's window ends
+// at most 10 elements past its start).  Such a step needs no bounds, masks or
+// tail handling: each lane keeps one byte offset per tile (chunk 0 at k = 0,
+// from the buffer base) and adds the uniform rest.
+template <bool KMAJOR>
+__device__ inline bool panel_interior(int64_t rows, int64_t r0, int64_t k0, int64_t K) {
+    if (r0 + BM > rows || k0 + BK > K) return false;
+    return KMAJOR ? (r0 + BM < rows || k0 + BK + 2 <= K) : (k0 + BK < K || r0 + BM + 2 <= rows);
+}
+
+// The lane's byte offset of chunk 0 at k = 0 (meaningful where the panel is
+// interior; it may wrap elsewhere and is then not used).
+template <bool KMAJOR>
+__device__ inline uint32_t lane_offset(const UBuf &u, int64_t ld, int64_t r0, int tid) {
+    const int64_t e = KMAJOR ? (r0 + (tid >> 3)) * ld + 8 * (tid & 7)
+                             : 8 * (tid >> 5) * ld + r0 + 8 * (tid & 31);
+    return u.mis + 2 * static_cast<uint32_t>(e);
+}
+
+// KMAJOR: chunk i sits 32*i rows below chunk 0, and the step adds k0, both
+// multiples of four bytes, so the dword-aligned offset splits into the lane's
+// constant part (voffset) and a uniform part (soffset), and the shift is the
+// lane's own.  Otherwise chunk i is i rows of k below chunk 0: the uniform
+// part can change the offset's alignment and is added per chunk.
+template <bool KMAJOR>
+__device__ inline void issue_panel_fast(const UBuf &u, uint32_t lane, int64_t ld, int64_t k0,
+                                        Raw8 raw[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t voff, soff;
+        if (KMAJOR) {
+            voff = lane & ~3u;
+            soff = static_cast<uint32_t>(2 * k0 + 64 * ld * i);
+        } else {
+            voff = (lane + static_cast<uint32_t>(2 * (k0 + i) * ld)) & ~3u;
+            soff = 0;
+        }
+        raw[i].lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(u.rs, voff, soff, 0));
+        raw[i].hi = __builtin_amdgcn_raw_buffer_load_b32(u.rs, voff + 16, soff, 0);
+    }
+}
+
+template <bool KMAJOR>
+__device__ inline void finish_panel_fast(uint32_t lane, int64_t ld, int64_t k0, const Raw8 raw[8],
+                                         u32x4 v[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        // v_alignbyte shifts by the low two bits of its third operand: 0 or 2
+        const uint32_t sh = KMAJOR ? lane : lane + static_cast<uint32_t>(2 * (k0 + i) * ld);
+        v[i][0] = __builtin_amdgcn_alignbyte(raw[i].lo[1], raw[i].lo[0], sh);
+        v[i][1] = __builtin_amdgcn_alignbyte(raw[i].lo[2], raw[i].lo[1], sh);
+        v[i][2] = __builtin_amdgcn_alignbyte(raw[i].lo[3], raw[i].lo[2], sh);
+        v[i][3] = __builtin_amdgcn_alignbyte(raw[i].hi, raw[i].lo[3], sh);
+    }
+}
+
 template <bool KMAJOR>
 __device__ inline void load_panel(const uint16_t *X, int64_t ld, int64_t rows, int64_t r0,
                                   int64_t k0, int64_t K, bool vec, int tid, u32x4 v[8]) {
@@ -350,11 +409,24 @@ __device__ __forceinline__ void tile_steps(const HgemmArgs &p, u32x4 (*smem)[2][
     const UBuf ua = make_ubuf(A, UB ? span_a : 0), ub = make_ubuf(B, UB ? span_b : 0);
     u32x4 va[8], vb[8];
     Raw8 ra[8], rb[8];
+    const uint32_t lane_a = UB ? lane_offset<A_KMAJOR>(ua, p.lda, m0, tid) : 0u;
+    const uint32_t lane_b = UB ? lane_offset<B_KMAJOR>(ub, p.ldb, n0, tid) : 0u;
+    // whether the panels of the step starting at k are interior (uniform)
+    auto interior = [&](int64_t k) {
+        return panel_interior<A_KMAJOR>(p.M, m0, k, p.K) && panel_interior<B_KMAJOR>(p.N, n0, k, p.K);
+    };
     if (UB) {
-        issue_panel<A_KMAJOR>(ua, p.lda, p.M, m0, kb * BK, p.K, tid, ra);
-        issue_panel<B_KMAJOR>(ub, p.ldb, p.N, n0, kb * BK, p.K, tid, rb);
-        finish_panel<A_KMAJOR>(ua, A, p.lda, p.M, m0, kb * BK, p.K, tid, ra, va);
-        finish_panel<B_KMAJOR>(ub, B, p.ldb, p.N, n0, kb * BK, p.K, tid, rb, vb);
+        if (interior(kb * BK)) {
+            issue_panel_fast<A_KMAJOR>(ua, lane_a, p.lda, kb * BK, ra);
+            issue_panel_fast<B_KMAJOR>(ub, lane_b, p.ldb, kb * BK, rb);
+            finish_panel_fast<A_KMAJOR>(lane_a, p.lda, kb * BK, ra, va);
+            finish_panel_fast<B_KMAJOR>(lane_b, p.ldb, kb * BK, rb, vb);
+        } else {
+            issue_panel<A_KMAJOR>(ua, p.lda, p.M, m0, kb * BK, p.K, tid, ra);
+            issue_panel<B_KMAJOR>(ub, p.ldb, p.N, n0, kb * BK, p.K, tid, rb);
+            finish_panel<A_KMAJOR>(ua, A, p.lda, p.M, m0, kb * BK, p.K, tid, ra, va);
+            finish_panel<B_KMAJOR>(ub, B, p.ldb, p.N, n0, kb * BK, p.K, tid, rb, vb);
+        }
     } else {
         load_panel<A_KMAJOR>(A, p.lda, p.M, m0, kb * BK, p.K, p.vec_a, tid, va);
         load_panel<B_KMAJOR>(B, p.ldb, p.N, n0, kb * BK, p.K, p.vec_b, tid, vb);
@@ -367,8 +439,12 @@ __device__ __forceinline__ void tile_steps(const HgemmArgs &p, u32x4 (*smem)[2][
         const int cur = (s - kb) & 1;
         const bool more = s + 1 < ke;
         const int64_t k0 = (s + 1) * BK;
+        const bool fast = UB && more && interior(k0);
         if (more) {
-            if (UB) {
+            if (fast) {
+                issue_panel_fast<A_KMAJOR>(ua, lane_a, p.lda, k0, ra);
+                issue_panel_fast<B_KMAJOR>(ub, lane_b, p.ldb, k0, rb);
+            } else if (UB) {
                 issue_panel<A_KMAJOR>(ua, p.lda, p.M, m0, k0, p.K, tid, ra);
                 issue_panel<B_KMAJOR>(ub, p.ldb, p.N, n0, k0, p.K, tid, rb);
             } else {
@@ -396,7 +472,10 @@ __device__ __forceinline__ void tile_steps(const HgemmArgs &p, u32x4 (*smem)[2][
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(a[i], b[j], acc[i][j]);
         }
         if (more) {
-            if (UB) {
+            if (fast) {
+                finish_panel_fast<A_KMAJOR>(lane_a, p.lda, k0, ra, va);
+                finish_panel_fast<B_KMAJOR>(lane_b, p.ldb, k0, rb, vb);
+            } else if (UB) {
                 finish_panel<A_KMAJOR>(ua, A, p.lda, p.M, m0, k0, p.K, tid, ra, va);
                 finish_panel<B_KMAJOR>(ub, B, p.ldb, p.N, n0, k0, p.K, tid, rb, vb);
             }
