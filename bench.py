@@ -52,7 +52,7 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "hgemm_mfma": "hgemm_mfma.hip", "hgemm_splitk": "hgemm_splitk.hip",
                  "sgemm_splitk": "sgemm_splitk.hip", "gemm_skinny": "gemm_skinny.hip",
                  "f8gemm_mfma_dma": "f8gemm_mfma.hip", "f8gemm_mfma": "f8gemm_mfma.hip",
-                 "hgemm_mfma_streamk": "hgemm_mfma.hip",
+                 "hgemm_mfma_streamk": "hgemm_mfma.hip", "hgemm_mfma_dma_streamk": "hgemm_mfma_dma.hip",
                  "scale": "scale.hip"}
 
 

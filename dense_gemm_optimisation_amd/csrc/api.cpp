@@ -80,6 +80,7 @@ enum class Kernel {
     F8Mfma,      // 8-bit floats, any shape and order
     F8Dma,       // 8-bit floats, K-contiguous aligned operands, direct loads
     HgemmStreamK,  // bf16/fp16 general kernel on the stream-K schedule (workspace)
+    HgemmDmaStreamK,  // bf16/fp16 direct-load kernel on the stream-K schedule (workspace)
 };
 
 const char *kernel_name(Kernel k) {
@@ -97,6 +98,7 @@ const char *kernel_name(Kernel k) {
     case Kernel::F8Mfma: return "f8gemm_mfma";
     case Kernel::F8Dma: return "f8gemm_mfma_dma";
     case Kernel::HgemmStreamK: return "hgemm_mfma_streamk";
+    case Kernel::HgemmDmaStreamK: return "hgemm_mfma_dma_streamk";
     }
     return "";
 }
@@ -136,7 +138,8 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::HgemmSplitk: return launch_hgemm_splitk(p, stream);
     case Kernel::F8Mfma: return launch_f8gemm(p, stream);
     case Kernel::F8Dma: return launch_f8gemm_dma(p, stream);
-    case Kernel::HgemmStreamK: return hipErrorInvalidValue;  // needs the workspace: run()
+    case Kernel::HgemmStreamK:
+    case Kernel::HgemmDmaStreamK: return hipErrorInvalidValue;  // need the workspace: run()
     }
     return hipErrorInvalidValue;
 }
@@ -238,8 +241,9 @@ gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K
     return GEMM_OK;
 }
 
-// With a workspace: its checks, and the switch of the general 16-bit kernel
-// to the stream-K schedule where that schedule applies.
+// With a workspace: its checks, and the switch of the 16-bit kernels (the
+// direct-load and the general one) to their stream-K schedule where it
+// applies.
 gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, int orderA,
                             int64_t lda, int orderB, int64_t ldb, int orderC, int64_t ldc,
                             int64_t strideA, int64_t strideB, int64_t strideC,
@@ -256,9 +260,11 @@ gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, i
         overlap(rw, range_of(B, span(K, N, orderB, ldb), p.batch, strideB, esz)) ||
         (bias != nullptr && overlap(rw, range_of(bias, N, p.batch, strideBias, esz))))
         return GEMM_ERR_INVALID_ARG;
-    if (k == Kernel::HgemmMfma && !force_general() &&
-        bytes >= static_cast<size_t>(hgemm_streamk_workspace_bytes()) && hgemm_streamk_eligible(p))
+    const bool room = bytes >= static_cast<size_t>(hgemm_streamk_workspace_bytes());
+    if (k == Kernel::HgemmMfma && !force_general() && room && hgemm_streamk_eligible(p))
         k = Kernel::HgemmStreamK;
+    else if (k == Kernel::HgemmDma && room && hgemm_dma_streamk_eligible(p))
+        k = Kernel::HgemmDmaStreamK;
     return GEMM_OK;
 }
 
@@ -276,8 +282,9 @@ gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K,
         st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
                            strideC, bias, strideBias, A, B, C, workspace, workspace_bytes, k);
     if (st != GEMM_OK || k == Kernel::None) return st;
-    const hipError_t err = k == Kernel::HgemmStreamK ? launch_hgemm_streamk(p, workspace, stream)
-                                                     : launch(k, p, stream);
+    const hipError_t err = k == Kernel::HgemmStreamK      ? launch_hgemm_streamk(p, workspace, stream)
+                           : k == Kernel::HgemmDmaStreamK ? launch_hgemm_dma_streamk(p, workspace, stream)
+                                                          : launch(k, p, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -66,6 +66,20 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on 
 // (two fp32 partial 256 x 256 tiles per workgroup); only where
 // hgemm_streamk_eligible() holds.
 constexpr int64_t HGEMM_STREAMK_MAX_GRID = 256;
+// Workgroups that share the k steps of a stream-K schedule's `cut` tiles of
+// `steps` k steps each, out of G: cutting each tile into s pieces costs
+// steps/s k steps of time and cut*s partial tiles written and read back;
+// with one k step worth `ratio` partial tiles (the kernel's step time over
+// the time to move one 256 x 256 fp32 partial tile through HBM twice),
+// s = sqrt(steps*ratio/cut) balances the two.
+inline int64_t streamk_groups(int64_t G, int64_t cut, int64_t steps, double ratio) {
+    const int64_t W = cut * steps;
+    int64_t s = static_cast<int64_t>(__builtin_sqrt(double(steps) * ratio / double(cut)) + 0.5);
+    s = s < 1 ? 1 : (s > steps ? steps : s);
+    int64_t g = cut * s;
+    g = g < G ? g : G;
+    return g < W ? g : W;
+}
 constexpr int64_t hgemm_streamk_workspace_bytes() {
     return 2 * HGEMM_STREAMK_MAX_GRID * 256 * 256 * 4;
 }
@@ -75,6 +89,11 @@ hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t s
 // hgemm_dma_eligible() holds (aligned operands, extents multiple of 8).
 bool hgemm_dma_eligible(const Problem &p);
 hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream);
+// Its stream-K schedule, through the same workspace as the general kernel's
+// (hgemm_streamk_workspace_bytes()); only where hgemm_dma_streamk_eligible()
+// holds.
+bool hgemm_dma_streamk_eligible(const Problem &p);
+hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream);
 // bf16/fp16 split-K inside a workgroup, for problems with few output tiles
 // and a long K (hgemm_splitk_eligible()).
 bool hgemm_splitk_eligible(const Problem &p);

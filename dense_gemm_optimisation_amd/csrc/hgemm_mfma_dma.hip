@@ -40,6 +40,8 @@
 namespace libgemm {
 namespace {
 
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
 using namespace dmatile;
 
 struct BF16 {};
@@ -203,6 +205,336 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
                                 reinterpret_cast<LDS float *>(stage_free) + wave * 32 * WTN);
 }
 
+// The same steps and epilogue as functions, for the stream-K kernel (the
+// one-tile kernel above keeps them inline, where they compile to slightly
+// faster code).
+// k steps [kb, ke) (BK each) of tile t into acc through the LDS ring at
+// `lds`; returns the ring buffer the last step used (the epilogue stages C in
+// the others).  On return every wave has passed the last barrier.
+template <class T, bool A_KMAJOR, bool B_KMAJOR, int WAVES_M, int WAVES_N, int BK, int STAGES>
+__device__ __forceinline__ int dma_tile_steps(const DmaArgs &p, LDS char *lds, const TileCoord &t,
+                                              int64_t kb, int64_t ke,
+                                              f32x16 (&acc)[BM / WAVES_M / 32][BN / WAVES_N / 32]) {
+    constexpr int WAVES = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int KK = BK / 16;  // matrix-instruction k steps per stage
+    // LDS read instructions per k step: one per K-contiguous fragment, two
+    // transpose reads per M/N-contiguous one
+    constexpr int NREAD = FM * (A_KMAJOR ? 1 : 2) + FN * (B_KMAJOR ? 1 : 2);
+    using OpA = Operand<A_KMAJOR, WAVES, BK>;
+    using OpB = Operand<B_KMAJOR, WAVES, BK>;
+    constexpr int PANEL = OpA::PANEL;
+    constexpr int STAGE = 2 * PANEL;
+    constexpr int PER_STAGE = OpA::PER_WAVE + OpB::PER_WAVE;  // direct loads per wave per stage
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The wave index is uniform across the wave; saying so keeps the LDS
+    // destination of the direct loads (M0) in a scalar register.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+
+    OpA opa;
+    OpB opb;
+    const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
+    const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
+    opa.init(p.A + t.batch * p.sA, p.lda, p.M, m0, span_a, wave, lane);
+    opb.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, span_b, wave, lane);
+
+    const int64_t steps = ke - kb;
+
+    // Prologue: fill every stage buffer, then wait for the first.
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) {
+        if (st < steps) {
+            opa.issue(lds + st * STAGE, kb + st, p.K, wave);
+            opb.issue(lds + st * STAGE + PANEL, kb + st, p.K, wave);
+        }
+    }
+    wait_stages<PER_STAGE, STAGES>(int(steps - 1 < STAGES - 1 ? steps - 1 : STAGES - 1));
+    __syncthreads();
+
+    u32x4 fa[2][FM], fb[2][FN];
+    auto read = [&](int buf, int kk, int slot) {
+        const LDS char *sa = lds + buf * STAGE;
+        const LDS char *sb = sa + PANEL;
+        // in the order the matrix instructions consume them: all of B's
+        // fragments are used by the first row of instructions
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[slot][j] = opb.frag(sb, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[slot][i] = opa.frag(sa, wm * WTM + i * 32, kk, lane);
+    };
+    read(0, 0, 0);
+
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<T>(fb[slot][j], fa[slot][i], acc[i][j]);
+    };
+
+    // Every stage but the last.  Its first KK - 1 k16 steps read the next
+    // step's fragments while computing.  Its last step waits for stage s + 1
+    // (this wave's loads, then every wave's through the barrier, which also
+    // says every wave is done reading this stage's buffer), reads stage
+    // s + 1's first fragments, and runs its matrix instructions with the
+    // refill of this buffer (stage s + STAGES) spread between them, so a load
+    // that waits for the memory pipeline does not hold back the matrix core.
+    // The last stage is peeled off so that no branch joins the code after the
+    // barrier: the LDS counter waits stay exact there.
+    int buf = 0;
+    const int64_t main_steps = steps - 1;
+    for (int64_t s = 0; s < main_steps; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < KK - 1; ++kk) {
+            read(buf, kk + 1, (kk & 1) ^ 1);
+            mfmas(kk & 1);
+            interleave_reads<NREAD, FM * FN>();
+        }
+        constexpr int LAST = (KK - 1) & 1;
+        const int64_t later = steps - 2 - s;
+        wait_stages<PER_STAGE, STAGES>(int(later < STAGES - 2 ? later : STAGES - 2));
+        wait_lgkmcnt0();
+        __syncthreads();
+        const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
+        read(nbuf, 0, LAST ^ 1);
+        const int64_t refill = s + STAGES;
+        const bool do_refill = refill < steps;
+        const u32x4 ra = opa.rsrc(kb + refill), rb = opb.rsrc(kb + refill);
+        const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + buf * STAGE));
+        const uint32_t lb = la + PANEL;
+        const int64_t kleft = p.K - (kb + refill) * BK;
+        // one direct load after each matrix instruction
+        static_assert(PER_STAGE <= FM * FN, "loads per instruction");
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j] = mfma32<T>(fb[LAST][j], fa[LAST][i], acc[i][j]);
+                const int q = i * FN + j;
+                if (do_refill) {
+                    if (q < OpA::PER_WAVE) opa.load(ra, la, q, kleft, wave);
+                    else if (q < PER_STAGE) opb.load(rb, lb, q - OpA::PER_WAVE, kleft, wave);
+                }
+            }
+        buf = nbuf;
+    }
+    // The last stage.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        if (kk < KK - 1) read(buf, kk + 1, (kk & 1) ^ 1);
+        mfmas(kk & 1);
+        interleave_reads<NREAD, FM * FN>();
+    }
+    return buf;
+}
+
+// C is staged in stage buffers the last stage does not use: every wave
+// finished reading them before the last barrier, and no load targets them
+// any more, so no further barrier is needed.  Staging takes NEED consecutive
+// buffers: the next one when one suffices, else the first NEED or the NEED
+// after them, whichever excludes the last stage's.
+template <int OUT, int WAVES_M, int WAVES_N, int BK, int STAGES>
+__device__ __forceinline__ void dma_tile_store(const DmaArgs &p, LDS char *lds, const TileCoord &t,
+                                               int buf,
+                                               const f32x16 (&acc)[BM / WAVES_M / 32][BN / WAVES_N / 32]) {
+    constexpr int WAVES = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int STAGE = 2 * Operand<true, WAVES, BK>::PANEL;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    constexpr int NEED = (WAVES * 32 * WTN * 4 + STAGE - 1) / STAGE;
+    static_assert(NEED == 1 || 2 * NEED <= STAGES, "epilogue staging fits beside the last stage");
+    const int free0 = NEED == 1 ? (buf + 1 == STAGES ? 0 : buf + 1) : (buf >= NEED ? 0 : NEED);
+    LDS char *stage_free = lds + free0 * STAGE;
+    store_tile_lds<OUT, FM, FN>(p, acc, t.batch, t.tm * BM + wm * WTM, t.tn * BN + wn * WTN, lane,
+                                reinterpret_cast<LDS float *>(stage_free) + wave * 32 * WTN);
+}
+
+// Stream-K schedule of the fast path (section 12.5 of "CUDA GEMM 矩阵乘法优化
+// 指南", blog.zhenwei.site, persistent kernels and Stream-K), the same split
+// as the general kernel's: one workgroup per compute unit (G); the tiles
+// filling whole waves of G are computed whole, tile w + n*G by workgroup w;
+// the (tile, k step) iterations of the other tiles are split evenly over
+// Gs = min(G, iterations) workgroups; a piece covering a whole tile is stored
+// through the epilogue, any other is written to the workgroup's slot 2w (the
+// piece holding its last iteration) or 2w + 1 (its first), and
+// hgemm_dma_streamk_fixup adds the pieces of each cut tile in increasing
+// workgroup order and applies the epilogue.
+struct DmaStreamK {
+    float *partials;    // 2 * Gs slots of 256 x 256 floats
+    int64_t steps;      // k steps per tile (S)
+    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
+    int64_t iters;      // W = (tiles - dp_tiles) * steps
+    int64_t groups;     // Gs = min(grid, W)
+};
+
+constexpr int SK_SLOT = BM * BN;  // floats per partial tile
+
+// Slot `slot` as a raw buffer.  Register quad q of block (i, j) of thread
+// tid is the 16 bytes at ((i*FN + j)*4 + q) * threads * 16 + tid * 16.
+__device__ inline __amdgpu_buffer_rsrc_t sk_slot(const DmaStreamK &sk, int64_t slot) {
+    return __builtin_amdgcn_make_buffer_rsrc(sk.partials + slot * SK_SLOT, 0, SK_SLOT * 4,
+                                             0x00020000);
+}
+
+template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, int WAVES_M, int WAVES_N, int BK,
+          int STAGES>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_streamk_kernel(DmaArgs p,
+                                                                                   DmaStreamK sk) {
+    constexpr int FM = BM / WAVES_M / 32, FN = BN / WAVES_N / 32;
+    constexpr int THREADS = WAVES_M * WAVES_N * 64;
+    constexpr int STAGE = 2 * Operand<A_KMAJOR, WAVES_M * WAVES_N, BK>::PANEL;
+    static_assert(STAGES * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(FM * FN * 4 * THREADS * 16 == SK_SLOT * 4, "a slot holds one tile");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+    LDS char *lds = (LDS char *)smem;
+
+    // logical workgroup: the hardware id regrouped per XCD, so that the
+    // workgroups of one die take consecutive tiles and ranges
+    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t w = uniform(xcd_remap(blockIdx.x, G, 8));
+    const int64_t n_dp = w < sk.dp_tiles ? uniform((sk.dp_tiles - w + G - 1) / G) : 0;
+    const int64_t begin = w < Gs ? uniform(w * W / Gs) : 0;
+    const int64_t end = w < Gs ? uniform((w + 1) * W / Gs) : 0;
+    int64_t it = begin;
+    for (int64_t item = 0;; ++item) {
+        int64_t tile, kb, ke, local = 0;
+        if (item < n_dp) {
+            tile = w + item * G;
+            kb = 0;
+            ke = S;
+        } else {
+            if (it >= end) break;
+            local = uniform(it / S);
+            kb = it - local * S;
+            ke = end - local * S < S ? end - local * S : S;
+            tile = sk.dp_tiles + local;
+            it = local * S + ke;
+        }
+        TileCoord t = tile_of(p.grid, tile);
+        t.batch = uniform(t.batch);
+        t.tm = uniform(t.tm);
+        t.tn = uniform(t.tn);
+        // the previous piece's epilogue has read its staging buffers before
+        // the ring is refilled
+        if (item > 0) __syncthreads();
+        f32x16 acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        const int buf = dma_tile_steps<T, A_KMAJOR, B_KMAJOR, WAVES_M, WAVES_N, BK, STAGES>(
+            p, lds, t, kb, ke, acc);
+        if (kb == 0 && ke == S) {
+            dma_tile_store<OUT, WAVES_M, WAVES_N, BK, STAGES>(p, lds, t, buf, acc);
+        } else {
+            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
+            const __amdgpu_buffer_rsrc_t rs = sk_slot(sk, 2 * w + side);
+            const int tid = threadIdx.x;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    // the whole vector is reinterpreted, then indexed
+                    const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const u32x4 v = {bits[4 * q], bits[4 * q + 1], bits[4 * q + 2],
+                                         bits[4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v, rs, tid * 16, ((i * FN + j) * 4 + q) * THREADS * 16, 0);
+                    }
+                }
+        }
+    }
+}
+
+// Workgroup (local tile, piece), piece = (i*FN + j)*4 + q: sums register
+// quad q of block (i, j) over the pieces of cut tile `local`, lowest
+// workgroup first, and stores it.  With the operands swapped in the matrix
+// instruction, register r of block (i, j) of lane l holds row l%32 and column
+// 8*(r/4) + 4*(l/32) + r%4 of that block: a quad is four consecutive columns
+// of one row.
+template <int OUT, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void hgemm_dma_streamk_fixup(DmaArgs p,
+                                                                                DmaStreamK sk) {
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int FN = WTN / 32;
+    constexpr int THREADS = WAVES_M * WAVES_N * 64;
+    constexpr int PIECES = (BM / WAVES_M / 32) * FN * 4;
+    constexpr int BATCH = 8;  // pieces whose loads are in flight together
+    const int64_t S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t local = blockIdx.x / PIECES;
+    const int piece = blockIdx.x % PIECES;
+    const int64_t g0 = ((local * S + 1) * Gs - 1) / W;
+    const int64_t g1 = ((local * S + S) * Gs - 1) / W;
+    if (g0 == g1) return;
+    const int tid = threadIdx.x;
+    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t g = g0; g <= g1; g += BATCH) {
+        u32x4 v[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            // past the last piece: an offset beyond the buffer reads zeros
+            const int64_t gu = g + u <= g1 ? g + u : g1;
+            const int64_t end = (gu + 1) * W / Gs;
+            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
+            const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
+            v[u] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(sk_slot(sk, 2 * gu + side), off,
+                                                             piece * THREADS * 16, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) sum += __builtin_bit_cast(f32x4, v[u]);
+    }
+    const TileCoord t = tile_of(p.grid, sk.dp_tiles + local);
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int blk = piece >> 2, q = piece & 3;
+    const int i = blk / FN, j = blk % FN;
+    const int64_t row = t.tm * BM + wm * WTM + i * 32 + (lane & 31);
+    const int64_t col0 = t.tn * BN + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+    if (row >= p.M) return;
+    char *Cb = static_cast<char *>(p.C) + t.batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
+    float old[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t off = row * p.ldc + (col0 + e < p.N ? col0 + e : 0);
+        old[e] = 0.0f;
+        if (p.beta != 0.0f) {
+            if (OUT == OUT_F32) {
+                old[e] = reinterpret_cast<const float *>(Cb)[off];
+            } else {
+                const uint16_t b = reinterpret_cast<const uint16_t *>(Cb)[off];
+                old[e] = OUT == OUT_BF16 ? __builtin_bit_cast(float, uint32_t(b) << 16)
+                                         : static_cast<float>(__builtin_bit_cast(_Float16, b));
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t col = col0 + e;
+        if (col >= p.N) continue;
+        float x = p.alpha * sum[e];
+        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, old[e], x);
+        if (p.epi.active()) x = epilogue_apply(p.epi, x, t.batch, row, col);
+        const int64_t off = row * p.ldc + col;
+        if (OUT == OUT_F32)
+            reinterpret_cast<float *>(Cb)[off] = x;
+        else if (OUT == OUT_BF16)
+            reinterpret_cast<uint16_t *>(Cb)[off] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+        else
+            reinterpret_cast<uint16_t *>(Cb)[off] =
+                __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+    }
+}
 
 // Tile configuration of the fast path: 256 x 256 block tile, BK-deep
 // stages, a ring of STAGES buffers, WAVES_M x WAVES_N waves.
@@ -241,6 +573,32 @@ hipError_t launch_layout(const Problem &p, DmaArgs &a, hipStream_t stream) {
                       : launch<T, OUT, false, false>(a, stream);
 }
 
+template <class T, int OUT, bool AK, bool BKM>
+hipError_t launch_sk(DmaArgs &a, DmaStreamK &sk, int64_t grid, hipStream_t stream) {
+    constexpr int WM = LIBGEMM_DMA_WM, WN = LIBGEMM_DMA_WN;
+    void *args[] = {&a, &sk};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(&hgemm_dma_streamk_kernel<T, OUT, AK, BKM, WM, WN,
+                                                                 LIBGEMM_DMA_BK, LIBGEMM_DMA_STAGES>),
+        dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), args, 0, stream);
+    if (e != hipSuccess || sk.iters == 0) return e;
+    constexpr int PIECES = (BM / WM / 32) * (BN / WN / 32) * 4;
+    const int64_t cut = a.grid.count() - sk.dp_tiles;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&hgemm_dma_streamk_fixup<OUT, WM, WN>),
+                           dim3(static_cast<unsigned>(cut * PIECES)), dim3(WM * WN * 64), args, 0,
+                           stream);
+}
+
+template <class T, int OUT>
+hipError_t launch_sk_layout(const Problem &p, DmaArgs &a, DmaStreamK &sk, int64_t grid,
+                            hipStream_t stream) {
+    if (p.a_kmajor)
+        return p.b_kmajor ? launch_sk<T, OUT, true, true>(a, sk, grid, stream)
+                          : launch_sk<T, OUT, true, false>(a, sk, grid, stream);
+    return p.b_kmajor ? launch_sk<T, OUT, false, true>(a, sk, grid, stream)
+                      : launch_sk<T, OUT, false, false>(a, sk, grid, stream);
+}
+
 int64_t span_of(int64_t rows, int64_t cols, bool row_contig, int64_t ld) {
     // rows x cols with `cols` contiguous when row_contig
     return row_contig ? (rows - 1) * ld + cols : (cols - 1) * ld + rows;
@@ -263,7 +621,9 @@ bool hgemm_dma_eligible(const Problem &p) {
     return true;
 }
 
-hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
+namespace {
+
+DmaArgs make_dma_args(const Problem &p, int32_t xcds) {
     DmaArgs a{};
     a.M = p.M;
     a.N = p.N;
@@ -279,19 +639,75 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
     a.sA = p.batch > 1 ? p.sA : 0;
     a.sB = p.batch > 1 ? p.sB : 0;
     a.sC = p.batch > 1 ? p.sC : 0;
-    a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, LIBGEMM_DMA_GROUP_M, 8};
-    if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
+    a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, LIBGEMM_DMA_GROUP_M, xcds};
     const int esz = p.out == Elem::F32 ? 4 : 2;
     // 16-byte chunks of C rows (8 bf16/fp16 or 4 fp32 elements)
     const int cw = 16 / esz;
     a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % 16) == 0 && p.ldc % cw == 0 && a.sC % cw == 0;
     a.epi = p.epi;
+    return a;
+}
+
+// Cost of the partial-tile exchange of the fast path's stream-K schedule
+// (writing the pieces, the fix-up kernel), in k steps of one tile, measured
+// on MI355X.
+constexpr int64_t DMA_SK_EXCHANGE_STEPS = 10;
+
+}  // namespace
+
+hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
+    DmaArgs a = make_dma_args(p, 8);
+    if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)
         return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)
                   : launch_layout<F16, OUT_F32>(p, a, stream);
     return bf ? launch_layout<BF16, OUT_BF16>(p, a, stream)
               : launch_layout<F16, OUT_F16>(p, a, stream);
+}
+
+// Step time over partial-tile time for streamk_groups (1.8 us per k step of the direct-load kernel at 4096^3, 0.13 us per partial tile).
+#ifndef LIBGEMM_DMA_SK_RATIO
+#define LIBGEMM_DMA_SK_RATIO 14
+#endif
+
+// As for the general kernel: worth it when the steps the cut last wave saves
+// exceed the exchange, ceil(T_r * S / G) steps per workgroup instead of S,
+// with G = HGEMM_STREAMK_MAX_GRID compute units.
+bool hgemm_dma_streamk_eligible(const Problem &p) {
+    if (!hgemm_dma_eligible(p)) return false;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+    const int64_t steps = (p.K + LIBGEMM_DMA_BK - 1) / LIBGEMM_DMA_BK;
+    const int64_t g = HGEMM_STREAMK_MAX_GRID;
+    const int64_t cut = tiles % g;
+    if (cut == 0 || tiles >= (int64_t(1) << 24) || steps >= (int64_t(1) << 24)) return false;
+    const int64_t tail = (cut * steps + g - 1) / g;
+    return steps - tail > DMA_SK_EXCHANGE_STEPS;
+}
+
+hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+    DmaArgs a = make_dma_args(p, 1);  // the work order itself spreads tiles over the dies
+    const int64_t tiles = a.grid.count();
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = HGEMM_STREAMK_MAX_GRID;
+    const int64_t G = cus < HGEMM_STREAMK_MAX_GRID ? cus : HGEMM_STREAMK_MAX_GRID;
+    DmaStreamK sk{};
+    sk.partials = static_cast<float *>(workspace);
+    sk.steps = (p.K + LIBGEMM_DMA_BK - 1) / LIBGEMM_DMA_BK;
+    sk.dp_tiles = tiles / G * G;
+    sk.iters = (tiles - sk.dp_tiles) * sk.steps;
+    sk.groups = sk.iters == 0 ? 0 : streamk_groups(G, tiles - sk.dp_tiles, sk.steps, LIBGEMM_DMA_SK_RATIO);
+    const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
+    if (grid == 0) return hipSuccess;
+    const bool bf = p.in == Elem::BF16;
+    if (p.out == Elem::F32)
+        return bf ? launch_sk_layout<BF16, OUT_F32>(p, a, sk, grid, stream)
+                  : launch_sk_layout<F16, OUT_F32>(p, a, sk, grid, stream);
+    return bf ? launch_sk_layout<BF16, OUT_BF16>(p, a, sk, grid, stream)
+              : launch_sk_layout<F16, OUT_F16>(p, a, sk, grid, stream);
 }
 
 }  // namespace libgemm

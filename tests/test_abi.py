@@ -296,7 +296,7 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_4096": "hgemm_mfma_dma", "f16_4096": "hgemm_mfma_dma",
             "bf16_qkv": "hgemm_mfma_dma", "bf16_ffn_up": "hgemm_mfma_dma",
             "bf16_ffn_down": "hgemm_mfma_dma", "f32_edge": "sgemm_mfma",
-            "bf16_edge": "hgemm_mfma", "bf16_skinny": "gemm_skinny",
+            "bf16_edge": "hgemm_mfma", "bf16_tail": "hgemm_mfma_dma", "bf16_skinny": "gemm_skinny",
             "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma",
             "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma"}
     assert sorted(want) == sorted(workloads.CONFIGS)
@@ -347,7 +347,13 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "bf16", 5119, 6399, 1001) == "hgemm_mfma"
     # 65 batches of 4 tiles: 256 tiles whole, 4 cut over the grid
     assert kname_ws(lib, "bf16", 300, 290, 1001, batch=65) == "hgemm_mfma_streamk"
-    assert kname_ws(lib, "bf16", 4096, 4352, 1024) == "hgemm_mfma_dma"
+    # aligned: the direct-load kernel's schedule, where the saved steps exceed its exchange
+    assert kname_ws(lib, "bf16", 4096, 4352, 1024) == "hgemm_mfma_dma_streamk"
+    assert kname_ws(lib, "f16", 2048, 2304, 1024, oa=1, ob=1) == "hgemm_mfma_dma_streamk"
+    # fewer than 64 tiles: the split-K kernel, workspace or not
+    assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
+    assert kname_ws(lib, "bf16", 4096, 4352, 256) == "hgemm_mfma_dma"       # 4 steps per tile
+    assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # whole waves
     # fp32 has no workspace entry point; K = 0 scales C
     assert kname_ws(lib, "f32", 4095, 4097, 1001) is None
     assert kname_ws(lib, "bf16", 4095, 4097, 0, lda=1) == "scale"

@@ -197,7 +197,7 @@ def test_repeat_runs_bit_identical(dt):
 # ------------------------------------------------------------------ the workloads
 
 SMALL_CONFIGS = ["f32_256"]
-FULL_CONFIGS = ["f32_4096", "bf16_4096", "f16_4096", "f32_edge", "bf16_edge", "bf16_skinny",
+FULL_CONFIGS = ["f32_4096", "bf16_4096", "f16_4096", "f32_edge", "bf16_edge", "bf16_tail", "bf16_skinny",
                 "bf16_attn_qk", "bf16_attn_pv", "bf16_qkv", "bf16_ffn_up", "bf16_ffn_down",
                 "bf16_ffn_up_gelu", "fp8_4096"]
 
@@ -691,6 +691,48 @@ def test_streamk_whole_waves_and_cut_tail(dt):
     # grid (16 pieces each); beta = 0.5, so the fix-up also reads C
     check(P(f"streamk-dp-{dt}", dt, 300, 290, 1001, beta=0.5, batch=65),
           kernel="hgemm_mfma_streamk", seed=84, use_workspace=True, repeat=2)
+
+
+# The direct-load kernel's stream-K schedule: aligned operands (extents and
+# leading dimensions multiples of 8 elements) and at least 64 tiles (fewer
+# go to the split-K kernel).
+DMA_SK_SHAPES = [(2048, 2304, 1024), (2304, 2048, 1536)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", DMA_SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_dma_streamk(dt, shape, orders):
+    M, N, K = shape
+    oa, ob = orders
+    check(P(f"dma-streamk-{dt}", dt, M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
+          kernel="hgemm_mfma_dma_streamk", seed=M + N + K, use_workspace=True, repeat=2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_dma_streamk_whole_waves_fp32_output_and_col_major_c(dt):
+    # 65 batches of 2 x 2 tiles: 256 whole, 4 cut over the grid
+    check(P(f"dma-streamk-dp-{dt}", dt, 512, 512, 2048, beta=0.5, batch=65),
+          kernel="hgemm_mfma_dma_streamk", seed=90, use_workspace=True, repeat=2)
+    check(P(f"dma-streamk-f32out-{dt}", dt, 512, 768, 2048, c_dtype="f32", beta=1.0, batch=12),
+          kernel="hgemm_mfma_dma_streamk", seed=91, use_workspace=True)
+    check(P(f"dma-streamk-colC-{dt}", dt, 2304, 2048, 1024, order_c=COL, beta=0.5),
+          kernel="hgemm_mfma_dma_streamk", seed=92, use_workspace=True)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_dma_streamk_integers_bit_exact(dt):
+    p = P(f"dma-streamk-int-{dt}", dt, 2048, 2304, 1024, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="hgemm_mfma_dma_streamk", host=_int_host(p, np.random.default_rng(93)),
+                   use_workspace=True)
+    assert res.max_err == 0.0 and res.max_ulp == 0
+
+
+def test_dma_streamk_tail_config_sampled():
+    # aligned 4096 x 4352 x 4096: 272 tiles on 256 compute units
+    check(workloads.config("bf16_tail"), kernel="hgemm_mfma_dma_streamk", sample="auto",
+          use_workspace=True, repeat=2)
 
 
 def test_streamk_workspace_too_small_is_the_plain_call():

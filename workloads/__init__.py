@@ -238,6 +238,10 @@ def _configs():
                 note="unaligned fp32 4095x4097x1001, alpha=0.5 beta=2, C0 U[-1,1]"),
         Problem("bf16_edge", "bf16", "bf16", 4095, 4097, 1001, alpha=0.5, beta=2.0,
                 note="unaligned bf16 4095x4097x1001, alpha=0.5 beta=2, C0 N(0,1)"),
+        # aligned, but 16 x 17 = 272 tiles of 256 x 256: one wave of 256
+        # compute units and 16 tiles more (the stream-K case of the fast path)
+        Problem("bf16_tail", "bf16", "bf16", 4096, 4352, 4096,
+                note="aligned bf16 4096x4352x4096 (272 tiles: one wave plus 16)"),
         Problem("bf16_skinny", "bf16", "bf16", 16, 4096, 4096,
                 note="skinny bf16 16x4096x4096 (bandwidth-bound)"),
         # Q (2048x128) times K^T: K is stored 2048x128 row-major, which is the
