@@ -68,10 +68,17 @@ struct SgemmArgs {
 };
 
 // Four consecutive elements x[0..3] of one operand row, zero outside
-// [0, limit); `inside` says the whole row exists.
-__device__ __attribute__((always_inline)) inline f4 load4(const float *x, bool vec, bool inside,
+// [0, limit); `inside` says the whole row exists.  A chunk inside the matrix
+// is one 16-byte load whatever its alignment: every fp32 element is 4-byte
+// aligned, and the global load instructions need no more than that.
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __attribute__((always_inline)) inline f4 load4(const float *x, bool, bool inside,
                                                           int64_t first, int64_t limit) {
-    if (vec && inside && first + 4 <= limit) return *reinterpret_cast<const f4 *>(x);
+    if (inside && first + 4 <= limit) {
+        const f4u u = *reinterpret_cast<const f4u *>(x);
+        return f4{u[0], u[1], u[2], u[3]};
+    }
     f4 v;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (inside && first + e < limit) ? x[e] : 0.0f;
