@@ -242,16 +242,19 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
 
 /* Workspace entry points.  gemm_bf16_ws / gemm_f16_ws take the arguments of
  * gemm_bf16 / gemm_f16 plus a device workspace, and compute the same product.
- * With at least gemm_workspace_size() bytes, a problem on the general kernel
- * (operands that are not 16-byte aligned) whose 256 x 256 tiles leave the
- * last wave of workgroups partly idle runs on the stream-K schedule ("CUDA
- * GEMM 矩阵乘法优化指南", blog.zhenwei.site, section 12.5, persistent kernels
- * and Stream-K): the tiles that fill whole waves of one workgroup per compute
- * unit are computed whole, and the k steps of the remaining tiles are split
- * evenly over the workgroups; the pieces of a tile that was cut are written to
- * the workspace and added, in a fixed order, by a second kernel on the same
- * stream, which also applies the epilogue.  It is chosen when the steps saved
- * in the last wave outweigh that exchange (about four k steps of one tile).
+ * With at least gemm_workspace_size() bytes, a problem on either 16-bit
+ * kernel (the general one for operands that are not 16-byte aligned, the
+ * direct-load one for aligned operands with 64 tiles or more) whose
+ * 256 x 256 tiles leave the last wave of workgroups partly idle runs on the
+ * stream-K schedule ("CUDA GEMM 矩阵乘法优化指南", blog.zhenwei.site, section
+ * 12.5, persistent kernels and Stream-K): the tiles that fill whole waves of
+ * one workgroup per compute unit are computed whole, and the k steps of the
+ * remaining tiles are split evenly over a number of workgroups that balances
+ * the tail against the exchange; the pieces of a tile that was cut are
+ * written to the workspace and added, in a fixed order, by a second kernel on
+ * the same stream, which also applies the epilogue.  It is chosen when the
+ * steps saved in the last wave outweigh that exchange (about four k steps of
+ * one tile on the general kernel, ten on the direct-load one).
  * Results are deterministic run to run; they may differ in rounding from
  * gemm_bf16 (the partial sums are grouped differently), within the same
  * accuracy.  Every other call ignores the workspace and behaves exactly like
