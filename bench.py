@@ -16,7 +16,7 @@ Each kernel cycles through at least three copies of its buffers, enough that
 their footprint exceeds twice the 256 MB MALL, so inputs come from HBM;
 --no-rotate reuses one set (the warm-cache figure).
 --workload runs the named workload, or a comma-separated list of them (see
-workloads.CONFIGS), instead of the headline step, for profiling.  --workspace runs bf16/fp16 workloads
+workloads.CONFIGS), instead of the headline step, for profiling.  --workspace runs fp32/bf16/fp16 workloads
 through the workspace entry points, which use the stream-K schedule where
 it applies.  --copy-calibration runs only a plain
 device-to-device copy of the given size (the reference kernel against which
@@ -53,6 +53,7 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "sgemm_splitk": "sgemm_splitk.hip", "gemm_skinny": "gemm_skinny.hip",
                  "f8gemm_mfma_dma": "f8gemm_mfma.hip", "f8gemm_mfma": "f8gemm_mfma.hip",
                  "hgemm_mfma_streamk": "hgemm_mfma.hip", "hgemm_mfma_dma_streamk": "hgemm_mfma_dma.hip",
+                 "sgemm_mfma_streamk": "sgemm_mfma.hip",
                  "scale": "scale.hip"}
 
 
@@ -206,7 +207,7 @@ def main():
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--workspace", action="store_true",
-                    help="bf16/fp16 workloads through the workspace entry points (stream-K)")
+                    help="fp32/bf16/fp16 workloads through the workspace entry points (stream-K)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the GEMM path has no multi-GPU "
@@ -234,7 +235,7 @@ def main():
             bufs = device_buffers(p, torch)
             sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
             nsets[p.name] = len(sets)
-            pws = ws if (ws is not None and p.in_dtype in ("bf16", "f16") and not p.bias
+            pws = ws if (ws is not None and p.in_dtype in ("f32", "bf16", "f16") and not p.bias
                          and not p.act) else None
             families[p.name] = kernel_family(p, bufs, pws)
             bias = device_bias(p, torch)

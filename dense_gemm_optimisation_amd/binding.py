@@ -74,6 +74,8 @@ def library() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = common + [i32, i64, i64, i64, i64, vp, sz, vp]
             fn.restype = i32
+        lib.gemm_f32_ws.argtypes = common + [i64, i64, i64, i64, vp, sz, vp]
+        lib.gemm_f32_ws.restype = i32
         lib.gemm_kernel_name_ws.argtypes = [i32] + common + [i32, i64, i64, i64, i64, vp, sz]
         lib.gemm_kernel_name_ws.restype = ctypes.c_char_p
         _lib = lib
@@ -182,8 +184,18 @@ def f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, f
 
 
 def workspace_size() -> int:
-    """Bytes of workspace that let gemm_bf16_ws / gemm_f16_ws use every schedule."""
+    """Bytes of workspace that let the *_ws entry points use every schedule."""
     return library().gemm_workspace_size()
+
+
+def gemm_f32_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                batch=1, stride_a=0, stride_b=0, stride_c=0, workspace=0, workspace_bytes=0,
+                stream=None, raise_on_error=True):
+    """gemm_f32 with a device workspace (address, bytes) for the stream-K schedule."""
+    st = library().gemm_f32_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                               order_c, batch, stride_a, stride_b, stride_c, workspace,
+                               workspace_bytes, _stream(stream))
+    return _check(st, "gemm_f32_ws", raise_on_error)
 
 
 def gemm_bf16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
@@ -220,8 +232,8 @@ def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta
     """The kernel the GEMM call with these arguments would launch ("" for an
     empty problem, None for invalid arguments); host only, no GPU needed.
     For 8-bit inputs ("e4m3"/"e5m2") b_dtype and out_dtype name B's format
-    and C's type, as in gemm(); a workspace (16-bit inputs) asks about the
-    workspace entry points."""
+    and C's type, as in gemm(); a workspace (fp32, bf16, fp16 inputs) asks
+    about the workspace entry points."""
     if workspace is not None:
         name = library().gemm_kernel_name_ws(_INPUT[in_dtype], M, N, K, alpha, A, lda, order_a, B,
                                              ldb, order_b, beta, C, ldc, order_c, c_dtype, batch,
@@ -246,10 +258,14 @@ def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ld
     "e4m3"/"e5m2" with B's format in b_dtype (default: A's) and C's type
     name in out_dtype); a bias address or an activation selects the
     fused-epilogue entry point (not offered for 8-bit inputs); a workspace
-    address (bf16/fp16, no epilogue) selects the workspace entry point."""
+    address (fp32/bf16/fp16, no epilogue) selects the workspace entry point."""
     if workspace is not None:
-        if in_dtype not in ("bf16", "f16") or bias is not None or act != ACT_NONE:
-            raise ValueError("the workspace entry points take bf16/fp16 inputs without epilogue")
+        if in_dtype not in ("f32", "bf16", "f16") or bias is not None or act != ACT_NONE:
+            raise ValueError("the workspace entry points take fp32/bf16/fp16 inputs without epilogue")
+        if in_dtype == "f32":
+            return gemm_f32_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                               order_c, batch, stride_a, stride_b, stride_c, workspace,
+                               workspace_bytes, stream, raise_on_error)
         fn = gemm_bf16_ws if in_dtype == "bf16" else gemm_f16_ws
         return fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c, c_dtype,
                   batch, stride_a, stride_b, stride_c, workspace, workspace_bytes, stream,

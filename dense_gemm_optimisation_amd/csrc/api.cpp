@@ -81,6 +81,7 @@ enum class Kernel {
     F8Dma,       // 8-bit floats, K-contiguous aligned operands, direct loads
     HgemmStreamK,  // bf16/fp16 general kernel on the stream-K schedule (workspace)
     HgemmDmaStreamK,  // bf16/fp16 direct-load kernel on the stream-K schedule (workspace)
+    SgemmStreamK,  // fp32 general kernel on the stream-K schedule (workspace)
 };
 
 const char *kernel_name(Kernel k) {
@@ -99,6 +100,7 @@ const char *kernel_name(Kernel k) {
     case Kernel::F8Dma: return "f8gemm_mfma_dma";
     case Kernel::HgemmStreamK: return "hgemm_mfma_streamk";
     case Kernel::HgemmDmaStreamK: return "hgemm_mfma_dma_streamk";
+    case Kernel::SgemmStreamK: return "sgemm_mfma_streamk";
     }
     return "";
 }
@@ -139,7 +141,8 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::F8Mfma: return launch_f8gemm(p, stream);
     case Kernel::F8Dma: return launch_f8gemm_dma(p, stream);
     case Kernel::HgemmStreamK:
-    case Kernel::HgemmDmaStreamK: return hipErrorInvalidValue;  // need the workspace: run()
+    case Kernel::HgemmDmaStreamK:
+    case Kernel::SgemmStreamK: return hipErrorInvalidValue;  // need the workspace: run()
     }
     return hipErrorInvalidValue;
 }
@@ -242,8 +245,8 @@ gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K
 }
 
 // With a workspace: its checks, and the switch of the 16-bit kernels (the
-// direct-load and the general one) to their stream-K schedule where it
-// applies.
+// direct-load and the general one) and of the general fp32 kernel to their
+// stream-K schedule where it applies.
 gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, int orderA,
                             int64_t lda, int orderB, int64_t ldb, int orderC, int64_t ldc,
                             int64_t strideA, int64_t strideB, int64_t strideC,
@@ -265,6 +268,8 @@ gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, i
         k = Kernel::HgemmStreamK;
     else if (k == Kernel::HgemmDma && room && hgemm_dma_streamk_eligible(p))
         k = Kernel::HgemmDmaStreamK;
+    else if (k == Kernel::SgemmMfma && !force_general() && room && sgemm_streamk_eligible(p))
+        k = Kernel::SgemmStreamK;
     return GEMM_OK;
 }
 
@@ -284,6 +289,7 @@ gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K,
     if (st != GEMM_OK || k == Kernel::None) return st;
     const hipError_t err = k == Kernel::HgemmStreamK      ? launch_hgemm_streamk(p, workspace, stream)
                            : k == Kernel::HgemmDmaStreamK ? launch_hgemm_dma_streamk(p, workspace, stream)
+                           : k == Kernel::SgemmStreamK    ? launch_sgemm_streamk(p, workspace, stream)
                                                           : launch(k, p, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
@@ -316,6 +322,16 @@ gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float
                        int64_t strideA, int64_t strideB, int64_t strideC, hipStream_t stream) {
     return run(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
                orderC, batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream);
+}
+
+gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                          int64_t lda, gemm_order_t orderA, const float *B, int64_t ldb,
+                          gemm_order_t orderB, float beta, float *C, int64_t ldc, gemm_order_t orderC,
+                          int64_t batch, int64_t strideA, int64_t strideB, int64_t strideC,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return run(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
+               orderC, batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream, workspace,
+               workspace_bytes);
 }
 
 gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
@@ -479,8 +495,11 @@ const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K
         ein = Elem::BF16;
     else if (in == GEMM_INPUT_F16)
         ein = Elem::F16;
+    else if (in == GEMM_INPUT_F32)
+        ein = Elem::F32;
     else
         return nullptr;
+    if (ein == Elem::F32) c_dtype = GEMM_DTYPE_SAME;  // gemm_f32_ws has no c_dtype
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return nullptr;
     Problem p;
     Kernel k;

@@ -60,6 +60,13 @@ hipError_t launch_sgemm_dma(const Problem &p, hipStream_t stream);
 // (sgemm_splitk_eligible()).
 bool sgemm_splitk_eligible(const Problem &p);
 hipError_t launch_sgemm_splitk(const Problem &p, hipStream_t stream);
+// The general fp32 kernel's stream-K schedule, through the same workspace as
+// the 16-bit kernels' (two 128 x 128 fp32 partial tiles per workgroup, four
+// workgroups per compute unit: the same bytes); only where
+// sgemm_streamk_eligible() holds.
+constexpr int64_t SGEMM_STREAMK_MAX_GRID = 1024;
+bool sgemm_streamk_eligible(const Problem &p);
+hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA, any shape
 // The same kernel's stream-K schedule, which cuts tiles across workgroups
 // through a caller-provided workspace of hgemm_streamk_workspace_bytes()
@@ -83,6 +90,8 @@ inline int64_t streamk_groups(int64_t G, int64_t cut, int64_t steps, double rati
 constexpr int64_t hgemm_streamk_workspace_bytes() {
     return 2 * HGEMM_STREAMK_MAX_GRID * 256 * 256 * 4;
 }
+static_assert(2 * 1024 * 128 * 128 * 4 == hgemm_streamk_workspace_bytes(),
+              "the fp32 stream-K schedule (1024 workgroups, 128 x 128 tiles) fits the workspace");
 bool hgemm_streamk_eligible(const Problem &p);
 hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);
 // bf16/fp16 on MFMA with direct global->LDS loads; only for problems where

@@ -48,6 +48,7 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128, BK = 16;
 constexpr int THREADS = 256;
@@ -459,6 +460,215 @@ int64_t span_of(int64_t rows, int64_t cols, bool row_contig, int64_t ld) {
     return row_contig ? (rows - 1) * ld + cols : (cols - 1) * ld + rows;
 }
 
+// Stream-K schedule of the general fp32 kernel (section 12.5 of "CUDA GEMM
+// 矩阵乘法优化指南", blog.zhenwei.site, persistent kernels and Stream-K), the
+// split of the 16-bit kernels' schedule with 128 x 128 tiles and four
+// workgroups per compute unit (G = 4 per unit): the tiles filling whole
+// waves of G are computed whole, tile w + n*G by workgroup w; the (tile, k
+// step) iterations of the other tiles are split evenly over Gs workgroups; a
+// piece covering a whole tile is stored through the epilogue, any other is
+// written to the workgroup's slot 2w (the piece holding its last iteration)
+// or 2w + 1 (its first), and sgemm_streamk_fixup adds the pieces of each cut
+// tile in increasing workgroup order and applies the epilogue.
+struct SgStreamK {
+    float *partials;    // 2 * Gs slots of 128 x 128 floats
+    int64_t steps;      // k steps per tile (S)
+    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
+    int64_t iters;      // W = (tiles - dp_tiles) * steps
+    int64_t groups;     // Gs
+};
+
+constexpr int SG_SLOT = BM * BN;  // floats per partial tile
+
+// Slot `slot` as a raw buffer: register quad q of accumulator (i, j) of
+// thread tid is the 16 bytes at ((i*2 + j)*4 + q) * THREADS * 16 + tid * 16.
+__device__ inline __amdgpu_buffer_rsrc_t sg_slot(const SgStreamK &sk, int64_t slot) {
+    return __builtin_amdgcn_make_buffer_rsrc(sk.partials + slot * SG_SLOT, 0, SG_SLOT * 4,
+                                             0x00020000);
+}
+
+__device__ inline int64_t sg_uniform(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(uint64_t(x) >> 32));
+    return static_cast<int64_t>((uint64_t(hi) << 32) | lo);
+}
+
+// k steps [kb, ke) of tile t into acc: the general kernel's loop.
+template <bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void sg_tile_steps(const SgemmArgs &p, float (*smem)[2][PANEL],
+                                              const TileCoord &t, int64_t kb, int64_t ke,
+                                              f32x16 (&acc)[2][2]) {
+    using PA = Panel<A_KMAJOR>;
+    using PB = Panel<B_KMAJOR>;
+    const float *A = p.A + t.batch * p.sA;
+    const float *B = p.B + t.batch * p.sB;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int idx = lane & 31, half = lane >> 5;
+    f4 va[2], vb[2];
+    PA::load(A, p.lda, p.vec_a, m0, p.M, kb * BK, p.K, tid, va);
+    PB::load(B, p.ldb, p.vec_b, n0, p.N, kb * BK, p.K, tid, vb);
+    PA::store(smem[0][0], tid, va);
+    PB::store(smem[0][1], tid, vb);
+    __syncthreads();
+    for (int64_t s = kb; s < ke; ++s) {
+        const int cur = (s - kb) & 1;
+        const bool more = s + 1 < ke;
+        if (more) {
+            PA::load(A, p.lda, p.vec_a, m0, p.M, (s + 1) * BK, p.K, tid, va);
+            PB::load(B, p.ldb, p.vec_b, n0, p.N, (s + 1) * BK, p.K, tid, vb);
+        }
+#pragma unroll
+        for (int g = 0; g < BK / 8; ++g) {
+            float fa[2][4], fb[2][4];
+            PA::frag(smem[cur][0], wm * 64, g, idx, half, fa);
+            PB::frag(smem[cur][1], wn * 64, g, idx, half, fb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[j][e], fa[i][e],
+                                                                         acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            PA::store(smem[cur ^ 1][0], tid, va);
+            PB::store(smem[cur ^ 1][1], tid, vb);
+        }
+        __syncthreads();
+    }
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR>
+__global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, SgStreamK sk) {
+    __shared__ __attribute__((aligned(16))) float smem[2][2][PANEL];
+    // logical workgroup: the hardware id regrouped per XCD
+    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t w = sg_uniform(xcd_remap(blockIdx.x, G, 8));
+    const int64_t n_dp = w < sk.dp_tiles ? sg_uniform((sk.dp_tiles - w + G - 1) / G) : 0;
+    const int64_t begin = w < Gs ? sg_uniform(w * W / Gs) : 0;
+    const int64_t end = w < Gs ? sg_uniform((w + 1) * W / Gs) : 0;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    int64_t it = begin;
+    for (int64_t item = 0;; ++item) {
+        int64_t tile, kb, ke, local = 0;
+        if (item < n_dp) {
+            tile = w + item * G;
+            kb = 0;
+            ke = S;
+        } else {
+            if (it >= end) break;
+            local = sg_uniform(it / S);
+            kb = it - local * S;
+            ke = end - local * S < S ? end - local * S : S;
+            tile = sk.dp_tiles + local;
+            it = local * S + ke;
+        }
+        TileCoord t = tile_of(p.grid, tile);
+        t.batch = sg_uniform(t.batch);
+        t.tm = sg_uniform(t.tm);
+        t.tn = sg_uniform(t.tn);
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        sg_tile_steps<A_KMAJOR, B_KMAJOR>(p, smem, t, kb, ke, acc);
+        if (kb == 0 && ke == S) {
+            store_c<A_KMAJOR, B_KMAJOR>(p, acc, p.C + t.batch * p.sC, t.tm * BM + wm * 64,
+                                        t.tn * BN + wn * 64, lane & 31, lane >> 5, t.batch);
+        } else {
+            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
+            const __amdgpu_buffer_rsrc_t rs = sg_slot(sk, 2 * w + side);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                      acc[i][j][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u4, v), rs,
+                            tid * 16, ((i * 2 + j) * 4 + q) * THREADS * 16, 0);
+                    }
+        }
+    }
+}
+
+// Workgroup (local tile, piece), piece = (i*2 + j)*4 + q: sums register quad
+// q of accumulator (i, j) over the pieces of cut tile `local`, lowest
+// workgroup first, and stores it.  Register 4q + e of accumulator (i, j) of a
+// lane holds C[mw + row_of_A(i, idx)][nw + row_of_B(j, 8q + 4*half + e)].
+template <bool A_KMAJOR, bool B_KMAJOR>
+__global__ __launch_bounds__(THREADS) void sgemm_streamk_fixup(SgemmArgs p, SgStreamK sk) {
+    constexpr int BATCH = 8;  // pieces whose loads are in flight together
+    const int64_t S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t local = blockIdx.x / 16;
+    const int piece = blockIdx.x % 16;
+    const int64_t g0 = ((local * S + 1) * Gs - 1) / W;
+    const int64_t g1 = ((local * S + S) * Gs - 1) / W;
+    if (g0 == g1) return;
+    const int tid = threadIdx.x;
+    f4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t g = g0; g <= g1; g += BATCH) {
+        f4 v[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            // past the last piece: an offset beyond the buffer reads zeros
+            const int64_t gu = g + u <= g1 ? g + u : g1;
+            const int64_t end = (gu + 1) * W / Gs;
+            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
+            const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
+            v[u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              sg_slot(sk, 2 * gu + side), off, piece * THREADS * 16, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) sum += v[u];
+    }
+    const TileCoord t = tile_of(p.grid, sk.dp_tiles + local);
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int idx = lane & 31, half = lane >> 5;
+    const int i = piece >> 3, j = (piece >> 2) & 1, q = piece & 3;
+    const int64_t row = t.tm * BM + wm * 64 + Panel<A_KMAJOR>::row_of(i, idx);
+    if (row >= p.M) return;
+    float *C = p.C + t.batch * p.sC;
+    float old[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t col = t.tn * BN + wn * 64 + Panel<B_KMAJOR>::row_of(j, 8 * q + 4 * half + e);
+        old[e] = p.beta != 0.0f ? C[row * p.ldc + (col < p.N ? col : 0)] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t col = t.tn * BN + wn * 64 + Panel<B_KMAJOR>::row_of(j, 8 * q + 4 * half + e);
+        if (col >= p.N) continue;
+        float x = p.alpha * sum[e];
+        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, old[e], x);
+        if (p.epi.active()) x = epilogue_apply(p.epi, x, t.batch, row, col);
+        C[row * p.ldc + col] = x;
+    }
+}
+
+template <bool AK, bool BKM>
+hipError_t launch_sk(SgemmArgs &a, SgStreamK &sk, int64_t grid, hipStream_t stream) {
+    void *args[] = {&a, &sk};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sgemm_streamk_kernel<AK, BKM>),
+                                   dim3(static_cast<unsigned>(grid)), dim3(THREADS), args, 0, stream);
+    if (e != hipSuccess || sk.iters == 0) return e;
+    const int64_t cut = a.grid.count() - sk.dp_tiles;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&sgemm_streamk_fixup<AK, BKM>),
+                           dim3(static_cast<unsigned>(cut * 16)), dim3(THREADS), args, 0, stream);
+}
+
 }  // namespace
 
 // The direct-load kernel needs 16-byte aligned operand rows (base, leading
@@ -520,6 +730,65 @@ hipError_t launch_sgemm_mfma(const Problem &p, hipStream_t stream) {
 
 hipError_t launch_sgemm_dma(const Problem &p, hipStream_t stream) {
     return launch_any(p, true, stream);
+}
+
+namespace {
+
+// Workgroups of the fp32 stream-K grid: four per compute unit (the general
+// kernel's occupancy), at most SGEMM_STREAMK_MAX_GRID.
+int64_t sg_streamk_grid() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = SGEMM_STREAMK_MAX_GRID / 4;
+    const int64_t g = 4 * int64_t(cus);
+    return g < SGEMM_STREAMK_MAX_GRID ? g : SGEMM_STREAMK_MAX_GRID;
+}
+
+// Cost of the partial-tile exchange, in k steps (16 k) of one tile, and the
+// step time over partial-tile time for streamk_groups (4.4 us per k step of
+// a workgroup at 4096^3 with four per compute unit, 0.03 us per 64 KiB
+// partial tile moved through HBM twice).
+constexpr int64_t SG_SK_EXCHANGE_STEPS = 8;
+#ifndef LIBGEMM_SG_SK_RATIO
+#define LIBGEMM_SG_SK_RATIO 140
+#endif
+
+}  // namespace
+
+// Worth it when the steps the cut last wave saves exceed the exchange:
+// ceil(T_r * S / G) steps per workgroup instead of S, with G =
+// SGEMM_STREAMK_MAX_GRID workgroups (four per compute unit of MI355X).
+bool sgemm_streamk_eligible(const Problem &p) {
+    if (p.in != Elem::F32) return false;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+    const int64_t steps = (p.K + BK - 1) / BK;
+    const int64_t g = SGEMM_STREAMK_MAX_GRID;
+    const int64_t cut = tiles % g;
+    if (cut == 0 || tiles >= (int64_t(1) << 24) || steps >= (int64_t(1) << 24)) return false;
+    const int64_t tail = (cut * steps + g - 1) / g;
+    return steps - tail > SG_SK_EXCHANGE_STEPS;
+}
+
+hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+    SgemmArgs a = make_args(p);
+    a.grid.xcds = 1;  // the work order itself spreads tiles over the dies
+    const int64_t tiles = a.grid.count();
+    const int64_t G = sg_streamk_grid();
+    SgStreamK sk{};
+    sk.partials = static_cast<float *>(workspace);
+    sk.steps = (p.K + BK - 1) / BK;
+    sk.dp_tiles = tiles / G * G;
+    sk.iters = (tiles - sk.dp_tiles) * sk.steps;
+    sk.groups = sk.iters == 0 ? 0 : streamk_groups(G, tiles - sk.dp_tiles, sk.steps, LIBGEMM_SG_SK_RATIO);
+    const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
+    if (grid == 0) return hipSuccess;
+    if (p.a_kmajor)
+        return p.b_kmajor ? launch_sk<true, true>(a, sk, grid, stream)
+                          : launch_sk<true, false>(a, sk, grid, stream);
+    return p.b_kmajor ? launch_sk<false, true>(a, sk, grid, stream)
+                      : launch_sk<false, false>(a, sk, grid, stream);
 }
 
 }  // namespace libgemm

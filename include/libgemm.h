@@ -23,7 +23,7 @@
  *              and an activation applied before the store (see below).
  *   gemm_f8    8-bit float inputs (OCP E4M3 or E5M2, each operand in its own
  *              format), fp32 accumulation, output in fp32, bf16 or fp16.
- *   gemm_bf16_ws, gemm_f16_ws  gemm_bf16 / gemm_f16 with a caller-provided
+ *   gemm_f32_ws, gemm_bf16_ws, gemm_f16_ws  the products with a caller-provided
  *              workspace, which lets the library run the stream-K schedule
  *              (see below); gemm_workspace_size gives the bytes it uses.
  *   gemm_kernel_name, gemm_f8_kernel_name, gemm_kernel_name_ws  which kernel
@@ -240,8 +240,11 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
                       gemm_output_t typeC, int64_t batch, int64_t strideA,
                       int64_t strideB, int64_t strideC, hipStream_t stream);
 
-/* Workspace entry points.  gemm_bf16_ws / gemm_f16_ws take the arguments of
- * gemm_bf16 / gemm_f16 plus a device workspace, and compute the same product.
+/* Workspace entry points.  gemm_f32_ws / gemm_bf16_ws / gemm_f16_ws take the
+ * arguments of gemm_f32 / gemm_bf16 / gemm_f16 plus a device workspace, and
+ * compute the same product.  For fp32 the general kernel (operands that are
+ * not 16-byte aligned, 128 x 128 tiles, four workgroups per compute unit)
+ * has the same schedule, with the same workspace.
  * With at least gemm_workspace_size() bytes, a problem on either 16-bit
  * kernel (the general one for operands that are not 16-byte aligned, the
  * direct-load one for aligned operands with 64 tiles or more) whose
@@ -269,6 +272,14 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
  * A misaligned, overlapping or NULL (with bytes > 0) workspace is
  * GEMM_ERR_INVALID_ARG; everything else is as for gemm_bf16. */
 size_t gemm_workspace_size(void);
+
+gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                          const float *A, int64_t lda, gemm_order_t orderA,
+                          const float *B, int64_t ldb, gemm_order_t orderB,
+                          float beta, float *C, int64_t ldc, gemm_order_t orderC,
+                          int64_t batch, int64_t strideA, int64_t strideB,
+                          int64_t strideC, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha,
                            const uint16_t *A, int64_t lda, gemm_order_t orderA,
@@ -327,11 +338,12 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
                                 int64_t batch, int64_t strideA,
                                 int64_t strideB, int64_t strideC);
 
-/* The kernel gemm_bf16_ws (in = GEMM_INPUT_BF16) or gemm_f16_ws
- * (GEMM_INPUT_F16) would launch: the names of gemm_kernel_name, or
- * "hgemm_mfma_streamk" for the stream-K schedule; "" and NULL as for
- * gemm_kernel_name (NULL also for in = GEMM_INPUT_F32).  The workspace is
- * only checked, never dereferenced. */
+/* The kernel gemm_f32_ws (in = GEMM_INPUT_F32; c_dtype is then ignored),
+ * gemm_bf16_ws (GEMM_INPUT_BF16) or gemm_f16_ws (GEMM_INPUT_F16) would
+ * launch: the names of gemm_kernel_name, or "hgemm_mfma_streamk",
+ * "hgemm_mfma_dma_streamk" or "sgemm_mfma_streamk" for the stream-K
+ * schedules; "" and NULL as for gemm_kernel_name.  The workspace is only
+ * checked, never dereferenced. */
 const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K,
                                 float alpha, const void *A, int64_t lda,
                                 gemm_order_t orderA, const void *B, int64_t ldb,

@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
                                     "gemm_bf16_ws", "gemm_f16", "gemm_f16_bias_act",
-                                    "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act", "gemm_f8",
+                                    "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act", "gemm_f32_ws",
+                                    "gemm_f8",
                                     "gemm_f8_kernel_name", "gemm_kernel_name",
                                     "gemm_kernel_name_ws", "gemm_status_string",
                                     "gemm_workspace_size"]
@@ -354,8 +355,12 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
     assert kname_ws(lib, "bf16", 4096, 4352, 256) == "hgemm_mfma_dma"       # 4 steps per tile
     assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # whole waves
-    # fp32 has no workspace entry point; K = 0 scales C
-    assert kname_ws(lib, "f32", 4095, 4097, 1001) is None
+    # fp32: the general kernel's schedule (128 x 128 tiles, 1024 workgroups)
+    assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_streamk"
+    assert kname_ws(lib, "f32", 4095, 4097, 129) == "sgemm_mfma"          # 9 steps per tile
+    assert kname_ws(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma_dma"     # aligned
+    assert kname_ws(lib, "f32", 4095, 4097, 1001, nbytes=1 << 20) == "sgemm_mfma"
+    # K = 0 scales C
     assert kname_ws(lib, "bf16", 4095, 4097, 0, lda=1) == "scale"
     clean_env.setenv("LIBGEMM_FORCE_GENERAL", "1")
     assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma"

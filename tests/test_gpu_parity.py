@@ -735,6 +735,41 @@ def test_dma_streamk_tail_config_sampled():
           use_workspace=True, repeat=2)
 
 
+# The general fp32 kernel's stream-K schedule (128 x 128 tiles, four
+# workgroups per compute unit).
+F32_SK_SHAPES = [(300, 290, 8193), (1000, 1030, 2001)]
+
+
+@pytest.mark.parametrize("shape", F32_SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_f32_streamk(shape, orders):
+    M, N, K = shape
+    oa, ob = orders
+    check(P("f32-streamk", "f32", M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
+          kernel="sgemm_mfma_streamk", seed=M + K + 7, use_workspace=True, repeat=2)
+
+
+def test_f32_streamk_whole_waves_batches_and_col_major_c():
+    # 114 batches of 3 x 3 tiles: 1024 whole, 2 cut over the grid
+    check(P("f32-streamk-dp", "f32", 300, 290, 1001, beta=0.5, batch=114),
+          kernel="sgemm_mfma_streamk", seed=94, use_workspace=True, repeat=2)
+    check(P("f32-streamk-colC", "f32", 1030, 1000, 2001, order_c=COL, ldc=1033, beta=0.5),
+          kernel="sgemm_mfma_streamk", seed=95, use_workspace=True)
+
+
+def test_f32_streamk_integers_bit_exact():
+    p = P("f32-streamk-int", "f32", 1000, 1030, 2001, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="sgemm_mfma_streamk", host=_int_host(p, np.random.default_rng(96)),
+                   use_workspace=True)
+    assert res.max_err == 0.0
+
+
+def test_f32_streamk_edge_config_sampled():
+    check(workloads.config("f32_edge"), kernel="sgemm_mfma_streamk", sample="auto",
+          use_workspace=True, repeat=2)
+
+
 def test_streamk_workspace_too_small_is_the_plain_call():
     p = P("streamk-small-ws", "bf16", 513, 770, 3001, beta=0.5)
     host = workloads.generate(p, seed=83)
