@@ -487,12 +487,6 @@ __device__ inline __amdgpu_buffer_rsrc_t sg_slot(const SgStreamK &sk, int64_t sl
                                              0x00020000);
 }
 
-__device__ inline int64_t sg_uniform(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(uint64_t(x) >> 32));
-    return static_cast<int64_t>((uint64_t(hi) << 32) | lo);
-}
-
 // k steps [kb, ke) of tile t into acc: the general kernel's loop.
 template <bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void sg_tile_steps(const SgemmArgs &p, float (*smem)[2][PANEL],
@@ -547,10 +541,10 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, 
     __shared__ __attribute__((aligned(16))) float smem[2][2][PANEL];
     // logical workgroup: the hardware id regrouped per XCD
     const int64_t G = gridDim.x, S = sk.steps, W = sk.iters, Gs = sk.groups;
-    const int64_t w = sg_uniform(xcd_remap(blockIdx.x, G, 8));
-    const int64_t n_dp = w < sk.dp_tiles ? sg_uniform((sk.dp_tiles - w + G - 1) / G) : 0;
-    const int64_t begin = w < Gs ? sg_uniform(w * W / Gs) : 0;
-    const int64_t end = w < Gs ? sg_uniform((w + 1) * W / Gs) : 0;
+    const int64_t w = dma::uniform(xcd_remap(blockIdx.x, G, 8));
+    const int64_t n_dp = w < sk.dp_tiles ? dma::uniform((sk.dp_tiles - w + G - 1) / G) : 0;
+    const int64_t begin = w < Gs ? dma::uniform(w * W / Gs) : 0;
+    const int64_t end = w < Gs ? dma::uniform((w + 1) * W / Gs) : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -563,16 +557,16 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, 
             ke = S;
         } else {
             if (it >= end) break;
-            local = sg_uniform(it / S);
+            local = dma::uniform(it / S);
             kb = it - local * S;
             ke = end - local * S < S ? end - local * S : S;
             tile = sk.dp_tiles + local;
             it = local * S + ke;
         }
         TileCoord t = tile_of(p.grid, tile);
-        t.batch = sg_uniform(t.batch);
-        t.tm = sg_uniform(t.tm);
-        t.tn = sg_uniform(t.tn);
+        t.batch = dma::uniform(t.batch);
+        t.tm = dma::uniform(t.tm);
+        t.tn = dma::uniform(t.tn);
         f32x16 acc[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
