@@ -50,6 +50,14 @@ bool force_general() {
     return v != nullptr && v[0] == '1';
 }
 
+// LIBGEMM_FORCE_STREAMK=1 makes the workspace entry points run the stream-K
+// schedule wherever it can run, whatever its cost model says (used to test
+// the schedule on small problems).
+bool force_streamk() {
+    const char *v = std::getenv("LIBGEMM_FORCE_STREAMK");
+    return v != nullptr && v[0] == '1';
+}
+
 // LIBGEMM_NO_SPLITK=1 keeps few-tile and skinny problems on the main
 // kernels instead of the split-K ones (used to test them against each other).
 bool no_splitk() {
@@ -264,11 +272,12 @@ gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, i
         (bias != nullptr && overlap(rw, range_of(bias, N, p.batch, strideBias, esz))))
         return GEMM_ERR_INVALID_ARG;
     const bool room = bytes >= static_cast<size_t>(hgemm_streamk_workspace_bytes());
-    if (k == Kernel::HgemmMfma && !force_general() && room && hgemm_streamk_eligible(p))
+    const bool force = force_streamk();
+    if (k == Kernel::HgemmMfma && !force_general() && room && hgemm_streamk_eligible(p, force))
         k = Kernel::HgemmStreamK;
-    else if (k == Kernel::HgemmDma && room && hgemm_dma_streamk_eligible(p))
+    else if (k == Kernel::HgemmDma && room && hgemm_dma_streamk_eligible(p, force))
         k = Kernel::HgemmDmaStreamK;
-    else if (k == Kernel::SgemmMfma && !force_general() && room && sgemm_streamk_eligible(p))
+    else if (k == Kernel::SgemmMfma && !force_general() && room && sgemm_streamk_eligible(p, force))
         k = Kernel::SgemmStreamK;
     return GEMM_OK;
 }

@@ -65,9 +65,11 @@ hipError_t launch_sgemm_splitk(const Problem &p, hipStream_t stream);
 // workgroups per compute unit: the same bytes); only where
 // sgemm_streamk_eligible() holds.
 constexpr int64_t SGEMM_STREAMK_MAX_GRID = 1024;
-bool sgemm_streamk_eligible(const Problem &p);
+bool sgemm_streamk_eligible(const Problem &p, bool force = false);
 hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA, any shape
+// The *_streamk_eligible functions check whether a problem can run on the
+// schedule and, unless `force`, whether the cost model says it pays.
 // The same kernel's stream-K schedule, which cuts tiles across workgroups
 // through a caller-provided workspace of hgemm_streamk_workspace_bytes()
 // (two fp32 partial 256 x 256 tiles per workgroup); only where
@@ -92,7 +94,7 @@ constexpr int64_t hgemm_streamk_workspace_bytes() {
 }
 static_assert(2 * 1024 * 128 * 128 * 4 == hgemm_streamk_workspace_bytes(),
               "the fp32 stream-K schedule (1024 workgroups, 128 x 128 tiles) fits the workspace");
-bool hgemm_streamk_eligible(const Problem &p);
+bool hgemm_streamk_eligible(const Problem &p, bool force = false);
 hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);
 // bf16/fp16 on MFMA with direct global->LDS loads; only for problems where
 // hgemm_dma_eligible() holds (aligned operands, extents multiple of 8).
@@ -101,7 +103,7 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream);
 // Its stream-K schedule, through the same workspace as the general kernel's
 // (hgemm_streamk_workspace_bytes()); only where hgemm_dma_streamk_eligible()
 // holds.
-bool hgemm_dma_streamk_eligible(const Problem &p);
+bool hgemm_dma_streamk_eligible(const Problem &p, bool force = false);
 hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream);
 // bf16/fp16 split-K inside a workgroup, for problems with few output tiles
 // and a long K (hgemm_splitk_eligible()).

@@ -903,7 +903,7 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream) {
 // cost of exchanging partial tiles: the last wave then takes
 // ceil(T_r * S / G) steps per workgroup instead of S.  The model uses
 // HGEMM_STREAMK_MAX_GRID compute units (MI355X has 256).
-bool hgemm_streamk_eligible(const Problem &p) {
+bool hgemm_streamk_eligible(const Problem &p, bool force) {
     if (p.in != Elem::BF16 && p.in != Elem::F16) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
     const int64_t steps = (p.K + BK - 1) / BK;
@@ -912,7 +912,7 @@ bool hgemm_streamk_eligible(const Problem &p) {
     if (cut == 0 || tiles >= (int64_t(1) << 24) || steps >= (int64_t(1) << 24)) return false;
     const int64_t tail = (cut * steps + g - 1) / g;
     const HgemmArgs a = make_args(p, 1);
-    return a.ubuf_a && a.ubuf_b && steps - tail > SK_EXCHANGE_STEPS;
+    return a.ubuf_a && a.ubuf_b && (force || steps - tail > SK_EXCHANGE_STEPS);
 }
 
 hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {

@@ -648,10 +648,12 @@ DmaArgs make_dma_args(const Problem &p, int32_t xcds) {
     return a;
 }
 
-// Cost of the partial-tile exchange of the fast path's stream-K schedule
-// (writing the pieces, the fix-up kernel), in k steps of one tile, measured
-// on MI355X.
-constexpr int64_t DMA_SK_EXCHANGE_STEPS = 10;
+// Cost of the partial-tile exchange of the fast path's stream-K schedule, in
+// k steps of one tile (1.8 us at 4096^3), measured on MI355X: about 0.14
+// per partial tile written and read back (there are at most Gs + T_r), and 2
+// for the fix-up launch.
+constexpr double DMA_SK_STEPS_PER_PIECE = 0.14;
+constexpr double DMA_SK_FIXED_STEPS = 2.0;
 
 }  // namespace
 
@@ -671,18 +673,21 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
 #define LIBGEMM_DMA_SK_RATIO 14
 #endif
 
-// As for the general kernel: worth it when the steps the cut last wave saves
-// exceed the exchange, ceil(T_r * S / G) steps per workgroup instead of S,
-// with G = HGEMM_STREAMK_MAX_GRID compute units.
-bool hgemm_dma_streamk_eligible(const Problem &p) {
+// Worth it when the steps the cut last wave saves exceed the exchange: the
+// last wave takes ceil(T_r * S / Gs) steps per workgroup instead of S, and
+// the exchange grows with the pieces, about Gs + T_r partial tiles (G =
+// HGEMM_STREAMK_MAX_GRID compute units, Gs from streamk_groups).
+bool hgemm_dma_streamk_eligible(const Problem &p, bool force) {
     if (!hgemm_dma_eligible(p)) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
     const int64_t steps = (p.K + LIBGEMM_DMA_BK - 1) / LIBGEMM_DMA_BK;
     const int64_t g = HGEMM_STREAMK_MAX_GRID;
     const int64_t cut = tiles % g;
     if (cut == 0 || tiles >= (int64_t(1) << 24) || steps >= (int64_t(1) << 24)) return false;
-    const int64_t tail = (cut * steps + g - 1) / g;
-    return steps - tail > DMA_SK_EXCHANGE_STEPS;
+    if (force) return true;
+    const int64_t gs = streamk_groups(g, cut, steps, LIBGEMM_DMA_SK_RATIO);
+    const int64_t tail = (cut * steps + gs - 1) / gs;
+    return double(steps - tail) > DMA_SK_STEPS_PER_PIECE * double(gs + cut) + DMA_SK_FIXED_STEPS;
 }
 
 hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream) {

@@ -754,7 +754,7 @@ constexpr int64_t SG_SK_EXCHANGE_STEPS = 8;
 // Worth it when the steps the cut last wave saves exceed the exchange:
 // ceil(T_r * S / G) steps per workgroup instead of S, with G =
 // SGEMM_STREAMK_MAX_GRID workgroups (four per compute unit of MI355X).
-bool sgemm_streamk_eligible(const Problem &p) {
+bool sgemm_streamk_eligible(const Problem &p, bool force) {
     if (p.in != Elem::F32) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
     const int64_t steps = (p.K + BK - 1) / BK;
@@ -762,7 +762,7 @@ bool sgemm_streamk_eligible(const Problem &p) {
     const int64_t cut = tiles % g;
     if (cut == 0 || tiles >= (int64_t(1) << 24) || steps >= (int64_t(1) << 24)) return false;
     const int64_t tail = (cut * steps + g - 1) / g;
-    return steps - tail > SG_SK_EXCHANGE_STEPS;
+    return force || steps - tail > SG_SK_EXCHANGE_STEPS;
 }
 
 hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {

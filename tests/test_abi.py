@@ -210,7 +210,7 @@ def kname(lib, dt, M, N, K, alpha=1.0, oa=0, ob=0, oc=0, lda=None, ldb=None, ldc
 
 @pytest.fixture
 def clean_env(monkeypatch):
-    for v in ("LIBGEMM_F32_VALU", "LIBGEMM_FORCE_GENERAL", "LIBGEMM_NO_SPLITK"):
+    for v in ("LIBGEMM_F32_VALU", "LIBGEMM_FORCE_GENERAL", "LIBGEMM_NO_SPLITK", "LIBGEMM_FORCE_STREAMK"):
         monkeypatch.delenv(v, raising=False)
     return monkeypatch
 
@@ -348,13 +348,27 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "bf16", 5119, 6399, 1001) == "hgemm_mfma"
     # 65 batches of 4 tiles: 256 tiles whole, 4 cut over the grid
     assert kname_ws(lib, "bf16", 300, 290, 1001, batch=65) == "hgemm_mfma_streamk"
-    # aligned: the direct-load kernel's schedule, where the saved steps exceed its exchange
-    assert kname_ws(lib, "bf16", 4096, 4352, 1024) == "hgemm_mfma_dma_streamk"
-    assert kname_ws(lib, "f16", 2048, 2304, 1024, oa=1, ob=1) == "hgemm_mfma_dma_streamk"
+    # aligned: the direct-load kernel's schedule where the saved steps exceed
+    # its exchange (the shapes and outcomes measured on MI355X: 272 tiles of
+    # 32 and 64 steps gain, 16 steps and 136 tiles lose, 288 tiles of 32 tie)
+    assert kname_ws(lib, "bf16", 4096, 4352, 4096) == "hgemm_mfma_dma_streamk"
+    assert kname_ws(lib, "bf16", 4096, 4352, 2048) == "hgemm_mfma_dma_streamk"
+    assert kname_ws(lib, "bf16", 4096, 4352, 1024) == "hgemm_mfma_dma"
+    assert kname_ws(lib, "bf16", 2048, 4352, 2048) == "hgemm_mfma_dma"
+    assert kname_ws(lib, "bf16", 4096, 4608, 2048) == "hgemm_mfma_dma"
+    assert kname_ws(lib, "f16", 2048, 2304, 1024, oa=1, ob=1) == "hgemm_mfma_dma"
     # fewer than 64 tiles: the split-K kernel, workspace or not
     assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
     assert kname_ws(lib, "bf16", 4096, 4352, 256) == "hgemm_mfma_dma"       # 4 steps per tile
     assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # whole waves
+    # LIBGEMM_FORCE_STREAMK=1 skips the cost model, not the structural checks
+    clean_env.setenv("LIBGEMM_FORCE_STREAMK", "1")
+    assert kname_ws(lib, "f16", 2048, 2304, 1024, oa=1, ob=1) == "hgemm_mfma_dma_streamk"
+    assert kname_ws(lib, "bf16", 4096, 4352, 256) == "hgemm_mfma_dma_streamk"
+    assert kname_ws(lib, "bf16", 300, 290, 131) == "hgemm_mfma_streamk"
+    assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # nothing to cut
+    assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
+    clean_env.delenv("LIBGEMM_FORCE_STREAMK")
     # fp32: the general kernel's schedule (128 x 128 tiles, 1024 workgroups)
     assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_streamk"
     assert kname_ws(lib, "f32", 4095, 4097, 129) == "sgemm_mfma"          # 9 steps per tile
