@@ -257,7 +257,9 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
  * written to the workspace and added, in a fixed order, by a second kernel on
  * the same stream, which also applies the epilogue.  It is chosen when the
  * steps saved in the last wave outweigh that exchange (about four k steps of
- * one tile on the general kernel, ten on the direct-load one).
+ * one tile on the general kernels; on the direct-load one about 0.14 k steps
+ * per partial tile plus two).  The environment variable
+ * LIBGEMM_FORCE_STREAMK=1 chooses it wherever it can run (for testing).
  * Results are deterministic run to run; they may differ in rounding from
  * gemm_bf16 (the partial sums are grouped differently), within the same
  * accuracy.  Every other call ignores the workspace and behaves exactly like
