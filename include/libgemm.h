@@ -344,7 +344,8 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
  * gemm_bf16_ws (GEMM_INPUT_BF16) or gemm_f16_ws (GEMM_INPUT_F16) would
  * launch: the names of gemm_kernel_name, or "hgemm_mfma_streamk",
  * "hgemm_mfma_dma_streamk" or "sgemm_mfma_streamk" for the stream-K
- * schedules; "" and NULL as for gemm_kernel_name.  The workspace is only
+ * schedules; "" and NULL as for gemm_kernel_name, whose environment
+ * switches apply, and so does LIBGEMM_FORCE_STREAMK.  The workspace is only
  * checked, never dereferenced. */
 const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K,
                                 float alpha, const void *A, int64_t lda,
