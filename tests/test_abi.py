@@ -393,3 +393,14 @@ def test_workspace_invalid_arguments(lib):
         assert fn(-1, *args[1:], WS, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG
         assert fn(0, *args[1:], WS, n, 0, raise_on_error=False) == lib.OK
         assert fn(*args[:14], 2, *args[15:], WS, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG
+    # gemm_f32_ws: the same checks (it has no c_dtype argument)
+    f32args = args[:14] + args[15:]
+    f = lib.gemm_f32_ws
+    assert f(*f32args, 0, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG              # NULL
+    assert f(*f32args, WS + 16, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG        # misaligned
+    assert f(*f32args, P * 5 - 256, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG    # over C
+    assert f(*f32args, P * 3, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG          # over B
+    assert f(-1, *f32args[1:], WS, n, 0, raise_on_error=False) == lib.ERR_INVALID_ARG
+    assert f(0, *f32args[1:], WS, n, 0, raise_on_error=False) == lib.OK
+    assert kname_ws(lib, "f32", 4095, 4097, 1001, ws=WS + 16) is None
+    assert kname_ws(lib, "f32", 4095, 4097, 1001, ws=3 * GB - 256) is None
