@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libgemm")
-    config.addinivalue_line("markers", "slow: full-size workload, minutes of GPU box time")
+    config.addinivalue_line("markers", "slow: full-size workload, minutes of GPU time")
 
 
 def _gpu_available():
