@@ -54,6 +54,9 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "f8gemm_mfma_dma": "f8gemm_mfma.hip", "f8gemm_mfma": "f8gemm_mfma.hip",
                  "hgemm_mfma_streamk": "hgemm_mfma.hip", "hgemm_mfma_dma_streamk": "hgemm_mfma_dma.hip",
                  "sgemm_mfma_streamk": "sgemm_mfma.hip",
+                 "hgemm_mfma_dma_packed": "hgemm_mfma_dma.hip",
+                 "hgemm_mfma_dma_streamk_packed": "hgemm_mfma_dma.hip",
+                 "sgemm_mfma_dma_packed": "sgemm_mfma.hip",
                  "scale": "scale.hip"}
 
 

@@ -90,7 +90,15 @@ enum class Kernel {
     HgemmStreamK,  // bf16/fp16 general kernel on the stream-K schedule (workspace)
     HgemmDmaStreamK,  // bf16/fp16 direct-load kernel on the stream-K schedule (workspace)
     SgemmStreamK,  // fp32 general kernel on the stream-K schedule (workspace)
+    // operands copied into aligned, zero-padded copies in the workspace first
+    HgemmPackDma,         // then the bf16/fp16 direct-load kernel
+    HgemmPackDmaStreamK,  // then its stream-K schedule
+    SgemmPackDma,         // then the fp32 direct-load kernel
 };
+
+bool is_packed(Kernel k) {
+    return k == Kernel::HgemmPackDma || k == Kernel::HgemmPackDmaStreamK || k == Kernel::SgemmPackDma;
+}
 
 const char *kernel_name(Kernel k) {
     switch (k) {
@@ -109,6 +117,9 @@ const char *kernel_name(Kernel k) {
     case Kernel::HgemmStreamK: return "hgemm_mfma_streamk";
     case Kernel::HgemmDmaStreamK: return "hgemm_mfma_dma_streamk";
     case Kernel::SgemmStreamK: return "sgemm_mfma_streamk";
+    case Kernel::HgemmPackDma: return "hgemm_mfma_dma_packed";
+    case Kernel::HgemmPackDmaStreamK: return "hgemm_mfma_dma_streamk_packed";
+    case Kernel::SgemmPackDma: return "sgemm_mfma_dma_packed";
     }
     return "";
 }
@@ -150,7 +161,10 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::F8Dma: return launch_f8gemm_dma(p, stream);
     case Kernel::HgemmStreamK:
     case Kernel::HgemmDmaStreamK:
-    case Kernel::SgemmStreamK: return hipErrorInvalidValue;  // need the workspace: run()
+    case Kernel::SgemmStreamK:
+    case Kernel::HgemmPackDma:
+    case Kernel::HgemmPackDmaStreamK:
+    case Kernel::SgemmPackDma: return hipErrorInvalidValue;  // need the workspace: run()
     }
     return hipErrorInvalidValue;
 }
@@ -252,14 +266,123 @@ gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K
     return GEMM_OK;
 }
 
-// With a workspace: its checks, and the switch of the 16-bit kernels (the
-// direct-load and the general one) and of the general fp32 kernel to their
-// stream-K schedule where it applies.
+// What a workspace call runs: the kernel, the problem it runs on (a packed
+// copy of the canonical problem, or that problem itself), the operand copies
+// to make first and where everything sits in the workspace.
+struct WsPlan {
+    Kernel k = Kernel::None;
+    Problem q;
+    PackSpec pa{}, pb{};
+    int64_t off_a = 0, off_b = 0;  // byte offsets of the copies (partial tiles at 0)
+};
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Copy of operand X (rows `rows` x cols `cols` of the canonical problem, K
+// contiguous when kmajor) for a packed problem with K padded to kp.
+PackSpec pack_spec(const void *x, int64_t ld, int64_t stride, int64_t batch, bool kmajor,
+                   int64_t mn, int64_t K, int64_t kp, int esize) {
+    const int64_t v = 16 / esize;
+    PackSpec s{};
+    s.src = x;
+    s.ld = ld;
+    s.stride = batch > 1 ? stride : 0;
+    s.batch = batch;
+    s.esize = esize;
+    if (kmajor) {  // mn rows of K contiguous elements
+        s.outer = mn;
+        s.inner = K;
+        s.outer_p = mn;
+        s.inner_p = kp;
+    } else {  // K rows of mn contiguous elements
+        s.outer = K;
+        s.inner = mn;
+        s.outer_p = kp;
+        s.inner_p = round_up(mn, v);
+    }
+    return s;
+}
+
+// The canonical problem p with its operands replaced by packed copies at
+// `a` and `b` (device addresses inside the workspace).
+Problem packed_problem(const Problem &p, const PackSpec &sa, const PackSpec &sb, const void *a,
+                       const void *b, int64_t kp) {
+    Problem q = p;
+    q.packed = true;
+    q.K = kp;
+    q.A = a;
+    q.lda = sa.inner_p;
+    q.sA = sa.stride == 0 ? 0 : sa.outer_p * sa.inner_p;
+    q.span_a = sa.outer_p * sa.inner_p;
+    q.B = b;
+    q.ldb = sb.inner_p;
+    q.sB = sb.stride == 0 ? 0 : sb.outer_p * sb.inner_p;
+    q.span_b = sb.outer_p * sb.inner_p;
+    return q;
+}
+
+// Unaligned operands of a problem big enough to fill the chip (at least 64
+// tiles of 256 x 256 for 16-bit inputs, where smaller problems go to the
+// split-K and stream-K kernels, or 160 tiles of 128 x 128 for fp32) are
+// copied into the workspace so the direct-load kernels can run: the copy
+// reads and writes each operand once at HBM rate, against a general kernel
+// that runs two to three times slower than the direct-load one.  Returns
+// false when the copies (and the partial tiles of a stream-K schedule) do not
+// fit the workspace or the problem does not qualify.
+bool plan_packed(const Problem &p, Kernel k, const void *workspace, size_t bytes, bool force,
+                 WsPlan &w) {
+    const bool h16 = k == Kernel::HgemmMfma || k == Kernel::HgemmStreamK;
+    const bool f32 = k == Kernel::SgemmMfma || k == Kernel::SgemmStreamK;
+    if (!h16 && !f32) return false;
+    const int esize = elem_bytes(p.in);
+    const int64_t tile = h16 ? 256 : 128;
+    const int64_t tiles = ((p.M + tile - 1) / tile) * ((p.N + tile - 1) / tile) * p.batch;
+    if (tiles < (h16 ? 64 : 160)) return false;
+    const int64_t kp = round_up(p.K, 16 / esize);
+    const PackSpec sa = pack_spec(p.A, p.lda, p.sA, p.batch, p.a_kmajor, p.M, p.K, kp, esize);
+    const PackSpec sb = pack_spec(p.B, p.ldb, p.sB, p.batch, p.b_kmajor, p.N, p.K, kp, esize);
+    // the copy kernel addresses a source slice with 32-bit byte offsets
+    const int64_t limit = (int64_t(1) << 31) - 64;
+    if (((sa.outer - 1) * sa.ld + sa.inner) * esize >= limit ||
+        ((sb.outer - 1) * sb.ld + sb.inner) * esize >= limit)
+        return false;
+    const int64_t bytes_a = round_up(packed_bytes(sa), 256), bytes_b = round_up(packed_bytes(sb), 256);
+    // where the copies go once the partial-tile area is known
+    auto place = [&](int64_t partials, Kernel kk) {
+        if (partials + bytes_a + bytes_b > static_cast<int64_t>(bytes)) return false;
+        const char *ws = static_cast<const char *>(workspace);
+        w.k = kk;
+        w.pa = sa;
+        w.pb = sb;
+        w.off_a = partials;
+        w.off_b = partials + bytes_a;
+        w.q = packed_problem(p, sa, sb, ws + w.off_a, ws + w.off_b, kp);
+        return true;
+    };
+    if (!place(0, h16 ? Kernel::HgemmPackDma : Kernel::SgemmPackDma)) return false;
+    if (h16) {
+        if (!hgemm_dma_eligible(w.q)) return false;
+        if (hgemm_dma_streamk_eligible(w.q, force)) {
+            const int64_t partials = round_up(hgemm_dma_streamk_bytes(w.q), 256);
+            WsPlan keep = w;
+            if (!place(partials, Kernel::HgemmPackDmaStreamK)) w = keep;  // no room: plain schedule
+        }
+        return true;
+    }
+    return sgemm_dma_eligible(w.q);
+}
+
+// With a workspace: its checks, then the plan.  Unaligned operands of large
+// problems are copied into aligned buffers for the direct-load kernels
+// (plan_packed); otherwise the 16-bit kernels (the direct-load and the
+// general one) and the general fp32 kernel switch to their stream-K schedule
+// where it applies.
 gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, int orderA,
                             int64_t lda, int orderB, int64_t ldb, int orderC, int64_t ldc,
                             int64_t strideA, int64_t strideB, int64_t strideC,
                             const void *bias, int64_t strideBias, const void *A, const void *B,
-                            const void *C, const void *workspace, size_t bytes, Kernel &k) {
+                            const void *C, const void *workspace, size_t bytes, WsPlan &w) {
+    w.q = p;
     if (bytes == 0) return GEMM_OK;
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return GEMM_ERR_INVALID_ARG;
@@ -273,6 +396,8 @@ gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, i
         return GEMM_ERR_INVALID_ARG;
     const bool room = bytes >= static_cast<size_t>(hgemm_streamk_workspace_bytes());
     const bool force = force_streamk();
+    Kernel &k = w.k;
+    if (room && !force_general() && plan_packed(p, k, workspace, bytes, force, w)) return GEMM_OK;
     if (k == Kernel::HgemmMfma && !force_general() && room && hgemm_streamk_eligible(p, force))
         k = Kernel::HgemmStreamK;
     else if (k == Kernel::HgemmDma && room && hgemm_dma_streamk_eligible(p, force))
@@ -282,24 +407,39 @@ gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, i
     return GEMM_OK;
 }
 
+hipError_t launch_planned(const WsPlan &w, void *workspace, hipStream_t stream) {
+    char *ws = static_cast<char *>(workspace);
+    if (is_packed(w.k)) {
+        hipError_t e = launch_pack(w.pa, ws + w.off_a, stream);
+        if (e == hipSuccess) e = launch_pack(w.pb, ws + w.off_b, stream);
+        if (e != hipSuccess) return e;
+    }
+    switch (w.k) {
+    case Kernel::HgemmStreamK: return launch_hgemm_streamk(w.q, workspace, stream);
+    case Kernel::HgemmDmaStreamK:
+    case Kernel::HgemmPackDmaStreamK: return launch_hgemm_dma_streamk(w.q, workspace, stream);
+    case Kernel::SgemmStreamK: return launch_sgemm_streamk(w.q, workspace, stream);
+    case Kernel::HgemmPackDma: return launch_hgemm_dma(w.q, stream);
+    case Kernel::SgemmPackDma: return launch_sgemm_dma(w.q, stream);
+    default: return launch(w.k, w.q, stream);
+    }
+}
+
 gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                   float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
                   int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
                   hipStream_t stream, void *workspace = nullptr, size_t workspace_bytes = 0) {
     Problem p;
-    Kernel k;
+    WsPlan w;
     gemm_status_t st =
         plan(in, in_b, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC,
-             batch, strideA, strideB, strideC, bias, strideBias, act, p, k);
-    if (st == GEMM_OK && k != Kernel::None)
+             batch, strideA, strideB, strideC, bias, strideBias, act, p, w.k);
+    if (st == GEMM_OK && w.k != Kernel::None)
         st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
-                           strideC, bias, strideBias, A, B, C, workspace, workspace_bytes, k);
-    if (st != GEMM_OK || k == Kernel::None) return st;
-    const hipError_t err = k == Kernel::HgemmStreamK      ? launch_hgemm_streamk(p, workspace, stream)
-                           : k == Kernel::HgemmDmaStreamK ? launch_hgemm_dma_streamk(p, workspace, stream)
-                           : k == Kernel::SgemmStreamK    ? launch_sgemm_streamk(p, workspace, stream)
-                                                          : launch(k, p, stream);
+                           strideC, bias, strideBias, A, B, C, workspace, workspace_bytes, w);
+    if (st != GEMM_OK || w.k == Kernel::None) return st;
+    const hipError_t err = launch_planned(w, workspace, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -511,15 +651,15 @@ const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K
     if (ein == Elem::F32) c_dtype = GEMM_DTYPE_SAME;  // gemm_f32_ws has no c_dtype
     if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return nullptr;
     Problem p;
-    Kernel k;
+    WsPlan w;
     gemm_status_t st =
         plan(ein, ein, out_type(ein, c_dtype), M, N, K, alpha, A, lda, orderA, B, ldb, orderB,
              beta, const_cast<void *>(C), ldc, orderC, batch, strideA, strideB, strideC, nullptr,
-             0, GEMM_ACT_NONE, p, k);
-    if (st == GEMM_OK && k != Kernel::None)
+             0, GEMM_ACT_NONE, p, w.k);
+    if (st == GEMM_OK && w.k != Kernel::None)
         st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
-                           strideC, nullptr, 0, A, B, C, workspace, workspace_bytes, k);
-    return st == GEMM_OK ? kernel_name(k) : nullptr;
+                           strideC, nullptr, 0, A, B, C, workspace, workspace_bytes, w);
+    return st == GEMM_OK ? kernel_name(w.k) : nullptr;
 }
 
 }  // extern "C"

@@ -50,6 +50,7 @@ struct DmaArgs {
     TileGrid grid;
     int vec_c;
     Epilogue epi;
+    int64_t span_a, span_b;  // elements of one slice of A and of B the loads may touch
 };
 
 // Swizzle of a K-contiguous panel row (CH 16-byte chunks per row): a

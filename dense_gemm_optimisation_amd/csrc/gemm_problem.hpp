@@ -34,6 +34,13 @@ struct Problem {
     int64_t batch, sA, sB, sC;  // batch count and per-batch strides (elements)
     Elem in, in_b, out;         // types of A, of B (differs from A's only for 8-bit), of C
     Epilogue epi;               // bias and activation applied before the store
+    // packed: A and B are zero-padded copies whose contiguous extents are
+    // whole 16-byte chunks (K itself padded when it is contiguous), so the
+    // direct-load kernels may read whole chunks past M, N or K; span_a and
+    // span_b are then the elements of one slice of each copy (0 otherwise:
+    // the operand's own extent).
+    bool packed = false;
+    int64_t span_a = 0, span_b = 0;
 };
 
 // Element size in bytes.
@@ -48,6 +55,30 @@ inline bool vec16_ok(const void *p, int64_t ld, int64_t stride, int esize) {
     const int64_t per = 16 / esize;
     return (reinterpret_cast<uintptr_t>(p) % 16) == 0 && ld % per == 0 && stride % per == 0;
 }
+
+// Elements of one slice of operand A (B) that the kernels may read: the
+// matrix's own extent, or the whole padded copy of a packed problem.
+inline int64_t operand_span_a(const Problem &p) {
+    if (p.span_a) return p.span_a;
+    return p.a_kmajor ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
+}
+inline int64_t operand_span_b(const Problem &p) {
+    if (p.span_b) return p.span_b;
+    return p.b_kmajor ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
+}
+
+// An operand copy for a packed problem: `outer` rows of `inner` contiguous
+// elements of `esize` bytes (leading dimension ld, `batch` slices `stride`
+// apart, stride 0 = one shared slice) become outer_p x inner_p, zero-padded,
+// inner_p * esize a multiple of 16, slices outer_p * inner_p apart.
+struct PackSpec {
+    const void *src;
+    int64_t outer, inner, ld, stride, batch;
+    int64_t outer_p, inner_p;
+    int esize;
+};
+int64_t packed_bytes(const PackSpec &s);
+hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream);
 
 // Kernel launchers; each returns the launch status.
 hipError_t launch_sgemm(const Problem &p, hipStream_t stream);       // fp32 on the vector ALUs
@@ -105,6 +136,8 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream);
 // holds.
 bool hgemm_dma_streamk_eligible(const Problem &p, bool force = false);
 hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream);
+// Workspace bytes launch_hgemm_dma_streamk uses for p (its partial tiles).
+int64_t hgemm_dma_streamk_bytes(const Problem &p);
 // bf16/fp16 split-K inside a workgroup, for problems with few output tiles
 // and a long K (hgemm_splitk_eligible()).
 bool hgemm_splitk_eligible(const Problem &p);

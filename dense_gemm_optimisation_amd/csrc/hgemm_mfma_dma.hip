@@ -91,10 +91,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
 
     OpA opa;
     OpB opb;
-    const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
-    const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
-    opa.init(p.A + t.batch * p.sA, p.lda, p.M, m0, span_a, wave, lane);
-    opb.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, span_b, wave, lane);
+    opa.init(p.A + t.batch * p.sA, p.lda, p.M, m0, p.span_a, wave, lane);
+    opb.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, p.span_b, wave, lane);
 
     LDS char *lds = (LDS char *)smem;  // generic -> LDS address space
     const int64_t steps = (p.K + BK - 1) / BK;
@@ -237,10 +235,8 @@ __device__ __forceinline__ int dma_tile_steps(const DmaArgs &p, LDS char *lds, c
 
     OpA opa;
     OpB opb;
-    const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
-    const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
-    opa.init(p.A + t.batch * p.sA, p.lda, p.M, m0, span_a, wave, lane);
-    opb.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, span_b, wave, lane);
+    opa.init(p.A + t.batch * p.sA, p.lda, p.M, m0, p.span_a, wave, lane);
+    opb.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, p.span_b, wave, lane);
 
     const int64_t steps = ke - kb;
 
@@ -599,11 +595,6 @@ hipError_t launch_sk_layout(const Problem &p, DmaArgs &a, DmaStreamK &sk, int64_
                       : launch_sk<T, OUT, false, false>(a, sk, grid, stream);
 }
 
-int64_t span_of(int64_t rows, int64_t cols, bool row_contig, int64_t ld) {
-    // rows x cols with `cols` contiguous when row_contig
-    return row_contig ? (rows - 1) * ld + cols : (cols - 1) * ld + rows;
-}
-
 }  // namespace
 
 // The fast path needs every operand chunk either fully inside or fully
@@ -614,10 +605,9 @@ bool hgemm_dma_eligible(const Problem &p) {
     if (p.in != Elem::BF16 && p.in != Elem::F16) return false;
     const int64_t sa = p.batch > 1 ? p.sA : 0, sb = p.batch > 1 ? p.sB : 0;
     if (!vec16_ok(p.A, p.lda, sa, 2) || !vec16_ok(p.B, p.ldb, sb, 2)) return false;
-    if ((p.a_kmajor ? p.K : p.M) % 8 || (p.b_kmajor ? p.K : p.N) % 8) return false;
+    if (!p.packed && ((p.a_kmajor ? p.K : p.M) % 8 || (p.b_kmajor ? p.K : p.N) % 8)) return false;
     const int64_t limit = int64_t(1) << 30;
-    if (2 * span_of(p.M, p.K, p.a_kmajor, p.lda) >= limit) return false;
-    if (2 * span_of(p.K, p.N, !p.b_kmajor, p.ldb) >= limit) return false;
+    if (2 * operand_span_a(p) >= limit || 2 * operand_span_b(p) >= limit) return false;
     return true;
 }
 
@@ -645,6 +635,8 @@ DmaArgs make_dma_args(const Problem &p, int32_t xcds) {
     const int cw = 16 / esz;
     a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % 16) == 0 && p.ldc % cw == 0 && a.sC % cw == 0;
     a.epi = p.epi;
+    a.span_a = operand_span_a(p);
+    a.span_b = operand_span_b(p);
     return a;
 }
 
@@ -690,21 +682,33 @@ bool hgemm_dma_streamk_eligible(const Problem &p, bool force) {
     return double(steps - tail) > DMA_SK_STEPS_PER_PIECE * double(gs + cut) + DMA_SK_FIXED_STEPS;
 }
 
-hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream) {
-    DmaArgs a = make_dma_args(p, 1);  // the work order itself spreads tiles over the dies
-    const int64_t tiles = a.grid.count();
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = HGEMM_STREAMK_MAX_GRID;
-    const int64_t G = cus < HGEMM_STREAMK_MAX_GRID ? cus : HGEMM_STREAMK_MAX_GRID;
+namespace {
+
+// The stream-K split of p: one workgroup per compute unit of MI355X (G =
+// HGEMM_STREAMK_MAX_GRID; on a part with fewer units the schedule is still
+// correct, the workgroups just do not all run at once).
+DmaStreamK dma_streamk_split(const Problem &p) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+    const int64_t G = HGEMM_STREAMK_MAX_GRID;
     DmaStreamK sk{};
-    sk.partials = static_cast<float *>(workspace);
     sk.steps = (p.K + LIBGEMM_DMA_BK - 1) / LIBGEMM_DMA_BK;
     sk.dp_tiles = tiles / G * G;
     sk.iters = (tiles - sk.dp_tiles) * sk.steps;
     sk.groups = sk.iters == 0 ? 0 : streamk_groups(G, tiles - sk.dp_tiles, sk.steps, LIBGEMM_DMA_SK_RATIO);
+    return sk;
+}
+
+}  // namespace
+
+int64_t hgemm_dma_streamk_bytes(const Problem &p) {
+    return 2 * dma_streamk_split(p).groups * int64_t(SK_SLOT) * 4;
+}
+
+hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+    DmaArgs a = make_dma_args(p, 1);  // the work order itself spreads tiles over the dies
+    const int64_t G = HGEMM_STREAMK_MAX_GRID;
+    DmaStreamK sk = dma_streamk_split(p);
+    sk.partials = static_cast<float *>(workspace);
     const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
     if (grid == 0) return hipSuccess;
     const bool bf = p.in == Elem::BF16;

@@ -1,0 +1,138 @@
+// Copy of an operand into a zero-padded, 16-byte aligned layout, so that a
+// problem whose operands are not aligned can run on the direct-load kernels.
+//
+// The source is `outer` rows of `inner` contiguous elements (leading
+// dimension ld, `batch` slices `stride` elements apart); the destination is
+// `outer_p` >= outer rows of `inner_p` >= inner elements, inner_p a multiple
+// of 16 bytes, slices outer_p * inner_p apart (or one slice when the source
+// stride is 0: a shared operand stays shared).  Rows and columns beyond the
+// source extent are zero, which is the zero fill at matrix edges that
+// section 5.2 of "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site) does with
+// predicated loads, done once per operand instead of on every tile.
+//
+// One thread writes one 16-byte chunk.  The source chunk may start at any
+// element boundary: the kernel reads the 4-byte aligned words that cover it
+// with buffer loads (the buffer's range check keeps every read inside the
+// operand) and shifts them into place; the last chunk of a slice is read
+// element by element, so no read depends on how the range check treats a
+// load that straddles the end of the buffer.
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_problem.hpp"
+
+namespace libgemm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct PackArgs {
+    const char *src;
+    char *dst;
+    int64_t outer, inner, ld, stride;  // source extent, elements
+    int64_t outer_p, inner_p;          // destination extent, elements
+    int64_t batch;
+    int64_t chunks_per_row;            // inner_p * esize / 16
+};
+
+template <int ESIZE>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+    constexpr int PER = 16 / ESIZE;  // elements per chunk
+    const int64_t per_slice = a.outer_p * a.chunks_per_row;
+    const int64_t total = per_slice * a.batch;
+    for (int64_t g = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; g < total;
+         g += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t b = g / per_slice;
+        const int64_t r = g - b * per_slice;
+        const int64_t o = r / a.chunks_per_row;
+        const int64_t e0 = (r - o * a.chunks_per_row) * PER;
+        u32x4 out = {0u, 0u, 0u, 0u};
+        if (o < a.outer && e0 < a.inner) {
+            const char *slice = a.src + b * a.stride * ESIZE;
+            // the slice as a raw buffer from its first 4-byte boundary
+            const uintptr_t base = reinterpret_cast<uintptr_t>(slice);
+            const uintptr_t base4 = base & ~uintptr_t(3);
+            const int64_t span = (a.outer - 1) * a.ld + a.inner;  // elements of the slice
+            const int64_t bytes = span * ESIZE + int64_t(base - base4);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                reinterpret_cast<void *>(base4), 0, static_cast<int>(bytes), 0x00020000);
+            const int64_t off = (o * a.ld + e0) * ESIZE + int64_t(base - base4);  // byte offset
+            const int64_t off4 = off & ~int64_t(3);
+            const int nvalid = a.inner - e0 < PER ? int(a.inner - e0) : PER;
+            if (off4 + 20 <= bytes) {
+                const u32x4 w = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(off4), 0, 0));
+                if (off == off4) {
+                    out = w;
+                } else {
+                    // 16-bit elements at a 2-byte offset: one more word, then
+                    // each output word takes the high half of one word and the
+                    // low half of the next
+                    const uint32_t w4 = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(off4 + 16), 0, 0);
+                    out[0] = __builtin_amdgcn_alignbyte(w[1], w[0], 2);
+                    out[1] = __builtin_amdgcn_alignbyte(w[2], w[1], 2);
+                    out[2] = __builtin_amdgcn_alignbyte(w[3], w[2], 2);
+                    out[3] = __builtin_amdgcn_alignbyte(w4, w[3], 2);
+                }
+            } else {
+                // end of the slice: element by element, all inside it
+                uint32_t e[PER];
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    e[i] = 0u;
+                    if (i < nvalid) {
+                        if (ESIZE == 2)
+                            e[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<int>(off + 2 * i), 0, 0);
+                        else
+                            e[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(off + 4 * i), 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    out[q] = ESIZE == 2 ? (e[2 * q] & 0xffffu) | (e[2 * q + 1] << 16) : e[q];
+            }
+            // elements past the end of the row are zero
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                if (i >= nvalid) {
+                    if (ESIZE == 2)
+                        out[i / 2] &= (i & 1) ? 0x0000ffffu : 0xffff0000u;
+                    else
+                        out[i] = 0u;
+                }
+            }
+        }
+        *reinterpret_cast<u32x4 *>(a.dst + g * 16) = out;
+    }
+}
+
+}  // namespace
+
+int64_t packed_bytes(const PackSpec &s) {
+    return (s.stride == 0 && s.batch > 1 ? 1 : s.batch) * s.outer_p * s.inner_p * s.esize;
+}
+
+hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream) {
+    PackArgs a{};
+    a.src = static_cast<const char *>(s.src);
+    a.dst = static_cast<char *>(dst);
+    a.outer = s.outer;
+    a.inner = s.inner;
+    a.ld = s.ld;
+    a.stride = s.stride;
+    a.outer_p = s.outer_p;
+    a.inner_p = s.inner_p;
+    a.batch = s.stride == 0 && s.batch > 1 ? 1 : s.batch;
+    a.chunks_per_row = s.inner_p * s.esize / 16;
+    const int64_t total = a.outer_p * a.chunks_per_row * a.batch;
+    if (total == 0) return hipSuccess;
+    // enough workgroups to fill the chip several times over; the loop covers the rest
+    const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
+    void *args[] = {&a};
+    const void *k = s.esize == 2 ? reinterpret_cast<const void *>(&pack_kernel<2>)
+                                 : reinterpret_cast<const void *>(&pack_kernel<4>);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(blocks)), dim3(256), args, 0, stream);
+}
+
+}  // namespace libgemm

@@ -66,6 +66,7 @@ struct SgemmArgs {
     TileGrid grid;
     int vec_a, vec_b, vec_c;  // 16-byte vector access allowed for the operand
     Epilogue epi;
+    int64_t span_a, span_b;   // elements of one slice of A and of B the direct loads may touch
 };
 
 // Four consecutive elements x[0..3] of one operand row, zero outside
@@ -380,10 +381,8 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p)
 
     DmaPanel<A_KMAJOR> da;
     DmaPanel<B_KMAJOR> db;
-    const int64_t span_a = A_KMAJOR ? (p.M - 1) * p.lda + p.K : (p.K - 1) * p.lda + p.M;
-    const int64_t span_b = B_KMAJOR ? (p.N - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + p.N;
-    da.init(p.A + t.batch * p.sA, p.lda, p.M, m0, span_a, wave, lane);
-    db.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, span_b, wave, lane);
+    da.init(p.A + t.batch * p.sA, p.lda, p.M, m0, p.span_a, wave, lane);
+    db.init(p.B + t.batch * p.sB, p.ldb, p.N, n0, p.span_b, wave, lane);
     auto addr = [&](int buf, int op) {
         return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS float *)&smem[buf][op][0]));
     };
@@ -453,11 +452,6 @@ hipError_t launch(const SgemmArgs &a0, bool direct, hipStream_t stream) {
                             : reinterpret_cast<const void *>(&sgemm_mfma_kernel<AK, BK_>);
     return hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.grid.count())), dim3(THREADS), args, 0,
                            stream);
-}
-
-int64_t span_of(int64_t rows, int64_t cols, bool row_contig, int64_t ld) {
-    // rows x cols with `cols` contiguous when row_contig
-    return row_contig ? (rows - 1) * ld + cols : (cols - 1) * ld + rows;
 }
 
 // Stream-K schedule of the general fp32 kernel (section 12.5 of "CUDA GEMM
@@ -674,10 +668,9 @@ bool sgemm_dma_eligible(const Problem &p) {
     if (p.in != Elem::F32) return false;
     const int64_t sa = p.batch > 1 ? p.sA : 0, sb = p.batch > 1 ? p.sB : 0;
     if (!vec16_ok(p.A, p.lda, sa, 4) || !vec16_ok(p.B, p.ldb, sb, 4)) return false;
-    if ((p.a_kmajor ? p.K : p.M) % 4 || (p.b_kmajor ? p.K : p.N) % 4) return false;
+    if (!p.packed && ((p.a_kmajor ? p.K : p.M) % 4 || (p.b_kmajor ? p.K : p.N) % 4)) return false;
     const int64_t limit = int64_t(1) << 31;
-    return 4 * span_of(p.M, p.K, p.a_kmajor, p.lda) < limit &&
-           4 * span_of(p.K, p.N, !p.b_kmajor, p.ldb) < limit;
+    return 4 * operand_span_a(p) < limit && 4 * operand_span_b(p) < limit;
 }
 
 namespace {
@@ -703,6 +696,8 @@ SgemmArgs make_args(const Problem &p) {
     a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 4);
     a.vec_c = vec16_ok(p.C, p.ldc, a.sC, 4);
     a.epi = p.epi;
+    a.span_a = operand_span_a(p);
+    a.span_b = operand_span_b(p);
     return a;
 }
 

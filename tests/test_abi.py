@@ -335,19 +335,26 @@ def kname_ws(lib, dt, M, N, K, ws=WS, nbytes=None, **kw):
 
 
 def test_streamk_kernel_choice(lib, clean_env):
-    # unaligned (general kernel), 272 tiles: stream-K
-    assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_streamk"
+    # unaligned with at least 64 tiles: operands copied into the workspace,
+    # then the direct-load kernel (272 tiles of 16 k-steps: the cut tail
+    # saves less than its exchange costs) or its stream-K schedule (64 steps)
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_dma_packed"
+    assert kname_ws(lib, "bf16", 4095, 4351, 4095) == "hgemm_mfma_dma_streamk_packed"
+    assert kname_ws(lib, "f16", 4095, 4095, 1001, oa=1, ob=1) == "hgemm_mfma_dma_packed"
+    # fewer than 64 tiles: the general kernel's stream-K schedule
     assert kname_ws(lib, "f16", 300, 290, 8193) == "hgemm_mfma_streamk"
     # workspace too small, or absent: the plain general kernel
     assert kname_ws(lib, "bf16", 4095, 4097, 1001, nbytes=1 << 20) == "hgemm_mfma"
     assert kname_ws(lib, "bf16", 4095, 4097, 1001, ws=0, nbytes=0) == "hgemm_mfma"
-    # whole waves (256 tiles), too little work, or the aligned fast path
-    assert kname_ws(lib, "bf16", 4095, 4095, 1001) == "hgemm_mfma"
+    # copies larger than the workspace (16384 x 4104 bf16 is 134 MB): the
+    # general kernel (4096 tiles are whole waves, nothing to cut)
+    assert kname_ws(lib, "bf16", 16383, 16383, 4097) == "hgemm_mfma"
+    # too little work for stream-K on few tiles
     assert kname_ws(lib, "bf16", 300, 290, 131) == "hgemm_mfma"
     # 500 tiles: the last wave (244 tiles) is nearly full, the exchange would cost more
-    assert kname_ws(lib, "bf16", 5119, 6399, 1001) == "hgemm_mfma"
-    # 65 batches of 4 tiles: 256 tiles whole, 4 cut over the grid
-    assert kname_ws(lib, "bf16", 300, 290, 1001, batch=65) == "hgemm_mfma_streamk"
+    assert kname_ws(lib, "bf16", 5119, 6399, 1001) == "hgemm_mfma_dma_packed"
+    # 65 batches of 4 tiles: copied, 256 tiles whole and 4 cut over the grid
+    assert kname_ws(lib, "bf16", 300, 290, 1001, batch=65) == "hgemm_mfma_dma_streamk_packed"
     # aligned: the direct-load kernel's schedule where the saved steps exceed
     # its exchange (the shapes and outcomes measured on MI355X: 272 tiles of
     # 32 and 64 steps gain, 16 steps and 136 tiles lose, 288 tiles of 32 tie)
@@ -368,10 +375,15 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "bf16", 300, 290, 131) == "hgemm_mfma_streamk"
     assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # nothing to cut
     assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_dma_streamk_packed"
     clean_env.delenv("LIBGEMM_FORCE_STREAMK")
-    # fp32: the general kernel's schedule (128 x 128 tiles, 1024 workgroups)
-    assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_streamk"
-    assert kname_ws(lib, "f32", 4095, 4097, 129) == "sgemm_mfma"          # 9 steps per tile
+    # fp32: unaligned with at least 160 tiles of 128 x 128 is copied for the
+    # direct-load kernel; fewer tiles use the general kernel's schedule
+    # (128 x 128 tiles, 1024 workgroups)
+    assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_dma_packed"
+    assert kname_ws(lib, "f32", 4095, 4097, 129) == "sgemm_mfma_dma_packed"
+    assert kname_ws(lib, "f32", 1500, 1300, 2001) == "sgemm_mfma_streamk"   # 132 tiles
+    assert kname_ws(lib, "f32", 1500, 1300, 129) == "sgemm_mfma"            # 9 steps per tile
     assert kname_ws(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma_dma"     # aligned
     assert kname_ws(lib, "f32", 4095, 4097, 1001, nbytes=1 << 20) == "sgemm_mfma"
     # K = 0 scales C

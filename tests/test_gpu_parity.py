@@ -688,8 +688,10 @@ def test_streamk_integers_bit_exact(dt):
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_streamk_whole_waves_and_cut_tail(dt):
     # 65 batches of 2 x 2 tiles: 256 tiles computed whole, 4 cut over the
-    # grid (16 pieces each); beta = 0.5, so the fix-up also reads C
-    check(P(f"streamk-dp-{dt}", dt, 300, 290, 1001, beta=0.5, batch=65),
+    # grid; beta = 0.5, so the fix-up also reads C.  K = 3001 makes the
+    # aligned copies (233 MB) larger than the workspace, so the general
+    # kernel runs on the caller's operands.
+    check(P(f"streamk-dp-{dt}", dt, 300, 290, 3001, beta=0.5, batch=65),
           kernel="hgemm_mfma_streamk", seed=84, use_workspace=True, repeat=2)
 
 
@@ -772,8 +774,10 @@ def test_f32_streamk_integers_bit_exact():
     assert res.max_err == 0.0
 
 
-def test_f32_streamk_edge_config_sampled():
-    check(workloads.config("f32_edge"), kernel="sgemm_mfma_streamk", sample="auto",
+def test_f32_packed_edge_config_sampled():
+    # the unaligned 4095 x 4097 x 1001 fp32 problem with a workspace: copied
+    # to aligned operands, then the direct-load kernel
+    check(workloads.config("f32_edge"), kernel="sgemm_mfma_dma_packed", sample="auto",
           use_workspace=True, repeat=2)
 
 
@@ -786,7 +790,101 @@ def test_streamk_workspace_too_small_is_the_plain_call():
     assert np.array_equal(plain, small)
 
 
-def test_streamk_edge_config_sampled():
-    # the unaligned 4095 x 4097 x 1001 problem: 272 tiles on 256 compute units
-    check(workloads.config("bf16_edge"), kernel="hgemm_mfma_streamk", sample="auto",
+def test_packed_edge_config_sampled():
+    # the unaligned 4095 x 4097 x 1001 problem with a workspace: copied to
+    # aligned, zero-padded operands, then the direct-load kernel
+    check(workloads.config("bf16_edge"), kernel="hgemm_mfma_dma_packed", sample="auto",
           use_workspace=True, repeat=2)
+
+
+# ------------------------------------------------------------------ packed operands (workspace entry points)
+
+# Problems with unaligned operands and enough tiles for the direct-load
+# kernels: the workspace entry points copy A and B into zero-padded aligned
+# buffers first.  Extents and leading dimensions are odd, so every operand
+# row starts at a different alignment, and K is padded (1001 -> 1008).
+PACK_SHAPES = [(2047, 2049, 1001), (2305, 1999, 515)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", PACK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_packed_16bit(dt, shape, orders):
+    M, N, K = shape
+    oa, ob = orders
+    check(P(f"packed-{dt}", dt, M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
+          kernel="hgemm_mfma_dma_packed", seed=M + N + K + 3, use_workspace=True, repeat=2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("orders", [(ROW, ROW), (COL, COL)], ids=lambda o: "%d%d" % o)
+def test_packed_16bit_padded_ld_and_misaligned_bases(dt, orders):
+    # aligned extents but padded odd leading dimensions, then misaligned base
+    # pointers with leading dimensions that are multiples of 8
+    oa, ob = orders
+    M, N, K = 2048, 2304, 1024
+    lda = (K if oa == ROW else M) + 3
+    ldb = (N if ob == ROW else K) + 5
+    check(P(f"packed-ld-{dt}", dt, M, N, K, beta=0.5, order_a=oa, order_b=ob, lda=lda, ldb=ldb,
+            ldc=N + 7), kernel="hgemm_mfma_dma_packed", seed=101, use_workspace=True)
+    check(P(f"packed-base-{dt}", dt, M, N, K, alpha=-1.5, order_a=oa, order_b=ob),
+          kernel="hgemm_mfma_dma_packed", seed=102, use_workspace=True, base_offset=(1, 3, 1))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_packed_16bit_batches_fp32_output_and_col_major_c(dt):
+    # 65 batches of 2 x 2 tiles: copied, then the direct-load stream-K
+    # schedule (256 tiles whole, 4 cut); a batch sharing one B (stride 0);
+    # fp32 output; a column-major C (computed as C^T = B^T A^T)
+    check(P(f"packed-batch-{dt}", dt, 300, 290, 1001, beta=0.5, batch=65),
+          kernel="hgemm_mfma_dma_streamk_packed", seed=103, use_workspace=True, repeat=2)
+    check(P(f"packed-shared-b-{dt}", dt, 1025, 777, 333, batch=9, stride_b=0),
+          kernel="hgemm_mfma_dma_packed", seed=104, use_workspace=True)
+    check(P(f"packed-f32out-{dt}", dt, 2047, 2049, 1001, c_dtype="f32", beta=1.0),
+          kernel="hgemm_mfma_dma_packed", seed=105, use_workspace=True)
+    check(P(f"packed-colC-{dt}", dt, 2049, 2047, 1001, order_c=COL, ldc=2051, beta=0.5),
+          kernel="hgemm_mfma_dma_packed", seed=106, use_workspace=True)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_packed_16bit_integers_bit_exact(dt):
+    p = P(f"packed-int-{dt}", dt, 2047, 2049, 1001, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="hgemm_mfma_dma_packed", host=_int_host(p, np.random.default_rng(107)),
+                   use_workspace=True)
+    assert res.max_err == 0.0 and res.max_ulp == 0
+
+
+def test_packed_16bit_forced_streamk(force_streamk):
+    # every tile of a 72-tile problem cut across the grid, on the copies
+    p = P("packed-sk-bf16", "bf16", 2047, 2049, 1001, alpha=0.75, beta=0.5, order_b=COL)
+    check(p, kernel="hgemm_mfma_dma_streamk_packed", seed=108, use_workspace=True, repeat=2)
+    res, _ = check(p, kernel="hgemm_mfma_dma_streamk_packed",
+                   host=_int_host(p, np.random.default_rng(109)), use_workspace=True)
+    assert res.max_ulp == 0
+
+
+F32_PACK_SHAPES = [(1537, 1665, 257), (2049, 1283, 1001)]
+
+
+@pytest.mark.parametrize("shape", F32_PACK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_packed_f32(shape, orders):
+    M, N, K = shape
+    oa, ob = orders
+    check(P("packed-f32", "f32", M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
+          kernel="sgemm_mfma_dma_packed", seed=M + N + K + 5, use_workspace=True, repeat=2)
+
+
+def test_packed_f32_bases_batch_col_major_c_and_integers():
+    check(P("packed-f32-base", "f32", 1664, 1664, 256, beta=0.5),
+          kernel="sgemm_mfma_dma_packed", seed=110, use_workspace=True, base_offset=(1, 2, 0))
+    check(P("packed-f32-batch", "f32", 515, 517, 203, batch=8, beta=1.0),
+          kernel="sgemm_mfma_dma_packed", seed=111, use_workspace=True)
+    check(P("packed-f32-colC", "f32", 1665, 1537, 257, order_c=COL, ldc=1669, beta=0.5),
+          kernel="sgemm_mfma_dma_packed", seed=112, use_workspace=True)
+    p = P("packed-f32-int", "f32", 1537, 1665, 257, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="sgemm_mfma_dma_packed", host=_int_host(p, np.random.default_rng(113)),
+                   use_workspace=True)
+    assert res.max_err == 0.0
