@@ -274,6 +274,7 @@ struct WsPlan {
     Problem q;
     PackSpec pa{}, pb{};
     int64_t off_a = 0, off_b = 0;  // byte offsets of the copies (partial tiles at 0)
+    int64_t used = 0;              // workspace bytes the plan touches
 };
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -356,6 +357,7 @@ bool plan_packed(const Problem &p, Kernel k, const void *workspace, size_t bytes
         w.pb = sb;
         w.off_a = partials;
         w.off_b = partials + bytes_a;
+        w.used = w.off_b + bytes_b;
         w.q = packed_problem(p, sa, sb, ws + w.off_a, ws + w.off_b, kp);
         return true;
     };
@@ -372,17 +374,13 @@ bool plan_packed(const Problem &p, Kernel k, const void *workspace, size_t bytes
     return sgemm_dma_eligible(w.q);
 }
 
-// With a workspace: its checks, then the plan.  Unaligned operands of large
-// problems are copied into aligned buffers for the direct-load kernels
-// (plan_packed); otherwise the 16-bit kernels (the direct-load and the
-// general one) and the general fp32 kernel switch to their stream-K schedule
-// where it applies.
-gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, int orderA,
-                            int64_t lda, int orderB, int64_t ldb, int orderC, int64_t ldc,
-                            int64_t strideA, int64_t strideB, int64_t strideC,
-                            const void *bias, int64_t strideBias, const void *A, const void *B,
-                            const void *C, const void *workspace, size_t bytes, WsPlan &w) {
-    w.q = p;
+// The checks of a workspace argument: 256-byte aligned, not NULL when it has
+// bytes, and not overlapping A, B, C or the bias.
+gemm_status_t check_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, int orderA,
+                              int64_t lda, int orderB, int64_t ldb, int orderC, int64_t ldc,
+                              int64_t strideA, int64_t strideB, int64_t strideC,
+                              const void *bias, int64_t strideBias, const void *A, const void *B,
+                              const void *C, const void *workspace, size_t bytes) {
     if (bytes == 0) return GEMM_OK;
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return GEMM_ERR_INVALID_ARG;
@@ -394,16 +392,45 @@ gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, i
         overlap(rw, range_of(B, span(K, N, orderB, ldb), p.batch, strideB, esz)) ||
         (bias != nullptr && overlap(rw, range_of(bias, N, p.batch, strideBias, esz))))
         return GEMM_ERR_INVALID_ARG;
+    return GEMM_OK;
+}
+
+// The plan for a checked workspace of `bytes` bytes at `workspace` (only its
+// address is used, to place the operand copies).  Unaligned operands of large
+// problems are copied into aligned buffers for the direct-load kernels
+// (plan_packed); otherwise the 16-bit kernels (the direct-load and the
+// general one) and the general fp32 kernel switch to their stream-K schedule
+// where it applies.  w.k holds the kernel chosen without a workspace.
+void plan_workspace(const Problem &p, const void *workspace, size_t bytes, WsPlan &w) {
+    w.q = p;
+    w.used = 0;
     const bool room = bytes >= static_cast<size_t>(hgemm_streamk_workspace_bytes());
+    if (!room || force_general()) return;
     const bool force = force_streamk();
+    if (plan_packed(p, w.k, workspace, bytes, force, w)) return;
     Kernel &k = w.k;
-    if (room && !force_general() && plan_packed(p, k, workspace, bytes, force, w)) return GEMM_OK;
-    if (k == Kernel::HgemmMfma && !force_general() && room && hgemm_streamk_eligible(p, force))
+    if (k == Kernel::HgemmMfma && hgemm_streamk_eligible(p, force)) {
         k = Kernel::HgemmStreamK;
-    else if (k == Kernel::HgemmDma && room && hgemm_dma_streamk_eligible(p, force))
+        w.used = hgemm_streamk_bytes(p);
+    } else if (k == Kernel::HgemmDma && hgemm_dma_streamk_eligible(p, force)) {
         k = Kernel::HgemmDmaStreamK;
-    else if (k == Kernel::SgemmMfma && !force_general() && room && sgemm_streamk_eligible(p, force))
+        w.used = hgemm_dma_streamk_bytes(p);
+    } else if (k == Kernel::SgemmMfma && sgemm_streamk_eligible(p, force)) {
         k = Kernel::SgemmStreamK;
+        w.used = sgemm_streamk_bytes(p);
+    }
+}
+
+gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, int orderA,
+                            int64_t lda, int orderB, int64_t ldb, int orderC, int64_t ldc,
+                            int64_t strideA, int64_t strideB, int64_t strideC,
+                            const void *bias, int64_t strideBias, const void *A, const void *B,
+                            const void *C, const void *workspace, size_t bytes, WsPlan &w) {
+    const gemm_status_t st = check_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc,
+                                             strideA, strideB, strideC, bias, strideBias, A, B,
+                                             C, workspace, bytes);
+    if (st != GEMM_OK) return st;
+    plan_workspace(p, workspace, bytes, w);
     return GEMM_OK;
 }
 

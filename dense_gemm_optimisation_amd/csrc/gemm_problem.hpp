@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "epilogue.hpp"
+#include "streamk_schedule.hpp"
 
 namespace libgemm {
 
@@ -98,6 +99,8 @@ hipError_t launch_sgemm_splitk(const Problem &p, hipStream_t stream);
 constexpr int64_t SGEMM_STREAMK_MAX_GRID = 1024;
 bool sgemm_streamk_eligible(const Problem &p, bool force = false);
 hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);
+// Workspace bytes launch_sgemm_streamk uses for p (its partial tiles).
+int64_t sgemm_streamk_bytes(const Problem &p);
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA, any shape
 // The *_streamk_eligible functions check whether a problem can run on the
 // schedule and, unless `force`, whether the cost model says it pays.
@@ -106,20 +109,6 @@ hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on 
 // (two fp32 partial 256 x 256 tiles per workgroup); only where
 // hgemm_streamk_eligible() holds.
 constexpr int64_t HGEMM_STREAMK_MAX_GRID = 256;
-// Workgroups that share the k steps of a stream-K schedule's `cut` tiles of
-// `steps` k steps each, out of G: cutting each tile into s pieces costs
-// steps/s k steps of time and cut*s partial tiles written and read back;
-// with one k step worth `ratio` partial tiles (the kernel's step time over
-// the time to move one 256 x 256 fp32 partial tile through HBM twice),
-// s = sqrt(steps*ratio/cut) balances the two.
-inline int64_t streamk_groups(int64_t G, int64_t cut, int64_t steps, double ratio) {
-    const int64_t W = cut * steps;
-    int64_t s = static_cast<int64_t>(__builtin_sqrt(double(steps) * ratio / double(cut)) + 0.5);
-    s = s < 1 ? 1 : (s > steps ? steps : s);
-    int64_t g = cut * s;
-    g = g < G ? g : G;
-    return g < W ? g : W;
-}
 constexpr int64_t hgemm_streamk_workspace_bytes() {
     return 2 * HGEMM_STREAMK_MAX_GRID * 256 * 256 * 4;
 }
@@ -127,6 +116,8 @@ static_assert(2 * 1024 * 128 * 128 * 4 == hgemm_streamk_workspace_bytes(),
               "the fp32 stream-K schedule (1024 workgroups, 128 x 128 tiles) fits the workspace");
 bool hgemm_streamk_eligible(const Problem &p, bool force = false);
 hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);
+// Workspace bytes launch_hgemm_streamk uses for p (its partial tiles).
+int64_t hgemm_streamk_bytes(const Problem &p);
 // bf16/fp16 on MFMA with direct global->LDS loads; only for problems where
 // hgemm_dma_eligible() holds (aligned operands, extents multiple of 8).
 bool hgemm_dma_eligible(const Problem &p);

@@ -63,12 +63,8 @@ struct HgemmArgs {
     Epilogue epi;
 };
 
-struct StreamK {
+struct StreamK : StreamKSplit {
     float *partials;    // 2 * Gs slots of 256 x 256 floats
-    int64_t steps;      // k steps per tile (S)
-    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
-    int64_t iters;      // W = (tiles - dp_tiles) * steps
-    int64_t groups;     // Gs = min(grid, W)
 };
 
 namespace {
@@ -648,11 +644,11 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, 
     // Logical workgroup w: the hardware id regrouped per XCD (xcd_remap), so
     // that the workgroups of one die take consecutive tiles and ranges and
     // share their panels in its L2.
-    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t G = gridDim.x, S = sk.steps;
     const int64_t w = sk_uniform(xcd_remap(blockIdx.x, G, 8));
-    const int64_t n_dp = w < sk.dp_tiles ? sk_uniform((sk.dp_tiles - w + G - 1) / G) : 0;
-    const int64_t begin = w < Gs ? sk_uniform(w * W / Gs) : 0;
-    const int64_t end = w < Gs ? sk_uniform((w + 1) * W / Gs) : 0;
+    const int64_t n_dp = sk_uniform(sk_whole_tiles(sk, w, G));
+    const int64_t begin = sk_uniform(sk_begin(sk, w));
+    const int64_t end = sk_uniform(sk_end(sk, w));
     int64_t it = begin;
     for (int64_t item = 0;; ++item) {
         int64_t tile, kb, ke, local = 0;
@@ -663,8 +659,9 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, 
         } else {
             if (it >= end) break;
             local = sk_uniform(it / S);
-            kb = it - local * S;
-            ke = end - local * S < S ? end - local * S : S;
+            const StreamKPiece pc = sk_piece(sk, local, it, end);
+            kb = pc.kb;
+            ke = pc.ke;
             tile = sk.dp_tiles + local;
             it = local * S + ke;
         }
@@ -683,8 +680,7 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, 
         if (kb == 0 && ke == S) {
             tile_store<OUT>(p, t, acc);
         } else {
-            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
-            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, 2 * w + side);
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, sk_slot(sk, w, local, end));
             const int tid = opaque_tid();
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -706,12 +702,6 @@ __global__ __launch_bounds__(THREADS, 1) void hgemm_streamk_kernel(HgemmArgs p, 
     }
 }
 
-// The workgroup that owns iteration x of the cut tiles: the largest g with
-// g*W/Gs <= x.
-__device__ inline int64_t sk_owner(const StreamK &sk, int64_t x) {
-    return ((x + 1) * sk.groups - 1) / sk.iters;
-}
-
 // Workgroup (local tile, piece): piece = (i*4 + j)*4 + q sums register quad q
 // of block (i, j) over the pieces of local tile `local` of the cut tiles,
 // lowest workgroup first, and stores it.  A tile inside one range was stored
@@ -720,7 +710,7 @@ constexpr int SK_BATCH = 8;  // pieces whose loads are in flight together
 
 template <int OUT>
 __global__ __launch_bounds__(THREADS) void hgemm_streamk_fixup(HgemmArgs p, StreamK sk) {
-    const int64_t S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t S = sk.steps;
     const int64_t local = blockIdx.x / 64;
     const int piece = blockIdx.x % 64;
     const int64_t g0 = sk_owner(sk, local * S), g1 = sk_owner(sk, local * S + S - 1);
@@ -733,11 +723,9 @@ __global__ __launch_bounds__(THREADS) void hgemm_streamk_fixup(HgemmArgs p, Stre
         for (int u = 0; u < SK_BATCH; ++u) {
             // past the last piece: an offset beyond the buffer reads zeros
             const int64_t gu = g + u <= g1 ? g + u : g1;
-            const int64_t end = (gu + 1) * W / Gs;
-            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
             const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
             v[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, 2 * gu + side), off,
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, sk_slot(sk, gu, local, sk_end(sk, gu))), off,
                                                              piece * THREADS * 16, 0));
         }
 #pragma unroll
@@ -864,17 +852,6 @@ HgemmArgs make_args(const Problem &p, int32_t xcds) {
     return a;
 }
 
-// Workgroups of the stream-K grid: one per compute unit of the current
-// device, at most HGEMM_STREAMK_MAX_GRID (the workspace is sized for that).
-int64_t streamk_grid() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = HGEMM_STREAMK_MAX_GRID;
-    return cus < HGEMM_STREAMK_MAX_GRID ? cus : HGEMM_STREAMK_MAX_GRID;
-}
-
 // Cost of the partial-tile exchange (writing the pieces, the fix-up kernel),
 // in k steps of one 256 x 256 tile, measured on MI355X.
 constexpr int64_t SK_EXCHANGE_STEPS = 4;
@@ -915,17 +892,27 @@ bool hgemm_streamk_eligible(const Problem &p, bool force) {
     return a.ubuf_a && a.ubuf_b && (force || steps - tail > SK_EXCHANGE_STEPS);
 }
 
+namespace {
+
+// The split over HGEMM_STREAMK_MAX_GRID workgroups (one per compute unit of
+// MI355X; on a part with fewer units the schedule is still correct).
+StreamKSplit hg_streamk_split(const Problem &p) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+    return streamk_split(tiles, (p.K + BK - 1) / BK, HGEMM_STREAMK_MAX_GRID, LIBGEMM_SK_RATIO);
+}
+
+}  // namespace
+
+int64_t hgemm_streamk_bytes(const Problem &p) {
+    return 2 * hg_streamk_split(p).groups * int64_t(SK_SLOT) * 4;
+}
+
 hipError_t launch_hgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {
     HgemmArgs a = make_args(p, 1);  // the work order itself spreads tiles over the dies
-    const int64_t tiles = a.grid.count();
-    const int64_t G = streamk_grid();
     StreamK sk{};
+    static_cast<StreamKSplit &>(sk) = hg_streamk_split(p);
     sk.partials = static_cast<float *>(workspace);
-    sk.steps = (p.K + BK - 1) / BK;
-    sk.dp_tiles = tiles / G * G;
-    sk.iters = (tiles - sk.dp_tiles) * sk.steps;
-    sk.groups = sk.iters == 0 ? 0 : streamk_groups(G, tiles - sk.dp_tiles, sk.steps, LIBGEMM_SK_RATIO);
-    const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
+    const int64_t grid = streamk_grid(sk, HGEMM_STREAMK_MAX_GRID);
     if (grid == 0) return hipSuccess;
     const int part = (p.in == Elem::BF16 ? 0 : 2) + (p.a_kmajor ? 1 : 0);
     switch (part) {

@@ -361,19 +361,15 @@ __device__ __forceinline__ void dma_tile_store(const DmaArgs &p, LDS char *lds, 
 // piece holding its last iteration) or 2w + 1 (its first), and
 // hgemm_dma_streamk_fixup adds the pieces of each cut tile in increasing
 // workgroup order and applies the epilogue.
-struct DmaStreamK {
+struct DmaStreamK : StreamKSplit {
     float *partials;    // 2 * Gs slots of 256 x 256 floats
-    int64_t steps;      // k steps per tile (S)
-    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
-    int64_t iters;      // W = (tiles - dp_tiles) * steps
-    int64_t groups;     // Gs = min(grid, W)
 };
 
 constexpr int SK_SLOT = BM * BN;  // floats per partial tile
 
 // Slot `slot` as a raw buffer.  Register quad q of block (i, j) of thread
 // tid is the 16 bytes at ((i*FN + j)*4 + q) * threads * 16 + tid * 16.
-__device__ inline __amdgpu_buffer_rsrc_t sk_slot(const DmaStreamK &sk, int64_t slot) {
+__device__ inline __amdgpu_buffer_rsrc_t slot_rsrc(const DmaStreamK &sk, int64_t slot) {
     return __builtin_amdgcn_make_buffer_rsrc(sk.partials + slot * SK_SLOT, 0, SK_SLOT * 4,
                                              0x00020000);
 }
@@ -392,11 +388,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_streamk_ke
 
     // logical workgroup: the hardware id regrouped per XCD, so that the
     // workgroups of one die take consecutive tiles and ranges
-    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t G = gridDim.x, S = sk.steps;
     const int64_t w = uniform(xcd_remap(blockIdx.x, G, 8));
-    const int64_t n_dp = w < sk.dp_tiles ? uniform((sk.dp_tiles - w + G - 1) / G) : 0;
-    const int64_t begin = w < Gs ? uniform(w * W / Gs) : 0;
-    const int64_t end = w < Gs ? uniform((w + 1) * W / Gs) : 0;
+    const int64_t n_dp = uniform(sk_whole_tiles(sk, w, G));
+    const int64_t begin = uniform(sk_begin(sk, w));
+    const int64_t end = uniform(sk_end(sk, w));
     int64_t it = begin;
     for (int64_t item = 0;; ++item) {
         int64_t tile, kb, ke, local = 0;
@@ -407,8 +403,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_streamk_ke
         } else {
             if (it >= end) break;
             local = uniform(it / S);
-            kb = it - local * S;
-            ke = end - local * S < S ? end - local * S : S;
+            const StreamKPiece pc = sk_piece(sk, local, it, end);
+            kb = pc.kb;
+            ke = pc.ke;
             tile = sk.dp_tiles + local;
             it = local * S + ke;
         }
@@ -431,8 +428,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_streamk_ke
         if (kb == 0 && ke == S) {
             dma_tile_store<OUT, WAVES_M, WAVES_N, BK, STAGES>(p, lds, t, buf, acc);
         } else {
-            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
-            const __amdgpu_buffer_rsrc_t rs = sk_slot(sk, 2 * w + side);
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, sk_slot(sk, w, local, end));
             const int tid = threadIdx.x;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -466,11 +462,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void hgemm_dma_streamk_fixup
     constexpr int THREADS = WAVES_M * WAVES_N * 64;
     constexpr int PIECES = (BM / WAVES_M / 32) * FN * 4;
     constexpr int BATCH = 8;  // pieces whose loads are in flight together
-    const int64_t S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t S = sk.steps;
     const int64_t local = blockIdx.x / PIECES;
     const int piece = blockIdx.x % PIECES;
-    const int64_t g0 = ((local * S + 1) * Gs - 1) / W;
-    const int64_t g1 = ((local * S + S) * Gs - 1) / W;
+    const int64_t g0 = sk_owner(sk, local * S), g1 = sk_owner(sk, local * S + S - 1);
     if (g0 == g1) return;
     const int tid = threadIdx.x;
     f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -480,11 +475,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void hgemm_dma_streamk_fixup
         for (int u = 0; u < BATCH; ++u) {
             // past the last piece: an offset beyond the buffer reads zeros
             const int64_t gu = g + u <= g1 ? g + u : g1;
-            const int64_t end = (gu + 1) * W / Gs;
-            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
             const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
             v[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(sk_slot(sk, 2 * gu + side), off,
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, sk_slot(sk, gu, local, sk_end(sk, gu))), off,
                                                              piece * THREADS * 16, 0));
         }
 #pragma unroll
@@ -687,15 +680,10 @@ namespace {
 // The stream-K split of p: one workgroup per compute unit of MI355X (G =
 // HGEMM_STREAMK_MAX_GRID; on a part with fewer units the schedule is still
 // correct, the workgroups just do not all run at once).
-DmaStreamK dma_streamk_split(const Problem &p) {
+StreamKSplit dma_streamk_split(const Problem &p) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
-    const int64_t G = HGEMM_STREAMK_MAX_GRID;
-    DmaStreamK sk{};
-    sk.steps = (p.K + LIBGEMM_DMA_BK - 1) / LIBGEMM_DMA_BK;
-    sk.dp_tiles = tiles / G * G;
-    sk.iters = (tiles - sk.dp_tiles) * sk.steps;
-    sk.groups = sk.iters == 0 ? 0 : streamk_groups(G, tiles - sk.dp_tiles, sk.steps, LIBGEMM_DMA_SK_RATIO);
-    return sk;
+    return streamk_split(tiles, (p.K + LIBGEMM_DMA_BK - 1) / LIBGEMM_DMA_BK, HGEMM_STREAMK_MAX_GRID,
+                         LIBGEMM_DMA_SK_RATIO);
 }
 
 }  // namespace
@@ -706,10 +694,10 @@ int64_t hgemm_dma_streamk_bytes(const Problem &p) {
 
 hipError_t launch_hgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream) {
     DmaArgs a = make_dma_args(p, 1);  // the work order itself spreads tiles over the dies
-    const int64_t G = HGEMM_STREAMK_MAX_GRID;
-    DmaStreamK sk = dma_streamk_split(p);
+    DmaStreamK sk{};
+    static_cast<StreamKSplit &>(sk) = dma_streamk_split(p);
     sk.partials = static_cast<float *>(workspace);
-    const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
+    const int64_t grid = streamk_grid(sk, HGEMM_STREAMK_MAX_GRID);
     if (grid == 0) return hipSuccess;
     const bool bf = p.in == Elem::BF16;
     if (p.out == Elem::F32)

@@ -464,12 +464,8 @@ hipError_t launch(const SgemmArgs &a0, bool direct, hipStream_t stream) {
 // written to the workgroup's slot 2w (the piece holding its last iteration)
 // or 2w + 1 (its first), and sgemm_streamk_fixup adds the pieces of each cut
 // tile in increasing workgroup order and applies the epilogue.
-struct SgStreamK {
+struct SgStreamK : StreamKSplit {
     float *partials;    // 2 * Gs slots of 128 x 128 floats
-    int64_t steps;      // k steps per tile (S)
-    int64_t dp_tiles;   // tiles computed whole (a multiple of the grid)
-    int64_t iters;      // W = (tiles - dp_tiles) * steps
-    int64_t groups;     // Gs
 };
 
 constexpr int SG_SLOT = BM * BN;  // floats per partial tile
@@ -534,11 +530,11 @@ template <bool A_KMAJOR, bool B_KMAJOR>
 __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, SgStreamK sk) {
     __shared__ __attribute__((aligned(16))) float smem[2][2][PANEL];
     // logical workgroup: the hardware id regrouped per XCD
-    const int64_t G = gridDim.x, S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t G = gridDim.x, S = sk.steps;
     const int64_t w = dma::uniform(xcd_remap(blockIdx.x, G, 8));
-    const int64_t n_dp = w < sk.dp_tiles ? dma::uniform((sk.dp_tiles - w + G - 1) / G) : 0;
-    const int64_t begin = w < Gs ? dma::uniform(w * W / Gs) : 0;
-    const int64_t end = w < Gs ? dma::uniform((w + 1) * W / Gs) : 0;
+    const int64_t n_dp = dma::uniform(sk_whole_tiles(sk, w, G));
+    const int64_t begin = dma::uniform(sk_begin(sk, w));
+    const int64_t end = dma::uniform(sk_end(sk, w));
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -552,8 +548,9 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, 
         } else {
             if (it >= end) break;
             local = dma::uniform(it / S);
-            kb = it - local * S;
-            ke = end - local * S < S ? end - local * S : S;
+            const StreamKPiece pc = sk_piece(sk, local, it, end);
+            kb = pc.kb;
+            ke = pc.ke;
             tile = sk.dp_tiles + local;
             it = local * S + ke;
         }
@@ -573,8 +570,7 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, 
             store_c<A_KMAJOR, B_KMAJOR>(p, acc, p.C + t.batch * p.sC, t.tm * BM + wm * 64,
                                         t.tn * BN + wn * 64, lane & 31, lane >> 5, t.batch);
         } else {
-            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
-            const __amdgpu_buffer_rsrc_t rs = sg_slot(sk, 2 * w + side);
+            const __amdgpu_buffer_rsrc_t rs = sg_slot(sk, sk_slot(sk, w, local, end));
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -598,11 +594,10 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, 
 template <bool A_KMAJOR, bool B_KMAJOR>
 __global__ __launch_bounds__(THREADS) void sgemm_streamk_fixup(SgemmArgs p, SgStreamK sk) {
     constexpr int BATCH = 8;  // pieces whose loads are in flight together
-    const int64_t S = sk.steps, W = sk.iters, Gs = sk.groups;
+    const int64_t S = sk.steps;
     const int64_t local = blockIdx.x / 16;
     const int piece = blockIdx.x % 16;
-    const int64_t g0 = ((local * S + 1) * Gs - 1) / W;
-    const int64_t g1 = ((local * S + S) * Gs - 1) / W;
+    const int64_t g0 = sk_owner(sk, local * S), g1 = sk_owner(sk, local * S + S - 1);
     if (g0 == g1) return;
     const int tid = threadIdx.x;
     f4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -612,11 +607,10 @@ __global__ __launch_bounds__(THREADS) void sgemm_streamk_fixup(SgemmArgs p, SgSt
         for (int u = 0; u < BATCH; ++u) {
             // past the last piece: an offset beyond the buffer reads zeros
             const int64_t gu = g + u <= g1 ? g + u : g1;
-            const int64_t end = (gu + 1) * W / Gs;
-            const int64_t side = end - 1 < (local + 1) * S ? 0 : 1;
             const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
             v[u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              sg_slot(sk, 2 * gu + side), off, piece * THREADS * 16, 0));
+                                              sg_slot(sk, sk_slot(sk, gu, local, sk_end(sk, gu))), off,
+                                              piece * THREADS * 16, 0));
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) sum += v[u];
@@ -723,18 +717,6 @@ hipError_t launch_sgemm_dma(const Problem &p, hipStream_t stream) {
 
 namespace {
 
-// Workgroups of the fp32 stream-K grid: four per compute unit (the general
-// kernel's occupancy), at most SGEMM_STREAMK_MAX_GRID.
-int64_t sg_streamk_grid() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = SGEMM_STREAMK_MAX_GRID / 4;
-    const int64_t g = 4 * int64_t(cus);
-    return g < SGEMM_STREAMK_MAX_GRID ? g : SGEMM_STREAMK_MAX_GRID;
-}
-
 // Cost of the partial-tile exchange, in k steps (16 k) of one tile, and the
 // step time over partial-tile time for streamk_groups (4.4 us per k step of
 // a workgroup at 4096^3 with four per compute unit, 0.03 us per 64 KiB
@@ -760,18 +742,28 @@ bool sgemm_streamk_eligible(const Problem &p, bool force) {
     return force || steps - tail > SG_SK_EXCHANGE_STEPS;
 }
 
+namespace {
+
+// The split over SGEMM_STREAMK_MAX_GRID workgroups (four per compute unit of
+// MI355X; on a part with fewer units the schedule is still correct).
+StreamKSplit sg_streamk_split(const Problem &p) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+    return streamk_split(tiles, (p.K + BK - 1) / BK, SGEMM_STREAMK_MAX_GRID, LIBGEMM_SG_SK_RATIO);
+}
+
+}  // namespace
+
+int64_t sgemm_streamk_bytes(const Problem &p) {
+    return 2 * sg_streamk_split(p).groups * int64_t(SG_SLOT) * 4;
+}
+
 hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {
     SgemmArgs a = make_args(p);
     a.grid.xcds = 1;  // the work order itself spreads tiles over the dies
-    const int64_t tiles = a.grid.count();
-    const int64_t G = sg_streamk_grid();
     SgStreamK sk{};
+    static_cast<StreamKSplit &>(sk) = sg_streamk_split(p);
     sk.partials = static_cast<float *>(workspace);
-    sk.steps = (p.K + BK - 1) / BK;
-    sk.dp_tiles = tiles / G * G;
-    sk.iters = (tiles - sk.dp_tiles) * sk.steps;
-    sk.groups = sk.iters == 0 ? 0 : streamk_groups(G, tiles - sk.dp_tiles, sk.steps, LIBGEMM_SG_SK_RATIO);
-    const int64_t grid = sk.dp_tiles > 0 ? G : sk.groups;
+    const int64_t grid = streamk_grid(sk, SGEMM_STREAMK_MAX_GRID);
     if (grid == 0) return hipSuccess;
     if (p.a_kmajor)
         return p.b_kmajor ? launch_sk<true, true>(a, sk, grid, stream)

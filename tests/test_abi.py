@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
-                                    "gemm_bf16_ws", "gemm_f16", "gemm_f16_bias_act",
+                                    "gemm_bf16_ws", "gemm_f16",
+                                    "gemm_f16_bias_act",
                                     "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act", "gemm_f32_ws",
                                     "gemm_f8",
                                     "gemm_f8_kernel_name", "gemm_kernel_name",

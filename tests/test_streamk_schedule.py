@@ -1,115 +1,174 @@
-"""The stream-K partition as the kernels compute it, checked on the CPU.
+"""The stream-K partition, checked on the CPU through a host build of the
+header the kernels include (streamk_schedule.hpp).
 
-The stream-K kernels (hgemm_streamk_kernel, hgemm_dma_streamk_kernel,
-sgemm_streamk_kernel) and their fix-up kernels share one piece of integer
-arithmetic, restated here from their source: the cut tiles' W = T_r * S
-(tile, k step) iterations are split over Gs workgroups, workgroup w taking
-[w*W/Gs, (w+1)*W/Gs); a piece that does not cover a whole tile goes to slot
-2w (it holds the range's last iteration) or 2w + 1; the fix-up of cut tile t
-sums the pieces of workgroups owner(t*S) .. owner(t*S + S - 1) in that order,
-reading slot 2g + side with side = 0 iff g's last iteration lies in t.  The
-piece count comes from streamk_groups (gemm_problem.hpp).  These tests check
-the invariants the kernels rely on: every iteration is computed exactly once,
-no workgroup writes more than its two slots, the fix-up finds exactly the
-pieces that were written, and a tile inside one range is stored whole.
+The three stream-K kernels (hgemm_streamk_kernel, hgemm_dma_streamk_kernel,
+sgemm_streamk_kernel), their fix-up kernels and the host code that sizes
+their workspace all call the functions of that header; the shim below walks
+the partition with the same calls, in the order the kernels make them.  The
+invariants the kernels rely on: every (tile, k step) iteration of the cut
+tiles is computed exactly once, no workgroup writes more than its two slots,
+the fix-up of a cut tile reads exactly the pieces that were written, in
+increasing workgroup order, and a tile inside one range is stored whole.
 """
-import math
+import ctypes
+import os
+import subprocess
 
+import numpy as np
 import pytest
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "dense_gemm_optimisation_amd", "csrc")
 
-def streamk_groups(G, cut, steps, ratio):
-    W = cut * steps
-    s = int(math.sqrt(steps * ratio / cut) + 0.5)
-    s = max(1, min(s, steps))
-    return min(cut * s, G, W)
+SHIM = r'''
+#include "streamk_schedule.hpp"
+using namespace libgemm;
+extern "C" int64_t groups(int64_t G, int64_t cut, int64_t steps, double ratio) {
+    return streamk_groups(G, cut, steps, ratio);
+}
+extern "C" void split(int64_t tiles, int64_t steps, int64_t G, double ratio, int64_t *out) {
+    const StreamKSplit s = streamk_split(tiles, steps, G, ratio);
+    out[0] = s.steps; out[1] = s.dp_tiles; out[2] = s.iters; out[3] = s.groups;
+    out[4] = streamk_grid(s, G);
+}
+// The main kernel's walk: for each workgroup w of the grid, its whole tiles
+// (tile, -1, 0, S) then its pieces (w, local, kb, ke, slot or -1 when
+// stored whole).  Returns the number of rows written to out (5 per row).
+extern "C" int64_t walk(int64_t tiles, int64_t steps, int64_t G, double ratio, int64_t *out) {
+    const StreamKSplit s = streamk_split(tiles, steps, G, ratio);
+    const int64_t grid = streamk_grid(s, G);
+    int64_t n = 0;
+    for (int64_t w = 0; w < grid; ++w) {
+        const int64_t n_dp = sk_whole_tiles(s, w, G);
+        for (int64_t i = 0; i < n_dp; ++i) {
+            int64_t *r = out + 5 * n++;
+            r[0] = w; r[1] = -1 - (w + i * G); r[2] = 0; r[3] = s.steps; r[4] = -1;
+        }
+        const int64_t end = sk_end(s, w);
+        for (int64_t it = sk_begin(s, w); it < end;) {
+            const StreamKPiece pc = sk_piece(s, it / s.steps, it, end);
+            it = pc.local * s.steps + pc.ke;
+            int64_t *r = out + 5 * n++;
+            r[0] = w; r[1] = pc.local; r[2] = pc.kb; r[3] = pc.ke;
+            r[4] = (pc.kb == 0 && pc.ke == s.steps) ? -1 : sk_slot(s, w, pc.local, end);
+        }
+    }
+    return n;
+}
+// The fix-up of cut tile `local`: the slots it adds, in order (0 when the
+// tile was stored whole).
+extern "C" int64_t fixup(int64_t tiles, int64_t steps, int64_t G, double ratio, int64_t local,
+                         int64_t *out) {
+    const StreamKSplit s = streamk_split(tiles, steps, G, ratio);
+    const int64_t g0 = sk_owner(s, local * s.steps), g1 = sk_owner(s, local * s.steps + s.steps - 1);
+    if (g0 == g1) return 0;
+    int64_t n = 0;
+    for (int64_t g = g0; g <= g1; ++g) out[n++] = sk_slot(s, g, local, sk_end(s, g));
+    return n;
+}
+'''
 
 
-def pieces(W, S, Gs):
-    """(workgroup, local tile, kb, ke, slot or None) as the main kernel walks them."""
-    out = []
-    for w in range(Gs):
-        begin, end = w * W // Gs, (w + 1) * W // Gs
-        it = begin
-        while it < end:
-            local = it // S
-            kb = it - local * S
-            ke = min(end - local * S, S)
-            it = local * S + ke
-            if kb == 0 and ke == S:
-                out.append((w, local, kb, ke, None))
-            else:
-                side = 0 if end - 1 < (local + 1) * S else 1
-                out.append((w, local, kb, ke, 2 * w + side))
-    return out
+@pytest.fixture(scope="module")
+def sk(tmp_path_factory):
+    d = tmp_path_factory.mktemp("streamk")
+    src = d / "shim.cpp"
+    src.write_text(SHIM)
+    lib = d / "libshim.so"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-I", CSRC, str(src), "-o",
+                    str(lib)], check=True)
+    L = ctypes.CDLL(str(lib))
+    i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    L.groups.argtypes = [i64, i64, i64, dbl]
+    L.groups.restype = i64
+    L.split.argtypes = [i64, i64, i64, dbl, vp]
+    L.walk.argtypes = [i64, i64, i64, dbl, vp]
+    L.walk.restype = i64
+    L.fixup.argtypes = [i64, i64, i64, dbl, i64, vp]
+    L.fixup.restype = i64
+
+    class K:
+        groups = L.groups
+
+        @staticmethod
+        def split(tiles, S, G, ratio):
+            out = np.zeros(5, np.int64)
+            L.split(tiles, S, G, ratio, out.ctypes.data)
+            return dict(zip(("steps", "dp_tiles", "iters", "groups", "grid"), out.tolist()))
+
+        @staticmethod
+        def walk(tiles, S, G, ratio):
+            out = np.zeros((tiles * (S + 2) + 2 * G, 5), np.int64)
+            n = L.walk(tiles, S, G, ratio, out.ctypes.data)
+            return out[:n]
+
+        @staticmethod
+        def fixup(tiles, S, G, ratio, local):
+            out = np.zeros(G + 1, np.int64)
+            n = L.fixup(tiles, S, G, ratio, local, out.ctypes.data)
+            return out[:n].tolist()
+    return K
 
 
-def fixup_reads(local, W, S, Gs):
-    """Slots the fix-up of cut tile `local` adds, in order (empty: not cut)."""
-    g0 = ((local * S + 1) * Gs - 1) // W
-    g1 = ((local * S + S) * Gs - 1) // W
-    if g0 == g1:
-        return []
-    reads = []
-    for g in range(g0, g1 + 1):
-        end = (g + 1) * W // Gs
-        side = 0 if end - 1 < (local + 1) * S else 1
-        reads.append(2 * g + side)
-    return reads
-
-
-CASES = [(cut, S, G) for G in (256, 1024) for cut in (1, 4, 16, 32, 100, 255)
+# (tiles, steps per tile, grid): whole waves plus a cut tail, a tail alone,
+# one tile, few steps, many steps, the fp32 grid of 1024 workgroups
+CASES = [(tiles, S, G) for G in (256, 1024) for tiles in (1, 4, 16, 100, G + 16, 2 * G + 255)
          for S in (1, 2, 16, 63, 129)]
 
 
-@pytest.mark.parametrize("cut,S,G", CASES)
+@pytest.mark.parametrize("tiles,S,G", CASES)
 @pytest.mark.parametrize("ratio", [14, 40, 140, 1e9])
-def test_partition_covers_every_iteration_once(cut, S, G, ratio):
-    W = cut * S
-    Gs = streamk_groups(G, cut, S, ratio)
-    assert 1 <= Gs <= min(G, W)
-    ps = pieces(W, S, Gs)
-    seen = [0] * W
-    for w, local, kb, ke, _ in ps:
-        assert 0 <= kb < ke <= S
-        for k in range(kb, ke):
-            seen[local * S + k] += 1
-    assert seen == [1] * W
+def test_partition_covers_every_iteration_once(sk, tiles, S, G, ratio):
+    s = sk.split(tiles, S, G, ratio)
+    assert s["dp_tiles"] == tiles // G * G and s["iters"] == (tiles - s["dp_tiles"]) * S
+    cut = tiles - s["dp_tiles"]
+    assert (s["groups"] == 0) == (cut == 0)
+    if cut:
+        assert 1 <= s["groups"] <= min(G, s["iters"])
+    rows = sk.walk(tiles, S, G, ratio)
+    seen = np.zeros((tiles, S), np.int64)
+    for w, t, kb, ke, slot in rows:
+        assert 0 <= kb < ke <= S and 0 <= w < s["grid"]
+        tile = -1 - t if t < 0 else s["dp_tiles"] + t
+        assert t >= 0 or slot == -1
+        seen[tile, kb:ke] += 1
+    assert (seen == 1).all()
     # at most two partial pieces per workgroup, in distinct slots of its own
-    slots = [slot for *_, slot in ps if slot is not None]
+    slots = [int(r[4]) for r in rows if r[4] >= 0]
     assert len(slots) == len(set(slots))
-    assert all(slot // 2 == w for w, *_, slot in ps if slot is not None)
+    assert all(int(r[4]) // 2 == int(r[0]) for r in rows if r[4] >= 0)
 
 
-@pytest.mark.parametrize("cut,S,G", CASES)
+@pytest.mark.parametrize("tiles,S,G", CASES)
 @pytest.mark.parametrize("ratio", [14, 40, 140, 1e9])
-def test_fixup_reads_exactly_the_written_pieces(cut, S, G, ratio):
-    W = cut * S
-    Gs = streamk_groups(G, cut, S, ratio)
-    ps = pieces(W, S, Gs)
+def test_fixup_reads_exactly_the_written_pieces(sk, tiles, S, G, ratio):
+    rows = sk.walk(tiles, S, G, ratio)
+    cut = tiles - tiles // G * G
     for local in range(cut):
-        written = sorted((w, slot) for w, t, kb, ke, slot in ps if t == local and slot is not None)
-        whole = [p for p in ps if p[1] == local and p[4] is None]
-        reads = fixup_reads(local, W, S, Gs)
+        mine = [r for r in rows if r[1] == local]
+        written = sorted((int(w), int(slot)) for w, _, _, _, slot in mine if slot >= 0)
+        whole = [r for r in mine if r[4] < 0]
+        reads = sk.fixup(tiles, S, G, ratio, local)
         if whole:
             # stored whole by one workgroup: no partial pieces, no fix-up
-            assert not written and not reads and len(whole) == 1
+            assert not written and not reads and len(whole) == 1 and len(mine) == 1
         else:
             # the fix-up adds the written slots in increasing workgroup order
-            assert reads == [slot for _, slot in written]
-            assert len(reads) >= 2
-            # and their k ranges tile [0, S) in that order
-            ranges = sorted((kb, ke) for w, t, kb, ke, slot in ps if t == local)
+            assert reads == [slot for _, slot in written] and len(reads) >= 2
+            ranges = sorted((int(kb), int(ke)) for _, _, kb, ke, _ in mine)
             assert ranges[0][0] == 0 and ranges[-1][1] == S
             assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
 
 
-def test_balanced_split_examples():
+def test_balanced_split_examples(sk):
     # the cases the measurements quote: 16 cut tiles of 16 steps on the general
     # kernel, 16 of 64 on the direct-load one, 32 of 63 on the fp32 one
-    assert streamk_groups(256, 16, 16, 40) == 96
-    assert streamk_groups(256, 16, 64, 14) == 112
-    assert streamk_groups(1024, 32, 63, 140) == 544
+    assert sk.groups(256, 16, 16, 40) == 96
+    assert sk.groups(256, 16, 64, 14) == 112
+    assert sk.groups(1024, 32, 63, 140) == 544
     # a huge ratio spreads over every workgroup (or every iteration)
-    assert streamk_groups(256, 16, 16, 1e9) == 256
-    assert streamk_groups(256, 4, 3, 1e9) == 12
+    assert sk.groups(256, 16, 16, 1e9) == 256
+    assert sk.groups(256, 4, 3, 1e9) == 12
+    # the grid: G when whole tiles exist, else only the sharing workgroups
+    assert sk.split(272, 16, 256, 14)["grid"] == 256
+    assert sk.split(16, 16, 256, 14)["grid"] == sk.groups(256, 16, 16, 14)
