@@ -22,7 +22,8 @@ DTYPE_SAME, DTYPE_F32 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 F8_E4M3, F8_E5M2 = 0, 1
 OUTPUT_F32, OUTPUT_BF16, OUTPUT_F16 = 0, 1, 2
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -74,6 +75,8 @@ def library() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = common + [i32, i64, i64, i64, i64, vp, sz, vp]
             fn.restype = i32
+        lib.gemm_bf16_noalloc.argtypes = common + [i32, i64, i64, i64, i64, vp]
+        lib.gemm_bf16_noalloc.restype = i32
         lib.gemm_f32_ws.argtypes = common + [i64, i64, i64, i64, vp, sz, vp]
         lib.gemm_f32_ws.restype = i32
         lib.gemm_kernel_name_ws.argtypes = [i32] + common + [i32, i64, i64, i64, i64, vp, sz]
@@ -206,6 +209,16 @@ def gemm_bf16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
                                 order_c, c_dtype, batch, stride_a, stride_b, stride_c, workspace,
                                 workspace_bytes, _stream(stream))
     return _check(st, "gemm_bf16_ws", raise_on_error)
+
+
+def gemm_bf16_noalloc(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                      c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0,
+                      stream=None, raise_on_error=True):
+    """gemm_bf16_ws without a caller workspace: the library's per-device scratch."""
+    st = library().gemm_bf16_noalloc(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C,
+                                     ldc, order_c, c_dtype, batch, stride_a, stride_b, stride_c,
+                                     _stream(stream))
+    return _check(st, "gemm_bf16_noalloc", raise_on_error)
 
 
 def gemm_f16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,

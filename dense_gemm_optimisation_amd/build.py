@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "libgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "scale.hip", "pack.hip", "sgemm_valu.hip", "sgemm_mfma.hip", "sgemm_splitk.hip", "hgemm_mfma.hip", "hgemm_mfma_dma.hip",
+SOURCES = ["api.cpp", "scale.hip", "pack.hip", "noalloc.hip", "sgemm_valu.hip", "sgemm_mfma.hip", "sgemm_splitk.hip", "hgemm_mfma.hip", "hgemm_mfma_dma.hip",
            "hgemm_splitk.hip", "gemm_skinny.hip", "f8gemm_mfma.hip"]
 # Sources compiled once per part (-DLIBGEMM_HGEMM_PART=k, one object each), so
 # that their many kernel instantiations build in parallel.

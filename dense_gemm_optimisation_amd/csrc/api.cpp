@@ -607,12 +607,47 @@ gemm_status_t gemm_f16_ws(int64_t M, int64_t N, int64_t K, float alpha, const ui
                nullptr, 0, GEMM_ACT_NONE, stream, workspace, workspace_bytes);
 }
 
+gemm_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                                int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                                gemm_order_t orderB, float beta, void *C, int64_t ldc,
+                                gemm_order_t orderC, gemm_dtype_t c_dtype, int64_t batch,
+                                int64_t strideA, int64_t strideB, int64_t strideC,
+                                hipStream_t stream) {
+    if (c_dtype != GEMM_DTYPE_SAME && c_dtype != GEMM_DTYPE_F32) return GEMM_ERR_INVALID_ARG;
+    Problem p;
+    WsPlan w;
+    gemm_status_t st = plan(Elem::BF16, Elem::BF16, out_type(Elem::BF16, c_dtype), M, N, K, alpha,
+                            A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC, batch, strideA,
+                            strideB, strideC, nullptr, 0, GEMM_ACT_NONE, p, w.k);
+    if (st != GEMM_OK || w.k == Kernel::None) return st;
+    // The plan gemm_bf16_ws would make with a workspace of
+    // gemm_workspace_size() bytes, first at a stand-in address (only the
+    // bytes it uses matter here), so an oversized call is refused before any
+    // HIP call.
+    const size_t full = static_cast<size_t>(hgemm_streamk_workspace_bytes());
+    const Kernel chosen = w.k;
+    plan_workspace(p, reinterpret_cast<const void *>(uintptr_t(256)), full, w);
+    if (w.used > static_cast<int64_t>(GEMM_NOALLOC_SCRATCH_BYTES)) return GEMM_ERR_SCRATCH;
+    void *scratch = nullptr;
+    if (w.used > 0) {
+        if (scratch_address(stream, &scratch) != hipSuccess) return GEMM_ERR_HIP;
+        w.k = chosen;
+        plan_workspace(p, scratch, full, w);  // the same plan, placed in the scratch
+    }
+    const hipError_t err = launch_planned(w, scratch, stream);
+    if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 const char *gemm_status_string(gemm_status_t status) {
     switch (status) {
     case GEMM_OK: return "GEMM_OK";
     case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: invalid argument";
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: combination not supported";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: kernel launch failed";
+    case GEMM_ERR_SCRATCH:
+        return "GEMM_ERR_SCRATCH: the call needs more than the 64 MiB of scratch memory of the "
+               "allocation-free entry point";
     }
     return "unknown gemm_status_t";
 }

@@ -81,6 +81,10 @@ struct PackSpec {
 int64_t packed_bytes(const PackSpec &s);
 hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream);
 
+// Address of this library's scratch array on the device `stream` belongs to
+// (looked up once per device; see noalloc.hip).
+hipError_t scratch_address(hipStream_t stream, void **ptr);
+
 // Kernel launchers; each returns the launch status.
 hipError_t launch_sgemm(const Problem &p, hipStream_t stream);       // fp32 on the vector ALUs
 hipError_t launch_sgemm_mfma(const Problem &p, hipStream_t stream);  // fp32 on the matrix cores

@@ -126,7 +126,9 @@ typedef enum gemm_status_t {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_ARG = -1,
     GEMM_ERR_UNSUPPORTED = -2,
-    GEMM_ERR_HIP = -3
+    GEMM_ERR_HIP = -3,
+    GEMM_ERR_SCRATCH = -4 /* gemm_bf16_noalloc only: the call would need more
+                             than GEMM_NOALLOC_SCRATCH_BYTES of scratch */
 } gemm_status_t;
 
 /* fp32 SGEMM.  A, B, C point to float; see the header comment for layout,
@@ -299,6 +301,44 @@ gemm_status_t gemm_f16_ws(int64_t M, int64_t N, int64_t K, float alpha,
                           gemm_dtype_t c_dtype, int64_t batch, int64_t strideA,
                           int64_t strideB, int64_t strideC, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/* Allocation-free variant of gemm_bf16_ws, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ * It takes the arguments of gemm_bf16 and computes exactly what gemm_bf16_ws
+ * computes with a workspace of gemm_workspace_size() bytes: the same kernels,
+ * the same schedule, bit-identical results.  In place of a caller's
+ * workspace it uses a scratch array of GEMM_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on every GPU it runs on, from the time its code is
+ * loaded there until the process ends; it calls no allocating routine.
+ *   Limit: a call whose schedule would use more scratch than that returns
+ *          GEMM_ERR_SCRATCH before any HIP call and launches nothing.  Only
+ *          the stream-K schedule of the general kernel can need more (up to
+ *          128 MiB of partial tiles: unaligned operands, fewer than 64 tiles
+ *          of 256 x 256, a long K); gemm_bf16 computes those calls without
+ *          scratch.  Copies of unaligned operands and the direct-load
+ *          kernel's partial tiles stay within the limit at the workload
+ *          sizes tested (4095 x 4097 x 1001: 17 MB; 4096 x 4352 x 4096: 59 MB).
+ *   Set-up: the first call on a device looks up the scratch's address there
+ *          (hipGetSymbolAddress, with that device current for the lookup;
+ *          the caller's current device is restored) and keeps it.  Make one
+ *          call on each device before capturing calls into a graph.  The
+ *          device is the one `stream` belongs to.
+ *   Sharing: every call on one GPU uses that GPU's scratch, which keeps the
+ *          last call's contents.  Nothing in it needs to start at zero: each
+ *          byte a kernel reads was written earlier in the same call.  Calls
+ *          that may run at the same time on one GPU (on different streams,
+ *          or from several host threads) race on the scratch and give wrong
+ *          results; order them, for example on one stream.
+ * Errors are those of gemm_bf16, plus GEMM_ERR_SCRATCH. */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gemm_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
+                                const uint16_t *A, int64_t lda, gemm_order_t orderA,
+                                const uint16_t *B, int64_t ldb, gemm_order_t orderB,
+                                float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                                gemm_dtype_t c_dtype, int64_t batch, int64_t strideA,
+                                int64_t strideB, int64_t strideC, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *gemm_status_string(gemm_status_t status);

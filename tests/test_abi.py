@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
-                                    "gemm_bf16_ws", "gemm_f16",
+                                    "gemm_bf16_noalloc", "gemm_bf16_ws", "gemm_f16",
                                     "gemm_f16_bias_act",
                                     "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act", "gemm_f32_ws",
                                     "gemm_f8",
@@ -56,7 +56,7 @@ def test_header_compiles_as_c(tmp_path):
 
 def test_status_strings(lib):
     assert lib.status_string(0) == "GEMM_OK"
-    for code in (-1, -2, -3):
+    for code in (-1, -2, -3, -4):
         assert lib.status_string(code).startswith("GEMM_ERR_")
     assert lib.status_string(7) == "unknown gemm_status_t"
     assert lib.abi_version() == 1
@@ -417,3 +417,21 @@ def test_workspace_invalid_arguments(lib):
     assert f(0, *f32args[1:], WS, n, 0, raise_on_error=False) == lib.OK
     assert kname_ws(lib, "f32", 4095, 4097, 1001, ws=WS + 16) is None
     assert kname_ws(lib, "f32", 4095, 4097, 1001, ws=3 * GB - 256) is None
+
+
+# ------------------------------------------------------------------ allocation-free entry point (host only)
+
+def test_noalloc_refuses_calls_beyond_its_scratch(lib):
+    # unaligned 300 x 290 x 8193: 4 tiles of 129 k-steps cut over 144
+    # workgroups of the general kernel's stream-K schedule, whose partial
+    # tiles (72 MiB) exceed the 64 MiB scratch: refused before any HIP call
+    # (the pointers here are never dereferenced)
+    args = (300, 290, 8193, 1.0, GB, 8193, 0, 2 * GB, 290, 0, 0.0, 3 * GB, 290, 0, 0, 1, 0, 0, 0)
+    assert kname_ws(lib, "bf16", 300, 290, 8193) == "hgemm_mfma_streamk"
+    assert lib.gemm_bf16_noalloc(*args, raise_on_error=False) == lib.ERR_SCRATCH
+    assert lib.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # invalid arguments and empty problems are answered as by gemm_bf16
+    assert lib.gemm_bf16_noalloc(-1, *args[1:], raise_on_error=False) == lib.ERR_INVALID_ARG
+    assert lib.gemm_bf16_noalloc(*args[:14], 2, *args[15:], raise_on_error=False) == \
+        lib.ERR_INVALID_ARG
+    assert lib.gemm_bf16_noalloc(0, *args[1:], raise_on_error=False) == lib.OK
