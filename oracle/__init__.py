@@ -48,6 +48,8 @@ def _load():
         lib.orc_round.argtypes = [i32, vp, vp, i64]
         lib.orc_round.restype = None
         lib.orc_max_threads.restype = i32
+        lib.orc_set_threads.argtypes = [i32]
+        lib.orc_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -73,6 +75,11 @@ def _buf(x, dtype):
 
 def max_threads() -> int:
     return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on."""
+    _load().orc_set_threads(int(n))
 
 
 def decode(dtype, bits) -> np.ndarray:

@@ -48,6 +48,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_F32 0
@@ -239,6 +240,9 @@ struct problem {
  * M x K matrix, which starts sA elements after the previous one; likewise
  * B(b,k,j) and C0(b,i,j).
  */
+static void finish(const struct problem *P, int64_t b, int64_t i, int64_t j, double s,
+                   double t, double *ref, double *den);
+
 static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
                     double *ref, double *den) {
     double s = 0.0, t = 0.0;
@@ -252,6 +256,16 @@ static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
             t = t + fabs(p);
         }
     }
+    finish(P, b, i, j, s, t, ref, den);
+}
+
+/*
+ * The rest of the definition once the dot product s (and the sum of the
+ * absolute values of its terms, t) is known: alpha * s + beta * C0, the bias
+ * and the activation.
+ */
+static void finish(const struct problem *P, int64_t b, int64_t i, int64_t j, double s,
+                   double t, double *ref, double *den) {
     double r = P->alpha * s;
     double d = fabs(P->alpha) * t;
     if (P->beta != 0.0) {
@@ -283,15 +297,81 @@ static void element(const struct problem *P, int64_t b, int64_t i, int64_t j,
                         B,       C0,     lda,    ldb,   ldc, oA, oB,    oC,   sA,    \
                         sB,      sC,     bias,   sBias, act}
 
-/* All batch*M*N elements; ref and den are dense [batch][M][N]. */
+/*
+ * All batch*M*N elements; ref and den are dense [batch][M][N].
+ *
+ * The same arithmetic as element(), in another loop order: the slice of B is
+ * decoded into doubles once, and each block of ROWS rows of C keeps one
+ * running sum per element while k goes up, so every element still receives
+ * its products one at a time in increasing k order, each a rounded double
+ * multiply followed by a rounded double add (the file is built with
+ * -ffp-contract=off).  Only the order in which different elements advance
+ * changes, which no element's value depends on: the result equals element()
+ * bit for bit (a CPU test compares the two on every element).
+ */
+#define ROWS 16
 void orc_gemm(PROBLEM_ARGS, int64_t batch, double *ref, double *den) {
     PROBLEM_INIT;
-    const int64_t total = batch * M * N;
+    double *bd = alpha == 0.0 || K == 0 || N == 0
+                     ? NULL
+                     : (double *)malloc((size_t)K * (size_t)N * sizeof(double));
+    if (bd == NULL) {  /* no product term, or no room for the decoded slice */
+        const int64_t total = batch * M * N;
 #pragma omp parallel for schedule(dynamic, 64)
-    for (int64_t e = 0; e < total; ++e) {
-        int64_t b = e / (M * N), i = (e / N) % M, j = e % N;
-        element(&P, b, i, j, &ref[e], &den[e]);
+        for (int64_t e = 0; e < total; ++e) {
+            int64_t b = e / (M * N), i = (e / N) % M, j = e % N;
+            element(&P, b, i, j, &ref[e], &den[e]);
+        }
+        return;
     }
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t b0 = b * sB, a0 = b * sA;
+        if (b == 0 || sB != 0) {
+#pragma omp parallel for schedule(static)
+            for (int64_t k = 0; k < K; ++k)
+                for (int64_t j = 0; j < N; ++j)
+                    bd[k * N + j] = load(b_type, B, b0 + offset(oB, k, j, ldb));
+        }
+        const int64_t blocks = (M + ROWS - 1) / ROWS;
+#pragma omp parallel
+        {
+            double *s = (double *)malloc((size_t)ROWS * (size_t)N * 2 * sizeof(double));
+            double *t = s + (size_t)ROWS * (size_t)N;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t blk = 0; blk < blocks; ++blk) {
+                const int64_t i0 = blk * ROWS;
+                const int64_t rows = M - i0 < ROWS ? M - i0 : ROWS;
+                if (s == NULL) {  /* no room for the running sums: the element loop */
+                    for (int64_t r = 0; r < rows; ++r)
+                        for (int64_t j = 0; j < N; ++j) {
+                            const int64_t e = (b * M + i0 + r) * N + j;
+                            element(&P, b, i0 + r, j, &ref[e], &den[e]);
+                        }
+                    continue;
+                }
+                for (int64_t e = 0; e < rows * N; ++e) s[e] = 0.0, t[e] = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const double *x = bd + k * N;
+                    for (int64_t r = 0; r < rows; ++r) {
+                        const double a = load(in_type, A, a0 + offset(oA, i0 + r, k, lda));
+                        double *sr = s + r * N, *tr = t + r * N;
+                        for (int64_t j = 0; j < N; ++j) {
+                            const double p = a * x[j];
+                            sr[j] = sr[j] + p;
+                            tr[j] = tr[j] + fabs(p);
+                        }
+                    }
+                }
+                for (int64_t r = 0; r < rows; ++r)
+                    for (int64_t j = 0; j < N; ++j) {
+                        const int64_t e = (b * M + i0 + r) * N + j;
+                        finish(&P, b, i0 + r, j, s[r * N + j], t[r * N + j], &ref[e], &den[e]);
+                    }
+            }
+            free(s);
+        }
+    }
+    free(bd);
 }
 
 /* Only the listed elements; idx holds count triples (b, i, j). */
@@ -306,6 +386,8 @@ void orc_gemm_at(PROBLEM_ARGS, int64_t count, const int64_t *idx, double *ref,
 #ifdef _OPENMP
 #include <omp.h>
 int orc_max_threads(void) { return omp_get_max_threads(); }
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int orc_max_threads(void) { return 1; }
+void orc_set_threads(int n) { (void)n; }
 #endif

@@ -212,6 +212,16 @@ def test_full_config_sampled(name):
     check(workloads.config(name), sample="auto")
 
 
+@pytest.mark.parametrize("name", ["f32_4096", "bf16_4096", "f16_4096"])
+def test_headline_config_every_element(name):
+    # the 4096^3 headline problems compared element by element (16.8 M each),
+    # on the kernel the benchmark times
+    res, _ = check(workloads.config(name))
+    assert res.checked == 4096 * 4096
+    log(f"{name}: every element checked, max_err={res.max_err:.3e} max_ulp={res.max_ulp} "
+        f"strict_fail={res.strict_fail} exempt={res.exempt}")
+
+
 @pytest.mark.parametrize("name", ["bf16_4096", "bf16_edge", "bf16_attn_pv"])
 def test_full_config_fp32_output(name):
     p = workloads.config(name)

@@ -46,6 +46,15 @@ MUTANTS = {
     "e5m2_inf_as_nan": ("v = m ? NAN : INFINITY;\n    else if (e == 0)\n        v = ldexp((double)m, -16);",
                         "v = NAN;\n    else if (e == 0)\n        v = ldexp((double)m, -16);"),
     "b_type_ignored": ("load(P->b_type, P->B", "load(P->in_type, P->B"),
+    # the same mistakes in the row-blocked full-matrix path
+    "rows_sum_sign": ("sr[j] = sr[j] + p;", "sr[j] = sr[j] - p;"),
+    "rows_den_not_abs": ("tr[j] = tr[j] + fabs(p);", "tr[j] = tr[j] + p;"),
+    "rows_a_transposed": ("offset(oA, i0 + r, k, lda)", "offset(oA, k, i0 + r, lda)"),
+    "rows_b_transposed": ("offset(oB, k, j, ldb)", "offset(oB, j, k, ldb)"),
+    "rows_b_type_ignored": ("load(b_type, B,", "load(in_type, B,"),
+    "rows_batch_b_decoded_once": ("if (b == 0 || sB != 0)", "if (b == 0)"),
+    "rows_last_k_dropped": ("for (int64_t k = 0; k < K; ++k) {\n                    const double *x",
+                            "for (int64_t k = 0; k + 1 < K; ++k) {\n                    const double *x"),
 }
 
 

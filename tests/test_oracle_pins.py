@@ -62,6 +62,11 @@ FORMATS = {"bf16": (8, -126, 127), "f16": (11, -14, 15), "f32": (24, -126, 127)}
 
 
 def rand_bits(rng, dtype, n, scale=1.0):
+    if dtype in ("e4m3", "e5m2"):
+        # any finite pattern: E4M3 S.1111.111 is NaN, E5M2 exponent 31 is Inf/NaN
+        b = rng.integers(0, 256, n).astype(np.uint8)
+        bad = (b & 0x7F) == 0x7F if dtype == "e4m3" else ((b >> 2) & 0x1F) == 0x1F
+        return np.where(bad, b & 0xF3, b).astype(np.uint8)
     x = rng.standard_normal(n) * scale
     if dtype == "f32":
         return x.astype(np.float32)
@@ -394,6 +399,46 @@ def test_gemm_at_matches_full():
                           idx, **kw)
     assert np.array_equal(r, ref[idx[:, 0], idx[:, 1], idx[:, 2]])
     assert np.array_equal(d, den[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
+PATHS = [("f32", "f32", "f32"), ("bf16", "bf16", "bf16"), ("f16", "f16", "f32"),
+         ("e4m3", "e5m2", "bf16"), ("e5m2", "e4m3", "f16")]
+
+
+@pytest.mark.parametrize("ta,tb,tc", PATHS, ids=lambda x: str(x))
+@pytest.mark.parametrize("orders", [(ROW, ROW, ROW), (COL, ROW, COL), (ROW, COL, ROW),
+                                    (COL, COL, COL)], ids=lambda o: "%d%d%d" % o)
+def test_full_matrix_path_equals_element_path(ta, tb, tc, orders):
+    # orc_gemm (row blocks, i-k-j order over a decoded B) against orc_gemm_at
+    # (one textbook dot product per element) on every element, bit for bit:
+    # M not a multiple of the row block, padded leading dimensions, strided
+    # batches, then a batch sharing one B, a bias and an activation
+    rng = np.random.default_rng(23)
+    oA, oB, oC = orders
+    M, N, K, batch = 37, 29, 41, 3
+    lda = (K if oA == ROW else M) + 3
+    ldb = (N if oB == ROW else K) + 2
+    ldc = (N if oC == ROW else M) + 1
+    sA = lda * (M if oA == ROW else K) + 5
+    sB = ldb * (K if oB == ROW else N) + 7
+    sC = ldc * (M if oC == ROW else N) + 2
+    A = rand_bits(rng, ta, batch * sA)
+    B = rand_bits(rng, tb, batch * sB)
+    C = rand_bits(rng, tc, batch * sC)
+    bias = rand_bits(rng, ta, batch * N) if ta in ("f32", "bf16", "f16") else None
+    idx = np.stack(np.meshgrid(np.arange(batch), np.arange(M), np.arange(N), indexing="ij"),
+                   -1).reshape(-1, 3)
+    for stride_b, act, alpha, beta, with_bias in ((sB, oracle.ACT_NONE, 0.75, 1.5, False),
+                                                   (0, oracle.ACT_GELU, -2.0, 0.0, True),
+                                                   (sB, oracle.ACT_RELU, 1.0, -0.5, True)):
+        kw = dict(stride_a=sA, stride_b=stride_b, stride_c=sC, b_dtype=tb,
+                  bias=bias if with_bias else None, stride_bias=N, act=act)
+        ref, den = oracle.gemm(ta, tc, M, N, K, alpha, A, lda, oA, B, ldb, oB, beta, C, ldc, oC,
+                               batch=batch, **kw)
+        r, d = oracle.gemm_at(ta, tc, M, N, K, alpha, A, lda, oA, B, ldb, oB, beta, C, ldc, oC,
+                              idx, **kw)
+        assert np.array_equal(r.view(np.int64), ref.reshape(-1).view(np.int64))
+        assert np.array_equal(d.view(np.int64), den.reshape(-1).view(np.int64))
 
 
 def test_beta_zero_does_not_read_c():
