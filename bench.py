@@ -10,8 +10,8 @@ each GEMM's own TFLOPS and fraction of MI355X's dense peak for its dtype,
 from HIP events recorded on the stream the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-context] [--no-rotate]
-                       [--copy-calibration MiB] [--workspace]
+                       [--no-cpu-baseline] [--no-context] [--no-rotate] [--no-clocks]
+                       [--copy-calibration MiB] [--workspace] [--results FILE]
 Each kernel cycles through at least three copies of its buffers, enough that
 their footprint exceeds twice the 256 MB MALL, so inputs come from HBM;
 --no-rotate reuses one set (the warm-cache figure).
@@ -21,6 +21,16 @@ through the workspace entry points, which use the stream-K schedule where
 it applies.  --copy-calibration runs only a plain
 device-to-device copy of the given size (the reference kernel against which
 the HBM byte counters FETCH_SIZE / WRITE_SIZE are scaled).
+
+Besides the back-to-back mean that `value` uses, each kernel is also timed
+launch by launch (its own event pair around each of --launch-samples
+launches) for the median and the minimum.  With amd-smi present, the gfx
+clock, power and temperatures are read before the run, while each kernel runs
+in a loop, and after.  The CPU baseline runs the oracle once per workload
+(all rows, or the first rows that fit the time budget, as stated in its
+`sample`), the 256^3 problem as the median of 10 and once on one thread, and
+records the CPU model; the same oracle values give the error statistics of
+the GPU result on those rows.
 
 The roofline's `traffic` is the dominant kernel's HBM bytes per launch, read
 from profiles/hbm_traffic.txt (counters taken with rocprofv3 --pmc, scaled by
@@ -110,7 +120,7 @@ def make_launch(p, sets, stream, bias=None, workspace=None):
                 p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch,
                 p.stride_a, p.stride_b, p.stride_c, stream.cuda_stream) for da, db, dc in sets]
     epi = dict(bias=None if bias is None else bias.data_ptr(), stride_bias=p.stride_bias,
-               act=p.act, b_dtype=p.b_dtype, out_dtype=p.c_dtype)
+               act=p.act, b_dtype=p.b_dtype, out_dtype=p.c_dtype, valu=p.entry == "valu")
     if workspace is not None:
         epi.update(workspace=workspace.data_ptr(), workspace_bytes=workspace.numel() * 4)
     turn = [0]
@@ -118,6 +128,7 @@ def make_launch(p, sets, stream, bias=None, workspace=None):
     def launch():
         binding.gemm(*argsets[turn[0]], **epi)
         turn[0] = (turn[0] + 1) % len(argsets)
+    launch.turn = lambda: turn[0]
     return launch
 
 
@@ -126,6 +137,8 @@ def kernel_family(p, bufs, workspace=None):
     (asked of the library itself, so the answer follows its dispatch rules
     and the buffers' actual alignment)."""
     from dense_gemm_optimisation_amd import binding
+    if p.entry == "valu":
+        return "sgemm_valu"
     da, db, dc = bufs
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     return binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a,
@@ -169,32 +182,151 @@ def copy_calibration(mib, torch):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
 
 
-def cpu_baseline(problems, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_model():
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for ln in out.splitlines():
+        if ln.startswith("Model name:"):
+            return ln.split(":", 1)[1].strip()
+    return None
+
+
+def error_stats(p, got_bits, ref, den):
+    """Error of GPU results (stored bit patterns) against oracle values."""
+    import oracle
+    if p.c_dtype == "f32":
+        got = got_bits.view(np.float32).astype(np.float64)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            err = np.where(den > 0, np.abs(got - ref) / np.where(den > 0, den, 1.0),
+                           np.where(got == ref, 0.0, np.inf))
+        return {"max_norm_err": float(err.max()), "elements": int(ref.size)}
+    q = oracle.round_bits(p.c_dtype, ref).astype(np.int64)
+    g = got_bits.view(np.uint16).astype(np.int64)
+    key = lambda b: np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    d = np.abs(key(g) - key(q))
+    return {"max_ulp": int(d.max()), "beyond_2ulp": int((d > 2).sum()), "elements": int(ref.size)}
+
+
+def cpu_baseline(problems, budget_s, gpu_results):
+    """The CPU oracle, as it stands, on each workload (a bounded sample of its
+    rows), timed on this host; its values also give the error statistics of
+    the GPU result on the same rows (gpu_results[name] = C bits as stored)."""
     import oracle
     import workloads
-    total_flop, total_t, parts = 0.0, 0.0, []
-    per = budget_s / len(problems)
+    threads = oracle.max_threads()
+    total_flop, total_t, parts, per, errs = 0.0, 0.0, [], {}, {}
+    share = budget_s / max(1, len(problems))
     for p in problems:
         a, b, c = workloads.generate(p)
-        rows = 1
-        while True:  # calibrate on one row, then size the sample to the budget
-            idx = np.stack([np.zeros(rows * p.N, np.int64), np.repeat(np.arange(rows), p.N),
-                            np.tile(np.arange(p.N), rows)], 1)
-            t0 = time.perf_counter()
-            oracle.gemm_at(p.in_dtype, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda, p.order_a, b,
-                           p.ldb, p.order_b, p.beta, c, p.ldc, p.order_c, idx, b_dtype=p.b_dtype)
-            dt = time.perf_counter() - t0
-            if dt >= 0.5 * per or rows >= p.M:
-                break
-            rows = min(p.M, max(rows * 2, int(rows * per / max(dt, 1e-3))))
-        flop = 2.0 * rows * p.N * p.K
+        # rows [0, r) of C for the first batch entry: a sub-problem with
+        # M = r when A is row-major (rows contiguous), else listed elements
+        r = p.M
+        est = 2.0 * p.M * p.N * p.K / 10e9  # ~10 GFLOP/s with all threads
+        if est > share:
+            r = max(1, int(p.M * share / est))
+        t0 = time.perf_counter()
+        if p.order_a == workloads.ROW and p.order_c == workloads.ROW:
+            ref, den = oracle.gemm(p.in_dtype, p.c_dtype, r, p.N, p.K, p.alpha, a, p.lda,
+                                   p.order_a, b, p.ldb, p.order_b, p.beta, c, p.ldc, p.order_c,
+                                   stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
+                                   bias=workloads.bias_vector(p), stride_bias=p.stride_bias,
+                                   act=p.act, b_dtype=p.b_dtype)
+            ref, den = ref[0].ravel(), den[0].ravel()
+        else:
+            idx = np.stack([np.zeros(r * p.N, np.int64), np.repeat(np.arange(r), p.N),
+                            np.tile(np.arange(p.N), r)], 1)
+            ref, den = oracle.gemm_at(p.in_dtype, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda,
+                                      p.order_a, b, p.ldb, p.order_b, p.beta, c, p.ldc,
+                                      p.order_c, idx, stride_a=p.stride_a, stride_b=p.stride_b,
+                                      stride_c=p.stride_c, bias=workloads.bias_vector(p),
+                                      stride_bias=p.stride_bias, act=p.act, b_dtype=p.b_dtype)
+        dt = time.perf_counter() - t0
+        flop = 2.0 * r * p.N * p.K
         total_flop += flop
         total_t += dt
-        parts.append(f"{p.name}: first {rows} rows x {p.N} cols ({dt:.1f} s)")
-    return {"value": total_flop / total_t / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
-            "kind": "oracle", "sample": "; ".join(parts) +
-            " -- double-accumulating triple loop, timed with perf_counter"}
+        per[p.name] = {"rows": r, "of_rows": p.M, "seconds": round(dt, 3),
+                       "gflops": round(flop / dt / 1e9, 3)}
+        parts.append(f"{p.name}: rows 0..{r - 1} of {p.M} (batch entry 0), {dt:.1f} s")
+        got = gpu_results.get(p.name)
+        if got is not None:
+            if p.order_c == workloads.ROW:
+                sel = (np.arange(r)[:, None] * p.ldc + np.arange(p.N)[None, :]).ravel()
+            else:
+                sel = (np.arange(p.N)[None, :] * p.ldc + np.arange(r)[:, None]).ravel()
+            errs[p.name] = error_stats(p, got[sel], ref, den)
+    # the 256^3 problem whole: median of 10 with every thread, and once on one
+    small = workloads.config("f32_256")
+    a, b, c = workloads.generate(small)
+    args = (small.in_dtype, small.c_dtype, small.M, small.N, small.K, small.alpha, a, small.lda,
+            small.order_a, b, small.ldb, small.order_b, small.beta, c, small.ldc, small.order_c)
+    ts = []
+    for _ in range(10):
+        t0 = time.perf_counter()
+        oracle.gemm(*args)
+        ts.append(time.perf_counter() - t0)
+    oracle.set_threads(1)
+    t0 = time.perf_counter()
+    oracle.gemm(*args)
+    t1 = time.perf_counter() - t0
+    oracle.set_threads(threads)
+    out = {"value": total_flop / total_t / 1e12, "unit": "TFLOPS", "cores": threads,
+           "kind": "oracle",
+           "sample": "; ".join(parts) + " -- the oracle's full-matrix path (double "
+                     "accumulation, increasing k per element), perf_counter around the call",
+           "cpu_model": cpu_model(), "per_config": per,
+           "f32_256": {"median_s": round(float(np.median(ts)), 5), "threads": threads,
+                       "gflops": round(small.flops / float(np.median(ts)) / 1e9, 3),
+                       "single_thread_s": round(t1, 5),
+                       "single_thread_gflops": round(small.flops / t1 / 1e9, 3)}}
+    if errs:
+        out["gpu_error_on_sampled_rows"] = errs
+    return out
+
+
+def smi():
+    """gfx clock (mean over the dies), memory clock, power and temperatures
+    from amd-smi, or None when it is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--temperature", "--power",
+                            "--json"], capture_output=True, text=True, timeout=30)
+        g = json.loads(r.stdout)["gpu_data"][0]
+    except (OSError, subprocess.SubprocessError, ValueError, KeyError, IndexError):
+        return None
+
+    def val(x):
+        return x.get("value") if isinstance(x, dict) else None
+    clocks = g.get("clock", {})
+    gfx = [val(v.get("clk")) for k, v in clocks.items() if k.startswith("gfx_")]
+    gfx = [x for x in gfx if isinstance(x, (int, float))]
+    temp = g.get("temperature", {})
+    return {"gfx_mhz": round(sum(gfx) / len(gfx), 1) if gfx else None,
+            "mem_mhz": val(clocks.get("mem_0", {}).get("clk")),
+            "power_w": val(g.get("power", {}).get("socket_power")),
+            "hotspot_c": val(temp.get("hotspot")), "mem_c": val(temp.get("mem"))}
+
+
+def clocks_under_load(fn, torch, seconds=1.5):
+    """amd-smi readings taken while `fn` runs back to back for `seconds`."""
+    import threading
+    stop = threading.Event()
+
+    def loop():
+        while not stop.is_set():
+            for _ in range(64):
+                fn()
+            torch.cuda.synchronize()
+    th = threading.Thread(target=loop)
+    th.start()
+    time.sleep(seconds / 3)
+    reading = smi()
+    time.sleep(seconds / 3)
+    stop.set()
+    th.join()
+    return reading
 
 
 def main():
@@ -206,11 +338,15 @@ def main():
                     help="reuse one buffer set per kernel (inputs may stay in the MALL)")
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=24.0)
     ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true")
+    ap.add_argument("--launch-samples", type=int, default=50,
+                    help="launches timed one by one for the median and minimum")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--workspace", action="store_true",
                     help="fp32/bf16/fp16 workloads through the workspace entry points (stream-K)")
+    ap.add_argument("--results", default=None, help="append the JSON line to this file")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the GEMM path has no multi-GPU "
@@ -231,6 +367,7 @@ def main():
     ws = None
     if args.workspace:
         ws = torch.empty(binding.workspace_size() // 4, dtype=torch.int32, device="cuda")
+    clocks = {"before": None if args.no_clocks else smi()}
     launches, nsets, families = [], {}, {}
     with torch.cuda.stream(stream):
         for p in problems:
@@ -239,7 +376,7 @@ def main():
             sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
             nsets[p.name] = len(sets)
             pws = ws if (ws is not None and p.in_dtype in ("f32", "bf16", "f16") and not p.bias
-                         and not p.act) else None
+                         and not p.act and not p.entry) else None
             families[p.name] = kernel_family(p, bufs, pws)
             bias = device_bias(p, torch)
             launches.append((p, sets, make_launch(p, sets, stream, bias, pws)))
@@ -268,6 +405,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Launch by launch (outside the timed region): each launch between its
+    # own event pair, for the median and the minimum.
+    one_by_one = {}
+    for p, _, fn in launches:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.launch_samples)]
+        for e0, e1 in pairs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        one_by_one[p.name] = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+
+    if not args.no_clocks:
+        clocks["under_load"] = {p.name: clocks_under_load(fn, torch) for p, _, fn in launches}
+        clocks["after"] = smi()
+
     per_kernel = {}
     flops_step = 0
     for k, (p, _, _) in enumerate(launches):
@@ -276,11 +430,19 @@ def main():
         flops_step += p.flops
         alg_bytes = (p.M * p.K * ESIZE[p.in_dtype] + p.K * p.N * ESIZE[p.b_dtype]) * p.batch + \
             p.M * p.N * ESIZE[p.c_dtype] * p.batch * (2 if p.beta else 1)
+        t1 = one_by_one[p.name]
+        med, mn = t1[len(t1) // 2], t1[0]
         per_kernel[p.name] = {
+            "kernel": families[p.name],
             "dtype": p.in_dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
             "mean_us": round(ms * 1e3, 2), "tflops": round(tfl, 2),
             "frac_of_peak": round(tfl / PEAK_TFLOPS[p.in_dtype], 4),
-            "alg_gbs": round(alg_bytes / (ms * 1e-3) / 1e9, 1)}
+            "alg_gbs": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+            "alg_frac_of_hbm": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_GBS, 4),
+            "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+            "tflops_median": round(p.flops / (med * 1e-3) / 1e12, 2),
+            "frac_of_peak_median": round(p.flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS[p.in_dtype], 4),
+            "tflops_best": round(p.flops / (mn * 1e-3) / 1e12, 2)}
     ms_step = wall / args.steps * 1e3
     value = flops_step / (wall / args.steps) / 1e12
 
@@ -310,13 +472,40 @@ def main():
         "per_kernel": per_kernel,
         "roofline": roof(dominant),
         "roofline_all": [roof(n) for n in per_kernel],
+        "clocks": None if args.no_clocks else clocks,
     }
     if not args.no_context:
         out["context_torch_matmul"] = torch_context(problems, stream, torch)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(problems[:2], args.cpu_budget)
-    print(json.dumps(out), flush=True)
+        out["cpu_baseline"] = cpu_baseline(problems, args.cpu_budget,
+                                           single_results(launches, torch))
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.results:
+        with open(args.results, "a") as f:
+            f.write(line + "\n")
+
+
+def single_results(launches, torch):
+    """C of one clean launch per workload (C0 restored first), as stored bits,
+    for the error statistics of the CPU-baseline leg."""
+    import workloads
+    res = {}
+    for p, sets, fn in launches:
+        _, _, c0 = workloads.generate(p)
+        dc = sets[0][2]
+        dc.copy_(torch.from_numpy(c0.view(VIEW[p.c_dtype])).to(dc.device))
+        torch.cuda.synchronize()
+        # the launcher cycles through the buffer sets: run until set 0 comes round
+        for _ in range(len(sets)):
+            turn = fn.turn()
+            fn()
+            if turn == 0:
+                break
+        torch.cuda.synchronize()
+        res[p.name] = dc.cpu().numpy().view(workloads.storage(p.c_dtype))
+    return res
 
 
 def torch_context(problems, stream, torch):

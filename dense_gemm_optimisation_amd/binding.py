@@ -23,6 +23,8 @@ ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 F8_E4M3, F8_E5M2 = 0, 1
 OUTPUT_F32, OUTPUT_BF16, OUTPUT_F16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4
+# gemm_test_switches flags
+TEST_FORCE_GENERAL, TEST_NO_SPLITK, TEST_FORCE_STREAMK, TEST_F32_VALU = 1, 2, 4, 8
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -75,6 +77,10 @@ def library() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = common + [i32, i64, i64, i64, i64, vp, sz, vp]
             fn.restype = i32
+        lib.gemm_f32_valu.argtypes = common + [i64, i64, i64, i64, vp]
+        lib.gemm_f32_valu.restype = i32
+        lib.gemm_test_switches.argtypes = [i32]
+        lib.gemm_test_switches.restype = i32
         lib.gemm_bf16_noalloc.argtypes = common + [i32, i64, i64, i64, i64, vp]
         lib.gemm_bf16_noalloc.restype = i32
         lib.gemm_f32_ws.argtypes = common + [i64, i64, i64, i64, vp, sz, vp]
@@ -113,6 +119,20 @@ def gemm_f32(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, ord
     st = library().gemm_f32(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
                             order_c, batch, stride_a, stride_b, stride_c, _stream(stream))
     return _check(st, "gemm_f32", raise_on_error)
+
+
+def gemm_f32_valu(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                  batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None, raise_on_error=True):
+    """gemm_f32 on the vector-ALU kernel (register-tiled fused multiply-adds)."""
+    st = library().gemm_f32_valu(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                                 order_c, batch, stride_a, stride_b, stride_c, _stream(stream))
+    return _check(st, "gemm_f32_valu", raise_on_error)
+
+
+def test_switches(flags: int) -> int:
+    """Set the process-wide kernel-choice overrides (TEST_* flags, 0 clears
+    them); returns the previous set.  For tests only."""
+    return library().gemm_test_switches(int(flags))
 
 
 def gemm_bf16(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
@@ -266,12 +286,18 @@ def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta
 def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
          c_dtype=DTYPE_SAME, batch=1, stride_a=0, stride_b=0, stride_c=0, stream=None,
          raise_on_error=True, bias=None, stride_bias=0, act=ACT_NONE, b_dtype=None,
-         out_dtype=None, workspace=None, workspace_bytes=0):
+         out_dtype=None, workspace=None, workspace_bytes=0, valu=False):
     """Dispatch on the input type name ("f32", "bf16", "f16", or the 8-bit
     "e4m3"/"e5m2" with B's format in b_dtype (default: A's) and C's type
     name in out_dtype); a bias address or an activation selects the
     fused-epilogue entry point (not offered for 8-bit inputs); a workspace
-    address (fp32/bf16/fp16, no epilogue) selects the workspace entry point."""
+    address (fp32/bf16/fp16, no epilogue) selects the workspace entry point;
+    valu=True (fp32, no epilogue, no workspace) selects gemm_f32_valu."""
+    if valu:
+        if in_dtype != "f32" or workspace is not None or bias is not None or act != ACT_NONE:
+            raise ValueError("gemm_f32_valu takes fp32 inputs without workspace or epilogue")
+        return gemm_f32_valu(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
+                             order_c, batch, stride_a, stride_b, stride_c, stream, raise_on_error)
     if workspace is not None:
         if in_dtype not in ("f32", "bf16", "f16") or bias is not None or act != ACT_NONE:
             raise ValueError("the workspace entry points take fp32/bf16/fp16 inputs without epilogue")

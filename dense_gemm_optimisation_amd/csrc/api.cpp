@@ -5,6 +5,7 @@
 // C^T = B^T A^T (the transpose identity used with the column-major BLAS call
 // in section 7.1 of "第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech).
 // The kernels therefore only ever write a row-major C.
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -42,36 +43,13 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.h
 // Product of non-negative dimensions overflowing int64 (or the 2^31 grid).
 bool too_big(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
 
-// LIBGEMM_FORCE_GENERAL=1 routes every call to the general matrix-core
-// kernel of its type instead of a fast path (used to test the kernels
-// against each other).
-bool force_general() {
-    const char *v = std::getenv("LIBGEMM_FORCE_GENERAL");
-    return v != nullptr && v[0] == '1';
-}
-
-// LIBGEMM_FORCE_STREAMK=1 makes the workspace entry points run the stream-K
-// schedule wherever it can run, whatever its cost model says (used to test
-// the schedule on small problems).
-bool force_streamk() {
-    const char *v = std::getenv("LIBGEMM_FORCE_STREAMK");
-    return v != nullptr && v[0] == '1';
-}
-
-// LIBGEMM_NO_SPLITK=1 keeps few-tile and skinny problems on the main
-// kernels instead of the split-K ones (used to test them against each other).
-bool no_splitk() {
-    const char *v = std::getenv("LIBGEMM_NO_SPLITK");
-    return v != nullptr && v[0] == '1';
-}
-
-// LIBGEMM_F32_VALU=1 routes fp32 calls to the register-tiled vector-ALU
-// kernel instead of the matrix-core one (used to test the two against each
-// other and to time the vector-ALU design).
-bool f32_valu() {
-    const char *v = std::getenv("LIBGEMM_F32_VALU");
-    return v != nullptr && v[0] == '1';
-}
+// Kernel-choice overrides for testing (gemm_test_switches): one atomic word
+// for the whole process, read on every call.
+std::atomic<int> g_switches{0};
+bool force_general() { return g_switches.load(std::memory_order_relaxed) & GEMM_TEST_FORCE_GENERAL; }
+bool no_splitk() { return g_switches.load(std::memory_order_relaxed) & GEMM_TEST_NO_SPLITK; }
+bool force_streamk() { return g_switches.load(std::memory_order_relaxed) & GEMM_TEST_FORCE_STREAMK; }
+bool f32_valu() { return g_switches.load(std::memory_order_relaxed) & GEMM_TEST_F32_VALU; }
 
 // The kernels a call can end in.
 enum class Kernel {
@@ -128,12 +106,12 @@ const char *kernel_name(Kernel k) {
 // kernel for at most 16 rows of C, split-K for other few-tile problems, the
 // direct-load kernel for aligned operands, the register-staged kernel for
 // everything else.
-Kernel choose(const Problem &p) {
+Kernel choose(const Problem &p, bool valu) {
     const bool splits = !force_general() && !no_splitk();
     if (elem_is_8bit(p.in))
         return !force_general() && f8gemm_dma_eligible(p) ? Kernel::F8Dma : Kernel::F8Mfma;
     if (p.in == Elem::F32) {
-        if (f32_valu()) return Kernel::SgemmValu;
+        if (valu || f32_valu()) return Kernel::SgemmValu;
         if (force_general()) return Kernel::SgemmMfma;
         if (splits && skinny_eligible(p)) return Kernel::Skinny;
         if (splits && sgemm_splitk_eligible(p)) return Kernel::SgemmSplitk;
@@ -176,7 +154,7 @@ gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K
                    const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                    float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
                    int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
-                   Problem &p, Kernel &kernel) {
+                   Problem &p, Kernel &kernel, bool valu = false) {
     kernel = Kernel::None;
     // ---- argument checks (no HIP call before this block is done)
     if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
@@ -262,7 +240,7 @@ gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K
         p.sB = strideA;
     }
 
-    kernel = reads_ab ? choose(p) : Kernel::Scale;
+    kernel = reads_ab ? choose(p, valu) : Kernel::Scale;
     return GEMM_OK;
 }
 
@@ -456,12 +434,13 @@ gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K,
                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                   float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
                   int64_t strideB, int64_t strideC, const void *bias, int64_t strideBias, int act,
-                  hipStream_t stream, void *workspace = nullptr, size_t workspace_bytes = 0) {
+                  hipStream_t stream, void *workspace = nullptr, size_t workspace_bytes = 0,
+                  bool valu = false) {
     Problem p;
     WsPlan w;
     gemm_status_t st =
         plan(in, in_b, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC,
-             batch, strideA, strideB, strideC, bias, strideBias, act, p, w.k);
+             batch, strideA, strideB, strideC, bias, strideBias, act, p, w.k, valu);
     if (st == GEMM_OK && w.k != Kernel::None)
         st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
                            strideC, bias, strideBias, A, B, C, workspace, workspace_bytes, w);
@@ -498,6 +477,21 @@ gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float
                        int64_t strideA, int64_t strideB, int64_t strideC, hipStream_t stream) {
     return run(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc,
                orderC, batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream);
+}
+
+gemm_status_t gemm_f32_valu(int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                            int64_t lda, gemm_order_t orderA, const float *B, int64_t ldb,
+                            gemm_order_t orderB, float beta, float *C, int64_t ldc,
+                            gemm_order_t orderC, int64_t batch, int64_t strideA, int64_t strideB,
+                            int64_t strideC, hipStream_t stream) {
+    return run(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta,
+               C, ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream,
+               nullptr, 0, true);
+}
+
+int gemm_test_switches(int flags) {
+    return g_switches.exchange(flags & (GEMM_TEST_FORCE_GENERAL | GEMM_TEST_NO_SPLITK |
+                                        GEMM_TEST_FORCE_STREAMK | GEMM_TEST_F32_VALU));
 }
 
 gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const float *A,

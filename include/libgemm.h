@@ -13,8 +13,8 @@
  * column-major-only convention of that library.
  *
  * Entry points
- *   gemm_f32   fp32 inputs, fp32 output, fp32 arithmetic (on the matrix cores;
- *              the vector-ALU kernel when LIBGEMM_F32_VALU=1 is set).
+ *   gemm_f32   fp32 inputs, fp32 output, fp32 arithmetic (on the matrix cores).
+ *   gemm_f32_valu  the same product on the vector ALUs (register-tiled).
  *   gemm_bf16  bf16 inputs, fp32 accumulation on the matrix cores, output in
  *              bf16 (c_dtype = GEMM_DTYPE_SAME) or fp32 (GEMM_DTYPE_F32).
  *   gemm_f16   the same for IEEE fp16 inputs.
@@ -24,12 +24,15 @@
  *   gemm_f8    8-bit float inputs (OCP E4M3 or E5M2, each operand in its own
  *              format), fp32 accumulation, output in fp32, bf16 or fp16.
  *   gemm_f32_ws, gemm_bf16_ws, gemm_f16_ws  the products with a caller-provided
- *              workspace, which lets the library run the stream-K schedule
- *              (see below); gemm_workspace_size gives the bytes it uses.
+ *              workspace, which lets the library copy unaligned operands
+ *              into aligned ones and run the stream-K schedule (see below);
+ *              gemm_workspace_size gives the bytes it needs.
+ *   gemm_bf16_noalloc  gemm_bf16_ws on the library's own scratch memory.
  *   gemm_kernel_name, gemm_f8_kernel_name, gemm_kernel_name_ws  which kernel
  *              a GEMM call with the
  *              given arguments would launch (host only; for tests and
  *              profiling).
+ *   gemm_test_switches  kernel-choice overrides for testing.
  *
  * Layout
  *   Each matrix has its own order.  Element (i, k) of A is at
@@ -260,17 +263,28 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
  * the same stream, which also applies the epilogue.  It is chosen when the
  * steps saved in the last wave outweigh that exchange (about four k steps of
  * one tile on the general kernels; on the direct-load one about 0.14 k steps
- * per partial tile plus two).  The environment variable
- * LIBGEMM_FORCE_STREAMK=1 chooses it wherever it can run (for testing).
+ * per partial tile plus two).  The testing switch
+ * GEMM_TEST_FORCE_STREAMK chooses it wherever it can run.
+ * Operands that are not 16-byte aligned (base, leading dimension, stride or
+ * contiguous extent), in a problem of at least 64 tiles of 256 x 256
+ * (bf16/fp16) or 160 tiles of 128 x 128 (fp32), are first copied into the
+ * workspace in the same order, zero-padded to whole 16-byte chunks along
+ * their contiguous dimension (K padded to a multiple of 8, resp. 4, with zero
+ * rows or columns), and the direct-load kernel (bf16/fp16: or its stream-K
+ * schedule, by the same cost model) runs on the copies, with the caller's M,
+ * N and C.  The zero padding adds nothing to any result.  This is chosen
+ * whenever the copies and any partial tiles fit the workspace; otherwise the
+ * general kernel runs on the caller's operands as described above.
  * Results are deterministic run to run; they may differ in rounding from
  * gemm_bf16 (the partial sums are grouped differently), within the same
  * accuracy.  Every other call ignores the workspace and behaves exactly like
  * gemm_bf16.
  *   workspace        device memory, 256-byte aligned, not overlapping A, B or
  *                    C; owned by the caller and clobbered by the call (it
- *                    holds partial tiles while the kernels run on
- *                    `stream`; calls that share a workspace must be ordered
- *                    on one stream).  NULL only with workspace_bytes = 0.
+ *                    holds operand copies and partial tiles while the
+ *                    kernels run on `stream`; calls that share a workspace
+ *                    must be ordered on one stream).  NULL only with
+ *                    workspace_bytes = 0.
  *   workspace_bytes  its size; smaller than gemm_workspace_size() (0
  *                    included) means the workspace is not used.
  * A misaligned, overlapping or NULL (with bytes > 0) workspace is
@@ -340,6 +354,39 @@ gemm_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
                                 gemm_dtype_t c_dtype, int64_t batch, int64_t strideA,
                                 int64_t strideB, int64_t strideC, hipStream_t stream);
 
+/* fp32 SGEMM on the vector ALUs: the register-tiled design of section 7 of
+ * "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site) -- LDS-staged 128 x 256 x 16
+ * tiles, an 8 x 16 tile of fused multiply-adds per thread -- instead of the
+ * matrix-core kernels gemm_f32 uses.  Arguments, semantics and errors are
+ * those of gemm_f32. */
+gemm_status_t gemm_f32_valu(int64_t M, int64_t N, int64_t K, float alpha,
+                            const float *A, int64_t lda, gemm_order_t orderA,
+                            const float *B, int64_t ldb, gemm_order_t orderB,
+                            float beta, float *C, int64_t ldc, gemm_order_t orderC,
+                            int64_t batch, int64_t strideA, int64_t strideB,
+                            int64_t strideC, hipStream_t stream);
+
+/* Testing aid: process-wide overrides of the kernel choice, so that tests
+ * can run every kernel on problems the normal choice sends elsewhere.  Not
+ * for production use.  The set holds until the next call; 0 (the initial
+ * state) clears every override.  Returns the previous set.  Every GEMM entry
+ * point and kernel-name query reads the set at each call.
+ *   GEMM_TEST_FORCE_GENERAL  every call on the general kernel of its type
+ *                            (no direct-load, split-K, skinny or stream-K
+ *                            kernel, no operand copies)
+ *   GEMM_TEST_NO_SPLITK      few-tile and skinny problems on the main kernels
+ *   GEMM_TEST_FORCE_STREAMK  workspace calls take the stream-K schedule
+ *                            wherever it can run, whatever its cost model says
+ *   GEMM_TEST_F32_VALU       fp32 calls on the vector-ALU kernel */
+typedef enum gemm_test_switch_t {
+    GEMM_TEST_FORCE_GENERAL = 1,
+    GEMM_TEST_NO_SPLITK = 2,
+    GEMM_TEST_FORCE_STREAMK = 4,
+    GEMM_TEST_F32_VALU = 8
+} gemm_test_switch_t;
+
+int gemm_test_switches(int flags);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *gemm_status_string(gemm_status_t status);
 
@@ -353,9 +400,8 @@ int gemm_abi_version(void);
  * "" when the call would return without launching anything (M, N or batch
  * is 0); NULL when the arguments are invalid (the GEMM call would return an
  * error status).  The choice depends on the shape, the orders, the
- * alignment of the pointers, leading dimensions and strides, and the
- * environment switches LIBGEMM_F32_VALU, LIBGEMM_FORCE_GENERAL and
- * LIBGEMM_NO_SPLITK, exactly as in the GEMM calls.  Pointers are compared
+ * alignment of the pointers, leading dimensions and strides, and the testing
+ * switches (gemm_test_switches), exactly as in the GEMM calls.  Pointers are compared
  * and tested for alignment but never dereferenced; no HIP call is made, so
  * this works without a GPU. */
 const char *gemm_kernel_name(gemm_input_t in, int64_t M, int64_t N, int64_t K,
@@ -368,8 +414,8 @@ const char *gemm_kernel_name(gemm_input_t in, int64_t M, int64_t N, int64_t K,
 
 /* The kernel that gemm_f8 would launch for the same arguments:
  * "f8gemm_mfma_dma", "f8gemm_mfma" or "scale"; "" and NULL as for
- * gemm_kernel_name (which also describes the environment switches; only
- * LIBGEMM_FORCE_GENERAL applies here). */
+ * gemm_kernel_name (of the testing switches, only GEMM_TEST_FORCE_GENERAL
+ * applies here). */
 const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
                                 const uint8_t *A, int64_t lda,
                                 gemm_order_t orderA, gemm_f8_format_t formatA,
@@ -384,8 +430,10 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
  * gemm_bf16_ws (GEMM_INPUT_BF16) or gemm_f16_ws (GEMM_INPUT_F16) would
  * launch: the names of gemm_kernel_name, or "hgemm_mfma_streamk",
  * "hgemm_mfma_dma_streamk" or "sgemm_mfma_streamk" for the stream-K
- * schedules; "" and NULL as for gemm_kernel_name, whose environment
- * switches apply, and so does LIBGEMM_FORCE_STREAMK.  The workspace is only
+ * schedules, "hgemm_mfma_dma_packed", "hgemm_mfma_dma_streamk_packed" or
+ * "sgemm_mfma_dma_packed" when the operands are first copied into the
+ * workspace; "" and NULL as for gemm_kernel_name, whose testing switches
+ * apply, GEMM_TEST_FORCE_STREAMK included.  The workspace is only
  * checked, never dereferenced. */
 const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K,
                                 float alpha, const void *A, int64_t lda,

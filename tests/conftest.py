@@ -28,3 +28,25 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def switches():
+    """Set libgemm's kernel-choice overrides for one test (binding.TEST_*
+    flags, or'ed); they are cleared again when the test ends."""
+    from dense_gemm_optimisation_amd import binding
+    state = {"flags": 0}
+
+    def set_(*flags):
+        f = 0
+        for x in flags:
+            f |= x
+        state["flags"] = f
+        binding.test_switches(f)
+    set_.clear = lambda: set_()
+    set_.add = lambda flag: set_(state["flags"] | flag)
+    set_.drop = lambda flag: set_(state["flags"] & ~flag)
+    binding.test_switches(0)
+    yield set_
+    binding.test_switches(0)
+

@@ -245,6 +245,9 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
                                  p.ldb, p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch,
                                  p.stride_a, p.stride_b, p.stride_c, b_dtype=p.b_dtype,
                                  out_dtype=p.c_dtype, **ws)
+    valu = p.entry == "valu"  # gemm_f32_valu runs the vector-ALU kernel whatever the shape
+    if valu and kernel not in ("", "scale", None):
+        kernel = "sgemm_valu"
     outs = []
     for r in range(repeat):
         if r:
@@ -252,7 +255,7 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         binding.gemm(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
                      p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch, p.stride_a,
                      p.stride_b, p.stride_c, bias=pbias, stride_bias=p.stride_bias, act=p.act,
-                     b_dtype=p.b_dtype, out_dtype=p.c_dtype, **ws)
+                     b_dtype=p.b_dtype, out_dtype=p.c_dtype, valu=valu, **ws)
         torch.cuda.synchronize()
         outs.append(dc.cpu().numpy().view(fc.dtype).copy())
     out = outs[0]

@@ -30,11 +30,12 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
                                     "gemm_bf16_noalloc", "gemm_bf16_ws", "gemm_f16",
                                     "gemm_f16_bias_act",
-                                    "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act", "gemm_f32_ws",
+                                    "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act",
+                                    "gemm_f32_valu", "gemm_f32_ws",
                                     "gemm_f8",
                                     "gemm_f8_kernel_name", "gemm_kernel_name",
                                     "gemm_kernel_name_ws", "gemm_status_string",
-                                    "gemm_workspace_size"]
+                                    "gemm_test_switches", "gemm_workspace_size"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -210,10 +211,10 @@ def kname(lib, dt, M, N, K, alpha=1.0, oa=0, ob=0, oc=0, lda=None, ldb=None, ldc
 
 
 @pytest.fixture
-def clean_env(monkeypatch):
-    for v in ("LIBGEMM_F32_VALU", "LIBGEMM_FORCE_GENERAL", "LIBGEMM_NO_SPLITK", "LIBGEMM_FORCE_STREAMK"):
-        monkeypatch.delenv(v, raising=False)
-    return monkeypatch
+def clean_env(switches):
+    """No kernel-choice override is set (the switches fixture clears them
+    before and after the test)."""
+    return switches
 
 
 KERNEL_CASES = [
@@ -272,22 +273,29 @@ def test_kernel_choice(lib, clean_env, case):
     assert kname(lib, dt, M, N, K, **kw) == want
 
 
-def test_kernel_choice_environment_switches(lib, clean_env):
-    clean_env.setenv("LIBGEMM_NO_SPLITK", "1")
+def test_kernel_choice_testing_switches(lib, clean_env):
+    clean_env(lib.TEST_NO_SPLITK)
     assert kname(lib, "f32", 256, 256, 256) == "sgemm_mfma_dma"
     assert kname(lib, "bf16", 16, 4096, 4096) == "hgemm_mfma_dma"
-    clean_env.delenv("LIBGEMM_NO_SPLITK")
-    clean_env.setenv("LIBGEMM_FORCE_GENERAL", "1")
+    clean_env(lib.TEST_FORCE_GENERAL)
     assert kname(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma"
     assert kname(lib, "bf16", 16, 4096, 4096) == "hgemm_mfma"
     assert kname(lib, "e4m3", 4096, 4096, 4096, ob=1) == "f8gemm_mfma"
-    clean_env.delenv("LIBGEMM_FORCE_GENERAL")
-    clean_env.setenv("LIBGEMM_NO_SPLITK", "1")
+    clean_env(lib.TEST_NO_SPLITK)
     assert kname(lib, "e4m3", 4096, 4096, 4096, ob=1) == "f8gemm_mfma_dma"
-    clean_env.delenv("LIBGEMM_NO_SPLITK")
-    clean_env.setenv("LIBGEMM_F32_VALU", "1")
+    clean_env(lib.TEST_F32_VALU)
     assert kname(lib, "f32", 16, 4096, 4096, ob=1) == "sgemm_valu"
     assert kname(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"
+    # the setter returns the previous set; flags outside the four are dropped
+    assert lib.test_switches(0xff) == lib.TEST_F32_VALU
+    assert lib.test_switches(0) == 15
+    # an environment variable no longer changes anything
+    import os
+    os.environ["LIBGEMM_FORCE_GENERAL"] = "1"
+    try:
+        assert kname(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma_dma"
+    finally:
+        del os.environ["LIBGEMM_FORCE_GENERAL"]
 
 
 def test_kernel_choice_for_every_workload(lib, clean_env):
@@ -300,7 +308,9 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_ffn_down": "hgemm_mfma_dma", "f32_edge": "sgemm_mfma",
             "bf16_edge": "hgemm_mfma", "bf16_tail": "hgemm_mfma_dma", "bf16_skinny": "gemm_skinny",
             "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma",
-            "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma"}
+            "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma",
+            # called through gemm_f32_valu; gemm_kernel_name describes gemm_f32
+            "f32_4096_valu": "sgemm_mfma_dma"}
     assert sorted(want) == sorted(workloads.CONFIGS)
     for name, k in want.items():
         p = workloads.config(name)
@@ -369,15 +379,15 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
     assert kname_ws(lib, "bf16", 4096, 4352, 256) == "hgemm_mfma_dma"       # 4 steps per tile
     assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # whole waves
-    # LIBGEMM_FORCE_STREAMK=1 skips the cost model, not the structural checks
-    clean_env.setenv("LIBGEMM_FORCE_STREAMK", "1")
+    # GEMM_TEST_FORCE_STREAMK skips the cost model, not the structural checks
+    clean_env(lib.TEST_FORCE_STREAMK)
     assert kname_ws(lib, "f16", 2048, 2304, 1024, oa=1, ob=1) == "hgemm_mfma_dma_streamk"
     assert kname_ws(lib, "bf16", 4096, 4352, 256) == "hgemm_mfma_dma_streamk"
     assert kname_ws(lib, "bf16", 300, 290, 131) == "hgemm_mfma_streamk"
     assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # nothing to cut
     assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
     assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_dma_streamk_packed"
-    clean_env.delenv("LIBGEMM_FORCE_STREAMK")
+    clean_env(0)
     # fp32: unaligned with at least 160 tiles of 128 x 128 is copied for the
     # direct-load kernel; fewer tiles use the general kernel's schedule
     # (128 x 128 tiles, 1024 workgroups)
@@ -389,7 +399,7 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "f32", 4095, 4097, 1001, nbytes=1 << 20) == "sgemm_mfma"
     # K = 0 scales C
     assert kname_ws(lib, "bf16", 4095, 4097, 0, lda=1) == "scale"
-    clean_env.setenv("LIBGEMM_FORCE_GENERAL", "1")
+    clean_env(lib.TEST_FORCE_GENERAL)
     assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma"
 
 

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import workloads
+from dense_gemm_optimisation_amd import binding
 from workloads import COL, ROW, Problem
 
 from parity import log, run
@@ -238,11 +239,11 @@ DMA_SHAPES = [(8, 8, 8), (256, 256, 64), (264, 520, 72), (512, 256, 128), (1000,
 @pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
                          ids=lambda o: "%d%d" % o)
-def test_direct_load_path_ragged_aligned(monkeypatch, dt, shape, orders):
+def test_direct_load_path_ragged_aligned(switches, dt, shape, orders):
     # extents multiples of 8 but not of the 256 x 256 x 64 tile: the direct
     # loads' range check and the last-stage k mask produce the edge zeros
     # (few-tile shapes kept off the split-K kernel)
-    monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
+    switches(binding.TEST_NO_SPLITK)
     M, N, K = shape
     oa, ob = orders
     check(P(f"dma-{dt}", dt, M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob),
@@ -257,9 +258,9 @@ def test_direct_load_path_fp32_out_and_col_major_c(dt):
           kernel="hgemm_mfma_dma", seed=32)
 
 
-def test_general_kernel_forced_on_aligned_problem(monkeypatch):
+def test_general_kernel_forced_on_aligned_problem(switches):
     # the same aligned problem through the general kernel (register-staged)
-    monkeypatch.setenv("LIBGEMM_FORCE_GENERAL", "1")
+    switches(binding.TEST_FORCE_GENERAL)
     check(P("forced-general-bf16", "bf16", 512, 768, 320, beta=1.0), kernel="hgemm_mfma", seed=33)
 
 
@@ -272,19 +273,19 @@ F32_DMA_SHAPES = [(4, 4, 4), (128, 128, 16), (132, 260, 20), (260, 132, 1000), (
 @pytest.mark.parametrize("shape", F32_DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
                          ids=lambda o: "%d%d" % o)
-def test_f32_direct_load_path_ragged_aligned(monkeypatch, shape, orders):
+def test_f32_direct_load_path_ragged_aligned(switches, shape, orders):
     # extents multiples of 4 but not of the 128 x 128 x 16 tile: the direct
     # loads' range check and the last-stage k mask produce the edge zeros
     # (few-tile shapes kept off the split-K kernel)
-    monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
+    switches(binding.TEST_NO_SPLITK)
     M, N, K = shape
     oa, ob = orders
     check(P("dma-f32", "f32", M, N, K, alpha=0.5, beta=1.0, order_a=oa, order_b=ob),
           kernel="sgemm_mfma_dma", seed=M + N + K)
 
 
-def test_f32_direct_load_path_batch_and_col_major_c(monkeypatch):
-    monkeypatch.setenv("LIBGEMM_NO_SPLITK", "1")
+def test_f32_direct_load_path_batch_and_col_major_c(switches):
+    switches(binding.TEST_NO_SPLITK)
     check(P("dma-f32-batch", "f32", 260, 132, 200, beta=-1.0, batch=3), kernel="sgemm_mfma_dma",
           seed=51)
     check(P("dma-f32-colC", "f32", 260, 132, 200, order_c=COL, beta=0.25), kernel="sgemm_mfma_dma",
@@ -294,17 +295,64 @@ def test_f32_direct_load_path_batch_and_col_major_c(monkeypatch):
     assert res.max_err == 0.0
 
 
-@pytest.mark.parametrize("env", ["LIBGEMM_FORCE_GENERAL", "LIBGEMM_F32_VALU"])
+@pytest.mark.parametrize("env", ["force_general", "f32_valu"])
 @pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
                          ids=lambda o: "%d%d" % o)
-def test_f32_other_kernels_forced_on_aligned_problem(monkeypatch, env, orders):
+def test_f32_other_kernels_forced_on_aligned_problem(switches, env, orders):
     # the aligned problem the direct-load kernel would take, through the
     # register-staged matrix-core kernel and through the vector-ALU kernel
-    monkeypatch.setenv(env, "1")
+    switches({"force_general": binding.TEST_FORCE_GENERAL, "f32_valu": binding.TEST_F32_VALU}[env])
     oa, ob = orders
-    want = {"LIBGEMM_FORCE_GENERAL": "sgemm_mfma", "LIBGEMM_F32_VALU": "sgemm_valu"}[env]
+    want = {"force_general": "sgemm_mfma", "f32_valu": "sgemm_valu"}[env]
     check(P(f"forced-{env}", "f32", 520, 392, 300, beta=1.0, order_a=oa, order_b=ob), kernel=want,
           seed=54)
+
+
+# ------------------------------------------------------------------ vector-ALU fp32 kernel (register tiles)
+
+# The register-tiled vector-ALU kernel (128 x 256 x 16 block tiles, 8 x 16
+# outputs per thread) on the shapes, layouts and edges the matrix-core fp32
+# kernels are held to; the switch routes every fp32 call to it.
+VALU_SHAPES = [(1, 1, 1), (7, 9, 13), (31, 33, 17), (127, 129, 65), (129, 255, 200),
+               (255, 257, 63), (300, 290, 130), (513, 130, 77), (33, 70, 1000)]
+
+
+@pytest.mark.parametrize("shape", VALU_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (COL, COL)], ids=lambda o: "%d%d" % o)
+def test_valu_kernel_shapes(switches, shape, orders):
+    switches(binding.TEST_F32_VALU)
+    M, N, K = shape
+    oa, ob = orders
+    check(P("valu", "f32", M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
+          kernel="sgemm_valu", seed=M + N + K + 11)
+
+
+def test_valu_kernel_misaligned_batches_col_major_c_and_integers(switches):
+    switches(binding.TEST_F32_VALU)
+    check(P("valu-misaligned", "f32", 190, 211, 97, beta=1.0, lda=99, ldb=213, ldc=215),
+          kernel="sgemm_valu", seed=120, base_offset=(1, 3, 1))
+    for bcast in ("none", "a", "b"):
+        kw = {"stride_a": 0} if bcast == "a" else {"stride_b": 0} if bcast == "b" else {}
+        check(P(f"valu-batch-{bcast}", "f32", 130, 260, 90, batch=3, beta=1.0,
+                stride_c=130 * 260 + 17, **kw), kernel="sgemm_valu", seed=121)
+    check(P("valu-colC", "f32", 300, 290, 130, order_c=COL, ldc=303, beta=0.5),
+          kernel="sgemm_valu", seed=122)
+    p = P("valu-int", "f32", 300, 517, 260, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="sgemm_valu", host=_int_host(p, np.random.default_rng(123)))
+    assert res.max_err == 0.0
+
+
+@pytest.mark.parametrize("name", ["f32_4096", "f32_edge"])
+def test_valu_kernel_full_configs_sampled(switches, name):
+    switches(binding.TEST_F32_VALU)
+    check(workloads.config(name), kernel="sgemm_valu", sample="auto")
+
+
+def test_valu_entry_point():
+    # gemm_f32_valu itself, without the switch, on the 4096^3 headline problem
+    p = workloads.config("f32_4096_valu")
+    res, _ = check(p, sample="auto")
+    assert res.ok
 
 
 # ------------------------------------------------------------------ skinny path (at most 16 rows of C)
@@ -398,8 +446,8 @@ def test_fused_epilogue_without_product_term(dt):
           seed=86)
 
 
-def test_fused_epilogue_on_vector_alu_kernel(monkeypatch):
-    monkeypatch.setenv("LIBGEMM_F32_VALU", "1")
+def test_fused_epilogue_on_vector_alu_kernel(switches):
+    switches(binding.TEST_F32_VALU)
     check(P("epi-valu", "f32", 520, 264, 200, beta=0.5, bias=True, act=GELU),
           kernel="sgemm_valu", seed=87)
 
@@ -544,16 +592,16 @@ def test_f8_padded_ld_and_misaligned_bases(orders):
     check(p.with_(name="f8-misaligned"), kernel="f8gemm_mfma", seed=64, base_offset=(1, 3, 1))
 
 
-def test_f8_general_kernel_forced_on_aligned_problem(monkeypatch):
-    monkeypatch.setenv("LIBGEMM_FORCE_GENERAL", "1")
+def test_f8_general_kernel_forced_on_aligned_problem(switches):
+    switches(binding.TEST_FORCE_GENERAL)
     check(F8("f8-forced", "e5m2", "e4m3", "f16", 1000, 1032, 1008, beta=1.0, **TN),
           kernel="f8gemm_mfma", seed=65)
 
 
 @pytest.mark.parametrize("kernel", ["f8gemm_mfma_dma", "f8gemm_mfma"])
-def test_f8_batches_and_col_major_c(monkeypatch, kernel):
+def test_f8_batches_and_col_major_c(switches, kernel):
     if kernel == "f8gemm_mfma":
-        monkeypatch.setenv("LIBGEMM_FORCE_GENERAL", "1")
+        switches(binding.TEST_FORCE_GENERAL)
     M, N, K = 130, 264, 96
     check(F8("f8-batch", "e4m3", "e5m2", "f32", M, N, K, batch=3, beta=1.0,
              stride_c=M * N + 17, **TN), kernel=kernel, seed=66)
@@ -602,11 +650,11 @@ def test_f8_repeat_runs_bit_identical():
 
 
 @pytest.mark.parametrize("kernel", ["f8gemm_mfma_dma", "f8gemm_mfma"])
-def test_f8_nan_and_infinity_propagate(monkeypatch, kernel):
+def test_f8_nan_and_infinity_propagate(switches, kernel):
     # A NaN in A makes its row of C NaN; an E5M2 infinity at A(i, k) makes
     # C(i, j) an infinity of the sign of B(k, j), or NaN where B(k, j) == 0.
     if kernel == "f8gemm_mfma":
-        monkeypatch.setenv("LIBGEMM_FORCE_GENERAL", "1")
+        switches(binding.TEST_FORCE_GENERAL)
     M, N, K = 64, 72, 96
     p = F8("f8-special", "e5m2", "e5m2", "f32", M, N, K, **TN)
     a, b, c = workloads.generate(p, seed=74)
@@ -709,13 +757,13 @@ def test_streamk_whole_waves_and_cut_tail(dt):
 # leading dimensions multiples of 8 elements) and at least 64 tiles (fewer
 # go to the split-K kernel).  Its cost model only picks it for large
 # problems with a short cut wave (the bf16_tail workload below), so these
-# small cases switch the model off (LIBGEMM_FORCE_STREAMK=1).
+# small cases switch the model off (the GEMM_TEST_FORCE_STREAMK switch).
 DMA_SK_SHAPES = [(2048, 2304, 1024), (2304, 2048, 1536)]
 
 
 @pytest.fixture
-def force_streamk(monkeypatch):
-    monkeypatch.setenv("LIBGEMM_FORCE_STREAMK", "1")
+def force_streamk(switches):
+    switches(binding.TEST_FORCE_STREAMK)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
