@@ -195,19 +195,36 @@ def cpu_model():
 
 
 def error_stats(p, got_bits, ref, den):
-    """Error of GPU results (stored bit patterns) against oracle values."""
+    """Error of GPU results (stored bit patterns) against oracle values, by
+    the tolerances the parity tests apply: fp32 output |C - ref| / den; 16-bit
+    output the distance in units in the last place from the oracle rounded
+    to that type, where an element beyond 2 ulp is accepted only as a genuine
+    cancellation (|ref| <= 2^-8 den and |C - ref| <= 2 ulp + 1e-3 den; for
+    8-bit inputs, whose instruction truncates small products, only the
+    second condition)."""
     import oracle
-    if p.c_dtype == "f32":
-        got = got_bits.view(np.float32).astype(np.float64)
-        with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        if p.c_dtype == "f32":
+            got = got_bits.view(np.float32).astype(np.float64)
             err = np.where(den > 0, np.abs(got - ref) / np.where(den > 0, den, 1.0),
                            np.where(got == ref, 0.0, np.inf))
-        return {"max_norm_err": float(err.max()), "elements": int(ref.size)}
-    q = oracle.round_bits(p.c_dtype, ref).astype(np.int64)
-    g = got_bits.view(np.uint16).astype(np.int64)
-    key = lambda b: np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
-    d = np.abs(key(g) - key(q))
-    return {"max_ulp": int(d.max()), "beyond_2ulp": int((d > 2).sum()), "elements": int(ref.size)}
+            return {"max_norm_err": float(err.max()), "elements": int(ref.size)}
+        q = oracle.round_bits(p.c_dtype, ref).astype(np.int64)
+        g = got_bits.view(np.uint16).astype(np.int64)
+        key = lambda b: np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+        d = np.abs(key(g) - key(q))
+        gv = oracle.decode(p.c_dtype, g.astype(np.uint16))
+        qv = oracle.decode(p.c_dtype, q.astype(np.uint16))
+        ulp = np.abs(oracle.decode(p.c_dtype, (q + 1).astype(np.uint16)) - qv)
+        near = np.abs(gv - ref) <= 2 * ulp + 1e-3 * den
+        if p.in_dtype not in ("e4m3", "e5m2"):
+            near &= np.abs(ref) <= 2.0 ** -8 * den
+        bad = d > 2
+        norm = np.where(den > 0, np.abs(gv - ref) / np.where(den > 0, den, 1.0), 0.0)
+    return {"max_ulp": int(d.max()), "beyond_2ulp": int(bad.sum()),
+            "accepted_cancellations": int((bad & near).sum()),
+            "violations": int((bad & ~near).sum()), "max_norm_err": float(norm.max()),
+            "elements": int(ref.size)}
 
 
 def cpu_baseline(problems, budget_s, gpu_results):
@@ -309,24 +326,29 @@ def smi():
             "hotspot_c": val(temp.get("hotspot")), "mem_c": val(temp.get("mem"))}
 
 
-def clocks_under_load(fn, torch, seconds=1.5):
-    """amd-smi readings taken while `fn` runs back to back for `seconds`."""
+def clocks_under_load(fn, torch, seconds=3.0):
+    """amd-smi readings taken while `fn` runs back to back for `seconds`
+    (amd-smi reports values that trail the hardware by up to a second, so two
+    readings are taken after the load has run a while, and the one drawing
+    more power is kept)."""
     import threading
     stop = threading.Event()
 
     def loop():
         while not stop.is_set():
-            for _ in range(64):
+            for _ in range(256):
                 fn()
             torch.cuda.synchronize()
     th = threading.Thread(target=loop)
     th.start()
-    time.sleep(seconds / 3)
-    reading = smi()
-    time.sleep(seconds / 3)
+    time.sleep(seconds * 0.4)
+    first = smi()
+    time.sleep(seconds * 0.3)
+    second = smi()
     stop.set()
     th.join()
-    return reading
+    readings = [r for r in (first, second) if r]
+    return max(readings, key=lambda r: r.get("power_w") or 0) if readings else None
 
 
 def main():
