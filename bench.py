@@ -67,6 +67,8 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "hgemm_mfma_dma_packed": "hgemm_mfma_dma.hip",
                  "hgemm_mfma_dma_streamk_packed": "hgemm_mfma_dma.hip",
                  "sgemm_mfma_dma_packed": "sgemm_mfma.hip",
+                 "sgemm_mfma_dma_streamk": "sgemm_mfma.hip",
+                 "sgemm_mfma_dma_streamk_packed": "sgemm_mfma.hip",
                  "scale": "scale.hip"}
 
 
@@ -150,10 +152,25 @@ def kernel_family(p, bufs, workspace=None):
 
 
 def source_hash(family):
+    """Hash of the source file that defines the kernel family and of every
+    header of the package it includes, directly or not (the kernel's code
+    lives in both)."""
     import hashlib
-    path = os.path.join(ROOT, "dense_gemm_optimisation_amd", "csrc", KERNEL_SOURCE[family])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    csrc = os.path.join(ROOT, "dense_gemm_optimisation_amd", "csrc")
+    h = hashlib.sha256()
+    todo, seen = [KERNEL_SOURCE[family]], set()
+    while todo:
+        name = todo.pop(0)
+        path = os.path.join(csrc, name)
+        if name in seen or not os.path.exists(path):
+            continue
+        seen.add(name)
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(name.encode() + b"\0" + data)
+        todo += [m.decode() for m in re.findall(rb'#include "([^"]+)"', data)]
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(family, workload):

@@ -68,14 +68,17 @@ enum class Kernel {
     HgemmStreamK,  // bf16/fp16 general kernel on the stream-K schedule (workspace)
     HgemmDmaStreamK,  // bf16/fp16 direct-load kernel on the stream-K schedule (workspace)
     SgemmStreamK,  // fp32 general kernel on the stream-K schedule (workspace)
+    SgemmDmaStreamK,  // fp32 direct-load kernel on the stream-K schedule (workspace)
     // operands copied into aligned, zero-padded copies in the workspace first
     HgemmPackDma,         // then the bf16/fp16 direct-load kernel
     HgemmPackDmaStreamK,  // then its stream-K schedule
     SgemmPackDma,         // then the fp32 direct-load kernel
+    SgemmPackDmaStreamK,  // then its stream-K schedule
 };
 
 bool is_packed(Kernel k) {
-    return k == Kernel::HgemmPackDma || k == Kernel::HgemmPackDmaStreamK || k == Kernel::SgemmPackDma;
+    return k == Kernel::HgemmPackDma || k == Kernel::HgemmPackDmaStreamK ||
+           k == Kernel::SgemmPackDma || k == Kernel::SgemmPackDmaStreamK;
 }
 
 const char *kernel_name(Kernel k) {
@@ -95,9 +98,11 @@ const char *kernel_name(Kernel k) {
     case Kernel::HgemmStreamK: return "hgemm_mfma_streamk";
     case Kernel::HgemmDmaStreamK: return "hgemm_mfma_dma_streamk";
     case Kernel::SgemmStreamK: return "sgemm_mfma_streamk";
+    case Kernel::SgemmDmaStreamK: return "sgemm_mfma_dma_streamk";
     case Kernel::HgemmPackDma: return "hgemm_mfma_dma_packed";
     case Kernel::HgemmPackDmaStreamK: return "hgemm_mfma_dma_streamk_packed";
     case Kernel::SgemmPackDma: return "sgemm_mfma_dma_packed";
+    case Kernel::SgemmPackDmaStreamK: return "sgemm_mfma_dma_streamk_packed";
     }
     return "";
 }
@@ -140,9 +145,11 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::HgemmStreamK:
     case Kernel::HgemmDmaStreamK:
     case Kernel::SgemmStreamK:
+    case Kernel::SgemmDmaStreamK:
     case Kernel::HgemmPackDma:
     case Kernel::HgemmPackDmaStreamK:
-    case Kernel::SgemmPackDma: return hipErrorInvalidValue;  // need the workspace: run()
+    case Kernel::SgemmPackDma:
+    case Kernel::SgemmPackDmaStreamK: return hipErrorInvalidValue;  // need the workspace: run()
     }
     return hipErrorInvalidValue;
 }
@@ -181,6 +188,11 @@ gemm_status_t plan(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K
     const int64_t span_c = span(M, N, orderC, ldc);
     if (C == nullptr) return GEMM_ERR_INVALID_ARG;
     if (reads_ab && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_ARG;
+    // every pointer at a multiple of its element size
+    auto misaligned = [](const void *x, int e) { return reinterpret_cast<uintptr_t>(x) % e != 0; };
+    if (misaligned(C, eout) || (reads_ab && (misaligned(A, ein) || misaligned(B, ein_b))) ||
+        (bias != nullptr && misaligned(bias, ein)))
+        return GEMM_ERR_INVALID_ARG;
     if (batch > 1 && strideC < span_c) return GEMM_ERR_INVALID_ARG;  // C slices overlap
     if (too_big(batch - 1, strideC) || too_big(batch - 1, strideA) || too_big(batch - 1, strideB) ||
         too_big(batch - 1, strideBias))
@@ -311,7 +323,7 @@ Problem packed_problem(const Problem &p, const PackSpec &sa, const PackSpec &sb,
 bool plan_packed(const Problem &p, Kernel k, const void *workspace, size_t bytes, bool force,
                  WsPlan &w) {
     const bool h16 = k == Kernel::HgemmMfma || k == Kernel::HgemmStreamK;
-    const bool f32 = k == Kernel::SgemmMfma || k == Kernel::SgemmStreamK;
+    const bool f32 = k == Kernel::SgemmMfma;
     if (!h16 && !f32) return false;
     const int esize = elem_bytes(p.in);
     const int64_t tile = h16 ? 256 : 128;
@@ -340,16 +352,14 @@ bool plan_packed(const Problem &p, Kernel k, const void *workspace, size_t bytes
         return true;
     };
     if (!place(0, h16 ? Kernel::HgemmPackDma : Kernel::SgemmPackDma)) return false;
-    if (h16) {
-        if (!hgemm_dma_eligible(w.q)) return false;
-        if (hgemm_dma_streamk_eligible(w.q, force)) {
-            const int64_t partials = round_up(hgemm_dma_streamk_bytes(w.q), 256);
-            WsPlan keep = w;
-            if (!place(partials, Kernel::HgemmPackDmaStreamK)) w = keep;  // no room: plain schedule
-        }
-        return true;
+    if (!(h16 ? hgemm_dma_eligible(w.q) : sgemm_dma_eligible(w.q))) return false;
+    if (h16 ? hgemm_dma_streamk_eligible(w.q, force) : sgemm_dma_streamk_eligible(w.q, force)) {
+        const int64_t partials = round_up(h16 ? hgemm_dma_streamk_bytes(w.q) : sgemm_streamk_bytes(w.q), 256);
+        WsPlan keep = w;
+        if (!place(partials, h16 ? Kernel::HgemmPackDmaStreamK : Kernel::SgemmPackDmaStreamK))
+            w = keep;  // no room: plain schedule
     }
-    return sgemm_dma_eligible(w.q);
+    return true;
 }
 
 // The checks of a workspace argument: 256-byte aligned, not NULL when it has
@@ -376,9 +386,8 @@ gemm_status_t check_workspace(const Problem &p, int64_t M, int64_t N, int64_t K,
 // The plan for a checked workspace of `bytes` bytes at `workspace` (only its
 // address is used, to place the operand copies).  Unaligned operands of large
 // problems are copied into aligned buffers for the direct-load kernels
-// (plan_packed); otherwise the 16-bit kernels (the direct-load and the
-// general one) and the general fp32 kernel switch to their stream-K schedule
-// where it applies.  w.k holds the kernel chosen without a workspace.
+// (plan_packed); otherwise the 16-bit and fp32 kernels (the direct-load and
+// the general ones) switch to their stream-K schedule where it applies.  w.k holds the kernel chosen without a workspace.
 void plan_workspace(const Problem &p, const void *workspace, size_t bytes, WsPlan &w) {
     w.q = p;
     w.used = 0;
@@ -395,6 +404,9 @@ void plan_workspace(const Problem &p, const void *workspace, size_t bytes, WsPla
         w.used = hgemm_dma_streamk_bytes(p);
     } else if (k == Kernel::SgemmMfma && sgemm_streamk_eligible(p, force)) {
         k = Kernel::SgemmStreamK;
+        w.used = sgemm_streamk_bytes(p);
+    } else if (k == Kernel::SgemmDma && sgemm_dma_streamk_eligible(p, force)) {
+        k = Kernel::SgemmDmaStreamK;
         w.used = sgemm_streamk_bytes(p);
     }
 }
@@ -424,6 +436,8 @@ hipError_t launch_planned(const WsPlan &w, void *workspace, hipStream_t stream) 
     case Kernel::HgemmDmaStreamK:
     case Kernel::HgemmPackDmaStreamK: return launch_hgemm_dma_streamk(w.q, workspace, stream);
     case Kernel::SgemmStreamK: return launch_sgemm_streamk(w.q, workspace, stream);
+    case Kernel::SgemmDmaStreamK:
+    case Kernel::SgemmPackDmaStreamK: return launch_sgemm_dma_streamk(w.q, workspace, stream);
     case Kernel::HgemmPackDma: return launch_hgemm_dma(w.q, stream);
     case Kernel::SgemmPackDma: return launch_sgemm_dma(w.q, stream);
     default: return launch(w.k, w.q, stream);

@@ -35,6 +35,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+// 16-byte chunks of C at element alignment only: a row of C starts wherever
+// ldc puts it, and the memory system takes a 16-byte access at any
+// element-aligned address (it splits one that straddles a cache line).
+typedef float f32x4_ea __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4_ea __attribute__((ext_vector_type(4), aligned(2)));
 
 constexpr int BM = 256, BN = 256;       // block tile (rows of A and columns of B)
 constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2;
@@ -48,7 +53,6 @@ struct DmaArgs {
     int64_t lda, ldb, ldc;
     int64_t sA, sB, sC;
     TileGrid grid;
-    int vec_c;
     Epilogue epi;
     int64_t span_a, span_b;  // elements of one slice of A and of B the loads may touch
 };
@@ -169,9 +173,9 @@ struct Operand {
 // that every lane owns 16 contiguous bytes of one output row: a store
 // instruction then writes whole rows of the strip (8 rows of 128 bytes for
 // a 64-column bf16 strip) instead of 32 rows of 16 bytes, and C_old is read
-// the same way when beta != 0.  Rows or columns outside C are skipped, and a
-// chunk that crosses the right edge of C, or any chunk when C's rows are not
-// 16-byte aligned, is stored element by element.
+// the same way when beta != 0, at any element alignment of C's rows.  Rows
+// or columns outside C are skipped, and the chunk that crosses the right
+// edge of C is stored element by element.
 template <int OUT, int FM, int FN>
 __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][FN], int64_t batch,
                                       int64_t mw, int64_t nw, int lane, LDS float *scratch) {
@@ -247,23 +251,23 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
             }
             if (m >= p.M || n >= p.N) continue;
             const int64_t off = m * p.ldc + n;
-            if (p.vec_c && n + CW <= p.N) {
+            if (n + CW <= p.N) {
                 if (OUT == OUT_F32) {
                     float *c = reinterpret_cast<float *>(Cb) + off;
                     f32x4 v = {x[0], x[1], x[2], x[3]};
                     if (p.beta != 0.0f) {
-                        const f32x4 o = *reinterpret_cast<const f32x4 *>(c);
+                        const f32x4 o = *reinterpret_cast<const f32x4_ea *>(c);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, o[e], v[e]);
                     }
                     if (epi)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = finish(v[e], i, it, e);
-                    *reinterpret_cast<f32x4 *>(c) = v;
+                    *reinterpret_cast<f32x4_ea *>(c) = v;
                 } else {
                     uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off;
                     if (p.beta != 0.0f) {
-                        const u32x4 o = *reinterpret_cast<const u32x4 *>(c);
+                        const u32x4 o = *reinterpret_cast<const u32x4_ea *>(c);
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             x[e] = __builtin_fmaf(p.beta, dec(uint16_t(o[e / 2] >> (16 * (e % 2)))), x[e]);
@@ -274,10 +278,12 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
                     u32x4 w;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = uint32_t(enc(x[2 * e])) | (uint32_t(enc(x[2 * e + 1])) << 16);
-                    *reinterpret_cast<u32x4 *>(c) = w;
+                    *reinterpret_cast<u32x4_ea *>(c) = w;
                 }
             } else {
-                const int nvalid = p.N - n < CW ? int(p.N - n) : CW;
+                // element by element (a loop that keeps this rare path
+                // small: unrolled, it pushes the accumulators into scratch)
+                const int nvalid = int(p.N - n);
                 for (int e = 0; e < nvalid; ++e) {
                     if (OUT == OUT_F32) {
                         float *c = reinterpret_cast<float *>(Cb) + off + e;

@@ -457,8 +457,6 @@ DmaArgs common_args(const Problem &p, int64_t tile, int group_m) {
     a.sB = p.batch > 1 ? p.sB : 0;
     a.sC = p.batch > 1 ? p.sC : 0;
     a.grid = TileGrid{(p.M + tile - 1) / tile, (p.N + tile - 1) / tile, p.batch, group_m, 8};
-    const int cw = 16 / elem_bytes(p.out);  // output elements per 16-byte chunk
-    a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % 16) == 0 && p.ldc % cw == 0 && a.sC % cw == 0;
     a.epi = p.epi;
     return a;
 }

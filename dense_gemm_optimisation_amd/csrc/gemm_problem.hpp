@@ -103,8 +103,13 @@ hipError_t launch_sgemm_splitk(const Problem &p, hipStream_t stream);
 constexpr int64_t SGEMM_STREAMK_MAX_GRID = 1024;
 bool sgemm_streamk_eligible(const Problem &p, bool force = false);
 hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream);
-// Workspace bytes launch_sgemm_streamk uses for p (its partial tiles).
+// Workspace bytes launch_sgemm_streamk and launch_sgemm_dma_streamk use for
+// p (their partial tiles).
 int64_t sgemm_streamk_bytes(const Problem &p);
+// The same schedule on the direct-load k loop, for problems where both
+// sgemm_dma_eligible() and sgemm_streamk_eligible() hold.
+bool sgemm_dma_streamk_eligible(const Problem &p, bool force = false);
+hipError_t launch_sgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream);
 hipError_t launch_hgemm(const Problem &p, hipStream_t stream);  // bf16/fp16 on MFMA, any shape
 // The *_streamk_eligible functions check whether a problem can run on the
 // schedule and, unless `force`, whether the cost model says it pays.

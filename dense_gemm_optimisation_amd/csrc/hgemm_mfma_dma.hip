@@ -623,10 +623,6 @@ DmaArgs make_dma_args(const Problem &p, int32_t xcds) {
     a.sB = p.batch > 1 ? p.sB : 0;
     a.sC = p.batch > 1 ? p.sC : 0;
     a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, LIBGEMM_DMA_GROUP_M, xcds};
-    const int esz = p.out == Elem::F32 ? 4 : 2;
-    // 16-byte chunks of C rows (8 bf16/fp16 or 4 fp32 elements)
-    const int cw = 16 / esz;
-    a.vec_c = (reinterpret_cast<uintptr_t>(p.C) % 16) == 0 && p.ldc % cw == 0 && a.sC % cw == 0;
     a.epi = p.epi;
     a.span_a = operand_span_a(p);
     a.span_b = operand_span_b(p);

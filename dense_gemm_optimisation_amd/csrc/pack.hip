@@ -10,7 +10,7 @@
 // section 5.2 of "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site) does with
 // predicated loads, done once per operand instead of on every tile.
 //
-// One thread writes one 16-byte chunk.  The source chunk may start at any
+// One thread writes one 16-byte chunk at a time.  The source chunk may start at any
 // element boundary: the kernel reads the 4-byte aligned words that cover it
 // with buffer loads (the buffer's range check keeps every read inside the
 // operand) and shifts them into place; the last chunk of a slice is read
@@ -31,22 +31,24 @@ struct PackArgs {
     const char *src;
     char *dst;
     int64_t outer, inner, ld, stride;  // source extent, elements
-    int64_t outer_p, inner_p;          // destination extent, elements
     int64_t batch;
-    int64_t chunks_per_row;            // inner_p * esize / 16
+    uint32_t outer_p;                  // destination rows of one slice
+    uint32_t chunks_per_row;           // inner_p * esize / 16
 };
 
+// Grid: x covers the chunks of one slice (a grid-stride loop past 8192
+// workgroups), y the slices (a loop past gridDim.y).  A slice has fewer than
+// 2^31 chunks (its source extent is below 2^31 bytes), so the index
+// arithmetic inside a slice is 32-bit.
 template <int ESIZE>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     constexpr int PER = 16 / ESIZE;  // elements per chunk
-    const int64_t per_slice = a.outer_p * a.chunks_per_row;
-    const int64_t total = per_slice * a.batch;
-    for (int64_t g = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; g < total;
-         g += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t b = g / per_slice;
-        const int64_t r = g - b * per_slice;
-        const int64_t o = r / a.chunks_per_row;
-        const int64_t e0 = (r - o * a.chunks_per_row) * PER;
+    const uint32_t per_slice = a.outer_p * a.chunks_per_row;
+    for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y)
+    for (uint32_t r = blockIdx.x * 256u + threadIdx.x; r < per_slice; r += gridDim.x * 256u) {
+        const int64_t g = b * per_slice + r;  // destination chunk
+        const uint32_t o = r / a.chunks_per_row;
+        const int64_t e0 = int64_t(r - o * a.chunks_per_row) * PER;
         u32x4 out = {0u, 0u, 0u, 0u};
         if (o < a.outer && e0 < a.inner) {
             const char *slice = a.src + b * a.stride * ESIZE;
@@ -121,18 +123,21 @@ hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream) {
     a.inner = s.inner;
     a.ld = s.ld;
     a.stride = s.stride;
-    a.outer_p = s.outer_p;
-    a.inner_p = s.inner_p;
     a.batch = s.stride == 0 && s.batch > 1 ? 1 : s.batch;
-    a.chunks_per_row = s.inner_p * s.esize / 16;
-    const int64_t total = a.outer_p * a.chunks_per_row * a.batch;
-    if (total == 0) return hipSuccess;
-    // enough workgroups to fill the chip several times over; the loop covers the rest
-    const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
+    const int64_t cpr = s.inner_p * s.esize / 16;
+    const int64_t per_slice = s.outer_p * cpr;
+    if (per_slice == 0 || a.batch == 0) return hipSuccess;
+    if (per_slice >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    a.outer_p = static_cast<uint32_t>(s.outer_p);
+    a.chunks_per_row = static_cast<uint32_t>(cpr);
+    // enough workgroups to fill the chip several times over; the loops cover the rest
+    const int64_t bx = (per_slice + 255) / 256 < 8192 ? (per_slice + 255) / 256 : 8192;
+    const int64_t by = a.batch < 1024 ? a.batch : 1024;
     void *args[] = {&a};
     const void *k = s.esize == 2 ? reinterpret_cast<const void *>(&pack_kernel<2>)
                                  : reinterpret_cast<const void *>(&pack_kernel<4>);
-    return hipLaunchKernel(k, dim3(static_cast<unsigned>(blocks)), dim3(256), args, 0, stream);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by)), dim3(256),
+                           args, 0, stream);
 }
 
 }  // namespace libgemm

@@ -25,8 +25,8 @@
 //     2i + t).  Neither layout has LDS bank conflicts on reads or writes;
 //   * the instruction computes C^T = B^T A^T (B's operand in the first
 //     slot), which leaves every lane with consecutive columns of one row of
-//     C (four, or eight when B is N-contiguous): 16-byte stores in the
-//     epilogue;
+//     C (four, or eight when B is N-contiguous): 16-byte loads and stores of
+//     C in the epilogue, at any leading dimension;
 //   * the next K step's global loads are issued before the current step's
 //     matrix instructions and written to the other LDS buffer after them
 //     (double buffering, section 9 of "CUDA GEMM 矩阵乘法优化指南",
@@ -64,7 +64,7 @@ struct SgemmArgs {
     int64_t lda, ldb, ldc;
     int64_t sA, sB, sC;
     TileGrid grid;
-    int vec_a, vec_b, vec_c;  // 16-byte vector access allowed for the operand
+    int vec_a, vec_b;  // 16-byte vector loads allowed for the operand
     Epilogue epi;
     int64_t span_a, span_b;   // elements of one slice of A and of B the direct loads may touch
 };
@@ -197,16 +197,16 @@ __device__ inline void store_c(const SgemmArgs &p, const f32x16 (&acc)[2][2], fl
                 for (int u = 0; u < 4; ++u) v[u] = p.alpha * acc[i][u & 1][4 * q + 2 * c + (u >> 1)];
             }
             float *dst = C + row * p.ldc + col;
-            if (p.vec_c && col + 4 <= p.N) {
+            if (col + 4 <= p.N) {
                 if (p.beta != 0.0f) {
-                    const f4 old = *reinterpret_cast<const f4 *>(dst);
+                    const f4 old = *reinterpret_cast<const f4u *>(dst);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, old[e], v[e]);
                 }
                 if (p.epi.active())
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = epilogue_apply(p.epi, v[e], batch, row, col + e);
-                *reinterpret_cast<f4 *>(dst) = v;
+                *reinterpret_cast<f4u *>(dst) = v;
             } else {
                 // the chunk's old values are loaded before any is used (from
                 // element 0 of C where an element lies outside the matrix), so
@@ -362,17 +362,14 @@ struct DmaPanel {
 // One barrier per stage: it follows this wave's wait for the next stage's
 // loads and for its own last reads of the current buffer, so after it every
 // wave's data has landed and the current buffer is free to be refilled with
-// stage s + 2.
+// stage s + 2.  Stages [kb, ke) of tile t are added into acc; the LDS
+// buffers are still being read by other waves when this returns.
 template <bool A_KMAJOR, bool B_KMAJOR>
-__global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) float smem[2][2][PANEL];  // [buffer][A, B]
+__device__ __forceinline__ void sg_dma_steps(const SgemmArgs &p, float (*smem)[2][PANEL],
+                                             const TileCoord &t, int64_t kb, int64_t ke,
+                                             f32x16 (&acc)[2][2]) {
     using PA = Panel<A_KMAJOR>;
     using PB = Panel<B_KMAJOR>;
-
-    TileCoord t = tile_of(p.grid, blockIdx.x);
-    t.batch = dma::uniform(t.batch);
-    t.tm = dma::uniform(t.tm);
-    t.tn = dma::uniform(t.tn);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -391,14 +388,6 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p)
         db.issue(addr(buf, 1), stage, p.K, wave);
     };
 
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
     float fa[2][2][4], fb[2][2][4];  // [k group slot][tile][instruction]
     auto read = [&](int buf, int g, int slot) {
         PA::frag(smem[buf][0], wm * 64, g, idx, half, fa[slot]);
@@ -415,10 +404,10 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p)
                                                                      acc[i][j], 0, 0, 0);
     };
 
-    const int64_t steps = (p.K + BK - 1) / BK;
-    issue(0, 0);
+    const int64_t steps = ke - kb;
+    issue(0, kb);
     if (steps > 1) {
-        issue(1, 1);
+        issue(1, kb + 1);
         dma::wait_vmcnt<2 * DmaPanel<A_KMAJOR>::PER_WAVE>();
     } else {
         dma::wait_vmcnt<0>();
@@ -432,16 +421,33 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p)
         dma::wait_vmcnt<0>();
         dma::wait_lgkmcnt0();
         __syncthreads();
-        if (s + 2 < steps) issue(buf, s + 2);
+        if (s + 2 < steps) issue(buf, kb + s + 2);
         read(buf ^ 1, 0, 0);
         mfmas(1);
     }
     read((steps - 1) & 1, 1, 1);
     mfmas(0);
     mfmas(1);
+}
 
-    float *C = p.C + t.batch * p.sC;
-    store_c<A_KMAJOR, B_KMAJOR>(p, acc, C, m0 + wm * 64, n0 + wn * 64, idx, half, t.batch);
+template <bool A_KMAJOR, bool B_KMAJOR>
+__global__ __launch_bounds__(THREADS, 4) void sgemm_mfma_dma_kernel(SgemmArgs p) {
+    __shared__ __attribute__((aligned(1024))) float smem[2][2][PANEL];  // [buffer][A, B]
+    TileCoord t = tile_of(p.grid, blockIdx.x);
+    t.batch = dma::uniform(t.batch);
+    t.tm = dma::uniform(t.tm);
+    t.tn = dma::uniform(t.tn);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    sg_dma_steps<A_KMAJOR, B_KMAJOR>(p, smem, t, 0, (p.K + BK - 1) / BK, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    store_c<A_KMAJOR, B_KMAJOR>(p, acc, p.C + t.batch * p.sC, t.tm * BM + (wave >> 1) * 64,
+                                t.tn * BN + (wave & 1) * 64, lane & 31, lane >> 5, t.batch);
 }
 
 template <bool AK, bool BK_>
@@ -526,9 +532,10 @@ __device__ __forceinline__ void sg_tile_steps(const SgemmArgs &p, float (*smem)[
     }
 }
 
-template <bool A_KMAJOR, bool B_KMAJOR>
+// DIRECT: the direct-load k loop (aligned operands), else the general one.
+template <bool A_KMAJOR, bool B_KMAJOR, bool DIRECT>
 __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, SgStreamK sk) {
-    __shared__ __attribute__((aligned(16))) float smem[2][2][PANEL];
+    __shared__ __attribute__((aligned(1024))) float smem[2][2][PANEL];
     // logical workgroup: the hardware id regrouped per XCD
     const int64_t G = gridDim.x, S = sk.steps;
     const int64_t w = dma::uniform(xcd_remap(blockIdx.x, G, 8));
@@ -565,7 +572,14 @@ __global__ __launch_bounds__(THREADS, 4) void sgemm_streamk_kernel(SgemmArgs p, 
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        sg_tile_steps<A_KMAJOR, B_KMAJOR>(p, smem, t, kb, ke, acc);
+        if (DIRECT) {
+            // the previous item's last LDS reads are done in every wave
+            // before this item's loads overwrite the buffers
+            if (item > 0) __syncthreads();
+            sg_dma_steps<A_KMAJOR, B_KMAJOR>(p, smem, t, kb, ke, acc);
+        } else {
+            sg_tile_steps<A_KMAJOR, B_KMAJOR>(p, smem, t, kb, ke, acc);
+        }
         if (kb == 0 && ke == S) {
             store_c<A_KMAJOR, B_KMAJOR>(p, acc, p.C + t.batch * p.sC, t.tm * BM + wm * 64,
                                         t.tn * BN + wn * 64, lane & 31, lane >> 5, t.batch);
@@ -640,10 +654,10 @@ __global__ __launch_bounds__(THREADS) void sgemm_streamk_fixup(SgemmArgs p, SgSt
     }
 }
 
-template <bool AK, bool BKM>
+template <bool AK, bool BKM, bool DIRECT>
 hipError_t launch_sk(SgemmArgs &a, SgStreamK &sk, int64_t grid, hipStream_t stream) {
     void *args[] = {&a, &sk};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sgemm_streamk_kernel<AK, BKM>),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sgemm_streamk_kernel<AK, BKM, DIRECT>),
                                    dim3(static_cast<unsigned>(grid)), dim3(THREADS), args, 0, stream);
     if (e != hipSuccess || sk.iters == 0) return e;
     const int64_t cut = a.grid.count() - sk.dp_tiles;
@@ -688,7 +702,6 @@ SgemmArgs make_args(const Problem &p) {
     a.grid = TileGrid{(p.M + BM - 1) / BM, (p.N + BN - 1) / BN, p.batch, 8, 8};
     a.vec_a = vec16_ok(p.A, p.lda, a.sA, 4);
     a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 4);
-    a.vec_c = vec16_ok(p.C, p.ldc, a.sC, 4);
     a.epi = p.epi;
     a.span_a = operand_span_a(p);
     a.span_b = operand_span_b(p);
@@ -757,7 +770,14 @@ int64_t sgemm_streamk_bytes(const Problem &p) {
     return 2 * sg_streamk_split(p).groups * int64_t(SG_SLOT) * 4;
 }
 
-hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+bool sgemm_dma_streamk_eligible(const Problem &p, bool force) {
+    return sgemm_dma_eligible(p) && sgemm_streamk_eligible(p, force);
+}
+
+namespace {
+
+template <bool DIRECT>
+hipError_t launch_streamk(const Problem &p, void *workspace, hipStream_t stream) {
     SgemmArgs a = make_args(p);
     a.grid.xcds = 1;  // the work order itself spreads tiles over the dies
     SgStreamK sk{};
@@ -766,10 +786,20 @@ hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t s
     const int64_t grid = streamk_grid(sk, SGEMM_STREAMK_MAX_GRID);
     if (grid == 0) return hipSuccess;
     if (p.a_kmajor)
-        return p.b_kmajor ? launch_sk<true, true>(a, sk, grid, stream)
-                          : launch_sk<true, false>(a, sk, grid, stream);
-    return p.b_kmajor ? launch_sk<false, true>(a, sk, grid, stream)
-                      : launch_sk<false, false>(a, sk, grid, stream);
+        return p.b_kmajor ? launch_sk<true, true, DIRECT>(a, sk, grid, stream)
+                          : launch_sk<true, false, DIRECT>(a, sk, grid, stream);
+    return p.b_kmajor ? launch_sk<false, true, DIRECT>(a, sk, grid, stream)
+                      : launch_sk<false, false, DIRECT>(a, sk, grid, stream);
+}
+
+}  // namespace
+
+hipError_t launch_sgemm_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+    return launch_streamk<false>(p, workspace, stream);
+}
+
+hipError_t launch_sgemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+    return launch_streamk<true>(p, workspace, stream);
 }
 
 }  // namespace libgemm

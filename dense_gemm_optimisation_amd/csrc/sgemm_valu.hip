@@ -47,11 +47,14 @@ struct SgemmArgs {
     int64_t lda, ldb, ldc;
     int64_t sA, sB, sC;
     TileGrid grid;
-    int vec_a, vec_b, vec_c;  // 16-byte vector access allowed for the operand
+    int vec_a, vec_b;  // 16-byte vector loads allowed for the operand
     Epilogue epi;
 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+// a 4-float chunk of C at 4-byte alignment (rows of C start wherever ldc
+// puts them; the memory system takes a 16-byte access at any such address)
+typedef float f4_ea __attribute__((ext_vector_type(4), aligned(4)));
 
 // Four consecutive elements x[0..3] of one row of an operand, zero outside
 // [0, limit).  `inside` says the whole row exists.
@@ -188,22 +191,30 @@ __global__ __launch_bounds__(THREADS, 1) void sgemm_kernel(SgemmArgs p) {
             f4 v;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = p.alpha * acc[i][h * 4 + j];
-            if (p.vec_c && col + 4 <= p.N) {
+            if (col + 4 <= p.N) {
                 if (p.beta != 0.0f) {
-                    const f4 old = *reinterpret_cast<const f4 *>(dst);
+                    const f4 old = *reinterpret_cast<const f4_ea *>(dst);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(p.beta, old[j], v[j]);
                 }
                 if (p.epi.active())
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = epilogue_apply(p.epi, v[j], t.batch, row, col + j);
-                *reinterpret_cast<f4 *>(dst) = v;
+                *reinterpret_cast<f4_ea *>(dst) = v;
             } else {
+                // the chunk across the right edge: its old values are loaded
+                // before any is used (element col stands in for those past
+                // the edge), so the loads are in flight together
+                float old[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (p.beta != 0.0f) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) old[j] = dst[col + j < p.N ? j : 0];
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (col + j < p.N) {
                         float x = v[j];
-                        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, dst[j], x);
+                        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, old[j], x);
                         if (p.epi.active()) x = epilogue_apply(p.epi, x, t.batch, row, col + j);
                         dst[j] = x;
                     }
@@ -243,7 +254,6 @@ hipError_t launch_sgemm(const Problem &p, hipStream_t stream) {
     if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.vec_a = vec16_ok(p.A, p.lda, a.sA, 4);
     a.vec_b = vec16_ok(p.B, p.ldb, a.sB, 4);
-    a.vec_c = vec16_ok(p.C, p.ldc, a.sC, 4);
     a.epi = p.epi;
     if (p.a_kmajor)
         return p.b_kmajor ? launch<true, true>(a, stream) : launch<true, false>(a, stream);

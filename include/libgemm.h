@@ -39,9 +39,12 @@
  *   A[i*lda + k] when orderA == GEMM_ROW_MAJOR and at A[k*lda + i] when
  *   GEMM_COL_MAJOR; element (k, j) of B and (i, j) of C likewise.  A leading
  *   dimension must be at least max(1, extent of the contiguous dimension).
- *   Any element-aligned pointer and leading dimension are accepted; 16-byte
- *   aligned bases with leading dimensions and strides that are multiples of
- *   16 bytes take the fast vector path, anything else a slower exact path.
+ *   Every pointer must be a multiple of its element size; any leading
+ *   dimension is accepted.  16-byte aligned A and B (bases, leading
+ *   dimensions and strides multiples of 16 bytes) take the fast direct-load
+ *   path, anything else a slower exact path (or, with a workspace, aligned
+ *   copies made first); C is read and written in 16-byte chunks at any
+ *   leading dimension.
  *
  * Batch
  *   `batch` independent problems; problem b uses A + b*strideA, B + b*strideB
@@ -69,7 +72,8 @@
  *   printed and no exception crosses this interface.
  *     GEMM_ERR_INVALID_ARG  negative dimension, batch or stride; leading
  *                           dimension too small; null pointer for a matrix
- *                           that must be read or written; order or dtype out
+ *                           that must be read or written; a pointer that is
+ *                           not a multiple of its element size; order or dtype out
  *                           of range; C slices overlapping each other; C
  *                           overlapping A or B (checked on the address ranges
  *                           the operands span).
@@ -247,9 +251,9 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
 
 /* Workspace entry points.  gemm_f32_ws / gemm_bf16_ws / gemm_f16_ws take the
  * arguments of gemm_f32 / gemm_bf16 / gemm_f16 plus a device workspace, and
- * compute the same product.  For fp32 the general kernel (operands that are
- * not 16-byte aligned, 128 x 128 tiles, four workgroups per compute unit)
- * has the same schedule, with the same workspace.
+ * compute the same product.  For fp32 both kernels (the general one and the
+ * direct-load one; 128 x 128 tiles, four workgroups per compute unit) have
+ * the same schedule, with the same workspace.
  * With at least gemm_workspace_size() bytes, a problem on either 16-bit
  * kernel (the general one for operands that are not 16-byte aligned, the
  * direct-load one for aligned operands with 64 tiles or more) whose
@@ -262,16 +266,17 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
  * written to the workspace and added, in a fixed order, by a second kernel on
  * the same stream, which also applies the epilogue.  It is chosen when the
  * steps saved in the last wave outweigh that exchange (about four k steps of
- * one tile on the general kernels; on the direct-load one about 0.14 k steps
- * per partial tile plus two).  The testing switch
+ * one tile on the general 16-bit kernel, eight on the fp32 kernels; on the
+ * 16-bit direct-load one about 0.14 k steps per partial tile plus two).  The
+ * testing switch
  * GEMM_TEST_FORCE_STREAMK chooses it wherever it can run.
  * Operands that are not 16-byte aligned (base, leading dimension, stride or
  * contiguous extent), in a problem of at least 64 tiles of 256 x 256
  * (bf16/fp16) or 160 tiles of 128 x 128 (fp32), are first copied into the
  * workspace in the same order, zero-padded to whole 16-byte chunks along
  * their contiguous dimension (K padded to a multiple of 8, resp. 4, with zero
- * rows or columns), and the direct-load kernel (bf16/fp16: or its stream-K
- * schedule, by the same cost model) runs on the copies, with the caller's M,
+ * rows or columns), and the direct-load kernel (or its stream-K schedule, by
+ * the same cost model) runs on the copies, with the caller's M,
  * N and C.  The zero padding adds nothing to any result.  This is chosen
  * whenever the copies and any partial tiles fit the workspace; otherwise the
  * general kernel runs on the caller's operands as described above.
@@ -429,10 +434,11 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
 /* The kernel gemm_f32_ws (in = GEMM_INPUT_F32; c_dtype is then ignored),
  * gemm_bf16_ws (GEMM_INPUT_BF16) or gemm_f16_ws (GEMM_INPUT_F16) would
  * launch: the names of gemm_kernel_name, or "hgemm_mfma_streamk",
- * "hgemm_mfma_dma_streamk" or "sgemm_mfma_streamk" for the stream-K
- * schedules, "hgemm_mfma_dma_packed", "hgemm_mfma_dma_streamk_packed" or
- * "sgemm_mfma_dma_packed" when the operands are first copied into the
- * workspace; "" and NULL as for gemm_kernel_name, whose testing switches
+ * "hgemm_mfma_dma_streamk", "sgemm_mfma_streamk" or "sgemm_mfma_dma_streamk"
+ * for the stream-K schedules, "hgemm_mfma_dma_packed",
+ * "hgemm_mfma_dma_streamk_packed", "sgemm_mfma_dma_packed" or
+ * "sgemm_mfma_dma_streamk_packed" when the operands are first copied into
+ * the workspace; "" and NULL as for gemm_kernel_name, whose testing switches
  * apply, GEMM_TEST_FORCE_STREAMK included.  The workspace is only
  * checked, never dereferenced. */
 const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K,

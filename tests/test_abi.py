@@ -118,6 +118,19 @@ def test_invalid_arguments(lib, fn, case):
     assert call(lib, fn, **kw) == lib.ERR_INVALID_ARG, case
 
 
+@pytest.mark.parametrize("fn", ["f32", "bf16", "f16", "e4m3"])
+def test_pointers_off_their_element_size(lib, fn):
+    # C is fp32 for f32 and bf16 for e4m3 (type_c default); A and B have
+    # the input element size (no constraint for 8-bit inputs)
+    esz = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}[fn]
+    esz_c = 4 if fn == "f32" else 2
+    for off in range(1, esz_c):
+        assert call(lib, fn, C=P * 5 + off) == lib.ERR_INVALID_ARG, off
+    for off in range(1, esz):
+        assert call(lib, fn, A=P + off) == lib.ERR_INVALID_ARG, off
+        assert call(lib, fn, B=P * 3 + off) == lib.ERR_INVALID_ARG, off
+
+
 def test_f8_bad_formats_and_output_type(lib):
     for kw in (dict(fa=2), dict(fa=-1), dict(fb=2), dict(type_c=3), dict(type_c=-1)):
         assert call(lib, "e4m3", **kw) == lib.ERR_INVALID_ARG, kw
@@ -389,13 +402,21 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_dma_streamk_packed"
     clean_env(0)
     # fp32: unaligned with at least 160 tiles of 128 x 128 is copied for the
-    # direct-load kernel; fewer tiles use the general kernel's schedule
-    # (128 x 128 tiles, 1024 workgroups)
-    assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_dma_packed"
+    # direct-load kernel, on its stream-K schedule where the cut tail pays
+    # (1056 tiles of 63 k steps: 1024 whole and 32 cut; of 9 steps: no);
+    # fewer tiles use the general kernel's schedule (128 x 128 tiles, 1024
+    # workgroups)
+    assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_dma_streamk_packed"
     assert kname_ws(lib, "f32", 4095, 4097, 129) == "sgemm_mfma_dma_packed"
+    # 187 tiles of 63 steps: the partial tiles and copies exceed the workspace
+    assert kname_ws(lib, "f32", 2049, 1283, 1001) == "sgemm_mfma_dma_packed"
     assert kname_ws(lib, "f32", 1500, 1300, 2001) == "sgemm_mfma_streamk"   # 132 tiles
     assert kname_ws(lib, "f32", 1500, 1300, 129) == "sgemm_mfma"            # 9 steps per tile
-    assert kname_ws(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma_dma"     # aligned
+    # aligned: the direct-load kernel, on its stream-K schedule when tiles are cut
+    assert kname_ws(lib, "f32", 4096, 4096, 4096) == "sgemm_mfma_dma"       # whole waves
+    assert kname_ws(lib, "f32", 4096, 4224, 256) == "sgemm_mfma_dma_streamk"
+    assert kname_ws(lib, "f32", 2048, 2176, 1000, oa=1, ob=1) == "sgemm_mfma_dma_streamk"
+    assert kname_ws(lib, "f32", 4096, 4224, 64) == "sgemm_mfma_dma"         # 4 steps per tile
     assert kname_ws(lib, "f32", 4095, 4097, 1001, nbytes=1 << 20) == "sgemm_mfma"
     # K = 0 scales C
     assert kname_ws(lib, "bf16", 4095, 4097, 0, lda=1) == "scale"

@@ -834,8 +834,9 @@ def test_f32_streamk_integers_bit_exact():
 
 def test_f32_packed_edge_config_sampled():
     # the unaligned 4095 x 4097 x 1001 fp32 problem with a workspace: copied
-    # to aligned operands, then the direct-load kernel
-    check(workloads.config("f32_edge"), kernel="sgemm_mfma_dma_packed", sample="auto",
+    # to aligned operands, then the direct-load kernel's stream-K schedule
+    # (1056 tiles: 1024 whole, 32 cut)
+    check(workloads.config("f32_edge"), kernel="sgemm_mfma_dma_streamk_packed", sample="auto",
           use_workspace=True, repeat=2)
 
 
@@ -922,27 +923,63 @@ def test_packed_16bit_forced_streamk(force_streamk):
     assert res.max_ulp == 0
 
 
-F32_PACK_SHAPES = [(1537, 1665, 257), (2049, 1283, 1001)]
+# (shape, kernel): 182 tiles of 17 k steps are cut over the grid by the
+# direct-load stream-K schedule; 187 tiles of 63 steps would need more
+# partial tiles than the workspace holds beside the copies, so they run on
+# the plain direct-load kernel.
+F32_PACK_SHAPES = [((1537, 1665, 257), "sgemm_mfma_dma_streamk_packed"),
+                   ((2049, 1283, 1001), "sgemm_mfma_dma_packed")]
 
 
-@pytest.mark.parametrize("shape", F32_PACK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape,kernel", F32_PACK_SHAPES, ids=lambda s: "x".join(map(str, s))
+                         if isinstance(s, tuple) else s.rsplit("_", 1)[-1])
 @pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
                          ids=lambda o: "%d%d" % o)
-def test_packed_f32(shape, orders):
+def test_packed_f32(shape, kernel, orders):
     M, N, K = shape
     oa, ob = orders
     check(P("packed-f32", "f32", M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
-          kernel="sgemm_mfma_dma_packed", seed=M + N + K + 5, use_workspace=True, repeat=2)
+          kernel=kernel, seed=M + N + K + 5, use_workspace=True, repeat=2)
 
 
 def test_packed_f32_bases_batch_col_major_c_and_integers():
     check(P("packed-f32-base", "f32", 1664, 1664, 256, beta=0.5),
-          kernel="sgemm_mfma_dma_packed", seed=110, use_workspace=True, base_offset=(1, 2, 0))
+          kernel="sgemm_mfma_dma_streamk_packed", seed=110, use_workspace=True,
+          base_offset=(1, 2, 0))
     check(P("packed-f32-batch", "f32", 515, 517, 203, batch=8, beta=1.0),
-          kernel="sgemm_mfma_dma_packed", seed=111, use_workspace=True)
+          kernel="sgemm_mfma_dma_streamk_packed", seed=111, use_workspace=True)
     check(P("packed-f32-colC", "f32", 1665, 1537, 257, order_c=COL, ldc=1669, beta=0.5),
-          kernel="sgemm_mfma_dma_packed", seed=112, use_workspace=True)
+          kernel="sgemm_mfma_dma_streamk_packed", seed=112, use_workspace=True)
     p = P("packed-f32-int", "f32", 1537, 1665, 257, alpha=2.0, beta=1.0)
-    res, _ = check(p, kernel="sgemm_mfma_dma_packed", host=_int_host(p, np.random.default_rng(113)),
+    res, _ = check(p, kernel="sgemm_mfma_dma_streamk_packed",
+                   host=_int_host(p, np.random.default_rng(113)), use_workspace=True)
+    assert res.max_err == 0.0
+
+
+# The fp32 direct-load kernel's stream-K schedule on aligned operands: 272
+# tiles, all cut over the grid, and 1056 tiles (1024 whole, 32 cut).
+F32_DMA_SK_SHAPES = [(2048, 2176, 1000), (4096, 4224, 256)]
+
+
+@pytest.mark.parametrize("shape", F32_DMA_SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=lambda o: "%d%d" % o)
+def test_f32_dma_streamk(shape, orders):
+    M, N, K = shape
+    oa, ob = orders
+    check(P("f32-dma-streamk", "f32", M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob),
+          kernel="sgemm_mfma_dma_streamk", seed=M + K + 11, use_workspace=True, repeat=2)
+
+
+def test_f32_dma_streamk_batches_col_major_c_and_integers():
+    # 114 batches of 3 x 3 tiles (1026 tiles: 1024 whole, 2 cut); a
+    # column-major C with a padded leading dimension; integer-valued inputs,
+    # exact in fp32
+    check(P("f32-dma-sk-dp", "f32", 384, 384, 1000, beta=0.5, batch=114),
+          kernel="sgemm_mfma_dma_streamk", seed=114, use_workspace=True, repeat=2)
+    check(P("f32-dma-sk-colC", "f32", 2048, 2176, 1000, order_c=COL, ldc=2051, beta=-1.0),
+          kernel="sgemm_mfma_dma_streamk", seed=115, use_workspace=True)
+    p = P("f32-dma-sk-int", "f32", 2048, 2176, 1000, alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="sgemm_mfma_dma_streamk", host=_int_host(p, np.random.default_rng(117)),
                    use_workspace=True)
     assert res.max_err == 0.0
