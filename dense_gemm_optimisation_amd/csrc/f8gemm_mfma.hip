@@ -1,8 +1,8 @@
 // 8-bit float GEMM on the CDNA4 matrix cores: OCP E4M3 or E5M2 operands
 // (each operand in its own format), exact products, fp32 accumulation, output
 // in fp32, bf16 or fp16.  The pages name the 8-bit formats E4M3 and E5M2 as
-// the next step down from fp16/bf16 for matrix units ("第4章：经典算子实现 ——
-// GEMM", aiinfra.vidrealm.tech, section 13.2).
+// the next step down from fp16/bf16 for matrix units ("CUDA GEMM 矩阵乘法优化
+// 指南", blog.zhenwei.site, section 13.2).
 //
 // Matrix instruction: v_mfma_scale_f32_32x32x64_f8f6f4 with both block
 // scales 2^0, 64 k per instruction.  A lane's fragment of a 32 x 64 block is

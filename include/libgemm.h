@@ -223,7 +223,7 @@ gemm_status_t gemm_f16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
  * holding E4M3 or E5M2 bit patterns (formatA, formatB; the two may differ),
  * and C of type typeC (float, or bf16 / fp16 bit patterns).  The pages list
  * E4M3 and E5M2 as the 8-bit floating formats below fp16/bf16 for matrix
- * units ("第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech, section 13.2).
+ * units ("CUDA GEMM 矩阵乘法优化指南", blog.zhenwei.site, section 13.2).
  * Accuracy: the products are formed exactly, but gfx950's 8-bit matrix
  * instruction adds them at reduced precision: within each group of 8
  * consecutive k, a product smaller than 2^-13 of the group's largest is

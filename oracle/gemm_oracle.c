@@ -10,7 +10,7 @@
  *   - "CUDA GEMM 矩阵乘法优化指南" (blog.zhenwei.site), section 2.1: the GEMM
  *     definition C = alpha x A x B + beta x C with A of size M x K, B of size
  *     K x N and C of size M x N, each output element taking K multiply-adds.
- *   - "三个周末，从 312 GFLOPS 到 10124 GFLOPS" (m.lqnn.cn), section 1.2: the
+ *   - the CUDA SGEMM optimisation article at m.lqnn.cn, section 1.2: the
  *     kernel result is checked against a CPU computation in double precision.
  *
  * Every output element is the textbook dot product, accumulated in double, in
@@ -34,7 +34,7 @@
  * gains |bias_j|; it stays the scale of the terms before the activation.
  *
  * 8-bit inputs: the pages list the 8-bit floating formats E4M3 and E5M2 for
- * matrix units ("第4章：经典算子实现 —— GEMM", aiinfra.vidrealm.tech, section
+ * matrix units ("CUDA GEMM 矩阵乘法优化指南", blog.zhenwei.site, section
  * 13.2).  They are the OCP formats: E4M3 has no infinities and one NaN
  * pattern per sign (S.1111.111), largest finite 448; E5M2 follows the IEEE
  * rules (infinities at exponent 31 with a zero fraction, NaNs otherwise).
