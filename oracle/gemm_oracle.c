@@ -40,6 +40,21 @@
  * rules (infinities at exponent 31 with a zero fraction, NaNs otherwise).
  * Both have subnormals.  A and B may be in different 8-bit formats.
  *
+ * Block-scaled (MX) inputs: the pages list the microscaling formats MXFP8,
+ * MXFP6 and MXFP4, in which every 32 consecutive elements share one E8M0
+ * scale factor, an 8-bit exponent with no sign or fraction ("CUDA GEMM
+ * 矩阵乘法优化指南", blog.zhenwei.site, section 13.2, on block-scale
+ * quantisation).  The value of element k of a row is its scale times its own
+ * value: X[k] = 2^(e(k/32) - 127) * x[k], the E8M0 pattern 255 being NaN.
+ * Element formats: E4M3 and E5M2 as above; E2M3 (1 sign, 2 exponent bits,
+ * bias 1, 3 fraction bits, largest 7.5) and E3M2 (1 sign, 3 exponent bits,
+ * bias 3, 2 fraction bits, largest 28), both with subnormals and no
+ * infinities or NaNs; E2M1 (1 sign, 2 exponent bits, bias 1, 1 fraction bit:
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6).  orc_mx_gemm below computes
+ *   C_ij = alpha * sum_k XA(i,k) XB(k,j) + beta * C0_ij,
+ * each product of two decoded, scaled elements formed in double and added
+ * in increasing k order, as for the other types.
+ *
  * Readings taken where the pages are silent:
  *   - beta == 0: C0 is not read (BLAS convention), so NaN in C0 does not leak.
  *   - alpha == 0 or K == 0: the product term is skipped and A, B are not read.
@@ -56,6 +71,12 @@
 #define ORC_F16 2
 #define ORC_E4M3 3 /* OCP 8-bit float: 1 sign, 4 exponent (bias 7), 3 fraction bits */
 #define ORC_E5M2 4 /* OCP 8-bit float: 1 sign, 5 exponent (bias 15), 2 fraction bits */
+/* Element and scale formats of the block-scaled (MX) inputs; orc_decode takes
+ * them one value per byte (low bits), orc_mx_gemm packed (see mx_load). */
+#define ORC_E2M3 5 /* 6-bit float: 1 sign, 2 exponent (bias 1), 3 fraction bits */
+#define ORC_E3M2 6 /* 6-bit float: 1 sign, 3 exponent (bias 3), 2 fraction bits */
+#define ORC_E2M1 7 /* 4-bit float: 1 sign, 2 exponent (bias 1), 1 fraction bit */
+#define ORC_E8M0 8 /* scale: 2^(e - 127), 255 is NaN */
 
 #define ORC_ROW 0
 #define ORC_COL 1
@@ -120,6 +141,27 @@ static double decode_e5m2(uint8_t bits) {
     return sign ? -v : v;
 }
 
+/*
+ * A small float with no infinities or NaNs: sign bit s (above the others),
+ * ebits exponent bits with bias `bias`, mbits fraction bits.  Normal values
+ * (1 + m/2^mbits) * 2^(e - bias), subnormals (e == 0) m/2^mbits * 2^(1 - bias).
+ */
+static double decode_small(unsigned bits, int ebits, int mbits, int bias) {
+    const unsigned m = bits & ((1u << mbits) - 1);
+    const unsigned e = (bits >> mbits) & ((1u << ebits) - 1);
+    const int s = (bits >> (ebits + mbits)) & 1;
+    double v = e == 0 ? ldexp((double)m, 1 - bias - mbits)
+                      : ldexp(1.0 + ldexp((double)m, -mbits), (int)e - bias);
+    return s ? -v : v;
+}
+
+static double decode_e2m3(uint8_t bits) { return decode_small(bits & 0x3f, 2, 3, 1); }
+static double decode_e3m2(uint8_t bits) { return decode_small(bits & 0x3f, 3, 2, 3); }
+static double decode_e2m1(uint8_t bits) { return decode_small(bits & 0x0f, 2, 1, 1); }
+
+/* E8M0: 2^(e - 127); the all-ones pattern is NaN. */
+static double decode_e8m0(uint8_t bits) { return bits == 255 ? NAN : ldexp(1.0, (int)bits - 127); }
+
 static double load(int type, const void *base, int64_t idx) {
     switch (type) {
     case ORC_F32: {
@@ -133,6 +175,14 @@ static double load(int type, const void *base, int64_t idx) {
         return decode_e4m3(((const uint8_t *)base)[idx]);
     case ORC_E5M2:
         return decode_e5m2(((const uint8_t *)base)[idx]);
+    case ORC_E2M3:
+        return decode_e2m3(((const uint8_t *)base)[idx]);
+    case ORC_E3M2:
+        return decode_e3m2(((const uint8_t *)base)[idx]);
+    case ORC_E2M1:
+        return decode_e2m1(((const uint8_t *)base)[idx]);
+    case ORC_E8M0:
+        return decode_e8m0(((const uint8_t *)base)[idx]);
     default:
         return decode_f16(((const uint16_t *)base)[idx]);
     }
@@ -193,7 +243,7 @@ static uint16_t encode_f16(double r) {
 
 /* ---------------------------------------------------------------- exports */
 
-int orc_version(void) { return 3; }
+int orc_version(void) { return 4; }
 
 void orc_decode(int type, const void *src, double *dst, int64_t n) {
     for (int64_t i = 0; i < n; ++i) dst[i] = load(type, src, i);
@@ -382,6 +432,109 @@ void orc_gemm_at(PROBLEM_ARGS, int64_t count, const int64_t *idx, double *ref,
     for (int64_t e = 0; e < count; ++e)
         element(&P, idx[3 * e], idx[3 * e + 1], idx[3 * e + 2], &ref[e], &den[e]);
 }
+
+/* ---------------------------------------------------------------- MX */
+
+/*
+ * Element idx of a packed MX operand in format fmt.  Storage: the elements
+ * of a row follow one another as one little-endian bit stream, 8, 6 or 4
+ * bits each: element idx occupies bits [w*idx, w*idx + w) of the stream,
+ * bit n of the stream being bit n % 8 of byte n / 8.  (E4M3/E5M2: one byte
+ * each; E2M3/E3M2: four elements in three bytes; E2M1: two per byte, the
+ * lower index in the low half.)
+ */
+static int mx_width(int fmt) {
+    return fmt == ORC_E2M1 ? 4 : (fmt == ORC_E2M3 || fmt == ORC_E3M2) ? 6 : 8;
+}
+
+static double mx_load(int fmt, const uint8_t *base, int64_t idx) {
+    const int w = mx_width(fmt);
+    const int64_t bit = idx * w;
+    /* the (at most two) bytes that hold the element, low byte first */
+    unsigned v = base[bit / 8];
+    if (bit % 8 + w > 8) v |= (unsigned)base[bit / 8 + 1] << 8;
+    v = (v >> (bit % 8)) & ((1u << w) - 1);
+    switch (fmt) {
+    case ORC_E4M3: return decode_e4m3((uint8_t)v);
+    case ORC_E5M2: return decode_e5m2((uint8_t)v);
+    case ORC_E2M3: return decode_e2m3((uint8_t)v);
+    case ORC_E3M2: return decode_e3m2((uint8_t)v);
+    default: return decode_e2m1((uint8_t)v);
+    }
+}
+
+struct mx_problem {
+    int fa, fb, c_type;
+    int64_t M, N, K;
+    double alpha, beta;
+    const uint8_t *A, *SA, *B, *SB;
+    const void *C0;
+    int64_t lda, ldsa, ldb, ldsb, ldc;
+    int oC;
+    int64_t sA, sB, sSA, sSB, sC;
+};
+
+/*
+ * Output element (b, i, j): A(i, k) is element b*sA + i*lda + k of A's
+ * stream with scale SA[b*sSA + i*ldsa + k/32]; B(k, j) is element
+ * b*sB + j*ldb + k of B's (K contiguous along each column of B) with scale
+ * SB[b*sSB + j*ldsb + k/32].  Each side is decoded and scaled exactly, their
+ * product formed in double and added in increasing k.
+ */
+static void mx_element(const struct mx_problem *P, int64_t b, int64_t i, int64_t j,
+                       double *ref, double *den) {
+    double s = 0.0, t = 0.0;
+    if (P->alpha != 0.0) {
+        for (int64_t k = 0; k < P->K; ++k) {
+            const double xa = decode_e8m0(P->SA[b * P->sSA + i * P->ldsa + k / 32]) *
+                              mx_load(P->fa, P->A, b * P->sA + i * P->lda + k);
+            const double xb = decode_e8m0(P->SB[b * P->sSB + j * P->ldsb + k / 32]) *
+                              mx_load(P->fb, P->B, b * P->sB + j * P->ldb + k);
+            const double p = xa * xb;
+            s = s + p;
+            t = t + fabs(p);
+        }
+    }
+    double r = P->alpha * s;
+    double d = fabs(P->alpha) * t;
+    if (P->beta != 0.0) {
+        const double c0 = load(P->c_type, P->C0, b * P->sC + offset(P->oC, i, j, P->ldc));
+        r = r + P->beta * c0;
+        d = d + fabs(P->beta) * fabs(c0);
+    }
+    *ref = r;
+    *den = d;
+}
+
+#define MX_ARGS                                                                           \
+    int fa, int fb, int c_type, int64_t M, int64_t N, int64_t K, double alpha,            \
+        const uint8_t *A, int64_t lda, const uint8_t *SA, int64_t ldsa, const uint8_t *B, \
+        int64_t ldb, const uint8_t *SB, int64_t ldsb, double beta, const void *C0,        \
+        int64_t ldc, int oC, int64_t sA, int64_t sB, int64_t sSA, int64_t sSB, int64_t sC
+
+#define MX_INIT                                                                           \
+    struct mx_problem P = {fa, fb,  c_type, M,   N,   K,  alpha, beta, A,   SA,  B,  SB,   \
+                           C0, lda, ldsa,   ldb, ldsb, ldc, oC,   sA,   sB,  sSA, sSB, sC}
+
+/* All batch*M*N elements; ref and den are dense [batch][M][N]. */
+void orc_mx_gemm(MX_ARGS, int64_t batch, double *ref, double *den) {
+    MX_INIT;
+    const int64_t total = batch * M * N;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t e = 0; e < total; ++e)
+        mx_element(&P, e / (M * N), (e / N) % M, e % N, &ref[e], &den[e]);
+}
+
+/* Only the listed elements; idx holds count triples (b, i, j). */
+void orc_mx_gemm_at(MX_ARGS, int64_t count, const int64_t *idx, double *ref, double *den) {
+    MX_INIT;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t e = 0; e < count; ++e)
+        mx_element(&P, idx[3 * e], idx[3 * e + 1], idx[3 * e + 2], &ref[e], &den[e]);
+}
+
+/* Element idx of a packed MX operand, decoded (unscaled). */
+double orc_mx_element(int fmt, const uint8_t *base, int64_t idx) { return mx_load(fmt, base, idx); }
 
 #ifdef _OPENMP
 #include <omp.h>

@@ -53,6 +53,21 @@ MUTANTS = {
     "rows_b_transposed": ("offset(oB, k, j, ldb)", "offset(oB, j, k, ldb)"),
     "rows_b_type_ignored": ("load(b_type, B,", "load(in_type, B,"),
     "rows_batch_b_decoded_once": ("if (b == 0 || sB != 0)", "if (b == 0)"),
+    # block-scaled (MX) inputs
+    "mx_scale_block_16": ("i * P->ldsa + k / 32]", "i * P->ldsa + k / 16]"),
+    "mx_b_scale_row_of_a": ("j * P->ldsb + k / 32]", "i * P->ldsb + k / 32]"),
+    "mx_b_uses_lda": ("j * P->ldb + k)", "j * P->lda + k)"),
+    "mx_stream_high_bits_first": ("v = (v >> (bit % 8)) & ((1u << w) - 1);",
+                                  "v = (v >> ((8 - w - bit % 8) & 7)) & ((1u << w) - 1);"),
+    "mx_e3m2_bias_off": ("decode_small(bits & 0x3f, 3, 2, 3)", "decode_small(bits & 0x3f, 3, 2, 2)"),
+    "mx_subnormal_exponent": ("ldexp((double)m, 1 - bias - mbits)", "ldexp((double)m, -bias - mbits)"),
+    "mx_e8m0_bias_128": ("ldexp(1.0, (int)bits - 127)", "ldexp(1.0, (int)bits - 128)"),
+    "mx_e8m0_nan_ignored": ("bits == 255 ? NAN :", "0 ? NAN :"),
+    "mx_sum_sign": ("const double p = xa * xb;\n            s = s + p;",
+                    "const double p = xa * xb;\n            s = s - p;"),
+    "mx_beta_dropped": ("r = r + P->beta * c0;\n        d = d + fabs(P->beta) * fabs(c0);\n    }\n    *ref = r;",
+                        "r = r + c0;\n        d = d + fabs(P->beta) * fabs(c0);\n    }\n    *ref = r;"),
+    "mx_scale_raw_exponent": ("decode_e8m0(P->SB[", "(double)(P->SB["),
     "rows_last_k_dropped": ("for (int64_t k = 0; k < K; ++k) {\n                    const double *x",
                             "for (int64_t k = 0; k + 1 < K; ++k) {\n                    const double *x"),
 }

@@ -596,3 +596,218 @@ def test_8bit_formats_are_read_per_operand():
         ref, _ = oracle.gemm(fa, "f32", 1, 1, 1, 1.0, a, 1, ROW, a, 1, ROW, 0.0, None, 1, ROW,
                              b_dtype=fb)
         assert ref[0, 0, 0] == want, (fa, fb)
+
+
+# --------------------------------------------------------------- block-scaled (MX) inputs
+
+MX_WIDTH = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
+
+
+def mx_pack(fmt, patterns):
+    """Pack element patterns (one per entry, low bits) into a little-endian
+    bit stream of MX_WIDTH[fmt] bits per element."""
+    w = MX_WIDTH[fmt]
+    p = np.asarray(patterns, np.uint64).ravel()
+    out = np.zeros((p.size * w + 7) // 8, np.uint8)
+    for i, v in enumerate(p.tolist()):
+        bit = i * w
+        word = int(v) << (bit % 8)
+        for b in range(bit // 8, (bit + w + 7) // 8):
+            out[b] |= (word >> (8 * (b - bit // 8))) & 0xFF
+    return out
+
+
+def test_decode_every_e8m0_pattern_matches_torch():
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    got = oracle.decode("e8m0", bits)
+    want = torch.from_numpy(bits).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(got[255]) and np.isnan(want[255])
+    assert np.array_equal(got[:255], want[:255])
+    # bias 127: pattern 127 is 1; every step doubles
+    assert got[127] == 1.0 and np.all(got[1:255] == 2 * got[:254])
+
+
+def test_decode_e2m1_is_the_eight_listed_magnitudes():
+    got = oracle.decode("e2m1", np.arange(16, dtype=np.uint8))
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert got[:8].tolist() == mags
+    assert got[8:].tolist() == [-m for m in mags]
+    assert math.copysign(1.0, got[8]) == -1.0  # pattern 0x8 is -0
+
+
+@pytest.mark.parametrize("fmt,largest,min_normal,min_sub,within", [
+    ("e2m3", 7.5, 1.0, 0.125, "e4m3"),
+    ("e3m2", 28.0, 0.25, 0.0625, "e5m2"),
+    ("e2m1", 6.0, 1.0, 0.5, "e2m3"),
+])
+def test_small_formats_extremes_order_and_containment(fmt, largest, min_normal, min_sub, within):
+    n = 1 << MX_WIDTH[fmt]
+    got = oracle.decode(fmt, np.arange(n, dtype=np.uint8))
+    half = n // 2
+    pos, neg = got[:half], got[half:]
+    assert not np.isnan(got).any() and not np.isinf(got).any()
+    assert np.array_equal(neg, -pos)
+    assert np.all(np.diff(pos) > 0)  # patterns in increasing order of value
+    assert pos.max() == largest and pos[1] == min_sub
+    mbits = {"e2m3": 3, "e3m2": 2, "e2m1": 1}[fmt]
+    assert pos[1 << mbits] == min_normal
+    # every value is exactly a value of the wider format of the same family
+    wider = oracle.decode(within, np.arange(256 if within in ("e4m3", "e5m2") else 64,
+                                            dtype=np.uint8))
+    assert set(pos.tolist()) <= set(wider[~np.isnan(wider)].tolist())
+
+
+def test_mx_stream_bit_order():
+    # E2M1: two per byte, the lower index in the low half: 0x21 holds
+    # element 0 = 0x1 (0.5) and element 1 = 0x2 (1.0)
+    s4 = np.array([0x21, 0xF7], np.uint8)
+    assert [oracle.mx_element("e2m1", s4, i) for i in range(4)] == [0.5, 1.0, 6.0, -6.0]
+    # E2M3: patterns 1, 2, 3, 4 as one 24-bit little-endian word
+    # 1 | 2<<6 | 3<<12 | 4<<18 = 0x103081 -> bytes 81 30 10
+    s6 = np.array([0x81, 0x30, 0x10], np.uint8)
+    want = oracle.decode("e2m3", np.array([1, 2, 3, 4], np.uint8)).tolist()
+    assert [oracle.mx_element("e2m3", s6, i) for i in range(4)] == want
+    assert want == [0.125, 0.25, 0.375, 0.5]
+    # the packer used by the tests agrees with the hand-written bytes
+    assert mx_pack("e2m3", [1, 2, 3, 4]).tolist() == [0x81, 0x30, 0x10]
+    assert mx_pack("e2m1", [1, 2, 7, 15]).tolist() == [0x21, 0xF7]
+    # E4M3 elements are whole bytes
+    assert oracle.mx_element("e4m3", np.array([0x00, 0x38], np.uint8), 1) == 1.0
+
+
+def mx_int_operand(rng, fmt, rows, K):
+    """rows x K integer-valued elements of fmt (magnitudes exact in every
+    format), packed row by row, with their values."""
+    pats = {"e2m1": {0: 0, 1: 2, 2: 4, 3: 5, 4: 6, 6: 7},
+            "e2m3": {0: 0, 1: 8, 2: 16, 3: 20, 4: 24, 6: 28, 7: 30},
+            "e3m2": {0: 0, 1: 12, 2: 16, 3: 18, 4: 20, 6: 22, 7: 23},
+            "e4m3": {0: 0, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 6: 0x4C, 7: 0x4E},
+            "e5m2": {0: 0, 1: 0x3C, 2: 0x40, 3: 0x42, 4: 0x44, 6: 0x46, 7: 0x47}}[fmt]
+    sign = {"e2m1": 8, "e2m3": 32, "e3m2": 32, "e4m3": 128, "e5m2": 128}[fmt]
+    mags = np.array(sorted(pats))
+    vals = rng.choice(mags, (rows, K)) * rng.choice([-1, 1], (rows, K))
+    bits = np.array([[pats[abs(int(v))] | (sign if v < 0 else 0) for v in r] for r in vals])
+    # check the table against the oracle's decoder once
+    assert np.array_equal(oracle.decode(fmt, bits.astype(np.uint8).ravel()),
+                          np.abs(vals).ravel() * np.sign(vals).ravel() + 0.0)
+    return mx_pack(fmt, bits), vals
+
+
+@pytest.mark.parametrize("fa,fb", [("e2m1", "e2m1"), ("e2m3", "e3m2"), ("e4m3", "e2m1"),
+                                   ("e5m2", "e5m2"), ("e3m2", "e2m3")])
+def test_mx_integer_products_with_scales_match_exact_arithmetic(fa, fb):
+    rng = np.random.default_rng(41)
+    M, N, K, batch = 5, 7, 96, 2
+    A, va, SA, B, vb, SB = [], [], [], [], [], []
+    for _ in range(batch):
+        a, x = mx_int_operand(rng, fa, M, K)
+        b, y = mx_int_operand(rng, fb, N, K)
+        A.append(a); va.append(x); B.append(b); vb.append(y)
+        SA.append(rng.integers(122, 133, (M, K // 32)).astype(np.uint8))
+        SB.append(rng.integers(122, 133, (N, K // 32)).astype(np.uint8))
+    bytes_a, bytes_b = A[0].size, B[0].size
+    Af, Bf = np.concatenate(A), np.concatenate(B)
+    SAf, SBf = np.concatenate([s.ravel() for s in SA]), np.concatenate([s.ravel() for s in SB])
+    C0 = rng.integers(-5, 6, (batch, M, N)).astype(np.float32)
+    ref, den = oracle.mx_gemm(fa, fb, "f32", M, N, K, 2.0, Af, K, SAf, K // 32, Bf, K, SBf,
+                              K // 32, -1.0, C0.ravel(), N, ROW, batch=batch,
+                              stride_a=bytes_a * 8 // MX_WIDTH[fa], stride_b=bytes_b * 8 // MX_WIDTH[fb],
+                              stride_sa=M * K // 32, stride_sb=N * K // 32, stride_c=M * N)
+    for b in range(batch):
+        for i in range(M):
+            for j in range(N):
+                s = sum(Fraction(int(va[b][i, k]) * int(vb[b][j, k])) *
+                        Fraction(2) ** (int(SA[b][i, k // 32]) + int(SB[b][j, k // 32]) - 254)
+                        for k in range(K))
+                assert ref[b, i, j] == float(2 * s - Fraction(float(C0[b, i, j])))
+                t = sum(Fraction(abs(int(va[b][i, k]) * int(vb[b][j, k]))) *
+                        Fraction(2) ** (int(SA[b][i, k // 32]) + int(SB[b][j, k // 32]) - 254)
+                        for k in range(K))
+                assert den[b, i, j] == float(2 * t + abs(Fraction(float(C0[b, i, j]))))
+
+
+@pytest.mark.parametrize("f", ["e4m3", "e5m2"])
+def test_mx_with_unit_scales_is_the_8bit_gemm(f):
+    # every scale 127 (a factor of 1): the block-scaled product of 8-bit
+    # elements is the plain 8-bit GEMM of A row-major and B column-major
+    rng = np.random.default_rng(43)
+    M, N, K = 9, 11, 128
+    A = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    B = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    A[(A & 0x7F) >= (0x7F if f == "e4m3" else 0x7C)] = 0x11  # no NaN or Inf
+    B[(B & 0x7F) >= (0x7F if f == "e4m3" else 0x7C)] = 0x22
+    C0 = rng.standard_normal((M, N)).astype(np.float32)
+    one = lambda r: np.full((r, K // 32), 127, np.uint8)
+    ref, den = oracle.mx_gemm(f, f, "f32", M, N, K, 0.5, A, K, one(M), K // 32, B, K, one(N),
+                              K // 32, 2.0, C0, N, ROW)
+    ref8, den8 = oracle.gemm(f, "f32", M, N, K, 0.5, A, K, ROW, B, K, COL, 2.0, C0, N, ROW)
+    assert np.array_equal(ref, ref8) and np.array_equal(den, den8)
+
+
+def test_mx_scale_applies_to_its_32_element_block_only():
+    # K = 96: three blocks; raising one block's scale by d multiplies that
+    # block's share of the dot product by 2^d and leaves the others alone
+    rng = np.random.default_rng(47)
+    M, N, K = 3, 4, 96
+    a, va = mx_int_operand(rng, "e2m1", M, K)
+    b, vb = mx_int_operand(rng, "e2m1", N, K)
+    SB = np.full((N, 3), 127, np.uint8)
+    part = [(va[:, 32 * q:32 * q + 32] @ vb[:, 32 * q:32 * q + 32].T).astype(np.float64)
+            for q in range(3)]
+    for q in range(3):
+        for d in (-3, 2):
+            SA = np.full((M, 3), 127, np.uint8)
+            SA[:, q] = 127 + d
+            ref, _ = oracle.mx_gemm("e2m1", "e2m1", "f32", M, N, K, 1.0, a, K, SA, 3, b, K, SB, 3,
+                                    0.0, None, N, ROW)
+            want = sum(part) + (2.0 ** d - 1) * part[q]
+            assert np.array_equal(ref[0], want), (q, d)
+    # a scale on one row of A (or column of B) touches only that row (column)
+    SA = np.full((M, 3), 127, np.uint8)
+    SA[1, :] = 128
+    SB2 = SB.copy()
+    SB2[2, :] = 126
+    ref, _ = oracle.mx_gemm("e2m1", "e2m1", "f32", M, N, K, 1.0, a, K, SA, 3, b, K, SB2, 3, 0.0,
+                            None, N, ROW)
+    want = sum(part) * np.outer([1, 2, 1], [1, 1, 0.5, 1])
+    assert np.array_equal(ref[0], want)
+
+
+def test_mx_nan_scale_poisons_only_its_rows_and_columns():
+    rng = np.random.default_rng(53)
+    M, N, K = 4, 5, 64
+    a, _ = mx_int_operand(rng, "e2m3", M, K)
+    b, _ = mx_int_operand(rng, "e2m3", N, K)
+    SA = np.full((M, 2), 127, np.uint8)
+    SB = np.full((N, 2), 127, np.uint8)
+    SA[2, 1] = 255
+    SB[3, 0] = 255
+    ref, _ = oracle.mx_gemm("e2m3", "e2m3", "f32", M, N, K, 1.0, a, K, SA, 2, b, K, SB, 2, 0.0,
+                            None, N, ROW)
+    nan = np.isnan(ref[0])
+    assert nan[2, :].all() and nan[:, 3].all() and nan.sum() == N + M - 1
+
+
+def test_mx_gemm_at_and_leading_dimensions_match_full():
+    rng = np.random.default_rng(59)
+    M, N, K, lda, ldb = 6, 5, 128, 192, 160
+    pa = rng.integers(0, 16, (M, lda))
+    pb = rng.integers(0, 16, (N, ldb))
+    A, B = mx_pack("e2m1", pa), mx_pack("e2m1", pb)
+    SA = rng.integers(120, 135, (M, 7)).astype(np.uint8)
+    SB = rng.integers(120, 135, (N, 6)).astype(np.uint8)
+    C0 = rng.standard_normal((N, M)).astype(np.float32)  # column-major C, ldc = M
+    ref, den = oracle.mx_gemm("e2m1", "e2m1", "f32", M, N, K, 1.0, A, lda, SA.ravel(), 7, B, ldb,
+                              SB.ravel(), 6, 0.5, C0.ravel(), M, COL)
+    # the same problem with the padding cut away and C transposed to row-major
+    A2, B2 = mx_pack("e2m1", pa[:, :K]), mx_pack("e2m1", pb[:, :K])
+    ref2, den2 = oracle.mx_gemm("e2m1", "e2m1", "f32", M, N, K, 1.0, A2, K,
+                                np.ascontiguousarray(SA[:, :4]).ravel(), 4, B2, K,
+                                np.ascontiguousarray(SB[:, :4]).ravel(), 4, 0.5,
+                                np.ascontiguousarray(C0.T).ravel(), N, ROW)
+    assert np.array_equal(ref, ref2) and np.array_equal(den, den2)
+    idx = np.array([[0, i, j] for i in range(M) for j in range(N)])
+    r, d = oracle.mx_gemm_at("e2m1", "e2m1", "f32", M, N, K, 1.0, A, lda, SA.ravel(), 7, B, ldb,
+                             SB.ravel(), 6, 0.5, C0.ravel(), M, COL, idx)
+    assert np.array_equal(r, ref[0].ravel()) and np.array_equal(d, den[0].ravel())
