@@ -17,13 +17,16 @@ from oracle import build as obuild
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTANTS = {
-    "sum_sign": ("s = s + p;", "s = s - p;"),
+    "sum_sign": ("double p = a * x;\n            s = s + p;", "double p = a * x;\n            s = s - p;"),
     "a_transposed": ("offset(P->oA, i, k, P->lda)", "offset(P->oA, k, i, P->lda)"),
     "b_transposed": ("offset(P->oB, k, j, P->ldb)", "offset(P->oB, j, k, P->ldb)"),
-    "beta_dropped": ("r = r + P->beta * c0;", "r = r + c0;"),
-    "alpha_dropped": ("double r = P->alpha * s;", "double r = s;"),
-    "den_beta_dropped": ("d = d + fabs(P->beta) * fabs(c0);", "d = d;"),
-    "last_k_dropped": ("k < P->K; ++k", "k + 1 < P->K; ++k"),
+    "beta_dropped": ("r = r + P->beta * c0;\n        d = d + fabs(P->beta) * fabs(c0);\n    }\n    if (P->bias",
+                     "r = r + c0;\n        d = d + fabs(P->beta) * fabs(c0);\n    }\n    if (P->bias"),
+    "alpha_dropped": ("double r = P->alpha * s;\n    double d = fabs(P->alpha) * t;\n    if (P->beta != 0.0) {\n        double c0",
+                      "double r = s;\n    double d = fabs(P->alpha) * t;\n    if (P->beta != 0.0) {\n        double c0"),
+    "den_beta_dropped": ("d = d + fabs(P->beta) * fabs(c0);\n    }\n    if (P->bias",
+                         "d = d;\n    }\n    if (P->bias"),
+    "last_k_dropped": ("k < P->K; ++k) {\n            double a", "k + 1 < P->K; ++k) {\n            double a"),
     "col_major_ignored": ("order == ORC_ROW ? r * ld + c : c * ld + r",
                           "order == ORC_ROW ? r * ld + c : r * ld + c"),
     "batch_stride_b_wrong": ("b0 = b * P->sB", "b0 = b * P->sA"),
@@ -67,6 +70,9 @@ MUTANTS = {
                     "const double p = xa * xb;\n            s = s - p;"),
     "mx_beta_dropped": ("r = r + P->beta * c0;\n        d = d + fabs(P->beta) * fabs(c0);\n    }\n    *ref = r;",
                         "r = r + c0;\n        d = d + fabs(P->beta) * fabs(c0);\n    }\n    *ref = r;"),
+    "mx_alpha_dropped": ("double r = P->alpha * s;\n    double d = fabs(P->alpha) * t;\n    if (P->beta != 0.0) {\n        const double c0",
+                         "double r = s;\n    double d = fabs(P->alpha) * t;\n    if (P->beta != 0.0) {\n        const double c0"),
+    "mx_last_k_dropped": ("k < P->K; ++k) {\n            const double xa", "k + 1 < P->K; ++k) {\n            const double xa"),
     "mx_scale_raw_exponent": ("decode_e8m0(P->SB[", "(double)(P->SB["),
     "rows_last_k_dropped": ("for (int64_t k = 0; k < K; ++k) {\n                    const double *x",
                             "for (int64_t k = 0; k + 1 < K; ++k) {\n                    const double *x"),
