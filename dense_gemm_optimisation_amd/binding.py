@@ -21,6 +21,8 @@ ROW_MAJOR, COL_MAJOR = 0, 1
 DTYPE_SAME, DTYPE_F32 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 F8_E4M3, F8_E5M2 = 0, 1
+MX_E4M3, MX_E5M2, MX_E2M3, MX_E3M2, MX_E2M1 = 0, 1, 2, 3, 4
+MX_FORMAT = {"e4m3": MX_E4M3, "e5m2": MX_E5M2, "e2m3": MX_E2M3, "e3m2": MX_E3M2, "e2m1": MX_E2M1}
 OUTPUT_F32, OUTPUT_BF16, OUTPUT_F16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4
 # gemm_test_switches flags
@@ -70,6 +72,12 @@ def library() -> ctypes.CDLL:
         lib.gemm_f8.restype = i32
         lib.gemm_f8_kernel_name.argtypes = f8
         lib.gemm_f8_kernel_name.restype = ctypes.c_char_p
+        mx = [i64, i64, i64, f32, vp, i64, i32, vp, i64, vp, i64, i32, vp, i64, f32, vp, i64,
+              i32, i32, i64, i64, i64, i64, i64, i64]
+        lib.gemm_mx.argtypes = mx + [vp]
+        lib.gemm_mx.restype = i32
+        lib.gemm_mx_kernel_name.argtypes = mx
+        lib.gemm_mx_kernel_name.restype = ctypes.c_char_p
         sz = ctypes.c_size_t
         lib.gemm_workspace_size.argtypes = []
         lib.gemm_workspace_size.restype = sz
@@ -203,6 +211,29 @@ def f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, f
     name = library().gemm_f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb,
                                          order_b, format_b, beta, C, ldc, order_c, type_c, batch,
                                          stride_a, stride_b, stride_c)
+    return None if name is None else name.decode()
+
+
+def gemm_mx(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb, format_b, scale_b, ldsb,
+            beta, C, ldc, order_c, type_c, batch=1, stride_a=0, stride_b=0, stride_scale_a=0,
+            stride_scale_b=0, stride_c=0, stream=None, raise_on_error=True):
+    """Block-scaled inputs (MX_* formats, E8M0 scales per 32 elements along
+    K), A row-major and B column-major (both contiguous along K), output
+    type_c (OUTPUT_*).  Device addresses as integers."""
+    st = library().gemm_mx(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb, format_b,
+                           scale_b, ldsb, beta, C, ldc, order_c, type_c, batch, stride_a, stride_b,
+                           stride_scale_a, stride_scale_b, stride_c, _stream(stream))
+    return _check(st, "gemm_mx", raise_on_error)
+
+
+def mx_kernel_name(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb, format_b, scale_b,
+                   ldsb, beta, C, ldc, order_c, type_c, batch=1, stride_a=0, stride_b=0,
+                   stride_scale_a=0, stride_scale_b=0, stride_c=0):
+    """The kernel gemm_mx would launch for these arguments (None if invalid)."""
+    name = library().gemm_mx_kernel_name(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb,
+                                          format_b, scale_b, ldsb, beta, C, ldc, order_c, type_c,
+                                          batch, stride_a, stride_b, stride_scale_a,
+                                          stride_scale_b, stride_c)
     return None if name is None else name.decode()
 
 

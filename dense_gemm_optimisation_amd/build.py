@@ -26,10 +26,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "scale.hip", "pack.hip", "noalloc.hip", "sgemm_valu.hip", "sgemm_mfma.hip", "sgemm_splitk.hip", "hgemm_mfma.hip", "hgemm_mfma_dma.hip",
-           "hgemm_splitk.hip", "gemm_skinny.hip", "f8gemm_mfma.hip"]
-# Sources compiled once per part (-DLIBGEMM_HGEMM_PART=k, one object each), so
-# that their many kernel instantiations build in parallel.
-PARTS = {"hgemm_mfma.hip": 4}
+           "hgemm_splitk.hip", "gemm_skinny.hip", "f8gemm_mfma.hip", "mxgemm.hip"]
+# Sources compiled once per part (-D<macro>=k, one object each), so that
+# their many kernel instantiations build in parallel: source -> (macro, parts).
+PARTS = {"hgemm_mfma.hip": ("LIBGEMM_HGEMM_PART", 4), "mxgemm.hip": ("LIBGEMM_MX_PART", 3)}
 
 
 def units():
@@ -37,7 +37,7 @@ def units():
     out = []
     for s in SOURCES:
         n = PARTS.get(s)
-        out += [(s, None)] if n is None else [(s, k) for k in range(n)]
+        out += [(s, None)] if n is None else [(s, k) for k in range(n[1])]
     return out
 
 
@@ -54,7 +54,7 @@ def _compile(src: str, verbose: bool, part=None):
     obj = object_path(src, part)
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if part is not None:
-        cmd.insert(1, f"-DLIBGEMM_HGEMM_PART={part}")
+        cmd.insert(1, f"-D{PARTS[src][0]}={part}")
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
         cmd.append("-Rpass-analysis=kernel-resource-usage")

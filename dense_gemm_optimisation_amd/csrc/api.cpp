@@ -74,6 +74,7 @@ enum class Kernel {
     HgemmPackDmaStreamK,  // then its stream-K schedule
     SgemmPackDma,         // then the fp32 direct-load kernel
     SgemmPackDmaStreamK,  // then its stream-K schedule
+    Mx,                   // block-scaled narrow floats (gemm_mx), direct loads
 };
 
 bool is_packed(Kernel k) {
@@ -103,6 +104,7 @@ const char *kernel_name(Kernel k) {
     case Kernel::HgemmPackDmaStreamK: return "hgemm_mfma_dma_streamk_packed";
     case Kernel::SgemmPackDma: return "sgemm_mfma_dma_packed";
     case Kernel::SgemmPackDmaStreamK: return "sgemm_mfma_dma_streamk_packed";
+    case Kernel::Mx: return "mxgemm_mfma_dma";
     }
     return "";
 }
@@ -150,6 +152,7 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::HgemmPackDmaStreamK:
     case Kernel::SgemmPackDma:
     case Kernel::SgemmPackDmaStreamK: return hipErrorInvalidValue;  // need the workspace: run()
+    case Kernel::Mx: return hipErrorInvalidValue;  // needs the scales: gemm_mx
     }
     return hipErrorInvalidValue;
 }
@@ -481,9 +484,140 @@ bool output_type(gemm_output_t t, Elem &e) {
     return true;
 }
 
+// Validates a gemm_mx call and builds its canonical problem (row-major C;
+// a column-major C is computed as C^T = B^T A^T, which swaps the roles of
+// the two K-contiguous operands and their scales).  No HIP call.
+gemm_status_t mx_plan(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                      gemm_mx_format_t formatA, const uint8_t *scaleA, int64_t ldsa,
+                      const void *B, int64_t ldb, gemm_mx_format_t formatB,
+                      const uint8_t *scaleB, int64_t ldsb, float beta, const void *C,
+                      int64_t ldc, gemm_order_t orderC, gemm_output_t typeC, int64_t batch,
+                      int64_t strideA, int64_t strideB, int64_t strideScaleA,
+                      int64_t strideScaleB, int64_t strideC, MxProblem &m, Kernel &kernel) {
+    kernel = Kernel::None;
+    Elem ec;
+    auto fmt_ok = [](gemm_mx_format_t f) { return f >= GEMM_MX_E4M3 && f <= GEMM_MX_E2M1; };
+    if (!fmt_ok(formatA) || !fmt_ok(formatB) || !output_type(typeC, ec) || !valid_order(orderC))
+        return GEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || batch < 0 || strideA < 0 || strideB < 0 || strideC < 0 ||
+        strideScaleA < 0 || strideScaleB < 0)
+        return GEMM_ERR_INVALID_ARG;
+    if (K % 64 != 0) return GEMM_ERR_INVALID_ARG;
+    const int64_t min_ldc = orderC == GEMM_ROW_MAJOR ? N : M;
+    if (ldc < (min_ldc > 1 ? min_ldc : 1)) return GEMM_ERR_INVALID_ARG;
+    if (too_big(M, N) || too_big(M * N, batch) || too_big(M, K) || too_big(K, N) ||
+        too_big(batch - 1, strideC) || too_big(batch - 1, strideA) || too_big(batch - 1, strideB) ||
+        too_big(batch - 1, strideScaleA) || too_big(batch - 1, strideScaleB))
+        return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+
+    const bool reads = K > 0 && alpha != 0.0f;
+    const int eout = elem_bytes(ec);
+    const int wa = mx_width(formatA), wb = mx_width(formatB);
+    const int64_t span_c = span(M, N, orderC, ldc);
+    if (C == nullptr || reinterpret_cast<uintptr_t>(C) % eout != 0) return GEMM_ERR_INVALID_ARG;
+    if (batch > 1 && strideC < span_c) return GEMM_ERR_INVALID_ARG;  // C slices overlap
+    const Range rc = range_of(C, span_c, batch, strideC, eout);
+    const int64_t sbytes = 4 * ((K + 127) / 128);  // scale bytes per row the kernel reads
+    if (reads) {
+        if (A == nullptr || B == nullptr || scaleA == nullptr || scaleB == nullptr)
+            return GEMM_ERR_INVALID_ARG;
+        if (lda < K || ldb < K || lda % 64 != 0 || ldb % 64 != 0) return GEMM_ERR_INVALID_ARG;
+        if (batch > 1 && (strideA % 64 != 0 || strideB % 64 != 0)) return GEMM_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(A) % 16 != 0 || reinterpret_cast<uintptr_t>(B) % 16 != 0)
+            return GEMM_ERR_INVALID_ARG;
+        if (ldsa < sbytes || ldsb < sbytes || ldsa % 4 != 0 || ldsb % 4 != 0)
+            return GEMM_ERR_INVALID_ARG;
+        if (batch > 1 && (strideScaleA % 4 != 0 || strideScaleB % 4 != 0)) return GEMM_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(scaleA) % 4 != 0 ||
+            reinterpret_cast<uintptr_t>(scaleB) % 4 != 0)
+            return GEMM_ERR_INVALID_ARG;
+        // byte extents of one slice of each operand and of its scales
+        const int64_t bytes_a = ((M - 1) * lda + K) * wa / 8, bytes_b = ((N - 1) * ldb + K) * wb / 8;
+        const int64_t sc_a = (M - 1) * ldsa + sbytes, sc_b = (N - 1) * ldsb + sbytes;
+        if (overlap(rc, range_of(A, bytes_a, batch, strideA * wa / 8, 1)) ||
+            overlap(rc, range_of(B, bytes_b, batch, strideB * wb / 8, 1)) ||
+            overlap(rc, range_of(scaleA, sc_a, batch, strideScaleA, 1)) ||
+            overlap(rc, range_of(scaleB, sc_b, batch, strideScaleB, 1)))
+            return GEMM_ERR_INVALID_ARG;
+        if (wa != wb) return GEMM_ERR_UNSUPPORTED;
+        // the kernel addresses a slice with 32-bit byte offsets
+        const int64_t limit = int64_t(1) << 30;
+        if (bytes_a >= limit || bytes_b >= limit || M * ldsa >= limit || N * ldsb >= limit)
+            return GEMM_ERR_UNSUPPORTED;
+    }
+
+    Problem &p = m.p;
+    p = Problem{};
+    p.K = K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.C = const_cast<void *>(C);
+    p.ldc = ldc;
+    p.batch = batch;
+    p.sC = strideC;
+    p.out = ec;
+    p.in = p.in_b = Elem::E4M3;  // unused: the formats are in m
+    p.a_kmajor = p.b_kmajor = true;
+    const bool row = orderC == GEMM_ROW_MAJOR;
+    p.M = row ? M : N;
+    p.N = row ? N : M;
+    p.A = row ? A : B;
+    p.lda = row ? lda : ldb;
+    p.sA = row ? strideA : strideB;
+    p.B = row ? B : A;
+    p.ldb = row ? ldb : lda;
+    p.sB = row ? strideB : strideA;
+    m.fa = static_cast<int>(row ? formatA : formatB);
+    m.fb = static_cast<int>(row ? formatB : formatA);
+    m.sa = row ? scaleA : scaleB;
+    m.sb = row ? scaleB : scaleA;
+    m.ldsa = row ? ldsa : ldsb;
+    m.ldsb = row ? ldsb : ldsa;
+    m.ssa = row ? strideScaleA : strideScaleB;
+    m.ssb = row ? strideScaleB : strideScaleA;
+    kernel = reads ? Kernel::Mx : Kernel::Scale;
+    return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+gemm_status_t gemm_mx(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                      gemm_mx_format_t formatA, const uint8_t *scaleA, int64_t ldsa,
+                      const void *B, int64_t ldb, gemm_mx_format_t formatB,
+                      const uint8_t *scaleB, int64_t ldsb, float beta, void *C, int64_t ldc,
+                      gemm_order_t orderC, gemm_output_t typeC, int64_t batch, int64_t strideA,
+                      int64_t strideB, int64_t strideScaleA, int64_t strideScaleB,
+                      int64_t strideC, hipStream_t stream) {
+    MxProblem m;
+    Kernel k;
+    const gemm_status_t st =
+        mx_plan(M, N, K, alpha, A, lda, formatA, scaleA, ldsa, B, ldb, formatB, scaleB, ldsb, beta, C,
+                ldc, orderC, typeC, batch, strideA, strideB, strideScaleA, strideScaleB, strideC, m, k);
+    if (st != GEMM_OK || k == Kernel::None) return st;
+    const hipError_t err = k == Kernel::Mx ? launch_mxgemm(m, stream) : launch_scale(m.p, stream);
+    if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+const char *gemm_mx_kernel_name(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                                int64_t lda, gemm_mx_format_t formatA, const uint8_t *scaleA,
+                                int64_t ldsa, const void *B, int64_t ldb,
+                                gemm_mx_format_t formatB, const uint8_t *scaleB, int64_t ldsb,
+                                float beta, const void *C, int64_t ldc, gemm_order_t orderC,
+                                gemm_output_t typeC, int64_t batch, int64_t strideA,
+                                int64_t strideB, int64_t strideScaleA, int64_t strideScaleB,
+                                int64_t strideC) {
+    MxProblem m;
+    Kernel k;
+    if (mx_plan(M, N, K, alpha, A, lda, formatA, scaleA, ldsa, B, ldb, formatB, scaleB, ldsb, beta, C,
+                ldc, orderC, typeC, batch, strideA, strideB, strideScaleA, strideScaleB, strideC, m,
+                k) != GEMM_OK)
+        return nullptr;
+    return kernel_name(k);
+}
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                        gemm_order_t orderA, const float *B, int64_t ldb, gemm_order_t orderB,

@@ -72,8 +72,10 @@ __device__ inline int swz_k(int row) {
 __device__ inline int swz_mn(int krow) { return ((krow & 7) ^ (((krow >> 3) & 1) << 2)) << 2; }
 
 // One operand panel of the tile (256 rows of A or 256 columns of B, BK deep):
-// where each lane fetches from, and how the wave reads fragments back.
-template <bool KMAJOR, int WAVES, int BK>
+// where each lane fetches from, and how the wave reads fragments back.  A
+// K-contiguous panel's stage advances STEP 16-bit units along the rows
+// (BK unless a stage uses only the first STEP of the BK it loads).
+template <bool KMAJOR, int WAVES, int BK, int STEP = BK>
 struct Operand {
     static constexpr int PANEL = 256 * BK * 2;        // bytes
     static constexpr int BLOCKS = PANEL / 1024;       // 1 KiB direct loads per panel
@@ -109,7 +111,7 @@ struct Operand {
                 voff[i] = gc < R ? uint32_t((krow * ld + gc) * 2) : OOB;
             }
         }
-        step = KMAJOR ? int64_t(BK) * 2 : int64_t(BK) * ld * 2;
+        step = KMAJOR ? int64_t(STEP) * 2 : int64_t(BK) * ld * 2;
     }
 
     // Buffer descriptor of the slice that stage `stage` starts (raw buffer:
@@ -122,7 +124,7 @@ struct Operand {
     }
 
     // Direct load i (of PER_WAVE) of this wave for the stage with descriptor
-    // rs and kleft = K - stage*BK valid k values, into the panel at lds0.
+    // rs and kleft = K - stage*STEP valid k values, into the panel at lds0.
     __device__ void load(u32x4 rs, uint32_t lds0, int i, int64_t kleft, int wave) const {
         const uint32_t v = (kleft < BK && kl[i] >= kleft) ? OOB : voff[i];
         direct_load16(rs, lds0 + (wave * PER_WAVE + i) * 1024, v);
@@ -133,7 +135,7 @@ struct Operand {
         const u32x4 rs = rsrc(stage);
         const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) load(rs, lds0, i, K - stage * BK, wave);
+        for (int i = 0; i < PER_WAVE; ++i) load(rs, lds0, i, K - stage * STEP, wave);
     }
 
     // Fragment of 32 rows (from row `row0` of the panel) for k16 step kk.

@@ -1,0 +1,411 @@
+// The direct-load GEMM of narrow floats on the CDNA4 matrix cores, for
+// operands stored K-contiguous (row-major A, column-major B): 8-bit floats
+// (E4M3, E5M2) with no scaling, and the block-scaled formats (MXFP8 with
+// E4M3/E5M2 elements, MXFP6 with E2M3/E3M2, MXFP4 with E2M1), in which each
+// 32 consecutive elements of a row share one E8M0 scale ("CUDA GEMM 矩阵乘法
+// 优化指南", blog.zhenwei.site, section 13.2, FP8 and the block-scale
+// quantisation of FP4/FP6).  Output in fp32, bf16 or fp16.
+//
+// Matrix instruction: v_mfma_scale_f32_32x32x64_f8f6f4, 64 k per instruction.
+// A lane's fragment of a 32 x 64 block is 32 k of one row (row lane % 32):
+// for 6- and 4-bit elements (24 or 16 bytes) the consecutive k of block
+// lane / 32, for 8-bit ones 16 k of each block (see frag8); the lane's
+// scale operand is the E8M0 byte of block lane / 32 (a constant 2^0 without
+// scaling).  The
+// operands are swapped (C^T = B^T A^T) as in the 16-bit kernels, so a lane's
+// accumulators hold consecutive columns of C.
+//
+// The pipeline is the 16-bit direct-load one of dma_tile.hpp (256 x 256 block
+// tile, 2 x 4 waves, two LDS stages) run on the bytes viewed as 16-bit pairs.
+// A stage is 128 k of every format: a K-contiguous panel row of 128 bytes
+// for 8-bit elements, 64 bytes for 4-bit ones, and for 6-bit ones 128 bytes
+// loaded of which the first 96 are that stage's (the stage advances 96 bytes
+// along the row; the rest is loaded again as the next stage's start).  With
+// scales, each stage also moves the four scale bytes (blocks 4s .. 4s+3) of
+// every panel row into LDS, one 4-byte direct load per lane, in the same
+// load group as the stage's operands.
+#pragma once
+
+#include <type_traits>
+
+#include "dma_tile.hpp"
+
+namespace libgemm {
+namespace {
+
+using namespace dmatile;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Operand format codes of the scaled matrix instruction.
+constexpr int FMT_E4M3 = 0, FMT_E5M2 = 1, FMT_E2M3 = 2, FMT_E3M2 = 3, FMT_E2M1 = 4;
+
+template <int F>
+struct Fmt {
+    static constexpr int WIDTH = F == FMT_E2M1 ? 4 : (F == FMT_E2M3 || F == FMT_E3M2) ? 6 : 8;
+    static constexpr int ROWB = WIDTH == 4 ? 64 : 128;  // LDS bytes per panel row per stage
+    static constexpr int STEPB = 128 * WIDTH / 8;       // bytes of a row per stage (128 k)
+};
+
+// Kernel arguments.  d carries C, the scalars, the epilogue, the tile grid,
+// and the leading dimensions and batch strides of A and B in 16-bit units.
+struct F8Args {
+    DmaArgs d;
+    int64_t K;                // k extent (elements); a multiple of 16 bytes per row
+    int64_t ka, kb;           // row extents along K of A and B, in 16-bit units
+    const uint8_t *sa, *sb;   // E8M0 scales: A(i, k) has sa[i*ldsa + k/32]; B(k, j) sb[j*ldsb + k/32]
+    int64_t ldsa, ldsb;       // bytes, multiples of 4
+    int64_t ssa, ssb;         // batch strides of the scales, bytes
+};
+
+// The 32-byte fragment of row row0 + lane % 32 for k step kk (64 k) of a
+// K-contiguous panel with 8 chunks of 16 bytes per row, swizzled by
+// swz_k<8>.  With 8-bit elements the instruction takes the low 16 bytes of
+// every lane as k of the first 32-k block and the high 16 as k of the
+// second (measured on gfx950: a one-hot A at each k under two block scales),
+// so lane half h reads 16-k chunk 4kk + h (block 2kk) and chunk 4kk + 2 + h
+// (block 2kk + 1), and its scale byte is that of block 2kk + h for the
+// instruction's own pairing of lanes with blocks.  row0 is a multiple of
+// 32, so the row's swizzle is that of lane % 32 with bit 2 flipped when bit
+// 5 of row0 is set; written this way the per-lane part of every fragment
+// address is one of eight values shared by all rows of both panels, and the
+// row enters as a constant or wave-uniform offset.
+__device__ inline i32x8 frag8(const LDS char *panel, int row0, int kk, int lane) {
+    const int l = lane & 31;
+    const int s = swz_k<8>(l) ^ ((row0 >> 3) & 7);
+    const int c = kk * 4 + (lane >> 5);
+    const LDS char *r = panel + row0 * 128 + l * 128;
+    const u32x4 lo = *reinterpret_cast<const LDS u32x4 *>(r + ((c ^ s) << 4));
+    const u32x4 hi = *reinterpret_cast<const LDS u32x4 *>(r + (((c + 2) ^ s) << 4));
+    return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                 int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+}
+
+// 6-bit elements: the lane's 24 bytes start at byte 24*(2kk + lane/32) of a
+// 128-byte panel row; read as three 8-byte words, each inside one chunk.
+__device__ inline i32x8 frag6(const LDS char *panel, int row0, int kk, int lane) {
+    const int row = row0 + (lane & 31);
+    const int s = swz_k<8>(row);
+    const int o0 = 24 * (2 * kk + (lane >> 5));
+    const LDS char *r = panel + row * 128;
+    i32x8 out = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const int o = o0 + 8 * w;
+        const u32x2 v = *reinterpret_cast<const LDS u32x2 *>(r + (((o >> 4) ^ s) << 4) + (o & 8));
+        out[2 * w] = int(v[0]);
+        out[2 * w + 1] = int(v[1]);
+    }
+    return out;
+}
+
+// 4-bit elements: the lane's 16 bytes are chunk 2kk + lane/32 of a 64-byte
+// panel row swizzled by swz_k<4>.
+__device__ inline i32x8 frag4(const LDS char *panel, int row0, int kk, int lane) {
+    const int row = row0 + (lane & 31);
+    const int c = 2 * kk + (lane >> 5);
+    const u32x4 v = *reinterpret_cast<const LDS u32x4 *>(panel + row * 64 + ((c ^ swz_k<4>(row)) << 4));
+    return i32x8{int(v[0]), int(v[1]), int(v[2]), int(v[3]), 0, 0, 0, 0};
+}
+
+template <int F>
+__device__ inline i32x8 frag(const LDS char *panel, int row0, int kk, int lane) {
+    if (Fmt<F>::WIDTH == 8) return frag8(panel, row0, kk, lane);
+    if (Fmt<F>::WIDTH == 6) return frag6(panel, row0, kk, lane);
+    return frag4(panel, row0, kk, lane);
+}
+
+// acc + (B^T block) (A^T block) for k step KK of a stage: the first operand
+// is B's fragment in B's format.  Scale operands: byte 2*KK of sb and sa
+// (each lane's word holds the stage's block 2*kk + lane/32 in byte 2*kk).
+template <int FA, int FB, int KK>
+__device__ inline f32x16 mma8(i32x8 b, i32x8 a, f32x16 c, int sb, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, 2 * KK, sb, 2 * KK, sa);
+}
+
+// 0x7F in every byte: E8M0 2^0 whichever byte the instruction selects.
+constexpr int UNIT_SCALE = 0x7F7F7F7F;
+
+// Schedule of one row of a wave tile: one matrix instruction, the NREAD LDS
+// reads issued with it, the row's other instructions; then a scheduling
+// barrier, so that the compiler keeps the rows in program order instead of
+// hoisting every read of a stage to its top (which would need all the
+// fragments live at once) and sinking the matrix instructions past the
+// workgroup barrier.
+template <int NREAD, int FN>
+__device__ inline void hint_row() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, FN - 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// An empty volatile statement that takes x as an operand in the given
+// register file: the instruction that produced x cannot move past it.
+template <bool AGPR>
+__device__ inline void pin(const f32x16 &x) {
+    if (!AGPR) asm volatile("" ::"v"(x));
+}
+
+// buffer_load_dword ... lds: 4 bytes per lane from the buffer `rs` at byte
+// offset `voffset` into LDS at `lds` + 4 * lane (the same contract as
+// dma::direct_load16).
+__device__ inline void direct_load4(u32x4 rs, uint32_t lds, uint32_t voffset) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"(voffset), "s"(rs)
+        : "memory", "m0");
+}
+
+#ifndef LIBGEMM_F8_WM
+#define LIBGEMM_F8_WM 2
+#endif
+#ifndef LIBGEMM_F8_WN
+#define LIBGEMM_F8_WN 4
+#endif
+#ifndef LIBGEMM_F8_STAGES
+#define LIBGEMM_F8_STAGES 2
+#endif
+#ifndef LIBGEMM_F8_GROUP_M
+#define LIBGEMM_F8_GROUP_M 16
+#endif
+
+constexpr int F8_BM = 256, F8_BN = 256;
+
+// 2 x 4 waves, each with a 128 x 64 wave tile (4 x 2 accumulator blocks,
+// 128 registers); a stage is 128 k, two 64-k steps.  A lane's fragments are
+// twice the size of the 16-bit kernel's, so double-buffering all of them
+// would not fit beside the accumulators in the 256 registers a wave has at
+// two waves per SIMD.  Instead B's two fragments are double-buffered by k
+// step and A's four rotate through two slots: the instructions of row i (two
+// of them) run while row i + 1's fragment is read, and the last row's run
+// while the next k step's fragments are read.  At the end of a stage those
+// reads target the next stage's buffer, so they follow the wait for that
+// stage and the workgroup barrier; the refill of the stage just consumed is
+// issued between the last two instructions, after the barrier has shown
+// that every wave has read it.  With scales (MX), each lane reads its six
+// fragments' scale words from the stage's buffer right after the barrier,
+// into registers that take over once the current stage's last row is done.
+template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8Args p) {
+    constexpr int WAVES = WAVES_M * WAVES_N;
+    constexpr int BM = F8_BM, BN = F8_BN;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 32, FN = WTN / 32;
+    // Accumulators beyond 128 registers per lane live in the AGPRs (one
+    // wave per SIMD); the statement that pins the instructions in place
+    // must name the register file they are in.
+    constexpr bool ACC_AGPR = FM * FN * 16 > 128;
+    static_assert(FM % 2 == 0, "A fragments alternate between two slots");
+    static_assert(!MX || WAVES == 8, "scale loads: four waves per operand, 64 rows each");
+    using OpA = Operand<true, WAVES, Fmt<FA>::ROWB / 2, Fmt<FA>::STEPB / 2>;
+    using OpB = Operand<true, WAVES, Fmt<FB>::ROWB / 2, Fmt<FB>::STEPB / 2>;
+    constexpr int PANEL_A = OpA::PANEL, PANEL_B = OpB::PANEL;
+    constexpr int SCALES = MX ? 4 * (BM + BN) : 0;   // bytes per stage
+    constexpr int DATA = PANEL_A + PANEL_B + SCALES;
+    constexpr int EPI = WAVES * 32 * WTN * 4;        // epilogue staging
+    constexpr int STAGE = DATA > EPI ? DATA : EPI;
+    constexpr int PER_DATA = OpA::PER_WAVE + OpB::PER_WAVE;
+    constexpr int PER_STAGE = PER_DATA + (MX ? 1 : 0);  // direct loads per wave per stage
+    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(PER_DATA % FN == 0, "refill split over the last row's instructions");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+    const DmaArgs &d = p.d;
+    TileCoord t = tile_of(d.grid, blockIdx.x);
+    t.batch = uniform(t.batch);
+    t.tm = uniform(t.tm);
+    t.tn = uniform(t.tn);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+
+    OpA opa;
+    OpB opb;
+    opa.init(d.A + t.batch * d.sA, d.lda, d.M, m0, (d.M - 1) * d.lda + p.ka, wave, lane);
+    opb.init(d.B + t.batch * d.sB, d.ldb, d.N, n0, (d.N - 1) * d.ldb + p.kb, wave, lane);
+
+    // MX: this wave's scale load of a stage: waves 0-3 fetch the scale words
+    // of A's panel rows 64w .. 64w+63, waves 4-7 those of B's; rows past the
+    // matrix read zeros (their data is zero too).
+    u32x4 srs = {0u, 0u, 0u, 0u};
+    uint32_t svoff = OOB, slds = 0;
+    int64_t sld = 0;
+    if (MX) {
+        const bool on_a = wave < 4;
+        const int q = wave & 3;
+        const int64_t r = (on_a ? m0 : n0) + 64 * q + lane;
+        const int64_t R = on_a ? d.M : d.N;
+        sld = on_a ? p.ldsa : p.ldsb;
+        const uint8_t *base = on_a ? p.sa + t.batch * p.ssa : p.sb + t.batch * p.ssb;
+        srs = dma::raw_buffer(static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(base))),
+                              static_cast<uint32_t>(uniform(R * sld)));
+        svoff = r < R ? static_cast<uint32_t>(r * sld) : OOB;
+        slds = PANEL_A + PANEL_B + (on_a ? 0 : 4 * BM) + 256 * q;
+    }
+    LDS char *lds = (LDS char *)smem;
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+    auto load_scales = [&](int buf, int64_t stage) {
+        if (MX)
+            direct_load4(srs, lds_base + buf * STAGE + slds,
+                         svoff == OOB ? OOB : svoff + static_cast<uint32_t>(4 * stage));
+    };
+    const int64_t steps = (p.K + 127) / 128;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) {
+        if (st < steps) {
+            opa.issue(lds + st * STAGE, st, p.ka, wave);
+            opb.issue(lds + st * STAGE + PANEL_A, st, p.kb, wave);
+            load_scales(st, st);
+        }
+    }
+    wait_stages<PER_STAGE, STAGES>(int(steps - 1 < STAGES - 1 ? steps - 1 : STAGES - 1));
+    __syncthreads();
+
+    i32x8 fb[2][FN], fa[2];
+    auto read_b = [&](int buf, int kk, int slot) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fb[slot][j] = frag<FB>(lds + buf * STAGE + PANEL_A, wn * WTN + j * 32, kk, lane);
+    };
+    auto read_a = [&](int buf, int kk, int i) {
+        fa[i & 1] = frag<FA>(lds + buf * STAGE, wm * WTM + i * 32, kk, lane);
+    };
+    // the scale words of the stage in `buf`: fragment rows' four bytes,
+    // shifted so that k step kk's block (2kk + lane/32) sits in byte 2kk
+    int sa[FM], sb[FN], nsa[FM], nsb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa[i] = nsa[i] = UNIT_SCALE;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sb[j] = nsb[j] = UNIT_SCALE;
+    auto read_scales = [&](int buf) {
+        if (!MX) return;
+        const LDS uint32_t *s = reinterpret_cast<const LDS uint32_t *>(lds + buf * STAGE + PANEL_A + PANEL_B);
+        const int sh = 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) nsa[i] = int(s[wm * WTM + i * 32 + (lane & 31)] >> sh);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) nsb[j] = int(s[BM + wn * WTN + j * 32 + (lane & 31)] >> sh);
+    };
+    auto take_scales = [&]() {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sa[i] = nsa[i];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sb[j] = nsb[j];
+    };
+    // The empty volatile statement takes the results as operands, so the
+    // instructions stay where they are written: the compiler otherwise sinks
+    // them to the end of the loop body, past the workgroup barrier, and then
+    // has to keep every fragment of the stage live.
+    auto row = [&](int i, auto kk) {
+        constexpr int KK = decltype(kk)::value;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            acc[i][j] = mma8<FA, FB, KK>(fb[KK][j], fa[i & 1], acc[i][j], sb[j], sa[i]);
+            pin<ACC_AGPR>(acc[i][j]);
+        }
+    };
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    // k step 0 of a stage in buffer `buf` (B fragments in slot 0); its last
+    // row reads k step 1's fragments from the same buffer.
+    auto first_step = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            if (i + 1 < FM) {
+                read_a(buf, 0, i + 1);
+            } else {
+                read_b(buf, 1, 1);
+                read_a(buf, 1, 0);
+            }
+            row(i, K0{});
+            if (i + 1 < FM) hint_row<2, FN>();
+            else hint_row<2 * FN + 2, FN>();
+        }
+    };
+
+    read_b(0, 0, 0);
+    read_a(0, 0, 0);
+    read_scales(0);
+    take_scales();
+    int buf = 0;
+    const int64_t main_steps = steps - 1;
+    for (int64_t s = 0; s < main_steps; ++s) {
+        first_step(buf);
+        // k step 1: rows 0 .. FM-2 read the next row from this buffer
+#pragma unroll
+        for (int i = 0; i + 1 < FM; ++i) {
+            read_a(buf, 1, i + 1);
+            row(i, K1{});
+            hint_row<2, FN>();
+        }
+        const int64_t later = steps - 2 - s;
+        wait_stages<PER_STAGE, STAGES>(int(later < STAGES - 2 ? later : STAGES - 2));
+        wait_lgkmcnt0();
+        __syncthreads();
+        const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
+        read_b(nbuf, 0, 0);
+        read_a(nbuf, 0, 0);
+        read_scales(nbuf);
+        const int64_t refill = s + STAGES;
+        const bool do_refill = refill < steps;
+        const u32x4 ra = opa.rsrc(refill), rb = opb.rsrc(refill);
+        const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + buf * STAGE));
+        const int64_t kla = p.ka - refill * (Fmt<FA>::STEPB / 2);
+        const int64_t klb = p.kb - refill * (Fmt<FB>::STEPB / 2);
+        // the last row, with the refill of this buffer split around its
+        // instructions
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            acc[FM - 1][j] = mma8<FA, FB, 1>(fb[1][j], fa[(FM - 1) & 1], acc[FM - 1][j], sb[j], sa[FM - 1]);
+            pin<ACC_AGPR>(acc[FM - 1][j]);
+            if (do_refill) {
+#pragma unroll
+                for (int q = j * PER_DATA / FN; q < (j + 1) * PER_DATA / FN; ++q) {
+                    if (q < OpA::PER_WAVE) opa.load(ra, la, q, kla, wave);
+                    else opb.load(rb, la + PANEL_A, q - OpA::PER_WAVE, klb, wave);
+                }
+                if (j == 0) load_scales(buf, refill);
+            }
+        }
+        take_scales();
+        buf = nbuf;
+    }
+    // The last stage.  When it holds only 64 k (K = 64 mod 128), its second
+    // k step reads zeros from both panels; its scales come from bytes past
+    // the last scale block, so they are replaced by 2^0 (a NaN pattern there
+    // would turn the zero products into NaN).
+    first_step(buf);
+    if (MX && (p.K & 127) != 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sa[i] = UNIT_SCALE;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sb[j] = UNIT_SCALE;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        if (i + 1 < FM) read_a(buf, 1, i + 1);
+        row(i, K1{});
+        if (i + 1 < FM) hint_row<2, FN>();
+    }
+
+    // C is staged in the buffer after the last stage's: every wave finished
+    // reading it before the last barrier and no load targets it any more.
+    LDS char *stage_free = lds + (buf + 1 == STAGES ? 0 : buf + 1) * STAGE;
+    store_tile_lds<OUT, FM, FN>(d, acc, t.batch, m0 + wm * WTM, n0 + wn * WTN, lane,
+                                reinterpret_cast<LDS float *>(stage_free) + wave * 32 * WTN);
+}
+
+}  // namespace
+}  // namespace libgemm

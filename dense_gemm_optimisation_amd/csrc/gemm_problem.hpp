@@ -154,4 +154,24 @@ hipError_t launch_f8gemm_dma(const Problem &p, hipStream_t stream);
 hipError_t launch_f8gemm(const Problem &p, hipStream_t stream);
 hipError_t launch_scale(const Problem &p, hipStream_t stream);  // C <- beta*C only
 
+// A block-scaled (MX) problem.  p holds the extents, scalars, C and the batch
+// with A and B K-contiguous (A(i, k) at element i*lda + k, B(k, j) at
+// element j*ldb + k of their packed element streams; lda, ldb, sA and sB in
+// elements); fa and fb are the matrix instruction's format codes (0 E4M3,
+// 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1); A(i, k)'s E8M0 scale is
+// sa[i*ldsa + k/32] (+ ssa per batch entry, bytes), B(k, j)'s sb[j*ldsb + k/32].
+struct MxProblem {
+    Problem p;
+    int fa, fb;
+    const uint8_t *sa, *sb;
+    int64_t ldsa, ldsb, ssa, ssb;
+};
+// Bits per element of a format code.
+inline int mx_width(int fmt) { return fmt == 4 ? 4 : (fmt == 2 || fmt == 3) ? 6 : 8; }
+// The direct-load 8-bit kernel with scales; needs K a multiple of 64, lda,
+// ldb, sA, sB multiples of 64 elements, 16-byte aligned A and B, ldsa and
+// ldsb multiples of 4 of at least 4*ceil(K/128) bytes, 4-byte aligned
+// scales, and fa, fb of one width (the api checks all of it).
+hipError_t launch_mxgemm(const MxProblem &m, hipStream_t stream);
+
 }  // namespace libgemm

@@ -23,12 +23,16 @@
  *              and an activation applied before the store (see below).
  *   gemm_f8    8-bit float inputs (OCP E4M3 or E5M2, each operand in its own
  *              format), fp32 accumulation, output in fp32, bf16 or fp16.
+ *   gemm_mx    block-scaled inputs (MXFP8, MXFP6, MXFP4: one E8M0 scale per
+ *              32 elements along K), fp32 accumulation, output in fp32,
+ *              bf16 or fp16.
  *   gemm_f32_ws, gemm_bf16_ws, gemm_f16_ws  the products with a caller-provided
  *              workspace, which lets the library copy unaligned operands
  *              into aligned ones and run the stream-K schedule (see below);
  *              gemm_workspace_size gives the bytes it needs.
  *   gemm_bf16_noalloc  gemm_bf16_ws on the library's own scratch memory.
- *   gemm_kernel_name, gemm_f8_kernel_name, gemm_kernel_name_ws  which kernel
+ *   gemm_kernel_name, gemm_f8_kernel_name, gemm_mx_kernel_name,
+ *   gemm_kernel_name_ws  which kernel
  *              a GEMM call with the
  *              given arguments would launch (host only; for tests and
  *              profiling).
@@ -116,7 +120,18 @@ typedef enum gemm_f8_format_t {
                          IEEE-style infinities and NaNs, largest finite 57344 */
 } gemm_f8_format_t;
 
-/* Element type of gemm_f8's C. */
+/* Element formats of gemm_mx's operands (the OCP microscaling element
+ * types).  None of the 6- and 4-bit ones has infinities or NaNs. */
+typedef enum gemm_mx_format_t {
+    GEMM_MX_E4M3 = 0, /* MXFP8: as GEMM_F8_E4M3 */
+    GEMM_MX_E5M2 = 1, /* MXFP8: as GEMM_F8_E5M2 */
+    GEMM_MX_E2M3 = 2, /* MXFP6: 1 sign, 2 exponent (bias 1), 3 fraction bits; largest 7.5 */
+    GEMM_MX_E3M2 = 3, /* MXFP6: 1 sign, 3 exponent (bias 3), 2 fraction bits; largest 28 */
+    GEMM_MX_E2M1 = 4  /* MXFP4: 1 sign, 2 exponent (bias 1), 1 fraction bit;
+                         0, 0.5, 1, 1.5, 2, 3, 4, 6 */
+} gemm_mx_format_t;
+
+/* Element type of the C of gemm_f8 and gemm_mx. */
 typedef enum gemm_output_t {
     GEMM_OUTPUT_F32 = 0,
     GEMM_OUTPUT_BF16 = 1,
@@ -248,6 +263,51 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
                       float beta, void *C, int64_t ldc, gemm_order_t orderC,
                       gemm_output_t typeC, int64_t batch, int64_t strideA,
                       int64_t strideB, int64_t strideC, hipStream_t stream);
+
+/* Block-scaled GEMM: C <- alpha * A * B + beta * C, where every 32
+ * consecutive elements along K of a row of A (a column of B) share one
+ * E8M0 scale, a power of two 2^(e - 127) (e = 255 is NaN): the block-scale
+ * quantisation of MXFP8/MXFP6/MXFP4 ("CUDA GEMM 矩阵乘法优化指南",
+ * blog.zhenwei.site, section 13.2).  The value of A(i, k) is
+ * 2^(scaleA[i*ldsa + k/32] - 127) times its element; products are exact and
+ * accumulate in fp32 (with the same reduced-precision additions as gemm_f8:
+ * the matrix instruction is the same), then alpha * acc + beta * C in fp32,
+ * rounded to typeC to nearest-even.
+ *   A        M x K, contiguous along K: row i is elements i*lda .. i*lda+K-1
+ *            of a packed element stream (8-bit formats one byte each; 6-bit
+ *            ones four elements in three bytes, 4-bit ones two per byte, the
+ *            stream little-endian: element n occupies bits w*n .. w*n+w-1,
+ *            bit b being bit b%8 of byte b/8).  Device memory, 16-byte
+ *            aligned; lda a multiple of 64 elements, at least K.
+ *   B        K x N, contiguous along K: column j is elements j*ldb ..
+ *            j*ldb+K-1 of its stream; the same rules.
+ *   scaleA   E8M0 bytes, row i of A's at scaleA + i*ldsa; 4-byte aligned,
+ *            ldsa a multiple of 4 and at least 4*ceil(K/128) (the kernel
+ *            reads scales four blocks at a time; bytes past ceil(K/32) in a
+ *            row are read but never used).  scaleB likewise for B's columns.
+ *   formatA, formatB  element formats of one width: both 8-bit (E4M3/E5M2,
+ *            in any combination), both 6-bit (E2M3/E3M2) or both E2M1;
+ *            a mixed-width pair is GEMM_ERR_UNSUPPORTED.
+ *   K        a multiple of 64 (two scale blocks).
+ *   C        typeC (fp32, or bf16/fp16 bit patterns), orderC, ldc as for
+ *            gemm_f8; a column-major C is computed as C^T = B^T A^T.
+ *   batch    strideA and strideB in elements (multiples of 64),
+ *            strideScaleA and strideScaleB in bytes (multiples of 4),
+ *            strideC in elements; 0 shares an operand or its scales.
+ * alpha == 0 or K == 0 gives beta * C without reading A, B or the scales.
+ * Any other layout rule broken, a format or typeC out of range, or C
+ * overlapping an operand or a scale array is GEMM_ERR_INVALID_ARG, before
+ * any HIP call; a slice of A, B or a scale array of 2^30 bytes or more is
+ * GEMM_ERR_UNSUPPORTED.  Ownership and synchronisation as for gemm_bf16. */
+gemm_status_t gemm_mx(int64_t M, int64_t N, int64_t K, float alpha,
+                      const void *A, int64_t lda, gemm_mx_format_t formatA,
+                      const uint8_t *scaleA, int64_t ldsa,
+                      const void *B, int64_t ldb, gemm_mx_format_t formatB,
+                      const uint8_t *scaleB, int64_t ldsb,
+                      float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                      gemm_output_t typeC, int64_t batch, int64_t strideA,
+                      int64_t strideB, int64_t strideScaleA,
+                      int64_t strideScaleB, int64_t strideC, hipStream_t stream);
 
 /* Workspace entry points.  gemm_f32_ws / gemm_bf16_ws / gemm_f16_ws take the
  * arguments of gemm_f32 / gemm_bf16 / gemm_f16 plus a device workspace, and
@@ -430,6 +490,22 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
                                 gemm_order_t orderC, gemm_output_t typeC,
                                 int64_t batch, int64_t strideA,
                                 int64_t strideB, int64_t strideC);
+
+/* The kernel gemm_mx would launch: "mxgemm_mfma_dma", "scale" when only
+ * beta * C is computed, "" when nothing is done, NULL for an invalid call
+ * (any status other than GEMM_OK).  Host only; no pointer is dereferenced. */
+const char *gemm_mx_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
+                                const void *A, int64_t lda,
+                                gemm_mx_format_t formatA,
+                                const uint8_t *scaleA, int64_t ldsa,
+                                const void *B, int64_t ldb,
+                                gemm_mx_format_t formatB,
+                                const uint8_t *scaleB, int64_t ldsb,
+                                float beta, const void *C, int64_t ldc,
+                                gemm_order_t orderC, gemm_output_t typeC,
+                                int64_t batch, int64_t strideA, int64_t strideB,
+                                int64_t strideScaleA, int64_t strideScaleB,
+                                int64_t strideC);
 
 /* The kernel gemm_f32_ws (in = GEMM_INPUT_F32; c_dtype is then ignored),
  * gemm_bf16_ws (GEMM_INPUT_BF16) or gemm_f16_ws (GEMM_INPUT_F16) would

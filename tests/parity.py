@@ -122,14 +122,16 @@ def ulp_keys(bits16: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
-def compare(p: workloads.Problem, got_bits: np.ndarray, ref: np.ndarray, den: np.ndarray,
-            name: str) -> Result:
-    """got_bits: output patterns at the compared elements; ref, den from the oracle."""
+def compare(p, got_bits: np.ndarray, ref: np.ndarray, den: np.ndarray, name: str) -> Result:
+    """got_bits: output patterns at the compared elements; ref, den from the oracle.
+    A block-scaled problem (workloads.MxProblem) runs on the 8-bit matrix
+    instruction and is held to its rule."""
     res = Result(name=name, checked=int(ref.size))
     out = p.c_dtype
+    narrow = isinstance(p, workloads.MxProblem) or p.in_dtype in workloads.EIGHT_BIT
     if out == "f32":
         got = got_bits.view(np.float32).astype(np.float64)
-        tol = TOL[(p.in_dtype, "f32")]
+        tol = F8_DOT if narrow else TOL[(p.in_dtype, "f32")]
         zero = den == 0
         if np.any(zero & (got != ref)):
             res.ok, res.why = False, "den == 0 but result differs from ref"
@@ -152,7 +154,7 @@ def compare(p: workloads.Problem, got_bits: np.ndarray, ref: np.ndarray, den: np
         got = oracle.decode(out, got_bits)
         qv = oracle.decode(out, ref_q)
         ulp = np.abs(oracle.decode(out, (ref_q.astype(np.int64) + 1).astype(np.uint16)) - qv)
-        if p.in_dtype in workloads.EIGHT_BIT:
+        if narrow:
             ok_exempt = np.abs(got - ref) <= 2 * ulp + F8_DOT * den
         else:
             ok_exempt = (np.abs(got - ref) <= 2 * ulp + 1e-3 * den) & \
@@ -293,6 +295,92 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
     got = out[sc + offsets(p, "c", bb, ii, jj)]
     res = compare(p, got, ref, den, p.name)
     res.kernel = kernel
+    log(f"[parity]   -> {kernel} ok={res.ok} max_err={res.max_err:.3e} max_ulp={res.max_ulp} "
+        f"strict_fail={res.strict_fail} exempt={res.exempt} checked={res.checked} {res.why}")
+    return res, out
+
+
+# Element patterns of small integers (magnitudes 0, 1, 2, 3, 4, 6) in each MX
+# element format, and the sign bit: products of two of them times scales of
+# 2^-1 .. 2^1 are multiples of 2^-2 below 2^8, exact in the 8-bit matrix
+# instruction's window and in fp32.
+MX_INT = {"e2m1": ({0: 0, 1: 2, 2: 4, 3: 5, 4: 6, 6: 7}, 8),
+          "e2m3": ({0: 0, 1: 8, 2: 16, 3: 20, 4: 24, 6: 28}, 32),
+          "e3m2": ({0: 0, 1: 12, 2: 16, 3: 18, 4: 20, 6: 22}, 32),
+          "e4m3": ({0: 0, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 6: 0x4C}, 128),
+          "e5m2": ({0: 0, 1: 0x3C, 2: 0x40, 3: 0x42, 4: 0x44, 6: 0x46}, 128)}
+
+
+def mx_int_patterns(rng, fmt, batch, rows, K):
+    table, sign = MX_INT[fmt]
+    mags = np.array(sorted(table))
+    v = rng.choice(mags, (batch, rows, K))
+    neg = rng.integers(0, 2, (batch, rows, K)).astype(bool)
+    lut = np.zeros(7, np.uint8)
+    for m, code in table.items():
+        lut[m] = code
+    return (lut[v] | np.where(neg, sign, 0)).astype(np.uint8)
+
+
+def run_mx(p: "workloads.MxProblem", *, seed=None, sample=None, repeat=1, patterns=None):
+    """Run a block-scaled problem through gemm_mx and compare with the oracle
+    (every element, or `sample` as in run()).  patterns: optional element
+    patterns for A and B (see workloads.generate_mx)."""
+    log(f"[parity] {p.name} mx {p.fa}x{p.fb}->{p.c_dtype} M={p.M} N={p.N} K={p.K} "
+        f"batch={p.batch} orderC={p.order_c} ld={p.lda},{p.ldb},{p.ldc} lds={p.ldsa},{p.ldsb} "
+        f"alpha={p.alpha} beta={p.beta}")
+    a, sa, b, sb, c0 = workloads.generate_mx(p, seed, patterns)
+    ins = [torch.from_numpy(x.view(np.int8)).to("cuda") if x.size else
+           torch.zeros(16, dtype=torch.int8, device="cuda") for x in (a, sa, b, sb)]
+    da, dsa, db, dsb = ins
+    dc, fc, sc = _device(c0, p.c_dtype)
+    esz_out = 4 if p.c_dtype == "f32" else 2
+    pc = dc.data_ptr() + sc * esz_out
+    out_t = {"f32": binding.OUTPUT_F32, "bf16": binding.OUTPUT_BF16, "f16": binding.OUTPUT_F16}
+    args = (p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, binding.MX_FORMAT[p.fa], dsa.data_ptr(),
+            p.ldsa, db.data_ptr(), p.ldb, binding.MX_FORMAT[p.fb], dsb.data_ptr(), p.ldsb, p.beta,
+            pc, p.ldc, p.order_c, out_t[p.c_dtype], p.batch, p.stride_a, p.stride_b, p.stride_sa,
+            p.stride_sb, p.stride_c)
+    kernel = binding.mx_kernel_name(*args)
+    cview = np.int32 if p.c_dtype == "f32" else np.int16
+    outs = []
+    for r in range(repeat):
+        if r:
+            dc.copy_(torch.from_numpy(fc.view(cview)))
+        binding.gemm_mx(*args)
+        torch.cuda.synchronize()
+        outs.append(dc.cpu().numpy().view(fc.dtype).copy())
+    out = outs[0]
+    res = Result(name=p.name, kernel=kernel or "")
+    if any(not np.array_equal(o, out) for o in outs[1:]):
+        res.ok, res.why = False, "repeated runs differ"
+        return res, out
+    for t, h in zip(ins, (a, sa, b, sb)):
+        if h.size and not np.array_equal(t.cpu().numpy().view(np.uint8), h):
+            res.ok, res.why = False, "an operand or a scale array was modified"
+            return res, out
+    outside = np.ones(out.size, bool)
+    outside[sc:sc + c0.size] = ~matrix_mask(p, "c", c0.size)
+    if not np.array_equal(out[outside], fc[outside]):
+        k = int(np.flatnonzero(outside & (out != fc))[0])
+        res.ok, res.why = False, f"write outside C at buffer element {k} (data starts at {sc})"
+        log(f"[parity]   -> FAIL {res.why}")
+        return res, out
+    okw = dict(stride_a=p.stride_a, stride_b=p.stride_b, stride_sa=p.stride_sa,
+               stride_sb=p.stride_sb, stride_c=p.stride_c)
+    oargs = (p.fa, p.fb, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda, sa, p.ldsa, b, p.ldb, sb,
+             p.ldsb, p.beta, c0, p.ldc, p.order_c)
+    if sample is None:
+        ref, den = oracle.mx_gemm(*oargs, batch=p.batch, **okw)
+        bb, ii, jj = np.meshgrid(np.arange(p.batch), np.arange(p.M), np.arange(p.N),
+                                 indexing="ij")
+    else:
+        idx = default_sample(p, np.random.default_rng(1234)) if isinstance(sample, str) else sample
+        ref, den = oracle.mx_gemm_at(*oargs, idx, **okw)
+        bb, ii, jj = idx[:, 0], idx[:, 1], idx[:, 2]
+    got = out[sc + offsets(p, "c", bb, ii, jj)]
+    res = compare(p, got, ref, den, p.name)
+    res.kernel = kernel or ""
     log(f"[parity]   -> {kernel} ok={res.ok} max_err={res.max_err:.3e} max_ulp={res.max_ulp} "
         f"strict_fail={res.strict_fail} exempt={res.exempt} checked={res.checked} {res.why}")
     return res, out

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                                     "gemm_f32_valu", "gemm_f32_ws",
                                     "gemm_f8",
                                     "gemm_f8_kernel_name", "gemm_kernel_name",
-                                    "gemm_kernel_name_ws", "gemm_status_string",
+                                    "gemm_kernel_name_ws", "gemm_mx", "gemm_mx_kernel_name",
+                                    "gemm_status_string",
                                     "gemm_test_switches", "gemm_workspace_size"]
 
 
@@ -129,6 +130,73 @@ def test_pointers_off_their_element_size(lib, fn):
     for off in range(1, esz):
         assert call(lib, fn, A=P + off) == lib.ERR_INVALID_ARG, off
         assert call(lib, fn, B=P * 3 + off) == lib.ERR_INVALID_ARG, off
+
+
+def mx_call(lib, M=300, N=260, K=256, alpha=1.0, A=P, lda=256, fa=4, SA=P * 2, ldsa=8, B=P * 3,
+            ldb=256, fb=4, SB=P * 4, ldsb=8, beta=0.0, C=P * 5, ldc=260, oc=0, tc=1, batch=1,
+            sa=0, sb=0, ssa=0, ssb=0, sc=0, name=False):
+    """gemm_mx (or, with name=True, gemm_mx_kernel_name) with fake addresses:
+    by default an MXFP4 300 x 260 x 256 problem, bf16 C."""
+    args = (M, N, K, alpha, A, lda, fa, SA, ldsa, B, ldb, fb, SB, ldsb, beta, C, ldc, oc, tc, batch,
+            sa, sb, ssa, ssb, sc)
+    if name:
+        return lib.mx_kernel_name(*args)
+    return lib.gemm_mx(*args, 0, raise_on_error=False)
+
+
+MX_INVALID = {
+    "K not a multiple of 64": dict(K=224),
+    "negative M": dict(M=-1),
+    "negative scale stride": dict(ssa=-4),
+    "format out of range": dict(fa=5),
+    "format negative": dict(fb=-1),
+    "typeC out of range": dict(tc=3),
+    "order C out of range": dict(oc=2),
+    "lda not a multiple of 64": dict(lda=288, K=256),
+    "ldb below K": dict(ldb=192),
+    "A not 16-byte aligned": dict(A=P + 8),
+    "B not 16-byte aligned": dict(B=P * 3 + 4),
+    "ldsa not a multiple of 4": dict(ldsa=10),
+    "ldsb below 4*ceil(K/128)": dict(ldsb=4, K=256),
+    "scale not 4-byte aligned": dict(SA=P * 2 + 2),
+    "scale stride not a multiple of 4": dict(batch=2, ssa=6, sa=300 * 256, sb=0, sc=300 * 260),
+    "A stride not a multiple of 64": dict(batch=2, sa=32, sc=300 * 260),
+    "null scale": dict(SB=0),
+    "null A": dict(A=0),
+    "C not element-aligned": dict(C=P * 5 + 1),
+    "ldc below N": dict(ldc=259),
+    "C slices overlap": dict(batch=2, sc=100),
+    "C overlaps a scale array": dict(C=P * 2 + 64),
+    "C overlaps A": dict(C=P + 64),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MX_INVALID))
+def test_mx_invalid_arguments(lib, case):
+    assert mx_call(lib, **MX_INVALID[case]) == lib.ERR_INVALID_ARG, case
+    assert mx_call(lib, name=True, **MX_INVALID[case]) is None, case
+
+
+def test_mx_kernel_choice_and_unsupported_pairs(lib):
+    assert mx_call(lib, name=True) == "mxgemm_mfma_dma"
+    for fa, fb in ((0, 0), (0, 1), (1, 0), (1, 1), (2, 2), (2, 3), (3, 2), (3, 3), (4, 4)):
+        assert mx_call(lib, name=True, fa=fa, fb=fb) == "mxgemm_mfma_dma", (fa, fb)
+    # formats of different widths share no stage layout
+    for fa, fb in ((0, 4), (4, 2), (2, 1)):
+        assert mx_call(lib, fa=fa, fb=fb) == lib.ERR_UNSUPPORTED, (fa, fb)
+    # column-major C, padded leading dimensions, K = 64 mod 128, batches
+    assert mx_call(lib, name=True, oc=1, ldc=300) == "mxgemm_mfma_dma"
+    assert mx_call(lib, name=True, K=320, lda=384, ldb=320, ldsa=12, ldsb=12) == "mxgemm_mfma_dma"
+    assert mx_call(lib, name=True, batch=3, sa=300 * 256, sb=0, ssa=300 * 8, ssb=0,
+                   sc=300 * 260) == "mxgemm_mfma_dma"
+    # alpha == 0 or K == 0: only beta * C, the operands and scales are not checked
+    assert mx_call(lib, name=True, alpha=0.0, A=0, SA=0) == "scale"
+    assert mx_call(lib, name=True, K=0, lda=64, ldsa=0, ldsb=0) == "scale"
+    assert mx_call(lib, name=True, M=0) == ""
+    # slices too large for 32-bit offsets
+    far = 1 << 40
+    assert mx_call(lib, M=70000, N=4, K=32768, lda=32768, ldb=32768, ldsa=1024, ldsb=1024, ldc=4,
+                   SA=far, B=2 * far, SB=3 * far, C=4 * far) == lib.ERR_UNSUPPORTED
 
 
 def test_f8_bad_formats_and_output_type(lib):
@@ -324,7 +392,16 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma",
             # called through gemm_f32_valu; gemm_kernel_name describes gemm_f32
             "f32_4096_valu": "sgemm_mfma_dma"}
-    assert sorted(want) == sorted(workloads.CONFIGS)
+    mx = {n for n, p in workloads.CONFIGS.items() if isinstance(p, workloads.MxProblem)}
+    assert mx == {"mxfp4_4096", "mxfp6_4096", "mxfp8_4096"}
+    assert sorted(want) == sorted(set(workloads.CONFIGS) - mx)
+    for name in mx:
+        p = workloads.config(name)
+        got = lib.mx_kernel_name(p.M, p.N, p.K, p.alpha, GB, p.lda, lib.MX_FORMAT[p.fa], 4 * GB,
+                                 p.ldsa, 2 * GB, p.ldb, lib.MX_FORMAT[p.fb], 5 * GB, p.ldsb, p.beta,
+                                 3 * GB, p.ldc, p.order_c, lib.OUTPUT_BF16, p.batch, p.stride_a,
+                                 p.stride_b, p.stride_sa, p.stride_sb, p.stride_c)
+        assert got == "mxgemm_mfma_dma", name
     for name, k in want.items():
         p = workloads.config(name)
         c_dt = 1 if (p.c_dtype == "f32" and p.in_dtype != "f32") else 0

@@ -983,3 +983,73 @@ def test_f32_dma_streamk_batches_col_major_c_and_integers():
     res, _ = check(p, kernel="sgemm_mfma_dma_streamk", host=_int_host(p, np.random.default_rng(117)),
                    use_workspace=True)
     assert res.max_err == 0.0
+
+
+# ------------------------------------------------------------------ block-scaled (MX) inputs
+
+from parity import mx_int_patterns, run_mx  # noqa: E402
+
+MX_PAIRS = [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e2m3", "e2m3"), ("e3m2", "e2m3"),
+            ("e2m1", "e2m1")]
+
+
+def check_mx(p, **kw):
+    res, out = run_mx(p, **kw)
+    assert res.ok, res.why
+    assert res.kernel == "mxgemm_mfma_dma", f"{p.name} ran on {res.kernel!r}"
+    return res, out
+
+
+@pytest.mark.parametrize("fa,fb", MX_PAIRS, ids=lambda f: f)
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(300, 260, 320), (64, 96, 64), (513, 257, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mx_formats_and_shapes(fa, fb, out, shape):
+    # K = 320 leaves a last stage of 64 k (its scale padding bytes are NaN
+    # patterns the kernel must not use); ragged M and N cut the edge tiles
+    M, N, K = shape
+    check_mx(workloads.MxProblem(f"mx-{fa}-{fb}", fa, fb, out, M, N, K, alpha=0.5, beta=1.0),
+             seed=M + K, repeat=2)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e3m2", "e3m2"), ("e2m1", "e2m1")],
+                         ids=lambda f: f)
+def test_mx_layouts_batches_and_col_major_c(fa, fb):
+    # padded leading dimensions of the operands and of the scales; fp16
+    # output where the elements stay small (8-bit elements with scales up to
+    # 2^4 reach past fp16's range)
+    out = "bf16" if workloads.MX_WIDTH[fa] == 8 else "f16"
+    check_mx(workloads.MxProblem("mx-ld", fa, fb, out, 260, 300, 256, lda=384, ldb=320, ldsa=16,
+                                 ldsb=12, beta=-0.5), seed=3)
+    # column-major C (computed as C^T = B^T A^T, operands and scales swapped)
+    check_mx(workloads.MxProblem("mx-colC", fa, fb, "bf16", 300, 200, 192, order_c=COL, ldc=303,
+                                 beta=2.0), seed=4)
+    # a batch with one shared B (and shared B scales), per-entry A scales
+    check_mx(workloads.MxProblem("mx-batch", fa, fb, "f32", 130, 140, 128, batch=3, stride_b=0,
+                                 stride_sb=0, beta=1.0), seed=5)
+
+
+@pytest.mark.parametrize("fa,fb", MX_PAIRS, ids=lambda f: f)
+def test_mx_integers_bit_exact(fa, fb):
+    # small integers with scales 2^-1 .. 2^1: every product and partial sum
+    # is exact, and so is alpha = 2 (beta = 0: a random C0 would add one
+    # fp32 rounding), so the fp32 result must equal the oracle bit for bit
+    M, N, K, batch = 200, 230, 384, 2
+    rng = np.random.default_rng(17)
+    pats = (mx_int_patterns(rng, fa, batch, M, K), mx_int_patterns(rng, fb, batch, N, K))
+    p = workloads.MxProblem("mx-int", fa, fb, "f32", M, N, K, alpha=2.0, beta=0.0, batch=batch,
+                            scale_lo=126, scale_hi=128)
+    res, _ = check_mx(p, seed=18, patterns=pats)
+    assert res.max_err == 0.0
+
+
+def test_mx_alpha_zero_and_k_zero_scale_c():
+    p = workloads.MxProblem("mx-alpha0", "e2m1", "e2m1", "bf16", 100, 70, 128, alpha=0.0,
+                            beta=0.5)
+    res, _ = run_mx(p, seed=6)
+    assert res.ok and res.kernel == "scale", res.why
+
+
+@pytest.mark.parametrize("name", ["mxfp4_4096", "mxfp6_4096", "mxfp8_4096"])
+def test_mx_full_size_sampled(name):
+    check_mx(workloads.config(name), sample="auto")

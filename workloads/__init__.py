@@ -20,6 +20,14 @@ listed here, so the reading taken is stated once, here):
   B may have different 8-bit types (``b_dtype``);
 * softmax rows (the attention probabilities): logits uniform(-1, 1), a
   row-wise softmax in float64, then rounded like any bf16 entry;
+* block-scaled (MX) problems (``MxProblem``): element bit patterns drawn
+  uniformly from the format's finite patterns (every pattern of the 6- and
+  4-bit formats; the 8-bit ones without their NaN and infinity patterns), in
+  row-major order of A (M x K) then of B^T (N x K), packed as the library's
+  little-endian bit stream with zero elements as padding; the E8M0 scales
+  uniform integers in [scale_lo, scale_hi] (2^-4 .. 2^4 by default) for the
+  ceil(K/32) blocks of each row, the row padding up to ldsa filled with the
+  NaN pattern 0xFF (never used); then C0 as for the other problems;
 * the bias of a problem with a fused epilogue comes from a second stream,
   ``np.random.default_rng([seed, 1])``, N entries per batch entry (one vector
   when ``stride_bias`` is 0), drawn like an entry of A with ``sigma_bias``.
@@ -219,6 +227,158 @@ def bias_vector(p: Problem, seed: Optional[int] = None):
     return out
 
 
+# ---------------------------------------------------------------- block-scaled (MX)
+
+MX_WIDTH = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
+
+
+@dataclass
+class MxProblem:
+    """A block-scaled GEMM C = alpha * A @ B + beta * C (gemm_mx).
+
+    A is M x K and B is K x N, both contiguous along K: row i of A is
+    elements b*stride_a + i*lda + (0 .. K-1) of A's packed stream, column j
+    of B elements b*stride_b + j*ldb + (0 .. K-1) of B's; E8M0 scales
+    SA[b*stride_sa + i*ldsa + k//32] and SB[b*stride_sb + j*ldsb + k//32]
+    (bytes).  C as in Problem (c_dtype, order_c, ldc, stride_c).
+    """
+    name: str
+    fa: str
+    fb: str
+    c_dtype: str
+    M: int
+    N: int
+    K: int
+    alpha: float = 1.0
+    beta: float = 0.0
+    order_c: int = ROW
+    lda: Optional[int] = None
+    ldb: Optional[int] = None
+    ldc: Optional[int] = None
+    ldsa: Optional[int] = None
+    ldsb: Optional[int] = None
+    batch: int = 1
+    stride_a: Optional[int] = None
+    stride_b: Optional[int] = None
+    stride_sa: Optional[int] = None
+    stride_sb: Optional[int] = None
+    stride_c: Optional[int] = None
+    scale_lo: int = 123
+    scale_hi: int = 131
+    sigma_c: float = 1.0
+    seed: int = 0
+    note: str = ""
+
+    def __post_init__(self):
+        M, N, K = self.M, self.N, self.K
+        k64 = max(64, -(-K // 64) * 64)
+        sbytes = max(4, 4 * -(-K // 128))
+        self.lda = k64 if self.lda is None else self.lda
+        self.ldb = k64 if self.ldb is None else self.ldb
+        self.ldsa = sbytes if self.ldsa is None else self.ldsa
+        self.ldsb = sbytes if self.ldsb is None else self.ldsb
+        if self.ldc is None:
+            self.ldc = max(1, N if self.order_c == ROW else M)
+        if self.stride_a is None:
+            self.stride_a = M * self.lda
+        if self.stride_b is None:
+            self.stride_b = N * self.ldb
+        if self.stride_sa is None:
+            self.stride_sa = M * self.ldsa
+        if self.stride_sb is None:
+            self.stride_sb = N * self.ldsb
+        if self.stride_c is None:
+            outer, inner = (M, N) if self.order_c == ROW else (N, M)
+            self.stride_c = (outer - 1) * self.ldc + inner if M and N else 0
+
+    # C as a Problem sees it (for the parity harness's C handling)
+    def dims(self, which):
+        assert which == "c"
+        return (self.M, self.N, self.order_c, self.ldc)
+
+    def buffer_elems(self, which) -> int:
+        assert which == "c"
+        if self.batch == 0 or self.stride_c == 0 and self.M * self.N == 0:
+            return 0
+        outer, inner = (self.M, self.N) if self.order_c == ROW else (self.N, self.M)
+        return (self.batch - 1) * self.stride_c + (outer - 1) * self.ldc + inner
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K * self.batch
+
+    def with_(self, **kw) -> "MxProblem":
+        return replace(self, **kw)
+
+
+def finite_patterns(fmt: str) -> np.ndarray:
+    """Bit patterns of a format's finite values."""
+    n = 1 << MX_WIDTH[fmt]
+    p = np.arange(n, dtype=np.uint16)
+    if fmt == "e4m3":
+        p = p[(p & 0x7F) != 0x7F]
+    elif fmt == "e5m2":
+        p = p[(p & 0x7C) != 0x7C]
+    return p.astype(np.uint8)
+
+
+def mx_pack(patterns: np.ndarray, width: int) -> np.ndarray:
+    """Pack a rows x cols array of element patterns (cols * width a multiple
+    of 8) row by row into the little-endian bit stream: rows x cols*width/8."""
+    p = np.ascontiguousarray(patterns, dtype=np.uint32)
+    rows, cols = p.shape
+    if width == 8:
+        return p.astype(np.uint8)
+    if width == 4:
+        return (p[:, 0::2] | (p[:, 1::2] << 4)).astype(np.uint8)
+    assert width == 6 and cols % 4 == 0
+    w = p[:, 0::4] | (p[:, 1::4] << 6) | (p[:, 2::4] << 12) | (p[:, 3::4] << 18)
+    out = np.empty((rows, cols // 4, 3), np.uint8)
+    out[:, :, 0] = w & 0xFF
+    out[:, :, 1] = (w >> 8) & 0xFF
+    out[:, :, 2] = (w >> 16) & 0xFF
+    return out.reshape(rows, cols * 3 // 4)
+
+
+def generate_mx(p: MxProblem, seed: Optional[int] = None, patterns=None):
+    """Host buffers (flat uint8 arrays) A, SA, B, SB and the initial C.
+
+    patterns: optional (A, B) pattern arrays of shape (batch, M, K) and
+    (batch, N, K) used instead of random ones (scales are still drawn).
+    """
+    rng = np.random.default_rng(p.seed if seed is None else seed)
+    nblk = -(-p.K // 32)
+    out = {}
+    for which, fmt, rows, ld, stride, lds, sstride in (
+            ("a", p.fa, p.M, p.lda, p.stride_a, p.ldsa, p.stride_sa),
+            ("b", p.fb, p.N, p.ldb, p.stride_b, p.ldsb, p.stride_sb)):
+        w = MX_WIDTH[fmt]
+        nb = 1 if stride == 0 else p.batch
+        total = ((p.batch - 1) * stride + rows * ld) if p.batch and rows else 0
+        data = np.zeros(total * w // 8, np.uint8)
+        ns = ((p.batch - 1) * sstride + rows * lds) if p.batch and rows else 0
+        scales = np.full(ns, 0xFF, np.uint8)
+        fin = finite_patterns(fmt)
+        for b in range(nb):
+            if patterns is not None:
+                pat = np.asarray(patterns[0 if which == "a" else 1][b], np.uint8)
+            else:
+                pat = fin[rng.integers(0, fin.size, (rows, p.K))]
+            full = np.zeros((rows, ld), np.uint8)
+            full[:, :p.K] = pat
+            packed = mx_pack(full, w).ravel()
+            data[b * stride * w // 8:b * stride * w // 8 + packed.size] = packed
+        for b in range(1 if sstride == 0 else p.batch):
+            sc = rng.integers(p.scale_lo, p.scale_hi + 1, (rows, nblk)).astype(np.uint8)
+            view = scales[b * sstride:b * sstride + rows * lds].reshape(rows, lds)
+            view[:, :nblk] = sc
+        out[which], out["s" + which] = data, scales
+    c = np.zeros(p.buffer_elems("c"), storage(p.c_dtype))
+    for b in range(p.batch):
+        _store(_draw(rng, p.c_dtype, p.M, p.N, p.sigma_c), p.order_c, p.ldc, p.stride_c, b, c)
+    return out["a"], out["sa"], out["b"], out["sb"], c
+
+
 def _configs():
     cfgs = [
         Problem("f32_256", "f32", "f32", 256, 256, 256,
@@ -260,6 +420,14 @@ def _configs():
                 note="FFN up X(4096x4096) W1(4096x16384) + b1 then GELU, fused epilogue"),
         # 8-bit float inputs in the layout 8-bit GEMMs take: A row-major and B
         # column-major (both contiguous along K), output bf16
+        # block-scaled formats (one E8M0 scale per 32 k), K contiguous in
+        # both operands as the format requires
+        MxProblem("mxfp4_4096", "e2m1", "e2m1", "bf16", 4096, 4096, 4096,
+                  note="MXFP4 4096^3 (E2M1 elements, E8M0 scale per 32 k), bf16 out"),
+        MxProblem("mxfp6_4096", "e2m3", "e2m3", "bf16", 4096, 4096, 4096,
+                  note="MXFP6 4096^3 (E2M3 elements, E8M0 scale per 32 k), bf16 out"),
+        MxProblem("mxfp8_4096", "e4m3", "e4m3", "bf16", 4096, 4096, 4096,
+                  note="MXFP8 4096^3 (E4M3 elements, E8M0 scale per 32 k), bf16 out"),
         Problem("fp8_4096", "e4m3", "bf16", 4096, 4096, 4096, order_b=COL,
                 note="E4M3 GEMM 4096^3, A row-major, B column-major, fp32 accumulate, bf16 out"),
     ]
@@ -269,5 +437,7 @@ def _configs():
 CONFIGS = _configs()
 
 
-def config(name: str) -> Problem:
+def config(name: str):
+    """The workload of that name (a Problem, or an MxProblem for the
+    block-scaled ones)."""
     return CONFIGS[name]
