@@ -48,8 +48,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X dense peaks, published (8-bit floats: twice the 16-bit rate)
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2}
+# MI355X dense peaks, published (8-bit floats: twice the 16-bit rate; the
+# block-scaled 6- and 4-bit formats twice the 8-bit one)
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2,
+               "mxfp8": 5033.2, "mxfp6": 10066.3, "mxfp4": 10066.3}
 ESIZE = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1, "e5m2": 1}
 VIEW = {"f32": np.float32, "bf16": np.int16, "f16": np.int16, "e4m3": np.int8, "e5m2": np.int8}
 HBM_GBS = 8000.0
@@ -69,6 +71,7 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "sgemm_mfma_dma_packed": "sgemm_mfma.hip",
                  "sgemm_mfma_dma_streamk": "sgemm_mfma.hip",
                  "sgemm_mfma_dma_streamk_packed": "sgemm_mfma.hip",
+                 "mxgemm_mfma_dma": "mxgemm.hip",
                  "scale": "scale.hip"}
 
 
@@ -76,8 +79,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def is_mx(p):
+    import workloads
+    return isinstance(p, workloads.MxProblem)
+
+
+def dtype_key(p):
+    """The key of PEAK_TFLOPS for a workload: its input type, or mxfp8/6/4."""
+    import workloads
+    return f"mxfp{workloads.MX_WIDTH[p.fa]}" if is_mx(p) else p.in_dtype
+
+
+def algorithmic_bytes(p):
+    """Bytes a launch must move at least: A and B once (with their scales),
+    C written once and, when beta != 0, read once."""
+    import workloads
+    c = p.M * p.N * ESIZE[p.c_dtype] * p.batch * (2 if p.beta else 1)
+    if is_mx(p):
+        wa, wb = workloads.MX_WIDTH[p.fa], workloads.MX_WIDTH[p.fb]
+        return (p.M * p.K * wa // 8 + p.N * p.K * wb // 8 + (p.M + p.N) * (p.K // 32)) * p.batch + c
+    return (p.M * p.K * ESIZE[p.in_dtype] + p.K * p.N * ESIZE[p.b_dtype]) * p.batch + c
+
+
 def device_buffers(p, torch):
     import workloads
+    if is_mx(p):
+        a, sa, b, sb, c = workloads.generate_mx(p)
+        return tuple(torch.from_numpy(x.view(np.int8)).to("cuda") for x in (a, sa, b, sb)) + \
+            (torch.from_numpy(c.view(VIEW[p.c_dtype])).to("cuda"),)
     a, b, c = workloads.generate(p)
     return (torch.from_numpy(a.view(VIEW[p.in_dtype])).to("cuda"),
             torch.from_numpy(b.view(VIEW[p.b_dtype])).to("cuda"),
@@ -117,6 +146,8 @@ def make_launch(p, sets, stream, bias=None, workspace=None):
     workload's fused bias and activation, if it has them; through the
     workspace entry point when a workspace tensor is given)."""
     from dense_gemm_optimisation_amd import binding
+    if is_mx(p):
+        return make_mx_launch(p, sets, stream)
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     argsets = [(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a, db.data_ptr(),
                 p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch,
@@ -134,11 +165,36 @@ def make_launch(p, sets, stream, bias=None, workspace=None):
     return launch
 
 
+def mx_args(p, bufs, stream=0):
+    from dense_gemm_optimisation_amd import binding
+    da, dsa, db, dsb, dc = bufs
+    out = {"f32": binding.OUTPUT_F32, "bf16": binding.OUTPUT_BF16, "f16": binding.OUTPUT_F16}
+    return (p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, binding.MX_FORMAT[p.fa], dsa.data_ptr(),
+            p.ldsa, db.data_ptr(), p.ldb, binding.MX_FORMAT[p.fb], dsb.data_ptr(), p.ldsb, p.beta,
+            dc.data_ptr(), p.ldc, p.order_c, out[p.c_dtype], p.batch, p.stride_a, p.stride_b,
+            p.stride_sa, p.stride_sb, p.stride_c)
+
+
+def make_mx_launch(p, sets, stream):
+    """make_launch for a block-scaled workload (gemm_mx)."""
+    from dense_gemm_optimisation_amd import binding
+    argsets = [mx_args(p, bufs) for bufs in sets]
+    turn = [0]
+
+    def launch():
+        binding.gemm_mx(*argsets[turn[0]], stream=stream.cuda_stream)
+        turn[0] = (turn[0] + 1) % len(argsets)
+    launch.turn = lambda: turn[0]
+    return launch
+
+
 def kernel_family(p, bufs, workspace=None):
     """The kernel libgemm launches for workload p on these device buffers
     (asked of the library itself, so the answer follows its dispatch rules
     and the buffers' actual alignment)."""
     from dense_gemm_optimisation_amd import binding
+    if is_mx(p):
+        return binding.mx_kernel_name(*mx_args(p, bufs))
     if p.entry == "valu":
         return "sgemm_valu"
     da, db, dc = bufs
@@ -234,7 +290,7 @@ def error_stats(p, got_bits, ref, den):
         qv = oracle.decode(p.c_dtype, q.astype(np.uint16))
         ulp = np.abs(oracle.decode(p.c_dtype, (q + 1).astype(np.uint16)) - qv)
         near = np.abs(gv - ref) <= 2 * ulp + 1e-3 * den
-        if p.in_dtype not in ("e4m3", "e5m2"):
+        if not is_mx(p) and p.in_dtype not in ("e4m3", "e5m2"):
             near &= np.abs(ref) <= 2.0 ** -8 * den
         bad = d > 2
         norm = np.where(den > 0, np.abs(gv - ref) / np.where(den > 0, den, 1.0), 0.0)
@@ -254,7 +310,10 @@ def cpu_baseline(problems, budget_s, gpu_results):
     total_flop, total_t, parts, per, errs = 0.0, 0.0, [], {}, {}
     share = budget_s / max(1, len(problems))
     for p in problems:
-        a, b, c = workloads.generate(p)
+        if is_mx(p):
+            a, sa, b, sb, c = workloads.generate_mx(p)
+        else:
+            a, b, c = workloads.generate(p)
         # rows [0, r) of C for the first batch entry: a sub-problem with
         # M = r when A is row-major (rows contiguous), else listed elements
         r = p.M
@@ -262,7 +321,11 @@ def cpu_baseline(problems, budget_s, gpu_results):
         if est > share:
             r = max(1, int(p.M * share / est))
         t0 = time.perf_counter()
-        if p.order_a == workloads.ROW and p.order_c == workloads.ROW:
+        if is_mx(p):  # A rows are contiguous; C row-major in every MX workload
+            ref, den = oracle.mx_gemm(p.fa, p.fb, p.c_dtype, r, p.N, p.K, p.alpha, a, p.lda, sa,
+                                      p.ldsa, b, p.ldb, sb, p.ldsb, p.beta, c, p.ldc, p.order_c)
+            ref, den = ref[0].ravel(), den[0].ravel()
+        elif p.order_a == workloads.ROW and p.order_c == workloads.ROW:
             ref, den = oracle.gemm(p.in_dtype, p.c_dtype, r, p.N, p.K, p.alpha, a, p.lda,
                                    p.order_a, b, p.ldb, p.order_b, p.beta, c, p.ldc, p.order_c,
                                    stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
@@ -414,10 +477,10 @@ def main():
             bufs = device_buffers(p, torch)
             sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
             nsets[p.name] = len(sets)
-            pws = ws if (ws is not None and p.in_dtype in ("f32", "bf16", "f16") and not p.bias
-                         and not p.act and not p.entry) else None
+            pws = ws if (ws is not None and not is_mx(p) and p.in_dtype in ("f32", "bf16", "f16")
+                         and not p.bias and not p.act and not p.entry) else None
             families[p.name] = kernel_family(p, bufs, pws)
-            bias = device_bias(p, torch)
+            bias = None if is_mx(p) else device_bias(p, torch)
             launches.append((p, sets, make_launch(p, sets, stream, bias, pws)))
     torch.cuda.synchronize()
 
@@ -467,20 +530,20 @@ def main():
         ms = ev[k][0].elapsed_time(ev[k][1]) / args.steps
         tfl = p.flops / (ms * 1e-3) / 1e12
         flops_step += p.flops
-        alg_bytes = (p.M * p.K * ESIZE[p.in_dtype] + p.K * p.N * ESIZE[p.b_dtype]) * p.batch + \
-            p.M * p.N * ESIZE[p.c_dtype] * p.batch * (2 if p.beta else 1)
+        alg_bytes = algorithmic_bytes(p)
+        key = dtype_key(p)
         t1 = one_by_one[p.name]
         med, mn = t1[len(t1) // 2], t1[0]
         per_kernel[p.name] = {
             "kernel": families[p.name],
-            "dtype": p.in_dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+            "dtype": key, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
             "mean_us": round(ms * 1e3, 2), "tflops": round(tfl, 2),
-            "frac_of_peak": round(tfl / PEAK_TFLOPS[p.in_dtype], 4),
+            "frac_of_peak": round(tfl / PEAK_TFLOPS[key], 4),
             "alg_gbs": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
             "alg_frac_of_hbm": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_GBS, 4),
             "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
             "tflops_median": round(p.flops / (med * 1e-3) / 1e12, 2),
-            "frac_of_peak_median": round(p.flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS[p.in_dtype], 4),
+            "frac_of_peak_median": round(p.flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS[key], 4),
             "tflops_best": round(p.flops / (mn * 1e-3) / 1e12, 2)}
     ms_step = wall / args.steps * 1e3
     value = flops_step / (wall / args.steps) / 1e12
@@ -493,7 +556,7 @@ def main():
         # units; every other kernel by the matrix cores' rate for its dtype
         # (MI355X publishes the same 157.3 TF/s for both fp32 units)
         bound = "alu" if fam == "sgemm_valu" else "mfma"
-        peak = PEAK_TFLOPS[p.in_dtype]
+        peak = PEAK_TFLOPS[dtype_key(p)]
         return {"kernel": f"{fam} {name}", "bound": bound, "achieved": k["tflops"],
                 "peak": peak, "unit": "TFLOP/s", "frac": round(k["tflops"] / peak, 4),
                 "traffic": measured_traffic(fam, name)}
@@ -503,7 +566,7 @@ def main():
         "metric": "TFLOPS (2MNK/t) at 4096^3 fp32 and bf16; % of MI355X dense peak per dtype",
         "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "+".join(p.in_dtype for p in problems),
+        "scaling": "weak", "vs_baseline": None, "dtype": "+".join(dtype_key(p) for p in problems),
         "data": "synthetic",
         "config": {"workload": " + ".join(f"{p.name} ({p.note})" for p in problems),
                    "global_batch": 1, "parallelism": "none (1 GPU)",
@@ -532,8 +595,8 @@ def single_results(launches, torch):
     import workloads
     res = {}
     for p, sets, fn in launches:
-        _, _, c0 = workloads.generate(p)
-        dc = sets[0][2]
+        c0 = workloads.generate_mx(p)[4] if is_mx(p) else workloads.generate(p)[2]
+        dc = sets[0][-1]
         dc.copy_(torch.from_numpy(c0.view(VIEW[p.c_dtype])).to(dc.device))
         torch.cuda.synchronize()
         # the launcher cycles through the buffer sets: run until set 0 comes round
@@ -554,7 +617,7 @@ def torch_context(problems, stream, torch):
           "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
     with torch.cuda.stream(stream):
         for p in problems:
-            if p.batch != 1:
+            if p.batch != 1 or is_mx(p):
                 continue
             a = torch.randn(p.M, p.K, device="cuda").to(dt[p.in_dtype])
             b = torch.randn(p.K, p.N, device="cuda").to(dt[p.b_dtype])
