@@ -317,7 +317,7 @@ def cpu_baseline(problems, budget_s, gpu_results):
         # rows [0, r) of C for the first batch entry: a sub-problem with
         # M = r when A is row-major (rows contiguous), else listed elements
         r = p.M
-        est = 2.0 * p.M * p.N * p.K / 10e9  # ~10 GFLOP/s with all threads
+        est = 2.0 * p.M * p.N * p.K / 50e9  # ~50-65 GFLOP/s with 16 threads
         if est > share:
             r = max(1, int(p.M * share / est))
         t0 = time.perf_counter()
