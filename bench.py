@@ -72,6 +72,7 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "sgemm_mfma_dma_streamk": "sgemm_mfma.hip",
                  "sgemm_mfma_dma_streamk_packed": "sgemm_mfma.hip",
                  "mxgemm_mfma_dma": "mxgemm.hip",
+                 "gemm_skinny_splitk": "gemm_skinny.hip",
                  "scale": "scale.hip"}
 
 
@@ -215,6 +216,8 @@ def source_hash(family):
     import re
     csrc = os.path.join(ROOT, "dense_gemm_optimisation_amd", "csrc")
     h = hashlib.sha256()
+    if family not in KERNEL_SOURCE:
+        return None
     todo, seen = [KERNEL_SOURCE[family]], set()
     while todo:
         name = todo.pop(0)
@@ -235,6 +238,8 @@ def measured_traffic(family, workload):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     want = source_hash(family)
+    if want is None:
+        return None
     for ln in open(TRAFFIC_FILE):
         f = ln.split()
         # family  source-sha  workload  fetch_bytes  write_bytes  (scaled, per launch)
@@ -552,14 +557,21 @@ def main():
         k = per_kernel[name]
         p = workloads.config(name)
         fam = families[name]
-        # the vector-ALU fp32 kernel is bound by the FMA rate of the vector
-        # units; every other kernel by the matrix cores' rate for its dtype
-        # (MI355X publishes the same 157.3 TF/s for both fp32 units)
-        bound = "alu" if fam == "sgemm_valu" else "mfma"
         peak = PEAK_TFLOPS[dtype_key(p)]
+        traffic = measured_traffic(fam, name)
+        # below the ridge point (peak flop rate / HBM bandwidth) the problem
+        # is bound by HBM: its algorithmic bytes against 8 TB/s; above it by
+        # the matrix cores' rate for its dtype, or for the vector-ALU fp32
+        # kernel by the vector units' FMA rate (MI355X publishes the same
+        # 157.3 TF/s for both fp32 units)
+        if p.flops / algorithmic_bytes(p) < peak * 1e12 / (HBM_GBS * 1e9):
+            return {"kernel": f"{fam} {name}", "bound": "hbm", "achieved": k["alg_gbs"],
+                    "peak": HBM_GBS, "unit": "GB/s", "frac": round(k["alg_gbs"] / HBM_GBS, 4),
+                    "traffic": traffic}
+        bound = "alu" if fam == "sgemm_valu" else "mfma"
         return {"kernel": f"{fam} {name}", "bound": bound, "achieved": k["tflops"],
                 "peak": peak, "unit": "TFLOP/s", "frac": round(k["tflops"] / peak, 4),
-                "traffic": measured_traffic(fam, name)}
+                "traffic": traffic}
 
     dominant = max(per_kernel, key=lambda n: per_kernel[n]["mean_us"])
     out = {

@@ -75,6 +75,7 @@ enum class Kernel {
     SgemmPackDma,         // then the fp32 direct-load kernel
     SgemmPackDmaStreamK,  // then its stream-K schedule
     Mx,                   // block-scaled narrow floats (gemm_mx), direct loads
+    SkinnySplitK,         // at most 16 rows, N-contiguous B: split-K across workgroups (workspace)
 };
 
 bool is_packed(Kernel k) {
@@ -105,6 +106,7 @@ const char *kernel_name(Kernel k) {
     case Kernel::SgemmPackDma: return "sgemm_mfma_dma_packed";
     case Kernel::SgemmPackDmaStreamK: return "sgemm_mfma_dma_streamk_packed";
     case Kernel::Mx: return "mxgemm_mfma_dma";
+    case Kernel::SkinnySplitK: return "gemm_skinny_splitk";
     }
     return "";
 }
@@ -153,6 +155,7 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::SgemmPackDma:
     case Kernel::SgemmPackDmaStreamK: return hipErrorInvalidValue;  // need the workspace: run()
     case Kernel::Mx: return hipErrorInvalidValue;  // needs the scales: gemm_mx
+    case Kernel::SkinnySplitK: return hipErrorInvalidValue;  // needs the workspace: run()
     }
     return hipErrorInvalidValue;
 }
@@ -411,6 +414,10 @@ void plan_workspace(const Problem &p, const void *workspace, size_t bytes, WsPla
     } else if (k == Kernel::SgemmDma && sgemm_dma_streamk_eligible(p, force)) {
         k = Kernel::SgemmDmaStreamK;
         w.used = sgemm_streamk_bytes(p);
+    } else if (k == Kernel::Skinny && skinny_sk_eligible(p) &&
+               skinny_sk_bytes(p) <= static_cast<int64_t>(bytes)) {
+        k = Kernel::SkinnySplitK;
+        w.used = skinny_sk_bytes(p);
     }
 }
 
@@ -441,6 +448,7 @@ hipError_t launch_planned(const WsPlan &w, void *workspace, hipStream_t stream) 
     case Kernel::SgemmStreamK: return launch_sgemm_streamk(w.q, workspace, stream);
     case Kernel::SgemmDmaStreamK:
     case Kernel::SgemmPackDmaStreamK: return launch_sgemm_dma_streamk(w.q, workspace, stream);
+    case Kernel::SkinnySplitK: return launch_skinny_sk(w.q, workspace, stream);
     case Kernel::HgemmPackDma: return launch_hgemm_dma(w.q, stream);
     case Kernel::SgemmPackDma: return launch_sgemm_dma(w.q, stream);
     default: return launch(w.k, w.q, stream);

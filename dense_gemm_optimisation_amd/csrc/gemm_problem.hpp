@@ -146,6 +146,12 @@ hipError_t launch_hgemm_splitk(const Problem &p, hipStream_t stream);
 // inside a workgroup (skinny_eligible()).
 bool skinny_eligible(const Problem &p);
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
+// The same problems with an N-contiguous 16-bit B, split over K across
+// workgroups through a workspace of skinny_sk_bytes(p) (partial blocks), then
+// reduced in fixed order by a second kernel (skinny_sk_eligible()).
+bool skinny_sk_eligible(const Problem &p);
+int64_t skinny_sk_bytes(const Problem &p);
+hipError_t launch_skinny_sk(const Problem &p, void *workspace, hipStream_t stream);
 // 8-bit floats (E4M3/E5M2) on the scaled 8-bit matrix instructions: the
 // direct-load kernel for K-contiguous aligned operands (f8gemm_dma_eligible())
 // and a general kernel for any order, alignment and shape.

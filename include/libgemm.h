@@ -340,6 +340,14 @@ gemm_status_t gemm_mx(int64_t M, int64_t N, int64_t K, float alpha,
  * N and C.  The zero padding adds nothing to any result.  This is chosen
  * whenever the copies and any partial tiles fit the workspace; otherwise the
  * general kernel runs on the caller's operands as described above.
+ * A 16-bit problem of at most 16 rows of C (of K-contiguous A) with an
+ * N-contiguous B, N >= 256 and K >= 1024 is split along K across
+ * workgroups ("GPU GEMM 优化完全拆解（三）", pinghaoyang.com.cn, the
+ * rasterization and split-K section): each workgroup multiplies 128 columns
+ * of B over one slice of K (about 512 workgroups in all) and writes fp32
+ * partial sums, split * batch * M * ceil(N / 128) * 128 * 4 bytes of the
+ * workspace; a second kernel on the same stream adds each element's slices
+ * in one fixed order and applies the epilogue.
  * Results are deterministic run to run; they may differ in rounding from
  * gemm_bf16 (the partial sums are grouped differently), within the same
  * accuracy.  Every other call ignores the workspace and behaves exactly like
@@ -514,7 +522,7 @@ const char *gemm_mx_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
  * for the stream-K schedules, "hgemm_mfma_dma_packed",
  * "hgemm_mfma_dma_streamk_packed", "sgemm_mfma_dma_packed" or
  * "sgemm_mfma_dma_streamk_packed" when the operands are first copied into
- * the workspace; "" and NULL as for gemm_kernel_name, whose testing switches
+ * the workspace, "gemm_skinny_splitk" for the skinny split-K; "" and NULL as for gemm_kernel_name, whose testing switches
  * apply, GEMM_TEST_FORCE_STREAMK included.  The workspace is only
  * checked, never dereferenced. */
 const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K,

@@ -495,6 +495,17 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "f32", 2048, 2176, 1000, oa=1, ob=1) == "sgemm_mfma_dma_streamk"
     assert kname_ws(lib, "f32", 4096, 4224, 64) == "sgemm_mfma_dma"         # 4 steps per tile
     assert kname_ws(lib, "f32", 4095, 4097, 1001, nbytes=1 << 20) == "sgemm_mfma"
+    # at most 16 rows of C with a row-major (N-contiguous) 16-bit B: split-K
+    # across workgroups with a fixed-order reduction; a K-contiguous B keeps
+    # the skinny kernel (whole lines already), and so do short K or narrow N
+    assert kname_ws(lib, "bf16", 16, 4096, 4096) == "gemm_skinny_splitk"
+    assert kname_ws(lib, "f16", 1, 4096, 4096) == "gemm_skinny_splitk"
+    assert kname_ws(lib, "bf16", 7, 1000, 2048, batch=3) == "gemm_skinny_splitk"
+    assert kname_ws(lib, "bf16", 16, 4096, 4096, ob=1) == "gemm_skinny"
+    assert kname_ws(lib, "bf16", 16, 4096, 512) == "gemm_skinny"
+    assert kname_ws(lib, "bf16", 16, 200, 4096) == "gemm_skinny"
+    assert kname_ws(lib, "bf16", 16, 4096, 4096, ws=0, nbytes=0) == "gemm_skinny"
+    assert kname_ws(lib, "f32", 16, 4096, 4096) == "sgemm_splitk"
     # K = 0 scales C
     assert kname_ws(lib, "bf16", 4095, 4097, 0, lda=1) == "scale"
     clean_env(lib.TEST_FORCE_GENERAL)

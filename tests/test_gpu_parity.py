@@ -1053,3 +1053,38 @@ def test_mx_alpha_zero_and_k_zero_scale_c():
 @pytest.mark.parametrize("name", ["mxfp4_4096", "mxfp6_4096", "mxfp8_4096"])
 def test_mx_full_size_sampled(name):
     check_mx(workloads.config(name), sample="auto")
+
+
+# ------------------------------------------------------------------ skinny split-K across workgroups (workspace)
+
+# (5, 8192, 4008): slices of four 128-row rounds, the last slice ending in a
+# partial round whose last instruction step is itself partial
+SKINNY_SK_SHAPES = [(16, 4096, 4096), (1, 1024, 3000), (7, 1000, 2048), (12, 520, 1024), (5, 8192, 4008)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", SKINNY_SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_splitk(dt, shape):
+    # 128-column blocks of a row-major B split over K across workgroups, the
+    # slices added in fixed order by a second kernel: run twice, bit for bit
+    M, N, K = shape
+    check(P(f"skinny-sk-{dt}", dt, M, N, K, alpha=0.5, beta=1.5), kernel="gemm_skinny_splitk",
+          seed=M + N + K, use_workspace=True, repeat=2)
+
+
+def test_skinny_splitk_fp32_output_batches_and_integers():
+    check(P("skinny-sk-f32out", "bf16", 16, 2048, 4096, c_dtype="f32", beta=-1.0),
+          kernel="gemm_skinny_splitk", seed=31, use_workspace=True)
+    check(P("skinny-sk-batch", "f16", 9, 1536, 2048, batch=3, beta=0.5),
+          kernel="gemm_skinny_splitk", seed=32, use_workspace=True)
+    check(P("skinny-sk-shared-b", "bf16", 16, 1024, 2048, batch=2, stride_b=0),
+          kernel="gemm_skinny_splitk", seed=33, use_workspace=True)
+    p = P("skinny-sk-int", "bf16", 16, 4096, 4096, c_dtype="f32", alpha=2.0, beta=1.0)
+    res, _ = check(p, kernel="gemm_skinny_splitk", host=_int_host(p, np.random.default_rng(34)),
+                   use_workspace=True)
+    assert res.max_err == 0.0
+
+
+def test_skinny_splitk_workload_full_size():
+    check(workloads.config("bf16_skinny"), kernel="gemm_skinny_splitk", use_workspace=True,
+          repeat=2)
