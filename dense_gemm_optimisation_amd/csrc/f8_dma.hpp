@@ -147,17 +147,7 @@ __device__ inline void pin(const f32x16 &x) {
     if (!AGPR) asm volatile("" ::"v"(x));
 }
 
-// buffer_load_dword ... lds: 4 bytes per lane from the buffer `rs` at byte
-// offset `voffset` into LDS at `lds` + 4 * lane (the same contract as
-// dma::direct_load16).
-__device__ inline void direct_load4(u32x4 rs, uint32_t lds, uint32_t voffset) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dword %1, %2, 0 offen lds"
-        :
-        : "s"(lds), "v"(voffset), "s"(rs)
-        : "memory", "m0");
-}
+using dma::direct_load4;
 
 #ifndef LIBGEMM_F8_WM
 #define LIBGEMM_F8_WM 2

@@ -86,8 +86,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
     // The wave index is uniform across the wave; saying so keeps the LDS
     // destination of the direct loads (M0) in a scalar register.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    // Waves are dealt to the four SIMDs in turn, so consecutive waves share
+    // a column block: the waves of one block column then sit on different
+    // SIMDs, and when a tile hangs over the right edge of C (N = 128 in a
+    // 256-wide tile, or one column of a last tile column) the waves left
+    // with work are spread over all four matrix units.
+    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
     const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    // A wave whose WTM x WTN block lies wholly outside C only loads its share
+    // of the panels and keeps the barriers.
+    const bool live = m0 + wm * WTM < p.M && n0 + wn * WTN < p.N;
 
     OpA opa;
     OpB opb;
@@ -115,6 +123,24 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
     }
     wait_stages<PER_STAGE, STAGES>(int(steps - 1 < STAGES - 1 ? steps - 1 : STAGES - 1));
     __syncthreads();
+
+    const int64_t main_steps = steps - 1;
+    if (!live) {
+        // the refills and barriers of the loop below, nothing else
+        int b = 0;
+        for (int64_t s = 0; s < main_steps; ++s) {
+            const int64_t later = steps - 2 - s;
+            wait_stages<PER_STAGE, STAGES>(int(later < STAGES - 2 ? later : STAGES - 2));
+            __syncthreads();
+            const int64_t refill = s + STAGES;
+            if (refill < steps) {
+                opa.issue(lds + b * STAGE, refill, p.K, wave);
+                opb.issue(lds + b * STAGE + PANEL, refill, p.K, wave);
+            }
+            b = b + 1 == STAGES ? 0 : b + 1;
+        }
+        return;
+    }
 
     u32x4 fa[2][FM], fb[2][FN];
     auto read = [&](int buf, int kk, int slot) {
@@ -146,7 +172,6 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_kernel(Dma
     // The last stage is peeled off so that no branch joins the code after the
     // barrier: the LDS counter waits stay exact there.
     int buf = 0;
-    const int64_t main_steps = steps - 1;
     for (int64_t s = 0; s < main_steps; ++s) {
 #pragma unroll
         for (int kk = 0; kk < KK - 1; ++kk) {

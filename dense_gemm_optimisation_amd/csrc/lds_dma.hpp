@@ -66,5 +66,17 @@ __device__ inline void direct_load16(u32x4 rs, uint32_t lds, uint32_t voffset) {
         : "memory", "m0");
 }
 
+// buffer_load_dword ... lds: 4 bytes per lane from the buffer `rs` at byte
+// offset `voffset` into LDS at `lds` + 4 * lane (the same contract as
+// direct_load16).
+__device__ inline void direct_load4(u32x4 rs, uint32_t lds, uint32_t voffset) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"(voffset), "s"(rs)
+        : "memory", "m0");
+}
+
 }  // namespace dma
 }  // namespace libgemm
