@@ -51,7 +51,10 @@ sys.path.insert(0, ROOT)
 # MI355X dense peaks, published (8-bit floats: twice the 16-bit rate; the
 # block-scaled 6- and 4-bit formats twice the 8-bit one)
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2,
-               "mxfp8": 5033.2, "mxfp6": 10066.3, "mxfp4": 10066.3}
+               "mxfp8": 5033.2, "mxfp6": 10066.3, "mxfp4": 10066.3,
+               # fp32 through three bf16 products: the bf16 peak over three, in
+               # fp32-equivalent flops (2MNK)
+               "f32_bf16x3": 2516.6 / 3}
 ESIZE = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1, "e5m2": 1}
 VIEW = {"f32": np.float32, "bf16": np.int16, "f16": np.int16, "e4m3": np.int8, "e5m2": np.int8}
 HBM_GBS = 8000.0
@@ -86,9 +89,12 @@ def is_mx(p):
 
 
 def dtype_key(p):
-    """The key of PEAK_TFLOPS for a workload: its input type, or mxfp8/6/4."""
+    """The key of PEAK_TFLOPS for a workload: its input type, mxfp8/6/4, or
+    f32_bf16x3 for fp32 through split bf16 products."""
     import workloads
-    return f"mxfp{workloads.MX_WIDTH[p.fa]}" if is_mx(p) else p.in_dtype
+    if is_mx(p):
+        return f"mxfp{workloads.MX_WIDTH[p.fa]}"
+    return "f32_bf16x3" if p.entry == "bf16x3" else p.in_dtype
 
 
 def algorithmic_bytes(p):
@@ -158,6 +164,16 @@ def make_launch(p, sets, stream, bias=None, workspace=None):
     if workspace is not None:
         epi.update(workspace=workspace.data_ptr(), workspace_bytes=workspace.numel() * 4)
     turn = [0]
+    if p.entry == "bf16x3":
+        def launch():
+            a = argsets[turn[0]]
+            binding.gemm_f32_bf16x3(*a[1:15], batch=p.batch, stride_a=p.stride_a,
+                                    stride_b=p.stride_b, stride_c=p.stride_c,
+                                    workspace=workspace.data_ptr(),
+                                    workspace_bytes=workspace.numel() * 4, stream=a[-1])
+            turn[0] = (turn[0] + 1) % len(argsets)
+        launch.turn = lambda: turn[0]
+        return launch
 
     def launch():
         binding.gemm(*argsets[turn[0]], **epi)
@@ -199,6 +215,12 @@ def kernel_family(p, bufs, workspace=None):
     if p.entry == "valu":
         return "sgemm_valu"
     da, db, dc = bufs
+    if p.entry == "bf16x3":
+        name = binding.kernel_name_bf16x3(p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a,
+                                          db.data_ptr(), p.ldb, p.order_b, p.beta, dc.data_ptr(),
+                                          p.ldc, p.order_c, p.batch, p.stride_a, p.stride_b,
+                                          p.stride_c, workspace.data_ptr(), workspace.numel() * 4)
+        return f"f32_bf16x3 ({name})"
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     return binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a,
                                db.data_ptr(), p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc,
@@ -484,6 +506,9 @@ def main():
             nsets[p.name] = len(sets)
             pws = ws if (ws is not None and not is_mx(p) and p.in_dtype in ("f32", "bf16", "f16")
                          and not p.bias and not p.act and not p.entry) else None
+            if p.entry == "bf16x3":  # its own workspace, for the split copies
+                pws = torch.empty(binding.bf16x3_workspace_size(p.M, p.N, p.K, p.batch) // 4,
+                                  dtype=torch.int32, device="cuda")
             families[p.name] = kernel_family(p, bufs, pws)
             bias = None if is_mx(p) else device_bias(p, torch)
             launches.append((p, sets, make_launch(p, sets, stream, bias, pws)))

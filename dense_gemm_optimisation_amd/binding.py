@@ -95,6 +95,12 @@ def library() -> ctypes.CDLL:
         lib.gemm_f32_ws.restype = i32
         lib.gemm_kernel_name_ws.argtypes = [i32] + common + [i32, i64, i64, i64, i64, vp, sz]
         lib.gemm_kernel_name_ws.restype = ctypes.c_char_p
+        lib.gemm_f32_bf16x3_workspace_size.argtypes = [i64, i64, i64, i64]
+        lib.gemm_f32_bf16x3_workspace_size.restype = sz
+        lib.gemm_f32_bf16x3.argtypes = common + [i64, i64, i64, i64, vp, sz, vp]
+        lib.gemm_f32_bf16x3.restype = i32
+        lib.gemm_kernel_name_bf16x3.argtypes = common + [i64, i64, i64, i64, vp, sz]
+        lib.gemm_kernel_name_bf16x3.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -250,6 +256,33 @@ def gemm_f32_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, 
                                order_c, batch, stride_a, stride_b, stride_c, workspace,
                                workspace_bytes, _stream(stream))
     return _check(st, "gemm_f32_ws", raise_on_error)
+
+
+def bf16x3_workspace_size(M, N, K, batch=1):
+    """Bytes of workspace gemm_f32_bf16x3 needs for these sizes."""
+    return library().gemm_f32_bf16x3_workspace_size(M, N, K, batch)
+
+
+def gemm_f32_bf16x3(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                    batch=1, stride_a=0, stride_b=0, stride_c=0, workspace=0, workspace_bytes=0,
+                    stream=None, raise_on_error=True):
+    """fp32 GEMM as three bf16 products of split operands; the workspace
+    (address, bytes) receives the split copies."""
+    st = library().gemm_f32_bf16x3(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C,
+                                   ldc, order_c, batch, stride_a, stride_b, stride_c, workspace,
+                                   workspace_bytes, _stream(stream))
+    return _check(st, "gemm_f32_bf16x3", raise_on_error)
+
+
+def kernel_name_bf16x3(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,
+                       batch=1, stride_a=0, stride_b=0, stride_c=0, workspace=0,
+                       workspace_bytes=0):
+    """The bf16 kernel gemm_f32_bf16x3 would run ("scale"/"" when nothing is
+    multiplied, None for invalid arguments); host only."""
+    name = library().gemm_kernel_name_bf16x3(M, N, K, alpha, A, lda, order_a, B, ldb, order_b,
+                                             beta, C, ldc, order_c, batch, stride_a, stride_b,
+                                             stride_c, workspace, workspace_bytes)
+    return None if name is None else name.decode()
 
 
 def gemm_bf16_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, order_c,

@@ -26,7 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "scale.hip", "pack.hip", "noalloc.hip", "sgemm_valu.hip", "sgemm_mfma.hip", "sgemm_splitk.hip", "hgemm_mfma.hip", "hgemm_mfma_dma.hip",
-           "hgemm_splitk.hip", "gemm_skinny.hip", "f8gemm_mfma.hip", "mxgemm.hip"]
+           "hgemm_splitk.hip", "gemm_skinny.hip", "f8gemm_mfma.hip", "mxgemm.hip", "split_bf16.hip"]
 # Sources compiled once per part (-D<macro>=k, one object each), so that
 # their many kernel instantiations build in parallel: source -> (macro, parts).
 PARTS = {"hgemm_mfma.hip": ("LIBGEMM_HGEMM_PART", 4), "mxgemm.hip": ("LIBGEMM_MX_PART", 3)}

@@ -477,6 +477,61 @@ gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K,
 
 Elem out_type(Elem in, gemm_dtype_t c_dtype) { return c_dtype == GEMM_DTYPE_F32 ? Elem::F32 : in; }
 
+// An fp32 call computed as three bf16 products (gemm_f32_bf16x3): the
+// canonical fp32 problem, and the bf16 problem on the split copies in the
+// workspace (A' at its start, B' after it).  k is None or Scale when nothing
+// is multiplied (then the call is gemm_f32's), else the bf16 kernel.
+struct SplitPlan {
+    Problem p, q;
+    Kernel k = Kernel::None;
+    int64_t batch_a = 0, batch_b = 0;  // copies of A and B (1 for a broadcast operand)
+    int64_t off_b = 0;                 // byte offset of B' in the workspace
+};
+
+int64_t split_copies(const Problem &p, bool a) {
+    return p.batch > 1 && (a ? p.sA : p.sB) == 0 ? 1 : p.batch;
+}
+
+// Validates the call and the workspace; no HIP call.
+gemm_status_t split_plan(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                         int orderA, const void *B, int64_t ldb, int orderB, float beta,
+                         const void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
+                         int64_t strideB, int64_t strideC, const void *workspace, size_t bytes,
+                         SplitPlan &s) {
+    gemm_status_t st = plan(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B,
+                            ldb, orderB, beta, const_cast<void *>(C), ldc, orderC, batch, strideA,
+                            strideB, strideC, nullptr, 0, GEMM_ACT_NONE, s.p, s.k);
+    if (st != GEMM_OK || s.k == Kernel::None || s.k == Kernel::Scale) return st;
+    const Problem &p = s.p;
+    s.batch_a = split_copies(p, true);
+    s.batch_b = split_copies(p, false);
+    const int64_t need_a = split_bytes(p.M, p.K, s.batch_a);
+    const int64_t need_b = split_bytes(p.N, p.K, s.batch_b);
+    if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+        bytes < static_cast<size_t>(need_a + need_b))
+        return GEMM_ERR_INVALID_ARG;
+    st = check_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
+                         strideC, nullptr, 0, A, B, C, workspace, bytes);
+    if (st != GEMM_OK) return st;
+    s.off_b = need_a;
+    const int64_t K3 = 3 * split_kp(p.K);
+    Problem q = p;
+    q.in = q.in_b = Elem::BF16;
+    q.out = Elem::F32;
+    q.K = K3;
+    q.A = workspace;
+    q.lda = K3;
+    q.a_kmajor = true;
+    q.sA = s.batch_a > 1 ? p.M * K3 : 0;
+    q.B = static_cast<const char *>(workspace) + need_a;
+    q.ldb = K3;
+    q.b_kmajor = true;
+    q.sB = s.batch_b > 1 ? p.N * K3 : 0;
+    s.q = q;
+    s.k = choose(q, false);
+    return GEMM_OK;
+}
+
 // 8-bit format and output-type enumerators; false when out of range.
 bool f8_type(gemm_f8_format_t f, Elem &e) {
     if (f == GEMM_F8_E4M3) e = Elem::E4M3;
@@ -643,6 +698,42 @@ gemm_status_t gemm_f32_valu(int64_t M, int64_t N, int64_t K, float alpha, const 
     return run(Elem::F32, Elem::F32, Elem::F32, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta,
                C, ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream,
                nullptr, 0, true);
+}
+
+size_t gemm_f32_bf16x3_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch) {
+    if (M < 0 || N < 0 || K < 0 || batch < 0 || too_big(M, K) || too_big(N, K)) return 0;
+    const int64_t kp = split_kp(K);
+    if (too_big(6 * kp, M + N) || too_big(6 * kp * (M + N), batch)) return 0;
+    return static_cast<size_t>(split_bytes(M, K, batch) + split_bytes(N, K, batch));
+}
+
+gemm_status_t gemm_f32_bf16x3(int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                              int64_t lda, gemm_order_t orderA, const float *B, int64_t ldb,
+                              gemm_order_t orderB, float beta, float *C, int64_t ldc,
+                              gemm_order_t orderC, int64_t batch, int64_t strideA,
+                              int64_t strideB, int64_t strideC, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    SplitPlan s;
+    const gemm_status_t st = split_plan(M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C,
+                                        ldc, orderC, batch, strideA, strideB, strideC, workspace,
+                                        workspace_bytes, s);
+    if (st != GEMM_OK || s.k == Kernel::None) return st;
+    hipError_t e;
+    if (s.k == Kernel::Scale) {
+        e = launch(s.k, s.p, stream);
+    } else {
+        const Problem &p = s.p;
+        uint16_t *wa = static_cast<uint16_t *>(workspace);
+        uint16_t *wb = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + s.off_b);
+        e = launch_split_a(static_cast<const float *>(p.A), p.lda, p.sA, p.a_kmajor, p.M, p.K,
+                           s.batch_a, wa, stream);
+        if (e == hipSuccess)
+            e = launch_split_b(static_cast<const float *>(p.B), p.ldb, p.sB, p.b_kmajor, p.N,
+                               p.K, s.batch_b, wb, stream);
+        if (e == hipSuccess) e = launch(s.k, s.q, stream);
+    }
+    if (e == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 int gemm_test_switches(int flags) {
@@ -872,6 +963,19 @@ const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K
         st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
                            strideC, nullptr, 0, A, B, C, workspace, workspace_bytes, w);
     return st == GEMM_OK ? kernel_name(w.k) : nullptr;
+}
+
+const char *gemm_kernel_name_bf16x3(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                                    int64_t lda, gemm_order_t orderA, const void *B, int64_t ldb,
+                                    gemm_order_t orderB, float beta, const void *C, int64_t ldc,
+                                    gemm_order_t orderC, int64_t batch, int64_t strideA,
+                                    int64_t strideB, int64_t strideC, const void *workspace,
+                                    size_t workspace_bytes) {
+    SplitPlan s;
+    const gemm_status_t st = split_plan(M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C,
+                                        ldc, orderC, batch, strideA, strideB, strideC, workspace,
+                                        workspace_bytes, s);
+    return st == GEMM_OK ? kernel_name(s.k) : nullptr;
 }
 
 }  // extern "C"

@@ -81,6 +81,19 @@ struct PackSpec {
 int64_t packed_bytes(const PackSpec &s);
 hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream);
 
+// fp32 operands split into bf16 pieces for the three-product fp32 GEMM
+// (split_bf16.hip): Kp = K rounded up to a multiple of 8; a copy holds
+// [batch][rows][3 Kp] bf16, pieces (hi, hi, lo) for A and (hi, lo, hi) for
+// B, each zero-padded from K to Kp; split_bytes is its size rounded up to
+// 256 bytes.  Source element (r, k): src[b*stride + r*ld + k] when kmajor,
+// else src[b*stride + k*ld + r].
+int64_t split_kp(int64_t K);
+int64_t split_bytes(int64_t rows, int64_t K, int64_t batch);
+hipError_t launch_split_a(const float *A, int64_t lda, int64_t sA, bool kmajor, int64_t M,
+                          int64_t K, int64_t batch, uint16_t *dst, hipStream_t stream);
+hipError_t launch_split_b(const float *B, int64_t ldb, int64_t sB, bool kmajor, int64_t N,
+                          int64_t K, int64_t batch, uint16_t *dst, hipStream_t stream);
+
 // Address of this library's scratch array on the device `stream` belongs to
 // (looked up once per device; see noalloc.hip).
 hipError_t scratch_address(hipStream_t stream, void **ptr);

@@ -15,6 +15,9 @@
  * Entry points
  *   gemm_f32   fp32 inputs, fp32 output, fp32 arithmetic (on the matrix cores).
  *   gemm_f32_valu  the same product on the vector ALUs (register-tiled).
+ *   gemm_f32_bf16x3  fp32 inputs and output, computed as three bf16 products
+ *              of split operands on the bf16 matrix cores (a caller
+ *              workspace holds the split copies; accuracy below).
  *   gemm_bf16  bf16 inputs, fp32 accumulation on the matrix cores, output in
  *              bf16 (c_dtype = GEMM_DTYPE_SAME) or fp32 (GEMM_DTYPE_F32).
  *   gemm_f16   the same for IEEE fp16 inputs.
@@ -32,7 +35,7 @@
  *              gemm_workspace_size gives the bytes it needs.
  *   gemm_bf16_noalloc  gemm_bf16_ws on the library's own scratch memory.
  *   gemm_kernel_name, gemm_f8_kernel_name, gemm_mx_kernel_name,
- *   gemm_kernel_name_ws  which kernel
+ *   gemm_kernel_name_ws, gemm_kernel_name_bf16x3  which kernel
  *              a GEMM call with the
  *              given arguments would launch (host only; for tests and
  *              profiling).
@@ -439,6 +442,43 @@ gemm_status_t gemm_f32_valu(int64_t M, int64_t N, int64_t K, float alpha,
                             int64_t batch, int64_t strideA, int64_t strideB,
                             int64_t strideC, hipStream_t stream);
 
+/* fp32 GEMM on the bf16 matrix instructions, by splitting each operand into
+ * two bf16 pieces ("GPU GEMM 优化完全拆解（三）", pinghaoyang.com.cn, the
+ * section on numerical precision and why fp32 cuBLAS does not use Tensor
+ * Cores, describes the split into a high and a low part and three products
+ * for TF32; bf16 plays that part here).  Each element v of A and B becomes
+ * hi = v rounded to bf16 (nearest, ties to even; truncated if that would
+ * overflow) and lo = (v - hi) rounded to bf16, and a*b is summed as
+ * hi*hi + hi*lo + lo*hi in fp32.  The terms left out are at most 2^-15 |a*b|,
+ * so each element of C is within (2^-15 + the fp32 accumulation error of 3K
+ * terms) * sum_k |A_ik| |B_kj| of the exact result; alpha, beta, C and the
+ * orders are applied exactly as in gemm_f32 (beta = 0: C is not read).
+ * Non-finite elements of A or B give non-finite results in the elements
+ * they reach (NaN where an infinity meets a zero piece); subnormal low
+ * pieces may be flushed, an error below 2^-126 per product.
+ *   workspace        device memory of at least
+ *                    gemm_f32_bf16x3_workspace_size(M, N, K, batch) bytes,
+ *                    256-byte aligned, not overlapping A, B or C; it receives
+ *                    the bf16 copies (A: M x 3Kp per batch entry, B: N x 3Kp,
+ *                    Kp = K rounded up to a multiple of 8; one copy of an
+ *                    operand whose batch stride is 0), written on `stream`
+ *                    before the product runs.  Calls that share it must be
+ *                    ordered (for example, on one stream).
+ *   workspace_bytes  its size.
+ * A workspace that is NULL, misaligned, too small or overlapping is
+ * GEMM_ERR_INVALID_ARG.  When nothing is multiplied (M, N or batch = 0,
+ * K = 0 or alpha = 0) the call is gemm_f32's and the workspace is not used.
+ * Everything else is as for gemm_f32. */
+size_t gemm_f32_bf16x3_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch);
+
+gemm_status_t gemm_f32_bf16x3(int64_t M, int64_t N, int64_t K, float alpha,
+                              const float *A, int64_t lda, gemm_order_t orderA,
+                              const float *B, int64_t ldb, gemm_order_t orderB,
+                              float beta, float *C, int64_t ldc, gemm_order_t orderC,
+                              int64_t batch, int64_t strideA, int64_t strideB,
+                              int64_t strideC, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* Testing aid: process-wide overrides of the kernel choice, so that tests
  * can run every kernel on problems the normal choice sends elsewhere.  Not
  * for production use.  The set holds until the next call; 0 (the initial
@@ -533,6 +573,18 @@ const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K
                                 gemm_dtype_t c_dtype, int64_t batch,
                                 int64_t strideA, int64_t strideB, int64_t strideC,
                                 const void *workspace, size_t workspace_bytes);
+
+/* The bf16 kernel gemm_f32_bf16x3 would run on the split copies (one of the
+ * names of gemm_kernel_name for 16-bit inputs), "scale" or "" when nothing is
+ * multiplied, NULL when the arguments or the workspace are invalid.  The
+ * workspace is only checked, never dereferenced; no HIP call is made. */
+const char *gemm_kernel_name_bf16x3(int64_t M, int64_t N, int64_t K, float alpha,
+                                    const void *A, int64_t lda, gemm_order_t orderA,
+                                    const void *B, int64_t ldb, gemm_order_t orderB,
+                                    float beta, const void *C, int64_t ldc,
+                                    gemm_order_t orderC, int64_t batch, int64_t strideA,
+                                    int64_t strideB, int64_t strideC, const void *workspace,
+                                    size_t workspace_bytes);
 
 #ifdef __cplusplus
 }

@@ -250,14 +250,28 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
     valu = p.entry == "valu"  # gemm_f32_valu runs the vector-ALU kernel whatever the shape
     if valu and kernel not in ("", "scale", None):
         kernel = "sgemm_valu"
+    x3 = {}
+    if p.entry == "bf16x3":  # gemm_f32_bf16x3, with a workspace of its own
+        n = binding.bf16x3_workspace_size(p.M, p.N, p.K, p.batch)
+        w3 = torch.empty(max(n, 256) // 4 + 64, dtype=torch.int32, device="cuda")
+        x3 = dict(workspace=w3.data_ptr(), workspace_bytes=n if workspace_bytes is None
+                  else workspace_bytes)
+        kernel = binding.kernel_name_bf16x3(p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb,
+                                            p.ldb, p.order_b, p.beta, pc, p.ldc, p.order_c,
+                                            p.batch, p.stride_a, p.stride_b, p.stride_c, **x3)
     outs = []
     for r in range(repeat):
         if r:
             dc.copy_(torch.from_numpy(fc.view(cview)))
-        binding.gemm(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
-                     p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch, p.stride_a,
-                     p.stride_b, p.stride_c, bias=pbias, stride_bias=p.stride_bias, act=p.act,
-                     b_dtype=p.b_dtype, out_dtype=p.c_dtype, valu=valu, **ws)
+        if x3:
+            binding.gemm_f32_bf16x3(p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
+                                    p.order_b, p.beta, pc, p.ldc, p.order_c, p.batch,
+                                    p.stride_a, p.stride_b, p.stride_c, **x3)
+        else:
+            binding.gemm(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
+                         p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch, p.stride_a,
+                         p.stride_b, p.stride_c, bias=pbias, stride_bias=p.stride_bias,
+                         act=p.act, b_dtype=p.b_dtype, out_dtype=p.c_dtype, valu=valu, **ws)
         torch.cuda.synchronize()
         outs.append(dc.cpu().numpy().view(fc.dtype).copy())
     out = outs[0]

@@ -30,10 +30,12 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
                                     "gemm_bf16_noalloc", "gemm_bf16_ws", "gemm_f16",
                                     "gemm_f16_bias_act",
-                                    "gemm_f16_ws", "gemm_f32", "gemm_f32_bias_act",
+                                    "gemm_f16_ws", "gemm_f32", "gemm_f32_bf16x3",
+                                    "gemm_f32_bf16x3_workspace_size", "gemm_f32_bias_act",
                                     "gemm_f32_valu", "gemm_f32_ws",
                                     "gemm_f8",
                                     "gemm_f8_kernel_name", "gemm_kernel_name",
+                                    "gemm_kernel_name_bf16x3",
                                     "gemm_kernel_name_ws", "gemm_mx", "gemm_mx_kernel_name",
                                     "gemm_status_string",
                                     "gemm_test_switches", "gemm_workspace_size"]
@@ -390,8 +392,9 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_edge": "hgemm_mfma", "bf16_tail": "hgemm_mfma_dma", "bf16_skinny": "gemm_skinny",
             "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma",
             "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma",
-            # called through gemm_f32_valu; gemm_kernel_name describes gemm_f32
-            "f32_4096_valu": "sgemm_mfma_dma"}
+            # called through gemm_f32_valu and gemm_f32_bf16x3; gemm_kernel_name
+            # describes gemm_f32
+            "f32_4096_valu": "sgemm_mfma_dma", "f32_4096_bf16x3": "sgemm_mfma_dma"}
     mx = {n for n, p in workloads.CONFIGS.items() if isinstance(p, workloads.MxProblem)}
     assert mx == {"mxfp4_4096", "mxfp6_4096", "mxfp8_4096"}
     assert sorted(want) == sorted(set(workloads.CONFIGS) - mx)
@@ -554,3 +557,65 @@ def test_noalloc_refuses_calls_beyond_its_scratch(lib):
     assert lib.gemm_bf16_noalloc(*args[:14], 2, *args[15:], raise_on_error=False) == \
         lib.ERR_INVALID_ARG
     assert lib.gemm_bf16_noalloc(0, *args[1:], raise_on_error=False) == lib.OK
+
+
+# ------------------------------------------------------------------ fp32 as three bf16 products
+
+def kname_x3(lib, M, N, K, ws=WS, nbytes=None, **kw):
+    oa, ob, oc = kw.pop("oa", 0), kw.pop("ob", 0), kw.pop("oc", 0)
+    lda = kw.pop("lda", K if oa == 0 else M)
+    ldb = kw.pop("ldb", N if ob == 0 else K)
+    ldc = kw.pop("ldc", N if oc == 0 else M)
+    batch = kw.pop("batch", 1)
+    sa, sb = kw.pop("sa", M * K if batch > 1 else 0), kw.pop("sb", K * N if batch > 1 else 0)
+    nbytes = lib.bf16x3_workspace_size(M, N, K, batch) if nbytes is None else nbytes
+    return lib.kernel_name_bf16x3(M, N, K, kw.pop("alpha", 1.0), GB, lda, oa, 2 * GB, ldb, ob, 0.0,
+                                  3 * GB, ldc, oc, batch, sa, sb, M * N if batch > 1 else 0,
+                                  workspace=ws, workspace_bytes=nbytes)
+
+
+def test_bf16x3_workspace_size(lib):
+    # two bf16 copies of 3 Kp (K rounded up to a multiple of 8) per row of A
+    # and per column of B, each rounded up to 256 bytes
+    assert lib.bf16x3_workspace_size(4096, 4096, 4096, 1) == 2 * 4096 * 3 * 4096 * 2
+    assert lib.bf16x3_workspace_size(100, 30, 1001, 1) == \
+        -(-100 * 3 * 1008 * 2 // 256) * 256 + -(-30 * 3 * 1008 * 2 // 256) * 256
+    assert lib.bf16x3_workspace_size(8, 8, 8, 3) == 2 * 1280     # 3 x 8 x 24 x 2 = 1152, to 256
+    assert lib.bf16x3_workspace_size(0, 8, 8, 1) == 512   # B's copy: 8 x 24 x 2 bytes, to 256
+    assert lib.bf16x3_workspace_size(-1, 8, 8, 1) == 0
+    assert lib.bf16x3_workspace_size(1 << 40, 1 << 40, 1 << 40, 1) == 0   # overflows
+
+
+def test_bf16x3_kernel_choice(lib, clean_env):
+    # the bf16 kernel on the split copies (K-contiguous, 16-byte aligned,
+    # K' = 3 * Kp): the same choice as a bf16 problem of that K'
+    assert kname_x3(lib, 4096, 4096, 4096) == "hgemm_mfma_dma"
+    assert kname_x3(lib, 4095, 4097, 1001, oa=1, ob=1) == "hgemm_mfma_dma"   # any layout copies aligned
+    assert kname_x3(lib, 16, 4096, 4096) == "gemm_skinny"
+    assert kname_x3(lib, 4096, 16, 4096, oc=1) == "gemm_skinny"             # C^T has 16 rows
+    assert kname_x3(lib, 256, 256, 256) == "hgemm_splitk"                  # K' = 768
+    assert kname_x3(lib, 256, 256, 128) == "hgemm_mfma_dma"                # K' = 384: too short to split
+    assert kname_x3(lib, 520, 264, 200, batch=3, sb=0) == "hgemm_splitk"   # 18 tiles, K' = 600
+    # nothing to multiply: gemm_f32's quick paths, workspace not needed
+    assert kname_x3(lib, 4096, 4096, 4096, alpha=0.0, ws=0, nbytes=0) == "scale"
+    assert kname_x3(lib, 4096, 4096, 0, lda=1, ws=0, nbytes=0) == "scale"
+    assert kname_x3(lib, 0, 4096, 4096, ws=0, nbytes=0) == ""
+    clean_env(lib.TEST_NO_SPLITK)
+    assert kname_x3(lib, 256, 256, 256) == "hgemm_mfma_dma"
+
+
+def test_bf16x3_invalid_workspace(lib):
+    n = lib.bf16x3_workspace_size(520, 264, 200, 1)
+    assert kname_x3(lib, 520, 264, 200) is not None
+    assert kname_x3(lib, 520, 264, 200, nbytes=n - 1) is None               # too small
+    assert kname_x3(lib, 520, 264, 200, ws=0) is None                       # NULL
+    assert kname_x3(lib, 520, 264, 200, ws=WS + 16) is None                 # not 256-byte aligned
+    assert kname_x3(lib, 520, 264, 200, ws=GB + 256) is None                # overlaps A
+    assert kname_x3(lib, 520, 264, 200, ws=3 * GB - 256) is None            # overlaps C
+    assert kname_x3(lib, 520, 264, 200, lda=100) is None                    # lda < K
+    # a broadcast operand is copied once: A's one copy (520 x 600 x 2 bytes,
+    # to 256) and B's four
+    need = 624128 + 4 * 520 * 600 * 2
+    assert kname_x3(lib, 520, 520, 200, batch=4, sa=0, nbytes=need) is not None
+    assert kname_x3(lib, 520, 520, 200, batch=4, sa=0, nbytes=need - 1) is None
+    assert kname_x3(lib, 520, 520, 200, batch=4, nbytes=need) is None

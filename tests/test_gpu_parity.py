@@ -1055,6 +1055,75 @@ def test_mx_full_size_sampled(name):
     check_mx(workloads.config(name), sample="auto")
 
 
+# ------------------------------------------------------------------ fp32 as three bf16 products
+
+X3_SHAPES = [(8, 8, 8), (256, 256, 256), (264, 520, 1001), (1000, 1032, 1000), (4095, 97, 333),
+             (16, 4096, 4096), (3, 5, 7)]
+
+
+@pytest.mark.parametrize("shape", X3_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=["nn", "nt", "tn", "tt"])
+def test_bf16x3(shape, orders):
+    # fp32 within the fp32 criterion; the copies are always K-contiguous and
+    # aligned, whatever the caller's layout (K not a multiple of 8 padded)
+    M, N, K = shape
+    oa, ob = orders
+    res, _ = check(P("x3", "f32", M, N, K, alpha=0.75, beta=0.5, order_a=oa, order_b=ob,
+                     entry="bf16x3"), seed=M + N + K)
+    assert res.kernel in ("hgemm_mfma_dma", "hgemm_splitk", "gemm_skinny"), res.kernel
+
+
+def test_bf16x3_col_major_c_batches_and_beta_zero():
+    check(P("x3-colC", "f32", 520, 264, 300, order_c=COL, beta=-1.0, entry="bf16x3"), seed=51)
+    check(P("x3-batch", "f32", 264, 136, 520, batch=3, beta=0.5, entry="bf16x3"), seed=52)
+    check(P("x3-shared-b", "f32", 264, 136, 520, batch=3, stride_b=0, entry="bf16x3"), seed=53)
+    check(P("x3-shared-a", "f32", 264, 136, 520, batch=3, stride_a=0, entry="bf16x3"), seed=54)
+    # beta = 0: C is not read (NaN there does not propagate)
+    check(P("x3-nan-c", "f32", 300, 200, 100, entry="bf16x3"), seed=55, c_init=np.nan)
+
+
+def test_bf16x3_misaligned_bases():
+    # fp32 operands 4 or 12 bytes off a 16-byte boundary: the split reads them
+    # element by element; its copies are aligned all the same
+    for oa, ob in [(ROW, ROW), (COL, COL)]:
+        res, _ = check(P("x3-misaligned", "f32", 264, 520, 512, beta=0.5, order_a=oa, order_b=ob,
+                         entry="bf16x3"), seed=60, base_offset=(1, 3, 1))
+        assert res.kernel == "hgemm_splitk"  # six tiles of K' = 1536
+
+
+def test_bf16x3_nothing_to_multiply():
+    res, _ = check(P("x3-alpha0", "f32", 130, 70, 40, alpha=0.0, beta=0.5, entry="bf16x3"),
+                   seed=56)
+    assert res.kernel == "scale"
+    res, _ = check(P("x3-k0", "f32", 130, 70, 0, beta=-1.5, entry="bf16x3"), seed=57)
+    assert res.kernel == "scale"
+
+
+def test_bf16x3_integers_bit_exact():
+    # small integers split with lo = 0: every product and sum is exact
+    p = P("x3-int", "f32", 520, 1032, 2000, alpha=2.0, beta=1.0, batch=2, entry="bf16x3")
+    res, _ = check(p, host=_int_host(p, np.random.default_rng(58)), repeat=2)
+    assert res.max_err == 0.0
+
+
+def test_bf16x3_wide_exponent_range():
+    # operands spread over 2^-40 .. 2^40: the split is relative, so the
+    # normalised error stays at the fp32 level
+    p = P("x3-range", "f32", 264, 264, 520, entry="bf16x3")
+    rng = np.random.default_rng(59)
+    def mk(n):
+        return (rng.uniform(-1, 1, n) * np.exp2(rng.integers(-40, 41, n))).astype(np.float32)
+    host = (mk(p.buffer_elems("a")), mk(p.buffer_elems("b")), mk(p.buffer_elems("c")))
+    res, _ = check(p, host=host)
+    assert res.max_err < 2.0 ** -14, res.max_err
+
+
+def test_bf16x3_workload_full_size():
+    res, _ = check(workloads.config("f32_4096_bf16x3"), sample="auto")
+    assert res.kernel == "hgemm_mfma_dma"
+
+
 # ------------------------------------------------------------------ skinny split-K across workgroups (workspace)
 
 # (5, 8192, 4008): slices of four 128-row rounds, the last slice ending in a

@@ -85,7 +85,7 @@ class Problem:
     sigma_bias: float = 1.0
     act: int = 0                     # 0 none, 1 ReLU, 2 GELU
     b_dtype: Optional[str] = None    # type of B when it differs from A's (8-bit floats)
-    entry: str = ""                  # "valu": called through gemm_f32_valu
+    entry: str = ""                  # "valu": gemm_f32_valu; "bf16x3": gemm_f32_bf16x3
 
     def __post_init__(self):
         M, N, K = self.M, self.N, self.K
@@ -387,6 +387,9 @@ def _configs():
                 note="fp32 SGEMM 4096^3, row-major, alpha=1 beta=0, U[-1,1]"),
         Problem("f32_4096_valu", "f32", "f32", 4096, 4096, 4096, entry="valu",
                 note="fp32 SGEMM 4096^3 on the vector-ALU kernel (gemm_f32_valu), U[-1,1]"),
+        Problem("f32_4096_bf16x3", "f32", "f32", 4096, 4096, 4096, entry="bf16x3",
+                note="fp32 SGEMM 4096^3 as three bf16 products of split operands "
+                     "(gemm_f32_bf16x3), U[-1,1]"),
         Problem("bf16_4096", "bf16", "bf16", 4096, 4096, 4096,
                 note="bf16 HGEMM 4096^3, fp32 accumulate, bf16 out, N(0,1)"),
         Problem("f16_4096", "f16", "f16", 4096, 4096, 4096,
