@@ -107,10 +107,13 @@ def decode(dtype, bits) -> np.ndarray:
 def round_bits(dtype, x) -> np.ndarray:
     """Round float64 values to ``dtype`` (nearest-even, directly from double).
 
-    Returns the stored patterns: uint32 for f32, uint16 for bf16/f16.
+    Returns the stored patterns: uint32 for f32, uint16 for bf16/f16, uint8
+    for e4m3/e5m2 (saturating: beyond the largest finite value, infinities
+    included, gives that value; NaN the canonical NaN).
     """
     src = np.ascontiguousarray(x, dtype=np.float64)
-    out = np.empty(src.size, np.uint32 if dtype == "f32" else np.uint16)
+    store = {"f32": np.uint32, "e4m3": np.uint8, "e5m2": np.uint8}.get(dtype, np.uint16)
+    out = np.empty(src.size, store)
     _load().orc_round(_TYPES[dtype], src.ctypes.data, out.ctypes.data, src.size)
     return out.reshape(src.shape)
 

@@ -241,9 +241,35 @@ static uint16_t encode_f16(double r) {
     return sign | (uint16_t)((e + 15) << 10) | m;
 }
 
+/*
+ * 8-bit float outputs (the quantised epilogue: the epilogue section of "GPU
+ * GEMM 优化完全拆解（三）" folds quantisation scaling into the write-back).
+ * Round x to E4M3 or E5M2 by round_to_format, saturating: magnitudes beyond
+ * the largest finite value (448 for E4M3, whose all-ones pattern is NaN;
+ * 57344 for E5M2), infinities included, become that value with x's sign; a
+ * NaN becomes the canonical NaN (0x7f, resp. 0x7e).
+ */
+static uint8_t encode_f8(double x, int e5m2) {
+    const int p = e5m2 ? 3 : 4, emin = e5m2 ? -14 : -6, bias = e5m2 ? 15 : 7;
+    const double maxfinite = e5m2 ? 57344.0 : 448.0;
+    if (isnan(x)) return e5m2 ? 0x7e : 0x7f;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    /* at most maxfinite, a value of the format, rounds to at most maxfinite */
+    double r = a > maxfinite ? maxfinite : round_to_format(a, p, emin, e5m2 ? 15 : 8);
+    if (r == 0.0) return sign;
+    int e2;
+    frexp(r, &e2);
+    int e = e2 - 1;
+    if (e < emin) /* subnormal: r = m * 2^(emin - p + 1) */
+        return sign | (uint8_t)ldexp(r, -(emin - p + 1));
+    uint8_t m = (uint8_t)(ldexp(r, p - 1 - e) - ldexp(1.0, p - 1));
+    return sign | (uint8_t)((e + bias) << (p - 1)) | m;
+}
+
 /* ---------------------------------------------------------------- exports */
 
-int orc_version(void) { return 4; }
+int orc_version(void) { return 5; }
 
 void orc_decode(int type, const void *src, double *dst, int64_t n) {
     for (int64_t i = 0; i < n; ++i) dst[i] = load(type, src, i);
@@ -262,6 +288,10 @@ void orc_round(int type, const double *src, void *dst, int64_t n) {
         }
         case ORC_BF16:
             ((uint16_t *)dst)[i] = encode_bf16(round_to_format(src[i], 8, -126, 127));
+            break;
+        case ORC_E4M3:
+        case ORC_E5M2:
+            ((uint8_t *)dst)[i] = encode_f8(src[i], type == ORC_E5M2);
             break;
         default:
             ((uint16_t *)dst)[i] = encode_f16(round_to_format(src[i], 11, -14, 15));

@@ -56,6 +56,14 @@ MUTANTS = {
     "rows_b_transposed": ("offset(oB, k, j, ldb)", "offset(oB, j, k, ldb)"),
     "rows_b_type_ignored": ("load(b_type, B,", "load(in_type, B,"),
     "rows_batch_b_decoded_once": ("if (b == 0 || sB != 0)", "if (b == 0)"),
+    # 8-bit outputs (saturating rounding)
+    "f8out_no_saturation": ("double r = a > maxfinite ? maxfinite : round_to_format",
+                            "double r = a > maxfinite ? a : round_to_format"),
+    "f8out_e4m3_max_480": ("const double maxfinite = e5m2 ? 57344.0 : 448.0;",
+                           "const double maxfinite = e5m2 ? 57344.0 : 480.0;"),
+    "f8out_subnormal_scale": ("return sign | (uint8_t)ldexp(r, -(emin - p + 1));",
+                              "return sign | (uint8_t)ldexp(r, -(emin - p));"),
+    "f8out_e5m2_bias": ("bias = e5m2 ? 15 : 7;", "bias = e5m2 ? 16 : 7;"),
     # block-scaled (MX) inputs
     "mx_scale_block_16": ("i * P->ldsa + k / 32]", "i * P->ldsa + k / 16]"),
     "mx_b_scale_row_of_a": ("j * P->ldsb + k / 32]", "i * P->ldsb + k / 32]"),

@@ -563,6 +563,61 @@ def test_decode_every_8bit_pattern(dtype):
         assert np.nanmax(got[~np.isinf(got)]) == 57344.0 and np.isinf(got).sum() == 2
 
 
+# --------------------------------------------------------------- 8-bit outputs
+
+F8_MAX = {"e4m3": (448.0, 0x7E, 0x7F), "e5m2": (57344.0, 0x7B, 0x7E)}  # max, its pattern, NaN
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "e5m2"])
+def test_round_8bit_every_finite_pattern_round_trips(dtype):
+    bits = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode(dtype, bits)
+    fin = np.isfinite(vals)
+    assert np.array_equal(oracle.round_bits(dtype, vals[fin]), bits[fin])
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "e5m2"])
+def test_round_8bit_midpoints_go_to_even(dtype):
+    bits = np.arange(0, 128, dtype=np.uint8)
+    vals = oracle.decode(dtype, bits)
+    fin = np.isfinite(vals)
+    v, b = vals[fin], bits[fin]           # increasing, 0 .. max
+    mid = (v[:-1] + v[1:]) / 2
+    got = oracle.round_bits(dtype, mid)
+    even = np.where(b[:-1] % 2 == 0, b[:-1], b[1:])
+    assert np.array_equal(got, even)
+    # a hair either side of a midpoint goes to the nearer neighbour
+    eps = (v[1:] - v[:-1]) * 1e-6
+    assert np.array_equal(oracle.round_bits(dtype, mid - eps), b[:-1])
+    assert np.array_equal(oracle.round_bits(dtype, mid + eps), b[1:])
+    # and the negative side mirrors it with the sign bit
+    assert np.array_equal(oracle.round_bits(dtype, -mid), even | 0x80)
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "e5m2"])
+def test_round_8bit_saturates(dtype):
+    mx, pat, nan = F8_MAX[dtype]
+    x = np.array([mx, mx * 1.0001, mx * 1.07, 1e30, np.inf, -mx * 3, -np.inf, np.nan, 0.0, -0.0])
+    want = np.array([pat, pat, pat, pat, pat, pat | 0x80, pat | 0x80, nan, 0x00, 0x80], np.uint8)
+    assert np.array_equal(oracle.round_bits(dtype, x), want)
+    # below half the smallest subnormal: zero; at half: a tie, to even (zero)
+    tiny = oracle.decode(dtype, np.array([1], np.uint8))[0]
+    assert list(oracle.round_bits(dtype, np.array([tiny * 0.49, tiny * 0.5, tiny * 0.51, -tiny * 0.49]))) \
+        == [0, 0, 1, 0x80]
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "e5m2"])
+def test_round_8bit_agrees_with_torch_in_range(dtype):
+    torch = pytest.importorskip("torch")
+    mx = F8_MAX[dtype][0]
+    rng = np.random.default_rng(9)
+    x = (rng.uniform(-1, 1, 200000) * np.exp2(rng.integers(-22, 17, 200000))).astype(np.float32)
+    x = x[np.abs(x) <= mx]                       # torch does not saturate: compare in range only
+    tdt = torch.float8_e4m3fn if dtype == "e4m3" else torch.float8_e5m2
+    want = torch.from_numpy(x).to(tdt).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.round_bits(dtype, x.astype(np.float64)), want)
+
+
 def stored8(dtype, values):
     import torch
     tdt = torch.float8_e4m3fn if dtype == "e4m3" else torch.float8_e5m2
