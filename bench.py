@@ -164,6 +164,15 @@ def make_launch(p, sets, stream, bias=None, workspace=None):
     if workspace is not None:
         epi.update(workspace=workspace.data_ptr(), workspace_bytes=workspace.numel() * 4)
     turn = [0]
+    if p.entry == "quant":
+        def launch():
+            a = argsets[turn[0]]
+            binding.gemm_quant(p.in_dtype, *a[1:11], *a[12:15], p.c_dtype, p.c_scale, p.batch,
+                               p.stride_a, p.stride_b, p.stride_c, bias=epi["bias"],
+                               stride_bias=p.stride_bias or 0, act=p.act, stream=a[-1])
+            turn[0] = (turn[0] + 1) % len(argsets)
+        launch.turn = lambda: turn[0]
+        return launch
     if p.entry == "bf16x3":
         def launch():
             a = argsets[turn[0]]
@@ -215,6 +224,11 @@ def kernel_family(p, bufs, workspace=None):
     if p.entry == "valu":
         return "sgemm_valu"
     da, db, dc = bufs
+    if p.entry == "quant":
+        return binding.kernel_name_quant(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda,
+                                         p.order_a, db.data_ptr(), p.ldb, p.order_b, dc.data_ptr(),
+                                         p.ldc, p.order_c, p.c_dtype, p.batch, p.stride_a,
+                                         p.stride_b, p.stride_c)
     if p.entry == "bf16x3":
         name = binding.kernel_name_bf16x3(p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a,
                                           db.data_ptr(), p.ldb, p.order_b, p.beta, dc.data_ptr(),

@@ -95,6 +95,15 @@ def library() -> ctypes.CDLL:
         lib.gemm_f32_ws.restype = i32
         lib.gemm_kernel_name_ws.argtypes = [i32] + common + [i32, i64, i64, i64, i64, vp, sz]
         lib.gemm_kernel_name_ws.restype = ctypes.c_char_p
+        quant = [i64, i64, i64, f32, vp, i64, i32, vp, i64, i32, vp, i64, i32, i32, f32, i64, i64,
+                 i64, i64, vp, i64, i32, vp]
+        for name in ("gemm_bf16_quant", "gemm_f16_quant"):
+            fn = getattr(lib, name)
+            fn.argtypes = quant
+            fn.restype = i32
+        lib.gemm_kernel_name_quant.argtypes = [i32, i64, i64, i64, f32, vp, i64, i32, vp, i64, i32,
+                                               vp, i64, i32, i32, i64, i64, i64, i64]
+        lib.gemm_kernel_name_quant.restype = ctypes.c_char_p
         lib.gemm_f32_bf16x3_workspace_size.argtypes = [i64, i64, i64, i64]
         lib.gemm_f32_bf16x3_workspace_size.restype = sz
         lib.gemm_f32_bf16x3.argtypes = common + [i64, i64, i64, i64, vp, sz, vp]
@@ -256,6 +265,27 @@ def gemm_f32_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc, 
                                order_c, batch, stride_a, stride_b, stride_c, workspace,
                                workspace_bytes, _stream(stream))
     return _check(st, "gemm_f32_ws", raise_on_error)
+
+
+def gemm_quant(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+               c_format, c_scale=1.0, batch=1, stride_a=0, stride_b=0, stride_c=0, bias=None,
+               stride_bias=0, act=0, stream=None, raise_on_error=True):
+    """gemm_bf16_quant / gemm_f16_quant: the fused epilogue, scaled by c_scale
+    and stored as 8-bit floats of c_format ("e4m3" or "e5m2")."""
+    fn = library().gemm_bf16_quant if in_dtype == "bf16" else library().gemm_f16_quant
+    st = fn(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+            _F8_FORMAT[c_format], c_scale, batch, stride_a, stride_b, stride_c, bias, stride_bias,
+            act, _stream(stream))
+    return _check(st, "gemm_quant", raise_on_error)
+
+
+def kernel_name_quant(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+                      c_format, batch=1, stride_a=0, stride_b=0, stride_c=0):
+    """The kernel gemm_bf16_quant / gemm_f16_quant would launch, or None."""
+    name = library().gemm_kernel_name_quant(_INPUT[in_dtype], M, N, K, alpha, A, lda, order_a, B,
+                                            ldb, order_b, C, ldc, order_c, _F8_FORMAT[c_format],
+                                            batch, stride_a, stride_b, stride_c)
+    return None if name is None else name.decode()
 
 
 def bf16x3_workspace_size(M, N, K, batch=1):

@@ -700,6 +700,50 @@ gemm_status_t gemm_f32_valu(int64_t M, int64_t N, int64_t K, float alpha, const 
                nullptr, 0, true);
 }
 
+// A quantised-output call (gemm_bf16_quant / gemm_f16_quant): the canonical
+// problem with an 8-bit C and the epilogue's scale, and its kernel (the
+// 16-bit direct-load kernel, or the scale kernel when nothing is
+// multiplied).  GEMM_ERR_UNSUPPORTED for operands the direct-load kernel
+// cannot read.  No HIP call.
+gemm_status_t quant_plan(Elem in, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                         int64_t lda, int orderA, const void *B, int64_t ldb, int orderB, void *C,
+                         int64_t ldc, int orderC, gemm_f8_format_t c_format, float c_scale,
+                         int64_t batch, int64_t strideA, int64_t strideB, int64_t strideC,
+                         const void *bias, int64_t strideBias, int act, Problem &p, Kernel &k) {
+    Elem out;
+    if (!f8_type(c_format, out)) return GEMM_ERR_INVALID_ARG;
+    gemm_status_t st = plan(in, in, out, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, 0.0f, C,
+                            ldc, orderC, batch, strideA, strideB, strideC, bias, strideBias, act, p,
+                            k);
+    if (st != GEMM_OK || k == Kernel::None) return st;
+    p.epi.out_scale = c_scale;
+    p.epi.out_e5m2 = out == Elem::E5M2 ? 1 : 0;
+    if (k != Kernel::Scale) {
+        if (!hgemm_dma_eligible(p)) {
+            k = Kernel::None;
+            return GEMM_ERR_UNSUPPORTED;
+        }
+        k = Kernel::HgemmDma;
+    }
+    return GEMM_OK;
+}
+
+gemm_status_t run_quant(Elem in, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                        int64_t lda, int orderA, const void *B, int64_t ldb, int orderB, void *C,
+                        int64_t ldc, int orderC, gemm_f8_format_t c_format, float c_scale,
+                        int64_t batch, int64_t strideA, int64_t strideB, int64_t strideC,
+                        const void *bias, int64_t strideBias, int act, hipStream_t stream) {
+    Problem p;
+    Kernel k;
+    const gemm_status_t st =
+        quant_plan(in, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, C, ldc, orderC, c_format,
+                   c_scale, batch, strideA, strideB, strideC, bias, strideBias, act, p, k);
+    if (st != GEMM_OK || k == Kernel::None) return st;
+    const hipError_t e = launch(k, p, stream);
+    if (e == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 size_t gemm_f32_bf16x3_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch) {
     if (M < 0 || N < 0 || K < 0 || batch < 0 || too_big(M, K) || too_big(N, K)) return 0;
     const int64_t kp = split_kp(K);
@@ -734,6 +778,30 @@ gemm_status_t gemm_f32_bf16x3(int64_t M, int64_t N, int64_t K, float alpha, cons
     }
     if (e == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+gemm_status_t gemm_bf16_quant(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                              int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                              gemm_order_t orderB, uint8_t *C, int64_t ldc, gemm_order_t orderC,
+                              gemm_f8_format_t c_format, float c_scale, int64_t batch,
+                              int64_t strideA, int64_t strideB, int64_t strideC,
+                              const uint16_t *bias, int64_t strideBias, gemm_activation_t act,
+                              hipStream_t stream) {
+    return run_quant(Elem::BF16, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, C, ldc, orderC,
+                     c_format, c_scale, batch, strideA, strideB, strideC, bias, strideBias, act,
+                     stream);
+}
+
+gemm_status_t gemm_f16_quant(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                             int64_t lda, gemm_order_t orderA, const uint16_t *B, int64_t ldb,
+                             gemm_order_t orderB, uint8_t *C, int64_t ldc, gemm_order_t orderC,
+                             gemm_f8_format_t c_format, float c_scale, int64_t batch,
+                             int64_t strideA, int64_t strideB, int64_t strideC,
+                             const uint16_t *bias, int64_t strideBias, gemm_activation_t act,
+                             hipStream_t stream) {
+    return run_quant(Elem::F16, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, C, ldc, orderC,
+                     c_format, c_scale, batch, strideA, strideB, strideC, bias, strideBias, act,
+                     stream);
 }
 
 int gemm_test_switches(int flags) {
@@ -963,6 +1031,21 @@ const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K
         st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
                            strideC, nullptr, 0, A, B, C, workspace, workspace_bytes, w);
     return st == GEMM_OK ? kernel_name(w.k) : nullptr;
+}
+
+const char *gemm_kernel_name_quant(gemm_input_t in, int64_t M, int64_t N, int64_t K, float alpha,
+                                   const void *A, int64_t lda, gemm_order_t orderA, const void *B,
+                                   int64_t ldb, gemm_order_t orderB, const void *C, int64_t ldc,
+                                   gemm_order_t orderC, gemm_f8_format_t c_format, int64_t batch,
+                                   int64_t strideA, int64_t strideB, int64_t strideC) {
+    if (in != GEMM_INPUT_BF16 && in != GEMM_INPUT_F16) return nullptr;
+    Problem p;
+    Kernel k;
+    const gemm_status_t st =
+        quant_plan(in == GEMM_INPUT_BF16 ? Elem::BF16 : Elem::F16, M, N, K, alpha, A, lda, orderA,
+                   B, ldb, orderB, const_cast<void *>(C), ldc, orderC, c_format, 1.0f, batch,
+                   strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, p, k);
+    return st == GEMM_OK ? kernel_name(k) : nullptr;
 }
 
 const char *gemm_kernel_name_bf16x3(int64_t M, int64_t N, int64_t K, float alpha, const void *A,

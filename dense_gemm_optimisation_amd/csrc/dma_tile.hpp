@@ -40,9 +40,11 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 // element-aligned address (it splits one that straddles a cache line).
 typedef float f32x4_ea __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4_ea __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2_b1 __attribute__((ext_vector_type(2), aligned(1)));
 
 constexpr int BM = 256, BN = 256;       // block tile (rows of A and columns of B)
 constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2;
+constexpr int OUT_F8 = 3;  // E4M3 or E5M2 (Epilogue::out_e5m2), scaled and saturated
 
 struct DmaArgs {
     int64_t M, N, K;
@@ -187,10 +189,14 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
     auto at = [&](int r, int col) {     // staged float (r, col), col a multiple of 4
         return scratch + r * PITCH + ((((col >> 2) ^ (r & SWZ))) << 2);
     };
-    constexpr int CW = OUT == OUT_F32 ? 4 : 8;  // output elements per 16-byte chunk
+    constexpr int ESZ = OUT == OUT_F32 ? 4 : OUT == OUT_F8 ? 1 : 2;  // bytes per element of C
+    // output elements per store: 16 bytes, or 8 for 8-bit outputs (whose
+    // 16-element chunks need more registers than the accumulators leave)
+    constexpr int CW = OUT == OUT_F8 ? 8 : 16 / ESZ;
     constexpr int CPR = W / CW;         // chunks per row
     constexpr int RPI = 64 / CPR;       // rows per store instruction
-    char *Cb = static_cast<char *>(p.C) + batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
+    static_assert(CPR >= 1 && 32 % RPI == 0, "strip shape");
+    char *Cb = static_cast<char *>(p.C) + batch * p.sC * ESZ;
     auto dec = [](uint16_t b) {
         return OUT == OUT_BF16 ? __builtin_bit_cast(float, uint32_t(b) << 16)
                                : static_cast<float>(__builtin_bit_cast(_Float16, b));
@@ -253,50 +259,70 @@ __device__ inline void store_tile_lds(const DmaArgs &p, const f32x16 (&acc)[FM][
             }
             if (m >= p.M || n >= p.N) continue;
             const int64_t off = m * p.ldc + n;
-            if (n + CW <= p.N) {
-                if (OUT == OUT_F32) {
-                    float *c = reinterpret_cast<float *>(Cb) + off;
-                    f32x4 v = {x[0], x[1], x[2], x[3]};
-                    if (p.beta != 0.0f) {
-                        const f32x4 o = *reinterpret_cast<const f32x4_ea *>(c);
+            if constexpr (OUT == OUT_F8) {
+                // quantised: C is not read (beta is 0 for these outputs)
+                uint8_t *c = reinterpret_cast<uint8_t *>(Cb) + off;
+                u32x2_b1 w;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, o[e], v[e]);
-                    }
-                    if (epi)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = finish(v[e], i, it, e);
-                    *reinterpret_cast<f32x4_ea *>(c) = v;
+                for (int h = 0; h < 2; ++h)
+                    w[h] = epilogue_f8x2(p.epi, finish(x[4 * h], i, it, 4 * h),
+                                         finish(x[4 * h + 1], i, it, 4 * h + 1)) |
+                           (epilogue_f8x2(p.epi, finish(x[4 * h + 2], i, it, 4 * h + 2),
+                                          finish(x[4 * h + 3], i, it, 4 * h + 3)) << 16);
+                if (n + CW <= p.N) {
+                    *reinterpret_cast<u32x2_b1 *>(c) = w;
                 } else {
-                    uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off;
-                    if (p.beta != 0.0f) {
-                        const u32x4 o = *reinterpret_cast<const u32x4_ea *>(c);
+                    const int nvalid = int(p.N - n);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            x[e] = __builtin_fmaf(p.beta, dec(uint16_t(o[e / 2] >> (16 * (e % 2)))), x[e]);
-                    }
-                    if (epi)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] = finish(x[e], i, it, e);
-                    u32x4 w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = uint32_t(enc(x[2 * e])) | (uint32_t(enc(x[2 * e + 1])) << 16);
-                    *reinterpret_cast<u32x4_ea *>(c) = w;
+                    for (int e = 0; e < CW; ++e)
+                        if (e < nvalid) c[e] = uint8_t(w[e / 4] >> (8 * (e % 4)));
                 }
             } else {
-                // element by element (a loop that keeps this rare path
-                // small: unrolled, it pushes the accumulators into scratch)
-                const int nvalid = int(p.N - n);
-                for (int e = 0; e < nvalid; ++e) {
+                if (n + CW <= p.N) {
                     if (OUT == OUT_F32) {
-                        float *c = reinterpret_cast<float *>(Cb) + off + e;
-                        float v = p.beta != 0.0f ? __builtin_fmaf(p.beta, *c, x[e]) : x[e];
-                        if (epi) v = finish(v, i, it, e);
-                        *c = v;
+                        float *c = reinterpret_cast<float *>(Cb) + off;
+                        f32x4 v = {x[0], x[1], x[2], x[3]};
+                        if (p.beta != 0.0f) {
+                            const f32x4 o = *reinterpret_cast<const f32x4_ea *>(c);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, o[e], v[e]);
+                        }
+                        if (epi)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = finish(v[e], i, it, e);
+                        *reinterpret_cast<f32x4_ea *>(c) = v;
                     } else {
-                        uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off + e;
-                        float v = p.beta != 0.0f ? __builtin_fmaf(p.beta, dec(*c), x[e]) : x[e];
-                        if (epi) v = finish(v, i, it, e);
-                        *c = enc(v);
+                        uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off;
+                        if (p.beta != 0.0f) {
+                            const u32x4 o = *reinterpret_cast<const u32x4_ea *>(c);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                x[e] = __builtin_fmaf(p.beta, dec(uint16_t(o[e / 2] >> (16 * (e % 2)))), x[e]);
+                        }
+                        if (epi)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[e] = finish(x[e], i, it, e);
+                        u32x4 w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = uint32_t(enc(x[2 * e])) | (uint32_t(enc(x[2 * e + 1])) << 16);
+                        *reinterpret_cast<u32x4_ea *>(c) = w;
+                    }
+                } else {
+                    // element by element (a loop that keeps this rare path
+                    // small: unrolled, it pushes the accumulators into scratch)
+                    const int nvalid = int(p.N - n);
+                    for (int e = 0; e < nvalid; ++e) {
+                        if (OUT == OUT_F32) {
+                            float *c = reinterpret_cast<float *>(Cb) + off + e;
+                            float v = p.beta != 0.0f ? __builtin_fmaf(p.beta, *c, x[e]) : x[e];
+                            if (epi) v = finish(v, i, it, e);
+                            *c = v;
+                        } else {
+                            uint16_t *c = reinterpret_cast<uint16_t *>(Cb) + off + e;
+                            float v = p.beta != 0.0f ? __builtin_fmaf(p.beta, dec(*c), x[e]) : x[e];
+                            if (epi) v = finish(v, i, it, e);
+                            *c = enc(v);
+                        }
                     }
                 }
             }

@@ -25,6 +25,12 @@ struct Epilogue {
     int per_row = 0;             // bias indexed by the kernel's row (else its column)
     int bias_type = 0;           // element type of the bias: 0 fp32, 1 bf16, 2 fp16
     int act = ACT_NONE;
+    // 8-bit (quantised) output: the value is multiplied by out_scale and
+    // stored as OCP E4M3 (out_e5m2 = 0) or E5M2, rounded to nearest even and
+    // saturated (magnitudes beyond the largest finite value, infinities
+    // included, store that value; NaN stores a NaN).
+    float out_scale = 1.0f;
+    int out_e5m2 = 0;
 
     __host__ __device__ bool active() const { return bias != nullptr || act != ACT_NONE; }
 };
@@ -68,6 +74,24 @@ __device__ inline float epilogue_apply(const Epilogue &e, float v, int64_t batch
                                        int64_t col) {
     if (e.bias != nullptr) v += epilogue_bias(e, batch, e.per_row ? row : col);
     return epilogue_act(e.act, v);
+}
+
+// Quantisation of the epilogue's values for an 8-bit output: the epilogue
+// section of "GPU GEMM 优化完全拆解（三）" (pinghaoyang.com.cn) does the
+// quantisation scaling in the write-back.  v * out_scale is clamped to the
+// format's largest finite magnitude (448 for E4M3, 57344 for E5M2; a NaN
+// passes through) and converted by the matrix cores' companion instruction,
+// which rounds to nearest even: two values into bytes 0 and 1 of the result.
+__device__ inline uint32_t epilogue_f8x2(const Epilogue &e, float v0, float v1) {
+    const float maxf = e.out_e5m2 ? 57344.0f : 448.0f;
+    auto clamp = [&](float x) {
+        x *= e.out_scale;
+        return x > maxf ? maxf : (x < -maxf ? -maxf : x);
+    };
+    const float a = clamp(v0), b = clamp(v1);
+    const int r = e.out_e5m2 ? __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false)
+                             : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return static_cast<uint32_t>(r) & 0xffffu;
 }
 
 // The bias of element `i` of the vector (a row or a column index of the

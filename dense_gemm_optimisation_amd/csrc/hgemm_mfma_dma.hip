@@ -667,6 +667,9 @@ hipError_t launch_hgemm_dma(const Problem &p, hipStream_t stream) {
     DmaArgs a = make_dma_args(p, 8);
     if (a.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool bf = p.in == Elem::BF16;
+    if (elem_is_8bit(p.out))
+        return bf ? launch_layout<BF16, OUT_F8>(p, a, stream)
+                  : launch_layout<F16, OUT_F8>(p, a, stream);
     if (p.out == Elem::F32)
         return bf ? launch_layout<BF16, OUT_F32>(p, a, stream)
                   : launch_layout<F16, OUT_F32>(p, a, stream);

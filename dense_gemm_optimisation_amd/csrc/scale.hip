@@ -16,6 +16,11 @@ struct ScaleArgs {
     Epilogue epi;
 };
 
+__device__ inline bool out_is_8bit(int out) {
+    return out == static_cast<int>(Elem::E4M3) || out == static_cast<int>(Elem::E5M2);
+}
+
+// (8-bit outputs are quantised results and are never read: beta is 0 for them)
 __device__ inline float load_elem(const void *c, int64_t i, int out) {
     if (out == static_cast<int>(Elem::F32)) return static_cast<const float *>(c)[i];
     const uint16_t bits = static_cast<const uint16_t *>(c)[i];
@@ -43,7 +48,10 @@ __global__ __launch_bounds__(256) void scale_kernel(ScaleArgs a) {
         const int64_t off = b * a.sC + i * a.ldc + j;
         float v = a.beta == 0.0f ? 0.0f : a.beta * load_elem(a.C, off, a.out);
         if (a.epi.active()) v = epilogue_apply(a.epi, v, b, i, j);
-        store_elem(a.C, off, a.out, v);
+        if (out_is_8bit(a.out))
+            static_cast<uint8_t *>(a.C)[off] = uint8_t(epilogue_f8x2(a.epi, v, 0.0f));
+        else
+            store_elem(a.C, off, a.out, v);
     }
 }
 

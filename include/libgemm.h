@@ -24,6 +24,8 @@
  *   gemm_f32_bias_act, gemm_bf16_bias_act, gemm_f16_bias_act
  *              the same products with a fused epilogue: a per-column bias
  *              and an activation applied before the store (see below).
+ *   gemm_bf16_quant, gemm_f16_quant  the fused epilogue followed by a
+ *              scale and a saturating store as 8-bit floats (E4M3/E5M2).
  *   gemm_f8    8-bit float inputs (OCP E4M3 or E5M2, each operand in its own
  *              format), fp32 accumulation, output in fp32, bf16 or fp16.
  *   gemm_mx    block-scaled inputs (MXFP8, MXFP6, MXFP4: one E8M0 scale per
@@ -35,7 +37,8 @@
  *              gemm_workspace_size gives the bytes it needs.
  *   gemm_bf16_noalloc  gemm_bf16_ws on the library's own scratch memory.
  *   gemm_kernel_name, gemm_f8_kernel_name, gemm_mx_kernel_name,
- *   gemm_kernel_name_ws, gemm_kernel_name_bf16x3  which kernel
+ *   gemm_kernel_name_ws, gemm_kernel_name_bf16x3, gemm_kernel_name_quant
+ *              which kernel
  *              a GEMM call with the
  *              given arguments would launch (host only; for tests and
  *              profiling).
@@ -236,6 +239,45 @@ gemm_status_t gemm_f16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
                                 int64_t strideC, const uint16_t *bias,
                                 int64_t strideBias, gemm_activation_t act,
                                 hipStream_t stream);
+
+/* Quantised output: the fused epilogue above, then scaled and stored as
+ * 8-bit floats.  The pages do quantisation scaling in the epilogue's
+ * write-back ("GPU GEMM 优化完全拆解（三）", pinghaoyang.com.cn, section on
+ * mainloop and epilogue) and list quantised (INT8/INT4/FP8) GEMMs among the
+ * uses of a customisable epilogue ("第4章：经典算子实现 —— GEMM",
+ * aiinfra.vidrealm.tech, section 7.2).  For each element of C:
+ *   C <- Q(c_scale * act(alpha * op(A) * op(B) + bias))
+ * computed in fp32, where Q rounds to the nearest value of c_format (OCP
+ * E4M3 or E5M2, ties to even) and saturates: magnitudes beyond the largest
+ * finite value (448, resp. 57344), infinities included, store that value
+ * with their sign; a NaN stores a NaN pattern.  C holds one byte per element
+ * (uint8_t, its leading dimension and strides in elements); C is never read
+ * (there is no beta).  bias, strideBias and act are as for the _bias_act
+ * calls (bias of the input type, or NULL).  The product runs on the 16-bit
+ * direct-load kernel: operands it cannot read whole 16-byte chunks of (base,
+ * leading dimension or stride not 16-byte aligned, contiguous extent not a
+ * multiple of 8, a slice of 1 GiB or more) give GEMM_ERR_UNSUPPORTED before
+ * anything is launched.  With alpha == 0 or K == 0 the result is
+ * Q(c_scale * act(bias)).  A c_format out of range is GEMM_ERR_INVALID_ARG;
+ * all other arguments, layouts, batch rules, ownership and errors are those of
+ * gemm_bf16 / gemm_f16. */
+gemm_status_t gemm_bf16_quant(int64_t M, int64_t N, int64_t K, float alpha,
+                              const uint16_t *A, int64_t lda, gemm_order_t orderA,
+                              const uint16_t *B, int64_t ldb, gemm_order_t orderB,
+                              uint8_t *C, int64_t ldc, gemm_order_t orderC,
+                              gemm_f8_format_t c_format, float c_scale, int64_t batch,
+                              int64_t strideA, int64_t strideB, int64_t strideC,
+                              const uint16_t *bias, int64_t strideBias,
+                              gemm_activation_t act, hipStream_t stream);
+
+gemm_status_t gemm_f16_quant(int64_t M, int64_t N, int64_t K, float alpha,
+                             const uint16_t *A, int64_t lda, gemm_order_t orderA,
+                             const uint16_t *B, int64_t ldb, gemm_order_t orderB,
+                             uint8_t *C, int64_t ldc, gemm_order_t orderC,
+                             gemm_f8_format_t c_format, float c_scale, int64_t batch,
+                             int64_t strideA, int64_t strideB, int64_t strideC,
+                             const uint16_t *bias, int64_t strideBias,
+                             gemm_activation_t act, hipStream_t stream);
 
 /* 8-bit float GEMM: C <- alpha * op(A) * op(B) + beta * C with A and B
  * holding E4M3 or E5M2 bit patterns (formatA, formatB; the two may differ),
@@ -573,6 +615,18 @@ const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K
                                 gemm_dtype_t c_dtype, int64_t batch,
                                 int64_t strideA, int64_t strideB, int64_t strideC,
                                 const void *workspace, size_t workspace_bytes);
+
+/* The kernel gemm_bf16_quant (in = GEMM_INPUT_BF16) or gemm_f16_quant
+ * (GEMM_INPUT_F16) would launch: "hgemm_mfma_dma", "scale" when nothing is
+ * multiplied, "" for an empty problem, NULL for invalid arguments or a
+ * problem the call would reject as GEMM_ERR_UNSUPPORTED.  No HIP call. */
+const char *gemm_kernel_name_quant(gemm_input_t in, int64_t M, int64_t N, int64_t K,
+                                   float alpha, const void *A, int64_t lda,
+                                   gemm_order_t orderA, const void *B, int64_t ldb,
+                                   gemm_order_t orderB, const void *C, int64_t ldc,
+                                   gemm_order_t orderC, gemm_f8_format_t c_format,
+                                   int64_t batch, int64_t strideA, int64_t strideB,
+                                   int64_t strideC);
 
 /* The bf16 kernel gemm_f32_bf16x3 would run on the split copies (one of the
  * names of gemm_kernel_name for 16-bit inputs), "scale" or "" when nothing is

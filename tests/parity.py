@@ -145,6 +145,8 @@ def compare(p, got_bits: np.ndarray, ref: np.ndarray, den: np.ndarray, name: str
             res.why = f"max normalised error {res.max_err:.3e} > {tol:g} at flat {k}: " \
                       f"got {got.ravel()[k]!r} ref {ref.ravel()[k]!r} den {den.ravel()[k]!r}"
         return res
+    if out in workloads.EIGHT_BIT:
+        return compare8(p, got_bits, ref, den, name, res)
     ref_q = oracle.round_bits(out, ref)
     d = np.abs(ulp_keys(got_bits) - ulp_keys(ref_q))
     res.max_ulp = int(d.max()) if d.size else 0
@@ -168,6 +170,49 @@ def compare(p, got_bits: np.ndarray, ref: np.ndarray, den: np.ndarray, name: str
     zero = den == 0
     if np.any(zero & (ulp_keys(got_bits) != ulp_keys(ref_q))):
         res.ok, res.why = False, "den == 0 but result differs from ref"
+    return res
+
+
+def keys8(bits):
+    """8-bit sign-magnitude patterns as integers that step by one per
+    representable value (+0 and -0 both 0)."""
+    b = np.asarray(bits).astype(np.int64) & 0xFF
+    return np.where(b & 0x80, -(b & 0x7F), b & 0x7F)
+
+
+def compare8(p, got_bits, ref, den, name, res):
+    """8-bit (quantised) output against the oracle's exact value ref (already
+    scaled).  The kernel rounds its fp32 value, which is within the 16-bit
+    inputs' fp32 error of ref; rounding that to the format can differ from
+    rounding ref only where ref lies near the middle of two neighbours: at
+    most one step (ulp) apart, and NaN exactly where ref is NaN.  As for
+    16-bit outputs, an element under cancellation (|ref| <= 2^-8 den) may
+    instead be within one ulp plus 1e-3 den of ref."""
+    out = p.c_dtype
+    got_bits = np.asarray(got_bits).astype(np.uint8)
+    got = oracle.decode(out, got_bits)
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    if np.any(nan_ref != nan_got):
+        k = int(np.argmax(nan_ref != nan_got))
+        res.ok, res.why = False, f"NaN mismatch at flat {k}: got {got.ravel()[k]!r} ref {ref.ravel()[k]!r}"
+        return res
+    ok = ~nan_ref
+    ref_q = oracle.round_bits(out, ref[ok])
+    d = np.abs(keys8(got_bits[ok]) - keys8(ref_q))
+    res.max_ulp = int(d.max()) if d.size else 0
+    bad = d > 1
+    res.strict_fail = int(bad.sum())
+    if res.strict_fail:
+        qv = oracle.decode(out, ref_q)
+        step = np.abs(oracle.decode(out, (ref_q.astype(np.int64) + 1).astype(np.uint8)) - qv)
+        ok_exempt = (np.abs(got[ok] - ref[ok]) <= step + 1e-3 * den[ok]) & \
+            (np.abs(ref[ok]) <= 2.0 ** -8 * den[ok])
+        res.exempt = int((bad & ok_exempt).sum())
+        if res.exempt != res.strict_fail:
+            res.ok = False
+            k = int(np.argmax(bad & ~ok_exempt))
+            res.why = (f"{res.strict_fail - res.exempt} elements beyond 1 ulp; e.g. flat {k}: "
+                       f"got {got[ok][k]!r} ref {ref[ok][k]!r} den {den[ok][k]!r}")
     return res
 
 
@@ -232,7 +277,7 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         dbias, fbias, sbias = _device(bias, p.in_dtype)
     esz_in = np.dtype(STORE[p.in_dtype]).itemsize
     esz_b = np.dtype(STORE[p.b_dtype]).itemsize
-    esz_out = 4 if p.c_dtype == "f32" else 2
+    esz_out = {"f32": 4, "e4m3": 1, "e5m2": 1}.get(p.c_dtype, 2)
     pa, pb, pc = (da.data_ptr() + sa * esz_in, db.data_ptr() + sb * esz_b,
                   dc.data_ptr() + sc * esz_out)
     pbias = dbias.data_ptr() + sbias * esz_in if bias is not None else None
@@ -242,7 +287,7 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         w = workspace()
         ws = dict(workspace=w.data_ptr(),
                   workspace_bytes=w.numel() * 4 if workspace_bytes is None else workspace_bytes)
-    cview = np.int32 if p.c_dtype == "f32" else np.int16
+    cview = {"f32": np.int32, "e4m3": np.int8, "e5m2": np.int8}.get(p.c_dtype, np.int16)
     kernel = binding.kernel_name(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb,
                                  p.ldb, p.order_b, p.beta, pc, p.ldc, p.order_c, c_dt, p.batch,
                                  p.stride_a, p.stride_b, p.stride_c, b_dtype=p.b_dtype,
@@ -250,6 +295,12 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
     valu = p.entry == "valu"  # gemm_f32_valu runs the vector-ALU kernel whatever the shape
     if valu and kernel not in ("", "scale", None):
         kernel = "sgemm_valu"
+    quant = p.entry == "quant"
+    if quant:
+        kernel = binding.kernel_name_quant(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda,
+                                           p.order_a, pb, p.ldb, p.order_b, pc, p.ldc, p.order_c,
+                                           p.c_dtype, p.batch, p.stride_a, p.stride_b,
+                                           p.stride_c)
     x3 = {}
     if p.entry == "bf16x3":  # gemm_f32_bf16x3, with a workspace of its own
         n = binding.bf16x3_workspace_size(p.M, p.N, p.K, p.batch)
@@ -263,7 +314,12 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
     for r in range(repeat):
         if r:
             dc.copy_(torch.from_numpy(fc.view(cview)))
-        if x3:
+        if quant:
+            binding.gemm_quant(p.in_dtype, p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
+                               p.order_b, pc, p.ldc, p.order_c, p.c_dtype, p.c_scale, p.batch,
+                               p.stride_a, p.stride_b, p.stride_c, bias=pbias,
+                               stride_bias=p.stride_bias or 0, act=p.act)
+        elif x3:
             binding.gemm_f32_bf16x3(p.M, p.N, p.K, p.alpha, pa, p.lda, p.order_a, pb, p.ldb,
                                     p.order_b, p.beta, pc, p.ldc, p.order_c, p.batch,
                                     p.stride_a, p.stride_b, p.stride_c, **x3)
@@ -294,19 +350,24 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
         return res, out
     kw = dict(stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c, bias=bias,
               stride_bias=p.stride_bias, act=p.act, b_dtype=p.b_dtype)
+    odt, oc0 = p.c_dtype, c0
+    if quant:  # no beta: the oracle's fp64 value, scaled, against the 8-bit rounding
+        odt, oc0 = "f32", np.zeros(c0.size, np.float32)
     if sample is None:
-        ref, den = oracle.gemm(p.in_dtype, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda, p.order_a,
-                               b, p.ldb, p.order_b, p.beta, c0, p.ldc, p.order_c, batch=p.batch,
-                               **kw)
+        ref, den = oracle.gemm(p.in_dtype, odt, p.M, p.N, p.K, p.alpha, a, p.lda, p.order_a,
+                               b, p.ldb, p.order_b, 0.0 if quant else p.beta, oc0, p.ldc,
+                               p.order_c, batch=p.batch, **kw)
         bb, ii, jj = np.meshgrid(np.arange(p.batch), np.arange(p.M), np.arange(p.N),
                                  indexing="ij")
     else:
         idx = default_sample(p, np.random.default_rng(1234)) if isinstance(sample, str) else sample
-        ref, den = oracle.gemm_at(p.in_dtype, p.c_dtype, p.M, p.N, p.K, p.alpha, a, p.lda,
-                                  p.order_a, b, p.ldb, p.order_b, p.beta, c0, p.ldc, p.order_c,
-                                  idx, **kw)
+        ref, den = oracle.gemm_at(p.in_dtype, odt, p.M, p.N, p.K, p.alpha, a, p.lda,
+                                  p.order_a, b, p.ldb, p.order_b, 0.0 if quant else p.beta, oc0,
+                                  p.ldc, p.order_c, idx, **kw)
         bb, ii, jj = idx[:, 0], idx[:, 1], idx[:, 2]
     got = out[sc + offsets(p, "c", bb, ii, jj)]
+    if quant:
+        ref, den = p.c_scale * ref, abs(p.c_scale) * den
     res = compare(p, got, ref, den, p.name)
     res.kernel = kernel
     log(f"[parity]   -> {kernel} ok={res.ok} max_err={res.max_err:.3e} max_ulp={res.max_ulp} "

@@ -28,14 +28,16 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["gemm_abi_version", "gemm_bf16", "gemm_bf16_bias_act",
-                                    "gemm_bf16_noalloc", "gemm_bf16_ws", "gemm_f16",
+                                    "gemm_bf16_noalloc", "gemm_bf16_quant", "gemm_bf16_ws",
+                                    "gemm_f16",
                                     "gemm_f16_bias_act",
+                                    "gemm_f16_quant",
                                     "gemm_f16_ws", "gemm_f32", "gemm_f32_bf16x3",
                                     "gemm_f32_bf16x3_workspace_size", "gemm_f32_bias_act",
                                     "gemm_f32_valu", "gemm_f32_ws",
                                     "gemm_f8",
                                     "gemm_f8_kernel_name", "gemm_kernel_name",
-                                    "gemm_kernel_name_bf16x3",
+                                    "gemm_kernel_name_bf16x3", "gemm_kernel_name_quant",
                                     "gemm_kernel_name_ws", "gemm_mx", "gemm_mx_kernel_name",
                                     "gemm_status_string",
                                     "gemm_test_switches", "gemm_workspace_size"]
@@ -392,6 +394,7 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_edge": "hgemm_mfma", "bf16_tail": "hgemm_mfma_dma", "bf16_skinny": "gemm_skinny",
             "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma",
             "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma",
+            "bf16_ffn_up_gelu_e4m3": "hgemm_mfma_dma",
             # called through gemm_f32_valu and gemm_f32_bf16x3; gemm_kernel_name
             # describes gemm_f32
             "f32_4096_valu": "sgemm_mfma_dma", "f32_4096_bf16x3": "sgemm_mfma_dma"}
@@ -619,3 +622,51 @@ def test_bf16x3_invalid_workspace(lib):
     assert kname_x3(lib, 520, 520, 200, batch=4, sa=0, nbytes=need) is not None
     assert kname_x3(lib, 520, 520, 200, batch=4, sa=0, nbytes=need - 1) is None
     assert kname_x3(lib, 520, 520, 200, batch=4, nbytes=need) is None
+
+
+# ------------------------------------------------------------------ quantised (8-bit) output
+
+def kname_q(lib, dt, M, N, K, fmt="e4m3", **kw):
+    oa, ob, oc = kw.pop("oa", 0), kw.pop("ob", 0), kw.pop("oc", 0)
+    lda = kw.pop("lda", K if oa == 0 else M)
+    ldb = kw.pop("ldb", N if ob == 0 else K)
+    ldc = kw.pop("ldc", N if oc == 0 else M)
+    return lib.kernel_name_quant(dt, M, N, K, kw.pop("alpha", 1.0), kw.pop("A", GB), lda, oa,
+                                 kw.pop("B", 2 * GB), ldb, ob, kw.pop("C", 3 * GB), ldc, oc, fmt,
+                                 kw.pop("batch", 1), kw.pop("sa", 0), kw.pop("sb", 0),
+                                 kw.pop("sc", 0))
+
+
+def test_quant_kernel_choice(lib, clean_env):
+    # always the 16-bit direct-load kernel (no split-K or skinny variant of
+    # the 8-bit store), in any order; the scale kernel when nothing is multiplied
+    assert kname_q(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"
+    assert kname_q(lib, "f16", 4096, 4096, 4096, "e5m2", oa=1, ob=1, oc=1) == "hgemm_mfma_dma"
+    assert kname_q(lib, "bf16", 16, 4096, 4096) == "hgemm_mfma_dma"
+    assert kname_q(lib, "bf16", 256, 256, 8192) == "hgemm_mfma_dma"
+    # C needs no alignment (bytes; ldc = 4095)
+    assert kname_q(lib, "bf16", 4096, 4095, 4096, ob=1, C=3 * GB + 1) == "hgemm_mfma_dma"
+    assert kname_q(lib, "bf16", 4096, 4096, 4096, alpha=0.0) == "scale"
+    assert kname_q(lib, "bf16", 4096, 4096, 0, lda=1) == "scale"
+    assert kname_q(lib, "bf16", 0, 4096, 4096) == ""
+
+
+def test_quant_unsupported_and_invalid(lib):
+    # operands the direct-load kernel cannot read: GEMM_ERR_UNSUPPORTED, before
+    # any HIP call (so these calls are safe without a GPU)
+    def call(**kw):
+        oa, ob = kw.pop("oa", 0), kw.pop("ob", 0)
+        M, N, K = kw.pop("M", 4096), kw.pop("N", 4096), kw.pop("K", 4096)
+        return lib.gemm_quant(kw.pop("dt", "bf16"), M, N, K, 1.0, kw.pop("A", GB),
+                              kw.pop("lda", K if oa == 0 else M), oa, 2 * GB,
+                              kw.pop("ldb", N if ob == 0 else K), ob, 3 * GB, N, 0,
+                              kw.pop("fmt", "e4m3"), 1.0, raise_on_error=False)
+    assert call(A=GB + 2) == -2                      # A not 16-byte aligned
+    assert call(lda=4100) == -2                      # rows not 16-byte aligned
+    assert call(K=4095, lda=4095) == -2              # K-contiguous extent not a multiple of 8
+    assert call(dt="f16", oa=1, M=4095, lda=4095) == -2
+    assert kname_q(lib, "bf16", 4096, 4096, 4096, A=GB + 2) is None
+    assert call(lda=100) == -1                       # lda < K
+    assert lib.library().gemm_bf16_quant(64, 64, 64, 1.0, GB, 64, 0, 2 * GB, 64, 0, 3 * GB, 64, 0,
+                                         7, 1.0, 1, 0, 0, 0, None, 0, 0, None) == -1  # bad format
+    assert call(dt="f16", fmt="e5m2", oa=1, ob=1, M=4095, N=4095, lda=4095) == -2

@@ -200,7 +200,7 @@ def test_repeat_runs_bit_identical(dt):
 SMALL_CONFIGS = ["f32_256"]
 FULL_CONFIGS = ["f32_4096", "bf16_4096", "f16_4096", "f32_edge", "bf16_edge", "bf16_tail", "bf16_skinny",
                 "bf16_attn_qk", "bf16_attn_pv", "bf16_qkv", "bf16_ffn_up", "bf16_ffn_down",
-                "bf16_ffn_up_gelu", "fp8_4096"]
+                "bf16_ffn_up_gelu", "bf16_ffn_up_gelu_e4m3", "fp8_4096"]
 
 
 @pytest.mark.parametrize("name", SMALL_CONFIGS)
@@ -1053,6 +1053,81 @@ def test_mx_alpha_zero_and_k_zero_scale_c():
 @pytest.mark.parametrize("name", ["mxfp4_4096", "mxfp6_4096", "mxfp8_4096"])
 def test_mx_full_size_sampled(name):
     check_mx(workloads.config(name), sample="auto")
+
+
+# ------------------------------------------------------------------ quantised (8-bit) output
+
+QUANT_SHAPES = [(8, 8, 8), (256, 256, 64), (264, 520, 72), (1000, 1032, 1000), (24, 4096, 512)]
+
+
+@pytest.mark.parametrize("fmt,scale", [("e4m3", 0.5), ("e5m2", 64.0)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", QUANT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)],
+                         ids=["nn", "nt", "tn", "tt"])
+def test_quant_output(fmt, scale, dt, shape, orders):
+    M, N, K = shape
+    oa, ob = orders
+    res, _ = check(P(f"quant-{dt}-{fmt}", dt, M, N, K, c_dtype=fmt, alpha=0.75, beta=0.0,
+                     order_a=oa, order_b=ob, entry="quant", c_scale=scale),
+                   kernel="hgemm_mfma_dma", seed=M + N + K)
+    assert res.max_ulp <= 1
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quant_output_epilogue_layouts_batches(fmt):
+    for act, name in [(GELU, "gelu"), (RELU, "relu")]:
+        check(P(f"quant-{name}", "bf16", 520, 264, 200, c_dtype=fmt, beta=0.0, bias=True, act=act,
+                entry="quant", c_scale=2.0), kernel="hgemm_mfma_dma", seed=61 + act)
+    check(P("quant-colC", "f16", 264, 520, 200, c_dtype=fmt, beta=0.0, order_c=COL, bias=True,
+            act=GELU, entry="quant", c_scale=0.25), kernel="hgemm_mfma_dma", seed=63)
+    check(P("quant-batch", "bf16", 264, 136, 200, c_dtype=fmt, beta=0.0, batch=3, bias=True,
+            stride_bias=0, entry="quant", c_scale=1.0), kernel="hgemm_mfma_dma", seed=64)
+    # a scale that sends most values past the largest finite one (saturation)
+    # and one that sends most below the smallest normal (subnormals and zeros)
+    check(P("quant-saturate", "bf16", 264, 264, 256, c_dtype=fmt, beta=0.0, entry="quant",
+            c_scale=1e5), kernel="hgemm_mfma_dma", seed=65)
+    check(P("quant-tiny", "bf16", 264, 264, 256, c_dtype=fmt, beta=0.0, entry="quant",
+            c_scale=2.0 ** -18), kernel="hgemm_mfma_dma", seed=66)
+
+
+def test_quant_output_integers_exact():
+    # small integers: the fp32 result is exact, so its rounding is the oracle's
+    for fmt in ["e4m3", "e5m2"]:
+        p = P(f"quant-int-{fmt}", "bf16", 520, 264, 264, c_dtype=fmt, alpha=1.0, beta=0.0,
+              entry="quant", c_scale=0.5)
+        a, b, _ = _int_host(p, np.random.default_rng(67), -4, 4)
+        res, _ = check(p, kernel="hgemm_mfma_dma", repeat=2,
+                       host=(a, b, np.zeros(p.buffer_elems("c"), np.uint8)))
+        assert res.max_ulp == 0
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quant_rounding_is_exact_at_every_midpoint(fmt):
+    # alpha = 0: C = Q(c_scale * bias).  The bias holds every finite value of
+    # the format, every midpoint between neighbours (ties: to even), a hair
+    # either side of each midpoint, values past the largest finite one,
+    # infinities and NaN; all are bf16 values, the scale is 1, so the fp32
+    # input of the conversion is exact and the result must equal the
+    # oracle's rounding bit for bit.
+    vals = oracle.decode(fmt, np.arange(128, dtype=np.uint8))
+    v = vals[np.isfinite(vals)]
+    mids = (v[:-1] + v[1:]) / 2
+    gap = v[1:] - v[:-1]
+    cand = np.concatenate([v, mids, mids - gap / 64, mids + gap / 64,
+                           [v[-1] * 2, v[-1] * 4, 2.0 ** 100, np.inf, np.nan]])
+    cand = np.concatenate([cand, -cand])
+    # keep the values bf16 holds exactly
+    bf = workloads.to_16bit(cand.astype(np.float32), "bf16")
+    exact = oracle.decode("bf16", bf)
+    keep = np.isnan(cand) | (exact == cand)
+    bias = bf[keep]
+    n = bias.size
+    p = P(f"quant-midpoints-{fmt}", "bf16", 8, n, 16, c_dtype=fmt, alpha=0.0, beta=0.0, bias=True,
+          entry="quant", c_scale=1.0)
+    res, out = check(p, kernel="scale", bias_host=bias)
+    assert res.max_ulp == 0 and res.strict_fail == 0
+    assert n > 400 and np.isnan(oracle.decode("bf16", bias)).sum() == 2
 
 
 # ------------------------------------------------------------------ fp32 as three bf16 products

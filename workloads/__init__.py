@@ -85,7 +85,9 @@ class Problem:
     sigma_bias: float = 1.0
     act: int = 0                     # 0 none, 1 ReLU, 2 GELU
     b_dtype: Optional[str] = None    # type of B when it differs from A's (8-bit floats)
-    entry: str = ""                  # "valu": gemm_f32_valu; "bf16x3": gemm_f32_bf16x3
+    entry: str = ""                  # "valu": gemm_f32_valu; "bf16x3": gemm_f32_bf16x3;
+                                     # "quant": gemm_bf16_quant / gemm_f16_quant (8-bit C)
+    c_scale: float = 1.0             # "quant": the scale applied before the 8-bit store
 
     def __post_init__(self):
         M, N, K = self.M, self.N, self.K
@@ -421,6 +423,13 @@ def _configs():
         Problem("bf16_ffn_up_gelu", "bf16", "bf16", 4096, 16384, 4096, sigma_b=0.02,
                 bias=True, act=2,
                 note="FFN up X(4096x4096) W1(4096x16384) + b1 then GELU, fused epilogue"),
+        # the same layer with its output quantised to E4M3 in the epilogue
+        # (scale 16: GELU outputs of N(0, 0.02^2 * 4096) sums land well inside
+        # the format's range)
+        Problem("bf16_ffn_up_gelu_e4m3", "bf16", "e4m3", 4096, 16384, 4096, sigma_b=0.02,
+                bias=True, act=2, entry="quant", c_scale=16.0,
+                note="FFN up X(4096x4096) W1(4096x16384) + b1, GELU, x16 and E4M3 output, "
+                     "fused epilogue"),
         # 8-bit float inputs in the layout 8-bit GEMMs take: A row-major and B
         # column-major (both contiguous along K), output bf16
         # block-scaled formats (one E8M0 scale per 32 k), K contiguous in
