@@ -317,6 +317,15 @@ def error_stats(p, got_bits, ref, den):
     8-bit inputs, whose instruction truncates small products, only the
     second condition)."""
     import oracle
+    import workloads
+    if p.c_dtype in workloads.EIGHT_BIT:  # quantised output: steps of the 8-bit format
+        q = oracle.round_bits(p.c_dtype, ref).astype(np.int64)
+        g = got_bits.view(np.uint8).astype(np.int64)
+        key = lambda b: np.where(b & 0x80, -(b & 0x7F), b & 0x7F)
+        both_nan = np.isnan(oracle.decode(p.c_dtype, g.astype(np.uint8))) & np.isnan(ref)
+        d = np.where(both_nan, 0, np.abs(key(g) - key(q)))
+        return {"max_ulp": int(d.max()), "beyond_1ulp": int((d > 1).sum()),
+                "elements": int(ref.size)}
     with np.errstate(divide="ignore", invalid="ignore"):
         if p.c_dtype == "f32":
             got = got_bits.view(np.float32).astype(np.float64)
@@ -382,6 +391,8 @@ def cpu_baseline(problems, budget_s, gpu_results):
                                       stride_c=p.stride_c, bias=workloads.bias_vector(p),
                                       stride_bias=p.stride_bias, act=p.act, b_dtype=p.b_dtype)
         dt = time.perf_counter() - t0
+        if getattr(p, "entry", "") == "quant":  # stored: the epilogue's value times the scale
+            ref, den = p.c_scale * ref, abs(p.c_scale) * den
         flop = 2.0 * r * p.N * p.K
         total_flop += flop
         total_t += dt
@@ -520,7 +531,7 @@ def main():
             nsets[p.name] = len(sets)
             pws = ws if (ws is not None and not is_mx(p) and p.in_dtype in ("f32", "bf16", "f16")
                          and not p.bias and not p.act and not p.entry) else None
-            if p.entry == "bf16x3":  # its own workspace, for the split copies
+            if getattr(p, "entry", "") == "bf16x3":  # its own workspace, for the split copies
                 pws = torch.empty(binding.bf16x3_workspace_size(p.M, p.N, p.K, p.batch) // 4,
                                   dtype=torch.int32, device="cuda")
             families[p.name] = kernel_family(p, bufs, pws)
