@@ -16,9 +16,9 @@ Each kernel cycles through at least three copies of its buffers, enough that
 their footprint exceeds twice the 256 MB MALL, so inputs come from HBM;
 --no-rotate reuses one set (the warm-cache figure).
 --workload runs the named workload, or a comma-separated list of them (see
-workloads.CONFIGS), instead of the headline step, for profiling.  --workspace runs fp32/bf16/fp16 workloads
-through the workspace entry points, which use the stream-K schedule where
-it applies.  --copy-calibration runs only a plain
+workloads.CONFIGS), instead of the headline step, for profiling.  --workspace
+runs the workloads without a fused epilogue through the workspace entry
+points, which use the stream-K schedule where it applies.  --copy-calibration runs only a plain
 device-to-device copy of the given size (the reference kernel against which
 the HBM byte counters FETCH_SIZE / WRITE_SIZE are scaled).
 
@@ -75,6 +75,8 @@ KERNEL_SOURCE = {"sgemm_mfma_dma": "sgemm_mfma.hip", "sgemm_mfma": "sgemm_mfma.h
                  "sgemm_mfma_dma_streamk": "sgemm_mfma.hip",
                  "sgemm_mfma_dma_streamk_packed": "sgemm_mfma.hip",
                  "mxgemm_mfma_dma": "mxgemm.hip",
+                 "f8gemm_mfma_dma_streamk": "f8gemm_mfma.hip",
+                 "mxgemm_mfma_dma_streamk": "mxgemm.hip",
                  "gemm_skinny_splitk": "gemm_skinny.hip",
                  "scale": "scale.hip"}
 
@@ -154,7 +156,7 @@ def make_launch(p, sets, stream, bias=None, workspace=None):
     workspace entry point when a workspace tensor is given)."""
     from dense_gemm_optimisation_amd import binding
     if is_mx(p):
-        return make_mx_launch(p, sets, stream)
+        return make_mx_launch(p, sets, stream, workspace)
     c_dt = binding.DTYPE_F32 if (p.c_dtype == "f32" and p.in_dtype != "f32") else binding.DTYPE_SAME
     argsets = [(p.in_dtype, p.M, p.N, p.K, p.alpha, da.data_ptr(), p.lda, p.order_a, db.data_ptr(),
                 p.ldb, p.order_b, p.beta, dc.data_ptr(), p.ldc, p.order_c, c_dt, p.batch,
@@ -201,14 +203,19 @@ def mx_args(p, bufs, stream=0):
             p.stride_sa, p.stride_sb, p.stride_c)
 
 
-def make_mx_launch(p, sets, stream):
-    """make_launch for a block-scaled workload (gemm_mx)."""
+def make_mx_launch(p, sets, stream, workspace=None):
+    """make_launch for a block-scaled workload (gemm_mx, or gemm_mx_ws with
+    a workspace tensor)."""
     from dense_gemm_optimisation_amd import binding
     argsets = [mx_args(p, bufs) for bufs in sets]
     turn = [0]
 
     def launch():
-        binding.gemm_mx(*argsets[turn[0]], stream=stream.cuda_stream)
+        if workspace is None:
+            binding.gemm_mx(*argsets[turn[0]], stream=stream.cuda_stream)
+        else:
+            binding.gemm_mx_ws(*argsets[turn[0]], workspace.data_ptr(), workspace.numel() * 4,
+                               stream=stream.cuda_stream)
         turn[0] = (turn[0] + 1) % len(argsets)
     launch.turn = lambda: turn[0]
     return launch
@@ -220,7 +227,10 @@ def kernel_family(p, bufs, workspace=None):
     and the buffers' actual alignment)."""
     from dense_gemm_optimisation_amd import binding
     if is_mx(p):
-        return binding.mx_kernel_name(*mx_args(p, bufs))
+        if workspace is None:
+            return binding.mx_kernel_name(*mx_args(p, bufs))
+        return binding.mx_kernel_name(*mx_args(p, bufs), workspace=workspace.data_ptr(),
+                                      workspace_bytes=workspace.numel() * 4)
     if p.entry == "valu":
         return "sgemm_valu"
     da, db, dc = bufs
@@ -499,7 +509,8 @@ def main():
                     help="launches timed one by one for the median and minimum")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--workspace", action="store_true",
-                    help="fp32/bf16/fp16 workloads through the workspace entry points (stream-K)")
+                    help="workloads without a fused epilogue through the workspace entry "
+                         "points (stream-K)")
     ap.add_argument("--results", default=None, help="append the JSON line to this file")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -529,8 +540,8 @@ def main():
             bufs = device_buffers(p, torch)
             sets = buffer_sets(bufs, sets_needed(bufs, not args.no_rotate))
             nsets[p.name] = len(sets)
-            pws = ws if (ws is not None and not is_mx(p) and p.in_dtype in ("f32", "bf16", "f16")
-                         and not p.bias and not p.act and not p.entry) else None
+            takes_ws = is_mx(p) or (not p.bias and not p.act and not p.entry)
+            pws = ws if (ws is not None and takes_ws) else None
             if getattr(p, "entry", "") == "bf16x3":  # its own workspace, for the split copies
                 pws = torch.empty(binding.bf16x3_workspace_size(p.M, p.N, p.K, p.batch) // 4,
                                   dtype=torch.int32, device="cuda")

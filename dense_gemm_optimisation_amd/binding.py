@@ -79,6 +79,14 @@ def library() -> ctypes.CDLL:
         lib.gemm_mx_kernel_name.argtypes = mx
         lib.gemm_mx_kernel_name.restype = ctypes.c_char_p
         sz = ctypes.c_size_t
+        lib.gemm_f8_ws.argtypes = f8 + [vp, sz, vp]
+        lib.gemm_f8_ws.restype = i32
+        lib.gemm_f8_kernel_name_ws.argtypes = f8 + [vp, sz]
+        lib.gemm_f8_kernel_name_ws.restype = ctypes.c_char_p
+        lib.gemm_mx_ws.argtypes = mx + [vp, sz, vp]
+        lib.gemm_mx_ws.restype = i32
+        lib.gemm_mx_kernel_name_ws.argtypes = mx + [vp, sz]
+        lib.gemm_mx_kernel_name_ws.restype = ctypes.c_char_p
         lib.gemm_workspace_size.argtypes = []
         lib.gemm_workspace_size.restype = sz
         for name in ("gemm_bf16_ws", "gemm_f16_ws"):
@@ -220,12 +228,31 @@ def gemm_f8(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, format_b
     return _check(st, "gemm_f8", raise_on_error)
 
 
+def gemm_f8_ws(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, format_b, beta, C,
+               ldc, order_c, type_c, batch, stride_a, stride_b, stride_c, workspace,
+               workspace_bytes, stream=None, raise_on_error=True):
+    """gemm_f8 with a caller workspace (stream-K schedule where it pays)."""
+    st = library().gemm_f8_ws(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b,
+                              format_b, beta, C, ldc, order_c, type_c, batch, stride_a, stride_b,
+                              stride_c, workspace, workspace_bytes, _stream(stream))
+    return _check(st, "gemm_f8_ws", raise_on_error)
+
+
 def f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb, order_b, format_b, beta, C,
-                   ldc, order_c, type_c, batch=1, stride_a=0, stride_b=0, stride_c=0):
-    """The kernel gemm_f8 would launch for these arguments (see kernel_name)."""
-    name = library().gemm_f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb,
-                                         order_b, format_b, beta, C, ldc, order_c, type_c, batch,
-                                         stride_a, stride_b, stride_c)
+                   ldc, order_c, type_c, batch=1, stride_a=0, stride_b=0, stride_c=0,
+                   workspace=None, workspace_bytes=0):
+    """The kernel gemm_f8 (gemm_f8_ws with a workspace) would launch for these
+    arguments (see kernel_name)."""
+    lib = library()
+    if workspace is None:
+        name = lib.gemm_f8_kernel_name(M, N, K, alpha, A, lda, order_a, format_a, B, ldb,
+                                       order_b, format_b, beta, C, ldc, order_c, type_c, batch,
+                                       stride_a, stride_b, stride_c)
+    else:
+        name = lib.gemm_f8_kernel_name_ws(M, N, K, alpha, A, lda, order_a, format_a, B, ldb,
+                                          order_b, format_b, beta, C, ldc, order_c, type_c,
+                                          batch, stride_a, stride_b, stride_c, workspace,
+                                          workspace_bytes)
     return None if name is None else name.decode()
 
 
@@ -241,14 +268,35 @@ def gemm_mx(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb, format_b, s
     return _check(st, "gemm_mx", raise_on_error)
 
 
+def gemm_mx_ws(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb, format_b, scale_b, ldsb,
+               beta, C, ldc, order_c, type_c, batch, stride_a, stride_b, stride_scale_a,
+               stride_scale_b, stride_c, workspace, workspace_bytes, stream=None,
+               raise_on_error=True):
+    """gemm_mx with a caller workspace (stream-K schedule where it pays)."""
+    st = library().gemm_mx_ws(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb, format_b,
+                              scale_b, ldsb, beta, C, ldc, order_c, type_c, batch, stride_a,
+                              stride_b, stride_scale_a, stride_scale_b, stride_c, workspace,
+                              workspace_bytes, _stream(stream))
+    return _check(st, "gemm_mx_ws", raise_on_error)
+
+
 def mx_kernel_name(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb, format_b, scale_b,
                    ldsb, beta, C, ldc, order_c, type_c, batch=1, stride_a=0, stride_b=0,
-                   stride_scale_a=0, stride_scale_b=0, stride_c=0):
-    """The kernel gemm_mx would launch for these arguments (None if invalid)."""
-    name = library().gemm_mx_kernel_name(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb,
+                   stride_scale_a=0, stride_scale_b=0, stride_c=0, workspace=None,
+                   workspace_bytes=0):
+    """The kernel gemm_mx (gemm_mx_ws with a workspace) would launch for these
+    arguments (None if invalid)."""
+    lib = library()
+    if workspace is None:
+        name = lib.gemm_mx_kernel_name(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb,
+                                       format_b, scale_b, ldsb, beta, C, ldc, order_c, type_c,
+                                       batch, stride_a, stride_b, stride_scale_a, stride_scale_b,
+                                       stride_c)
+    else:
+        name = lib.gemm_mx_kernel_name_ws(M, N, K, alpha, A, lda, format_a, scale_a, ldsa, B, ldb,
                                           format_b, scale_b, ldsb, beta, C, ldc, order_c, type_c,
                                           batch, stride_a, stride_b, stride_scale_a,
-                                          stride_scale_b, stride_c)
+                                          stride_scale_b, stride_c, workspace, workspace_bytes)
     return None if name is None else name.decode()
 
 
@@ -359,18 +407,19 @@ def kernel_name(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta
     """The kernel the GEMM call with these arguments would launch ("" for an
     empty problem, None for invalid arguments); host only, no GPU needed.
     For 8-bit inputs ("e4m3"/"e5m2") b_dtype and out_dtype name B's format
-    and C's type, as in gemm(); a workspace (fp32, bf16, fp16 inputs) asks
-    about the workspace entry points."""
+    and C's type, as in gemm(); a workspace asks about the workspace entry
+    points."""
+    if in_dtype in _F8_FORMAT:
+        return f8_kernel_name(M, N, K, alpha, A, lda, order_a, _F8_FORMAT[in_dtype], B, ldb,
+                              order_b, _F8_FORMAT[b_dtype or in_dtype], beta, C, ldc, order_c,
+                              _OUTPUT[out_dtype], batch, stride_a, stride_b, stride_c, workspace,
+                              workspace_bytes)
     if workspace is not None:
         name = library().gemm_kernel_name_ws(_INPUT[in_dtype], M, N, K, alpha, A, lda, order_a, B,
                                              ldb, order_b, beta, C, ldc, order_c, c_dtype, batch,
                                              stride_a, stride_b, stride_c, workspace,
                                              workspace_bytes)
         return None if name is None else name.decode()
-    if in_dtype in _F8_FORMAT:
-        return f8_kernel_name(M, N, K, alpha, A, lda, order_a, _F8_FORMAT[in_dtype], B, ldb,
-                              order_b, _F8_FORMAT[b_dtype or in_dtype], beta, C, ldc, order_c,
-                              _OUTPUT[out_dtype], batch, stride_a, stride_b, stride_c)
     name = library().gemm_kernel_name(_INPUT[in_dtype], M, N, K, alpha, A, lda, order_a, B, ldb,
                                       order_b, beta, C, ldc, order_c, c_dtype, batch, stride_a,
                                       stride_b, stride_c)
@@ -385,7 +434,7 @@ def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ld
     "e4m3"/"e5m2" with B's format in b_dtype (default: A's) and C's type
     name in out_dtype); a bias address or an activation selects the
     fused-epilogue entry point (not offered for 8-bit inputs); a workspace
-    address (fp32/bf16/fp16, no epilogue) selects the workspace entry point;
+    address (no epilogue) selects the workspace entry point;
     valu=True (fp32, no epilogue, no workspace) selects gemm_f32_valu."""
     if valu:
         if in_dtype != "f32" or workspace is not None or bias is not None or act != ACT_NONE:
@@ -393,8 +442,13 @@ def gemm(in_dtype, M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ld
         return gemm_f32_valu(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
                              order_c, batch, stride_a, stride_b, stride_c, stream, raise_on_error)
     if workspace is not None:
-        if in_dtype not in ("f32", "bf16", "f16") or bias is not None or act != ACT_NONE:
-            raise ValueError("the workspace entry points take fp32/bf16/fp16 inputs without epilogue")
+        if bias is not None or act != ACT_NONE:
+            raise ValueError("the workspace entry points have no fused epilogue")
+        if in_dtype in _F8_FORMAT:
+            return gemm_f8_ws(M, N, K, alpha, A, lda, order_a, _F8_FORMAT[in_dtype], B, ldb,
+                              order_b, _F8_FORMAT[b_dtype or in_dtype], beta, C, ldc, order_c,
+                              _OUTPUT[out_dtype], batch, stride_a, stride_b, stride_c, workspace,
+                              workspace_bytes, stream, raise_on_error)
         if in_dtype == "f32":
             return gemm_f32_ws(M, N, K, alpha, A, lda, order_a, B, ldb, order_b, beta, C, ldc,
                                order_c, batch, stride_a, stride_b, stride_c, workspace,

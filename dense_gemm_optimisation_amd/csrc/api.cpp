@@ -75,6 +75,8 @@ enum class Kernel {
     SgemmPackDma,         // then the fp32 direct-load kernel
     SgemmPackDmaStreamK,  // then its stream-K schedule
     Mx,                   // block-scaled narrow floats (gemm_mx), direct loads
+    F8DmaStreamK,         // 8-bit direct-load kernel on the stream-K schedule (workspace)
+    MxStreamK,            // block-scaled kernel on the stream-K schedule (workspace)
     SkinnySplitK,         // at most 16 rows, N-contiguous B: split-K across workgroups (workspace)
 };
 
@@ -106,6 +108,8 @@ const char *kernel_name(Kernel k) {
     case Kernel::SgemmPackDma: return "sgemm_mfma_dma_packed";
     case Kernel::SgemmPackDmaStreamK: return "sgemm_mfma_dma_streamk_packed";
     case Kernel::Mx: return "mxgemm_mfma_dma";
+    case Kernel::F8DmaStreamK: return "f8gemm_mfma_dma_streamk";
+    case Kernel::MxStreamK: return "mxgemm_mfma_dma_streamk";
     case Kernel::SkinnySplitK: return "gemm_skinny_splitk";
     }
     return "";
@@ -154,7 +158,9 @@ hipError_t launch(Kernel k, const Problem &p, hipStream_t stream) {
     case Kernel::HgemmPackDmaStreamK:
     case Kernel::SgemmPackDma:
     case Kernel::SgemmPackDmaStreamK: return hipErrorInvalidValue;  // need the workspace: run()
-    case Kernel::Mx: return hipErrorInvalidValue;  // needs the scales: gemm_mx
+    case Kernel::Mx:
+    case Kernel::MxStreamK: return hipErrorInvalidValue;  // needs the scales: gemm_mx
+    case Kernel::F8DmaStreamK: return hipErrorInvalidValue;  // needs the workspace: run()
     case Kernel::SkinnySplitK: return hipErrorInvalidValue;  // needs the workspace: run()
     }
     return hipErrorInvalidValue;
@@ -393,7 +399,8 @@ gemm_status_t check_workspace(const Problem &p, int64_t M, int64_t N, int64_t K,
 // address is used, to place the operand copies).  Unaligned operands of large
 // problems are copied into aligned buffers for the direct-load kernels
 // (plan_packed); otherwise the 16-bit and fp32 kernels (the direct-load and
-// the general ones) switch to their stream-K schedule where it applies.  w.k holds the kernel chosen without a workspace.
+// the general ones) and the 8-bit direct-load kernel switch to their
+// stream-K schedule where it applies.  w.k holds the kernel chosen without a workspace.
 void plan_workspace(const Problem &p, const void *workspace, size_t bytes, WsPlan &w) {
     w.q = p;
     w.used = 0;
@@ -414,6 +421,9 @@ void plan_workspace(const Problem &p, const void *workspace, size_t bytes, WsPla
     } else if (k == Kernel::SgemmDma && sgemm_dma_streamk_eligible(p, force)) {
         k = Kernel::SgemmDmaStreamK;
         w.used = sgemm_streamk_bytes(p);
+    } else if (k == Kernel::F8Dma && f8gemm_dma_streamk_eligible(p, force)) {
+        k = Kernel::F8DmaStreamK;
+        w.used = f8gemm_dma_streamk_bytes(p);
     } else if (k == Kernel::Skinny && skinny_sk_eligible(p) &&
                skinny_sk_bytes(p) <= static_cast<int64_t>(bytes)) {
         k = Kernel::SkinnySplitK;
@@ -449,6 +459,7 @@ hipError_t launch_planned(const WsPlan &w, void *workspace, hipStream_t stream) 
     case Kernel::SgemmDmaStreamK:
     case Kernel::SgemmPackDmaStreamK: return launch_sgemm_dma_streamk(w.q, workspace, stream);
     case Kernel::SkinnySplitK: return launch_skinny_sk(w.q, workspace, stream);
+    case Kernel::F8DmaStreamK: return launch_f8gemm_dma_streamk(w.q, workspace, stream);
     case Kernel::HgemmPackDma: return launch_hgemm_dma(w.q, stream);
     case Kernel::SgemmPackDma: return launch_sgemm_dma(w.q, stream);
     default: return launch(w.k, w.q, stream);
@@ -556,7 +567,8 @@ gemm_status_t mx_plan(int64_t M, int64_t N, int64_t K, float alpha, const void *
                       const uint8_t *scaleB, int64_t ldsb, float beta, const void *C,
                       int64_t ldc, gemm_order_t orderC, gemm_output_t typeC, int64_t batch,
                       int64_t strideA, int64_t strideB, int64_t strideScaleA,
-                      int64_t strideScaleB, int64_t strideC, MxProblem &m, Kernel &kernel) {
+                      int64_t strideScaleB, int64_t strideC, MxProblem &m, Kernel &kernel,
+                      const void *workspace = nullptr, size_t ws_bytes = 0) {
     kernel = Kernel::None;
     Elem ec;
     auto fmt_ok = [](gemm_mx_format_t f) { return f >= GEMM_MX_E4M3 && f <= GEMM_MX_E2M1; };
@@ -582,6 +594,13 @@ gemm_status_t mx_plan(int64_t M, int64_t N, int64_t K, float alpha, const void *
     if (batch > 1 && strideC < span_c) return GEMM_ERR_INVALID_ARG;  // C slices overlap
     const Range rc = range_of(C, span_c, batch, strideC, eout);
     const int64_t sbytes = 4 * ((K + 127) / 128);  // scale bytes per row the kernel reads
+    // a workspace: 256-byte aligned, not NULL when it has bytes, and not
+    // overlapping C (nor, below, A, B or their scales)
+    const Range rw{reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + ws_bytes};
+    if (ws_bytes > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+                         overlap(rw, rc)))
+        return GEMM_ERR_INVALID_ARG;
     if (reads) {
         if (A == nullptr || B == nullptr || scaleA == nullptr || scaleB == nullptr)
             return GEMM_ERR_INVALID_ARG;
@@ -598,10 +617,13 @@ gemm_status_t mx_plan(int64_t M, int64_t N, int64_t K, float alpha, const void *
         // byte extents of one slice of each operand and of its scales
         const int64_t bytes_a = ((M - 1) * lda + K) * wa / 8, bytes_b = ((N - 1) * ldb + K) * wb / 8;
         const int64_t sc_a = (M - 1) * ldsa + sbytes, sc_b = (N - 1) * ldsb + sbytes;
-        if (overlap(rc, range_of(A, bytes_a, batch, strideA * wa / 8, 1)) ||
-            overlap(rc, range_of(B, bytes_b, batch, strideB * wb / 8, 1)) ||
-            overlap(rc, range_of(scaleA, sc_a, batch, strideScaleA, 1)) ||
-            overlap(rc, range_of(scaleB, sc_b, batch, strideScaleB, 1)))
+        const Range ra = range_of(A, bytes_a, batch, strideA * wa / 8, 1);
+        const Range rb = range_of(B, bytes_b, batch, strideB * wb / 8, 1);
+        const Range rsa = range_of(scaleA, sc_a, batch, strideScaleA, 1);
+        const Range rsb = range_of(scaleB, sc_b, batch, strideScaleB, 1);
+        if (overlap(rc, ra) || overlap(rc, rb) || overlap(rc, rsa) || overlap(rc, rsb))
+            return GEMM_ERR_INVALID_ARG;
+        if (overlap(rw, ra) || overlap(rw, rb) || overlap(rw, rsa) || overlap(rw, rsb))
             return GEMM_ERR_INVALID_ARG;
         if (wa != wb) return GEMM_ERR_UNSUPPORTED;
         // the kernel addresses a slice with 32-bit byte offsets
@@ -640,7 +662,22 @@ gemm_status_t mx_plan(int64_t M, int64_t N, int64_t K, float alpha, const void *
     m.ssa = row ? strideScaleA : strideScaleB;
     m.ssb = row ? strideScaleB : strideScaleA;
     kernel = reads ? Kernel::Mx : Kernel::Scale;
+    // with a workspace of at least gemm_workspace_size() bytes: the stream-K
+    // schedule where it applies
+    if (kernel == Kernel::Mx && ws_bytes >= static_cast<size_t>(hgemm_streamk_workspace_bytes()) &&
+        !force_general() && mxgemm_streamk_eligible(m, force_streamk()))
+        kernel = Kernel::MxStreamK;
     return GEMM_OK;
+}
+
+// Runs a planned gemm_mx call.
+gemm_status_t mx_run(const MxProblem &m, Kernel k, void *workspace, hipStream_t stream) {
+    if (k == Kernel::None) return GEMM_OK;
+    const hipError_t err = k == Kernel::MxStreamK ? launch_mxgemm_streamk(m, workspace, stream)
+                           : k == Kernel::Mx      ? launch_mxgemm(m, stream)
+                                                  : launch_scale(m.p, stream);
+    if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 }  // namespace
@@ -659,10 +696,26 @@ gemm_status_t gemm_mx(int64_t M, int64_t N, int64_t K, float alpha, const void *
     const gemm_status_t st =
         mx_plan(M, N, K, alpha, A, lda, formatA, scaleA, ldsa, B, ldb, formatB, scaleB, ldsb, beta, C,
                 ldc, orderC, typeC, batch, strideA, strideB, strideScaleA, strideScaleB, strideC, m, k);
-    if (st != GEMM_OK || k == Kernel::None) return st;
-    const hipError_t err = k == Kernel::Mx ? launch_mxgemm(m, stream) : launch_scale(m.p, stream);
-    if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
-    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    if (st != GEMM_OK) return st;
+    return mx_run(m, k, nullptr, stream);
+}
+
+gemm_status_t gemm_mx_ws(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                         gemm_mx_format_t formatA, const uint8_t *scaleA, int64_t ldsa,
+                         const void *B, int64_t ldb, gemm_mx_format_t formatB,
+                         const uint8_t *scaleB, int64_t ldsb, float beta, void *C, int64_t ldc,
+                         gemm_order_t orderC, gemm_output_t typeC, int64_t batch, int64_t strideA,
+                         int64_t strideB, int64_t strideScaleA, int64_t strideScaleB,
+                         int64_t strideC, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    MxProblem m;
+    Kernel k;
+    const gemm_status_t st =
+        mx_plan(M, N, K, alpha, A, lda, formatA, scaleA, ldsa, B, ldb, formatB, scaleB, ldsb, beta, C,
+                ldc, orderC, typeC, batch, strideA, strideB, strideScaleA, strideScaleB, strideC, m, k,
+                workspace, workspace_bytes);
+    if (st != GEMM_OK) return st;
+    return mx_run(m, k, workspace, stream);
 }
 
 const char *gemm_mx_kernel_name(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
@@ -673,11 +726,25 @@ const char *gemm_mx_kernel_name(int64_t M, int64_t N, int64_t K, float alpha, co
                                 gemm_output_t typeC, int64_t batch, int64_t strideA,
                                 int64_t strideB, int64_t strideScaleA, int64_t strideScaleB,
                                 int64_t strideC) {
+    return gemm_mx_kernel_name_ws(M, N, K, alpha, A, lda, formatA, scaleA, ldsa, B, ldb, formatB,
+                                  scaleB, ldsb, beta, C, ldc, orderC, typeC, batch, strideA,
+                                  strideB, strideScaleA, strideScaleB, strideC, nullptr, 0);
+}
+
+const char *gemm_mx_kernel_name_ws(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                                   int64_t lda, gemm_mx_format_t formatA, const uint8_t *scaleA,
+                                   int64_t ldsa, const void *B, int64_t ldb,
+                                   gemm_mx_format_t formatB, const uint8_t *scaleB, int64_t ldsb,
+                                   float beta, const void *C, int64_t ldc, gemm_order_t orderC,
+                                   gemm_output_t typeC, int64_t batch, int64_t strideA,
+                                   int64_t strideB, int64_t strideScaleA, int64_t strideScaleB,
+                                   int64_t strideC, const void *workspace,
+                                   size_t workspace_bytes) {
     MxProblem m;
     Kernel k;
     if (mx_plan(M, N, K, alpha, A, lda, formatA, scaleA, ldsa, B, ldb, formatB, scaleB, ldsb, beta, C,
                 ldc, orderC, typeC, batch, strideA, strideB, strideScaleA, strideScaleB, strideC, m,
-                k) != GEMM_OK)
+                k, workspace, workspace_bytes) != GEMM_OK)
         return nullptr;
     return kernel_name(k);
 }
@@ -890,6 +957,21 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha, const uint8_
                batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream);
 }
 
+gemm_status_t gemm_f8_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint8_t *A,
+                         int64_t lda, gemm_order_t orderA, gemm_f8_format_t formatA,
+                         const uint8_t *B, int64_t ldb, gemm_order_t orderB,
+                         gemm_f8_format_t formatB, float beta, void *C, int64_t ldc,
+                         gemm_order_t orderC, gemm_output_t typeC, int64_t batch, int64_t strideA,
+                         int64_t strideB, int64_t strideC, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    Elem ea, eb, ec;
+    if (!f8_type(formatA, ea) || !f8_type(formatB, eb) || !output_type(typeC, ec))
+        return GEMM_ERR_INVALID_ARG;
+    return run(ea, eb, ec, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta, C, ldc, orderC,
+               batch, strideA, strideB, strideC, nullptr, 0, GEMM_ACT_NONE, stream, workspace,
+               workspace_bytes);
+}
+
 size_t gemm_workspace_size(void) { return static_cast<size_t>(hgemm_streamk_workspace_bytes()); }
 
 gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
@@ -1002,6 +1084,28 @@ const char *gemm_f8_kernel_name(int64_t M, int64_t N, int64_t K, float alpha, co
              const_cast<void *>(C), ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
              GEMM_ACT_NONE, p, k);
     return st == GEMM_OK ? kernel_name(k) : nullptr;
+}
+
+const char *gemm_f8_kernel_name_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                                   const uint8_t *A, int64_t lda, gemm_order_t orderA,
+                                   gemm_f8_format_t formatA, const uint8_t *B, int64_t ldb,
+                                   gemm_order_t orderB, gemm_f8_format_t formatB, float beta,
+                                   const void *C, int64_t ldc, gemm_order_t orderC,
+                                   gemm_output_t typeC, int64_t batch, int64_t strideA,
+                                   int64_t strideB, int64_t strideC, const void *workspace,
+                                   size_t workspace_bytes) {
+    Elem ea, eb, ec;
+    if (!f8_type(formatA, ea) || !f8_type(formatB, eb) || !output_type(typeC, ec)) return nullptr;
+    Problem p;
+    WsPlan w;
+    gemm_status_t st =
+        plan(ea, eb, ec, M, N, K, alpha, A, lda, orderA, B, ldb, orderB, beta,
+             const_cast<void *>(C), ldc, orderC, batch, strideA, strideB, strideC, nullptr, 0,
+             GEMM_ACT_NONE, p, w.k);
+    if (st == GEMM_OK && w.k != Kernel::None)
+        st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
+                           strideC, nullptr, 0, A, B, C, workspace, workspace_bytes, w);
+    return st == GEMM_OK ? kernel_name(w.k) : nullptr;
 }
 
 const char *gemm_kernel_name_ws(gemm_input_t in, int64_t M, int64_t N, int64_t K, float alpha,

@@ -28,7 +28,7 @@
 
 #include <type_traits>
 
-#include "dma_tile.hpp"
+#include "dma_streamk.hpp"
 
 namespace libgemm {
 namespace {
@@ -164,6 +164,30 @@ using dma::direct_load4;
 
 constexpr int F8_BM = 256, F8_BN = 256;
 
+// The sizes of the kernel's tiles, panels and stages for formats FA, FB.
+template <int FA, int FB, int WAVES_M, int WAVES_N, bool MX>
+struct F8Tile {
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int WTM = F8_BM / WAVES_M, WTN = F8_BN / WAVES_N;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    // Accumulators beyond 128 registers per lane live in the AGPRs (one
+    // wave per SIMD); the statement that pins the instructions in place
+    // must name the register file they are in.
+    static constexpr bool ACC_AGPR = FM * FN * 16 > 128;
+    using OpA = Operand<true, WAVES, Fmt<FA>::ROWB / 2, Fmt<FA>::STEPB / 2>;
+    using OpB = Operand<true, WAVES, Fmt<FB>::ROWB / 2, Fmt<FB>::STEPB / 2>;
+    static constexpr int PANEL_A = OpA::PANEL, PANEL_B = OpB::PANEL;
+    static constexpr int SCALES = MX ? 4 * (F8_BM + F8_BN) : 0;  // bytes per stage
+    static constexpr int DATA = PANEL_A + PANEL_B + SCALES;
+    static constexpr int EPI = WAVES * 32 * WTN * 4;              // epilogue staging
+    static constexpr int STAGE = DATA > EPI ? DATA : EPI;
+    static constexpr int PER_DATA = OpA::PER_WAVE + OpB::PER_WAVE;
+    static constexpr int PER_STAGE = PER_DATA + (MX ? 1 : 0);  // direct loads per wave per stage
+    static_assert(FM % 2 == 0, "A fragments alternate between two slots");
+    static_assert(!MX || WAVES == 8, "scale loads: four waves per operand, 64 rows each");
+    static_assert(PER_DATA % FN == 0, "refill split over the last row's instructions");
+};
+
 // 2 x 4 waves, each with a 128 x 64 wave tile (4 x 2 accumulator blocks,
 // 128 registers); a stage is 128 k, two 64-k steps.  A lane's fragments are
 // twice the size of the 16-bit kernel's, so double-buffering all of them
@@ -178,39 +202,27 @@ constexpr int F8_BM = 256, F8_BN = 256;
 // that every wave has read it.  With scales (MX), each lane reads its six
 // fragments' scale words from the stage's buffer right after the barrier,
 // into registers that take over once the current stage's last row is done.
-template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8Args p) {
-    constexpr int WAVES = WAVES_M * WAVES_N;
-    constexpr int BM = F8_BM, BN = F8_BN;
-    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 32, FN = WTN / 32;
-    // Accumulators beyond 128 registers per lane live in the AGPRs (one
-    // wave per SIMD); the statement that pins the instructions in place
-    // must name the register file they are in.
-    constexpr bool ACC_AGPR = FM * FN * 16 > 128;
-    static_assert(FM % 2 == 0, "A fragments alternate between two slots");
-    static_assert(!MX || WAVES == 8, "scale loads: four waves per operand, 64 rows each");
-    using OpA = Operand<true, WAVES, Fmt<FA>::ROWB / 2, Fmt<FA>::STEPB / 2>;
-    using OpB = Operand<true, WAVES, Fmt<FB>::ROWB / 2, Fmt<FB>::STEPB / 2>;
-    constexpr int PANEL_A = OpA::PANEL, PANEL_B = OpB::PANEL;
-    constexpr int SCALES = MX ? 4 * (BM + BN) : 0;   // bytes per stage
-    constexpr int DATA = PANEL_A + PANEL_B + SCALES;
-    constexpr int EPI = WAVES * 32 * WTN * 4;        // epilogue staging
-    constexpr int STAGE = DATA > EPI ? DATA : EPI;
-    constexpr int PER_DATA = OpA::PER_WAVE + OpB::PER_WAVE;
-    constexpr int PER_STAGE = PER_DATA + (MX ? 1 : 0);  // direct loads per wave per stage
-    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(PER_DATA % FN == 0, "refill split over the last row's instructions");
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+//
+// f8_tile_steps runs stages [kb, ke) of one tile (128 k each, numbered from
+// the start of K) into acc and returns the ring buffer that held the last
+// one; the buffer after it is then free for the epilogue's staging.
+template <int FA, int FB, int WAVES_M, int WAVES_N, int STAGES, bool MX>
+__device__ __forceinline__ int f8_tile_steps(
+    const F8Args &p, LDS char *lds, const TileCoord &t, int64_t kb, int64_t ke,
+    f32x16 (&acc)[F8_BM / WAVES_M / 32][F8_BN / WAVES_N / 32]) {
+    using L = F8Tile<FA, FB, WAVES_M, WAVES_N, MX>;
+    constexpr int FM = L::FM, FN = L::FN, WTM = L::WTM, WTN = L::WTN;
+    constexpr bool ACC_AGPR = L::ACC_AGPR;
+    using OpA = typename L::OpA;
+    using OpB = typename L::OpB;
+    constexpr int PANEL_A = L::PANEL_A, PANEL_B = L::PANEL_B, STAGE = L::STAGE;
+    constexpr int PER_DATA = L::PER_DATA, PER_STAGE = L::PER_STAGE;
 
     const DmaArgs &d = p.d;
-    TileCoord t = tile_of(d.grid, blockIdx.x);
-    t.batch = uniform(t.batch);
-    t.tm = uniform(t.tm);
-    t.tn = uniform(t.tn);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int64_t m0 = t.tm * F8_BM, n0 = t.tn * F8_BN;
 
     OpA opa;
     OpB opb;
@@ -233,31 +245,22 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8
         srs = dma::raw_buffer(static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(base))),
                               static_cast<uint32_t>(uniform(R * sld)));
         svoff = r < R ? static_cast<uint32_t>(r * sld) : OOB;
-        slds = PANEL_A + PANEL_B + (on_a ? 0 : 4 * BM) + 256 * q;
+        slds = PANEL_A + PANEL_B + (on_a ? 0 : 4 * F8_BM) + 256 * q;
     }
-    LDS char *lds = (LDS char *)smem;
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     auto load_scales = [&](int buf, int64_t stage) {
         if (MX)
             direct_load4(srs, lds_base + buf * STAGE + slds,
                          svoff == OOB ? OOB : svoff + static_cast<uint32_t>(4 * stage));
     };
-    const int64_t steps = (p.K + 127) / 128;
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int64_t steps = ke - kb;
 
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) {
         if (st < steps) {
-            opa.issue(lds + st * STAGE, st, p.ka, wave);
-            opb.issue(lds + st * STAGE + PANEL_A, st, p.kb, wave);
-            load_scales(st, st);
+            opa.issue(lds + st * STAGE, kb + st, p.ka, wave);
+            opb.issue(lds + st * STAGE + PANEL_A, kb + st, p.kb, wave);
+            load_scales(st, kb + st);
         }
     }
     wait_stages<PER_STAGE, STAGES>(int(steps - 1 < STAGES - 1 ? steps - 1 : STAGES - 1));
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8
 #pragma unroll
         for (int i = 0; i < FM; ++i) nsa[i] = int(s[wm * WTM + i * 32 + (lane & 31)] >> sh);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) nsb[j] = int(s[BM + wn * WTN + j * 32 + (lane & 31)] >> sh);
+        for (int j = 0; j < FN; ++j) nsb[j] = int(s[F8_BM + wn * WTN + j * 32 + (lane & 31)] >> sh);
     };
     auto take_scales = [&]() {
 #pragma unroll
@@ -348,12 +351,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8
         read_b(nbuf, 0, 0);
         read_a(nbuf, 0, 0);
         read_scales(nbuf);
-        const int64_t refill = s + STAGES;
+        const int64_t refill = s + STAGES;  // within the range
         const bool do_refill = refill < steps;
-        const u32x4 ra = opa.rsrc(refill), rb = opb.rsrc(refill);
+        const u32x4 ra = opa.rsrc(kb + refill), rb = opb.rsrc(kb + refill);
         const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + buf * STAGE));
-        const int64_t kla = p.ka - refill * (Fmt<FA>::STEPB / 2);
-        const int64_t klb = p.kb - refill * (Fmt<FB>::STEPB / 2);
+        const int64_t kla = p.ka - (kb + refill) * (Fmt<FA>::STEPB / 2);
+        const int64_t klb = p.kb - (kb + refill) * (Fmt<FB>::STEPB / 2);
         // the last row, with the refill of this buffer split around its
         // instructions
 #pragma unroll
@@ -366,18 +369,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8
                     if (q < OpA::PER_WAVE) opa.load(ra, la, q, kla, wave);
                     else opb.load(rb, la + PANEL_A, q - OpA::PER_WAVE, klb, wave);
                 }
-                if (j == 0) load_scales(buf, refill);
+                if (j == 0) load_scales(buf, kb + refill);
             }
         }
         take_scales();
         buf = nbuf;
     }
-    // The last stage.  When it holds only 64 k (K = 64 mod 128), its second
-    // k step reads zeros from both panels; its scales come from bytes past
-    // the last scale block, so they are replaced by 2^0 (a NaN pattern there
-    // would turn the zero products into NaN).
+    // The last stage.  When it is the last of K and holds only 64 k (K = 64
+    // mod 128), its second k step reads zeros from both panels; its scales
+    // come from bytes past the last scale block, so they are replaced by 2^0
+    // (a NaN pattern there would turn the zero products into NaN).
     first_step(buf);
-    if (MX && (p.K & 127) != 0) {
+    if (MX && ke * 128 > p.K) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) sa[i] = UNIT_SCALE;
 #pragma unroll
@@ -389,12 +392,146 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8
         row(i, K1{});
         if (i + 1 < FM) hint_row<2, FN>();
     }
+    return buf;
+}
 
-    // C is staged in the buffer after the last stage's: every wave finished
-    // reading it before the last barrier and no load targets it any more.
-    LDS char *stage_free = lds + (buf + 1 == STAGES ? 0 : buf + 1) * STAGE;
-    store_tile_lds<OUT, FM, FN>(d, acc, t.batch, m0 + wm * WTM, n0 + wn * WTN, lane,
-                                reinterpret_cast<LDS float *>(stage_free) + wave * 32 * WTN);
+// The epilogue of a whole tile: C is staged in the ring buffer after the
+// last stage's (`buf`): every wave finished reading it before the last
+// barrier and no load targets it any more.
+template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX>
+__device__ __forceinline__ void f8_tile_store(
+    const F8Args &p, LDS char *lds, const TileCoord &t, int buf,
+    const f32x16 (&acc)[F8_BM / WAVES_M / 32][F8_BN / WAVES_N / 32]) {
+    using L = F8Tile<FA, FB, WAVES_M, WAVES_N, MX>;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    LDS char *stage_free = lds + (buf + 1 == STAGES ? 0 : buf + 1) * L::STAGE;
+    store_tile_lds<OUT, L::FM, L::FN>(p.d, acc, t.batch, t.tm * F8_BM + wm * L::WTM,
+                                      t.tn * F8_BN + wn * L::WTN, lane,
+                                      reinterpret_cast<LDS float *>(stage_free) + wave * 32 * L::WTN);
+}
+
+// One workgroup per tile.
+template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8Args p) {
+    using L = F8Tile<FA, FB, WAVES_M, WAVES_N, MX>;
+    static_assert(STAGES >= 2 && STAGES * L::STAGE <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * L::STAGE];
+    LDS char *lds = (LDS char *)smem;
+    TileCoord t = tile_of(p.d.grid, blockIdx.x);
+    t.batch = uniform(t.batch);
+    t.tm = uniform(t.tm);
+    t.tn = uniform(t.tn);
+    f32x16 acc[L::FM][L::FN];
+#pragma unroll
+    for (int i = 0; i < L::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < L::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int buf = f8_tile_steps<FA, FB, WAVES_M, WAVES_N, STAGES, MX>(p, lds, t, 0,
+                                                                        (p.K + 127) / 128, acc);
+    f8_tile_store<FA, FB, OUT, WAVES_M, WAVES_N, STAGES, MX>(p, lds, t, buf, acc);
+}
+
+// The stream-K schedule of dma_streamk.hpp over the same tiles (a k step is
+// one 128-k stage): G workgroups, one per compute unit, each computing its
+// whole tiles and then its range of the cut tiles' k steps; a piece that
+// covers a whole tile goes through the epilogue, any other to its slot in
+// the workspace for dma_streamk_fixup.
+template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_streamk_kernel(F8Args p,
+                                                                                   DmaStreamK sk) {
+    using L = F8Tile<FA, FB, WAVES_M, WAVES_N, MX>;
+    static_assert(STAGES >= 2 && STAGES * L::STAGE <= 160 * 1024, "LDS budget");
+    static_assert(L::FM * L::FN * 4 * L::WAVES * 64 * 16 == SK_SLOT * 4, "a slot holds one tile");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * L::STAGE];
+    LDS char *lds = (LDS char *)smem;
+
+    // logical workgroup: the hardware id regrouped per XCD, so that the
+    // workgroups of one die take consecutive tiles and ranges
+    const int64_t G = gridDim.x, S = sk.steps;
+    const int64_t w = uniform(xcd_remap(blockIdx.x, G, 8));
+    const int64_t n_dp = uniform(sk_whole_tiles(sk, w, G));
+    const int64_t begin = uniform(sk_begin(sk, w));
+    const int64_t end = uniform(sk_end(sk, w));
+    int64_t it = begin;
+    for (int64_t item = 0;; ++item) {
+        int64_t tile, kb, ke, local = 0;
+        if (item < n_dp) {
+            tile = w + item * G;
+            kb = 0;
+            ke = S;
+        } else {
+            if (it >= end) break;
+            local = uniform(it / S);
+            const StreamKPiece pc = sk_piece(sk, local, it, end);
+            kb = pc.kb;
+            ke = pc.ke;
+            tile = sk.dp_tiles + local;
+            it = local * S + ke;
+        }
+        TileCoord t = tile_of(p.d.grid, tile);
+        t.batch = uniform(t.batch);
+        t.tm = uniform(t.tm);
+        t.tn = uniform(t.tn);
+        // every wave is done with the previous piece's buffers (its last
+        // fragment reads and epilogue staging) before the ring is refilled
+        if (item > 0) __syncthreads();
+        f32x16 acc[L::FM][L::FN];
+#pragma unroll
+        for (int i = 0; i < L::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < L::FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        const int buf = f8_tile_steps<FA, FB, WAVES_M, WAVES_N, STAGES, MX>(p, lds, t, kb, ke, acc);
+        if (kb == 0 && ke == S)
+            f8_tile_store<FA, FB, OUT, WAVES_M, WAVES_N, STAGES, MX>(p, lds, t, buf, acc);
+        else
+            store_partial<L::FM, L::FN, L::WAVES * 64>(sk, sk_slot(sk, w, local, end), acc);
+    }
+}
+
+// ---- host side of the stream-K schedule (8-bit and MX launches)
+
+// Step time over partial-tile time for streamk_groups, and the cost of the
+// partial-tile exchange in k steps of one tile: about 0.14 per partial tile
+// written and read back and 2 for the fix-up launch.  These are the 16-bit
+// direct-load kernel's measured figures: its tiles are the same and a
+// 128-k stage of 8-bit operands, twice its 64-k step's bytes at twice the
+// instruction rate, takes about as long.
+#ifndef LIBGEMM_F8_SK_RATIO
+#define LIBGEMM_F8_SK_RATIO 14
+#endif
+constexpr double F8_SK_STEPS_PER_PIECE = 0.14;
+constexpr double F8_SK_FIXED_STEPS = 2.0;
+
+inline int64_t f8_tiles(int64_t M, int64_t N, int64_t batch) {
+    return ((M + F8_BM - 1) / F8_BM) * ((N + F8_BN - 1) / F8_BN) * batch;
+}
+
+// The split of `tiles` tiles of K elements (128-k steps) over one workgroup
+// per compute unit of MI355X (on a part with fewer units the schedule is
+// still correct, the workgroups just do not all run at once).
+inline StreamKSplit f8_streamk_split(int64_t tiles, int64_t K) {
+    return streamk_split(tiles, (K + 127) / 128, HGEMM_STREAMK_MAX_GRID, LIBGEMM_F8_SK_RATIO);
+}
+
+// Some tiles are left over after the whole waves, and (unless forced) the k
+// steps the cut last wave saves exceed the exchange: the last wave takes
+// ceil(T_r * S / Gs) steps per workgroup instead of S, and the exchange grows
+// with the pieces, about Gs + T_r partial tiles.
+inline bool f8_streamk_worth(int64_t tiles, int64_t K, bool force) {
+    const int64_t steps = (K + 127) / 128;
+    const int64_t g = HGEMM_STREAMK_MAX_GRID;
+    const int64_t cut = tiles % g;
+    if (cut == 0 || tiles >= (int64_t(1) << 24) || steps >= (int64_t(1) << 24)) return false;
+    if (force) return true;
+    const int64_t gs = streamk_groups(g, cut, steps, LIBGEMM_F8_SK_RATIO);
+    const int64_t tail = (cut * steps + gs - 1) / gs;
+    return double(steps - tail) > F8_SK_STEPS_PER_PIECE * double(gs + cut) + F8_SK_FIXED_STEPS;
 }
 
 }  // namespace

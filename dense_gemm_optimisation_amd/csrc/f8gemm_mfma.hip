@@ -198,6 +198,28 @@ struct LaunchDma {
     }
 };
 
+// The stream-K launch: its arguments, split and grid, then the fix-up of
+// the cut tiles.
+struct F8StreamKLaunch {
+    F8Args a;
+    DmaStreamK sk;
+    int64_t grid;
+};
+
+template <int FA, int FB, int OUT>
+struct LaunchDmaStreamK {
+    static hipError_t go(const Problem &, F8StreamKLaunch &l, hipStream_t stream) {
+        constexpr int WM = LIBGEMM_F8_WM, WN = LIBGEMM_F8_WN;
+        void *args[] = {&l.a, &l.sk};
+        const hipError_t e = hipLaunchKernel(
+            reinterpret_cast<const void *>(
+                &f8gemm_dma_streamk_kernel<FA, FB, OUT, WM, WN, LIBGEMM_F8_STAGES, false>),
+            dim3(static_cast<unsigned>(l.grid)), dim3(WM * WN * 64), args, 0, stream);
+        if (e != hipSuccess) return e;
+        return launch_dma_streamk_fixup<OUT, WM, WN>(l.a.d, l.sk, l.a.d.grid.count(), stream);
+    }
+};
+
 template <int FA, int FB, int OUT>
 struct LaunchGeneral {
     static hipError_t go(const Problem &p, GeneralArgs &a, hipStream_t stream) {
@@ -251,12 +273,16 @@ bool f8gemm_dma_eligible(const Problem &p) {
     return true;
 }
 
-hipError_t launch_f8gemm_dma(const Problem &p, hipStream_t stream) {
+namespace {
+
+// The direct-load kernel's arguments; xcds: the tile grid's regrouping per
+// die (1 when the work order does it).  The panels count in 16-bit units:
+// every extent along K, leading dimension and operand stride is halved (all
+// are even here).
+F8Args dma_args(const Problem &p, int32_t xcds) {
     F8Args a{};
     a.d = common_args(p, F8_BM, LIBGEMM_F8_GROUP_M);
-    if (a.d.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
-    // The panels count in 16-bit units: every extent along K, leading
-    // dimension and operand stride is halved (all are even here).
+    a.d.grid.xcds = xcds;
     a.K = p.K;
     a.ka = a.kb = p.K / 2;
     a.d.K = p.K / 2;
@@ -264,7 +290,33 @@ hipError_t launch_f8gemm_dma(const Problem &p, hipStream_t stream) {
     a.d.ldb /= 2;
     a.d.sA /= 2;
     a.d.sB /= 2;
+    return a;
+}
+
+}  // namespace
+
+hipError_t launch_f8gemm_dma(const Problem &p, hipStream_t stream) {
+    F8Args a = dma_args(p, 8);
+    if (a.d.grid.count() > 0x7fffffff) return hipErrorInvalidConfiguration;
     return by_output<LaunchDma>(p, a, stream);
+}
+
+bool f8gemm_dma_streamk_eligible(const Problem &p, bool force) {
+    return f8gemm_dma_eligible(p) && f8_streamk_worth(f8_tiles(p.M, p.N, p.batch), p.K, force);
+}
+
+int64_t f8gemm_dma_streamk_bytes(const Problem &p) {
+    return 2 * f8_streamk_split(f8_tiles(p.M, p.N, p.batch), p.K).groups * int64_t(SK_SLOT) * 4;
+}
+
+hipError_t launch_f8gemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream) {
+    F8StreamKLaunch l{};
+    l.a = dma_args(p, 1);  // the work order itself spreads tiles over the dies
+    static_cast<StreamKSplit &>(l.sk) = f8_streamk_split(f8_tiles(p.M, p.N, p.batch), p.K);
+    l.sk.partials = static_cast<float *>(workspace);
+    l.grid = streamk_grid(l.sk, HGEMM_STREAMK_MAX_GRID);
+    if (l.grid == 0) return hipSuccess;
+    return by_output<LaunchDmaStreamK>(p, l, stream);
 }
 
 hipError_t launch_f8gemm(const Problem &p, hipStream_t stream) {

@@ -170,6 +170,13 @@ hipError_t launch_skinny_sk(const Problem &p, void *workspace, hipStream_t strea
 // and a general kernel for any order, alignment and shape.
 bool f8gemm_dma_eligible(const Problem &p);
 hipError_t launch_f8gemm_dma(const Problem &p, hipStream_t stream);
+// The direct-load kernel's stream-K schedule, through the same workspace as
+// the 16-bit kernels' (hgemm_streamk_workspace_bytes()); only where
+// f8gemm_dma_streamk_eligible() holds.
+bool f8gemm_dma_streamk_eligible(const Problem &p, bool force = false);
+// Workspace bytes launch_f8gemm_dma_streamk uses for p (its partial tiles).
+int64_t f8gemm_dma_streamk_bytes(const Problem &p);
+hipError_t launch_f8gemm_dma_streamk(const Problem &p, void *workspace, hipStream_t stream);
 hipError_t launch_f8gemm(const Problem &p, hipStream_t stream);
 hipError_t launch_scale(const Problem &p, hipStream_t stream);  // C <- beta*C only
 
@@ -192,5 +199,12 @@ inline int mx_width(int fmt) { return fmt == 4 ? 4 : (fmt == 2 || fmt == 3) ? 6 
 // ldsb multiples of 4 of at least 4*ceil(K/128) bytes, 4-byte aligned
 // scales, and fa, fb of one width (the api checks all of it).
 hipError_t launch_mxgemm(const MxProblem &m, hipStream_t stream);
+// Its stream-K schedule (the 8-bit kernel's split: 256 x 256 tiles, 128-k
+// steps) through a workspace of mxgemm_streamk_bytes(m) bytes, where
+// mxgemm_streamk_eligible() holds (some tiles left over after the whole
+// waves, and worth the exchange unless forced).
+bool mxgemm_streamk_eligible(const MxProblem &m, bool force = false);
+int64_t mxgemm_streamk_bytes(const MxProblem &m);
+hipError_t launch_mxgemm_streamk(const MxProblem &m, void *workspace, hipStream_t stream);
 
 }  // namespace libgemm

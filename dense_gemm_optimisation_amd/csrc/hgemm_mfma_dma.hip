@@ -35,12 +35,10 @@
 //
 // The operand panels, their LDS layouts and the epilogue are in
 // dma_tile.hpp, shared with the 8-bit kernel.
-#include "dma_tile.hpp"
+#include "dma_streamk.hpp"
 
 namespace libgemm {
 namespace {
-
-typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 using namespace dmatile;
 
@@ -384,21 +382,8 @@ __device__ __forceinline__ void dma_tile_store(const DmaArgs &p, LDS char *lds, 
 // Gs = min(G, iterations) workgroups; a piece covering a whole tile is stored
 // through the epilogue, any other is written to the workgroup's slot 2w (the
 // piece holding its last iteration) or 2w + 1 (its first), and
-// hgemm_dma_streamk_fixup adds the pieces of each cut tile in increasing
-// workgroup order and applies the epilogue.
-struct DmaStreamK : StreamKSplit {
-    float *partials;    // 2 * Gs slots of 256 x 256 floats
-};
-
-constexpr int SK_SLOT = BM * BN;  // floats per partial tile
-
-// Slot `slot` as a raw buffer.  Register quad q of block (i, j) of thread
-// tid is the 16 bytes at ((i*FN + j)*4 + q) * threads * 16 + tid * 16.
-__device__ inline __amdgpu_buffer_rsrc_t slot_rsrc(const DmaStreamK &sk, int64_t slot) {
-    return __builtin_amdgcn_make_buffer_rsrc(sk.partials + slot * SK_SLOT, 0, SK_SLOT * 4,
-                                             0x00020000);
-}
-
+// dma_streamk_fixup (dma_streamk.hpp) adds the pieces of each cut tile in
+// increasing workgroup order and applies the epilogue.
 template <class T, int OUT, bool A_KMAJOR, bool B_KMAJOR, int WAVES_M, int WAVES_N, int BK,
           int STAGES>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_streamk_kernel(DmaArgs p,
@@ -453,100 +438,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void hgemm_dma_streamk_ke
         if (kb == 0 && ke == S) {
             dma_tile_store<OUT, WAVES_M, WAVES_N, BK, STAGES>(p, lds, t, buf, acc);
         } else {
-            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(sk, sk_slot(sk, w, local, end));
-            const int tid = threadIdx.x;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    // the whole vector is reinterpreted, then indexed
-                    const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const u32x4 v = {bits[4 * q], bits[4 * q + 1], bits[4 * q + 2],
-                                         bits[4 * q + 3]};
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            v, rs, tid * 16, ((i * FN + j) * 4 + q) * THREADS * 16, 0);
-                    }
-                }
+            store_partial<FM, FN, WAVES_M * WAVES_N * 64>(sk, sk_slot(sk, w, local, end), acc);
         }
-    }
-}
-
-// Workgroup (local tile, piece), piece = (i*FN + j)*4 + q: sums register
-// quad q of block (i, j) over the pieces of cut tile `local`, lowest
-// workgroup first, and stores it.  With the operands swapped in the matrix
-// instruction, register r of block (i, j) of lane l holds row l%32 and column
-// 8*(r/4) + 4*(l/32) + r%4 of that block: a quad is four consecutive columns
-// of one row.
-template <int OUT, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void hgemm_dma_streamk_fixup(DmaArgs p,
-                                                                                DmaStreamK sk) {
-    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    constexpr int FN = WTN / 32;
-    constexpr int THREADS = WAVES_M * WAVES_N * 64;
-    constexpr int PIECES = (BM / WAVES_M / 32) * FN * 4;
-    constexpr int BATCH = 8;  // pieces whose loads are in flight together
-    const int64_t S = sk.steps;
-    const int64_t local = blockIdx.x / PIECES;
-    const int piece = blockIdx.x % PIECES;
-    const int64_t g0 = sk_owner(sk, local * S), g1 = sk_owner(sk, local * S + S - 1);
-    if (g0 == g1) return;
-    const int tid = threadIdx.x;
-    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t g = g0; g <= g1; g += BATCH) {
-        u32x4 v[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            // past the last piece: an offset beyond the buffer reads zeros
-            const int64_t gu = g + u <= g1 ? g + u : g1;
-            const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
-            v[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, sk_slot(sk, gu, local, sk_end(sk, gu))), off,
-                                                             piece * THREADS * 16, 0));
-        }
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) sum += __builtin_bit_cast(f32x4, v[u]);
-    }
-    const TileCoord t = tile_of(p.grid, sk.dp_tiles + local);
-    const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int blk = piece >> 2, q = piece & 3;
-    const int i = blk / FN, j = blk % FN;
-    const int64_t row = t.tm * BM + wm * WTM + i * 32 + (lane & 31);
-    const int64_t col0 = t.tn * BN + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-    if (row >= p.M) return;
-    char *Cb = static_cast<char *>(p.C) + t.batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
-    float old[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t off = row * p.ldc + (col0 + e < p.N ? col0 + e : 0);
-        old[e] = 0.0f;
-        if (p.beta != 0.0f) {
-            if (OUT == OUT_F32) {
-                old[e] = reinterpret_cast<const float *>(Cb)[off];
-            } else {
-                const uint16_t b = reinterpret_cast<const uint16_t *>(Cb)[off];
-                old[e] = OUT == OUT_BF16 ? __builtin_bit_cast(float, uint32_t(b) << 16)
-                                         : static_cast<float>(__builtin_bit_cast(_Float16, b));
-            }
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t col = col0 + e;
-        if (col >= p.N) continue;
-        float x = p.alpha * sum[e];
-        if (p.beta != 0.0f) x = __builtin_fmaf(p.beta, old[e], x);
-        if (p.epi.active()) x = epilogue_apply(p.epi, x, t.batch, row, col);
-        const int64_t off = row * p.ldc + col;
-        if (OUT == OUT_F32)
-            reinterpret_cast<float *>(Cb)[off] = x;
-        else if (OUT == OUT_BF16)
-            reinterpret_cast<uint16_t *>(Cb)[off] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-        else
-            reinterpret_cast<uint16_t *>(Cb)[off] =
-                __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
     }
 }
 
@@ -595,12 +488,8 @@ hipError_t launch_sk(DmaArgs &a, DmaStreamK &sk, int64_t grid, hipStream_t strea
         reinterpret_cast<const void *>(&hgemm_dma_streamk_kernel<T, OUT, AK, BKM, WM, WN,
                                                                  LIBGEMM_DMA_BK, LIBGEMM_DMA_STAGES>),
         dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), args, 0, stream);
-    if (e != hipSuccess || sk.iters == 0) return e;
-    constexpr int PIECES = (BM / WM / 32) * (BN / WN / 32) * 4;
-    const int64_t cut = a.grid.count() - sk.dp_tiles;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&hgemm_dma_streamk_fixup<OUT, WM, WN>),
-                           dim3(static_cast<unsigned>(cut * PIECES)), dim3(WM * WN * 64), args, 0,
-                           stream);
+    if (e != hipSuccess) return e;
+    return launch_dma_streamk_fixup<OUT, WM, WN>(a, sk, a.grid.count(), stream);
 }
 
 template <class T, int OUT>

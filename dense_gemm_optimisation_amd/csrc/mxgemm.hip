@@ -17,9 +17,12 @@
 
 namespace libgemm {
 
-// The launch for one element width (defined in that width's part).
+// The launch for one element width (defined in that width's part): one
+// workgroup per tile when split is null, else the stream-K schedule `split`
+// with its partial tiles at `partials`, then its fix-up.
 template <int WIDTH>
-hipError_t mx_launch_width(const MxProblem &m, hipStream_t stream);
+hipError_t mx_launch_width(const MxProblem &m, const StreamKSplit *split, float *partials,
+                           hipStream_t stream);
 
 namespace {
 
@@ -61,61 +64,103 @@ F8Args mx_args(const MxProblem &m) {
 }
 
 template <int FA, int FB, int OUT>
-hipError_t mx_go(const MxProblem &m, hipStream_t stream) {
+hipError_t mx_go(const MxProblem &m, const StreamKSplit *split, float *partials,
+                 hipStream_t stream) {
+    constexpr int WM = LIBGEMM_F8_WM, WN = LIBGEMM_F8_WN;
     F8Args a = mx_args(m);
-    void *args[] = {&a};
-    return hipLaunchKernel(
-        reinterpret_cast<const void *>(&f8gemm_dma_kernel<FA, FB, OUT, LIBGEMM_F8_WM, LIBGEMM_F8_WN,
-                                                          LIBGEMM_F8_STAGES, true>),
-        dim3(static_cast<unsigned>(a.d.grid.count())), dim3(LIBGEMM_F8_WM * LIBGEMM_F8_WN * 64), args,
-        0, stream);
+    if (split == nullptr) {
+        void *args[] = {&a};
+        return hipLaunchKernel(
+            reinterpret_cast<const void *>(
+                &f8gemm_dma_kernel<FA, FB, OUT, WM, WN, LIBGEMM_F8_STAGES, true>),
+            dim3(static_cast<unsigned>(a.d.grid.count())), dim3(WM * WN * 64), args, 0, stream);
+    }
+    a.d.grid.xcds = 1;  // the work order itself spreads tiles over the dies
+    DmaStreamK sk{};
+    static_cast<StreamKSplit &>(sk) = *split;
+    sk.partials = partials;
+    const int64_t grid = streamk_grid(sk, HGEMM_STREAMK_MAX_GRID);
+    if (grid == 0) return hipSuccess;
+    void *args[] = {&a, &sk};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(
+            &f8gemm_dma_streamk_kernel<FA, FB, OUT, WM, WN, LIBGEMM_F8_STAGES, true>),
+        dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), args, 0, stream);
+    if (e != hipSuccess) return e;
+    return launch_dma_streamk_fixup<OUT, WM, WN>(a.d, sk, a.d.grid.count(), stream);
 }
 
 template <int FA, int FB>
-hipError_t mx_out(const MxProblem &m, hipStream_t stream) {
-    if (m.p.out == Elem::F32) return mx_go<FA, FB, OUT_F32>(m, stream);
-    if (m.p.out == Elem::BF16) return mx_go<FA, FB, OUT_BF16>(m, stream);
-    return mx_go<FA, FB, OUT_F16>(m, stream);
+hipError_t mx_out(const MxProblem &m, const StreamKSplit *split, float *partials,
+                  hipStream_t stream) {
+    if (m.p.out == Elem::F32) return mx_go<FA, FB, OUT_F32>(m, split, partials, stream);
+    if (m.p.out == Elem::BF16) return mx_go<FA, FB, OUT_BF16>(m, split, partials, stream);
+    return mx_go<FA, FB, OUT_F16>(m, split, partials, stream);
 }
 
 }  // namespace
 
 #if LIBGEMM_MX_HAS(0)
 template <>
-hipError_t mx_launch_width<8>(const MxProblem &m, hipStream_t stream) {
+hipError_t mx_launch_width<8>(const MxProblem &m, const StreamKSplit *split, float *partials,
+                              hipStream_t stream) {
     if (m.fa == FMT_E4M3)
-        return m.fb == FMT_E4M3 ? mx_out<FMT_E4M3, FMT_E4M3>(m, stream)
-                                : mx_out<FMT_E4M3, FMT_E5M2>(m, stream);
-    return m.fb == FMT_E4M3 ? mx_out<FMT_E5M2, FMT_E4M3>(m, stream)
-                            : mx_out<FMT_E5M2, FMT_E5M2>(m, stream);
+        return m.fb == FMT_E4M3 ? mx_out<FMT_E4M3, FMT_E4M3>(m, split, partials, stream)
+                                : mx_out<FMT_E4M3, FMT_E5M2>(m, split, partials, stream);
+    return m.fb == FMT_E4M3 ? mx_out<FMT_E5M2, FMT_E4M3>(m, split, partials, stream)
+                            : mx_out<FMT_E5M2, FMT_E5M2>(m, split, partials, stream);
 }
 #endif
 #if LIBGEMM_MX_HAS(1)
 template <>
-hipError_t mx_launch_width<6>(const MxProblem &m, hipStream_t stream) {
+hipError_t mx_launch_width<6>(const MxProblem &m, const StreamKSplit *split, float *partials,
+                              hipStream_t stream) {
     if (m.fa == FMT_E2M3)
-        return m.fb == FMT_E2M3 ? mx_out<FMT_E2M3, FMT_E2M3>(m, stream)
-                                : mx_out<FMT_E2M3, FMT_E3M2>(m, stream);
-    return m.fb == FMT_E2M3 ? mx_out<FMT_E3M2, FMT_E2M3>(m, stream)
-                            : mx_out<FMT_E3M2, FMT_E3M2>(m, stream);
+        return m.fb == FMT_E2M3 ? mx_out<FMT_E2M3, FMT_E2M3>(m, split, partials, stream)
+                                : mx_out<FMT_E2M3, FMT_E3M2>(m, split, partials, stream);
+    return m.fb == FMT_E2M3 ? mx_out<FMT_E3M2, FMT_E2M3>(m, split, partials, stream)
+                            : mx_out<FMT_E3M2, FMT_E3M2>(m, split, partials, stream);
 }
 #endif
 #if LIBGEMM_MX_HAS(2)
 template <>
-hipError_t mx_launch_width<4>(const MxProblem &m, hipStream_t stream) {
-    return mx_out<FMT_E2M1, FMT_E2M1>(m, stream);
+hipError_t mx_launch_width<4>(const MxProblem &m, const StreamKSplit *split, float *partials,
+                              hipStream_t stream) {
+    return mx_out<FMT_E2M1, FMT_E2M1>(m, split, partials, stream);
 }
 #endif
 
 #if LIBGEMM_MX_PART <= 0
-hipError_t launch_mxgemm(const MxProblem &m, hipStream_t stream) {
+namespace {
+
+hipError_t mx_launch(const MxProblem &m, const StreamKSplit *split, float *partials,
+                     hipStream_t stream) {
     const int w = mx_width(m.fa);
     if (w != mx_width(m.fb)) return hipErrorInvalidValue;
-    const int64_t tiles = ((m.p.M + F8_BM - 1) / F8_BM) * ((m.p.N + F8_BN - 1) / F8_BN) * m.p.batch;
-    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (w == 8) return mx_launch_width<8>(m, stream);
-    if (w == 6) return mx_launch_width<6>(m, stream);
-    return mx_launch_width<4>(m, stream);
+    if (f8_tiles(m.p.M, m.p.N, m.p.batch) > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (w == 8) return mx_launch_width<8>(m, split, partials, stream);
+    if (w == 6) return mx_launch_width<6>(m, split, partials, stream);
+    return mx_launch_width<4>(m, split, partials, stream);
+}
+
+}  // namespace
+
+hipError_t launch_mxgemm(const MxProblem &m, hipStream_t stream) {
+    return mx_launch(m, nullptr, nullptr, stream);
+}
+
+bool mxgemm_streamk_eligible(const MxProblem &m, bool force) {
+    return f8_streamk_worth(f8_tiles(m.p.M, m.p.N, m.p.batch), m.p.K, force);
+}
+
+int64_t mxgemm_streamk_bytes(const MxProblem &m) {
+    return 2 * f8_streamk_split(f8_tiles(m.p.M, m.p.N, m.p.batch), m.p.K).groups *
+           int64_t(SK_SLOT) * 4;
+}
+
+hipError_t launch_mxgemm_streamk(const MxProblem &m, void *workspace, hipStream_t stream) {
+    const StreamKSplit split = f8_streamk_split(f8_tiles(m.p.M, m.p.N, m.p.batch), m.p.K);
+    return mx_launch(m, &split, static_cast<float *>(workspace), stream);
 }
 #endif
 

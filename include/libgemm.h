@@ -31,13 +31,15 @@
  *   gemm_mx    block-scaled inputs (MXFP8, MXFP6, MXFP4: one E8M0 scale per
  *              32 elements along K), fp32 accumulation, output in fp32,
  *              bf16 or fp16.
- *   gemm_f32_ws, gemm_bf16_ws, gemm_f16_ws  the products with a caller-provided
- *              workspace, which lets the library copy unaligned operands
- *              into aligned ones and run the stream-K schedule (see below);
- *              gemm_workspace_size gives the bytes it needs.
+ *   gemm_f32_ws, gemm_bf16_ws, gemm_f16_ws, gemm_f8_ws, gemm_mx_ws
+ *              the products with a caller-provided workspace, which lets
+ *              the library copy unaligned operands into aligned ones and
+ *              run the stream-K schedule (see below); gemm_workspace_size
+ *              gives the bytes it needs.
  *   gemm_bf16_noalloc  gemm_bf16_ws on the library's own scratch memory.
  *   gemm_kernel_name, gemm_f8_kernel_name, gemm_mx_kernel_name,
- *   gemm_kernel_name_ws, gemm_kernel_name_bf16x3, gemm_kernel_name_quant
+ *   gemm_kernel_name_ws, gemm_f8_kernel_name_ws, gemm_mx_kernel_name_ws,
+ *   gemm_kernel_name_bf16x3, gemm_kernel_name_quant
  *              which kernel
  *              a GEMM call with the
  *              given arguments would launch (host only; for tests and
@@ -434,6 +436,43 @@ gemm_status_t gemm_f16_ws(int64_t M, int64_t N, int64_t K, float alpha,
                           int64_t strideB, int64_t strideC, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* 8-bit and block-scaled workspace entry points.  gemm_f8_ws takes the
+ * arguments of gemm_f8, gemm_mx_ws those of gemm_mx, each plus a workspace
+ * under the rules of gemm_bf16_ws, and computes the same product.  With at
+ * least gemm_workspace_size() bytes, a call on the direct-load kernel
+ * (gemm_f8's fast path; every gemm_mx call that multiplies) whose 256 x 256
+ * tiles leave the last wave of one workgroup per compute unit partly idle
+ * runs on the stream-K schedule described for gemm_bf16_ws ("CUDA GEMM 矩阵
+ * 乘法优化指南", blog.zhenwei.site, section 12.5), a k step being 128 k,
+ * when the cost model of the 16-bit direct-load kernel (about 0.14 k steps
+ * per partial tile plus two) says it pays; GEMM_TEST_FORCE_STREAMK chooses
+ * it wherever tiles are left over.  The pieces of a cut tile start and end
+ * at multiples of 128 k and are added in a fixed order, so results are
+ * deterministic and within the accuracy stated for gemm_f8 and gemm_mx
+ * (products of small integers stay exact).  Every other call ignores the
+ * workspace.  A misaligned or NULL (with bytes > 0) workspace, or one that
+ * overlaps A, B, C or (gemm_mx_ws) a scale array, is GEMM_ERR_INVALID_ARG;
+ * everything else is as for gemm_f8 / gemm_mx. */
+gemm_status_t gemm_f8_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                         const uint8_t *A, int64_t lda, gemm_order_t orderA,
+                         gemm_f8_format_t formatA, const uint8_t *B, int64_t ldb,
+                         gemm_order_t orderB, gemm_f8_format_t formatB,
+                         float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                         gemm_output_t typeC, int64_t batch, int64_t strideA,
+                         int64_t strideB, int64_t strideC, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+gemm_status_t gemm_mx_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                         const void *A, int64_t lda, gemm_mx_format_t formatA,
+                         const uint8_t *scaleA, int64_t ldsa,
+                         const void *B, int64_t ldb, gemm_mx_format_t formatB,
+                         const uint8_t *scaleB, int64_t ldsb,
+                         float beta, void *C, int64_t ldc, gemm_order_t orderC,
+                         gemm_output_t typeC, int64_t batch, int64_t strideA,
+                         int64_t strideB, int64_t strideScaleA,
+                         int64_t strideScaleB, int64_t strideC, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Allocation-free variant of gemm_bf16_ws, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.
@@ -596,6 +635,39 @@ const char *gemm_mx_kernel_name(int64_t M, int64_t N, int64_t K, float alpha,
                                 int64_t batch, int64_t strideA, int64_t strideB,
                                 int64_t strideScaleA, int64_t strideScaleB,
                                 int64_t strideC);
+
+/* The kernel gemm_f8_ws would launch: the names of gemm_f8_kernel_name, or
+ * "f8gemm_mfma_dma_streamk" for the stream-K schedule; "" and NULL as for
+ * gemm_kernel_name, whose testing switches apply, GEMM_TEST_FORCE_STREAMK
+ * included.  The workspace is only checked, never dereferenced. */
+const char *gemm_f8_kernel_name_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                                   const uint8_t *A, int64_t lda,
+                                   gemm_order_t orderA, gemm_f8_format_t formatA,
+                                   const uint8_t *B, int64_t ldb,
+                                   gemm_order_t orderB, gemm_f8_format_t formatB,
+                                   float beta, const void *C, int64_t ldc,
+                                   gemm_order_t orderC, gemm_output_t typeC,
+                                   int64_t batch, int64_t strideA,
+                                   int64_t strideB, int64_t strideC,
+                                   const void *workspace, size_t workspace_bytes);
+
+/* The kernel gemm_mx_ws would launch: the names of gemm_mx_kernel_name, or
+ * "mxgemm_mfma_dma_streamk" for the stream-K schedule (GEMM_TEST_FORCE_STREAMK
+ * and GEMM_TEST_FORCE_GENERAL, which keeps one workgroup per tile, apply).
+ * Host only; no pointer is dereferenced. */
+const char *gemm_mx_kernel_name_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                                   const void *A, int64_t lda,
+                                   gemm_mx_format_t formatA,
+                                   const uint8_t *scaleA, int64_t ldsa,
+                                   const void *B, int64_t ldb,
+                                   gemm_mx_format_t formatB,
+                                   const uint8_t *scaleB, int64_t ldsb,
+                                   float beta, const void *C, int64_t ldc,
+                                   gemm_order_t orderC, gemm_output_t typeC,
+                                   int64_t batch, int64_t strideA, int64_t strideB,
+                                   int64_t strideScaleA, int64_t strideScaleB,
+                                   int64_t strideC, const void *workspace,
+                                   size_t workspace_bytes);
 
 /* The kernel gemm_f32_ws (in = GEMM_INPUT_F32; c_dtype is then ignored),
  * gemm_bf16_ws (GEMM_INPUT_BF16) or gemm_f16_ws (GEMM_INPUT_F16) would

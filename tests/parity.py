@@ -259,8 +259,9 @@ def run(p: workloads.Problem, *, seed=None, host=None, sample=None, c_init=None,
     c_init: a value written over the whole initial C (e.g. NaN when beta == 0).
     base_offset: elements by which each device base pointer is shifted (to
     test misaligned bases).
-    use_workspace: call the workspace entry point (bf16/fp16) with the
-    shared workspace, of workspace_bytes bytes (default: all of it).
+    use_workspace: call the workspace entry point (gemm_f32_ws, gemm_bf16_ws,
+    gemm_f16_ws, gemm_f8_ws) with the shared workspace, of workspace_bytes
+    bytes (default: all of it).
     Returns (Result, output bits of the whole C buffer including guards).
     """
     log(f"[parity] {p.name} {p.in_dtype}->{p.c_dtype} M={p.M} N={p.N} K={p.K} "
@@ -397,10 +398,12 @@ def mx_int_patterns(rng, fmt, batch, rows, K):
     return (lut[v] | np.where(neg, sign, 0)).astype(np.uint8)
 
 
-def run_mx(p: "workloads.MxProblem", *, seed=None, sample=None, repeat=1, patterns=None):
-    """Run a block-scaled problem through gemm_mx and compare with the oracle
-    (every element, or `sample` as in run()).  patterns: optional element
-    patterns for A and B (see workloads.generate_mx)."""
+def run_mx(p: "workloads.MxProblem", *, seed=None, sample=None, repeat=1, patterns=None,
+           use_workspace=False):
+    """Run a block-scaled problem through gemm_mx (gemm_mx_ws with the shared
+    workspace when use_workspace) and compare with the oracle (every element,
+    or `sample` as in run()).  patterns: optional element patterns for A and
+    B (see workloads.generate_mx)."""
     log(f"[parity] {p.name} mx {p.fa}x{p.fb}->{p.c_dtype} M={p.M} N={p.N} K={p.K} "
         f"batch={p.batch} orderC={p.order_c} ld={p.lda},{p.ldb},{p.ldc} lds={p.ldsa},{p.ldsb} "
         f"alpha={p.alpha} beta={p.beta}")
@@ -416,13 +419,20 @@ def run_mx(p: "workloads.MxProblem", *, seed=None, sample=None, repeat=1, patter
             p.ldsa, db.data_ptr(), p.ldb, binding.MX_FORMAT[p.fb], dsb.data_ptr(), p.ldsb, p.beta,
             pc, p.ldc, p.order_c, out_t[p.c_dtype], p.batch, p.stride_a, p.stride_b, p.stride_sa,
             p.stride_sb, p.stride_c)
-    kernel = binding.mx_kernel_name(*args)
+    ws = {}
+    if use_workspace:
+        w = workspace()
+        ws = dict(workspace=w.data_ptr(), workspace_bytes=w.numel() * 4)
+    kernel = binding.mx_kernel_name(*args, **ws)
     cview = np.int32 if p.c_dtype == "f32" else np.int16
     outs = []
     for r in range(repeat):
         if r:
             dc.copy_(torch.from_numpy(fc.view(cview)))
-        binding.gemm_mx(*args)
+        if use_workspace:
+            binding.gemm_mx_ws(*args, ws["workspace"], ws["workspace_bytes"])
+        else:
+            binding.gemm_mx(*args)
         torch.cuda.synchronize()
         outs.append(dc.cpu().numpy().view(fc.dtype).copy())
     out = outs[0]

@@ -36,9 +36,11 @@ def test_header_declares_the_boundary():
                                     "gemm_f32_bf16x3_workspace_size", "gemm_f32_bias_act",
                                     "gemm_f32_valu", "gemm_f32_ws",
                                     "gemm_f8",
-                                    "gemm_f8_kernel_name", "gemm_kernel_name",
+                                    "gemm_f8_kernel_name", "gemm_f8_kernel_name_ws",
+                                    "gemm_f8_ws", "gemm_kernel_name",
                                     "gemm_kernel_name_bf16x3", "gemm_kernel_name_quant",
                                     "gemm_kernel_name_ws", "gemm_mx", "gemm_mx_kernel_name",
+                                    "gemm_mx_kernel_name_ws", "gemm_mx_ws",
                                     "gemm_status_string",
                                     "gemm_test_switches", "gemm_workspace_size"]
 
@@ -394,12 +396,13 @@ def test_kernel_choice_for_every_workload(lib, clean_env):
             "bf16_edge": "hgemm_mfma", "bf16_tail": "hgemm_mfma_dma", "bf16_skinny": "gemm_skinny",
             "bf16_attn_qk": "hgemm_mfma_dma", "bf16_attn_pv": "hgemm_mfma_dma",
             "bf16_ffn_up_gelu": "hgemm_mfma_dma", "fp8_4096": "f8gemm_mfma_dma",
+            "fp8_tail": "f8gemm_mfma_dma",
             "bf16_ffn_up_gelu_e4m3": "hgemm_mfma_dma",
             # called through gemm_f32_valu and gemm_f32_bf16x3; gemm_kernel_name
             # describes gemm_f32
             "f32_4096_valu": "sgemm_mfma_dma", "f32_4096_bf16x3": "sgemm_mfma_dma"}
     mx = {n for n, p in workloads.CONFIGS.items() if isinstance(p, workloads.MxProblem)}
-    assert mx == {"mxfp4_4096", "mxfp6_4096", "mxfp8_4096"}
+    assert mx == {"mxfp4_4096", "mxfp6_4096", "mxfp8_4096", "mxfp4_tail"}
     assert sorted(want) == sorted(set(workloads.CONFIGS) - mx)
     for name in mx:
         p = workloads.config(name)
@@ -670,3 +673,102 @@ def test_quant_unsupported_and_invalid(lib):
     assert lib.library().gemm_bf16_quant(64, 64, 64, 1.0, GB, 64, 0, 2 * GB, 64, 0, 3 * GB, 64, 0,
                                          7, 1.0, 1, 0, 0, 0, None, 0, 0, None) == -1  # bad format
     assert call(dt="f16", fmt="e5m2", oa=1, ob=1, M=4095, N=4095, lda=4095) == -2
+
+
+# ------------------------------------------------------------------ 8-bit and MX workspace entry points
+
+
+def f8_ws(lib, M, N, K, ws=WS, nbytes=None, name=True, **kw):
+    """gemm_f8_ws (name=False) or gemm_f8_kernel_name_ws with fake addresses:
+    E4M3 x E5M2, row-major A, column-major B (both K-contiguous), bf16 C."""
+    oa, ob = kw.pop("oa", 0), kw.pop("ob", 1)
+    lda = kw.pop("lda", K if oa == 0 else M)
+    ldb = kw.pop("ldb", N if ob == 0 else K)
+    batch = kw.pop("batch", 1)
+    strides = (M * K, K * N, M * N) if batch > 1 else (0, 0, 0)
+    C = kw.pop("C", 3 * GB)
+    nbytes = lib.workspace_size() if nbytes is None else nbytes
+    args = (M, N, K, kw.pop("alpha", 1.0), GB, lda, oa, lib.F8_E4M3, 2 * GB, ldb, ob,
+            lib.F8_E5M2, 0.0, C, N, 0, lib.OUTPUT_BF16, batch, *strides)
+    assert not kw, kw
+    if name:
+        return lib.f8_kernel_name(*args, workspace=ws, workspace_bytes=nbytes)
+    return lib.gemm_f8_ws(*args, ws, nbytes, raise_on_error=False)
+
+
+def test_f8_streamk_kernel_choice(lib, clean_env):
+    # 272 tiles of 32 k steps (128 k each): the cut tail pays for its exchange
+    assert f8_ws(lib, 4096, 4352, 4096) == "f8gemm_mfma_dma_streamk"
+    assert f8_ws(lib, 4096, 4352, 4096, batch=2) == "f8gemm_mfma_dma"   # 544 tiles: nearly full
+    assert f8_ws(lib, 4096, 4096, 4096) == "f8gemm_mfma_dma"            # whole waves
+    assert f8_ws(lib, 4096, 4352, 512) == "f8gemm_mfma_dma"             # 4 steps per tile
+    assert f8_ws(lib, 2048, 2304, 1024) == "f8gemm_mfma_dma"            # 72 tiles of 8 steps
+    # no workspace, or one that is too small: the plain kernel
+    assert f8_ws(lib, 4096, 4352, 4096, ws=0, nbytes=0) == "f8gemm_mfma_dma"
+    assert f8_ws(lib, 4096, 4352, 4096, nbytes=1 << 20) == "f8gemm_mfma_dma"
+    assert lib.f8_kernel_name(4096, 4352, 4096, 1.0, GB, 4096, 0, 0, 2 * GB, 4096, 1, 1, 0.0,
+                              3 * GB, 4352, 0, 1) == "f8gemm_mfma_dma"
+    # operands the direct-load kernel cannot read keep the general kernel
+    assert f8_ws(lib, 4096, 4352, 4096, ob=0) == "f8gemm_mfma"
+    assert f8_ws(lib, 4096, 4352, 4104, lda=4104, ldb=4104) == "f8gemm_mfma"
+    clean_env(lib.TEST_FORCE_STREAMK)
+    assert f8_ws(lib, 2048, 2304, 1024) == "f8gemm_mfma_dma_streamk"
+    assert f8_ws(lib, 4096, 4352, 512) == "f8gemm_mfma_dma_streamk"
+    assert f8_ws(lib, 4096, 4096, 4096) == "f8gemm_mfma_dma"            # nothing to cut
+    assert f8_ws(lib, 4096, 4352, 4096, ob=0) == "f8gemm_mfma"
+    clean_env(lib.TEST_FORCE_GENERAL)
+    assert f8_ws(lib, 4096, 4352, 4096) == "f8gemm_mfma"
+
+
+def test_f8_ws_invalid_workspace(lib):
+    assert f8_ws(lib, 4096, 4352, 4096, ws=WS + 8) is None              # not 256-byte aligned
+    assert f8_ws(lib, 4096, 4352, 4096, ws=0) is None                   # NULL with bytes
+    assert f8_ws(lib, 4096, 4352, 4096, ws=2 * GB) is None              # overlaps B
+    assert f8_ws(lib, 4096, 4352, 4096, C=WS + 4096) is None            # C inside it
+    for kw in (dict(ws=WS + 8), dict(ws=0), dict(ws=GB + 256)):
+        assert f8_ws(lib, 4096, 4352, 4096, name=False, **kw) == lib.ERR_INVALID_ARG, kw
+    # a format or output type out of range
+    assert lib.gemm_f8_ws(8, 8, 8, 1.0, GB, 8, 0, 2, 2 * GB, 8, 1, 0, 0.0, 3 * GB, 8, 0, 1, 1, 0,
+                          0, 0, WS, lib.workspace_size(), raise_on_error=False) == lib.ERR_INVALID_ARG
+    assert f8_ws(lib, 0, 4352, 4096, name=False) == lib.OK              # empty: nothing launched
+
+
+def mx_ws(lib, ws=WS, nbytes=None, **kw):
+    """gemm_mx_kernel_name_ws (name=True, default) or gemm_mx_ws for an MXFP4
+    problem, 4096 x 4352 x 4096 unless given, bf16 C, with fake addresses 4
+    GiB apart: A at GB, its scales at 2 GB, B at 3 GB, B's scales at 4 GB, C
+    at 6 GB (the workspace WS sits at 5 GB)."""
+    M, N, K = kw.pop("M", 4096), kw.pop("N", 4352), kw.pop("K", 4096)
+    name = kw.pop("name", True)
+    sb = 4 * (-(-K // 128))
+    args = (M, N, K, 1.0, GB, K, 4, 2 * GB, sb, 3 * GB, K, 4, 4 * GB, sb, 0.0, 6 * GB, N, 0, 1, 1,
+            0, 0, 0, 0, 0)
+    assert not kw, kw
+    nbytes = lib.workspace_size() if nbytes is None else nbytes
+    if name:
+        return lib.mx_kernel_name(*args, workspace=ws, workspace_bytes=nbytes)
+    return lib.gemm_mx_ws(*args, ws, nbytes, raise_on_error=False)
+
+
+def test_mx_streamk_kernel_choice(lib, clean_env):
+    assert mx_ws(lib) == "mxgemm_mfma_dma_streamk"                      # 272 tiles, 32 steps
+    assert mx_ws(lib, N=4096) == "mxgemm_mfma_dma"                      # whole waves
+    assert mx_ws(lib, K=512) == "mxgemm_mfma_dma"                       # 4 steps per tile
+    assert mx_ws(lib, ws=0, nbytes=0) == "mxgemm_mfma_dma"
+    assert mx_ws(lib, nbytes=1 << 20) == "mxgemm_mfma_dma"
+    clean_env(lib.TEST_FORCE_STREAMK)
+    assert mx_ws(lib, M=300, N=260, K=256) == "mxgemm_mfma_dma_streamk"
+    assert mx_ws(lib, K=512) == "mxgemm_mfma_dma_streamk"
+    assert mx_ws(lib, N=4096) == "mxgemm_mfma_dma"                      # nothing to cut
+    clean_env(lib.TEST_FORCE_GENERAL)
+    assert mx_ws(lib) == "mxgemm_mfma_dma"                              # one workgroup per tile
+
+
+def test_mx_ws_invalid_workspace(lib):
+    # misaligned, NULL with bytes, and overlapping A, A's scales, B, B's
+    # scales or C
+    for ws in (WS + 4, 0, GB + 256, 2 * GB, 3 * GB + 4096, 4 * GB, 6 * GB + 512):
+        assert mx_ws(lib, ws=ws) is None, ws
+        assert mx_ws(lib, ws=ws, name=False) == lib.ERR_INVALID_ARG, ws
+    # without a workspace NULL is fine
+    assert mx_ws(lib, ws=0, nbytes=0) == "mxgemm_mfma_dma"

@@ -200,7 +200,7 @@ def test_repeat_runs_bit_identical(dt):
 SMALL_CONFIGS = ["f32_256"]
 FULL_CONFIGS = ["f32_4096", "bf16_4096", "f16_4096", "f32_edge", "bf16_edge", "bf16_tail", "bf16_skinny",
                 "bf16_attn_qk", "bf16_attn_pv", "bf16_qkv", "bf16_ffn_up", "bf16_ffn_down",
-                "bf16_ffn_up_gelu", "bf16_ffn_up_gelu_e4m3", "fp8_4096"]
+                "bf16_ffn_up_gelu", "bf16_ffn_up_gelu_e4m3", "fp8_4096", "fp8_tail"]
 
 
 @pytest.mark.parametrize("name", SMALL_CONFIGS)
@@ -993,10 +993,10 @@ MX_PAIRS = [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e2m3", "e2m3"), ("e3m2", "e2m3
             ("e2m1", "e2m1")]
 
 
-def check_mx(p, **kw):
+def check_mx(p, kernel="mxgemm_mfma_dma", **kw):
     res, out = run_mx(p, **kw)
     assert res.ok, res.why
-    assert res.kernel == "mxgemm_mfma_dma", f"{p.name} ran on {res.kernel!r}"
+    assert res.kernel == kernel, f"{p.name} ran on {res.kernel!r}"
     return res, out
 
 
@@ -1053,6 +1053,89 @@ def test_mx_alpha_zero_and_k_zero_scale_c():
 @pytest.mark.parametrize("name", ["mxfp4_4096", "mxfp6_4096", "mxfp8_4096"])
 def test_mx_full_size_sampled(name):
     check_mx(workloads.config(name), sample="auto")
+
+
+# ------------------------------------------------------------------ 8-bit and MX stream-K (workspace)
+
+# The narrow-float direct-load kernel's stream-K schedule (256 x 256 tiles,
+# 128-k steps).  Small problems only take it when forced; the shapes cover
+# a K that ends in a partial stage (1040 = 8 * 128 + 16, 1088 = 8.5 * 128),
+# ragged M and N, all cut tiles (fewer tiles than compute units) and whole
+# waves plus a cut remainder (batches).
+F8_SK_SHAPES = [(2048, 2304, 1024), (2000, 2100, 1040), (1300, 1100, 1088)]
+
+
+@pytest.mark.parametrize("pair", [("e4m3", "e4m3"), ("e5m2", "e4m3")], ids="-".join)
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", F8_SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f8_streamk(pair, out, shape, force_streamk):
+    fa, fb = pair
+    M, N, K = shape
+    check(F8(f"f8-streamk-{fa}-{fb}-{out}", fa, fb, out, M, N, K, alpha=0.75, beta=0.5, **TN),
+          kernel="f8gemm_mfma_dma_streamk", seed=M + N + K, use_workspace=True, repeat=2)
+
+
+def test_f8_streamk_whole_waves_fp16_output_and_col_major_c(force_streamk):
+    # 65 batches of 2 x 2 tiles: 256 whole, 4 cut over the grid
+    check(F8("f8-streamk-dp", "e4m3", "e5m2", "f16", 512, 512, 2048, beta=0.5, batch=65, **TN),
+          kernel="f8gemm_mfma_dma_streamk", seed=94, use_workspace=True, repeat=2)
+    check(F8("f8-streamk-colC", "e5m2", "e4m3", "bf16", 2304, 2048, 1024, order_c=COL,
+             beta=0.5, **TN), kernel="f8gemm_mfma_dma_streamk", seed=95, use_workspace=True)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_f8_streamk_integers_bit_exact(out, force_streamk):
+    p = F8(f"f8-streamk-int-{out}", "e4m3", "e5m2", out, 2048, 2304, 1024, alpha=2.0, beta=1.0,
+           **TN)
+    res, _ = check(p, kernel="f8gemm_mfma_dma_streamk",
+                   host=_int_host_f8(p, np.random.default_rng(96)), use_workspace=True, repeat=2)
+    assert res.max_err == 0.0 and res.max_ulp == 0
+
+
+def test_f8_streamk_tail_config_sampled():
+    # 4096 x 4352 x 4096 in E4M3: 272 tiles on 256 compute units, the cost
+    # model's own choice (no switch), compared on sampled elements
+    check(workloads.config("fp8_tail"), kernel="f8gemm_mfma_dma_streamk", sample="auto",
+          use_workspace=True, repeat=2)
+
+
+MX_SK_PAIRS = [("e4m3", "e5m2"), ("e2m3", "e3m2"), ("e2m1", "e2m1")]
+
+
+@pytest.mark.parametrize("fa,fb", MX_SK_PAIRS, ids=lambda f: f)
+@pytest.mark.parametrize("shape", [(600, 700, 1088), (1300, 1100, 2048)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mx_streamk(fa, fb, shape, force_streamk):
+    # K = 1088 leaves a last stage of 64 k: the piece that ends there must
+    # not use the scale padding bytes (NaN patterns) past the last block
+    M, N, K = shape
+    check_mx(workloads.MxProblem(f"mx-streamk-{fa}-{fb}", fa, fb, "bf16", M, N, K, alpha=0.5,
+                                 beta=1.0), kernel="mxgemm_mfma_dma_streamk", seed=M + K,
+             repeat=2, use_workspace=True)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m1", "e2m1")], ids=lambda f: f)
+def test_mx_streamk_integers_bit_exact_batches_and_col_major_c(fa, fb, force_streamk):
+    M, N, K, batch = 520, 600, 1024, 3
+    rng = np.random.default_rng(98)
+    pats = (mx_int_patterns(rng, fa, batch, M, K), mx_int_patterns(rng, fb, batch, N, K))
+    p = workloads.MxProblem("mx-streamk-int", fa, fb, "f32", M, N, K, alpha=2.0, beta=0.0,
+                            batch=batch, scale_lo=126, scale_hi=128)
+    res, _ = check_mx(p, kernel="mxgemm_mfma_dma_streamk", seed=99, patterns=pats,
+                      use_workspace=True, repeat=2)
+    assert res.max_err == 0.0
+    check_mx(workloads.MxProblem("mx-streamk-colC", fa, fb, "bf16", 700, 520, 512, order_c=COL,
+                                 ldc=703, beta=2.0), kernel="mxgemm_mfma_dma_streamk", seed=100,
+             use_workspace=True)
+
+
+def test_mx_streamk_tail_config_sampled():
+    # MXFP4 at 4096 x 4352 x 4096 (272 tiles): the cost model's own choice,
+    # sampled; without the workspace the same workload runs one workgroup
+    # per tile
+    check_mx(workloads.config("mxfp4_tail"), kernel="mxgemm_mfma_dma_streamk", sample="auto",
+             use_workspace=True)
+    check_mx(workloads.config("mxfp4_tail"), sample="auto")
 
 
 # ------------------------------------------------------------------ quantised (8-bit) output

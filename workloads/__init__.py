@@ -442,6 +442,12 @@ def _configs():
                   note="MXFP8 4096^3 (E4M3 elements, E8M0 scale per 32 k), bf16 out"),
         Problem("fp8_4096", "e4m3", "bf16", 4096, 4096, 4096, order_b=COL,
                 note="E4M3 GEMM 4096^3, A row-major, B column-major, fp32 accumulate, bf16 out"),
+        # 16 x 17 = 272 tiles of 256 x 256 again: the stream-K case of the
+        # narrow-float kernel (through the workspace entry points)
+        Problem("fp8_tail", "e4m3", "bf16", 4096, 4352, 4096, order_b=COL,
+                note="E4M3 4096x4352x4096 TN, bf16 out (272 tiles: one wave plus 16)"),
+        MxProblem("mxfp4_tail", "e2m1", "e2m1", "bf16", 4096, 4352, 4096,
+                  note="MXFP4 4096x4352x4096, bf16 out (272 tiles: one wave plus 16)"),
     ]
     return {c.name: c for c in cfgs}
 
