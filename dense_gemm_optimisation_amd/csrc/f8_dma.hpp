@@ -158,11 +158,22 @@ using dma::direct_load4;
 #ifndef LIBGEMM_F8_STAGES
 #define LIBGEMM_F8_STAGES 2
 #endif
+// 4-bit elements: a stage is 34 KiB (two 16 KiB panels and the scales), so
+// four fit, and the epilogue stages C across two of them
+#ifndef LIBGEMM_MX4_STAGES
+#define LIBGEMM_MX4_STAGES 4
+#endif
 #ifndef LIBGEMM_F8_GROUP_M
 #define LIBGEMM_F8_GROUP_M 16
 #endif
 
 constexpr int F8_BM = 256, F8_BN = 256;
+
+// Stage buffers in the ring for formats FA, FB.
+template <int FA, int FB>
+constexpr int f8_stages() {
+    return Fmt<FA>::WIDTH == 4 && Fmt<FB>::WIDTH == 4 ? LIBGEMM_MX4_STAGES : LIBGEMM_F8_STAGES;
+}
 
 // The sizes of the kernel's tiles, panels and stages for formats FA, FB.
 template <int FA, int FB, int WAVES_M, int WAVES_N, bool MX>
@@ -180,7 +191,10 @@ struct F8Tile {
     static constexpr int SCALES = MX ? 4 * (F8_BM + F8_BN) : 0;  // bytes per stage
     static constexpr int DATA = PANEL_A + PANEL_B + SCALES;
     static constexpr int EPI = WAVES * 32 * WTN * 4;              // epilogue staging
-    static constexpr int STAGE = DATA > EPI ? DATA : EPI;
+    // A stage buffer holds one stage's data; C is staged across the NEED
+    // consecutive buffers the epilogue takes (f8_tile_store).
+    static constexpr int STAGE = DATA;
+    static constexpr int NEED = (EPI + STAGE - 1) / STAGE;
     static constexpr int PER_DATA = OpA::PER_WAVE + OpB::PER_WAVE;
     static constexpr int PER_STAGE = PER_DATA + (MX ? 1 : 0);  // direct loads per wave per stage
     static_assert(FM % 2 == 0, "A fragments alternate between two slots");
@@ -395,18 +409,23 @@ __device__ __forceinline__ int f8_tile_steps(
     return buf;
 }
 
-// The epilogue of a whole tile: C is staged in the ring buffer after the
-// last stage's (`buf`): every wave finished reading it before the last
-// barrier and no load targets it any more.
+// The epilogue of a whole tile: C is staged in ring buffers the last stage
+// (in `buf`) does not use: every wave finished reading them before the last
+// barrier and no load targets them any more.  Staging takes NEED
+// consecutive buffers: the next one when one suffices, else the first NEED
+// or the NEED after them, whichever excludes the last stage's.
 template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX>
 __device__ __forceinline__ void f8_tile_store(
     const F8Args &p, LDS char *lds, const TileCoord &t, int buf,
     const f32x16 (&acc)[F8_BM / WAVES_M / 32][F8_BN / WAVES_N / 32]) {
     using L = F8Tile<FA, FB, WAVES_M, WAVES_N, MX>;
+    constexpr int NEED = L::NEED;
+    static_assert(NEED == 1 || 2 * NEED <= STAGES, "epilogue staging fits beside the last stage");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    LDS char *stage_free = lds + (buf + 1 == STAGES ? 0 : buf + 1) * L::STAGE;
+    const int free0 = NEED == 1 ? (buf + 1 == STAGES ? 0 : buf + 1) : (buf >= NEED ? 0 : NEED);
+    LDS char *stage_free = lds + free0 * L::STAGE;
     store_tile_lds<OUT, L::FM, L::FN>(p.d, acc, t.batch, t.tm * F8_BM + wm * L::WTM,
                                       t.tn * F8_BN + wn * L::WTN, lane,
                                       reinterpret_cast<LDS float *>(stage_free) + wave * 32 * L::WTN);

@@ -192,7 +192,7 @@ struct LaunchDma {
         void *args[] = {&a};
         return hipLaunchKernel(
             reinterpret_cast<const void *>(&f8gemm_dma_kernel<FA, FB, OUT, LIBGEMM_F8_WM,
-                                                              LIBGEMM_F8_WN, LIBGEMM_F8_STAGES, false>),
+                                                              LIBGEMM_F8_WN, f8_stages<FA, FB>(), false>),
             dim3(static_cast<unsigned>(a.d.grid.count())), dim3(LIBGEMM_F8_WM * LIBGEMM_F8_WN * 64),
             args, 0, stream);
     }
@@ -213,7 +213,7 @@ struct LaunchDmaStreamK {
         void *args[] = {&l.a, &l.sk};
         const hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void *>(
-                &f8gemm_dma_streamk_kernel<FA, FB, OUT, WM, WN, LIBGEMM_F8_STAGES, false>),
+                &f8gemm_dma_streamk_kernel<FA, FB, OUT, WM, WN, f8_stages<FA, FB>(), false>),
             dim3(static_cast<unsigned>(l.grid)), dim3(WM * WN * 64), args, 0, stream);
         if (e != hipSuccess) return e;
         return launch_dma_streamk_fixup<OUT, WM, WN>(l.a.d, l.sk, l.a.d.grid.count(), stream);

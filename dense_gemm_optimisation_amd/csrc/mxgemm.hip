@@ -72,7 +72,7 @@ hipError_t mx_go(const MxProblem &m, const StreamKSplit *split, float *partials,
         void *args[] = {&a};
         return hipLaunchKernel(
             reinterpret_cast<const void *>(
-                &f8gemm_dma_kernel<FA, FB, OUT, WM, WN, LIBGEMM_F8_STAGES, true>),
+                &f8gemm_dma_kernel<FA, FB, OUT, WM, WN, f8_stages<FA, FB>(), true>),
             dim3(static_cast<unsigned>(a.d.grid.count())), dim3(WM * WN * 64), args, 0, stream);
     }
     a.d.grid.xcds = 1;  // the work order itself spreads tiles over the dies
@@ -84,7 +84,7 @@ hipError_t mx_go(const MxProblem &m, const StreamKSplit *split, float *partials,
     void *args[] = {&a, &sk};
     const hipError_t e = hipLaunchKernel(
         reinterpret_cast<const void *>(
-            &f8gemm_dma_streamk_kernel<FA, FB, OUT, WM, WN, LIBGEMM_F8_STAGES, true>),
+            &f8gemm_dma_streamk_kernel<FA, FB, OUT, WM, WN, f8_stages<FA, FB>(), true>),
         dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), args, 0, stream);
     if (e != hipSuccess) return e;
     return launch_dma_streamk_fixup<OUT, WM, WN>(a.d, sk, a.d.grid.count(), stream);
