@@ -107,7 +107,55 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void dma_streamk_fixup(DmaAr
     const int64_t row = t.tm * BM + wm * WTM + i * 32 + (lane & 31);
     const int64_t col0 = t.tn * BN + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
     if (row >= p.M) return;
-    char *Cb = static_cast<char *>(p.C) + t.batch * p.sC * (OUT == OUT_F32 ? 4 : 2);
+    constexpr int ESZ = OUT == OUT_F32 ? 4 : 2;
+    char *Cb = static_cast<char *>(p.C) + t.batch * p.sC * ESZ;
+    // the lane's four columns as one aligned vector access when they are
+    // all inside C and their address allows it (one 16- or 8-byte store
+    // instead of four)
+    char *quad = Cb + (row * p.ldc + col0) * ESZ;
+    if (col0 + 3 < p.N && reinterpret_cast<uintptr_t>(quad) % (4 * ESZ) == 0) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = p.alpha * sum[e];
+        if (OUT == OUT_F32) {
+            if (p.beta != 0.0f) {
+                const f32x4 o = *reinterpret_cast<const f32x4 *>(quad);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(p.beta, o[e], x[e]);
+            }
+        } else if (p.beta != 0.0f) {
+            const u32x2 o = *reinterpret_cast<const u32x2 *>(quad);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t b = uint16_t(o[e / 2] >> (16 * (e % 2)));
+                const float v = OUT == OUT_BF16 ? __builtin_bit_cast(float, uint32_t(b) << 16)
+                                                : static_cast<float>(__builtin_bit_cast(_Float16, b));
+                x[e] = __builtin_fmaf(p.beta, v, x[e]);
+            }
+        }
+        if (p.epi.active())
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = epilogue_apply(p.epi, x[e], t.batch, row, col0 + e);
+        if (OUT == OUT_F32) {
+            *reinterpret_cast<f32x4 *>(quad) = x;
+        } else {
+            u32x2 w;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint16_t lo, hi;
+                if (OUT == OUT_BF16) {
+                    lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2 * h]));
+                    hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2 * h + 1]));
+                } else {
+                    lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x[2 * h]));
+                    hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x[2 * h + 1]));
+                }
+                w[h] = uint32_t(lo) | (uint32_t(hi) << 16);
+            }
+            *reinterpret_cast<u32x2 *>(quad) = w;
+        }
+        return;
+    }
     float old[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
