@@ -84,6 +84,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void dma_streamk_fixup(DmaAr
     const int64_t g0 = sk_owner(sk, local * S), g1 = sk_owner(sk, local * S + S - 1);
     if (g0 == g1) return;
     const int tid = threadIdx.x;
+    // Every owner but the last ends its range inside this tile, so its piece
+    // is the one holding its last iteration, in slot 2g; only the last
+    // owner's range may go on into the next tile.
+    const int64_t slot1 = sk_slot(sk, g1, local, sk_end(sk, g1));
     f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t g = g0; g <= g1; g += BATCH) {
         u32x4 v[BATCH];
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void dma_streamk_fixup(DmaAr
             const int64_t gu = g + u <= g1 ? g + u : g1;
             const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
             v[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, sk_slot(sk, gu, local, sk_end(sk, gu))), off,
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, gu == g1 ? slot1 : 2 * gu), off,
                                                              piece * THREADS * 16, 0));
         }
 #pragma unroll

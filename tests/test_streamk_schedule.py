@@ -155,6 +155,10 @@ def test_fixup_reads_exactly_the_written_pieces(sk, tiles, S, G, ratio):
         else:
             # the fix-up adds the written slots in increasing workgroup order
             assert reads == [slot for _, slot in written] and len(reads) >= 2
+            # every owner but the last wrote the piece holding its last
+            # iteration, slot 2w: the direct-load fix-up computes only the
+            # last owner's slot
+            assert all(slot == 2 * w for w, slot in written[:-1])
             ranges = sorted((int(kb), int(ke)) for _, _, kb, ke, _ in mine)
             assert ranges[0][0] == 0 and ranges[-1][1] == S
             assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
