@@ -716,6 +716,8 @@ __global__ __launch_bounds__(THREADS) void hgemm_streamk_fixup(HgemmArgs p, Stre
     const int64_t g0 = sk_owner(sk, local * S), g1 = sk_owner(sk, local * S + S - 1);
     if (g0 == g1) return;
     const int tid = threadIdx.x;
+    // every owner but the last holds its last iteration here (slot 2g)
+    const int64_t slot1 = sk_slot(sk, g1, local, sk_end(sk, g1));
     f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t g = g0; g <= g1; g += SK_BATCH) {
         u32x4 v[SK_BATCH];
@@ -725,7 +727,7 @@ __global__ __launch_bounds__(THREADS) void hgemm_streamk_fixup(HgemmArgs p, Stre
             const int64_t gu = g + u <= g1 ? g + u : g1;
             const uint32_t off = g + u <= g1 ? static_cast<uint32_t>(tid * 16) : 0x80000000u;
             v[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, sk_slot(sk, gu, local, sk_end(sk, gu))), off,
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(sk, gu == g1 ? slot1 : 2 * gu), off,
                                                              piece * THREADS * 16, 0));
         }
 #pragma unroll
