@@ -188,8 +188,14 @@ struct F8Tile {
     using OpA = Operand<true, WAVES, Fmt<FA>::ROWB / 2, Fmt<FA>::STEPB / 2>;
     using OpB = Operand<true, WAVES, Fmt<FB>::ROWB / 2, Fmt<FB>::STEPB / 2>;
     static constexpr int PANEL_A = OpA::PANEL, PANEL_B = OpB::PANEL;
-    static constexpr int SCALES = MX ? 4 * (F8_BM + F8_BN) : 0;  // bytes per stage
-    static constexpr int DATA = PANEL_A + PANEL_B + SCALES;
+    static constexpr int DATA = PANEL_A + PANEL_B;
+    // MX: a ring of three scale groups after the stage ring; a group holds
+    // the scale words of four stages (16 bytes per panel row, A's 256 rows
+    // then B's), so one 16-row x 16-byte load fetches four stages' worth of
+    // 16 rows from 16 cache lines, where per-stage loads would touch a line
+    // per row every stage
+    static constexpr int SGROUP = 16 * (F8_BM + F8_BN);
+    static constexpr int SRING = MX ? 3 * SGROUP : 0;
     static constexpr int EPI = WAVES * 32 * WTN * 4;              // epilogue staging
     // A stage buffer holds one stage's data; C is staged across the NEED
     // consecutive buffers the epilogue takes (f8_tile_store).
@@ -230,6 +236,7 @@ __device__ __forceinline__ int f8_tile_steps(
     using OpA = typename L::OpA;
     using OpB = typename L::OpB;
     constexpr int PANEL_A = L::PANEL_A, PANEL_B = L::PANEL_B, STAGE = L::STAGE;
+    constexpr int SGROUP = L::SGROUP;
     constexpr int PER_DATA = L::PER_DATA, PER_STAGE = L::PER_STAGE;
 
     const DmaArgs &d = p.d;
@@ -243,38 +250,61 @@ __device__ __forceinline__ int f8_tile_steps(
     opa.init(d.A + t.batch * d.sA, d.lda, d.M, m0, (d.M - 1) * d.lda + p.ka, wave, lane);
     opb.init(d.B + t.batch * d.sB, d.ldb, d.N, n0, (d.N - 1) * d.ldb + p.kb, wave, lane);
 
-    // MX: this wave's scale load of a stage: waves 0-3 fetch the scale words
-    // of A's panel rows 64w .. 64w+63, waves 4-7 those of B's; rows past the
-    // matrix read zeros (their data is zero too).
-    u32x4 srs = {0u, 0u, 0u, 0u};
-    uint32_t svoff = OOB, slds = 0;
-    int64_t sld = 0;
+    // MX: scale group g (stages 4g .. 4g+3, scale bytes 16g .. 16g+15 of a
+    // row) sits in ring slot g % 3.  Load (g, part) is one 4-byte direct load
+    // per lane by wave w of part 8*part + w of the group's 32: 16 panel rows
+    // (A's when part < 2, else B's) of 16 bytes, lane l taking row l/4, word
+    // l%4.  Rows past the matrix read zeros; words past a row's scales are
+    // read but used only by stages past K.
+    u32x4 srs_a = {0u, 0u, 0u, 0u}, srs_b = {0u, 0u, 0u, 0u};
+    uint32_t sv[4] = {OOB, OOB, OOB, OOB};  // this lane's row offset for each part
     if (MX) {
-        const bool on_a = wave < 4;
-        const int q = wave & 3;
-        const int64_t r = (on_a ? m0 : n0) + 64 * q + lane;
-        const int64_t R = on_a ? d.M : d.N;
-        sld = on_a ? p.ldsa : p.ldsb;
-        const uint8_t *base = on_a ? p.sa + t.batch * p.ssa : p.sb + t.batch * p.ssb;
-        srs = dma::raw_buffer(static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(base))),
-                              static_cast<uint32_t>(uniform(R * sld)));
-        svoff = r < R ? static_cast<uint32_t>(r * sld) : OOB;
-        slds = PANEL_A + PANEL_B + (on_a ? 0 : 4 * F8_BM) + 256 * q;
+        const int sl = (lane >> 2) + 16 * wave, sd = 4 * (lane & 3);
+        srs_a = dma::raw_buffer(
+            static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(p.sa + t.batch * p.ssa))),
+            static_cast<uint32_t>(uniform(d.M * p.ldsa)));
+        srs_b = dma::raw_buffer(
+            static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(p.sb + t.batch * p.ssb))),
+            static_cast<uint32_t>(uniform(d.N * p.ldsb)));
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+            const bool on_a = part < 2;
+            const int64_t r = (on_a ? m0 : n0) + 128 * (part & 1) + sl;
+            const int64_t R = on_a ? d.M : d.N;
+            sv[part] = r < R ? static_cast<uint32_t>(r * (on_a ? p.ldsa : p.ldsb) + sd) : OOB;
+        }
     }
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-    auto load_scales = [&](int buf, int64_t stage) {
-        if (MX)
-            direct_load4(srs, lds_base + buf * STAGE + slds,
-                         svoff == OOB ? OOB : svoff + static_cast<uint32_t>(4 * stage));
+    const uint32_t sring = lds_base + STAGES * STAGE;
+    auto load_scales = [&](int64_t g, int part) {
+        if (!MX) return;
+        const uint32_t dst =
+            sring + static_cast<uint32_t>(g % 3) * SGROUP + static_cast<uint32_t>(8 * part + wave) * 256;
+        direct_load4(part < 2 ? srs_a : srs_b, dst,
+                     sv[part] == OOB ? OOB : sv[part] + static_cast<uint32_t>(16 * g));
     };
     const int64_t steps = ke - kb;
 
+    // MX prologue: groups g0 and g0 + 1 whole, and the parts of g0 + 2 the
+    // prologue stages do not carry (each stage's load group carries one
+    // scale load, so the count per stage stays uniform); older than every
+    // stage, so the first stage's wait covers them.
+    const int64_t g0 = kb >> 2;
+    if (MX) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+            load_scales(g0, part);
+            load_scales(g0 + 1, part);
+        }
+#pragma unroll
+        for (int part = STAGES; part < 4; ++part) load_scales(g0 + 2, part);
+    }
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) {
         if (st < steps) {
             opa.issue(lds + st * STAGE, kb + st, p.ka, wave);
             opb.issue(lds + st * STAGE + PANEL_A, kb + st, p.kb, wave);
-            load_scales(st, kb + st);
+            if (st < 4) load_scales(g0 + 2, st);
         }
     }
     wait_stages<PER_STAGE, STAGES>(int(steps - 1 < STAGES - 1 ? steps - 1 : STAGES - 1));
@@ -296,14 +326,18 @@ __device__ __forceinline__ int f8_tile_steps(
     for (int i = 0; i < FM; ++i) sa[i] = nsa[i] = UNIT_SCALE;
 #pragma unroll
     for (int j = 0; j < FN; ++j) sb[j] = nsb[j] = UNIT_SCALE;
-    auto read_scales = [&](int buf) {
+    // the scale words of absolute stage a, from its group's ring slot
+    auto read_scales = [&](int64_t a) {
         if (!MX) return;
-        const LDS uint32_t *s = reinterpret_cast<const LDS uint32_t *>(lds + buf * STAGE + PANEL_A + PANEL_B);
+        const LDS uint32_t *s = reinterpret_cast<const LDS uint32_t *>(
+            lds + STAGES * STAGE + static_cast<int>((a >> 2) % 3) * SGROUP);
+        const int w = static_cast<int>(a & 3);
         const int sh = 8 * (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) nsa[i] = int(s[wm * WTM + i * 32 + (lane & 31)] >> sh);
+        for (int i = 0; i < FM; ++i) nsa[i] = int(s[4 * (wm * WTM + i * 32 + (lane & 31)) + w] >> sh);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) nsb[j] = int(s[F8_BM + wn * WTN + j * 32 + (lane & 31)] >> sh);
+        for (int j = 0; j < FN; ++j)
+            nsb[j] = int(s[4 * (F8_BM + wn * WTN + j * 32 + (lane & 31)) + w] >> sh);
     };
     auto take_scales = [&]() {
 #pragma unroll
@@ -344,7 +378,7 @@ __device__ __forceinline__ int f8_tile_steps(
 
     read_b(0, 0, 0);
     read_a(0, 0, 0);
-    read_scales(0);
+    read_scales(kb);
     take_scales();
     int buf = 0;
     const int64_t main_steps = steps - 1;
@@ -364,7 +398,7 @@ __device__ __forceinline__ int f8_tile_steps(
         const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
         read_b(nbuf, 0, 0);
         read_a(nbuf, 0, 0);
-        read_scales(nbuf);
+        read_scales(kb + s + 1);
         const int64_t refill = s + STAGES;  // within the range
         const bool do_refill = refill < steps;
         const u32x4 ra = opa.rsrc(kb + refill), rb = opb.rsrc(kb + refill);
@@ -383,7 +417,8 @@ __device__ __forceinline__ int f8_tile_steps(
                     if (q < OpA::PER_WAVE) opa.load(ra, la, q, kla, wave);
                     else opb.load(rb, la + PANEL_A, q - OpA::PER_WAVE, klb, wave);
                 }
-                if (j == 0) load_scales(buf, kb + refill);
+                // two groups ahead of the stage that issues it, part a % 4
+                if (j == 0) load_scales(((kb + s) >> 2) + 2, static_cast<int>((kb + s) & 3));
             }
         }
         take_scales();
@@ -435,8 +470,8 @@ __device__ __forceinline__ void f8_tile_store(
 template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_kernel(F8Args p) {
     using L = F8Tile<FA, FB, WAVES_M, WAVES_N, MX>;
-    static_assert(STAGES >= 2 && STAGES * L::STAGE <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * L::STAGE];
+    static_assert(STAGES >= 2 && STAGES * L::STAGE + L::SRING <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * L::STAGE + L::SRING];
     LDS char *lds = (LDS char *)smem;
     TileCoord t = tile_of(p.d.grid, blockIdx.x);
     t.batch = uniform(t.batch);
@@ -463,9 +498,9 @@ template <int FA, int FB, int OUT, int WAVES_M, int WAVES_N, int STAGES, bool MX
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void f8gemm_dma_streamk_kernel(F8Args p,
                                                                                    DmaStreamK sk) {
     using L = F8Tile<FA, FB, WAVES_M, WAVES_N, MX>;
-    static_assert(STAGES >= 2 && STAGES * L::STAGE <= 160 * 1024, "LDS budget");
+    static_assert(STAGES >= 2 && STAGES * L::STAGE + L::SRING <= 160 * 1024, "LDS budget");
     static_assert(L::FM * L::FN * 4 * L::WAVES * 64 * 16 == SK_SLOT * 4, "a slot holds one tile");
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * L::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * L::STAGE + L::SRING];
     LDS char *lds = (LDS char *)smem;
 
     // logical workgroup: the hardware id regrouped per XCD, so that the
