@@ -253,13 +253,17 @@ __device__ __forceinline__ int f8_tile_steps(
     // MX: scale group g (stages 4g .. 4g+3, scale bytes 16g .. 16g+15 of a
     // row) sits in ring slot g % 3.  Load (g, part) is one 4-byte direct load
     // per lane by wave w of part 8*part + w of the group's 32: 16 panel rows
-    // (A's when part < 2, else B's) of 16 bytes, lane l taking row l/4, word
-    // l%4.  Rows past the matrix read zeros; words past a row's scales are
-    // read but used only by stages past K.
+    // (A's when part < 2, else B's) of 16 bytes, lane l taking row l/4.  Word
+    // v of panel row r holds the row's scale word v ^ ((r / 8) % 4), so that
+    // the 32 rows one scale read touches fall in distinct banks.  Rows past
+    // the matrix read zeros; words past a row's scales are read but used only
+    // by stages past K.
     u32x4 srs_a = {0u, 0u, 0u, 0u}, srs_b = {0u, 0u, 0u, 0u};
     uint32_t sv[4] = {OOB, OOB, OOB, OOB};  // this lane's row offset for each part
     if (MX) {
-        const int sl = (lane >> 2) + 16 * wave, sd = 4 * (lane & 3);
+        // panel row 128*(part & 1) + sl (plus 256 for B): (row / 8) % 4 is
+        // (2*wave + lane/32) % 4
+        const int sl = (lane >> 2) + 16 * wave, sd = 4 * ((lane & 3) ^ ((2 * wave + (lane >> 5)) & 3));
         srs_a = dma::raw_buffer(
             static_cast<uint64_t>(uniform(reinterpret_cast<int64_t>(p.sa + t.batch * p.ssa))),
             static_cast<uint32_t>(uniform(d.M * p.ldsa)));
@@ -331,7 +335,9 @@ __device__ __forceinline__ int f8_tile_steps(
         if (!MX) return;
         const LDS uint32_t *s = reinterpret_cast<const LDS uint32_t *>(
             lds + STAGES * STAGE + static_cast<int>((a >> 2) % 3) * SGROUP);
-        const int w = static_cast<int>(a & 3);
+        // the rows are 32-aligned blocks plus lane % 32, so (row / 8) % 4 is
+        // (lane / 8) % 4
+        const int w = static_cast<int>(a & 3) ^ ((lane >> 3) & 3);
         const int sh = 8 * (lane >> 5);
 #pragma unroll
         for (int i = 0; i < FM; ++i) nsa[i] = int(s[4 * (wm * WTM + i * 32 + (lane & 31)) + w] >> sh);
