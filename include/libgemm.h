@@ -329,9 +329,11 @@ gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, float alpha,
  *   B        K x N, contiguous along K: column j is elements j*ldb ..
  *            j*ldb+K-1 of its stream; the same rules.
  *   scaleA   E8M0 bytes, row i of A's at scaleA + i*ldsa; 4-byte aligned,
- *            ldsa a multiple of 4 and at least 4*ceil(K/128) (the kernel
- *            reads scales four blocks at a time; bytes past ceil(K/32) in a
- *            row are read but never used).  scaleB likewise for B's columns.
+ *            ldsa a multiple of 4 and at least 4*ceil(K/128).  The kernel
+ *            reads a row's scales sixteen blocks at a time, so it may read
+ *            bytes past the row's ceil(K/32) (into the row's padding or the
+ *            next row) but never past the slice's M*ldsa bytes; such bytes
+ *            are never used.  scaleB likewise for B's columns (N*ldsb).
  *   formatA, formatB  element formats of one width: both 8-bit (E4M3/E5M2,
  *            in any combination), both 6-bit (E2M3/E3M2) or both E2M1;
  *            a mixed-width pair is GEMM_ERR_UNSUPPORTED.
