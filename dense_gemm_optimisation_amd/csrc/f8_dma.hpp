@@ -16,14 +16,15 @@
 // accumulators hold consecutive columns of C.
 //
 // The pipeline is the 16-bit direct-load one of dma_tile.hpp (256 x 256 block
-// tile, 2 x 4 waves, two LDS stages) run on the bytes viewed as 16-bit pairs.
-// A stage is 128 k of every format: a K-contiguous panel row of 128 bytes
-// for 8-bit elements, 64 bytes for 4-bit ones, and for 6-bit ones 128 bytes
-// loaded of which the first 96 are that stage's (the stage advances 96 bytes
-// along the row; the rest is loaded again as the next stage's start).  With
-// scales, each stage also moves the four scale bytes (blocks 4s .. 4s+3) of
-// every panel row into LDS, one 4-byte direct load per lane, in the same
-// load group as the stage's operands.
+// tile, 2 x 4 waves, a ring of LDS stages: two, or four for 4-bit elements)
+// run on the bytes viewed as 16-bit pairs.  A stage is 128 k of every format:
+// a K-contiguous panel row of 128 bytes for 8-bit elements, 64 bytes for
+// 4-bit ones, and for 6-bit ones 128 bytes loaded of which the first 96 are
+// that stage's (the stage advances 96 bytes along the row; the rest is
+// loaded again as the next stage's start).  With scales, every stage's load
+// group also carries one 4-byte direct load per lane that fetches 16 bytes
+// (four stages' worth) of the scales of 16 panel rows into a ring of scale
+// groups two groups ahead (f8_tile_steps).
 #pragma once
 
 #include <type_traits>
@@ -220,8 +221,9 @@ struct F8Tile {
 // stage and the workgroup barrier; the refill of the stage just consumed is
 // issued between the last two instructions, after the barrier has shown
 // that every wave has read it.  With scales (MX), each lane reads its six
-// fragments' scale words from the stage's buffer right after the barrier,
-// into registers that take over once the current stage's last row is done.
+// fragments' scale words for the next stage from the scale ring right after
+// the barrier, into registers that take over once the current stage's last
+// row is done.
 //
 // f8_tile_steps runs stages [kb, ke) of one tile (128 k each, numbered from
 // the start of K) into acc and returns the ring buffer that held the last
