@@ -1138,6 +1138,42 @@ def test_mx_streamk_tail_config_sampled():
     check_mx(workloads.config("mxfp4_tail"), sample="auto")
 
 
+def _random_sk_cases():
+    # seeded random shapes for the narrow-float stream-K schedule: ragged M
+    # and N, K from one 16-byte chunk up (MX: from one 64-k pair of blocks),
+    # every output type, batches, both orders of C for MX
+    rng = np.random.default_rng(2024)
+    f8, mx = [], []
+    for n in range(6):
+        M, N = (int(v) for v in rng.integers(200, 2600, 2))
+        K = int(rng.integers(1, 190)) * 16
+        fa, fb = (str(v) for v in rng.choice(["e4m3", "e5m2"], 2))
+        f8.append(F8(f"f8-sk-rand{n}", fa, fb, str(rng.choice(["f32", "bf16", "f16"])), M, N, K,
+                     alpha=float(rng.choice([1.0, 0.5])), beta=float(rng.choice([0.0, 1.0])),
+                     batch=int(rng.integers(1, 3)), **TN))
+    for n in range(6):
+        fa, fb = [("e4m3", "e5m2"), ("e2m3", "e3m2"), ("e2m1", "e2m1")][n % 3]
+        M, N = (int(v) for v in rng.integers(200, 2600, 2))
+        mx.append(workloads.MxProblem(f"mx-sk-rand{n}", fa, fb, str(rng.choice(["f32", "bf16"])), M, N,
+                                      int(rng.integers(1, 48)) * 64, alpha=0.5,
+                                      beta=float(rng.choice([0.0, 1.0])), batch=int(rng.integers(1, 3)),
+                                      order_c=int(rng.choice([ROW, COL]))))
+    return f8, mx
+
+
+SK_RAND_F8, SK_RAND_MX = _random_sk_cases()
+
+
+@pytest.mark.parametrize("p", SK_RAND_F8, ids=lambda p: p.name)
+def test_f8_streamk_random_shapes(p, force_streamk):
+    check(p, kernel="f8gemm_mfma_dma_streamk", seed=7, sample="auto", use_workspace=True, repeat=2)
+
+
+@pytest.mark.parametrize("p", SK_RAND_MX, ids=lambda p: p.name)
+def test_mx_streamk_random_shapes(p, force_streamk):
+    check_mx(p, kernel="mxgemm_mfma_dma_streamk", seed=8, sample="auto", use_workspace=True, repeat=2)
+
+
 # ------------------------------------------------------------------ quantised (8-bit) output
 
 QUANT_SHAPES = [(8, 8, 8), (256, 256, 64), (264, 520, 72), (1000, 1032, 1000), (24, 4096, 512)]
