@@ -277,6 +277,10 @@ struct WsPlan {
     PackSpec pa{}, pb{};
     int64_t off_a = 0, off_b = 0;  // byte offsets of the copies (partial tiles at 0)
     int64_t used = 0;              // workspace bytes the plan touches
+    // the last few columns of a packed problem, run as a problem of their
+    // own after q (kt None when there is no such split)
+    Kernel kt = Kernel::None;
+    Problem qt;
 };
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -365,11 +369,43 @@ bool plan_packed(const Problem &p, Kernel k, const void *workspace, size_t bytes
     };
     if (!place(0, h16 ? Kernel::HgemmPackDma : Kernel::SgemmPackDma)) return false;
     if (!(h16 ? hgemm_dma_eligible(w.q) : sgemm_dma_eligible(w.q))) return false;
-    if (h16 ? hgemm_dma_streamk_eligible(w.q, force) : sgemm_dma_streamk_eligible(w.q, force)) {
-        const int64_t partials = round_up(h16 ? hgemm_dma_streamk_bytes(w.q) : sgemm_streamk_bytes(w.q), 256);
-        WsPlan keep = w;
-        if (!place(partials, h16 ? Kernel::HgemmPackDmaStreamK : Kernel::SgemmPackDmaStreamK))
+    // A last tile column with at most TAIL_COLS columns (N = 4097 leaves one)
+    // would cost the direct-load kernel a whole wave of tiles for a sliver of
+    // C; those columns run instead as a problem of their own on the packed
+    // copies, after the main part, when that problem goes to a split-K
+    // kernel (32 x 32 tiles, K split inside the workgroup).  No fused
+    // epilogue: the workspace entry points have none.
+    constexpr int64_t TAIL_COLS = 32;
+    auto split_tail = [&](WsPlan &x) {
+        const int64_t nt = x.q.N % tile;
+        if (nt == 0 || nt > TAIL_COLS || x.q.N < tile || x.q.epi.active()) return false;
+        Problem qt = x.q;
+        const int64_t nm = x.q.N - nt;
+        const int64_t boff = x.q.b_kmajor ? nm * x.q.ldb : nm;  // elements
+        qt.N = nt;
+        qt.B = static_cast<const char *>(x.q.B) + boff * esize;
+        qt.span_b = x.q.span_b - boff;
+        qt.C = static_cast<char *>(x.q.C) + nm * elem_bytes(x.q.out);  // canonical C is row-major
+        const Kernel kt = choose(qt, false);
+        if (kt != Kernel::HgemmSplitk && kt != Kernel::SgemmSplitk) return false;
+        x.q.N = nm;
+        x.qt = qt;
+        x.kt = kt;
+        return true;
+    };
+    WsPlan cand = w;
+    const bool tail = split_tail(cand);
+    const Problem &part = tail ? cand.q : w.q;  // what the direct-load kernel computes
+    if (h16 ? hgemm_dma_streamk_eligible(part, force) : sgemm_dma_streamk_eligible(part, force)) {
+        const int64_t partials = round_up(h16 ? hgemm_dma_streamk_bytes(part) : sgemm_streamk_bytes(part), 256);
+        WsPlan keep = tail ? cand : w;
+        if (place(partials, h16 ? Kernel::HgemmPackDmaStreamK : Kernel::SgemmPackDmaStreamK)) {
+            if (tail) split_tail(w);  // the copies moved: the tail's pointers again
+        } else {
             w = keep;  // no room: plain schedule
+        }
+    } else if (tail) {
+        w = cand;
     }
     return true;
 }
@@ -466,6 +502,13 @@ hipError_t launch_planned(const WsPlan &w, void *workspace, hipStream_t stream) 
     }
 }
 
+// A planned call: the plan's main launches, then its tail columns if split off.
+hipError_t launch_plan(const WsPlan &w, void *workspace, hipStream_t stream) {
+    const hipError_t e = launch_planned(w, workspace, stream);
+    if (e != hipSuccess || w.kt == Kernel::None) return e;
+    return launch(w.kt, w.qt, stream);
+}
+
 gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K, float alpha,
                   const void *A, int64_t lda, int orderA, const void *B, int64_t ldb, int orderB,
                   float beta, void *C, int64_t ldc, int orderC, int64_t batch, int64_t strideA,
@@ -481,7 +524,7 @@ gemm_status_t run(Elem in, Elem in_b, Elem out, int64_t M, int64_t N, int64_t K,
         st = use_workspace(p, M, N, K, orderA, lda, orderB, ldb, orderC, ldc, strideA, strideB,
                            strideC, bias, strideBias, A, B, C, workspace, workspace_bytes, w);
     if (st != GEMM_OK || w.k == Kernel::None) return st;
-    const hipError_t err = launch_planned(w, workspace, stream);
+    const hipError_t err = launch_plan(w, workspace, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -1025,7 +1068,7 @@ gemm_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, float alpha, co
         w.k = chosen;
         plan_workspace(p, scratch, full, w);  // the same plan, placed in the scratch
     }
-    const hipError_t err = launch_planned(w, scratch, stream);
+    const hipError_t err = launch_plan(w, scratch, stream);
     if (err == hipErrorInvalidConfiguration) return GEMM_ERR_UNSUPPORTED;
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -388,7 +388,10 @@ gemm_status_t gemm_mx(int64_t M, int64_t N, int64_t K, float alpha,
  * the same cost model) runs on the copies, with the caller's M,
  * N and C.  The zero padding adds nothing to any result.  This is chosen
  * whenever the copies and any partial tiles fit the workspace; otherwise the
- * general kernel runs on the caller's operands as described above.
+ * general kernel runs on the caller's operands as described above.  When the
+ * last column of tiles of the (row-major-C) problem holds at most 32 columns
+ * of C, those columns run after the rest as a problem of their own on the
+ * copies, on the split-K kernel, instead of taking a wave of tiles.
  * A 16-bit problem of at most 16 rows of C (of K-contiguous A) with an
  * N-contiguous B, N >= 256 and K >= 1024 is split along K across
  * workgroups ("GPU GEMM 优化完全拆解（三）", pinghaoyang.com.cn, the

@@ -485,14 +485,20 @@ def test_streamk_kernel_choice(lib, clean_env):
     assert kname_ws(lib, "bf16", 300, 290, 131) == "hgemm_mfma_streamk"
     assert kname_ws(lib, "bf16", 4096, 4096, 4096) == "hgemm_mfma_dma"      # nothing to cut
     assert kname_ws(lib, "bf16", 512, 768, 8192) == "hgemm_splitk"
-    assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_dma_streamk_packed"
+    # N = 4097: the one-column last tile column runs on its own (split-K on
+    # the copies), and the rest is whole waves; a wider last column (54) is
+    # kept in the grid, whose last wave is then cut
+    assert kname_ws(lib, "bf16", 4095, 4097, 1001) == "hgemm_mfma_dma_packed"
+    assert kname_ws(lib, "bf16", 4095, 4150, 1001) == "hgemm_mfma_dma_streamk_packed"
     clean_env(0)
     # fp32: unaligned with at least 160 tiles of 128 x 128 is copied for the
     # direct-load kernel, on its stream-K schedule where the cut tail pays
-    # (1056 tiles of 63 k steps: 1024 whole and 32 cut; of 9 steps: no);
-    # fewer tiles use the general kernel's schedule (128 x 128 tiles, 1024
-    # workgroups)
-    assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_dma_streamk_packed"
+    # (1056 tiles of 63 k steps: 1024 whole and 32 cut); fewer tiles use the
+    # general kernel's schedule (128 x 128 tiles, 1024 workgroups).  N = 4097
+    # leaves one column in its last tile column: that column runs on its own
+    # and the remaining 1024 tiles are whole waves
+    assert kname_ws(lib, "f32", 4095, 4097, 1001) == "sgemm_mfma_dma_packed"
+    assert kname_ws(lib, "f32", 4095, 4140, 1001) == "sgemm_mfma_dma_streamk_packed"  # last column: 44
     assert kname_ws(lib, "f32", 4095, 4097, 129) == "sgemm_mfma_dma_packed"
     # 187 tiles of 63 steps: the partial tiles and copies exceed the workspace
     assert kname_ws(lib, "f32", 2049, 1283, 1001) == "sgemm_mfma_dma_packed"

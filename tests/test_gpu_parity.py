@@ -834,9 +834,9 @@ def test_f32_streamk_integers_bit_exact():
 
 def test_f32_packed_edge_config_sampled():
     # the unaligned 4095 x 4097 x 1001 fp32 problem with a workspace: copied
-    # to aligned operands, then the direct-load kernel's stream-K schedule
-    # (1056 tiles: 1024 whole, 32 cut)
-    check(workloads.config("f32_edge"), kernel="sgemm_mfma_dma_streamk_packed", sample="auto",
+    # to aligned operands, then the direct-load kernel on 4095 x 4096 (1024
+    # tiles, whole waves) and the one remaining column on the split-K kernel
+    check(workloads.config("f32_edge"), kernel="sgemm_mfma_dma_packed", sample="auto",
           use_workspace=True, repeat=2)
 
 
