@@ -11,6 +11,12 @@
 #include <cstring>
 
 #include "gemm_problem.hpp"
+
+namespace libgemm {
+// The copies of both operands of a packed plan in one launch (pack.hip).
+hipError_t launch_pack2(const PackSpec &sa, void *dst_a, const PackSpec &sb, void *dst_b,
+                        hipStream_t stream);
+}  // namespace libgemm
 #include "libgemm.h"
 
 using namespace libgemm;
@@ -483,8 +489,7 @@ gemm_status_t use_workspace(const Problem &p, int64_t M, int64_t N, int64_t K, i
 hipError_t launch_planned(const WsPlan &w, void *workspace, hipStream_t stream) {
     char *ws = static_cast<char *>(workspace);
     if (is_packed(w.k)) {
-        hipError_t e = launch_pack(w.pa, ws + w.off_a, stream);
-        if (e == hipSuccess) e = launch_pack(w.pb, ws + w.off_b, stream);
+        const hipError_t e = launch_pack2(w.pa, ws + w.off_a, w.pb, ws + w.off_b, stream);
         if (e != hipSuccess) return e;
     }
     switch (w.k) {

@@ -36,16 +36,16 @@ struct PackArgs {
     uint32_t chunks_per_row;           // inner_p * esize / 16
 };
 
-// Grid: x covers the chunks of one slice (a grid-stride loop past 8192
-// workgroups), y the slices (a loop past gridDim.y).  A slice has fewer than
-// 2^31 chunks (its source extent is below 2^31 bytes), so the index
-// arithmetic inside a slice is 32-bit.
+// Grid: x covers the chunks of one slice (workgroups bx of gx, a
+// grid-stride loop past them), y the slices (a loop past gridDim.y).  A
+// slice has fewer than 2^31 chunks (its source extent is below 2^31 bytes),
+// so the index arithmetic inside a slice is 32-bit.
 template <int ESIZE>
-__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+__device__ __forceinline__ void pack_run(const PackArgs &a, uint32_t bx, uint32_t gx) {
     constexpr int PER = 16 / ESIZE;  // elements per chunk
     const uint32_t per_slice = a.outer_p * a.chunks_per_row;
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y)
-    for (uint32_t r = blockIdx.x * 256u + threadIdx.x; r < per_slice; r += gridDim.x * 256u) {
+    for (uint32_t r = bx * 256u + threadIdx.x; r < per_slice; r += gx * 256u) {
         const int64_t g = b * per_slice + r;  // destination chunk
         const uint32_t o = r / a.chunks_per_row;
         const int64_t e0 = int64_t(r - o * a.chunks_per_row) * PER;
@@ -109,14 +109,26 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     }
 }
 
-}  // namespace
-
-int64_t packed_bytes(const PackSpec &s) {
-    return (s.stride == 0 && s.batch > 1 ? 1 : s.batch) * s.outer_p * s.inner_p * s.esize;
+template <int ESIZE>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+    pack_run<ESIZE>(a, blockIdx.x, gridDim.x);
 }
 
-hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream) {
-    PackArgs a{};
+// Both operands in one launch: workgroups [0, na) copy a, the rest b, so
+// the two copies overlap instead of running one after the other.
+template <int ESIZE>
+__global__ __launch_bounds__(256) void pack2_kernel(PackArgs a, PackArgs b, uint32_t na) {
+    if (blockIdx.x < na)
+        pack_run<ESIZE>(a, blockIdx.x, na);
+    else
+        pack_run<ESIZE>(b, blockIdx.x - na, gridDim.x - na);
+}
+
+// The kernel arguments of spec s with destination dst, and the x workgroups
+// and y slices a launch of it takes (0 workgroups when there is nothing to
+// copy); false when a slice has 2^31 chunks or more.
+bool pack_args(const PackSpec &s, void *dst, PackArgs &a, int64_t &bx, int64_t &by) {
+    a = PackArgs{};
     a.src = static_cast<const char *>(s.src);
     a.dst = static_cast<char *>(dst);
     a.outer = s.outer;
@@ -126,18 +138,53 @@ hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream) {
     a.batch = s.stride == 0 && s.batch > 1 ? 1 : s.batch;
     const int64_t cpr = s.inner_p * s.esize / 16;
     const int64_t per_slice = s.outer_p * cpr;
-    if (per_slice == 0 || a.batch == 0) return hipSuccess;
-    if (per_slice >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    bx = by = 0;
+    if (per_slice == 0 || a.batch == 0) return true;
+    if (per_slice >= (int64_t(1) << 31)) return false;
     a.outer_p = static_cast<uint32_t>(s.outer_p);
     a.chunks_per_row = static_cast<uint32_t>(cpr);
     // enough workgroups to fill the chip several times over; the loops cover the rest
-    const int64_t bx = (per_slice + 255) / 256 < 8192 ? (per_slice + 255) / 256 : 8192;
-    const int64_t by = a.batch < 1024 ? a.batch : 1024;
+    bx = (per_slice + 255) / 256 < 8192 ? (per_slice + 255) / 256 : 8192;
+    by = a.batch < 1024 ? a.batch : 1024;
+    return true;
+}
+
+}  // namespace
+
+int64_t packed_bytes(const PackSpec &s) {
+    return (s.stride == 0 && s.batch > 1 ? 1 : s.batch) * s.outer_p * s.inner_p * s.esize;
+}
+
+hipError_t launch_pack(const PackSpec &s, void *dst, hipStream_t stream) {
+    PackArgs a;
+    int64_t bx, by;
+    if (!pack_args(s, dst, a, bx, by)) return hipErrorInvalidValue;
+    if (bx == 0) return hipSuccess;
     void *args[] = {&a};
     const void *k = s.esize == 2 ? reinterpret_cast<const void *>(&pack_kernel<2>)
                                  : reinterpret_cast<const void *>(&pack_kernel<4>);
     return hipLaunchKernel(k, dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by)), dim3(256),
                            args, 0, stream);
+}
+
+// Copies of two operands of one element size, in one launch when both have
+// something to copy.
+hipError_t launch_pack2(const PackSpec &sa, void *dst_a, const PackSpec &sb, void *dst_b,
+                        hipStream_t stream) {
+    PackArgs a, b;
+    int64_t ax, ay, bx, by;
+    if (!pack_args(sa, dst_a, a, ax, ay) || !pack_args(sb, dst_b, b, bx, by))
+        return hipErrorInvalidValue;
+    if (ax == 0 || bx == 0 || sa.esize != sb.esize) {
+        const hipError_t e = launch_pack(sa, dst_a, stream);
+        return e != hipSuccess ? e : launch_pack(sb, dst_b, stream);
+    }
+    uint32_t na = static_cast<uint32_t>(ax);
+    void *args[] = {&a, &b, &na};
+    const void *k = sa.esize == 2 ? reinterpret_cast<const void *>(&pack2_kernel<2>)
+                                  : reinterpret_cast<const void *>(&pack2_kernel<4>);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(ax + bx), static_cast<unsigned>(ay > by ? ay : by)),
+                           dim3(256), args, 0, stream);
 }
 
 }  // namespace libgemm
